@@ -1,0 +1,114 @@
+"""fp64 CPU oracle of the selective state-space scan.
+
+TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the benchmark's
+CPU-baseline leg are its only users. It shares no code with the GPU library
+and imports nothing from it.
+
+The arithmetic lives in ``ssm_oracle.c`` (a plain loop over the recurrence of
+the page "Mamba and State Space Models", sections "A State of Fixed Size" and
+"Chosen by the Token"); this module only marshals arrays into fp64 and calls
+it. Inputs may be numpy arrays or torch tensors of any float dtype: they are
+widened exactly to fp64 (bf16 and fp32 values are representable in fp64), so
+the oracle sees the very values the GPU consumed. Results stay fp64.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+_LIB = None
+
+
+def library_path():
+    return os.environ.get("SSM_ORACLE_LIB", _build.LIBRARY)
+
+
+def _load(path=None):
+    path = path or library_path()
+    if not os.path.exists(path):
+        _build.compile_oracle(output=path)
+    lib = ctypes.CDLL(path)
+    dp = ctypes.POINTER(ctypes.c_double)
+    i64 = ctypes.c_int64
+    lib.oracle_scan_fwd.argtypes = [i64, i64, i64, i64] + [dp] * 10 + [ctypes.c_int]
+    lib.oracle_scan_fwd.restype = ctypes.c_int
+    lib.oracle_state_update.argtypes = [i64, i64, i64] + [dp] * 9
+    lib.oracle_state_update.restype = ctypes.c_int
+    lib.oracle_max_dstate.restype = ctypes.c_int
+    return lib
+
+
+def _f64(a):
+    """Exact widening of a numpy array or torch tensor to a C-contiguous fp64 array."""
+    if a is None:
+        return None
+    if hasattr(a, "detach"):  # torch tensor: widen on the host with torch (knows bf16)
+        import torch
+        a = a.detach().to("cpu").to(torch.float64).contiguous().numpy()
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _ptr(a):
+    if a is None:
+        return ctypes.POINTER(ctypes.c_double)()
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+class Oracle:
+    """Handle on one compiled oracle library (the default one, or a test build)."""
+
+    def __init__(self, path=None):
+        self.lib = _load(path)
+        self.max_dstate = self.lib.oracle_max_dstate()
+
+    def scan_fwd(self, x, delta, A, B, C, D=None, z=None, h0=None, zoh=False,
+                 return_state=True):
+        """Scan a whole sequence.
+
+        Shapes: x, delta, z (batch, L, dim); A (dim, N); B, C (batch, L, N);
+        D (dim,); h0 (batch, dim, N). Returns (y, hL) as fp64 numpy arrays,
+        y of shape (batch, L, dim) and hL of shape (batch, dim, N).
+        """
+        x, delta, A, B, C = (_f64(v) for v in (x, delta, A, B, C))
+        D, z, h0 = _f64(D), _f64(z), _f64(h0)
+        batch, seqlen, dim = x.shape
+        dstate = A.shape[1]
+        assert delta.shape == x.shape and A.shape == (dim, dstate)
+        assert B.shape == (batch, seqlen, dstate) and C.shape == B.shape
+        assert D is None or D.shape == (dim,)
+        assert z is None or z.shape == x.shape
+        assert h0 is None or h0.shape == (batch, dim, dstate)
+        y = np.zeros((batch, seqlen, dim), dtype=np.float64)
+        hL = np.zeros((batch, dim, dstate), dtype=np.float64) if return_state else None
+        rc = self.lib.oracle_scan_fwd(batch, seqlen, dim, dstate, _ptr(x), _ptr(delta),
+                                      _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                                      _ptr(h0), _ptr(y), _ptr(hL), int(bool(zoh)))
+        if rc != 0:
+            raise ValueError(f"oracle_scan_fwd rejected its arguments (status {rc})")
+        return y, hL
+
+    def state_update(self, h, x, delta, A, B, C, D=None, z=None):
+        """One decode step. Shapes: h (batch, dim, N); x, delta, z (batch, dim);
+        B, C (batch, N). Returns (y, h_new); the input h is not modified."""
+        h = _f64(h).copy()
+        x, delta, A, B, C = (_f64(v) for v in (x, delta, A, B, C))
+        D, z = _f64(D), _f64(z)
+        batch, dim, dstate = h.shape
+        assert x.shape == (batch, dim) and delta.shape == x.shape
+        assert A.shape == (dim, dstate) and B.shape == (batch, dstate) and C.shape == B.shape
+        y = np.zeros((batch, dim), dtype=np.float64)
+        rc = self.lib.oracle_state_update(batch, dim, dstate, _ptr(h), _ptr(x), _ptr(delta),
+                                          _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(y))
+        if rc != 0:
+            raise ValueError(f"oracle_state_update rejected its arguments (status {rc})")
+        return y, h
+
+
+def get():
+    """The shared oracle instance built from ``ssm_oracle.c``."""
+    global _LIB
+    if _LIB is None:
+        _LIB = Oracle()
+    return _LIB

@@ -1,0 +1,160 @@
+"""Seeded synthetic inputs for the selective-scan workloads.
+
+This module draws random tensors and nothing else: it holds none of the
+scan's arithmetic, and both the GPU library's tests and the CPU oracle take
+their inputs from it. Every tensor comes from a seeded torch generator, on the
+device the caller names, with the shape, dtype and distribution of one
+workload. The shapes are the layer shapes of the page "Mamba and State Space
+Models" (world.lapla.si): 5,120 channels of 16 states for Mamba-2.8B, 64
+layers (section "A State of Fixed Size"), A running from -1 to -16 (section
+"Every Step the Same"), 2,048-token training context (section "What It Does
+Not Say") and million-token sequences (section "Remembering Selectively").
+
+Recipe shared by every workload:
+  - A (dim, N) fp32: "logunif" draws A = -exp(U(-1, 1)); "s4d_real" sets
+    A[d, n] = -(n + 1) for every channel.
+  - D (dim,) fp32 ~ N(0, 1).
+  - delta = softplus(N(0, 1) * delta_std + delta_shift), computed in fp32 and
+    then rounded to the I/O dtype (round to nearest even).
+  - x, z, B, C ~ N(0, 1), drawn in fp32 and rounded to the I/O dtype.
+  - h0: None (zero state) or N(0, 1) fp32.
+Draw order: A, D, x, delta, z, B, C, h0.
+"""
+from dataclasses import dataclass, field
+
+import torch
+
+__all__ = ["Workload", "WORKLOADS", "generate_scan", "generate_decode_layer",
+           "io_torch_dtype"]
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    kind: str            # "scan" or "decode"
+    batch: int
+    seqlen: int          # tokens per sequence (1 for decode)
+    dim: int             # channels D
+    dstate: int          # states per channel N
+    io: str              # "f32" or "bf16": dtype of x, delta, z, B, C, y
+    a_init: str          # "logunif" or "s4d_real"
+    delta_shift: float
+    delta_std: float
+    h0: str              # "zero" or "normal"
+    seed: int
+    layers: int = 1      # decode only: independent layers per step
+    note: str = field(default="", compare=False)
+
+    @property
+    def elements(self):
+        """Scan elements B*L*D (decode: per step over all layers)."""
+        return self.batch * self.seqlen * self.dim * self.layers
+
+
+WORKLOADS = {
+    "tiny_f32": Workload(
+        "tiny_f32", "scan", 1, 64, 16, 4, "f32", "logunif", -2.0, 1.0, "zero", 0,
+        note="tiny fp32 scan the oracle checks in milliseconds"),
+    "mamba130m_layer": Workload(
+        "mamba130m_layer", "scan", 8, 2048, 1536, 16, "bf16", "logunif", -4.0, 1.0, "zero", 1,
+        note="Mamba-130M-shaped layer scan"),
+    "mamba28b_layer": Workload(
+        "mamba28b_layer", "scan", 8, 2048, 5120, 16, "bf16", "s4d_real", -4.0, 0.5, "zero", 2,
+        note="Mamba-2.8B-shaped layer scan"),
+    "million_length": Workload(
+        "million_length", "scan", 1, 1 << 20, 2048, 16, "bf16", "s4d_real", -4.0, 0.5, "zero", 3,
+        note="million-token scan at batch 1"),
+    "decode_64layer": Workload(
+        "decode_64layer", "decode", 256, 1, 5120, 16, "bf16", "s4d_real", -4.0, 0.5, "normal", 4,
+        layers=64, note="single-token state update, batch 256, 64 layers of D=5120"),
+}
+
+
+def io_torch_dtype(io):
+    return {"f32": torch.float32, "bf16": torch.bfloat16}[io]
+
+
+def _gen(seed, device):
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return g
+
+
+def _normal(shape, g, device, dtype, mean=0.0, std=1.0, chunk=1 << 27):
+    """N(mean, std) drawn in fp32 and rounded to `dtype`, in slabs along dim 0
+    so very large tensors never need a full fp32 temporary."""
+    out = torch.empty(shape, dtype=dtype, device=device)
+    flat = out.view(-1)
+    n = flat.numel()
+    for s in range(0, n, chunk):
+        e = min(n, s + chunk)
+        v = torch.randn(e - s, generator=g, device=device, dtype=torch.float32)
+        if std != 1.0:
+            v.mul_(std)
+        if mean != 0.0:
+            v.add_(mean)
+        flat[s:e] = v.to(dtype)
+    return out
+
+
+def _softplus_normal(shape, g, device, dtype, mean, std, chunk=1 << 27):
+    out = torch.empty(shape, dtype=dtype, device=device)
+    flat = out.view(-1)
+    n = flat.numel()
+    for s in range(0, n, chunk):
+        e = min(n, s + chunk)
+        v = torch.randn(e - s, generator=g, device=device, dtype=torch.float32)
+        v = torch.nn.functional.softplus(v * std + mean)
+        flat[s:e] = v.to(dtype)
+    return out
+
+
+def _a_matrix(w, g, device, dim=None):
+    dim = w.dim if dim is None else dim
+    if w.a_init == "s4d_real":
+        row = -torch.arange(1, w.dstate + 1, dtype=torch.float32, device=device)
+        return row.expand(dim, w.dstate).contiguous()
+    if w.a_init == "logunif":
+        u = torch.rand(dim, w.dstate, generator=g, device=device, dtype=torch.float32)
+        return -torch.exp(u * 2.0 - 1.0)
+    raise ValueError(w.a_init)
+
+
+def generate_scan(w, device="cpu", batch=None, seqlen=None, dim=None, seed=None):
+    """Inputs for one scan call of workload `w` (sizes may be overridden for
+    small parity cases). Returns a dict with keys x, delta, A, B, C, D, z, h0."""
+    batch = w.batch if batch is None else batch
+    seqlen = w.seqlen if seqlen is None else seqlen
+    dim = w.dim if dim is None else dim
+    seed = w.seed if seed is None else seed
+    dt = io_torch_dtype(w.io)
+    g = _gen(seed, device)
+    A = _a_matrix(w, g, device, dim)
+    D = torch.randn(dim, generator=g, device=device, dtype=torch.float32)
+    x = _normal((batch, seqlen, dim), g, device, dt)
+    delta = _softplus_normal((batch, seqlen, dim), g, device, dt, w.delta_shift, w.delta_std)
+    z = _normal((batch, seqlen, dim), g, device, dt)
+    B = _normal((batch, seqlen, w.dstate), g, device, dt)
+    C = _normal((batch, seqlen, w.dstate), g, device, dt)
+    h0 = None
+    if w.h0 == "normal":
+        h0 = torch.randn(batch, dim, w.dstate, generator=g, device=device, dtype=torch.float32)
+    return dict(x=x, delta=delta, A=A, B=B, C=C, D=D, z=z, h0=h0)
+
+
+def generate_decode_layer(w, layer, device="cpu", batch=None, dim=None):
+    """Inputs of one layer of a decode step: h (batch, dim, N) fp32 state and
+    one token of x, delta, z (batch, dim) and B, C (batch, N)."""
+    batch = w.batch if batch is None else batch
+    dim = w.dim if dim is None else dim
+    dt = io_torch_dtype(w.io)
+    g = _gen(w.seed * 1000003 + layer, device)
+    A = _a_matrix(w, g, device, dim)
+    D = torch.randn(dim, generator=g, device=device, dtype=torch.float32)
+    x = _normal((batch, dim), g, device, dt)
+    delta = _softplus_normal((batch, dim), g, device, dt, w.delta_shift, w.delta_std)
+    z = _normal((batch, dim), g, device, dt)
+    B = _normal((batch, w.dstate), g, device, dt)
+    C = _normal((batch, w.dstate), g, device, dt)
+    h = torch.randn(batch, dim, w.dstate, generator=g, device=device, dtype=torch.float32)
+    return dict(h=h, x=x, delta=delta, A=A, B=B, C=C, D=D, z=z)

@@ -1,0 +1,249 @@
+"""Pins of the fp64 oracle against facts that do not come from the oracle.
+
+Each pin takes an oracle handle (``oracle.Oracle``) and raises AssertionError
+when it disagrees with an independent statement of the result:
+
+- pin_lti_convolution: with Delta, B and C constant over time the scan is a
+  convolution of x with one fixed kernel K_k = sum_n C_n Abar_n^k Delta B_n
+  (page "Mamba and State Space Models", section "Every Step the Same"),
+  evaluated with numpy's convolve, plus the closed-form decay of h0.
+- pin_brute_force: for sequences of at most 8 tokens, the unrolled solution
+  h_t = exp(A*S_(0..t)) h0 + sum_s exp(A*(S_t - S_s)) Delta_s B_s x_s,
+  with S the running sum of Delta (section "A State of Fixed Size" unrolled).
+- pin_chunk_split: scanning [0, L) equals scanning [0, m) and then [m, L)
+  from the carried state, bit for bit (the state is the whole memory,
+  section "A State of Fixed Size").
+- pin_theorem1: with one state, A = -1, B = C = 1 and Delta = softplus(u),
+  zero-order hold gives exactly the gated recurrence h <- (1-g)h + g*x with
+  g = sigmoid(u) (section "Chosen by the Token", the paper's Theorem 1); the
+  first-order form gives h <- (1-g)h + softplus(u)*x.
+- pin_ssd_matrix: for A a scalar per channel, the whole sequence map is one
+  lower-triangular matrix with entry (i, j) = (C_i . B_j) times the decay
+  from j to i (section "Mamba-2: Two Algorithms"), applied with a numpy
+  matmul to Delta*x.
+- pin_limits: Delta -> 0 keeps the state; a large Delta resets it to
+  Delta*B*x; x = 0 leaves pure decay (section "Chosen by the Token").
+- pin_structure: linearity in x, superposition of x and h0, the exact skip
+  contribution D*x*silu(z), channel permutation and batch independence.
+- pin_decode: the single-token update equals the scan over one token, and
+  T updates equal the scan over T tokens (section "Taken Apart").
+
+silu(z) = z * sigmoid(z) is evaluated with scipy's logistic function.
+"""
+import numpy as np
+from scipy.special import expit
+
+RTOL = 1e-12
+
+
+def _silu(z):
+    return z * expit(z)
+
+
+def _close(got, want, rtol=RTOL, what=""):
+    got = np.asarray(got)
+    want = np.asarray(want)
+    assert got.shape == want.shape, f"{what}: shape {got.shape} != {want.shape}"
+    scale = max(1.0, float(np.max(np.abs(want))))
+    err = float(np.max(np.abs(got - want))) if want.size else 0.0
+    assert err <= rtol * scale, f"{what}: max abs error {err:.3e} > {rtol:.1e} * {scale:.3e}"
+
+
+def _rand_inputs(rng, batch, seqlen, dim, dstate, h0=True):
+    x = rng.standard_normal((batch, seqlen, dim))
+    delta = np.log1p(np.exp(rng.standard_normal((batch, seqlen, dim)) - 1.0))
+    A = -np.exp(rng.uniform(-1.0, 1.0, (dim, dstate)))
+    B = rng.standard_normal((batch, seqlen, dstate))
+    C = rng.standard_normal((batch, seqlen, dstate))
+    D = rng.standard_normal(dim)
+    z = rng.standard_normal((batch, seqlen, dim))
+    h = rng.standard_normal((batch, dim, dstate)) if h0 else None
+    return dict(x=x, delta=delta, A=A, B=B, C=C, D=D, z=z, h0=h)
+
+
+def pin_lti_convolution(orc, seed=11):
+    rng = np.random.default_rng(seed)
+    batch, L, dim, N = 2, 48, 5, 3
+    dconst = 0.05 + rng.uniform(0.0, 0.6, dim)           # one Delta per channel
+    A = -np.exp(rng.uniform(-1.0, 1.0, (dim, N)))
+    Bc = rng.standard_normal((batch, N))                  # one B, one C per batch
+    Cc = rng.standard_normal((batch, N))
+    x = rng.standard_normal((batch, L, dim))
+    z = rng.standard_normal((batch, L, dim))
+    D = rng.standard_normal(dim)
+    h0 = rng.standard_normal((batch, dim, N))
+    delta = np.broadcast_to(dconst, (batch, L, dim)).copy()
+    B = np.broadcast_to(Bc[:, None, :], (batch, L, N)).copy()
+    C = np.broadcast_to(Cc[:, None, :], (batch, L, N)).copy()
+    y, hL = orc.scan_fwd(x, delta, A, B, C, D=D, z=z, h0=h0)
+
+    k = np.arange(L)
+    want_y = np.empty((batch, L, dim))
+    want_h = np.empty((batch, dim, N))
+    for b in range(batch):
+        for d in range(dim):
+            powers = np.exp(np.outer(k, dconst[d] * A[d]))          # Abar^k, (L, N)
+            kernel = powers @ (Cc[b] * dconst[d] * Bc[b])           # K_k
+            conv = np.convolve(x[b, :, d], kernel)[:L]
+            init = np.exp(np.outer(k + 1, dconst[d] * A[d])) @ (Cc[b] * h0[b, d])
+            pre = conv + init + D[d] * x[b, :, d]
+            want_y[b, :, d] = pre * _silu(z[b, :, d])
+            rev = x[b, ::-1, d]                                       # x_{L-1-k}
+            want_h[b, d] = (powers * (dconst[d] * Bc[b])).T @ rev + np.exp(L * dconst[d] * A[d]) * h0[b, d]
+    _close(y, want_y, what="LTI y")
+    _close(hL, want_h, what="LTI hL")
+
+
+def pin_brute_force(orc, seed=12):
+    rng = np.random.default_rng(seed)
+    for L in range(1, 9):
+        inp = _rand_inputs(rng, 2, L, 3, 4)
+        x, dl, A, B, C, D, z, h0 = (inp[k] for k in ("x", "delta", "A", "B", "C", "D", "z", "h0"))
+        y, hL = orc.scan_fwd(**inp)
+        want = np.empty_like(y)
+        want_h = np.empty_like(hL)
+        for b in range(2):
+            for d in range(3):
+                S = np.cumsum(dl[b, :, d])
+                for t in range(L):
+                    h = np.exp(A[d] * S[t]) * h0[b, d]
+                    for s in range(t + 1):
+                        h = h + np.exp(A[d] * (S[t] - S[s])) * dl[b, s, d] * B[b, s] * x[b, s, d]
+                    pre = float(np.dot(C[b, t], h)) + D[d] * x[b, t, d]
+                    want[b, t, d] = pre * _silu(z[b, t, d])
+                    if t == L - 1:
+                        want_h[b, d] = h
+        _close(y, want, rtol=1e-11, what=f"brute force y, L={L}")
+        _close(hL, want_h, rtol=1e-11, what=f"brute force hL, L={L}")
+
+
+def pin_chunk_split(orc, seed=13):
+    rng = np.random.default_rng(seed)
+    inp = _rand_inputs(rng, 3, 37, 4, 5)
+    y, hL = orc.scan_fwd(**inp)
+    for m in (0, 1, 7, 20, 36, 37):
+        first = {k: (v[:, :m] if k in ("x", "delta", "B", "C", "z") else v) for k, v in inp.items()}
+        second = {k: (v[:, m:] if k in ("x", "delta", "B", "C", "z") else v) for k, v in inp.items()}
+        y1, h1 = orc.scan_fwd(**first)
+        second["h0"] = h1
+        y2, h2 = orc.scan_fwd(**second)
+        assert np.array_equal(np.concatenate([y1, y2], axis=1), y), f"split at {m}: y differs"
+        assert np.array_equal(h2, hL), f"split at {m}: hL differs"
+
+
+def pin_theorem1(orc, seed=14):
+    rng = np.random.default_rng(seed)
+    batch, L, dim = 2, 30, 3
+    u = 2.0 * rng.standard_normal((batch, L, dim))
+    x = rng.standard_normal((batch, L, dim))
+    delta = np.logaddexp(0.0, u)                  # softplus(u)
+    A = -np.ones((dim, 1))
+    ones = np.ones((batch, L, 1))
+    h0 = rng.standard_normal((batch, dim, 1))
+    for zoh in (True, False):
+        y, hL = orc.scan_fwd(x, delta, A, ones, ones, h0=h0, zoh=zoh)
+        want = np.empty_like(y)
+        for b in range(batch):
+            for d in range(dim):
+                h = h0[b, d, 0]
+                for t in range(L):
+                    g = expit(u[b, t, d])
+                    write = g if zoh else delta[b, t, d]
+                    h = (1.0 - g) * h + write * x[b, t, d]
+                    want[b, t, d] = h
+        _close(y, want, what=f"Theorem 1 gate (zoh={zoh})")
+        _close(hL[:, :, 0], want[:, -1, :], what=f"Theorem 1 state (zoh={zoh})")
+
+
+def pin_ssd_matrix(orc, seed=15):
+    rng = np.random.default_rng(seed)
+    batch, L, dim, N = 2, 33, 4, 6
+    inp = _rand_inputs(rng, batch, L, dim, N, h0=False)
+    a = -np.exp(rng.uniform(-1.0, 1.0, dim))
+    inp["A"] = np.repeat(a[:, None], N, axis=1)
+    y, hL = orc.scan_fwd(**inp)
+    x, dl, B, C, D, z = (inp[k] for k in ("x", "delta", "B", "C", "D", "z"))
+    mask = np.tril(np.ones((L, L), dtype=bool))
+    for b in range(batch):
+        for d in range(dim):
+            S = np.cumsum(dl[b, :, d])
+            gap = np.where(mask, S[:, None] - S[None, :], 0.0)
+            M = (C[b] @ B[b].T) * np.exp(a[d] * gap) * mask
+            v = dl[b, :, d] * x[b, :, d]
+            pre = M @ v + D[d] * x[b, :, d]
+            _close(y[b, :, d], pre * _silu(z[b, :, d]), what="SSD matrix form y")
+            decay = np.exp(a[d] * (S[-1] - S))
+            _close(hL[b, d], B[b].T @ (decay * v), what="SSD matrix form hL")
+
+
+def pin_limits(orc, seed=16):
+    rng = np.random.default_rng(seed)
+    inp = _rand_inputs(rng, 2, 12, 3, 4)
+    x, B, C, D, z, h0 = (inp[k] for k in ("x", "B", "C", "D", "z", "h0"))
+    # Delta -> 0: the state is kept, y = C.h0 + D x
+    tiny = dict(inp, delta=np.full_like(x, 1e-14))
+    y, hL = orc.scan_fwd(**tiny)
+    want = (np.einsum("btn,bdn->btd", C, h0) + D * x) * _silu(z)
+    _close(y, want, rtol=1e-10, what="Delta -> 0 keeps the state")
+    _close(hL, h0, rtol=1e-10, what="Delta -> 0 final state")
+    # large Delta with A <= -1: h_t = Delta * B_t * x_t (reset to the current token)
+    big = dict(inp, delta=np.full_like(x, 60.0), A=-1.0 - rng.uniform(0, 1, inp["A"].shape))
+    y, hL = orc.scan_fwd(**big)
+    want = (60.0 * np.einsum("btn,btn->bt", C, B)[:, :, None] * x + D * x) * _silu(z)
+    _close(y, want, rtol=1e-10, what="large Delta resets the state")
+    # x = 0: pure decay of h0
+    zero = dict(inp, x=np.zeros_like(x))
+    y, hL = orc.scan_fwd(**zero)
+    S = np.cumsum(inp["delta"], axis=1)                                   # (b, t, d)
+    h = np.exp(S[:, :, :, None] * inp["A"][None, None]) * h0[:, None]     # (b, t, d, n)
+    _close(y, np.einsum("btn,btdn->btd", C, h) * _silu(z), what="x = 0 decays h0")
+    _close(hL, h[:, -1], what="x = 0 final state")
+
+
+def pin_structure(orc, seed=17):
+    rng = np.random.default_rng(seed)
+    inp = _rand_inputs(rng, 3, 25, 6, 5)
+    x2 = rng.standard_normal(inp["x"].shape)
+    nozero = dict(inp, h0=None)
+    y1, h1 = orc.scan_fwd(**nozero)
+    y2, h2 = orc.scan_fwd(**dict(nozero, x=x2))
+    y12, h12 = orc.scan_fwd(**dict(nozero, x=2.0 * inp["x"] - 3.0 * x2))
+    _close(y12, 2.0 * y1 - 3.0 * y2, what="linearity in x")
+    _close(h12, 2.0 * h1 - 3.0 * h2, what="linearity in x (state)")
+    # superposition of input and initial state
+    y, hL = orc.scan_fwd(**inp)
+    y0, s0 = orc.scan_fwd(**dict(inp, x=np.zeros_like(inp["x"])))
+    _close(y, y1 + y0, what="superposition of x and h0")
+    _close(hL, h1 + s0, what="superposition of x and h0 (state)")
+    # the skip term contributes exactly D * x * silu(z)
+    ynd, _ = orc.scan_fwd(**dict(inp, D=None))
+    _close(y - ynd, inp["D"] * inp["x"] * _silu(inp["z"]), what="skip term")
+    # no gate: y is the ungated readout, and gating multiplies by silu(z)
+    yng, _ = orc.scan_fwd(**dict(inp, z=None))
+    _close(y, yng * _silu(inp["z"]), what="gate")
+    # channels are independent: permuting them permutes the outputs
+    p = rng.permutation(inp["x"].shape[2])
+    perm = dict(inp, x=inp["x"][:, :, p], delta=inp["delta"][:, :, p], z=inp["z"][:, :, p],
+                A=inp["A"][p], D=inp["D"][p], h0=inp["h0"][:, p])
+    yp, hp = orc.scan_fwd(**perm)
+    assert np.array_equal(yp, y[:, :, p]) and np.array_equal(hp, hL[:, p]), "channel permutation"
+    # batches are independent
+    yb, hb = orc.scan_fwd(**{k: (v[1:2] if k in ("x", "delta", "B", "C", "z", "h0") else v)
+                             for k, v in inp.items()})
+    assert np.array_equal(yb, y[1:2]) and np.array_equal(hb, hL[1:2]), "batch independence"
+
+
+def pin_decode(orc, seed=18):
+    rng = np.random.default_rng(seed)
+    inp = _rand_inputs(rng, 3, 6, 5, 4)
+    y, hL = orc.scan_fwd(**inp)
+    h = inp["h0"].copy()
+    for t in range(6):
+        yt, h = orc.state_update(h, inp["x"][:, t], inp["delta"][:, t], inp["A"],
+                                 inp["B"][:, t], inp["C"][:, t], D=inp["D"], z=inp["z"][:, t])
+        assert np.array_equal(yt, y[:, t]), f"decode step {t} differs from the scan"
+    assert np.array_equal(h, hL), "decode state after T steps differs from the scan"
+
+
+ALL_PINS = [pin_lti_convolution, pin_brute_force, pin_chunk_split, pin_theorem1,
+            pin_ssd_matrix, pin_limits, pin_structure, pin_decode]

@@ -1,0 +1,63 @@
+"""Planted mistakes in the oracle must be caught by its pins.
+
+Each mutant rewrites one spot of oracle/ssm_oracle.c (a dropped term, a wrong
+sign, a wrong or transposed index, a swapped operand), compiles the result
+into a temporary library on the CPU and runs every pin against it: at least
+one pin must fail. The real oracle source is never modified.
+"""
+import os
+
+import pytest
+
+import oracle
+import oracle_pins
+from oracle import build as oracle_build
+
+MUTANTS = {
+    "decay sign flipped": ("exp(dt * a)", "exp(-dt * a)"),
+    "delta dropped from Bbar": (": dt * Bm[i_bc + n];", ": Bm[i_bc + n];"),
+    "decay of h dropped": ("Abar * h[n] + Bbar * u", "h[n] + Bbar * u"),
+    "readout uses B": ("out += Cm[i_bc + n] * h[n];", "out += Bm[i_bc + n] * h[n];"),
+    "A transposed": ("const double a = A[d * dstate + n];", "const double a = A[n * dim + d];"),
+    "skip term dropped": ("if (Dskip) out += Dskip[d] * u;", ""),
+    "gate sign flipped": ("out *= zz / (1.0 + exp(-zz));", "out *= zz / (1.0 + exp(zz));"),
+    "h0 ignored": ("h[n] = h0 ? h0[(b * dim + d) * dstate + n] : 0.0;", "h[n] = 0.0;"),
+    "readout before update": (
+        "h[n] = Abar * h[n] + Bbar * u;\n                    out += Cm[i_bc + n] * h[n];",
+        "out += Cm[i_bc + n] * h[n];\n                    h[n] = Abar * h[n] + Bbar * u;"),
+    "B, C from the previous token": ("const int64_t i_bc = (b * seqlen + t) * dstate;",
+                                     "const int64_t i_bc = (b * seqlen + (t > 0 ? t - 1 : 0)) * dstate;"),
+    "B, C ignore the batch": ("const int64_t i_bc = (b * seqlen + t) * dstate;",
+                              "const int64_t i_bc = t * dstate;"),
+    "x from the previous token": ("const double u = x[i_tok];",
+                                  "const double u = x[i_tok - (t > 0 ? dim : 0)];"),
+    "x and delta swapped": ("const double dt = delta[i_tok];\n                const double u = x[i_tok];",
+                            "const double dt = x[i_tok];\n                const double u = delta[i_tok];"),
+    "final state scaled": ("hL[(b * dim + d) * dstate + n] = h[n];",
+                           "hL[(b * dim + d) * dstate + n] = 0.5 * h[n];"),
+    "zero-order hold sign": ("(Abar - 1.0) / a", "(1.0 - Abar) / a"),
+    "skip uses the wrong channel": ("out += Dskip[d] * u;", "out += Dskip[dim - 1 - d] * u;"),
+}
+
+
+@pytest.fixture(scope="module")
+def source():
+    with open(oracle_build.SOURCE) as f:
+        return f.read()
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, source, tmp_path):
+    old, new = MUTANTS[name]
+    assert source.count(old) == 1, f"mutation site for '{name}' not unique in the oracle source"
+    src = tmp_path / "mutant.c"
+    src.write_text(source.replace(old, new))
+    lib = oracle_build.compile_oracle(str(src), str(tmp_path / "libmutant.so"))
+    mutant = oracle.Oracle(lib)
+    failed = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(mutant)
+        except AssertionError as e:
+            failed.append((pin.__name__, str(e)[:80]))
+    assert failed, f"no pin caught the planted mistake '{name}'"
