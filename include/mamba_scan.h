@@ -1,0 +1,131 @@
+/*
+ * mamba_scan.h: C ABI of the selective state-space scan for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The operation (page "Mamba and State Space Models", world.lapla.si):
+ * for every batch row b, channel d and state n, with A[d,n] < 0,
+ *
+ *     Abar = exp(delta[b,t,d] * A[d,n])                 ("Chosen by the Token")
+ *     h[n] <- Abar * h[n] + delta[b,t,d] * B[b,t,n] * x[b,t,d]
+ *                                                       ("A State of Fixed Size")
+ *     y[b,t,d] = (sum_n C[b,t,n] * h[n] + D[d] * x[b,t,d]) * silu(z[b,t,d])
+ *
+ * with silu(z) = z / (1 + exp(-z)). The output of token t reads the state
+ * after token t has been absorbed. The input discretisation is the
+ * first-order form Bbar = delta * B; the skip term D*x and the silu gate are
+ * optional. Delta, B and C arrive already computed per token (section
+ * "Chosen by the Token"); delta must be positive (not checked).
+ *
+ * Layout: every tensor is dense and row-major.
+ *     x, delta, z, y   (batch, seqlen, dim)      dim contiguous, I/O dtype
+ *     B, C             (batch, seqlen, dstate)   I/O dtype, shared by all channels
+ *     A                (dim, dstate)             fp32
+ *     D                (dim)                     fp32
+ *     h0, hL, h        (batch, dim, dstate)      fp32
+ * The I/O dtype (MAMBA_DTYPE_F32 or MAMBA_DTYPE_BF16) applies to x, delta,
+ * z, B, C and y. The state is always fp32 and all arithmetic is fp32.
+ *
+ * Ownership and threading: all pointers are device pointers on the current
+ * HIP device, owned by the caller. The library keeps no pointer after a call
+ * returns and allocates no device memory; ssm_scan_fwd takes its scratch
+ * space from the caller's workspace. Work is queued on `stream` (0 = the
+ * null stream) and the call returns before it finishes, so buffers must
+ * outlive the queued work. Calls on different streams do not share state.
+ *
+ * Errors: shape, dtype, null-pointer, alignment and workspace checks run on
+ * the host before any HIP call and return a negative mamba_status; nothing
+ * is queued then. A failed launch returns MAMBA_ERR_HIP. The library never
+ * prints or aborts. Every pointer must be 16-byte aligned.
+ */
+#ifndef MAMBA_SCAN_H
+#define MAMBA_SCAN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Largest supported number of states per channel (the pages' default is 16). */
+#define MAMBA_SCAN_MAX_DSTATE 16
+
+typedef enum mamba_status {
+    MAMBA_OK = 0,
+    MAMBA_ERR_INVALID_ARG = -1,   /* negative size, NULL required pointer, bad dtype */
+    MAMBA_ERR_UNSUPPORTED = -2,   /* dstate outside 1..MAMBA_SCAN_MAX_DSTATE, sizes too large */
+    MAMBA_ERR_MISALIGNED = -3,    /* a pointer is not 16-byte aligned */
+    MAMBA_ERR_WORKSPACE = -4,     /* workspace NULL or smaller than required */
+    MAMBA_ERR_HIP = -5            /* the HIP runtime reported an error */
+} mamba_status;
+
+typedef enum mamba_dtype {
+    MAMBA_DTYPE_F32 = 0,
+    MAMBA_DTYPE_BF16 = 1
+} mamba_dtype;
+
+/*
+ * Scratch bytes ssm_scan_fwd needs for this shape and chunk length.
+ *
+ * chunk_len: tokens per parallel chunk. The scan splits each sequence into
+ * chunks that run in parallel and joins them with an associative combine of
+ * the per-chunk (decay product, end state) pairs (the "parallel scan" of
+ * section "A Scan on the Chip"). 0 lets the library choose from the shape and
+ * the current device's compute-unit count; a positive value forces that
+ * length (results agree within rounding for any choice).
+ * Writes the size to *bytes (0 when the plan needs no scratch). May query the
+ * current device (a HIP call) when chunk_len is 0.
+ */
+int ssm_scan_fwd_workspace_size(int64_t batch, int64_t seqlen, int64_t dim, int dstate,
+                                int dtype, int64_t chunk_len, size_t* bytes);
+
+/*
+ * Selective scan over whole sequences (prefill).
+ *
+ * x, delta   (batch, seqlen, dim)     required
+ * A          (dim, dstate) fp32       required, A < 0 (not checked)
+ * B, C       (batch, seqlen, dstate)  required
+ * D          (dim) fp32               optional (NULL: no skip term)
+ * z          (batch, seqlen, dim)     optional (NULL: no gate)
+ * h0         (batch, dim, dstate)     optional (NULL: zero initial state)
+ * y          (batch, seqlen, dim)     written
+ * hL         (batch, dim, dstate)     optional, written with the state after
+ *                                     the last token; may alias h0
+ * workspace  at least ssm_scan_fwd_workspace_size(..., chunk_len) bytes, may
+ *            be NULL when that size is 0; its contents need no initialisation
+ * seqlen == 0 writes hL = h0 (or zeros) and no y; batch == 0 or dim == 0 is
+ * a no-op. y must not overlap any input.
+ */
+int ssm_scan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int dstate, int dtype,
+                 const void* x, const void* delta, const float* A,
+                 const void* B, const void* C, const float* D, const void* z,
+                 const float* h0, void* y, float* hL,
+                 int64_t chunk_len, void* workspace, size_t workspace_bytes,
+                 hipStream_t stream);
+
+/*
+ * Single-token decode update (section "Taken Apart": one token moves the
+ * state once). Equivalent to ssm_scan_fwd with seqlen = 1 and h0 = hL = h.
+ *
+ * h          (batch, dim, dstate) fp32, read and updated in place
+ * x, delta   (batch, dim)            required
+ * A          (dim, dstate) fp32      required
+ * B, C       (batch, dstate)         required
+ * D          (dim) fp32              optional
+ * z          (batch, dim)            optional
+ * y          (batch, dim)            written
+ */
+int ssm_state_update(int64_t batch, int64_t dim, int dstate, int dtype, float* h,
+                     const void* x, const void* delta, const float* A,
+                     const void* B, const void* C, const float* D, const void* z,
+                     void* y, hipStream_t stream);
+
+/* Static, human-readable name of a mamba_status value. */
+const char* mamba_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MAMBA_SCAN_H */

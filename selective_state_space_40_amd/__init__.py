@@ -1,0 +1,181 @@
+"""Selective state-space scan for AMD Instinct MI355X (gfx950).
+
+Python binding of the C ABI in include/mamba_scan.h. It only marshals
+arguments: it checks shapes and dtypes, allocates outputs and scratch with
+torch on the tensors' device, and passes raw device pointers and the current
+HIP stream to libmamba_scan.so, whose kernels do every step of the scan.
+There is no other code path: without the built library every call raises.
+
+    y, hL = scan_fwd(x, delta, A, B, C, D=None, z=None, h0=None)
+    y = state_update(h, x, delta, A, B, C, D=None, z=None)    # h updated in place
+
+Shapes (row-major, contiguous): x, delta, z, y (batch, L, dim); B, C
+(batch, L, N); A (dim, N) fp32; D (dim,) fp32; h0, hL (batch, dim, N) fp32.
+x, delta, z, B and C share one dtype, float32 or bfloat16, and y has it too.
+"""
+import ctypes
+import os
+
+import torch
+
+__all__ = ["scan_fwd", "state_update", "workspace_size", "library_path", "load_library",
+           "MambaScanError", "MAX_DSTATE"]
+
+MAX_DSTATE = 16
+_DTYPES = {torch.float32: 0, torch.bfloat16: 1}
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+_WS = {}
+
+
+class MambaScanError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(msg)
+        self.status = status
+
+
+def library_path():
+    return os.environ.get("MAMBA_SCAN_LIB", os.path.join(_HERE, "libmamba_scan.so"))
+
+
+def load_library():
+    """Load libmamba_scan.so (built in-tree by __graft_entry__.build())."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = library_path()
+    if not os.path.exists(path):
+        raise MambaScanError(-5, f"HIP library not built: {path} is missing "
+                                 "(run __graft_entry__.build())")
+    lib = ctypes.CDLL(path)
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.ssm_scan_fwd_workspace_size.argtypes = [i64, i64, i64, i32, i32, i64,
+                                                ctypes.POINTER(ctypes.c_size_t)]
+    lib.ssm_scan_fwd_workspace_size.restype = i32
+    lib.ssm_scan_fwd.argtypes = [i64, i64, i64, i32, i32] + [vp] * 10 + [i64, vp, ctypes.c_size_t, vp]
+    lib.ssm_scan_fwd.restype = i32
+    lib.ssm_state_update.argtypes = [i64, i64, i32, i32] + [vp] * 9 + [vp]
+    lib.ssm_state_update.restype = i32
+    lib.mamba_status_string.argtypes = [i32]
+    lib.mamba_status_string.restype = ctypes.c_char_p
+    _LIB = lib
+    return lib
+
+
+def _check(status, what):
+    if status != 0:
+        msg = load_library().mamba_status_string(status).decode()
+        raise MambaScanError(status, f"{what}: {msg}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t, name, shape, dtype, device):
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def workspace_size(batch, seqlen, dim, dstate, dtype=torch.bfloat16, chunk_len=0):
+    """Scratch bytes ssm_scan_fwd needs (queries the current device when chunk_len == 0)."""
+    out = ctypes.c_size_t(0)
+    _check(load_library().ssm_scan_fwd_workspace_size(batch, seqlen, dim, dstate, _DTYPES[dtype],
+                                                      chunk_len, ctypes.byref(out)),
+           "ssm_scan_fwd_workspace_size")
+    return out.value
+
+
+def _workspace(device, nbytes):
+    if nbytes == 0:
+        return None
+    key = (device, torch.cuda.current_stream(device).cuda_stream)
+    buf = _WS.get(key)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        _WS[key] = buf
+    return buf
+
+
+def scan_fwd(x, delta, A, B, C, D=None, z=None, h0=None, *, chunk_len=0, return_state=True,
+             out=None, state_out=None):
+    """Selective scan over whole sequences; returns (y, hL) (hL is None when
+    return_state is False). `chunk_len` > 0 forces the parallel chunk length."""
+    lib = load_library()
+    if x.dim() != 3:
+        raise ValueError("x must be (batch, L, dim)")
+    batch, seqlen, dim = x.shape
+    if A.dim() != 2 or A.shape[0] != dim:
+        raise ValueError("A must be (dim, N)")
+    dstate = A.shape[1]
+    dev, dt = x.device, x.dtype
+    if dt not in _DTYPES:
+        raise ValueError(f"unsupported I/O dtype {dt}")
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU device")
+    _need(x, "x", (batch, seqlen, dim), dt, dev)
+    _need(delta, "delta", (batch, seqlen, dim), dt, dev)
+    _need(A, "A", (dim, dstate), torch.float32, dev)
+    _need(B, "B", (batch, seqlen, dstate), dt, dev)
+    _need(C, "C", (batch, seqlen, dstate), dt, dev)
+    _need(D, "D", (dim,), torch.float32, dev)
+    _need(z, "z", (batch, seqlen, dim), dt, dev)
+    _need(h0, "h0", (batch, dim, dstate), torch.float32, dev)
+    y = out if out is not None else torch.empty_like(x)
+    _need(y, "out", (batch, seqlen, dim), dt, dev)
+    hL = None
+    if return_state:
+        hL = state_out if state_out is not None else torch.empty(batch, dim, dstate,
+                                                                 dtype=torch.float32, device=dev)
+        _need(hL, "state_out", (batch, dim, dstate), torch.float32, dev)
+    with torch.cuda.device(dev):
+        nbytes = workspace_size(batch, seqlen, dim, dstate, dt, chunk_len)
+        ws = _workspace(dev, nbytes)
+        st = lib.ssm_scan_fwd(batch, seqlen, dim, dstate, _DTYPES[dt], _ptr(x), _ptr(delta),
+                              _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0), _ptr(y),
+                              _ptr(hL), chunk_len, _ptr(ws), nbytes, _stream(dev))
+    _check(st, "ssm_scan_fwd")
+    return y, hL
+
+
+def state_update(h, x, delta, A, B, C, D=None, z=None, *, out=None):
+    """One decode step: h (batch, dim, N) fp32 is updated in place; returns y (batch, dim)."""
+    lib = load_library()
+    if h.dim() != 3:
+        raise ValueError("h must be (batch, dim, N)")
+    batch, dim, dstate = h.shape
+    dev, dt = x.device, x.dtype
+    if dt not in _DTYPES:
+        raise ValueError(f"unsupported I/O dtype {dt}")
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU device")
+    _need(h, "h", (batch, dim, dstate), torch.float32, dev)
+    _need(x, "x", (batch, dim), dt, dev)
+    _need(delta, "delta", (batch, dim), dt, dev)
+    _need(A, "A", (dim, dstate), torch.float32, dev)
+    _need(B, "B", (batch, dstate), dt, dev)
+    _need(C, "C", (batch, dstate), dt, dev)
+    _need(D, "D", (dim,), torch.float32, dev)
+    _need(z, "z", (batch, dim), dt, dev)
+    y = out if out is not None else torch.empty_like(x)
+    _need(y, "out", (batch, dim), dt, dev)
+    with torch.cuda.device(dev):
+        st = lib.ssm_state_update(batch, dim, dstate, _DTYPES[dt], _ptr(h), _ptr(x), _ptr(delta),
+                                  _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(y),
+                                  _stream(dev))
+    _check(st, "ssm_state_update")
+    return y

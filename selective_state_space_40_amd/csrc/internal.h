@@ -1,0 +1,73 @@
+// Internal interface between the C ABI layer (api.cpp) and the HIP kernels
+// (scan_kernels.hip). Not installed; not part of the public ABI.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+namespace mamba {
+
+// Lanes of one wavefront on gfx950.
+constexpr int kWave = 64;
+// Channels covered by one workgroup of the scan kernels (one wave).
+constexpr int kScanChannelsPerGroup = kWave;
+// Tokens fetched per register tile; chunk lengths are multiples of it.
+constexpr int kTokenTile = 8;
+
+enum IoType : int { kIoF32 = 0, kIoBF16 = 1 };
+
+// How one ssm_scan_fwd call is split: the sequence is cut into `nchunks`
+// chunks of `chunk_len` tokens (the last one may be shorter).
+struct ScanPlan {
+    int64_t chunk_len = 0;
+    int64_t nchunks = 1;
+    size_t workspace_bytes = 0;  // 0 when nchunks == 1
+};
+
+struct ScanArgs {
+    int64_t batch, seqlen, dim;
+    int dstate;
+    int io;
+    const void* x;
+    const void* delta;
+    const float* A;
+    const void* B;
+    const void* C;
+    const float* D;
+    const void* z;
+    const float* h0;
+    void* y;
+    float* hL;
+};
+
+struct DecodeArgs {
+    int64_t batch, dim;
+    int dstate;
+    int io;
+    float* h;
+    const void* x;
+    const void* delta;
+    const float* A;
+    const void* B;
+    const void* C;
+    const float* D;
+    const void* z;
+    void* y;
+};
+
+// Workspace layout for nchunks > 1: three fp32 arrays of
+// nchunks * batch * dim * dstate elements each: the state entering each
+// chunk, each chunk's end state from a zero start, and each chunk's decay
+// product.
+size_t scan_workspace_bytes(int64_t batch, int64_t dim, int dstate, int64_t nchunks);
+
+// Queue the kernels of one planned scan on `stream`. Arguments are already
+// validated. Returns the HIP error of the last launch.
+hipError_t launch_scan(const ScanArgs& a, const ScanPlan& plan, void* workspace,
+                       hipStream_t stream);
+
+// Queue the single-token update. Arguments are already validated.
+hipError_t launch_state_update(const DecodeArgs& a, hipStream_t stream);
+
+}  // namespace mamba
