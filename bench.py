@@ -38,6 +38,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="mamba28b_layer")
     p.add_argument("--chunk-len", type=int, default=0, help="0 = the library's automatic plan")
+    p.add_argument("--state-split", type=int, default=0, help="0 = the library's automatic plan")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-channels", type=int, default=0,
                    help="channels of the CPU-baseline sample (0 = sized to ~10 s)")
@@ -94,7 +95,8 @@ def main():
     def step(i):
         inp = sets[i % 2]
         ms.scan_fwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"],
-                    inp["h0"], chunk_len=args.chunk_len, out=y, state_out=hL)
+                    inp["h0"], chunk_len=args.chunk_len, state_split=args.state_split, out=y,
+                    state_out=hL)
 
     for i in range(args.warmup):
         step(i)
@@ -114,10 +116,10 @@ def main():
     ms_per_step = ev0.elapsed_time(ev1) / args.steps
 
     # the plan the library chose, for the record
-    lib = ms.load_library()
-    nbytes = ms.workspace_size(w.batch, w.seqlen, w.dim, w.dstate, W.io_torch_dtype(w.io),
-                               args.chunk_len)
-    nchunks = nbytes // (3 * w.batch * w.dim * w.dstate * 4) if nbytes else 1
+    chunk_len, split, _ = ms.resolve_plan(w.batch, w.seqlen, w.dim, w.dstate,
+                                          W.io_torch_dtype(w.io), args.chunk_len,
+                                          args.state_split)
+    nchunks = -(-w.seqlen // chunk_len)
 
     elems = w.batch * w.seqlen * w.dim
     sec = ms_per_step / 1e3
@@ -163,8 +165,9 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "seqlen": w.seqlen, "dim": w.dim,
-                   "dstate": w.dstate, "io_dtype": w.io, "chunk_len": args.chunk_len,
-                   "nchunks": int(nchunks), "parallelism": "single GPU"},
+                   "dstate": w.dstate, "io_dtype": w.io, "chunk_len": int(chunk_len),
+                   "nchunks": int(nchunks), "state_split": int(split),
+                   "parallelism": "single GPU"},
         "achieved_GBps": round(gbps, 1),
         "wall_s": round(wall, 4),
         "roofline": roofline,

@@ -54,7 +54,8 @@ extern "C" {
 typedef enum mamba_status {
     MAMBA_OK = 0,
     MAMBA_ERR_INVALID_ARG = -1,   /* negative size, NULL required pointer, bad dtype */
-    MAMBA_ERR_UNSUPPORTED = -2,   /* dstate outside 1..MAMBA_SCAN_MAX_DSTATE, sizes too large */
+    MAMBA_ERR_UNSUPPORTED = -2,   /* dstate outside 1..MAMBA_SCAN_MAX_DSTATE, sizes too large,
+                                     a state split the kernels do not provide */
     MAMBA_ERR_MISALIGNED = -3,    /* a pointer is not 16-byte aligned */
     MAMBA_ERR_WORKSPACE = -4,     /* workspace NULL or smaller than required */
     MAMBA_ERR_HIP = -5            /* the HIP runtime reported an error */
@@ -66,19 +67,42 @@ typedef enum mamba_dtype {
 } mamba_dtype;
 
 /*
- * Scratch bytes ssm_scan_fwd needs for this shape and chunk length.
+ * How ssm_scan_fwd divides its work over the GPU. A NULL plan, or a zero
+ * field, lets the library choose from the shape and the current device's
+ * compute-unit count; every choice gives the same result up to rounding.
  *
- * chunk_len: tokens per parallel chunk. The scan splits each sequence into
- * chunks that run in parallel and joins them with an associative combine of
- * the per-chunk (decay product, end state) pairs (the "parallel scan" of
- * section "A Scan on the Chip"). 0 lets the library choose from the shape and
- * the current device's compute-unit count; a positive value forces that
- * length (results agree within rounding for any choice).
- * Writes the size to *bytes (0 when the plan needs no scratch). May query the
- * current device (a HIP call) when chunk_len is 0.
+ * chunk_len    tokens per parallel chunk. Each sequence is cut into chunks
+ *              that run in parallel; a summary pass computes every chunk's
+ *              (decay product, end state) pair, an associative combine of the
+ *              pairs gives the state entering each chunk (the "parallel scan"
+ *              of section "A Scan on the Chip"), and the output pass reruns
+ *              each chunk from its entering state. A chunk_len of seqlen or
+ *              more means one chunk and a single pass. The library may
+ *              shorten a chunk so a chunk of one channel group spans less
+ *              than 4 GiB.
+ * state_split  waves sharing the dstate states of each channel: 1, 2, 4 or
+ *              8. Values above 1 need dstate of 4, 8 or 16 divisible by the
+ *              split.
+ * reserved     must be 0.
+ */
+typedef struct mamba_scan_plan {
+    int64_t chunk_len;
+    int32_t state_split;
+    int32_t reserved;
+} mamba_scan_plan;
+
+/*
+ * Resolve the plan ssm_scan_fwd will use for this shape and report the
+ * scratch bytes it needs (0 when the plan has a single chunk).
+ *
+ * request   the caller's plan (may be NULL: automatic)
+ * resolved  receives the plan with every field decided (may be NULL)
+ * bytes     receives the workspace size (required)
+ * May query the current device (a HIP call) when a field is automatic.
  */
 int ssm_scan_fwd_workspace_size(int64_t batch, int64_t seqlen, int64_t dim, int dstate,
-                                int dtype, int64_t chunk_len, size_t* bytes);
+                                int dtype, const mamba_scan_plan* request,
+                                mamba_scan_plan* resolved, size_t* bytes);
 
 /*
  * Selective scan over whole sequences (prefill).
@@ -92,8 +116,10 @@ int ssm_scan_fwd_workspace_size(int64_t batch, int64_t seqlen, int64_t dim, int 
  * y          (batch, seqlen, dim)     written
  * hL         (batch, dim, dstate)     optional, written with the state after
  *                                     the last token; may alias h0
- * workspace  at least ssm_scan_fwd_workspace_size(..., chunk_len) bytes, may
- *            be NULL when that size is 0; its contents need no initialisation
+ * plan       work division (may be NULL: automatic), see mamba_scan_plan
+ * workspace  at least the bytes ssm_scan_fwd_workspace_size reports for the
+ *            same shape and plan; may be NULL when that size is 0; its
+ *            contents need no initialisation
  * seqlen == 0 writes hL = h0 (or zeros) and no y; batch == 0 or dim == 0 is
  * a no-op. y must not overlap any input.
  */
@@ -101,7 +127,7 @@ int ssm_scan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int dstate, int dty
                  const void* x, const void* delta, const float* A,
                  const void* B, const void* C, const float* D, const void* z,
                  const float* h0, void* y, float* hL,
-                 int64_t chunk_len, void* workspace, size_t workspace_bytes,
+                 const mamba_scan_plan* plan, void* workspace, size_t workspace_bytes,
                  hipStream_t stream);
 
 /*

@@ -18,14 +18,21 @@ import os
 
 import torch
 
-__all__ = ["scan_fwd", "state_update", "workspace_size", "library_path", "load_library",
-           "MambaScanError", "MAX_DSTATE"]
+__all__ = ["scan_fwd", "state_update", "workspace_size", "resolve_plan", "library_path",
+           "load_library", "MambaScanError", "MAX_DSTATE", "ScanPlan"]
 
 MAX_DSTATE = 16
 _DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
 _WS = {}
+
+
+class ScanPlan(ctypes.Structure):
+    """mamba_scan_plan: chunk_len (tokens per parallel chunk) and state_split
+    (waves sharing one channel's states); 0 means automatic."""
+    _fields_ = [("chunk_len", ctypes.c_int64), ("state_split", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 
 class MambaScanError(RuntimeError):
@@ -49,10 +56,11 @@ def load_library():
                                  "(run __graft_entry__.build())")
     lib = ctypes.CDLL(path)
     vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
-    lib.ssm_scan_fwd_workspace_size.argtypes = [i64, i64, i64, i32, i32, i64,
+    pp = ctypes.POINTER(ScanPlan)
+    lib.ssm_scan_fwd_workspace_size.argtypes = [i64, i64, i64, i32, i32, pp, pp,
                                                 ctypes.POINTER(ctypes.c_size_t)]
     lib.ssm_scan_fwd_workspace_size.restype = i32
-    lib.ssm_scan_fwd.argtypes = [i64, i64, i64, i32, i32] + [vp] * 10 + [i64, vp, ctypes.c_size_t, vp]
+    lib.ssm_scan_fwd.argtypes = [i64, i64, i64, i32, i32] + [vp] * 10 + [pp, vp, ctypes.c_size_t, vp]
     lib.ssm_scan_fwd.restype = i32
     lib.ssm_state_update.argtypes = [i64, i64, i32, i32] + [vp] * 9 + [vp]
     lib.ssm_state_update.restype = i32
@@ -91,13 +99,23 @@ def _need(t, name, shape, dtype, device):
         raise ValueError(f"{name} must be contiguous")
 
 
-def workspace_size(batch, seqlen, dim, dstate, dtype=torch.bfloat16, chunk_len=0):
-    """Scratch bytes ssm_scan_fwd needs (queries the current device when chunk_len == 0)."""
-    out = ctypes.c_size_t(0)
+def resolve_plan(batch, seqlen, dim, dstate, dtype=torch.bfloat16, chunk_len=0, state_split=0):
+    """The plan ssm_scan_fwd uses for this shape, and its scratch bytes:
+    returns (chunk_len, state_split, workspace_bytes). Automatic fields query
+    the current device."""
+    req = ScanPlan(chunk_len, state_split, 0)
+    out = ScanPlan(0, 0, 0)
+    nbytes = ctypes.c_size_t(0)
     _check(load_library().ssm_scan_fwd_workspace_size(batch, seqlen, dim, dstate, _DTYPES[dtype],
-                                                      chunk_len, ctypes.byref(out)),
+                                                      ctypes.byref(req), ctypes.byref(out),
+                                                      ctypes.byref(nbytes)),
            "ssm_scan_fwd_workspace_size")
-    return out.value
+    return out.chunk_len, out.state_split, nbytes.value
+
+
+def workspace_size(batch, seqlen, dim, dstate, dtype=torch.bfloat16, chunk_len=0, state_split=0):
+    """Scratch bytes ssm_scan_fwd needs for this shape and plan."""
+    return resolve_plan(batch, seqlen, dim, dstate, dtype, chunk_len, state_split)[2]
 
 
 def _workspace(device, nbytes):
@@ -111,10 +129,11 @@ def _workspace(device, nbytes):
     return buf
 
 
-def scan_fwd(x, delta, A, B, C, D=None, z=None, h0=None, *, chunk_len=0, return_state=True,
-             out=None, state_out=None):
+def scan_fwd(x, delta, A, B, C, D=None, z=None, h0=None, *, chunk_len=0, state_split=0,
+             return_state=True, out=None, state_out=None):
     """Selective scan over whole sequences; returns (y, hL) (hL is None when
-    return_state is False). `chunk_len` > 0 forces the parallel chunk length."""
+    return_state is False). `chunk_len` > 0 forces the parallel chunk length
+    and `state_split` > 0 the number of waves sharing a channel's states."""
     lib = load_library()
     if x.dim() != 3:
         raise ValueError("x must be (batch, L, dim)")
@@ -142,12 +161,13 @@ def scan_fwd(x, delta, A, B, C, D=None, z=None, h0=None, *, chunk_len=0, return_
         hL = state_out if state_out is not None else torch.empty(batch, dim, dstate,
                                                                  dtype=torch.float32, device=dev)
         _need(hL, "state_out", (batch, dim, dstate), torch.float32, dev)
+    plan = ScanPlan(chunk_len, state_split, 0)
     with torch.cuda.device(dev):
-        nbytes = workspace_size(batch, seqlen, dim, dstate, dt, chunk_len)
+        nbytes = workspace_size(batch, seqlen, dim, dstate, dt, chunk_len, state_split)
         ws = _workspace(dev, nbytes)
         st = lib.ssm_scan_fwd(batch, seqlen, dim, dstate, _DTYPES[dt], _ptr(x), _ptr(delta),
                               _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0), _ptr(y),
-                              _ptr(hL), chunk_len, _ptr(ws), nbytes, _stream(dev))
+                              _ptr(hL), ctypes.byref(plan), _ptr(ws), nbytes, _stream(dev))
     _check(st, "ssm_scan_fwd")
     return y, hL
 

@@ -41,9 +41,8 @@ int current_cu_count(int* cu) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-int check_shape(int64_t batch, int64_t seqlen, int64_t dim, int dstate, int dtype,
-                int64_t chunk_len) {
-    if (batch < 0 || seqlen < 0 || dim < 0 || chunk_len < 0) return MAMBA_ERR_INVALID_ARG;
+int check_shape(int64_t batch, int64_t seqlen, int64_t dim, int dstate, int dtype) {
+    if (batch < 0 || seqlen < 0 || dim < 0) return MAMBA_ERR_INVALID_ARG;
     if (dtype != MAMBA_DTYPE_F32 && dtype != MAMBA_DTYPE_BF16) return MAMBA_ERR_INVALID_ARG;
     if (dstate < 1 || dstate > MAMBA_SCAN_MAX_DSTATE) return MAMBA_ERR_UNSUPPORTED;
     // every element and workgroup index must fit comfortably in int64 / the grid
@@ -57,47 +56,71 @@ int check_shape(int64_t batch, int64_t seqlen, int64_t dim, int dstate, int dtyp
     return MAMBA_OK;
 }
 
-// Work decomposition. One wave scans 64 channels of one batch row over one
-// chunk. The chunk count is picked so the launch holds about four waves per
-// SIMD (four SIMDs per compute unit), which the register budget of the scan
-// kernels allows; chunks are never shorter than kMinChunk tokens, since each
-// extra chunk costs a summary pass over its tokens.
-constexpr int64_t kWavesPerSimdTarget = 4;
+// Work decomposition. A workgroup of `state_split` waves scans 64 channels
+// of one batch row over one chunk. The automatic plan splits every channel's
+// states over four waves where the kernels allow it (dstate 4, 8 or 16):
+// that multiplies the waves by four for about a sixth more vector work, far
+// cheaper than cutting the sequence, where every chunk but the last pays a
+// summary pass. Only when the split launch still holds fewer than two waves
+// per SIMD is the sequence cut, into enough chunks for about six waves per
+// SIMD. Chunks are never shorter than kMinChunk tokens. (Measured on MI355X
+// for the Mamba-130M and Mamba-2.8B layer shapes.)
+constexpr int kPreferredSplit = 4;
+constexpr int64_t kWavesPerSimdNoChunk = 2;
+constexpr int64_t kWavesPerSimdChunked = 6;
 constexpr int64_t kMinChunk = 64;
 
-int make_plan(int64_t batch, int64_t seqlen, int64_t dim, int dstate, int64_t chunk_len,
-              ScanPlan* plan) {
+int make_plan(int64_t batch, int64_t seqlen, int64_t dim, int dstate, int dtype,
+              const mamba_scan_plan* req, ScanPlan* plan) {
+    int64_t len = req ? req->chunk_len : 0;
+    int split = req ? req->state_split : 0;
+    if (req && req->reserved != 0) return MAMBA_ERR_INVALID_ARG;
+    if (len < 0 || split < 0) return MAMBA_ERR_INVALID_ARG;
+    if (split != 0 && !mamba::split_supported(dstate, split)) return MAMBA_ERR_UNSUPPORTED;
     if (seqlen == 0 || batch == 0 || dim == 0) {
         plan->chunk_len = seqlen;
         plan->nchunks = 1;
+        plan->state_split = split ? split : 1;
         plan->workspace_bytes = 0;
         return MAMBA_OK;
     }
-    int64_t len = chunk_len;
-    if (len == 0) {
+    const int64_t groups = batch * ((dim + mamba::kWave - 1) / mamba::kWave);
+    if (split == 0 || len == 0) {
         int cu = 0;
         const int st = current_cu_count(&cu);
         if (st != MAMBA_OK) return st;
-        const int64_t waves = batch * ((dim + mamba::kWave - 1) / mamba::kWave);
-        const int64_t target = int64_t(cu) * 4 * kWavesPerSimdTarget;
-        int64_t n = (target + waves / 2) / waves;
-        const int64_t nmax = seqlen / kMinChunk;
-        if (n > nmax) n = nmax;
-        if (n < 1) n = 1;
-        len = (seqlen + n - 1) / n;
-        len = (len + mamba::kTokenTile - 1) / mamba::kTokenTile * mamba::kTokenTile;
+        const int64_t simds = int64_t(cu) * 4;
+        if (split == 0) {
+            split = 1;
+            for (int sp = kPreferredSplit; sp > 1; sp /= 2)
+                if (mamba::split_supported(dstate, sp)) {
+                    split = sp;
+                    break;
+                }
+        }
+        if (len == 0) {
+            const int64_t waves = groups * split;
+            int64_t n = 1;
+            if (waves < kWavesPerSimdNoChunk * simds)
+                n = (kWavesPerSimdChunked * simds + waves - 1) / waves;
+            const int64_t nmax = seqlen / kMinChunk;
+            if (n > nmax) n = nmax;
+            if (n < 1) n = 1;
+            len = (seqlen + n - 1) / n;
+            len = (len + mamba::kTokenTile - 1) / mamba::kTokenTile * mamba::kTokenTile;
+        }
     }
     if (len > seqlen) len = seqlen;
     // a chunk's x/delta/z/y rows are addressed with 32-bit byte offsets
-    const int64_t esz = 4;  // the wider I/O dtype, so the bound holds for both
+    const int64_t esz = dtype == MAMBA_DTYPE_F32 ? 4 : 2;
     const int64_t max_len = ((int64_t(1) << 32) - 1) / (dim * esz);
     if (max_len < 1) return MAMBA_ERR_UNSUPPORTED;
     if (len > max_len) len = max_len;
     const int64_t nchunks = (seqlen + len - 1) / len;
-    const int64_t nblk_d = (dim + mamba::kWave - 1) / mamba::kWave;
-    if (nblk_d > (int64_t(1) << 31) / (nchunks * batch)) return MAMBA_ERR_UNSUPPORTED;
+    if (groups > (int64_t(1) << 31) / nchunks) return MAMBA_ERR_UNSUPPORTED;
     plan->chunk_len = len;
     plan->nchunks = nchunks;
+    plan->state_split = split;
     plan->workspace_bytes = mamba::scan_workspace_bytes(batch, dim, dstate, nchunks);
     return MAMBA_OK;
 }
@@ -107,23 +130,29 @@ int make_plan(int64_t batch, int64_t seqlen, int64_t dim, int dstate, int64_t ch
 extern "C" {
 
 int ssm_scan_fwd_workspace_size(int64_t batch, int64_t seqlen, int64_t dim, int dstate,
-                                int dtype, int64_t chunk_len, size_t* bytes) {
+                                int dtype, const mamba_scan_plan* request,
+                                mamba_scan_plan* resolved, size_t* bytes) {
     if (bytes == nullptr) return MAMBA_ERR_INVALID_ARG;
-    const int st = check_shape(batch, seqlen, dim, dstate, dtype, chunk_len);
+    const int st = check_shape(batch, seqlen, dim, dstate, dtype);
     if (st != MAMBA_OK) return st;
     ScanPlan plan;
-    const int ps = make_plan(batch, seqlen, dim, dstate, chunk_len, &plan);
+    const int ps = make_plan(batch, seqlen, dim, dstate, dtype, request, &plan);
     if (ps != MAMBA_OK) return ps;
     *bytes = plan.workspace_bytes;
+    if (resolved != nullptr) {
+        resolved->chunk_len = plan.chunk_len;
+        resolved->state_split = plan.state_split;
+        resolved->reserved = 0;
+    }
     return MAMBA_OK;
 }
 
 int ssm_scan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int dstate, int dtype,
                  const void* x, const void* delta, const float* A, const void* B,
                  const void* C, const float* D, const void* z, const float* h0, void* y,
-                 float* hL, int64_t chunk_len, void* workspace, size_t workspace_bytes,
-                 hipStream_t stream) {
-    int st = check_shape(batch, seqlen, dim, dstate, dtype, chunk_len);
+                 float* hL, const mamba_scan_plan* plan_req, void* workspace,
+                 size_t workspace_bytes, hipStream_t stream) {
+    int st = check_shape(batch, seqlen, dim, dstate, dtype);
     if (st != MAMBA_OK) return st;
     if (batch == 0 || dim == 0) return MAMBA_OK;
     if (A == nullptr) return MAMBA_ERR_INVALID_ARG;
@@ -136,7 +165,7 @@ int ssm_scan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int dstate, int dty
     if (seqlen == 0 && hL == nullptr) return MAMBA_OK;
 
     ScanPlan plan;
-    st = make_plan(batch, seqlen, dim, dstate, chunk_len, &plan);
+    st = make_plan(batch, seqlen, dim, dstate, dtype, plan_req, &plan);
     if (st != MAMBA_OK) return st;
     if (plan.workspace_bytes > 0 && (workspace == nullptr || workspace_bytes < plan.workspace_bytes))
         return MAMBA_ERR_WORKSPACE;
@@ -164,7 +193,7 @@ int ssm_state_update(int64_t batch, int64_t dim, int dstate, int dtype, float* h
                      const void* x, const void* delta, const float* A, const void* B,
                      const void* C, const float* D, const void* z, void* y,
                      hipStream_t stream) {
-    int st = check_shape(batch, 1, dim, dstate, dtype, 0);
+    int st = check_shape(batch, 1, dim, dstate, dtype);
     if (st != MAMBA_OK) return st;
     if (batch == 0 || dim == 0) return MAMBA_OK;
     if (h == nullptr || x == nullptr || delta == nullptr || A == nullptr || B == nullptr ||

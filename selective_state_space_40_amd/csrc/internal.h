@@ -22,8 +22,18 @@ enum IoType : int { kIoF32 = 0, kIoBF16 = 1 };
 struct ScanPlan {
     int64_t chunk_len = 0;
     int64_t nchunks = 1;
+    int state_split = 1;         // waves sharing the states of one channel
     size_t workspace_bytes = 0;  // 0 when nchunks == 1
 };
+
+// State splits the kernels are built for: 1 for every dstate, and 2, 4, 8
+// where they divide a dstate of 4, 8 or 16.
+inline bool split_supported(int dstate, int split) {
+    if (split == 1) return true;
+    if (split != 2 && split != 4 && split != 8) return false;
+    if (dstate != 4 && dstate != 8 && dstate != 16) return false;
+    return dstate % split == 0;
+}
 
 struct ScanArgs {
     int64_t batch, seqlen, dim;

@@ -8,16 +8,18 @@
 //
 // Work mapping. The scan is elementwise in (b, d) and sequential in t, and it
 // is no dense contraction, so it runs on the vector ALUs, not the matrix
-// cores. One lane owns one channel d of one batch row b for one chunk of
-// tokens; its N states, its N decay rates A[d,:]*log2(e) and its running
-// readout stay in VGPRs for the whole chunk, so the N-times-larger expanded
+// cores. A workgroup covers 64 consecutive channels of one batch row over
+// one chunk of tokens, one channel per lane; its S waves split the N states
+// of each channel, so a lane keeps N/S states and N/S decay rates
+// A[d,n]*log2(e) in VGPRs for the whole chunk and the N-times-larger expanded
 // state never leaves the register file (section "A Scan on the Chip": only
-// inputs and outputs touch memory). A wave covers 64 consecutive channels,
-// so every x/delta/z load and y store of a token is one contiguous 128-byte
-// (bf16) or 256-byte (fp32) access. B[b,t,:] and C[b,t,:] are the same for
-// all channels of a wave, so they are fetched with scalar loads into SGPRs,
-// converted on the scalar unit and used straight from there by the vector
-// FMAs: no LDS round trip and no VGPRs for them.
+// inputs and outputs touch memory). Every x/delta/z load and y store of a
+// token is one contiguous 128-byte (bf16) or 256-byte (fp32) access of the
+// wave. B[b,t,:] and C[b,t,:] are shared by all channels: the workgroup
+// stages each tile's rows in LDS as fp32 and every wave reads its slice with
+// broadcast LDS reads. The S partial readouts of a token are summed through
+// LDS, and the epilogue (skip term, silu gate, bf16 rounding, store) is
+// spread over the S waves.
 //
 // x, delta and z are fetched one register tile of kTokenTile tokens ahead of
 // the tokens being computed, so the HBM latency of a tile overlaps the
@@ -33,6 +35,8 @@
 // delta, never from differences of long prefix sums.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "internal.h"
 
@@ -72,35 +76,6 @@ __device__ __forceinline__ void store_io(void* __restrict__ p, int64_t i, float 
     }
 }
 
-typedef __attribute__((address_space(4))) uint32_t kconst_u32;
-
-// One row of N B- or C-values at element offset `row` (wave-uniform): with
-// bf16 and even N the row is dword aligned and read as N/2 dwords, which the
-// compiler turns into scalar loads; the two halves of a dword are widened on
-// the scalar unit.
-template <int N, int IO>
-__device__ __forceinline__ void load_row(const void* __restrict__ p, int64_t row, float (&out)[N]) {
-    if constexpr (IO == kIoBF16 && (N % 2 == 0)) {
-        // B and C are never written while a scan runs: reading them through
-        // the constant address space lets the compiler use scalar loads even
-        // though the kernel also stores through buffer resources.
-        const kconst_u32* q = (const kconst_u32*)(p) + row / 2;
-#pragma unroll
-        for (int i = 0; i < N / 2; ++i) {
-            const uint32_t w = q[i];
-            out[2 * i] = __uint_as_float(w << 16);
-            out[2 * i + 1] = __uint_as_float(w & 0xffff0000u);
-        }
-    } else if constexpr (IO == kIoF32) {
-        const kconst_u32* q = (const kconst_u32*)(p) + row;
-#pragma unroll
-        for (int n = 0; n < N; ++n) out[n] = __uint_as_float(q[n]);
-    } else {
-#pragma unroll
-        for (int n = 0; n < N; ++n) out[n] = raw_to_f32<IO>(load_raw<IO>(p, row + n));
-    }
-}
-
 __device__ __forceinline__ float fast_exp2(float v) { return __builtin_amdgcn_exp2f(v); }
 __device__ __forceinline__ float fast_rcp(float v) { return __builtin_amdgcn_rcpf(v); }
 
@@ -112,7 +87,7 @@ __device__ __forceinline__ float silu(float z) {
 // ---------------------------------------------------------------------------
 // Per-wave addressing of one chunk. x, delta, z and y of the chunk are read
 // and written through buffer resources whose base is the chunk's first token
-// at the wave's first channel: token j of a lane is at byte offset
+// at the workgroup's first channel: token j of a lane is at byte offset
 // j * row_bytes (a scalar offset, advanced on the scalar unit) plus the
 // lane's fixed 32-bit channel offset (one VGPR for the whole chunk), so no
 // vector ALU work goes into addresses. The resource's record count is the
@@ -157,105 +132,287 @@ __device__ __forceinline__ void buf_store(__amdgpu_buffer_rsrc_t r, uint32_t lan
     }
 }
 
-// One token of the recurrence for one lane. Bt/Ct point at B[b,t,0] and
-// C[b,t,0] (wave-uniform).
-template <int N, int IO, bool WRITE_Y, bool HAS_D, bool HAS_Z>
-__device__ __forceinline__ void scan_token(const ChunkIo& io, const void* Bt, const void* Ct,
-                                           uint32_t row_off, uint32_t xr, uint32_t dr,
-                                           uint32_t zr, const float (&A2)[N], float (&h)[N],
-                                           float dskip, float& dsum) {
-    const float dt = raw_to_f32<IO>(dr);
-    const float u = raw_to_f32<IO>(xr);
-    float Bv[N];
-    load_row<N, IO>(Bt, 0, Bv);
-    const float du = dt * u;
-    if constexpr (WRITE_Y) {
-        float Cv[N];
-        load_row<N, IO>(Ct, 0, Cv);
-        float acc = HAS_D ? dskip * u : 0.0f;
+// ---------------------------------------------------------------------------
+// Work mapping. A workgroup of S waves covers 64 consecutive channels of one
+// batch row over one chunk of tokens, and its S waves split the N states of
+// every channel: wave w owns states [w*N/S, (w+1)*N/S). Each wave therefore
+// needs only its slice of B[b,t,:] and C[b,t,:], which is the same for all
+// 64 lanes and lives in SGPRs, and keeps N/S states and N/S decay rates per
+// lane. Splitting the states multiplies the waves of a launch by S without
+// the extra summary pass a further split of the sequence would cost; the
+// price is that the per-token conversions of x and delta are repeated in
+// each of the S waves and that the readout is summed across waves.
+//
+// The readout of a register tile of TT tokens is summed through LDS: every
+// wave writes its partial sums C.h over its states for the TT tokens, one
+// barrier, and wave w then finalises the tokens j = w, w+S, ... of the tile
+// (sum of the S partials in a fixed order, skip term, silu gate, rounding and
+// store), so the epilogue work is spread evenly over the S waves. The LDS
+// buffer is double-buffered by tile parity, so one barrier per tile suffices:
+// a wave only rewrites a buffer after every wave has passed the barrier of
+// the tile in between, which follows all reads of that buffer.
+template <int N, int S>
+struct Split {
+    static_assert(N % S == 0 && TT % S == 0, "states and tile tokens split evenly over waves");
+    static constexpr int NPW = N / S;   // states per wave
+    static constexpr int TPW = TT / S;  // tokens each wave finalises per tile
+};
+
+// B and C reach the waves through LDS. A tile's B[b, t, :] and C[b, t, :]
+// rows are one contiguous run of TT*N values per tensor; all lanes of the
+// workgroup fetch the next tile's run a tile ahead (one or two values each,
+// with the same in-order vector loads as x and delta), convert it to fp32
+// and store it to LDS right before the tile's barrier. Each wave then reads
+// its N/S-state slice with wave-uniform (broadcast, conflict-free) LDS reads.
+// Scalar loads are avoided on purpose: their completion counter cannot be
+// waited on in order, so they cannot be issued a tile ahead.
+template <int N, int S>
+struct BcStage {
+    static constexpr int kVals = TT * N;                                // per tensor per tile
+    static constexpr int kPerLane = (kVals + kWave * S - 1) / (kWave * S);
+    // LDS floats per tensor: every lane of every pass gets a slot, so lanes
+    // past the tile's values write padding instead of taking a branch
+    static constexpr int kSlots = kPerLane * kWave * S;
+};
+
+struct BcIo {
+    __amdgpu_buffer_rsrc_t B, C;  // base: B[b, t0, 0] / C[b, t0, 0], extent: the chunk's rows
+};
+
+template <int N, int S, int IO>
+__device__ __forceinline__ void fetch_bc(const BcIo& bc, int tile, int cnt,
+                                         uint32_t (&braw)[BcStage<N, S>::kPerLane],
+                                         uint32_t (&craw)[BcStage<N, S>::kPerLane]) {
+    constexpr int esz = IO == kIoF32 ? 4 : 2;
+    const int tid = threadIdx.x;
 #pragma unroll
-        for (int n = 0; n < N; ++n) {
-            const float e = fast_exp2(dt * A2[n]);
-            h[n] = fmaf(e, h[n], du * Bv[n]);
-            acc = fmaf(Cv[n], h[n], acc);
+    for (int q = 0; q < BcStage<N, S>::kPerLane; ++q) {
+        // values past the tile's last token are clamped onto it (in bounds, unused)
+        const int idx = min(q * kWave * S + tid, cnt * N - 1);
+        const uint32_t off = static_cast<uint32_t>((tile * TT * N + idx) * esz);
+        braw[q] = buf_load<IO>(bc.B, off, 0);
+        craw[q] = buf_load<IO>(bc.C, off, 0);
+    }
+}
+
+// LDS layout of one staged tile: [tensor B, C][token j][state n], fp32,
+// each tensor padded to kSlots floats.
+template <int N, int S, int IO>
+__device__ __forceinline__ void stage_bc(float* bcs, const uint32_t (&braw)[BcStage<N, S>::kPerLane],
+                                         const uint32_t (&craw)[BcStage<N, S>::kPerLane]) {
+    constexpr int P = BcStage<N, S>::kSlots;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int q = 0; q < BcStage<N, S>::kPerLane; ++q) {
+        const int idx = q * kWave * S + tid;
+        bcs[idx] = raw_to_f32<IO>(braw[q]);
+        bcs[P + idx] = raw_to_f32<IO>(craw[q]);
+    }
+}
+
+// This wave's slice of one staged row (wave-uniform LDS reads).
+template <int NPW>
+__device__ __forceinline__ void read_slice(const float* row, float (&out)[NPW]) {
+    if constexpr (NPW % 4 == 0) {
+#pragma unroll
+        for (int k = 0; k < NPW; k += 4) {
+            const float4 v = *reinterpret_cast<const float4*>(row + k);
+            out[k] = v.x; out[k + 1] = v.y; out[k + 2] = v.z; out[k + 3] = v.w;
         }
-        if constexpr (HAS_Z) acc *= silu(raw_to_f32<IO>(zr));
-        // Lanes past the last channel were clamped onto channel dim-1 and
-        // computed its value bit for bit, so they store the same bits to the
-        // same address; the store needs no lane mask and no branch.
-        buf_store<IO>(io.y, io.lane_bytes, row_off, acc);
+    } else if constexpr (NPW % 2 == 0) {
+#pragma unroll
+        for (int k = 0; k < NPW; k += 2) {
+            const float2 v = *reinterpret_cast<const float2*>(row + k);
+            out[k] = v.x; out[k + 1] = v.y;
+        }
     } else {
 #pragma unroll
-        for (int n = 0; n < N; ++n) {
-            const float e = fast_exp2(dt * A2[n]);
-            h[n] = fmaf(e, h[n], du * Bv[n]);
-        }
-        dsum += dt;
+        for (int k = 0; k < NPW; ++k) out[k] = row[k];
     }
 }
 
-template <int IO, bool LOAD_Z>
-__device__ __forceinline__ void fetch_tile(const ChunkIo& io, int tile, uint32_t (&xr)[TT],
-                                           uint32_t (&dr)[TT], uint32_t (&zr)[TT]) {
+// Register tile: x and delta of all TT tokens (every wave needs them), and
+// z and x of the TT/S tokens this wave finalises (tokens w, w+S, ...).
+template <int S>
+struct Tile {
+    uint32_t x[TT], dt[TT];
+    uint32_t zown[TT / S], xown[TT / S];
+};
+
+// Token indices are clamped to the chunk, so the ragged last tile reads only
+// tokens that exist.
+template <int S, int IO, bool LOAD_Z, bool LOAD_XOWN>
+__device__ __forceinline__ void fetch_tile(const ChunkIo& io, int tile, int w, int ntok,
+                                           Tile<S>& r) {
 #pragma unroll
     for (int j = 0; j < TT; ++j) {
-        const uint32_t off = static_cast<uint32_t>(tile * TT + j) * io.row_bytes;
-        xr[j] = buf_load<IO>(io.x, io.lane_bytes, off);
-        dr[j] = buf_load<IO>(io.delta, io.lane_bytes, off);
-        zr[j] = LOAD_Z ? buf_load<IO>(io.z, io.lane_bytes, off) : 0u;
-    }
-}
-
-template <int N, int IO, bool WRITE_Y, bool HAS_D, bool HAS_Z>
-__device__ __forceinline__ void compute_tile(const ChunkIo& io, const char* Bc, const char* Cc,
-                                             int tile, const uint32_t (&xr)[TT],
-                                             const uint32_t (&dr)[TT], const uint32_t (&zr)[TT],
-                                             const float (&A2)[N], float (&h)[N], float dskip,
-                                             float& dsum) {
-    constexpr int64_t kRowBytes = N * (IO == kIoF32 ? 4 : 2);
-#pragma unroll
-    for (int j = 0; j < TT; ++j) {
-        const int tok = tile * TT + j;
-        scan_token<N, IO, WRITE_Y, HAS_D, HAS_Z>(io, Bc + tok * kRowBytes, Cc + tok * kRowBytes,
-                                                 static_cast<uint32_t>(tok) * io.row_bytes, xr[j],
-                                                 dr[j], zr[j], A2, h, dskip, dsum);
-    }
-}
-
-// All `ntok` tokens of one lane's chunk. Bc/Cc point at B[b,t0,0] and
-// C[b,t0,0]. Two register tiles alternate: while one tile of tokens is
-// computed the next one is already in flight, and the tiles swap roles
-// without register copies.
-template <int N, int IO, bool WRITE_Y, bool HAS_D, bool HAS_Z>
-__device__ __forceinline__ void scan_chunk(const ChunkIo& io, const char* Bc, const char* Cc,
-                                           int ntok, const float (&A2)[N], float (&h)[N],
-                                           float dskip, float& dsum) {
-    constexpr bool LOAD_Z = WRITE_Y && HAS_Z;
-    constexpr int64_t kRowBytes = N * (IO == kIoF32 ? 4 : 2);
-    const int ntiles = ntok / TT;
-    if (ntiles > 0) {
-        // The fetch is unconditional (past the last tile it re-reads the last
-        // tile, whose values go unused) so every path into a compute step has
-        // the same loads in flight and the waits before it stay exact.
-        uint32_t xa[TT], da[TT], za[TT], xb[TT], db[TT], zb[TT];
-        fetch_tile<IO, LOAD_Z>(io, 0, xa, da, za);
-        int i = 0;
-        while (true) {
-            fetch_tile<IO, LOAD_Z>(io, min(i + 1, ntiles - 1), xb, db, zb);
-            compute_tile<N, IO, WRITE_Y, HAS_D, HAS_Z>(io, Bc, Cc, i, xa, da, za, A2, h, dskip, dsum);
-            if (++i == ntiles) break;
-            fetch_tile<IO, LOAD_Z>(io, min(i + 1, ntiles - 1), xa, da, za);
-            compute_tile<N, IO, WRITE_Y, HAS_D, HAS_Z>(io, Bc, Cc, i, xb, db, zb, A2, h, dskip, dsum);
-            if (++i == ntiles) break;
-        }
-    }
-    for (int tok = ntiles * TT; tok < ntok; ++tok) {  // ragged tail, fewer than TT tokens
+        const int tok = min(tile * TT + j, ntok - 1);
         const uint32_t off = static_cast<uint32_t>(tok) * io.row_bytes;
-        const uint32_t zr = LOAD_Z ? buf_load<IO>(io.z, io.lane_bytes, off) : 0u;
-        scan_token<N, IO, WRITE_Y, HAS_D, HAS_Z>(
-            io, Bc + tok * kRowBytes, Cc + tok * kRowBytes, off,
-            buf_load<IO>(io.x, io.lane_bytes, off), buf_load<IO>(io.delta, io.lane_bytes, off), zr,
-            A2, h, dskip, dsum);
+        r.x[j] = buf_load<IO>(io.x, io.lane_bytes, off);
+        r.dt[j] = buf_load<IO>(io.delta, io.lane_bytes, off);
+    }
+#pragma unroll
+    for (int jj = 0; jj < TT / S; ++jj) {
+        const int tok = min(tile * TT + jj * S + w, ntok - 1);
+        const uint32_t off = static_cast<uint32_t>(tok) * io.row_bytes;
+        r.zown[jj] = LOAD_Z ? buf_load<IO>(io.z, io.lane_bytes, off) : 0u;
+        r.xown[jj] = LOAD_XOWN ? buf_load<IO>(io.x, io.lane_bytes, off) : 0u;
+    }
+}
+
+// The state update of tokens tile*TT + [0, cnt) for this wave's states
+// (FULL: cnt == TT, compiled without per-token branches). With OUTPUT the
+// readout over the wave's states is kept per token in part[] (and with
+// S == 1 the token is finished and stored right away); without it the sum
+// of delta over the tokens accumulates in dsum.
+template <int N, int S, int IO, bool OUTPUT, bool HAS_D, bool HAS_Z, bool FULL>
+__device__ __forceinline__ void compute_tile(const ChunkIo& io, const float* bcs_w, int tile,
+                                             int cnt, const Tile<S>& r,
+                                             const float (&A2)[Split<N, S>::NPW],
+                                             float (&h)[Split<N, S>::NPW], float dskip,
+                                             float (&part)[TT], float& dsum) {
+    constexpr int NPW = Split<N, S>::NPW;
+    constexpr int P = BcStage<N, S>::kSlots;
+#pragma unroll
+    for (int j = 0; j < TT; ++j) {
+        part[j] = 0.0f;
+        if (FULL || j < cnt) {
+            const float dt = raw_to_f32<IO>(r.dt[j]);
+            const float du = dt * raw_to_f32<IO>(r.x[j]);
+            float Bv[NPW];
+            read_slice<NPW>(bcs_w + j * N, Bv);
+            if constexpr (OUTPUT) {
+                float Cv[NPW];
+                read_slice<NPW>(bcs_w + P + j * N, Cv);
+                float p = 0.0f;
+#pragma unroll
+                for (int k = 0; k < NPW; ++k) {
+                    const float e = fast_exp2(dt * A2[k]);
+                    h[k] = fmaf(e, h[k], du * Bv[k]);
+                    p = fmaf(Cv[k], h[k], p);
+                }
+                if constexpr (S == 1) {
+                    // one wave holds every state: finish the token right here
+                    if constexpr (HAS_D) p = fmaf(dskip, raw_to_f32<IO>(r.x[j]), p);
+                    if constexpr (HAS_Z) p *= silu(raw_to_f32<IO>(r.zown[j]));
+                    // Lanes past the last channel were clamped onto channel
+                    // dim-1 and computed its value bit for bit, so they store
+                    // the same bits to the same address; no lane mask needed.
+                    buf_store<IO>(io.y, io.lane_bytes,
+                                  static_cast<uint32_t>(tile * TT + j) * io.row_bytes, p);
+                }
+                part[j] = p;
+            } else {
+#pragma unroll
+                for (int k = 0; k < NPW; ++k) {
+                    const float e = fast_exp2(dt * A2[k]);
+                    h[k] = fmaf(e, h[k], du * Bv[k]);
+                }
+                dsum += dt;
+            }
+        }
+    }
+}
+
+// Wave w finishes its tokens j = w, w+S, ... of the tile: the S partial
+// readouts summed in a fixed wave order, the skip term, the gate, rounding
+// and the store.
+template <int S, int IO, bool HAS_D, bool HAS_Z, bool FULL>
+__device__ __forceinline__ void finalize_tile(const ChunkIo& io, const float* red_tile, int w,
+                                              int tile, int cnt, const Tile<S>& r, float dskip) {
+    const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+    for (int jj = 0; jj < TT / S; ++jj) {
+        const int j = jj * S + w;
+        if (FULL || j < cnt) {
+            const float* col = red_tile + j * kWave + lane;
+            float acc = col[0];
+#pragma unroll
+            for (int v = 1; v < S; ++v) acc += col[v * TT * kWave];
+            if constexpr (HAS_D) acc = fmaf(dskip, raw_to_f32<IO>(r.xown[jj]), acc);
+            if constexpr (HAS_Z) acc *= silu(raw_to_f32<IO>(r.zown[jj]));
+            // lanes past the last channel store the bits of channel dim-1
+            buf_store<IO>(io.y, io.lane_bytes, static_cast<uint32_t>(tile * TT + j) * io.row_bytes,
+                          acc);
+        }
+    }
+}
+
+// All `ntok` tokens of one chunk for one wave. Two register tiles alternate:
+// while one tile is computed the next one (x, delta, z, and the raw B/C run)
+// is already in flight, and the tiles swap roles without register copies.
+// Fetches are unconditional and clamp their tokens to the chunk (past the
+// last tile they re-read it, and the values go unused), and the full tiles
+// run in pairs inside a loop with a single exit, so every path into a compute
+// step has the same loads in flight and the waits before it stay exact. A
+// ragged last tile runs once after the loop.
+//
+// Per tile, in order: fetch tile i+1; compute tile i from LDS buffer i&1;
+// [S > 1: store the partial readouts]; stage tile i+1's B/C into LDS buffer
+// (i+1)&1; barrier; [S > 1: finalise this wave's tokens of tile i]. Every
+// LDS buffer is rewritten only after a barrier that follows its last read.
+template <int N, int S, int IO, bool OUTPUT, bool HAS_D, bool HAS_Z>
+__device__ __forceinline__ void scan_chunk(const ChunkIo& io, const BcIo& bcio, int ntok, int w,
+                                           int n0, float* red, float* bcs,
+                                           const float (&A2)[Split<N, S>::NPW],
+                                           float (&h)[Split<N, S>::NPW], float dskip,
+                                           float& dsum) {
+    constexpr bool LOAD_Z = OUTPUT && HAS_Z;
+    constexpr bool LOAD_XOWN = OUTPUT && HAS_D && S > 1;
+    constexpr int KP = BcStage<N, S>::kPerLane;
+    constexpr int P = BcStage<N, S>::kSlots;
+    const int ntiles = (ntok + TT - 1) / TT;
+    const int nfull = ntok / TT;
+    const int lane = threadIdx.x & (kWave - 1);
+    Tile<S> ta, tb;
+    uint32_t bra[KP], cra[KP];
+
+    auto step = [&](auto full_tag, int i, const Tile<S>& cur, Tile<S>& nxt) {
+        constexpr bool FULL = decltype(full_tag)::value;
+        const int inext = min(i + 1, ntiles - 1);
+        // The B/C run is issued first and kept first (scheduling fences), so
+        // staging it at the end of this step waits only for loads older than
+        // the x/delta/z of the next tile, which stay in flight.
+        fetch_bc<N, S, IO>(bcio, inext, min(TT, ntok - inext * TT), bra, cra);
+        __builtin_amdgcn_sched_barrier(0);
+        fetch_tile<S, IO, LOAD_Z, LOAD_XOWN>(io, inext, w, ntok, nxt);
+        __builtin_amdgcn_sched_barrier(0);
+        const int cnt = FULL ? TT : ntok - i * TT;
+        const float* bcs_w = bcs + (i & 1) * 2 * P + n0;
+        float* red_tile = red + (i & 1) * S * TT * kWave;
+        float part[TT];
+        compute_tile<N, S, IO, OUTPUT, HAS_D, HAS_Z, FULL>(io, bcs_w, i, cnt, cur, A2, h, dskip,
+                                                           part, dsum);
+        if constexpr (OUTPUT && S > 1) {
+            // the skip term D*x of token j is added by the wave that finalises
+            // j, in finalize_tile, from its own copy of x_j
+            float* mine = red_tile + w * TT * kWave + lane;
+#pragma unroll
+            for (int j = 0; j < TT; ++j) mine[j * kWave] = part[j];
+        }
+        stage_bc<N, S, IO>(bcs + ((i + 1) & 1) * 2 * P, bra, cra);
+        __syncthreads();
+        if constexpr (OUTPUT && S > 1)
+            finalize_tile<S, IO, HAS_D, HAS_Z, FULL>(io, red_tile, w, i, cnt, cur, dskip);
+    };
+    using Full = std::integral_constant<bool, true>;
+    using Ragged = std::integral_constant<bool, false>;
+
+    // prologue: tile 0's B/C into LDS buffer 0, tile 0's x/delta/z into regs
+    fetch_bc<N, S, IO>(bcio, 0, min(TT, ntok), bra, cra);
+    fetch_tile<S, IO, LOAD_Z, LOAD_XOWN>(io, 0, w, ntok, ta);
+    stage_bc<N, S, IO>(bcs, bra, cra);
+    __syncthreads();
+    int i = 0;
+    for (; i + 2 <= nfull; i += 2) {
+        step(Full{}, i, ta, tb);
+        step(Full{}, i + 1, tb, ta);
+    }
+    if (i < nfull) {
+        step(Full{}, i, ta, tb);
+        if (nfull < ntiles) step(Ragged{}, i + 1, tb, ta);
+    } else if (nfull < ntiles) {
+        step(Ragged{}, i, ta, tb);
     }
 }
 
@@ -280,49 +437,74 @@ struct Carry {
     float* decay;  // exp(A * sum of delta over chunk k)
 };
 
-// Pass 1: per-chunk summaries (end state, decay product), all chunks but the
-// last. Chunk 0 starts from h0, so its end state is already exact.
-template <int N, int IO>
-__global__ __launch_bounds__(kWave) void chunk_summary_kernel(ScanArgs a, ChunkGrid g, Carry c) {
-    int64_t dblk, k, b;
-    decode_block(g, blockIdx.x, dblk, k, b);
-    // lanes past the last channel work on channel dim-1 (see scan_token)
-    const int64_t d0 = dblk * kWave;
-    const int64_t d = min(d0 + static_cast<int64_t>(threadIdx.x), a.dim - 1);
-    const int64_t t0 = k * g.chunk_len;
-    const int64_t t1 = min(a.seqlen, t0 + g.chunk_len);
-    const int ntok = static_cast<int>(t1 - t0);
+// Everything one wave needs to know about its place in the launch.
+struct WaveSlot {
+    int64_t b, k, d;   // batch row, chunk, this lane's channel (clamped)
+    int w;             // wave index inside the workgroup = state slice
+    int n0;            // first state of the slice
+    int ntok;          // tokens of the chunk
+    ChunkIo io;
+    BcIo bc;
+};
+
+template <int N, int S, int IO>
+__device__ __forceinline__ WaveSlot wave_slot(const ScanArgs& a, const ChunkGrid& g) {
     constexpr int64_t esz = IO == kIoF32 ? 4 : 2;
-    const int64_t first = (b * a.seqlen + t0) * a.dim + d0;  // element (b, t0, d0)
+    WaveSlot s;
+    int64_t dblk;
+    decode_block(g, blockIdx.x, dblk, s.k, s.b);
+    s.w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
+    s.n0 = s.w * Split<N, S>::NPW;
+    const int lane = threadIdx.x & (kWave - 1);
+    // lanes past the last channel work on channel dim-1 (see compute_tile)
+    const int64_t d0 = dblk * kWave;
+    s.d = min(d0 + lane, a.dim - 1);
+    const int64_t t0 = s.k * g.chunk_len;
+    const int64_t t1 = min(a.seqlen, t0 + g.chunk_len);
+    s.ntok = static_cast<int>(t1 - t0);
+    const int64_t first = (s.b * a.seqlen + t0) * a.dim + d0;  // element (b, t0, d0)
     // bytes from (b, t0, d0) to the end of (b, t1-1, dim-1); below 2^32 by the plan
     const uint32_t extent = static_cast<uint32_t>(((t1 - t0) * a.dim - d0) * esz);
-    ChunkIo io;
-    io.row_bytes = static_cast<uint32_t>(a.dim * esz);
-    io.lane_bytes = static_cast<uint32_t>((d - d0) * esz);
-    io.x = make_rsrc(static_cast<const char*>(a.x) + first * esz, extent);
-    io.delta = make_rsrc(static_cast<const char*>(a.delta) + first * esz, extent);
-    io.z = make_rsrc(a.z != nullptr ? static_cast<const char*>(a.z) + first * esz : nullptr, extent);
-    io.y = make_rsrc(static_cast<const char*>(a.y) + first * esz, extent);
-    const char* Bc = static_cast<const char*>(a.B) + (b * a.seqlen + t0) * N * esz;
-    const char* Cc = static_cast<const char*>(a.C) + (b * a.seqlen + t0) * N * esz;
+    s.io.row_bytes = static_cast<uint32_t>(a.dim * esz);
+    s.io.lane_bytes = static_cast<uint32_t>((s.d - d0) * esz);
+    s.io.x = make_rsrc(static_cast<const char*>(a.x) + first * esz, extent);
+    s.io.delta = make_rsrc(static_cast<const char*>(a.delta) + first * esz, extent);
+    s.io.z = make_rsrc(a.z != nullptr ? static_cast<const char*>(a.z) + first * esz : nullptr,
+                       extent);
+    s.io.y = make_rsrc(static_cast<const char*>(a.y) + first * esz, extent);
+    const int64_t bc0 = (s.b * a.seqlen + t0) * N * esz;  // B[b, t0, 0]
+    const uint32_t bc_extent = static_cast<uint32_t>((t1 - t0) * N * esz);
+    s.bc.B = make_rsrc(static_cast<const char*>(a.B) + bc0, bc_extent);
+    s.bc.C = make_rsrc(static_cast<const char*>(a.C) + bc0, bc_extent);
+    return s;
+}
 
-    float A2[N], h[N];
-    const int64_t srow = ((k * a.batch + b) * a.dim + d) * N;
+// Pass 1: per-chunk summaries (end state, decay product), all chunks but the
+// last. Chunk 0 starts from h0, so its end state is already exact.
+template <int N, int S, int IO>
+__global__ __launch_bounds__(kWave * S) __attribute__((amdgpu_waves_per_eu(S == 1 ? 4 : 6)))
+void chunk_summary_kernel(ScanArgs a, ChunkGrid g, Carry c) {
+    constexpr int NPW = Split<N, S>::NPW;
+    const WaveSlot s = wave_slot<N, S, IO>(a, g);
+    float A2[NPW], h[NPW];
+    const int64_t srow = ((s.k * a.batch + s.b) * a.dim + s.d) * N + s.n0;
 #pragma unroll
-    for (int n = 0; n < N; ++n) {
-        A2[n] = a.A[d * N + n] * kLog2e;
-        h[n] = (k == 0 && a.h0 != nullptr) ? a.h0[(b * a.dim + d) * N + n] : 0.0f;
+    for (int q = 0; q < NPW; ++q) {
+        A2[q] = a.A[s.d * N + s.n0 + q] * kLog2e;
+        h[q] = (s.k == 0 && a.h0 != nullptr) ? a.h0[(s.b * a.dim + s.d) * N + s.n0 + q] : 0.0f;
     }
-    if (k == 0) {
+    if (s.k == 0) {
 #pragma unroll
-        for (int n = 0; n < N; ++n) c.start[srow + n] = h[n];
+        for (int q = 0; q < NPW; ++q) c.start[srow + q] = h[q];
     }
+    __shared__ float bcs[2 * 2 * BcStage<N, S>::kSlots];
     float dsum = 0.0f;
-    scan_chunk<N, IO, false, false, false>(io, Bc, Cc, ntok, A2, h, 0.0f, dsum);
+    scan_chunk<N, S, IO, false, false, false>(s.io, s.bc, s.ntok, s.w, s.n0, nullptr, bcs, A2, h,
+                                              0.0f, dsum);
 #pragma unroll
-    for (int n = 0; n < N; ++n) {
-        c.end[srow + n] = h[n];
-        c.decay[srow + n] = fast_exp2(A2[n] * dsum);
+    for (int q = 0; q < NPW; ++q) {
+        c.end[srow + q] = h[q];
+        c.decay[srow + q] = fast_exp2(A2[q] * dsum);
     }
 }
 
@@ -343,48 +525,32 @@ __global__ __launch_bounds__(256) void chunk_carry_kernel(int64_t columns, int64
 
 // Pass 2 (or the only pass when nchunks == 1): scan each chunk from its true
 // entering state and write y; the last chunk writes hL.
-template <int N, int IO, bool HAS_D, bool HAS_Z>
-__global__ __launch_bounds__(kWave) void chunk_output_kernel(ScanArgs a, ChunkGrid g, Carry c) {
-    int64_t dblk, k, b;
-    decode_block(g, blockIdx.x, dblk, k, b);
-    // lanes past the last channel work on channel dim-1 (see scan_token)
-    const int64_t d0 = dblk * kWave;
-    const int64_t d = min(d0 + static_cast<int64_t>(threadIdx.x), a.dim - 1);
-    const int64_t t0 = k * g.chunk_len;
-    const int64_t t1 = min(a.seqlen, t0 + g.chunk_len);
-    const int ntok = static_cast<int>(t1 - t0);
-    constexpr int64_t esz = IO == kIoF32 ? 4 : 2;
-    const int64_t first = (b * a.seqlen + t0) * a.dim + d0;  // element (b, t0, d0)
-    // bytes from (b, t0, d0) to the end of (b, t1-1, dim-1); below 2^32 by the plan
-    const uint32_t extent = static_cast<uint32_t>(((t1 - t0) * a.dim - d0) * esz);
-    ChunkIo io;
-    io.row_bytes = static_cast<uint32_t>(a.dim * esz);
-    io.lane_bytes = static_cast<uint32_t>((d - d0) * esz);
-    io.x = make_rsrc(static_cast<const char*>(a.x) + first * esz, extent);
-    io.delta = make_rsrc(static_cast<const char*>(a.delta) + first * esz, extent);
-    io.z = make_rsrc(a.z != nullptr ? static_cast<const char*>(a.z) + first * esz : nullptr, extent);
-    io.y = make_rsrc(static_cast<const char*>(a.y) + first * esz, extent);
-    const char* Bc = static_cast<const char*>(a.B) + (b * a.seqlen + t0) * N * esz;
-    const char* Cc = static_cast<const char*>(a.C) + (b * a.seqlen + t0) * N * esz;
-
-    float A2[N], h[N];
+template <int N, int S, int IO, bool HAS_D, bool HAS_Z>
+__global__ __launch_bounds__(kWave * S) __attribute__((amdgpu_waves_per_eu(S <= 2 ? 2 : 4)))
+void chunk_output_kernel(ScanArgs a, ChunkGrid g, Carry c) {
+    constexpr int NPW = Split<N, S>::NPW;
+    __shared__ float red[S > 1 ? 2 * S * TT * kWave : 1];
+    __shared__ float bcs[2 * 2 * BcStage<N, S>::kSlots];
+    const WaveSlot s = wave_slot<N, S, IO>(a, g);
+    float A2[NPW], h[NPW];
 #pragma unroll
-    for (int n = 0; n < N; ++n) A2[n] = a.A[d * N + n] * kLog2e;
+    for (int q = 0; q < NPW; ++q) A2[q] = a.A[s.d * N + s.n0 + q] * kLog2e;
     if (g.nchunks == 1) {
 #pragma unroll
-        for (int n = 0; n < N; ++n)
-            h[n] = a.h0 != nullptr ? a.h0[(b * a.dim + d) * N + n] : 0.0f;
+        for (int q = 0; q < NPW; ++q)
+            h[q] = a.h0 != nullptr ? a.h0[(s.b * a.dim + s.d) * N + s.n0 + q] : 0.0f;
     } else {
-        const int64_t srow = ((k * a.batch + b) * a.dim + d) * N;
+        const int64_t srow = ((s.k * a.batch + s.b) * a.dim + s.d) * N + s.n0;
 #pragma unroll
-        for (int n = 0; n < N; ++n) h[n] = c.start[srow + n];
+        for (int q = 0; q < NPW; ++q) h[q] = c.start[srow + q];
     }
-    const float dskip = HAS_D ? a.D[d] : 0.0f;
+    const float dskip = HAS_D ? a.D[s.d] : 0.0f;
     float dsum = 0.0f;
-    scan_chunk<N, IO, true, HAS_D, HAS_Z>(io, Bc, Cc, ntok, A2, h, dskip, dsum);
-    if (k == g.nchunks - 1 && a.hL != nullptr) {
+    scan_chunk<N, S, IO, true, HAS_D, HAS_Z>(s.io, s.bc, s.ntok, s.w, s.n0, red, bcs, A2, h,
+                                             dskip, dsum);
+    if (s.k == g.nchunks - 1 && a.hL != nullptr) {
 #pragma unroll
-        for (int n = 0; n < N; ++n) a.hL[(b * a.dim + d) * N + n] = h[n];
+        for (int q = 0; q < NPW; ++q) a.hL[(s.b * a.dim + s.d) * N + s.n0 + q] = h[q];
     }
 }
 
@@ -490,8 +656,8 @@ __global__ __launch_bounds__(256) void state_update_kernel(DecodeArgs a) {
 
 // ---------------------------------------------------------------------------
 // Host-side dispatch over the compile-time variants.
-template <int N, int IO>
-hipError_t launch_scan_n(const ScanArgs& a, const ScanPlan& plan, void* ws, hipStream_t s) {
+template <int N, int S, int IO>
+hipError_t launch_scan_ns(const ScanArgs& a, const ScanPlan& plan, void* ws, hipStream_t s) {
     ChunkGrid g;
     g.nblk_d = (a.dim + kWave - 1) / kWave;
     g.nchunks = plan.nchunks;
@@ -503,29 +669,43 @@ hipError_t launch_scan_n(const ScanArgs& a, const ScanPlan& plan, void* ws, hipS
         c.start = base;
         c.end = base + plan.nchunks * columns;
         c.decay = base + 2 * plan.nchunks * columns;
-        const int64_t blocks1 = g.nblk_d * (plan.nchunks - 1) * a.batch;
-        // pass 1 covers chunks 0 .. nchunks-2; its grid uses nchunks-1 as the
-        // chunk count so block indices map onto exactly those chunks
+        // Pass 1 covers chunks 0 .. nchunks-2: its grid describes nchunks-1
+        // chunks of the same length, so block indices map onto exactly those;
+        // the workspace rows keep the full nchunks stride through `columns`.
         ChunkGrid g1 = g;
         g1.nchunks = plan.nchunks - 1;
-        hipLaunchKernelGGL((chunk_summary_kernel<N, IO>), dim3(blocks1), dim3(kWave), 0, s, a, g1,
-                           c);
-        // g1 indexes chunks like g (k * chunk_len), only fewer of them; the
-        // workspace rows use the full nchunks stride through `columns`.
+        const int64_t blocks1 = g.nblk_d * g1.nchunks * a.batch;
+        hipLaunchKernelGGL((chunk_summary_kernel<N, S, IO>), dim3(blocks1), dim3(kWave * S), 0, s,
+                           a, g1, c);
         hipLaunchKernelGGL(chunk_carry_kernel, dim3(stride_blocks(columns)), dim3(256), 0, s,
                            columns, plan.nchunks, c);
     }
     const int64_t blocks = g.nblk_d * plan.nchunks * a.batch;
+    const dim3 grid(blocks), block(kWave * S);
     const bool has_d = a.D != nullptr, has_z = a.z != nullptr;
     if (has_d && has_z)
-        hipLaunchKernelGGL((chunk_output_kernel<N, IO, true, true>), dim3(blocks), dim3(kWave), 0, s, a, g, c);
+        hipLaunchKernelGGL((chunk_output_kernel<N, S, IO, true, true>), grid, block, 0, s, a, g, c);
     else if (has_d)
-        hipLaunchKernelGGL((chunk_output_kernel<N, IO, true, false>), dim3(blocks), dim3(kWave), 0, s, a, g, c);
+        hipLaunchKernelGGL((chunk_output_kernel<N, S, IO, true, false>), grid, block, 0, s, a, g, c);
     else if (has_z)
-        hipLaunchKernelGGL((chunk_output_kernel<N, IO, false, true>), dim3(blocks), dim3(kWave), 0, s, a, g, c);
+        hipLaunchKernelGGL((chunk_output_kernel<N, S, IO, false, true>), grid, block, 0, s, a, g, c);
     else
-        hipLaunchKernelGGL((chunk_output_kernel<N, IO, false, false>), dim3(blocks), dim3(kWave), 0, s, a, g, c);
+        hipLaunchKernelGGL((chunk_output_kernel<N, S, IO, false, false>), grid, block, 0, s, a, g, c);
     return hipGetLastError();
+}
+
+// The state split S is a compile-time parameter; every N supports S = 1 and
+// N = 16, 8 and 4 also support the splits that divide them (up to 8).
+template <int N, int IO>
+hipError_t launch_scan_n(const ScanArgs& a, const ScanPlan& plan, void* ws, hipStream_t s) {
+    switch (plan.state_split) {
+        case 1: return launch_scan_ns<N, 1, IO>(a, plan, ws, s);
+        case 2: if constexpr (N % 2 == 0 && (N == 4 || N == 8 || N == 16)) return launch_scan_ns<N, 2, IO>(a, plan, ws, s); break;
+        case 4: if constexpr (N % 4 == 0 && (N == 4 || N == 8 || N == 16)) return launch_scan_ns<N, 4, IO>(a, plan, ws, s); break;
+        case 8: if constexpr (N % 8 == 0 && (N == 8 || N == 16)) return launch_scan_ns<N, 8, IO>(a, plan, ws, s); break;
+        default: break;
+    }
+    return hipErrorInvalidValue;
 }
 
 template <int N, int IO>

@@ -47,19 +47,28 @@ P = ctypes.c_void_p(0x10000)
 PM = ctypes.c_void_p(0x10008)  # not 16-byte aligned
 
 
-def _scan(lib, batch=2, seqlen=8, dim=64, dstate=16, dtype=1, ptrs=None, chunk=0, ws=None,
+def _plan(chunk_len=0, split=0, reserved=0):
+    return ctypes.byref(ms.ScanPlan(chunk_len, split, reserved))
+
+
+def _scan(lib, batch=2, seqlen=8, dim=64, dstate=16, dtype=1, ptrs=None, plan=None, ws=None,
           wsb=0):
     p = dict(x=P, delta=P, A=P, B=P, C=P, D=None, z=None, h0=None, y=P, hL=None)
     p.update(ptrs or {})
     return lib.ssm_scan_fwd(batch, seqlen, dim, dstate, dtype, p["x"], p["delta"], p["A"], p["B"],
-                            p["C"], p["D"], p["z"], p["h0"], p["y"], p["hL"], chunk, ws, wsb, None)
+                            p["C"], p["D"], p["z"], p["h0"], p["y"], p["hL"], plan, ws, wsb, None)
 
 
 def test_scan_rejects_bad_shapes(lib):
     assert _scan(lib, batch=-1) == INVALID
     assert _scan(lib, seqlen=-3) == INVALID
     assert _scan(lib, dim=-1) == INVALID
-    assert _scan(lib, chunk=-8) == INVALID
+    assert _scan(lib, plan=_plan(chunk_len=-8, split=1)) == INVALID
+    assert _scan(lib, plan=_plan(chunk_len=8, split=1, reserved=1)) == INVALID
+    assert _scan(lib, plan=_plan(chunk_len=8, split=3)) == UNSUPPORTED
+    assert _scan(lib, plan=_plan(chunk_len=8, split=16)) == UNSUPPORTED
+    assert _scan(lib, dstate=4, plan=_plan(chunk_len=8, split=8)) == UNSUPPORTED
+    assert _scan(lib, dstate=12, plan=_plan(chunk_len=8, split=2)) == UNSUPPORTED
     assert _scan(lib, dtype=7) == INVALID
     assert _scan(lib, dstate=0) == UNSUPPORTED
     assert _scan(lib, dstate=17) == UNSUPPORTED
@@ -74,17 +83,26 @@ def test_scan_rejects_null_and_misaligned(lib):
 
 
 def test_scan_workspace_check(lib):
-    # a forced chunk length needs no device query; 2 chunks need scratch
+    # a fully forced plan needs no device query; 2 chunks need scratch
     need = ctypes.c_size_t(0)
-    assert lib.ssm_scan_fwd_workspace_size(2, 64, 64, 16, 1, 32, ctypes.byref(need)) == OK
+    got = ms.ScanPlan(0, 0, 0)
+    assert lib.ssm_scan_fwd_workspace_size(2, 64, 64, 16, 1, _plan(32, 4), ctypes.byref(got),
+                                           ctypes.byref(need)) == OK
     assert need.value == 3 * 2 * 2 * 64 * 16 * 4
-    assert _scan(lib, seqlen=64, chunk=32, ws=None, wsb=0) == WORKSPACE
-    assert _scan(lib, seqlen=64, chunk=32, ws=P, wsb=need.value - 4) == WORKSPACE
-    assert _scan(lib, seqlen=64, chunk=32, ws=PM, wsb=need.value) == MISALIGNED
-    # a single chunk needs none
-    assert lib.ssm_scan_fwd_workspace_size(2, 64, 64, 16, 1, 64, ctypes.byref(need)) == OK
-    assert need.value == 0
-    assert lib.ssm_scan_fwd_workspace_size(2, 64, 64, 16, 1, 32, None) == INVALID
+    assert (got.chunk_len, got.state_split) == (32, 4)
+    assert _scan(lib, seqlen=64, plan=_plan(32, 4), ws=None, wsb=0) == WORKSPACE
+    assert _scan(lib, seqlen=64, plan=_plan(32, 4), ws=P, wsb=need.value - 4) == WORKSPACE
+    assert _scan(lib, seqlen=64, plan=_plan(32, 4), ws=PM, wsb=need.value) == MISALIGNED
+    # one chunk needs none; a chunk longer than the sequence is one chunk
+    for cl in (64, 1000):
+        assert lib.ssm_scan_fwd_workspace_size(2, 64, 64, 16, 1, _plan(cl, 2), ctypes.byref(got),
+                                               ctypes.byref(need)) == OK
+        assert need.value == 0 and got.chunk_len == 64
+    assert lib.ssm_scan_fwd_workspace_size(2, 64, 64, 16, 1, _plan(32, 1), None, None) == INVALID
+    # a chunk of one channel group must span less than 4 GiB: the plan shortens it
+    assert lib.ssm_scan_fwd_workspace_size(1, 1 << 20, 1 << 14, 16, 0, _plan(1 << 20, 1),
+                                           ctypes.byref(got), ctypes.byref(need)) == OK
+    assert got.chunk_len * (1 << 14) * 4 < (1 << 32)
 
 
 def test_scan_empty_shapes_are_noops(lib):

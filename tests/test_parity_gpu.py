@@ -172,6 +172,37 @@ def test_forced_chunk_lengths(orc, chunk_len):
     _full_compare(orc, inp, y, hL, TOL["f32"], f"chunk_len {chunk_len}")
 
 
+SPLITS = [(16, s) for s in (1, 2, 4, 8)] + [(8, s) for s in (1, 2, 4, 8)] + \
+         [(4, s) for s in (1, 2, 4)]
+
+
+@pytest.mark.parametrize("dstate,split", SPLITS, ids=lambda v: str(v))
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_state_splits(orc, dstate, split, io):
+    # every division of a channel's states over waves, with and without
+    # sequence chunks, and a ragged last tile and channel group
+    inp = _case_inputs(2, 203, 100, dstate, io, seed=dstate * 10 + split)
+    yo, ho = orc.scan_fwd(**inp)
+    for chunk_len in (0, 24, 203):
+        _say(f"case N={dstate} split={split} chunk_len={chunk_len} {io}")
+        y, hL = _run(inp, chunk_len=chunk_len, state_split=split)
+        assert_close(y, yo, TOL[io], f"N={dstate} split={split} chunk={chunk_len} y")
+        assert_close(hL, ho, TOL[io], f"N={dstate} split={split} chunk={chunk_len} hL")
+
+
+def test_split_plan_choices_agree():
+    # different plans of one large scan agree closely with each other
+    w = W.WORKLOADS["mamba28b_layer"]
+    inp = W.generate_scan(w, device=DEV, batch=2, seqlen=512, dim=1024)
+    ref, href = _run(inp, chunk_len=512, state_split=1)
+    for split in (2, 4, 8):
+        for chunk_len in (64, 512):
+            _say(f"case plan agreement split={split} chunk_len={chunk_len}")
+            y, hL = _run(inp, chunk_len=chunk_len, state_split=split)
+            assert_close(y, ref.float(), TOL["bf16"], f"split {split} chunk {chunk_len} vs 1/512")
+            assert_close(hL, href, 1e-4, f"split {split} chunk {chunk_len} state")
+
+
 def test_optional_inputs(orc):
     base = _case_inputs(2, 50, 70, 16, "f32", seed=9)
     for drop in (("z",), ("D",), ("h0",), ("z", "D", "h0")):
