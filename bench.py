@@ -39,9 +39,17 @@ def parse():
     p.add_argument("--workload", default="mamba28b_layer")
     p.add_argument("--chunk-len", type=int, default=0, help="0 = the library's automatic plan")
     p.add_argument("--state-split", type=int, default=0, help="0 = the library's automatic plan")
+    p.add_argument("--batch", type=int, default=0, help="override the workload's batch (0 = keep)")
+    p.add_argument("--dim", type=int, default=0, help="override the workload's channels (0 = keep)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-channels", type=int, default=0,
                    help="channels of the CPU-baseline sample (0 = sized to ~10 s)")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="run only a plain 1 GiB device-to-device copy, for counter calibration")
+    p.add_argument("--record-traffic", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV",
+                                                         "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                   help="turn rocprofv3 FETCH_SIZE/WRITE_SIZE counter CSVs of the scan and of "
+                        "the calibration copy into profiles/traffic_<workload>.json")
     return p.parse_args()
 
 
@@ -69,8 +77,82 @@ def algorithmic_alu_ops(w):
     return per_elem * w.batch * w.seqlen * w.dim
 
 
+COPY_BYTES = 1 << 30
+DOMINANT = "chunk_output_kernel"
+KERNEL_SOURCE = os.path.join(ROOT, "selective_state_space_40_amd", "csrc", "scan_kernels.hip")
+
+
+def source_hash():
+    import hashlib
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_path(workload):
+    return os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+
+
+def _counter_per_dispatch(csv_path, name, kernel_substr):
+    import csv
+    vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(csv_path))
+            if r["Counter_Name"] == name and kernel_substr in r["Kernel_Name"]]
+    if not vals:
+        raise SystemExit(f"no {name} rows for kernels matching {kernel_substr!r} in {csv_path}")
+    vals.sort()
+    return vals[len(vals) // 2]
+
+
+def record_traffic(args):
+    """HBM bytes per launch of the dominant kernel from FETCH_SIZE and
+    WRITE_SIZE (KiB per dispatch), each scaled by what the same counter reads
+    for a plain copy of COPY_BYTES (read COPY_BYTES, write COPY_BYTES)."""
+    fetch_csv, write_csv, cfetch_csv, cwrite_csv = args.record_traffic
+    fetch = _counter_per_dispatch(fetch_csv, "FETCH_SIZE", DOMINANT)
+    write = _counter_per_dispatch(write_csv, "WRITE_SIZE", DOMINANT)
+    cfetch = _counter_per_dispatch(cfetch_csv, "FETCH_SIZE", "copy")
+    cwrite = _counter_per_dispatch(cwrite_csv, "WRITE_SIZE", "copy")
+    fetch_scale = COPY_BYTES / cfetch
+    write_scale = COPY_BYTES / cwrite
+    out = {"workload": args.workload, "kernel": DOMINANT, "source_sha256_16": source_hash(),
+           "fetch_bytes": fetch * fetch_scale, "write_bytes": write * write_scale,
+           "traffic_bytes": fetch * fetch_scale + write * write_scale,
+           "fetch_kib_raw": fetch, "write_kib_raw": write,
+           "copy_fetch_kib_raw": cfetch, "copy_write_kib_raw": cwrite,
+           "fetch_scale": fetch_scale, "write_scale": write_scale}
+    with open(traffic_path(args.workload), "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
+
+
+def calibrate_copy():
+    import torch
+    dev = torch.device("cuda:0")
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration_copy_bytes": COPY_BYTES, "launches": 3}))
+
+
+def recorded_traffic(workload):
+    """Measured HBM bytes per launch, or None when not recorded or recorded
+    for a different kernel source."""
+    try:
+        with open(traffic_path(workload)) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256_16") != source_hash():
+        return None
+    return rec.get("traffic_bytes")
+
+
 def main():
     args = parse()
+    if args.record_traffic:
+        record_traffic(args)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path "
               f"(asked for --gpus {args.gpus})", file=sys.stderr)
@@ -82,8 +164,17 @@ def main():
     import selective_state_space_40_amd as ms
     import ssm_workloads as W
 
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     w = W.WORKLOADS[args.workload]
-    assert w.kind == "scan", "bench.py times scan workloads"
+    if w.kind == "decode":
+        bench_decode(args, w)
+        return
+    if args.batch or args.dim:
+        import dataclasses
+        w = dataclasses.replace(w, batch=args.batch or w.batch, dim=args.dim or w.dim,
+                                name=f"{w.name} resized")
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     ms.load_library()
@@ -129,20 +220,24 @@ def main():
     ops = algorithmic_alu_ops(w)
     tops = ops / sec / 1e12
 
-    # Dominant kernel: the output pass. With a single chunk the step is that
-    # one kernel; otherwise the step also holds the summary and carry passes
-    # and the figure below is the whole step, a lower bound for the kernel.
+    # Dominant kernel: the output pass (chunk_output_kernel). With a single
+    # chunk the step is exactly that one launch, so the event time per step
+    # is its launch duration; with several chunks the step also holds the
+    # summary and carry passes and the figure covers the whole step.
     hbm_frac = gbps / HBM_PEAK_GBPS
     alu_frac = tops / ALU_PEAK_TOPS
     bound = "alu" if ops / (ALU_PEAK_TOPS * 1e12) > bytes_alg / (HBM_PEAK_GBPS * 1e9) else "hbm"
+    traffic = recorded_traffic(w.name) if nchunks == 1 and not (args.batch or args.dim) else None
     roofline = {
         "bound": bound,
         "achieved": round(tops if bound == "alu" else gbps, 3),
         "peak": ALU_PEAK_TOPS if bound == "alu" else HBM_PEAK_GBPS,
         "unit": "Tops/s (fp32 lane-ops)" if bound == "alu" else "GB/s",
         "frac": round(alu_frac if bound == "alu" else hbm_frac, 4),
-        "traffic": None,
-        "kernel": "chunk_output_kernel" if nchunks == 1 else "ssm_scan_fwd step (all passes)",
+        "traffic": traffic,
+        "kernel": DOMINANT if nchunks == 1 else "ssm_scan_fwd step (all passes)",
+        "algorithmic_bytes": bytes_alg,
+        "algorithmic_ops": ops,
         "hbm_GBps": round(gbps, 1),
         "hbm_frac": round(hbm_frac, 4),
     }
@@ -172,6 +267,79 @@ def main():
         "wall_s": round(wall, 4),
         "roofline": roofline,
         "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def decode_bytes(w):
+    """Bytes one decode step must move per layer: the fp32 state read and
+    written, x, delta, z in and y out, B and C in, A and D in."""
+    s = 4 if w.io == "f32" else 2
+    b, d, n = w.batch, w.dim, w.dstate
+    return 2 * b * d * n * 4 + 4 * b * d * s + 2 * b * n * s + d * n * 4 + d * 4
+
+
+def bench_decode(args, w):
+    """One step = one ssm_state_update per layer over all layers (each layer
+    with its own state and inputs), replayed as a HIP graph so the launch
+    rate of the host does not bound the timing."""
+    import torch
+
+    import selective_state_space_40_amd as ms
+    import ssm_workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    ms.load_library()
+    layers = [{k: v.to(dev) for k, v in W.generate_decode_layer(w, l).items()}
+              for l in range(w.layers)]
+    ys = [torch.empty_like(L["x"]) for L in layers]
+
+    def step():
+        for L, y in zip(layers, ys):
+            ms.state_update(L["h"], L["x"], L["delta"], L["A"], L["B"], L["C"], L["D"], L["z"],
+                            out=y)
+
+    stream = torch.cuda.Stream(dev)
+    stream.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(stream):
+        step()  # warm the library and the allocator outside the capture
+    torch.cuda.current_stream(dev).wait_stream(stream)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    cur = torch.cuda.current_stream(dev)
+    t0 = time.perf_counter()
+    ev0.record(cur)
+    for _ in range(args.steps):
+        graph.replay()
+    ev1.record(cur)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    sec = ms_per_step / 1e3
+    elems = w.batch * w.dim * w.layers
+    bytes_step = decode_bytes(w) * w.layers
+    gbps = bytes_step / sec / 1e9
+    line = {
+        "metric": "decode state-update elements/s (batch*D*layers per step) and achieved HBM GB/s",
+        "value": elems / sec, "unit": "elements/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "dim": w.dim, "dstate": w.dstate,
+                   "layers": w.layers, "io_dtype": w.io, "parallelism": "single GPU"},
+        "achieved_GBps": round(gbps, 1), "wall_s": round(wall, 4),
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "state_update_kernel (64 launches per step, graph replay)",
+                     "algorithmic_bytes": bytes_step},
+        "cpu_baseline": None,
     }
     print(json.dumps(line), flush=True)
 
