@@ -12,8 +12,12 @@ namespace mamba {
 constexpr int kWave = 64;
 // Channels covered by one workgroup of the scan kernels (one wave).
 constexpr int kScanChannelsPerGroup = kWave;
-// Tokens fetched per register tile; chunk lengths are multiples of it.
-constexpr int kTokenTile = 8;
+// Tokens per register tile (the unit of prefetch and of the per-tile
+// barrier); automatic chunk lengths are multiples of it.
+#ifndef MAMBA_TOKEN_TILE
+#define MAMBA_TOKEN_TILE 8
+#endif
+constexpr int kTokenTile = MAMBA_TOKEN_TILE;
 
 enum IoType : int { kIoF32 = 0, kIoBF16 = 1 };
 

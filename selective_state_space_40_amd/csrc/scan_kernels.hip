@@ -231,54 +231,77 @@ __device__ __forceinline__ void read_slice(const float* row, float (&out)[NPW]) 
     }
 }
 
-// Register tile: x and delta of all TT tokens (every wave needs them), and
-// z and x of the TT/S tokens this wave finalises (tokens w, w+S, ...).
+// With S > 1 the per-token inputs reach the waves through LDS as well. Wave w
+// fetches x, delta and z only of the tokens it finalises (j = w, w+S, ... of
+// the tile), converts them once and stages (delta, delta*x) as fp32 pairs for
+// every wave to read; D*x and z of those tokens stay in its registers for its
+// own epilogue. Each (channel, token) is converted once, whatever S is, and a
+// wave holds only TT/S tokens of prefetched inputs in VGPRs. With S == 1 the
+// single wave keeps all TT tokens in registers and uses them directly.
 template <int S>
 struct Tile {
-    uint32_t x[TT], dt[TT];
-    uint32_t zown[TT / S], xown[TT / S];
+    uint32_t x[TT / S], dt[TT / S], z[TT / S];
 };
 
 // Token indices are clamped to the chunk, so the ragged last tile reads only
-// tokens that exist.
-template <int S, int IO, bool LOAD_Z, bool LOAD_XOWN>
+// tokens that exist (the clamped copies are never used).
+template <int S, int IO, bool LOAD_Z>
 __device__ __forceinline__ void fetch_tile(const ChunkIo& io, int tile, int w, int ntok,
                                            Tile<S>& r) {
-#pragma unroll
-    for (int j = 0; j < TT; ++j) {
-        const int tok = min(tile * TT + j, ntok - 1);
-        const uint32_t off = static_cast<uint32_t>(tok) * io.row_bytes;
-        r.x[j] = buf_load<IO>(io.x, io.lane_bytes, off);
-        r.dt[j] = buf_load<IO>(io.delta, io.lane_bytes, off);
-    }
 #pragma unroll
     for (int jj = 0; jj < TT / S; ++jj) {
         const int tok = min(tile * TT + jj * S + w, ntok - 1);
         const uint32_t off = static_cast<uint32_t>(tok) * io.row_bytes;
-        r.zown[jj] = LOAD_Z ? buf_load<IO>(io.z, io.lane_bytes, off) : 0u;
-        r.xown[jj] = LOAD_XOWN ? buf_load<IO>(io.x, io.lane_bytes, off) : 0u;
+        r.x[jj] = buf_load<IO>(io.x, io.lane_bytes, off);
+        r.dt[jj] = buf_load<IO>(io.delta, io.lane_bytes, off);
+        r.z[jj] = LOAD_Z ? buf_load<IO>(io.z, io.lane_bytes, off) : 0u;
+    }
+}
+
+// LDS layout of the staged per-token inputs: [token j][lane] float2 (delta,
+// delta*x). Writes the wave's own tokens and returns D*x of them.
+template <int S, int IO, bool HAS_D>
+__device__ __forceinline__ void stage_tokens(float2* dtdu, int w, const Tile<S>& r, float dskip,
+                                             float (&skip)[TT / S]) {
+    const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+    for (int jj = 0; jj < TT / S; ++jj) {
+        const float dt = raw_to_f32<IO>(r.dt[jj]);
+        const float u = raw_to_f32<IO>(r.x[jj]);
+        dtdu[(jj * S + w) * kWave + lane] = make_float2(dt, dt * u);
+        skip[jj] = HAS_D ? dskip * u : 0.0f;
     }
 }
 
 // The state update of tokens tile*TT + [0, cnt) for this wave's states
-// (FULL: cnt == TT, compiled without per-token branches). With OUTPUT the
-// readout over the wave's states is kept per token in part[] (and with
-// S == 1 the token is finished and stored right away); without it the sum
-// of delta over the tokens accumulates in dsum.
+// (FULL: cnt == TT, compiled without per-token branches). With S > 1 the
+// per-token inputs come from LDS and the readout over the wave's states is
+// kept per token in part[]; with S == 1 the wave holds every state, takes
+// its inputs straight from its registers and finishes and stores each token
+// right away. Without OUTPUT the sum of delta accumulates in dsum.
 template <int N, int S, int IO, bool OUTPUT, bool HAS_D, bool HAS_Z, bool FULL>
-__device__ __forceinline__ void compute_tile(const ChunkIo& io, const float* bcs_w, int tile,
-                                             int cnt, const Tile<S>& r,
-                                             const float (&A2)[Split<N, S>::NPW],
+__device__ __forceinline__ void compute_tile(const ChunkIo& io, const float* bcs_w,
+                                             const float2* dtdu, const Tile<S>& r, int tile,
+                                             int cnt, const float (&A2)[Split<N, S>::NPW],
                                              float (&h)[Split<N, S>::NPW], float dskip,
                                              float (&part)[TT], float& dsum) {
     constexpr int NPW = Split<N, S>::NPW;
     constexpr int P = BcStage<N, S>::kSlots;
+    const int lane = threadIdx.x & (kWave - 1);
 #pragma unroll
     for (int j = 0; j < TT; ++j) {
         part[j] = 0.0f;
         if (FULL || j < cnt) {
-            const float dt = raw_to_f32<IO>(r.dt[j]);
-            const float du = dt * raw_to_f32<IO>(r.x[j]);
+            float dt, du, u = 0.0f;
+            if constexpr (S == 1) {
+                dt = raw_to_f32<IO>(r.dt[j]);
+                u = raw_to_f32<IO>(r.x[j]);
+                du = dt * u;
+            } else {
+                const float2 v = dtdu[j * kWave + lane];
+                dt = v.x;
+                du = v.y;
+            }
             float Bv[NPW];
             read_slice<NPW>(bcs_w + j * N, Bv);
             if constexpr (OUTPUT) {
@@ -292,9 +315,8 @@ __device__ __forceinline__ void compute_tile(const ChunkIo& io, const float* bcs
                     p = fmaf(Cv[k], h[k], p);
                 }
                 if constexpr (S == 1) {
-                    // one wave holds every state: finish the token right here
-                    if constexpr (HAS_D) p = fmaf(dskip, raw_to_f32<IO>(r.x[j]), p);
-                    if constexpr (HAS_Z) p *= silu(raw_to_f32<IO>(r.zown[j]));
+                    if constexpr (HAS_D) p = fmaf(dskip, u, p);
+                    if constexpr (HAS_Z) p *= silu(raw_to_f32<IO>(r.z[j]));
                     // Lanes past the last channel were clamped onto channel
                     // dim-1 and computed its value bit for bit, so they store
                     // the same bits to the same address; no lane mask needed.
@@ -317,9 +339,10 @@ __device__ __forceinline__ void compute_tile(const ChunkIo& io, const float* bcs
 // Wave w finishes its tokens j = w, w+S, ... of the tile: the S partial
 // readouts summed in a fixed wave order, the skip term, the gate, rounding
 // and the store.
-template <int S, int IO, bool HAS_D, bool HAS_Z, bool FULL>
+template <int S, int IO, bool HAS_Z, bool FULL>
 __device__ __forceinline__ void finalize_tile(const ChunkIo& io, const float* red_tile, int w,
-                                              int tile, int cnt, const Tile<S>& r, float dskip) {
+                                              int tile, int cnt, const Tile<S>& r,
+                                              const float (&skip)[TT / S]) {
     const int lane = threadIdx.x & (kWave - 1);
 #pragma unroll
     for (int jj = 0; jj < TT / S; ++jj) {
@@ -329,90 +352,101 @@ __device__ __forceinline__ void finalize_tile(const ChunkIo& io, const float* re
             float acc = col[0];
 #pragma unroll
             for (int v = 1; v < S; ++v) acc += col[v * TT * kWave];
-            if constexpr (HAS_D) acc = fmaf(dskip, raw_to_f32<IO>(r.xown[jj]), acc);
-            if constexpr (HAS_Z) acc *= silu(raw_to_f32<IO>(r.zown[jj]));
-            // lanes past the last channel store the bits of channel dim-1
+            acc += skip[jj];
+            if constexpr (HAS_Z) acc *= silu(raw_to_f32<IO>(r.z[jj]));
+            // Lanes past the last channel were clamped onto channel dim-1 and
+            // computed its value bit for bit, so they store the same bits to
+            // the same address; the store needs no lane mask.
             buf_store<IO>(io.y, io.lane_bytes, static_cast<uint32_t>(tile * TT + j) * io.row_bytes,
                           acc);
         }
     }
 }
 
+// LDS of one workgroup: B/C tiles, per-token inputs and partial readouts,
+// each double-buffered by tile parity.
+template <int N, int S>
+struct ScanLds {
+    float bcs[2][2 * BcStage<N, S>::kSlots];
+    float2 dtdu[2][S > 1 ? TT * kWave : 1];
+    float red[2][S > 1 ? S * TT * kWave : 1];
+};
+
 // All `ntok` tokens of one chunk for one wave. Two register tiles alternate:
-// while one tile is computed the next one (x, delta, z, and the raw B/C run)
-// is already in flight, and the tiles swap roles without register copies.
-// Fetches are unconditional and clamp their tokens to the chunk (past the
-// last tile they re-read it, and the values go unused), and the full tiles
-// run in pairs inside a loop with a single exit, so every path into a compute
-// step has the same loads in flight and the waits before it stay exact. A
-// ragged last tile runs once after the loop.
+// while one tile is computed the next one (this wave's x, delta, z and its
+// share of the raw B/C run) is already in flight, and the tiles swap roles
+// without register copies. Fetches are unconditional and clamp their tokens
+// to the chunk, and the full tiles run in pairs inside a loop with a single
+// exit, so every path into a compute step has the same loads in flight and
+// the waits before it stay exact. A ragged last tile runs once after the loop.
 //
-// Per tile, in order: fetch tile i+1; compute tile i from LDS buffer i&1;
-// [S > 1: store the partial readouts]; stage tile i+1's B/C into LDS buffer
-// (i+1)&1; barrier; [S > 1: finalise this wave's tokens of tile i]. Every
-// LDS buffer is rewritten only after a barrier that follows its last read.
+// Per tile, in order: fetch tile i+1; compute tile i from LDS buffers i&1
+// and store the partial readouts; stage tile i+1's B/C and per-token inputs
+// into LDS buffers (i+1)&1; barrier; finalise this wave's tokens of tile i.
+// Every LDS buffer is rewritten only after a barrier that follows its last
+// read.
 template <int N, int S, int IO, bool OUTPUT, bool HAS_D, bool HAS_Z>
 __device__ __forceinline__ void scan_chunk(const ChunkIo& io, const BcIo& bcio, int ntok, int w,
-                                           int n0, float* red, float* bcs,
+                                           int n0, ScanLds<N, S>& lds,
                                            const float (&A2)[Split<N, S>::NPW],
                                            float (&h)[Split<N, S>::NPW], float dskip,
                                            float& dsum) {
     constexpr bool LOAD_Z = OUTPUT && HAS_Z;
-    constexpr bool LOAD_XOWN = OUTPUT && HAS_D && S > 1;
     constexpr int KP = BcStage<N, S>::kPerLane;
-    constexpr int P = BcStage<N, S>::kSlots;
     const int ntiles = (ntok + TT - 1) / TT;
     const int nfull = ntok / TT;
     const int lane = threadIdx.x & (kWave - 1);
     Tile<S> ta, tb;
+    float ska[TT / S], skb[TT / S];
     uint32_t bra[KP], cra[KP];
 
-    auto step = [&](auto full_tag, int i, const Tile<S>& cur, Tile<S>& nxt) {
+    auto step = [&](auto full_tag, int i, const Tile<S>& cur, const float (&skc)[TT / S],
+                    Tile<S>& nxt, float (&skn)[TT / S]) {
         constexpr bool FULL = decltype(full_tag)::value;
         const int inext = min(i + 1, ntiles - 1);
         // The B/C run is issued first and kept first (scheduling fences), so
         // staging it at the end of this step waits only for loads older than
-        // the x/delta/z of the next tile, which stay in flight.
+        // the next tile's token inputs, which stay in flight a little longer.
         fetch_bc<N, S, IO>(bcio, inext, min(TT, ntok - inext * TT), bra, cra);
         __builtin_amdgcn_sched_barrier(0);
-        fetch_tile<S, IO, LOAD_Z, LOAD_XOWN>(io, inext, w, ntok, nxt);
+        fetch_tile<S, IO, LOAD_Z>(io, inext, w, ntok, nxt);
         __builtin_amdgcn_sched_barrier(0);
         const int cnt = FULL ? TT : ntok - i * TT;
-        const float* bcs_w = bcs + (i & 1) * 2 * P + n0;
-        float* red_tile = red + (i & 1) * S * TT * kWave;
         float part[TT];
-        compute_tile<N, S, IO, OUTPUT, HAS_D, HAS_Z, FULL>(io, bcs_w, i, cnt, cur, A2, h, dskip,
-                                                           part, dsum);
+        compute_tile<N, S, IO, OUTPUT, HAS_D, HAS_Z, FULL>(io, lds.bcs[i & 1] + n0,
+                                                           lds.dtdu[i & 1], cur, i, cnt, A2, h,
+                                                           dskip, part, dsum);
         if constexpr (OUTPUT && S > 1) {
-            // the skip term D*x of token j is added by the wave that finalises
-            // j, in finalize_tile, from its own copy of x_j
-            float* mine = red_tile + w * TT * kWave + lane;
+            float* mine = lds.red[i & 1] + w * TT * kWave + lane;
 #pragma unroll
             for (int j = 0; j < TT; ++j) mine[j * kWave] = part[j];
         }
-        stage_bc<N, S, IO>(bcs + ((i + 1) & 1) * 2 * P, bra, cra);
+        stage_bc<N, S, IO>(lds.bcs[(i + 1) & 1], bra, cra);
+        if constexpr (S > 1)
+            stage_tokens<S, IO, OUTPUT && HAS_D>(lds.dtdu[(i + 1) & 1], w, nxt, dskip, skn);
         __syncthreads();
         if constexpr (OUTPUT && S > 1)
-            finalize_tile<S, IO, HAS_D, HAS_Z, FULL>(io, red_tile, w, i, cnt, cur, dskip);
+            finalize_tile<S, IO, HAS_Z, FULL>(io, lds.red[i & 1], w, i, cnt, cur, skc);
     };
     using Full = std::integral_constant<bool, true>;
     using Ragged = std::integral_constant<bool, false>;
 
-    // prologue: tile 0's B/C into LDS buffer 0, tile 0's x/delta/z into regs
+    // prologue: tile 0's B/C and token inputs into LDS buffers 0
     fetch_bc<N, S, IO>(bcio, 0, min(TT, ntok), bra, cra);
-    fetch_tile<S, IO, LOAD_Z, LOAD_XOWN>(io, 0, w, ntok, ta);
-    stage_bc<N, S, IO>(bcs, bra, cra);
+    fetch_tile<S, IO, LOAD_Z>(io, 0, w, ntok, ta);
+    stage_bc<N, S, IO>(lds.bcs[0], bra, cra);
+    if constexpr (S > 1) stage_tokens<S, IO, OUTPUT && HAS_D>(lds.dtdu[0], w, ta, dskip, ska);
     __syncthreads();
     int i = 0;
     for (; i + 2 <= nfull; i += 2) {
-        step(Full{}, i, ta, tb);
-        step(Full{}, i + 1, tb, ta);
+        step(Full{}, i, ta, ska, tb, skb);
+        step(Full{}, i + 1, tb, skb, ta, ska);
     }
     if (i < nfull) {
-        step(Full{}, i, ta, tb);
-        if (nfull < ntiles) step(Ragged{}, i + 1, tb, ta);
+        step(Full{}, i, ta, ska, tb, skb);
+        if (nfull < ntiles) step(Ragged{}, i + 1, tb, skb, ta, ska);
     } else if (nfull < ntiles) {
-        step(Ragged{}, i, ta, tb);
+        step(Ragged{}, i, ta, ska, tb, skb);
     }
 }
 
@@ -497,10 +531,10 @@ void chunk_summary_kernel(ScanArgs a, ChunkGrid g, Carry c) {
 #pragma unroll
         for (int q = 0; q < NPW; ++q) c.start[srow + q] = h[q];
     }
-    __shared__ float bcs[2 * 2 * BcStage<N, S>::kSlots];
+    __shared__ ScanLds<N, S> lds;
     float dsum = 0.0f;
-    scan_chunk<N, S, IO, false, false, false>(s.io, s.bc, s.ntok, s.w, s.n0, nullptr, bcs, A2, h,
-                                              0.0f, dsum);
+    scan_chunk<N, S, IO, false, false, false>(s.io, s.bc, s.ntok, s.w, s.n0, lds, A2, h, 0.0f,
+                                              dsum);
 #pragma unroll
     for (int q = 0; q < NPW; ++q) {
         c.end[srow + q] = h[q];
@@ -529,8 +563,7 @@ template <int N, int S, int IO, bool HAS_D, bool HAS_Z>
 __global__ __launch_bounds__(kWave * S) __attribute__((amdgpu_waves_per_eu(S <= 2 ? 2 : 4)))
 void chunk_output_kernel(ScanArgs a, ChunkGrid g, Carry c) {
     constexpr int NPW = Split<N, S>::NPW;
-    __shared__ float red[S > 1 ? 2 * S * TT * kWave : 1];
-    __shared__ float bcs[2 * 2 * BcStage<N, S>::kSlots];
+    __shared__ ScanLds<N, S> lds;
     const WaveSlot s = wave_slot<N, S, IO>(a, g);
     float A2[NPW], h[NPW];
 #pragma unroll
@@ -546,8 +579,8 @@ void chunk_output_kernel(ScanArgs a, ChunkGrid g, Carry c) {
     }
     const float dskip = HAS_D ? a.D[s.d] : 0.0f;
     float dsum = 0.0f;
-    scan_chunk<N, S, IO, true, HAS_D, HAS_Z>(s.io, s.bc, s.ntok, s.w, s.n0, red, bcs, A2, h,
-                                             dskip, dsum);
+    scan_chunk<N, S, IO, true, HAS_D, HAS_Z>(s.io, s.bc, s.ntok, s.w, s.n0, lds, A2, h, dskip,
+                                             dsum);
     if (s.k == g.nchunks - 1 && a.hL != nullptr) {
 #pragma unroll
         for (int q = 0; q < NPW; ++q) a.hL[(s.b * a.dim + s.d) * N + s.n0 + q] = h[q];
