@@ -32,9 +32,10 @@ def _load(path=None):
     lib = ctypes.CDLL(path)
     dp = ctypes.POINTER(ctypes.c_double)
     i64 = ctypes.c_int64
-    lib.oracle_scan_fwd.argtypes = [i64, i64, i64, i64] + [dp] * 10 + [ctypes.c_int]
+    lib.oracle_scan_fwd.argtypes = [i64, i64, i64, i64] + [dp] * 10 + [ctypes.c_int, dp,
+                                                                       ctypes.c_int]
     lib.oracle_scan_fwd.restype = ctypes.c_int
-    lib.oracle_state_update.argtypes = [i64, i64, i64] + [dp] * 9
+    lib.oracle_state_update.argtypes = [i64, i64, i64] + [dp] * 9 + [dp, ctypes.c_int]
     lib.oracle_state_update.restype = ctypes.c_int
     lib.oracle_max_dstate.restype = ctypes.c_int
     return lib
@@ -64,15 +65,16 @@ class Oracle:
         self.max_dstate = self.lib.oracle_max_dstate()
 
     def scan_fwd(self, x, delta, A, B, C, D=None, z=None, h0=None, zoh=False,
-                 return_state=True):
+                 return_state=True, delta_bias=None, delta_softplus=False):
         """Scan a whole sequence.
 
         Shapes: x, delta, z (batch, L, dim); A (dim, N); B, C (batch, L, N);
-        D (dim,); h0 (batch, dim, N). Returns (y, hL) as fp64 numpy arrays,
-        y of shape (batch, L, dim) and hL of shape (batch, dim, N).
+        D, delta_bias (dim,); h0 (batch, dim, N). With delta_softplus the
+        delta used is softplus(delta + delta_bias). Returns (y, hL) as fp64
+        numpy arrays, y of shape (batch, L, dim) and hL of shape (batch, dim, N).
         """
         x, delta, A, B, C = (_f64(v) for v in (x, delta, A, B, C))
-        D, z, h0 = _f64(D), _f64(z), _f64(h0)
+        D, z, h0, bias = _f64(D), _f64(z), _f64(h0), _f64(delta_bias)
         batch, seqlen, dim = x.shape
         dstate = A.shape[1]
         assert delta.shape == x.shape and A.shape == (dim, dstate)
@@ -80,27 +82,31 @@ class Oracle:
         assert D is None or D.shape == (dim,)
         assert z is None or z.shape == x.shape
         assert h0 is None or h0.shape == (batch, dim, dstate)
+        assert bias is None or bias.shape == (dim,)
         y = np.zeros((batch, seqlen, dim), dtype=np.float64)
         hL = np.zeros((batch, dim, dstate), dtype=np.float64) if return_state else None
         rc = self.lib.oracle_scan_fwd(batch, seqlen, dim, dstate, _ptr(x), _ptr(delta),
                                       _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
-                                      _ptr(h0), _ptr(y), _ptr(hL), int(bool(zoh)))
+                                      _ptr(h0), _ptr(y), _ptr(hL), int(bool(zoh)), _ptr(bias),
+                                      int(bool(delta_softplus)))
         if rc != 0:
             raise ValueError(f"oracle_scan_fwd rejected its arguments (status {rc})")
         return y, hL
 
-    def state_update(self, h, x, delta, A, B, C, D=None, z=None):
+    def state_update(self, h, x, delta, A, B, C, D=None, z=None, delta_bias=None,
+                     delta_softplus=False):
         """One decode step. Shapes: h (batch, dim, N); x, delta, z (batch, dim);
         B, C (batch, N). Returns (y, h_new); the input h is not modified."""
         h = _f64(h).copy()
         x, delta, A, B, C = (_f64(v) for v in (x, delta, A, B, C))
-        D, z = _f64(D), _f64(z)
+        D, z, bias = _f64(D), _f64(z), _f64(delta_bias)
         batch, dim, dstate = h.shape
         assert x.shape == (batch, dim) and delta.shape == x.shape
         assert A.shape == (dim, dstate) and B.shape == (batch, dstate) and C.shape == B.shape
         y = np.zeros((batch, dim), dtype=np.float64)
         rc = self.lib.oracle_state_update(batch, dim, dstate, _ptr(h), _ptr(x), _ptr(delta),
-                                          _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(y))
+                                          _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(y),
+                                          _ptr(bias), int(bool(delta_softplus)))
         if rc != 0:
             raise ValueError(f"oracle_state_update rejected its arguments (status {rc})")
         return y, h

@@ -22,12 +22,17 @@
  *     the paper's Theorem 1 (section "Chosen by the Token");
  *   - the skip term D*x is added to C*h before the output gate, and the gate
  *     multiplies by silu(z) = z / (1 + exp(-z));
- *   - one B and one C per (batch, token), shared by all channels.
+ *   - one B and one C per (batch, token), shared by all channels;
+ *   - optionally delta arrives before its activation: a per-channel bias is
+ *     added and softplus(v) = log(1 + exp(v)) applied (the pages say delta
+ *     comes from a projection of the token and must be positive; softplus is
+ *     the activation the workloads use to make it so).
  *
  * Layout (row-major): x, delta, z, y are (batch, L, dim) with dim contiguous;
- * B and C are (batch, L, dstate); A is (dim, dstate); Dskip is (dim);
- * h0 and hL are (batch, dim, dstate). Every array is fp64. Dskip, z, h0 and
- * hL may be NULL (no skip, no gate, zero initial state, no final state).
+ * B and C are (batch, L, dstate); A is (dim, dstate); Dskip and delta_bias
+ * are (dim); h0 and hL are (batch, dim, dstate). Every array is fp64. Dskip,
+ * z, h0, hL and delta_bias may be NULL (no skip, no gate, zero initial
+ * state, no final state, no bias).
  *
  * Nothing is blocked, fused or reordered: for each (batch, channel) the loop
  * runs token by token and state by state, exactly as the recurrence is
@@ -43,11 +48,17 @@
 /* Status codes: 0 ok, -1 invalid argument. */
 int oracle_max_dstate(void) { return ORACLE_MAX_DSTATE; }
 
+/* softplus(v) = log(1 + exp(v)), written so exp never overflows */
+static double softplus(double v)
+{
+    return v > 0.0 ? v + log1p(exp(-v)) : log1p(exp(v));
+}
+
 int oracle_scan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
                     const double* x, const double* delta, const double* A,
                     const double* Bm, const double* Cm, const double* Dskip,
                     const double* z, const double* h0, double* y, double* hL,
-                    int zoh)
+                    int zoh, const double* delta_bias, int delta_softplus)
 {
     if (batch < 0 || seqlen < 0 || dim < 0 || dstate < 1 || dstate > ORACLE_MAX_DSTATE)
         return -1;
@@ -66,8 +77,10 @@ int oracle_scan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
             for (int64_t t = 0; t < seqlen; ++t) {
                 const int64_t i_tok = (b * seqlen + t) * dim + d;  /* (b, t, d) */
                 const int64_t i_bc = (b * seqlen + t) * dstate;    /* (b, t, 0) */
-                const double dt = delta[i_tok];
+                double dt = delta[i_tok];
                 const double u = x[i_tok];
+                if (delta_bias) dt += delta_bias[d];
+                if (delta_softplus) dt = softplus(dt);
 
                 /* h <- Abar*h + Bbar*x, then read out y = C*h */
                 double out = 0.0;
@@ -103,9 +116,10 @@ int oracle_scan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
 int oracle_state_update(int64_t batch, int64_t dim, int64_t dstate, double* h,
                         const double* x, const double* delta, const double* A,
                         const double* Bm, const double* Cm, const double* Dskip,
-                        const double* z, double* y)
+                        const double* z, double* y, const double* delta_bias,
+                        int delta_softplus)
 {
     if (!h) return -1;
     return oracle_scan_fwd(batch, 1, dim, dstate, x, delta, A, Bm, Cm, Dskip, z,
-                           h, y, h, 0);
+                           h, y, h, 0, delta_bias, delta_softplus);
 }

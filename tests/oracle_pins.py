@@ -27,6 +27,10 @@ when it disagrees with an independent statement of the result:
   contribution D*x*silu(z), channel permutation and batch independence.
 - pin_decode: the single-token update equals the scan over one token, and
   T updates equal the scan over T tokens (section "Taken Apart").
+- pin_delta_activation: delta given before its activation. With one state,
+  A ~ 0 and x = B = C = 1 the first output is delta itself, which must equal
+  softplus(delta_raw + bias) as numpy's logaddexp(0, .) computes it; and the
+  Theorem 1 gate identity holds with the softplus applied inside the scan.
 
 silu(z) = z * sigmoid(z) is evaluated with scipy's logistic function.
 """
@@ -245,5 +249,47 @@ def pin_decode(orc, seed=18):
     assert np.array_equal(h, hL), "decode state after T steps differs from the scan"
 
 
+def pin_delta_activation(orc, seed=19):
+    rng = np.random.default_rng(seed)
+    batch, dim = 40, 7
+    u = np.concatenate([rng.uniform(-60.0, 60.0, (batch - 8, 1, dim)),
+                        np.array([-800.0, -40.0, -1.0, 0.0, 1e-9, 1.0, 40.0, 800.0])
+                        .reshape(8, 1, 1).repeat(dim, axis=2)])
+    bias = rng.uniform(-3.0, 3.0, dim)
+    ones = np.ones((batch, 1, 1))
+    A = -np.full((dim, 1), 1e-300)
+    for softplus in (True, False):
+        y, hL = orc.scan_fwd(np.ones((batch, 1, dim)), u, A, ones, ones, delta_bias=bias,
+                             delta_softplus=softplus)
+        v = u + bias
+        want = np.logaddexp(0.0, v) if softplus else v
+        _close(y, want, rtol=1e-14, what=f"delta activation (softplus={softplus})")
+    # Theorem 1 with the activation inside the scan: delta = softplus(u)
+    batch, L, dim = 2, 30, 3
+    u = 2.0 * rng.standard_normal((batch, L, dim))
+    x = rng.standard_normal((batch, L, dim))
+    shift = rng.uniform(-1.0, 1.0, dim)
+    ones = np.ones((batch, L, 1))
+    y, _ = orc.scan_fwd(x, u - shift, -np.ones((dim, 1)), ones, ones, zoh=True,
+                        delta_bias=shift, delta_softplus=True)
+    want = np.empty_like(y)
+    for b in range(batch):
+        for d in range(dim):
+            h = 0.0
+            for t in range(L):
+                g = expit(u[b, t, d])
+                h = (1.0 - g) * h + g * x[b, t, d]
+                want[b, t, d] = h
+    _close(y, want, what="Theorem 1 gate with the fused activation")
+    # decode applies the same activation
+    inp = _rand_inputs(rng, 3, 1, 5, 4)
+    yo, ho = orc.scan_fwd(**dict(inp, delta=inp["delta"] - 1.0), delta_bias=np.arange(5) * 0.1,
+                          delta_softplus=True)
+    yd, hd = orc.state_update(inp["h0"], inp["x"][:, 0], inp["delta"][:, 0] - 1.0, inp["A"],
+                              inp["B"][:, 0], inp["C"][:, 0], D=inp["D"], z=inp["z"][:, 0],
+                              delta_bias=np.arange(5) * 0.1, delta_softplus=True)
+    assert np.array_equal(yd, yo[:, 0]) and np.array_equal(hd, ho), "decode activation"
+
+
 ALL_PINS = [pin_lti_convolution, pin_brute_force, pin_chunk_split, pin_theorem1,
-            pin_ssd_matrix, pin_limits, pin_structure, pin_decode]
+            pin_ssd_matrix, pin_limits, pin_structure, pin_decode, pin_delta_activation]

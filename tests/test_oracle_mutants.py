@@ -31,8 +31,16 @@ MUTANTS = {
                               "const int64_t i_bc = t * dstate;"),
     "x from the previous token": ("const double u = x[i_tok];",
                                   "const double u = x[i_tok - (t > 0 ? dim : 0)];"),
-    "x and delta swapped": ("const double dt = delta[i_tok];\n                const double u = x[i_tok];",
-                            "const double dt = x[i_tok];\n                const double u = delta[i_tok];"),
+    "x and delta swapped": ("double dt = delta[i_tok];\n                const double u = x[i_tok];",
+                            "double dt = x[i_tok];\n                const double u = delta[i_tok];"),
+    "delta bias ignored": ("if (delta_bias) dt += delta_bias[d];", ""),
+    "delta bias after the activation": (
+        "if (delta_bias) dt += delta_bias[d];\n                if (delta_softplus) dt = softplus(dt);",
+        "if (delta_softplus) dt = softplus(dt);\n                if (delta_bias) dt += delta_bias[d];"),
+    "softplus sign": ("return v > 0.0 ? v + log1p(exp(-v)) : log1p(exp(v));",
+                      "return v > 0.0 ? v + log1p(exp(-v)) : log1p(exp(-v));"),
+    "softplus dropped": ("if (delta_softplus) dt = softplus(dt);",
+                         "if (delta_softplus) dt = softplus(dt) * 0.0 + dt;"),
     "final state scaled": ("hL[(b * dim + d) * dstate + n] = h[n];",
                            "hL[(b * dim + d) * dstate + n] = 0.5 * h[n];"),
     "zero-order hold sign": ("(Abar - 1.0) / a", "(1.0 - Abar) / a"),
