@@ -41,6 +41,9 @@ def parse():
     p.add_argument("--state-split", type=int, default=0, help="0 = the library's automatic plan")
     p.add_argument("--batch", type=int, default=0, help="override the workload's batch (0 = keep)")
     p.add_argument("--dim", type=int, default=0, help="override the workload's channels (0 = keep)")
+    p.add_argument("--delta-softplus", action="store_true",
+                   help="pass delta before its activation with a per-channel bias and let the "
+                        "kernels apply bias and softplus")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-channels", type=int, default=0,
                    help="channels of the CPU-baseline sample (0 = sized to ~10 s)")
@@ -53,39 +56,50 @@ def parse():
     return p.parse_args()
 
 
-def algorithmic_bytes(w):
+def algorithmic_bytes(w, softplus=False):
     """Bytes the scan must move: x, delta, z in and y out (I/O dtype), B and C
     in, A and D in (fp32), final state out (fp32), initial state in when the
-    workload has one. The expanded (B, L, D, N) state is never stored."""
+    workload has one, the delta bias (fp32) with the fused activation. The
+    expanded (B, L, D, N) state is never stored."""
     s = 4 if w.io == "f32" else 2
     b, l, d, n = w.batch, w.seqlen, w.dim, w.dstate
     total = 4 * b * l * d * s + 2 * b * l * n * s + d * n * 4 + d * 4 + b * d * n * 4
     if w.h0 == "normal":
         total += b * d * n * 4
+    if softplus:
+        total += d * 4
     return total
 
 
-def algorithmic_alu_ops(w):
+def algorithmic_alu_ops(w, softplus=False):
     """fp32 lane-operations the scan must issue per element: per state one
     multiply for delta*A, one exponential, one multiply for (delta*x)*B, one
     FMA for the state update and one FMA for the readout; per element one
     multiply for delta*x, one FMA for the skip term, the gate (one multiply,
     one exponential, one add, one reciprocal, two multiplies) and one
-    conversion to the I/O dtype."""
+    conversion to the I/O dtype. The fused activation adds per element the
+    bias add and softplus: |v| scaling, exponential, add, compare, logarithm,
+    three multiplies, reciprocal, subtract, max and add (12)."""
     n = w.dstate
-    per_elem = 5 * n + 1 + 1 + 6 + (1 if w.io == "bf16" else 0)
+    per_elem = 5 * n + 1 + 1 + 6 + (1 if w.io == "bf16" else 0) + (13 if softplus else 0)
     return per_elem * w.batch * w.seqlen * w.dim
 
 
 COPY_BYTES = 1 << 30
 DOMINANT = "chunk_output_kernel"
-KERNEL_SOURCE = os.path.join(ROOT, "selective_state_space_40_amd", "csrc", "scan_kernels.hip")
+KERNEL_SOURCES = [os.path.join(ROOT, "selective_state_space_40_amd", "csrc", f)
+                  for f in ("internal.h", "device_common.h", "scan_chunked.h", "scan_variant.hip")]
 
 
 def source_hash():
+    """Digest of the sources the scan kernels are compiled from: recorded
+    counters are only used for the kernel they were taken on."""
     import hashlib
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def traffic_path(workload):
@@ -179,15 +193,16 @@ def main():
     torch.cuda.set_device(dev)
     ms.load_library()
 
-    sets = [W.generate_scan(w, device=dev, seed=w.seed + 101 * i) for i in range(2)]
+    sp = args.delta_softplus
+    sets = [W.generate_scan(w, device=dev, seed=w.seed + 101 * i, raw_delta=sp) for i in range(2)]
     y = torch.empty_like(sets[0]["x"])
     hL = torch.empty(w.batch, w.dim, w.dstate, dtype=torch.float32, device=dev)
 
     def step(i):
         inp = sets[i % 2]
         ms.scan_fwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"],
-                    inp["h0"], chunk_len=args.chunk_len, state_split=args.state_split, out=y,
-                    state_out=hL)
+                    inp["h0"], delta_bias=inp.get("delta_bias"), delta_softplus=sp,
+                    chunk_len=args.chunk_len, state_split=args.state_split, out=y, state_out=hL)
 
     for i in range(args.warmup):
         step(i)
@@ -215,9 +230,9 @@ def main():
     elems = w.batch * w.seqlen * w.dim
     sec = ms_per_step / 1e3
     value = elems / sec
-    bytes_alg = algorithmic_bytes(w)
+    bytes_alg = algorithmic_bytes(w, sp)
     gbps = bytes_alg / sec / 1e9
-    ops = algorithmic_alu_ops(w)
+    ops = algorithmic_alu_ops(w, sp)
     tops = ops / sec / 1e12
 
     # Dominant kernel: the output pass (chunk_output_kernel). With a single
@@ -227,7 +242,8 @@ def main():
     hbm_frac = gbps / HBM_PEAK_GBPS
     alu_frac = tops / ALU_PEAK_TOPS
     bound = "alu" if ops / (ALU_PEAK_TOPS * 1e12) > bytes_alg / (HBM_PEAK_GBPS * 1e9) else "hbm"
-    traffic = recorded_traffic(w.name) if nchunks == 1 and not (args.batch or args.dim) else None
+    plain = not (args.batch or args.dim or sp)
+    traffic = recorded_traffic(w.name) if nchunks == 1 and plain else None
     roofline = {
         "bound": bound,
         "achieved": round(tops if bound == "alu" else gbps, 3),
@@ -244,7 +260,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, sets[0], args.cpu_sample_channels)
+        cpu = cpu_baseline(w, sets[0], args.cpu_sample_channels, sp)
 
     line = {
         "metric": METRIC,
@@ -262,6 +278,8 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "seqlen": w.seqlen, "dim": w.dim,
                    "dstate": w.dstate, "io_dtype": w.io, "chunk_len": int(chunk_len),
                    "nchunks": int(nchunks), "state_split": int(split),
+                   "delta_activation": "bias + softplus in the kernels" if sp else
+                                       "none (delta passed activated)",
                    "parallelism": "single GPU"},
         "achieved_GBps": round(gbps, 1),
         "wall_s": round(wall, 4),
@@ -344,7 +362,7 @@ def bench_decode(args, w):
     print(json.dumps(line), flush=True)
 
 
-def cpu_baseline(w, inp, channels):
+def cpu_baseline(w, inp, channels, softplus=False):
     """The fp64 oracle, as it is, on the host over a channel sample of the
     same workload (all batch rows, all tokens)."""
     import numpy as np
@@ -363,10 +381,11 @@ def cpu_baseline(w, inp, channels):
     sub = {k: v for k, v in dict(
         x=inp["x"].index_select(2, idx), delta=inp["delta"].index_select(2, idx),
         A=inp["A"].index_select(0, idx), B=inp["B"], C=inp["C"], D=inp["D"].index_select(0, idx),
-        z=inp["z"].index_select(2, idx), h0=None).items()}
+        z=inp["z"].index_select(2, idx), h0=None,
+        delta_bias=inp["delta_bias"].index_select(0, idx) if softplus else None).items()}
     host = {k: (oracle._f64(v) if v is not None else None) for k, v in sub.items()}
     t0 = time.perf_counter()
-    orc.scan_fwd(**host)
+    orc.scan_fwd(**host, delta_softplus=softplus)
     dt = time.perf_counter() - t0
     elems = w.batch * w.seqlen * channels
     return {"value": elems / dt, "unit": "elements/s", "cores": threads, "kind": "oracle",

@@ -13,8 +13,9 @@
  * with silu(z) = z / (1 + exp(-z)). The output of token t reads the state
  * after token t has been absorbed. The input discretisation is the
  * first-order form Bbar = delta * B; the skip term D*x and the silu gate are
- * optional. Delta, B and C arrive already computed per token (section
- * "Chosen by the Token"); delta must be positive (not checked).
+ * optional. Delta, B and C arrive computed per token (section "Chosen by the
+ * Token"). Delta must be positive (not checked); it may also arrive before
+ * its activation, see mamba_scan_options.
  *
  * Layout: every tensor is dense and row-major.
  *     x, delta, z, y   (batch, seqlen, dim)      dim contiguous, I/O dtype
@@ -92,6 +93,27 @@ typedef struct mamba_scan_plan {
 } mamba_scan_plan;
 
 /*
+ * Optional transforms applied inside the kernels (a NULL options pointer
+ * turns all of them off).
+ *
+ * delta_bias      (dim) fp32 device pointer or NULL: added to delta before
+ *                 anything else uses it.
+ * delta_softplus  nonzero: delta <- softplus(delta + bias), with
+ *                 softplus(v) = log(1 + exp(v)). The pages have delta come
+ *                 from a projection of the token and require it positive
+ *                 (section "Chosen by the Token"); softplus is the activation
+ *                 that makes it so, and fusing it saves a full pass over
+ *                 delta. The activated delta feeds both exp(delta*A) and
+ *                 delta*B*x.
+ * reserved        must be 0.
+ */
+typedef struct mamba_scan_options {
+    const float* delta_bias;
+    int32_t delta_softplus;
+    int32_t reserved;
+} mamba_scan_options;
+
+/*
  * Resolve the plan ssm_scan_fwd will use for this shape and report the
  * scratch bytes it needs (0 when the plan has a single chunk).
  *
@@ -116,6 +138,8 @@ int ssm_scan_fwd_workspace_size(int64_t batch, int64_t seqlen, int64_t dim, int 
  * y          (batch, seqlen, dim)     written
  * hL         (batch, dim, dstate)     optional, written with the state after
  *                                     the last token; may alias h0
+ * options    delta bias and activation (may be NULL: none), see
+ *            mamba_scan_options
  * plan       work division (may be NULL: automatic), see mamba_scan_plan
  * workspace  at least the bytes ssm_scan_fwd_workspace_size reports for the
  *            same shape and plan; may be NULL when that size is 0; its
@@ -127,8 +151,8 @@ int ssm_scan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int dstate, int dty
                  const void* x, const void* delta, const float* A,
                  const void* B, const void* C, const float* D, const void* z,
                  const float* h0, void* y, float* hL,
-                 const mamba_scan_plan* plan, void* workspace, size_t workspace_bytes,
-                 hipStream_t stream);
+                 const mamba_scan_options* options, const mamba_scan_plan* plan,
+                 void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Single-token decode update (section "Taken Apart": one token moves the
@@ -141,11 +165,13 @@ int ssm_scan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int dstate, int dty
  * D          (dim) fp32              optional
  * z          (batch, dim)            optional
  * y          (batch, dim)            written
+ * options    delta bias and activation (may be NULL: none), as for
+ *            ssm_scan_fwd
  */
 int ssm_state_update(int64_t batch, int64_t dim, int dstate, int dtype, float* h,
                      const void* x, const void* delta, const float* A,
                      const void* B, const void* C, const float* D, const void* z,
-                     void* y, hipStream_t stream);
+                     void* y, const mamba_scan_options* options, hipStream_t stream);
 
 /* Static, human-readable name of a mamba_status value. */
 const char* mamba_status_string(int status);

@@ -6,11 +6,15 @@ torch on the tensors' device, and passes raw device pointers and the current
 HIP stream to libmamba_scan.so, whose kernels do every step of the scan.
 There is no other code path: without the built library every call raises.
 
-    y, hL = scan_fwd(x, delta, A, B, C, D=None, z=None, h0=None)
-    y = state_update(h, x, delta, A, B, C, D=None, z=None)    # h updated in place
+    y, hL = scan_fwd(x, delta, A, B, C, D=None, z=None, h0=None,
+                     delta_bias=None, delta_softplus=False)
+    y = state_update(h, x, delta, A, B, C, D=None, z=None,
+                     delta_bias=None, delta_softplus=False)   # h updated in place
 
 Shapes (row-major, contiguous): x, delta, z, y (batch, L, dim); B, C
-(batch, L, N); A (dim, N) fp32; D (dim,) fp32; h0, hL (batch, dim, N) fp32.
+(batch, L, N); A (dim, N) fp32; D and delta_bias (dim,) fp32; h0, hL
+(batch, dim, N) fp32. With delta_softplus the kernels use
+softplus(delta + delta_bias) in place of delta.
 x, delta, z, B and C share one dtype, float32 or bfloat16, and y has it too.
 """
 import ctypes
@@ -19,7 +23,7 @@ import os
 import torch
 
 __all__ = ["scan_fwd", "state_update", "workspace_size", "resolve_plan", "library_path",
-           "load_library", "MambaScanError", "MAX_DSTATE", "ScanPlan"]
+           "load_library", "MambaScanError", "MAX_DSTATE", "ScanPlan", "ScanOptions"]
 
 MAX_DSTATE = 16
 _DTYPES = {torch.float32: 0, torch.bfloat16: 1}
@@ -32,6 +36,12 @@ class ScanPlan(ctypes.Structure):
     """mamba_scan_plan: chunk_len (tokens per parallel chunk) and state_split
     (waves sharing one channel's states); 0 means automatic."""
     _fields_ = [("chunk_len", ctypes.c_int64), ("state_split", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+
+class ScanOptions(ctypes.Structure):
+    """mamba_scan_options: optional delta bias (device pointer) and softplus."""
+    _fields_ = [("delta_bias", ctypes.c_void_p), ("delta_softplus", ctypes.c_int32),
                 ("reserved", ctypes.c_int32)]
 
 
@@ -57,12 +67,14 @@ def load_library():
     lib = ctypes.CDLL(path)
     vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     pp = ctypes.POINTER(ScanPlan)
+    po = ctypes.POINTER(ScanOptions)
     lib.ssm_scan_fwd_workspace_size.argtypes = [i64, i64, i64, i32, i32, pp, pp,
                                                 ctypes.POINTER(ctypes.c_size_t)]
     lib.ssm_scan_fwd_workspace_size.restype = i32
-    lib.ssm_scan_fwd.argtypes = [i64, i64, i64, i32, i32] + [vp] * 10 + [pp, vp, ctypes.c_size_t, vp]
+    lib.ssm_scan_fwd.argtypes = ([i64, i64, i64, i32, i32] + [vp] * 10 +
+                                 [po, pp, vp, ctypes.c_size_t, vp])
     lib.ssm_scan_fwd.restype = i32
-    lib.ssm_state_update.argtypes = [i64, i64, i32, i32] + [vp] * 9 + [vp]
+    lib.ssm_state_update.argtypes = [i64, i64, i32, i32] + [vp] * 9 + [po, vp]
     lib.ssm_state_update.restype = i32
     lib.mamba_status_string.argtypes = [i32]
     lib.mamba_status_string.restype = ctypes.c_char_p
@@ -99,6 +111,13 @@ def _need(t, name, shape, dtype, device):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _options(delta_bias, delta_softplus):
+    if delta_bias is None and not delta_softplus:
+        return None
+    return ctypes.byref(ScanOptions(None if delta_bias is None else delta_bias.data_ptr(),
+                                    1 if delta_softplus else 0, 0))
+
+
 def resolve_plan(batch, seqlen, dim, dstate, dtype=torch.bfloat16, chunk_len=0, state_split=0):
     """The plan ssm_scan_fwd uses for this shape, and its scratch bytes:
     returns (chunk_len, state_split, workspace_bytes). Automatic fields query
@@ -129,11 +148,14 @@ def _workspace(device, nbytes):
     return buf
 
 
-def scan_fwd(x, delta, A, B, C, D=None, z=None, h0=None, *, chunk_len=0, state_split=0,
-             return_state=True, out=None, state_out=None):
+def scan_fwd(x, delta, A, B, C, D=None, z=None, h0=None, *, delta_bias=None,
+             delta_softplus=False, chunk_len=0, state_split=0, return_state=True, out=None,
+             state_out=None):
     """Selective scan over whole sequences; returns (y, hL) (hL is None when
-    return_state is False). `chunk_len` > 0 forces the parallel chunk length
-    and `state_split` > 0 the number of waves sharing a channel's states."""
+    return_state is False). `delta_bias` (dim,) fp32 is added to delta and
+    `delta_softplus` applies softplus after it, inside the kernels.
+    `chunk_len` > 0 forces the parallel chunk length and `state_split` > 0
+    the number of waves sharing a channel's states."""
     lib = load_library()
     if x.dim() != 3:
         raise ValueError("x must be (batch, L, dim)")
@@ -154,6 +176,7 @@ def scan_fwd(x, delta, A, B, C, D=None, z=None, h0=None, *, chunk_len=0, state_s
     _need(D, "D", (dim,), torch.float32, dev)
     _need(z, "z", (batch, seqlen, dim), dt, dev)
     _need(h0, "h0", (batch, dim, dstate), torch.float32, dev)
+    _need(delta_bias, "delta_bias", (dim,), torch.float32, dev)
     y = out if out is not None else torch.empty_like(x)
     _need(y, "out", (batch, seqlen, dim), dt, dev)
     hL = None
@@ -167,13 +190,16 @@ def scan_fwd(x, delta, A, B, C, D=None, z=None, h0=None, *, chunk_len=0, state_s
         ws = _workspace(dev, nbytes)
         st = lib.ssm_scan_fwd(batch, seqlen, dim, dstate, _DTYPES[dt], _ptr(x), _ptr(delta),
                               _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0), _ptr(y),
-                              _ptr(hL), ctypes.byref(plan), _ptr(ws), nbytes, _stream(dev))
+                              _ptr(hL), _options(delta_bias, delta_softplus), ctypes.byref(plan),
+                              _ptr(ws), nbytes, _stream(dev))
     _check(st, "ssm_scan_fwd")
     return y, hL
 
 
-def state_update(h, x, delta, A, B, C, D=None, z=None, *, out=None):
-    """One decode step: h (batch, dim, N) fp32 is updated in place; returns y (batch, dim)."""
+def state_update(h, x, delta, A, B, C, D=None, z=None, *, delta_bias=None,
+                 delta_softplus=False, out=None):
+    """One decode step: h (batch, dim, N) fp32 is updated in place; returns y
+    (batch, dim). delta_bias and delta_softplus act as in scan_fwd."""
     lib = load_library()
     if h.dim() != 3:
         raise ValueError("h must be (batch, dim, N)")
@@ -191,11 +217,12 @@ def state_update(h, x, delta, A, B, C, D=None, z=None, *, out=None):
     _need(C, "C", (batch, dstate), dt, dev)
     _need(D, "D", (dim,), torch.float32, dev)
     _need(z, "z", (batch, dim), dt, dev)
+    _need(delta_bias, "delta_bias", (dim,), torch.float32, dev)
     y = out if out is not None else torch.empty_like(x)
     _need(y, "out", (batch, dim), dt, dev)
     with torch.cuda.device(dev):
         st = lib.ssm_state_update(batch, dim, dstate, _DTYPES[dt], _ptr(h), _ptr(x), _ptr(delta),
                                   _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(y),
-                                  _stream(dev))
+                                  _options(delta_bias, delta_softplus), _stream(dev))
     _check(st, "ssm_state_update")
     return y

@@ -41,6 +41,18 @@ int current_cu_count(int* cu) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Reads the optional delta transforms; NULL means none.
+int read_options(const mamba_scan_options* o, const float** bias, int* softplus) {
+    *bias = nullptr;
+    *softplus = 0;
+    if (o == nullptr) return MAMBA_OK;
+    if (o->reserved != 0) return MAMBA_ERR_INVALID_ARG;
+    if (o->delta_bias != nullptr && !aligned16(o->delta_bias)) return MAMBA_ERR_MISALIGNED;
+    *bias = o->delta_bias;
+    *softplus = o->delta_softplus != 0;
+    return MAMBA_OK;
+}
+
 int check_shape(int64_t batch, int64_t seqlen, int64_t dim, int dstate, int dtype) {
     if (batch < 0 || seqlen < 0 || dim < 0) return MAMBA_ERR_INVALID_ARG;
     if (dtype != MAMBA_DTYPE_F32 && dtype != MAMBA_DTYPE_BF16) return MAMBA_ERR_INVALID_ARG;
@@ -150,9 +162,14 @@ int ssm_scan_fwd_workspace_size(int64_t batch, int64_t seqlen, int64_t dim, int 
 int ssm_scan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int dstate, int dtype,
                  const void* x, const void* delta, const float* A, const void* B,
                  const void* C, const float* D, const void* z, const float* h0, void* y,
-                 float* hL, const mamba_scan_plan* plan_req, void* workspace,
-                 size_t workspace_bytes, hipStream_t stream) {
+                 float* hL, const mamba_scan_options* options,
+                 const mamba_scan_plan* plan_req, void* workspace, size_t workspace_bytes,
+                 hipStream_t stream) {
     int st = check_shape(batch, seqlen, dim, dstate, dtype);
+    if (st != MAMBA_OK) return st;
+    const float* delta_bias = nullptr;
+    int delta_softplus = 0;
+    st = read_options(options, &delta_bias, &delta_softplus);
     if (st != MAMBA_OK) return st;
     if (batch == 0 || dim == 0) return MAMBA_OK;
     if (A == nullptr) return MAMBA_ERR_INVALID_ARG;
@@ -186,14 +203,20 @@ int ssm_scan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int dstate, int dty
     a.h0 = h0;
     a.y = y;
     a.hL = hL;
+    a.delta_bias = delta_bias;
+    a.delta_softplus = delta_softplus;
     return mamba::launch_scan(a, plan, workspace, stream) == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP;
 }
 
 int ssm_state_update(int64_t batch, int64_t dim, int dstate, int dtype, float* h,
                      const void* x, const void* delta, const float* A, const void* B,
                      const void* C, const float* D, const void* z, void* y,
-                     hipStream_t stream) {
+                     const mamba_scan_options* options, hipStream_t stream) {
     int st = check_shape(batch, 1, dim, dstate, dtype);
+    if (st != MAMBA_OK) return st;
+    const float* delta_bias = nullptr;
+    int delta_softplus = 0;
+    st = read_options(options, &delta_bias, &delta_softplus);
     if (st != MAMBA_OK) return st;
     if (batch == 0 || dim == 0) return MAMBA_OK;
     if (h == nullptr || x == nullptr || delta == nullptr || A == nullptr || B == nullptr ||
@@ -217,6 +240,8 @@ int ssm_state_update(int64_t batch, int64_t dim, int dstate, int dtype, float* h
     a.D = D;
     a.z = z;
     a.y = y;
+    a.delta_bias = delta_bias;
+    a.delta_softplus = delta_softplus;
     return mamba::launch_state_update(a, stream) == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP;
 }
 

@@ -1,0 +1,79 @@
+// Device helpers shared by the scan and decode kernels: I/O element access,
+// the hardware exp2/rcp/log2 approximations, silu and softplus, and the
+// grid of the grid-stride kernels. Included by exactly one translation unit
+// per kernel family; everything has internal linkage.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "internal.h"
+
+namespace mamba {
+namespace {
+
+constexpr float kLog2e = 1.44269504088896340736f;
+constexpr int TT = kTokenTile;
+
+// ---------------------------------------------------------------------------
+// I/O element access. Raw values are kept as 32-bit integers until use so a
+// prefetched tile is not forced to wait for its loads early.
+template <int IO>
+__device__ __forceinline__ uint32_t load_raw(const void* __restrict__ p, int64_t i) {
+    if constexpr (IO == kIoF32) {
+        return static_cast<const uint32_t*>(p)[i];
+    } else {
+        return static_cast<const uint16_t*>(p)[i];
+    }
+}
+
+template <int IO>
+__device__ __forceinline__ float raw_to_f32(uint32_t r) {
+    if constexpr (IO == kIoF32) {
+        return __uint_as_float(r);
+    } else {
+        return __uint_as_float(r << 16);  // bf16 -> fp32 is exact
+    }
+}
+
+template <int IO>
+__device__ __forceinline__ void store_io(void* __restrict__ p, int64_t i, float v) {
+    if constexpr (IO == kIoF32) {
+        static_cast<float*>(p)[i] = v;
+    } else {
+        static_cast<__bf16*>(p)[i] = static_cast<__bf16>(v);  // round to nearest even
+    }
+}
+
+__device__ __forceinline__ float fast_exp2(float v) { return __builtin_amdgcn_exp2f(v); }
+__device__ __forceinline__ float fast_rcp(float v) { return __builtin_amdgcn_rcpf(v); }
+
+// silu(z) = z / (1 + exp(-z))
+__device__ __forceinline__ float silu(float z) {
+    return z * fast_rcp(1.0f + fast_exp2(-z * kLog2e));
+}
+
+constexpr float kLn2 = 0.69314718055994530942f;
+
+// softplus(v) = log(1 + exp(v)) = max(v, 0) + log1p(e), e = exp(-|v|) in
+// (0, 1]. log1p(e) is taken as log(w) * e / (w - 1) with w = 1 + e rounded
+// (Goldberg, "What Every Computer Scientist Should Know About Floating-Point
+// Arithmetic", Theorem 4): the rounding of w cancels between the two
+// factors, so small e keep their relative accuracy instead of vanishing in
+// log(w). Overflow cannot happen; NaN stays NaN.
+__device__ __forceinline__ float softplus_f32(float v) {
+    const float e = fast_exp2(-fabsf(v) * kLog2e);
+    const float w = 1.0f + e;
+    const float l = w == 1.0f ? e : __builtin_amdgcn_logf(w) * kLn2 * (e * fast_rcp(w - 1.0f));
+    return fmaxf(v, 0.0f) + l;
+}
+
+// Grid for the grid-stride kernels above: enough 256-thread blocks to cover
+// `count` items, capped well below the 32-bit grid limit.
+inline int64_t stride_blocks(int64_t count) {
+    const int64_t b = (count + 255) / 256;
+    return b < (int64_t(1) << 20) ? (b > 0 ? b : 1) : (int64_t(1) << 20);
+}
+
+}  // namespace
+}  // namespace mamba

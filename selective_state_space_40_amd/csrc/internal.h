@@ -53,6 +53,8 @@ struct ScanArgs {
     const float* h0;
     void* y;
     float* hL;
+    const float* delta_bias;  // (dim) or nullptr
+    int delta_softplus;       // nonzero: delta <- softplus(delta + bias)
 };
 
 struct DecodeArgs {
@@ -68,6 +70,8 @@ struct DecodeArgs {
     const float* D;
     const void* z;
     void* y;
+    const float* delta_bias;
+    int delta_softplus;
 };
 
 // Workspace layout for nchunks > 1: three fp32 arrays of
@@ -80,6 +84,12 @@ size_t scan_workspace_bytes(int64_t batch, int64_t dim, int dstate, int64_t nchu
 // validated. Returns the HIP error of the last launch.
 hipError_t launch_scan(const ScanArgs& a, const ScanPlan& plan, void* workspace,
                        hipStream_t stream);
+
+// The chunked scan for one (I/O dtype, delta softplus) pair; each pair is
+// compiled in its own translation unit (scan_variant.hip).
+template <int IO, bool SP>
+hipError_t launch_scan_variant(const ScanArgs& a, const ScanPlan& plan, void* workspace,
+                               hipStream_t stream);
 
 // Queue the single-token update. Arguments are already validated.
 hipError_t launch_state_update(const DecodeArgs& a, hipStream_t stream);

@@ -5,6 +5,9 @@
 // b, channel d and state n:
 //     Abar = exp(delta*A[d,n]),  h[n] <- Abar*h[n] + delta*B[n]*x,
 //     y = (sum_n C[n]*h[n] + D[d]*x) * silu(z).
+// Delta may arrive raw: the kernels then add a per-channel bias and apply
+// softplus as they convert each (channel, token) once, and every later use,
+// the chunk sums of pass 1 included, sees the activated value.
 //
 // Work mapping. The scan is elementwise in (b, d) and sequential in t, and it
 // is no dense contraction, so it runs on the vector ALUs, not the matrix
@@ -33,56 +36,21 @@
 // pass 2 reruns each chunk from that state and writes y (the "parallel scan"
 // of section "A Scan on the Chip"). P is formed from a chunk-local sum of
 // delta, never from differences of long prefix sums.
+//
+// This header is the body of scan_variant.hip, which is compiled once per
+// (I/O dtype, delta activation) pair so the variants build in parallel.
+#pragma once
+
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include <type_traits>
 
+#include "device_common.h"
 #include "internal.h"
 
 namespace mamba {
 namespace {
-
-constexpr float kLog2e = 1.44269504088896340736f;
-constexpr int TT = kTokenTile;
-
-// ---------------------------------------------------------------------------
-// I/O element access. Raw values are kept as 32-bit integers until use so a
-// prefetched tile is not forced to wait for its loads early.
-template <int IO>
-__device__ __forceinline__ uint32_t load_raw(const void* __restrict__ p, int64_t i) {
-    if constexpr (IO == kIoF32) {
-        return static_cast<const uint32_t*>(p)[i];
-    } else {
-        return static_cast<const uint16_t*>(p)[i];
-    }
-}
-
-template <int IO>
-__device__ __forceinline__ float raw_to_f32(uint32_t r) {
-    if constexpr (IO == kIoF32) {
-        return __uint_as_float(r);
-    } else {
-        return __uint_as_float(r << 16);  // bf16 -> fp32 is exact
-    }
-}
-
-template <int IO>
-__device__ __forceinline__ void store_io(void* __restrict__ p, int64_t i, float v) {
-    if constexpr (IO == kIoF32) {
-        static_cast<float*>(p)[i] = v;
-    } else {
-        static_cast<__bf16*>(p)[i] = static_cast<__bf16>(v);  // round to nearest even
-    }
-}
-
-__device__ __forceinline__ float fast_exp2(float v) { return __builtin_amdgcn_exp2f(v); }
-__device__ __forceinline__ float fast_rcp(float v) { return __builtin_amdgcn_rcpf(v); }
-
-// silu(z) = z / (1 + exp(-z))
-__device__ __forceinline__ float silu(float z) {
-    return z * fast_rcp(1.0f + fast_exp2(-z * kLog2e));
-}
 
 // ---------------------------------------------------------------------------
 // Per-wave addressing of one chunk. x, delta, z and y of the chunk are read
@@ -243,6 +211,19 @@ struct Tile {
     uint32_t x[TT / S], dt[TT / S], z[TT / S];
 };
 
+// Delta as the recurrence uses it: the raw input plus the channel's bias,
+// through softplus when SP is set. SP is a compile-time switch: a runtime
+// branch here gets the main loop unswitched into two copies whose register
+// allocation is worse than either alone.
+template <int S, int IO, bool SP>
+__device__ __forceinline__ void delta_tile(const Tile<S>& r, float bias, float (&dt)[TT / S]) {
+#pragma unroll
+    for (int jj = 0; jj < TT / S; ++jj) {
+        const float v = raw_to_f32<IO>(r.dt[jj]) + bias;
+        dt[jj] = SP ? softplus_f32(v) : v;
+    }
+}
+
 // Token indices are clamped to the chunk, so the ragged last tile reads only
 // tokens that exist (the clamped copies are never used).
 template <int S, int IO, bool LOAD_Z>
@@ -260,15 +241,16 @@ __device__ __forceinline__ void fetch_tile(const ChunkIo& io, int tile, int w, i
 
 // LDS layout of the staged per-token inputs: [token j][lane] float2 (delta,
 // delta*x). Writes the wave's own tokens and returns D*x of them.
-template <int S, int IO, bool HAS_D>
-__device__ __forceinline__ void stage_tokens(float2* dtdu, int w, const Tile<S>& r, float dskip,
-                                             float (&skip)[TT / S]) {
+template <int S, int IO, bool SP, bool HAS_D>
+__device__ __forceinline__ void stage_tokens(float2* dtdu, int w, const Tile<S>& r, float dbias,
+                                             float dskip, float (&skip)[TT / S]) {
     const int lane = threadIdx.x & (kWave - 1);
+    float dt[TT / S];
+    delta_tile<S, IO, SP>(r, dbias, dt);
 #pragma unroll
     for (int jj = 0; jj < TT / S; ++jj) {
-        const float dt = raw_to_f32<IO>(r.dt[jj]);
         const float u = raw_to_f32<IO>(r.x[jj]);
-        dtdu[(jj * S + w) * kWave + lane] = make_float2(dt, dt * u);
+        dtdu[(jj * S + w) * kWave + lane] = make_float2(dt[jj], dt[jj] * u);
         skip[jj] = HAS_D ? dskip * u : 0.0f;
     }
 }
@@ -277,12 +259,13 @@ __device__ __forceinline__ void stage_tokens(float2* dtdu, int w, const Tile<S>&
 // (FULL: cnt == TT, compiled without per-token branches). With S > 1 the
 // per-token inputs come from LDS and the readout over the wave's states is
 // kept per token in part[]; with S == 1 the wave holds every state, takes
-// its inputs straight from its registers and finishes and stores each token
-// right away. Without OUTPUT the sum of delta accumulates in dsum.
+// its inputs straight from its registers (delta already activated in dtv)
+// and finishes and stores each token right away. Without OUTPUT the sum of
+// delta accumulates in dsum.
 template <int N, int S, int IO, bool OUTPUT, bool HAS_D, bool HAS_Z, bool FULL>
 __device__ __forceinline__ void compute_tile(const ChunkIo& io, const float* bcs_w,
-                                             const float2* dtdu, const Tile<S>& r, int tile,
-                                             int cnt, const float (&A2)[Split<N, S>::NPW],
+                                             const float2* dtdu, const Tile<S>& r,
+                                             const float (&dtv)[TT / S], int tile, int cnt, const float (&A2)[Split<N, S>::NPW],
                                              float (&h)[Split<N, S>::NPW], float dskip,
                                              float (&part)[TT], float& dsum) {
     constexpr int NPW = Split<N, S>::NPW;
@@ -294,7 +277,7 @@ __device__ __forceinline__ void compute_tile(const ChunkIo& io, const float* bcs
         if (FULL || j < cnt) {
             float dt, du, u = 0.0f;
             if constexpr (S == 1) {
-                dt = raw_to_f32<IO>(r.dt[j]);
+                dt = dtv[j];
                 u = raw_to_f32<IO>(r.x[j]);
                 du = dt * u;
             } else {
@@ -385,9 +368,10 @@ struct ScanLds {
 // into LDS buffers (i+1)&1; barrier; finalise this wave's tokens of tile i.
 // Every LDS buffer is rewritten only after a barrier that follows its last
 // read.
-template <int N, int S, int IO, bool OUTPUT, bool HAS_D, bool HAS_Z>
-__device__ __forceinline__ void scan_chunk(const ChunkIo& io, const BcIo& bcio, int ntok, int w,
-                                           int n0, ScanLds<N, S>& lds,
+template <int N, int S, int IO, bool SP, bool OUTPUT, bool HAS_D, bool HAS_Z>
+__device__ __forceinline__ void scan_chunk(const ChunkIo& io, const BcIo& bcio, float dbias,
+                                           int ntok, int w, int n0,
+                                           ScanLds<N, S>& lds,
                                            const float (&A2)[Split<N, S>::NPW],
                                            float (&h)[Split<N, S>::NPW], float dskip,
                                            float& dsum) {
@@ -412,10 +396,11 @@ __device__ __forceinline__ void scan_chunk(const ChunkIo& io, const BcIo& bcio, 
         fetch_tile<S, IO, LOAD_Z>(io, inext, w, ntok, nxt);
         __builtin_amdgcn_sched_barrier(0);
         const int cnt = FULL ? TT : ntok - i * TT;
-        float part[TT];
+        float part[TT], dtv[TT / S];
+        if constexpr (S == 1) delta_tile<S, IO, SP>(cur, dbias, dtv);
         compute_tile<N, S, IO, OUTPUT, HAS_D, HAS_Z, FULL>(io, lds.bcs[i & 1] + n0,
-                                                           lds.dtdu[i & 1], cur, i, cnt, A2, h,
-                                                           dskip, part, dsum);
+                                                           lds.dtdu[i & 1], cur, dtv, i, cnt, A2,
+                                                           h, dskip, part, dsum);
         if constexpr (OUTPUT && S > 1) {
             float* mine = lds.red[i & 1] + w * TT * kWave + lane;
 #pragma unroll
@@ -423,7 +408,8 @@ __device__ __forceinline__ void scan_chunk(const ChunkIo& io, const BcIo& bcio, 
         }
         stage_bc<N, S, IO>(lds.bcs[(i + 1) & 1], bra, cra);
         if constexpr (S > 1)
-            stage_tokens<S, IO, OUTPUT && HAS_D>(lds.dtdu[(i + 1) & 1], w, nxt, dskip, skn);
+            stage_tokens<S, IO, SP, OUTPUT && HAS_D>(lds.dtdu[(i + 1) & 1], w, nxt, dbias, dskip,
+                                                     skn);
         __syncthreads();
         if constexpr (OUTPUT && S > 1)
             finalize_tile<S, IO, HAS_Z, FULL>(io, lds.red[i & 1], w, i, cnt, cur, skc);
@@ -435,7 +421,8 @@ __device__ __forceinline__ void scan_chunk(const ChunkIo& io, const BcIo& bcio, 
     fetch_bc<N, S, IO>(bcio, 0, min(TT, ntok), bra, cra);
     fetch_tile<S, IO, LOAD_Z>(io, 0, w, ntok, ta);
     stage_bc<N, S, IO>(lds.bcs[0], bra, cra);
-    if constexpr (S > 1) stage_tokens<S, IO, OUTPUT && HAS_D>(lds.dtdu[0], w, ta, dskip, ska);
+    if constexpr (S > 1)
+        stage_tokens<S, IO, SP, OUTPUT && HAS_D>(lds.dtdu[0], w, ta, dbias, dskip, ska);
     __syncthreads();
     int i = 0;
     for (; i + 2 <= nfull; i += 2) {
@@ -477,6 +464,7 @@ struct WaveSlot {
     int w;             // wave index inside the workgroup = state slice
     int n0;            // first state of the slice
     int ntok;          // tokens of the chunk
+    float dbias;       // this lane's delta bias (0 without one)
     ChunkIo io;
     BcIo bc;
 };
@@ -496,6 +484,7 @@ __device__ __forceinline__ WaveSlot wave_slot(const ScanArgs& a, const ChunkGrid
     const int64_t t0 = s.k * g.chunk_len;
     const int64_t t1 = min(a.seqlen, t0 + g.chunk_len);
     s.ntok = static_cast<int>(t1 - t0);
+    s.dbias = a.delta_bias != nullptr ? a.delta_bias[s.d] : 0.0f;
     const int64_t first = (s.b * a.seqlen + t0) * a.dim + d0;  // element (b, t0, d0)
     // bytes from (b, t0, d0) to the end of (b, t1-1, dim-1); below 2^32 by the plan
     const uint32_t extent = static_cast<uint32_t>(((t1 - t0) * a.dim - d0) * esz);
@@ -515,7 +504,7 @@ __device__ __forceinline__ WaveSlot wave_slot(const ScanArgs& a, const ChunkGrid
 
 // Pass 1: per-chunk summaries (end state, decay product), all chunks but the
 // last. Chunk 0 starts from h0, so its end state is already exact.
-template <int N, int S, int IO>
+template <int N, int S, int IO, bool SP>
 __global__ __launch_bounds__(kWave * S) __attribute__((amdgpu_waves_per_eu(S == 1 ? 4 : 6)))
 void chunk_summary_kernel(ScanArgs a, ChunkGrid g, Carry c) {
     constexpr int NPW = Split<N, S>::NPW;
@@ -533,8 +522,8 @@ void chunk_summary_kernel(ScanArgs a, ChunkGrid g, Carry c) {
     }
     __shared__ ScanLds<N, S> lds;
     float dsum = 0.0f;
-    scan_chunk<N, S, IO, false, false, false>(s.io, s.bc, s.ntok, s.w, s.n0, lds, A2, h, 0.0f,
-                                              dsum);
+    scan_chunk<N, S, IO, SP, false, false, false>(s.io, s.bc, s.dbias, s.ntok, s.w, s.n0, lds,
+                                                  A2, h, 0.0f, dsum);
 #pragma unroll
     for (int q = 0; q < NPW; ++q) {
         c.end[srow + q] = h[q];
@@ -559,7 +548,7 @@ __global__ __launch_bounds__(256) void chunk_carry_kernel(int64_t columns, int64
 
 // Pass 2 (or the only pass when nchunks == 1): scan each chunk from its true
 // entering state and write y; the last chunk writes hL.
-template <int N, int S, int IO, bool HAS_D, bool HAS_Z>
+template <int N, int S, int IO, bool SP, bool HAS_D, bool HAS_Z>
 __global__ __launch_bounds__(kWave * S) __attribute__((amdgpu_waves_per_eu(S <= 2 ? 2 : 4)))
 void chunk_output_kernel(ScanArgs a, ChunkGrid g, Carry c) {
     constexpr int NPW = Split<N, S>::NPW;
@@ -579,117 +568,17 @@ void chunk_output_kernel(ScanArgs a, ChunkGrid g, Carry c) {
     }
     const float dskip = HAS_D ? a.D[s.d] : 0.0f;
     float dsum = 0.0f;
-    scan_chunk<N, S, IO, true, HAS_D, HAS_Z>(s.io, s.bc, s.ntok, s.w, s.n0, lds, A2, h, dskip,
-                                             dsum);
+    scan_chunk<N, S, IO, SP, true, HAS_D, HAS_Z>(s.io, s.bc, s.dbias, s.ntok, s.w, s.n0, lds, A2,
+                                                 h, dskip, dsum);
     if (s.k == g.nchunks - 1 && a.hL != nullptr) {
 #pragma unroll
         for (int q = 0; q < NPW; ++q) a.hL[(s.b * a.dim + s.d) * N + s.n0 + q] = h[q];
     }
 }
 
-// seqlen == 0: hL = h0 (or zeros).
-__global__ __launch_bounds__(256) void state_init_kernel(int64_t count, const float* h0,
-                                                         float* hL) {
-    const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
-    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < count;
-         i += stride)
-        hL[i] = h0 != nullptr ? h0[i] : 0.0f;
-}
-
-// Grid for the grid-stride kernels above: enough 256-thread blocks to cover
-// `count` items, capped well below the 32-bit grid limit.
-inline int64_t stride_blocks(int64_t count) {
-    const int64_t b = (count + 255) / 256;
-    return b < (int64_t(1) << 20) ? (b > 0 ? b : 1) : (int64_t(1) << 20);
-}
-
-// ---------------------------------------------------------------------------
-// Single-token update. G lanes share one (b, d) and hold S = N / G states
-// each, so the fp32 state row of N floats is read and written as G
-// contiguous pieces and a wave's accesses are dense. The partial readouts
-// are summed across the G lanes with DPP moves inside a quad.
-template <int G>
-__device__ __forceinline__ float group_sum(float v) {
-    if constexpr (G == 1) {
-        return v;
-    } else {
-        static_assert(G == 4, "groups of 1 or 4 lanes");
-        // quad_perm [1,0,3,2] then [2,3,0,1]
-        v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
-        v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
-        return v;
-    }
-}
-
-template <int N, int G, int IO, bool HAS_D, bool HAS_Z>
-__global__ __launch_bounds__(256) void state_update_kernel(DecodeArgs a) {
-    constexpr int S = N / G;
-    const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-    const int64_t pairs = a.batch * a.dim;
-    const int64_t p_raw = gid / G;
-    const int part = static_cast<int>(gid % G);
-    const bool live = p_raw < pairs;
-    const int64_t p = live ? p_raw : pairs - 1;
-    const int64_t b = p / a.dim;
-    const int64_t d = p - b * a.dim;
-
-    float hv[S], Av[S], Bv[S], Cv[S];
-    float* hrow = a.h + p * N + part * S;
-    const float* arow = a.A + d * N + part * S;
-    if constexpr (S == 4) {
-        const float4 h4 = *reinterpret_cast<const float4*>(hrow);
-        const float4 a4 = *reinterpret_cast<const float4*>(arow);
-        hv[0] = h4.x; hv[1] = h4.y; hv[2] = h4.z; hv[3] = h4.w;
-        Av[0] = a4.x; Av[1] = a4.y; Av[2] = a4.z; Av[3] = a4.w;
-    } else {
-#pragma unroll
-        for (int s = 0; s < S; ++s) {
-            hv[s] = hrow[s];
-            Av[s] = arow[s];
-        }
-    }
-    const int64_t brow = b * N + part * S;
-    if constexpr (IO == kIoBF16 && S == 4) {
-        const uint2 bw = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.B) + brow);
-        const uint2 cw = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.C) + brow);
-        Bv[0] = __uint_as_float(bw.x << 16); Bv[1] = __uint_as_float(bw.x & 0xffff0000u);
-        Bv[2] = __uint_as_float(bw.y << 16); Bv[3] = __uint_as_float(bw.y & 0xffff0000u);
-        Cv[0] = __uint_as_float(cw.x << 16); Cv[1] = __uint_as_float(cw.x & 0xffff0000u);
-        Cv[2] = __uint_as_float(cw.y << 16); Cv[3] = __uint_as_float(cw.y & 0xffff0000u);
-    } else {
-#pragma unroll
-        for (int s = 0; s < S; ++s) {
-            Bv[s] = raw_to_f32<IO>(load_raw<IO>(a.B, brow + s));
-            Cv[s] = raw_to_f32<IO>(load_raw<IO>(a.C, brow + s));
-        }
-    }
-    const float dt = raw_to_f32<IO>(load_raw<IO>(a.delta, p));
-    const float u = raw_to_f32<IO>(load_raw<IO>(a.x, p));
-    const float du = dt * u;
-    float acc = 0.0f;
-#pragma unroll
-    for (int s = 0; s < S; ++s) {
-        const float e = fast_exp2(dt * (Av[s] * kLog2e));
-        hv[s] = fmaf(e, hv[s], du * Bv[s]);
-        acc = fmaf(Cv[s], hv[s], acc);
-    }
-    acc = group_sum<G>(acc);
-    if constexpr (HAS_D) acc = fmaf(a.D[d], u, acc);
-    if constexpr (HAS_Z) acc *= silu(raw_to_f32<IO>(load_raw<IO>(a.z, p)));
-    if (live) {
-        if constexpr (S == 4) {
-            *reinterpret_cast<float4*>(hrow) = make_float4(hv[0], hv[1], hv[2], hv[3]);
-        } else {
-#pragma unroll
-            for (int s = 0; s < S; ++s) hrow[s] = hv[s];
-        }
-        if (part == 0) store_io<IO>(a.y, p, acc);
-    }
-}
-
 // ---------------------------------------------------------------------------
 // Host-side dispatch over the compile-time variants.
-template <int N, int S, int IO>
+template <int N, int S, int IO, bool SP>
 hipError_t launch_scan_ns(const ScanArgs& a, const ScanPlan& plan, void* ws, hipStream_t s) {
     ChunkGrid g;
     g.nblk_d = (a.dim + kWave - 1) / kWave;
@@ -708,7 +597,7 @@ hipError_t launch_scan_ns(const ScanArgs& a, const ScanPlan& plan, void* ws, hip
         ChunkGrid g1 = g;
         g1.nchunks = plan.nchunks - 1;
         const int64_t blocks1 = g.nblk_d * g1.nchunks * a.batch;
-        hipLaunchKernelGGL((chunk_summary_kernel<N, S, IO>), dim3(blocks1), dim3(kWave * S), 0, s,
+        hipLaunchKernelGGL((chunk_summary_kernel<N, S, IO, SP>), dim3(blocks1), dim3(kWave * S), 0, s,
                            a, g1, c);
         hipLaunchKernelGGL(chunk_carry_kernel, dim3(stride_blocks(columns)), dim3(256), 0, s,
                            columns, plan.nchunks, c);
@@ -717,95 +606,42 @@ hipError_t launch_scan_ns(const ScanArgs& a, const ScanPlan& plan, void* ws, hip
     const dim3 grid(blocks), block(kWave * S);
     const bool has_d = a.D != nullptr, has_z = a.z != nullptr;
     if (has_d && has_z)
-        hipLaunchKernelGGL((chunk_output_kernel<N, S, IO, true, true>), grid, block, 0, s, a, g, c);
+        hipLaunchKernelGGL((chunk_output_kernel<N, S, IO, SP, true, true>), grid, block, 0, s, a, g, c);
     else if (has_d)
-        hipLaunchKernelGGL((chunk_output_kernel<N, S, IO, true, false>), grid, block, 0, s, a, g, c);
+        hipLaunchKernelGGL((chunk_output_kernel<N, S, IO, SP, true, false>), grid, block, 0, s, a, g, c);
     else if (has_z)
-        hipLaunchKernelGGL((chunk_output_kernel<N, S, IO, false, true>), grid, block, 0, s, a, g, c);
+        hipLaunchKernelGGL((chunk_output_kernel<N, S, IO, SP, false, true>), grid, block, 0, s, a, g, c);
     else
-        hipLaunchKernelGGL((chunk_output_kernel<N, S, IO, false, false>), grid, block, 0, s, a, g, c);
+        hipLaunchKernelGGL((chunk_output_kernel<N, S, IO, SP, false, false>), grid, block, 0, s, a, g, c);
     return hipGetLastError();
 }
 
 // The state split S is a compile-time parameter; every N supports S = 1 and
 // N = 16, 8 and 4 also support the splits that divide them (up to 8).
-template <int N, int IO>
+template <int N, int IO, bool SP>
 hipError_t launch_scan_n(const ScanArgs& a, const ScanPlan& plan, void* ws, hipStream_t s) {
     switch (plan.state_split) {
-        case 1: return launch_scan_ns<N, 1, IO>(a, plan, ws, s);
-        case 2: if constexpr (N % 2 == 0 && (N == 4 || N == 8 || N == 16)) return launch_scan_ns<N, 2, IO>(a, plan, ws, s); break;
-        case 4: if constexpr (N % 4 == 0 && (N == 4 || N == 8 || N == 16)) return launch_scan_ns<N, 4, IO>(a, plan, ws, s); break;
-        case 8: if constexpr (N % 8 == 0 && (N == 8 || N == 16)) return launch_scan_ns<N, 8, IO>(a, plan, ws, s); break;
+        case 1: return launch_scan_ns<N, 1, IO, SP>(a, plan, ws, s);
+        case 2: if constexpr (N % 2 == 0 && (N == 4 || N == 8 || N == 16)) return launch_scan_ns<N, 2, IO, SP>(a, plan, ws, s); break;
+        case 4: if constexpr (N % 4 == 0 && (N == 4 || N == 8 || N == 16)) return launch_scan_ns<N, 4, IO, SP>(a, plan, ws, s); break;
+        case 8: if constexpr (N % 8 == 0 && (N == 8 || N == 16)) return launch_scan_ns<N, 8, IO, SP>(a, plan, ws, s); break;
         default: break;
     }
     return hipErrorInvalidValue;
 }
 
-template <int N, int IO>
-hipError_t launch_decode_n(const DecodeArgs& a, hipStream_t s) {
-    constexpr int G = (N % 4 == 0) ? 4 : 1;
-    const int64_t lanes = a.batch * a.dim * G;
-    const int64_t blocks = (lanes + 255) / 256;
-    const bool has_d = a.D != nullptr, has_z = a.z != nullptr;
-    if (has_d && has_z)
-        hipLaunchKernelGGL((state_update_kernel<N, G, IO, true, true>), dim3(blocks), dim3(256), 0, s, a);
-    else if (has_d)
-        hipLaunchKernelGGL((state_update_kernel<N, G, IO, true, false>), dim3(blocks), dim3(256), 0, s, a);
-    else if (has_z)
-        hipLaunchKernelGGL((state_update_kernel<N, G, IO, false, true>), dim3(blocks), dim3(256), 0, s, a);
-    else
-        hipLaunchKernelGGL((state_update_kernel<N, G, IO, false, false>), dim3(blocks), dim3(256), 0, s, a);
-    return hipGetLastError();
-}
-
-template <int IO>
-hipError_t dispatch_scan(const ScanArgs& a, const ScanPlan& p, void* ws, hipStream_t s) {
-    switch (a.dstate) {
-#define MAMBA_CASE(n) case n: return launch_scan_n<n, IO>(a, p, ws, s);
-        MAMBA_CASE(1) MAMBA_CASE(2) MAMBA_CASE(3) MAMBA_CASE(4) MAMBA_CASE(5) MAMBA_CASE(6)
-        MAMBA_CASE(7) MAMBA_CASE(8) MAMBA_CASE(9) MAMBA_CASE(10) MAMBA_CASE(11) MAMBA_CASE(12)
-        MAMBA_CASE(13) MAMBA_CASE(14) MAMBA_CASE(15) MAMBA_CASE(16)
-#undef MAMBA_CASE
-        default: return hipErrorInvalidValue;
-    }
-}
-
-template <int IO>
-hipError_t dispatch_decode(const DecodeArgs& a, hipStream_t s) {
-    switch (a.dstate) {
-#define MAMBA_CASE(n) case n: return launch_decode_n<n, IO>(a, s);
-        MAMBA_CASE(1) MAMBA_CASE(2) MAMBA_CASE(3) MAMBA_CASE(4) MAMBA_CASE(5) MAMBA_CASE(6)
-        MAMBA_CASE(7) MAMBA_CASE(8) MAMBA_CASE(9) MAMBA_CASE(10) MAMBA_CASE(11) MAMBA_CASE(12)
-        MAMBA_CASE(13) MAMBA_CASE(14) MAMBA_CASE(15) MAMBA_CASE(16)
-#undef MAMBA_CASE
-        default: return hipErrorInvalidValue;
-    }
-}
-
 }  // namespace
 
-size_t scan_workspace_bytes(int64_t batch, int64_t dim, int dstate, int64_t nchunks) {
-    if (nchunks <= 1) return 0;
-    return static_cast<size_t>(3) * static_cast<size_t>(nchunks) * static_cast<size_t>(batch) *
-           static_cast<size_t>(dim) * static_cast<size_t>(dstate) * sizeof(float);
-}
-
-hipError_t launch_scan(const ScanArgs& a, const ScanPlan& plan, void* workspace,
-                       hipStream_t stream) {
-    if (a.seqlen == 0) {
-        if (a.hL == nullptr) return hipSuccess;
-        const int64_t count = a.batch * a.dim * a.dstate;
-        hipLaunchKernelGGL(state_init_kernel, dim3(stride_blocks(count)), dim3(256), 0, stream,
-                           count, a.h0, a.hL);
-        return hipGetLastError();
+template <int IO, bool SP>
+hipError_t launch_scan_variant(const ScanArgs& a, const ScanPlan& p, void* ws, hipStream_t s) {
+    switch (a.dstate) {
+#define MAMBA_CASE(n) case n: return launch_scan_n<n, IO, SP>(a, p, ws, s);
+        MAMBA_CASE(1) MAMBA_CASE(2) MAMBA_CASE(3) MAMBA_CASE(4) MAMBA_CASE(5) MAMBA_CASE(6)
+        MAMBA_CASE(7) MAMBA_CASE(8) MAMBA_CASE(9) MAMBA_CASE(10) MAMBA_CASE(11) MAMBA_CASE(12)
+        MAMBA_CASE(13) MAMBA_CASE(14) MAMBA_CASE(15) MAMBA_CASE(16)
+#undef MAMBA_CASE
+        default: return hipErrorInvalidValue;
     }
-    return a.io == kIoF32 ? dispatch_scan<kIoF32>(a, plan, workspace, stream)
-                          : dispatch_scan<kIoBF16>(a, plan, workspace, stream);
-}
-
-hipError_t launch_state_update(const DecodeArgs& a, hipStream_t stream) {
-    return a.io == kIoF32 ? dispatch_decode<kIoF32>(a, stream)
-                          : dispatch_decode<kIoBF16>(a, stream);
 }
 
 }  // namespace mamba

@@ -19,6 +19,13 @@ Recipe shared by every workload:
   - x, z, B, C ~ N(0, 1), drawn in fp32 and rounded to the I/O dtype.
   - h0: None (zero state) or N(0, 1) fp32.
 Draw order: A, D, x, delta, z, B, C, h0.
+
+With raw_delta=True the inputs are those of a call that leaves the delta
+activation to the kernels: delta is the pre-activation N(0, 1) * delta_std
+(rounded to the I/O dtype) and delta_bias (dim,) fp32 is
+delta_shift + N(0, 1) * 0.5, drawn last; softplus(delta + delta_bias) then
+has the distribution of the default recipe's delta, give or take the
+per-channel spread.
 """
 from dataclasses import dataclass, field
 
@@ -120,9 +127,11 @@ def _a_matrix(w, g, device, dim=None):
     raise ValueError(w.a_init)
 
 
-def generate_scan(w, device="cpu", batch=None, seqlen=None, dim=None, seed=None):
+def generate_scan(w, device="cpu", batch=None, seqlen=None, dim=None, seed=None,
+                  raw_delta=False):
     """Inputs for one scan call of workload `w` (sizes may be overridden for
-    small parity cases). Returns a dict with keys x, delta, A, B, C, D, z, h0."""
+    small parity cases). Returns a dict with keys x, delta, A, B, C, D, z, h0
+    (and delta_bias with raw_delta=True)."""
     batch = w.batch if batch is None else batch
     seqlen = w.seqlen if seqlen is None else seqlen
     dim = w.dim if dim is None else dim
@@ -132,19 +141,30 @@ def generate_scan(w, device="cpu", batch=None, seqlen=None, dim=None, seed=None)
     A = _a_matrix(w, g, device, dim)
     D = torch.randn(dim, generator=g, device=device, dtype=torch.float32)
     x = _normal((batch, seqlen, dim), g, device, dt)
-    delta = _softplus_normal((batch, seqlen, dim), g, device, dt, w.delta_shift, w.delta_std)
+    if raw_delta:
+        delta = _normal((batch, seqlen, dim), g, device, dt, std=w.delta_std)
+    else:
+        delta = _softplus_normal((batch, seqlen, dim), g, device, dt, w.delta_shift, w.delta_std)
     z = _normal((batch, seqlen, dim), g, device, dt)
     B = _normal((batch, seqlen, w.dstate), g, device, dt)
     C = _normal((batch, seqlen, w.dstate), g, device, dt)
     h0 = None
     if w.h0 == "normal":
         h0 = torch.randn(batch, dim, w.dstate, generator=g, device=device, dtype=torch.float32)
-    return dict(x=x, delta=delta, A=A, B=B, C=C, D=D, z=z, h0=h0)
+    out = dict(x=x, delta=delta, A=A, B=B, C=C, D=D, z=z, h0=h0)
+    if raw_delta:
+        out["delta_bias"] = _bias(dim, g, device, w.delta_shift)
+    return out
 
 
-def generate_decode_layer(w, layer, device="cpu", batch=None, dim=None):
+def _bias(dim, g, device, shift):
+    return torch.randn(dim, generator=g, device=device, dtype=torch.float32) * 0.5 + shift
+
+
+def generate_decode_layer(w, layer, device="cpu", batch=None, dim=None, raw_delta=False):
     """Inputs of one layer of a decode step: h (batch, dim, N) fp32 state and
-    one token of x, delta, z (batch, dim) and B, C (batch, N)."""
+    one token of x, delta, z (batch, dim) and B, C (batch, N) (and
+    delta_bias with raw_delta=True, as in generate_scan)."""
     batch = w.batch if batch is None else batch
     dim = w.dim if dim is None else dim
     dt = io_torch_dtype(w.io)
@@ -152,9 +172,15 @@ def generate_decode_layer(w, layer, device="cpu", batch=None, dim=None):
     A = _a_matrix(w, g, device, dim)
     D = torch.randn(dim, generator=g, device=device, dtype=torch.float32)
     x = _normal((batch, dim), g, device, dt)
-    delta = _softplus_normal((batch, dim), g, device, dt, w.delta_shift, w.delta_std)
+    if raw_delta:
+        delta = _normal((batch, dim), g, device, dt, std=w.delta_std)
+    else:
+        delta = _softplus_normal((batch, dim), g, device, dt, w.delta_shift, w.delta_std)
     z = _normal((batch, dim), g, device, dt)
     B = _normal((batch, w.dstate), g, device, dt)
     C = _normal((batch, w.dstate), g, device, dt)
     h = torch.randn(batch, dim, w.dstate, generator=g, device=device, dtype=torch.float32)
-    return dict(h=h, x=x, delta=delta, A=A, B=B, C=C, D=D, z=z)
+    out = dict(h=h, x=x, delta=delta, A=A, B=B, C=C, D=D, z=z)
+    if raw_delta:
+        out["delta_bias"] = _bias(dim, g, device, w.delta_shift)
+    return out

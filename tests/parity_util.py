@@ -36,12 +36,16 @@ def sample_channels(dim, count=24, seed=0):
 
 
 def oracle_on_channels(orc, inp, idx):
-    """The oracle over a subset of channels (channels are independent)."""
+    """The oracle over a subset of channels (channels are independent).
+    Inputs that carry a delta_bias are raw-delta inputs (ssm_workloads'
+    raw_delta=True) and run with the softplus activation."""
     ix = torch.as_tensor(idx, dtype=torch.long, device=inp["x"].device)
     sub = dict(
         x=inp["x"].index_select(2, ix), delta=inp["delta"].index_select(2, ix),
         A=inp["A"].index_select(0, ix), B=inp["B"], C=inp["C"],
         D=None if inp.get("D") is None else inp["D"].index_select(0, ix),
         z=None if inp.get("z") is None else inp["z"].index_select(2, ix),
-        h0=None if inp.get("h0") is None else inp["h0"].index_select(1, ix))
-    return orc.scan_fwd(**sub)
+        h0=None if inp.get("h0") is None else inp["h0"].index_select(1, ix),
+        delta_bias=(None if inp.get("delta_bias") is None
+                    else inp["delta_bias"].index_select(0, ix)))
+    return orc.scan_fwd(**sub, delta_softplus=inp.get("delta_bias") is not None)

@@ -51,12 +51,17 @@ def _plan(chunk_len=0, split=0, reserved=0):
     return ctypes.byref(ms.ScanPlan(chunk_len, split, reserved))
 
 
+def _opts(bias=None, softplus=0, reserved=0):
+    return ctypes.byref(ms.ScanOptions(bias, softplus, reserved))
+
+
 def _scan(lib, batch=2, seqlen=8, dim=64, dstate=16, dtype=1, ptrs=None, plan=None, ws=None,
-          wsb=0):
+          wsb=0, opts=None):
     p = dict(x=P, delta=P, A=P, B=P, C=P, D=None, z=None, h0=None, y=P, hL=None)
     p.update(ptrs or {})
     return lib.ssm_scan_fwd(batch, seqlen, dim, dstate, dtype, p["x"], p["delta"], p["A"], p["B"],
-                            p["C"], p["D"], p["z"], p["h0"], p["y"], p["hL"], plan, ws, wsb, None)
+                            p["C"], p["D"], p["z"], p["h0"], p["y"], p["hL"], opts, plan, ws, wsb,
+                            None)
 
 
 def test_scan_rejects_bad_shapes(lib):
@@ -80,6 +85,14 @@ def test_scan_rejects_null_and_misaligned(lib):
         assert _scan(lib, ptrs={name: None}) == INVALID, name
     for name in ("x", "delta", "A", "B", "C", "D", "z", "h0", "y", "hL"):
         assert _scan(lib, ptrs={name: PM}) == MISALIGNED, name
+
+
+def test_scan_options_checked(lib):
+    assert _scan(lib, opts=_opts(reserved=1)) == INVALID
+    assert _scan(lib, opts=_opts(bias=PM.value)) == MISALIGNED
+    assert _scan(lib, opts=_opts(bias=PM.value, softplus=1)) == MISALIGNED
+    # a rejected option wins over an otherwise valid no-op call
+    assert _scan(lib, batch=0, opts=_opts(reserved=2)) == INVALID
 
 
 def test_scan_workspace_check(lib):
@@ -114,11 +127,11 @@ def test_scan_empty_shapes_are_noops(lib):
 
 
 def test_state_update_rejects_bad_arguments(lib):
-    def upd(batch=4, dim=64, dstate=16, dtype=1, **kw):
+    def upd(batch=4, dim=64, dstate=16, dtype=1, opts=None, **kw):
         p = dict(h=P, x=P, delta=P, A=P, B=P, C=P, D=None, z=None, y=P)
         p.update(kw)
         return lib.ssm_state_update(batch, dim, dstate, dtype, p["h"], p["x"], p["delta"], p["A"],
-                                    p["B"], p["C"], p["D"], p["z"], p["y"], None)
+                                    p["B"], p["C"], p["D"], p["z"], p["y"], opts, None)
     assert upd(batch=-1) == INVALID
     assert upd(dstate=17) == UNSUPPORTED
     assert upd(dtype=2) == INVALID
@@ -127,6 +140,8 @@ def test_state_update_rejects_bad_arguments(lib):
     for name in ("h", "x", "delta", "A", "B", "C", "D", "z", "y"):
         assert upd(**{name: PM}) == MISALIGNED, name
     assert upd(batch=0) == OK
+    assert upd(opts=_opts(reserved=1)) == INVALID
+    assert upd(opts=_opts(bias=PM.value, softplus=1)) == MISALIGNED
 
 
 def test_python_binding_requires_gpu_tensors():

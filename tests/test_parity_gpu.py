@@ -7,6 +7,7 @@ final state. Full-size workloads run in the same launch configuration the
 benchmark times (automatic chunk plan) and are compared on sampled channels
 over every batch row and every token; small cases are compared everywhere.
 """
+import dataclasses
 import sys
 
 import numpy as np
@@ -41,6 +42,10 @@ def _gen(w, **kw):
 
 
 def _run(inp, **kw):
+    # inputs with a delta_bias are raw-delta inputs: the kernels activate them
+    if inp.get("delta_bias") is not None:
+        kw.setdefault("delta_bias", inp["delta_bias"])
+        kw.setdefault("delta_softplus", True)
     y, hL = ms.scan_fwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp.get("D"),
                         inp.get("z"), inp.get("h0"), **kw)
     torch.cuda.synchronize()
@@ -48,7 +53,7 @@ def _run(inp, **kw):
 
 
 def _full_compare(orc, inp, y, hL, tol, what):
-    yo, ho = orc.scan_fwd(**inp)
+    yo, ho = orc.scan_fwd(**inp, delta_softplus=inp.get("delta_bias") is not None)
     assert_close(y, yo, tol, f"{what} y")
     assert_close(hL, ho, tol, f"{what} hL")
 
@@ -310,3 +315,110 @@ def test_nan_propagates():
     y, hL = _run(inp)
     assert torch.isnan(y[0, 10:, 5]).all()
     assert torch.isfinite(y[0, :10]).all() and torch.isfinite(y[0, :, 6]).all()
+
+
+# ---------------------------------------------------------------------------
+# fused delta bias and softplus (delta given before its activation)
+
+
+def test_softplus_values_across_range():
+    # One state, A ~ 0, x = B = C = 1 and a zero start: the first output is
+    # the activated delta itself, so y reads softplus(v + bias) directly. The
+    # fp64 reference is numpy's logaddexp(0, v), independent of the oracle.
+    # The sum v + bias is rounded to fp32 first, and softplus magnifies a
+    # relative input error by up to |v| where it decays like exp(v), hence
+    # the |v|-dependent bound.
+    v = np.concatenate([np.linspace(-120.0, 120.0, 4001), [-1e-7, 0.0, 1e-7, 1e-3, -1e-3],
+                        -np.logspace(-6, 2, 300), np.logspace(-6, 2, 300)]).astype(np.float32)
+    n = v.size
+    dim = 64
+    rows = (n + dim - 1) // dim
+    vv = np.zeros(rows * dim, np.float32)
+    vv[:n] = v
+    bias = np.linspace(-0.5, 0.5, dim).astype(np.float32)
+    raw = (vv.reshape(rows, dim) - bias).astype(np.float32)      # raw + bias ~ v
+    ones = torch.ones(rows, 1, 1, device=DEV)
+    A = torch.full((dim, 1), -1e-30, device=DEV)
+    x1 = torch.ones(rows, 1, dim, device=DEV)
+    _say(f"case softplus values: {n} points")
+    y, _ = ms.scan_fwd(x1, torch.as_tensor(raw, device=DEV).view(rows, 1, dim), A, ones, ones,
+                       delta_bias=torch.as_tensor(bias, device=DEV), delta_softplus=True)
+    torch.cuda.synchronize()
+    got = y.view(-1).double().cpu().numpy()
+    vin = raw.reshape(-1).astype(np.float64) + np.tile(bias.astype(np.float64), rows)
+    want = np.logaddexp(0.0, vin)
+    eps = 2.0 ** -24
+    bound = want * (8.0 + 2.0 * np.abs(vin)) * eps + 1e-37
+    bad = np.abs(got - want) > bound
+    assert not bad.any(), (f"softplus off at v={vin[bad][:5]}: got {got[bad][:5]}, "
+                           f"want {want[bad][:5]}")
+    # special values: +-inf and NaN
+    sp = torch.tensor([[[float("inf"), float("-inf"), float("nan")] + [0.0] * 61]], device=DEV)
+    y, _ = ms.scan_fwd(torch.ones(1, 1, 64, device=DEV), sp, A, torch.ones(1, 1, 1, device=DEV),
+                       torch.ones(1, 1, 1, device=DEV), delta_softplus=True)
+    torch.cuda.synchronize()
+    assert y[0, 0, 0] == float("inf") and y[0, 0, 1] == 0.0 and torch.isnan(y[0, 0, 2])
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_delta_softplus_scan(orc, io):
+    # raw delta + per-channel bias through softplus inside the kernels, for
+    # every state split, with and without sequence chunks
+    w = W.WORKLOADS["mamba28b_layer"]
+    for dstate, split in ((16, 1), (16, 2), (16, 4), (16, 8), (4, 2), (5, 1)):
+        inp = _gen(dataclasses.replace(w, io=io, dstate=dstate, h0="normal"), batch=2, seqlen=203, dim=100, seed=dstate * 7 + split, raw_delta=True)
+        yo, ho = orc.scan_fwd(**inp, delta_softplus=True)
+        for chunk_len in (0, 24):
+            _say(f"case delta softplus N={dstate} split={split} chunk_len={chunk_len} {io}")
+            y, hL = _run(inp, chunk_len=chunk_len, state_split=split)
+            assert_close(y, yo, TOL[io], f"softplus N={dstate} split={split} chunk={chunk_len} y")
+            assert_close(hL, ho, TOL[io], f"softplus N={dstate} split={split} chunk={chunk_len} hL")
+
+
+def test_delta_bias_without_softplus(orc):
+    inp = _case_inputs(2, 150, 70, 16, "f32", seed=12)
+    bias = torch.linspace(0.0, 0.3, 70, device=DEV)
+    yo, ho = orc.scan_fwd(**inp, delta_bias=bias)
+    for split, chunk_len in ((1, 0), (4, 0), (4, 32)):
+        _say(f"case delta bias only split={split} chunk_len={chunk_len}")
+        y, hL = _run(inp, delta_bias=bias, state_split=split, chunk_len=chunk_len)
+        assert_close(y, yo, TOL["f32"], "bias-only y")
+        assert_close(hL, ho, TOL["f32"], "bias-only hL")
+    # softplus without a bias
+    raw = inp["delta"] - 0.7
+    inp2 = dict(inp, delta=raw)
+    yo, ho = orc.scan_fwd(**inp2, delta_softplus=True)
+    _say("case softplus without bias")
+    y, hL = _run(inp2, delta_softplus=True)
+    assert_close(y, yo, TOL["f32"], "softplus-only y")
+    assert_close(hL, ho, TOL["f32"], "softplus-only hL")
+
+
+def test_delta_softplus_full_size_sampled(orc):
+    w = W.WORKLOADS["mamba28b_layer"]
+    inp = W.generate_scan(w, device=DEV, raw_delta=True)
+    _say(f"case {w.name} raw delta + softplus, full size, automatic plan")
+    y, hL = _run(inp)
+    idx = sample_channels(w.dim, seed=w.seed + 1)
+    yo, ho = oracle_on_channels(orc, inp, idx)
+    ix = torch.as_tensor(idx, device=DEV)
+    assert_close(y.index_select(2, ix), yo, TOL["bf16"], "full-size softplus y (sampled)")
+    assert_close(hL.index_select(1, ix), ho, TOL["bf16"], "full-size softplus hL (sampled)")
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_decode_delta_softplus(orc, io):
+    w = W.WORKLOADS["decode_64layer"]
+    for dstate in (16, 3):
+        ww = dataclasses.replace(w, io=io, dstate=dstate)
+        d = {k: v.to(DEV) for k, v in
+             W.generate_decode_layer(ww, 5, batch=9, dim=130, raw_delta=True).items()}
+        h_before = d["h"].clone()
+        _say(f"case decode softplus N={dstate} {io}")
+        y = ms.state_update(d["h"], d["x"], d["delta"], d["A"], d["B"], d["C"], d["D"], d["z"],
+                            delta_bias=d["delta_bias"], delta_softplus=True)
+        torch.cuda.synchronize()
+        yo, ho = orc.state_update(h_before, d["x"], d["delta"], d["A"], d["B"], d["C"], d["D"],
+                                  d["z"], delta_bias=d["delta_bias"], delta_softplus=True)
+        assert_close(y, yo, TOL[io], f"decode softplus N={dstate} {io} y")
+        assert_close(d["h"], ho, TOL[io], f"decode softplus N={dstate} {io} state")
