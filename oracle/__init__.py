@@ -38,6 +38,10 @@ def _load(path=None):
     lib.oracle_state_update.argtypes = [i64, i64, i64] + [dp] * 9 + [dp, ctypes.c_int]
     lib.oracle_state_update.restype = ctypes.c_int
     lib.oracle_max_dstate.restype = ctypes.c_int
+    lib.oracle_conv1d_fwd.argtypes = [i64] * 4 + [dp] * 6 + [ctypes.c_int]
+    lib.oracle_conv1d_fwd.restype = ctypes.c_int
+    lib.oracle_conv1d_update.argtypes = [i64] * 3 + [dp] * 5 + [ctypes.c_int]
+    lib.oracle_conv1d_update.restype = ctypes.c_int
     return lib
 
 
@@ -110,6 +114,44 @@ class Oracle:
         if rc != 0:
             raise ValueError(f"oracle_state_update rejected its arguments (status {rc})")
         return y, h
+
+
+    def conv1d_fwd(self, x, weight, bias=None, state_in=None, silu=True, return_state=True):
+        """Short causal depthwise convolution over whole sequences.
+
+        Shapes: x (batch, L, dim); weight (dim, W); bias (dim,); state_in
+        (batch, dim, W), the last W inputs before the sequence (None: zeros).
+        Returns (y, state_out) as fp64 numpy arrays: y (batch, L, dim) and
+        state_out (batch, dim, W), the last W inputs after the sequence.
+        """
+        x, weight, bias, state_in = _f64(x), _f64(weight), _f64(bias), _f64(state_in)
+        batch, seqlen, dim = x.shape
+        width = weight.shape[1]
+        assert weight.shape == (dim, width)
+        assert bias is None or bias.shape == (dim,)
+        assert state_in is None or state_in.shape == (batch, dim, width)
+        y = np.zeros((batch, seqlen, dim), dtype=np.float64)
+        st = np.zeros((batch, dim, width), dtype=np.float64) if return_state else None
+        rc = self.lib.oracle_conv1d_fwd(batch, seqlen, dim, width, _ptr(x), _ptr(weight),
+                                        _ptr(bias), _ptr(state_in), _ptr(y), _ptr(st),
+                                        int(bool(silu)))
+        if rc != 0:
+            raise ValueError(f"oracle_conv1d_fwd rejected its arguments (status {rc})")
+        return y, st
+
+    def conv1d_update(self, state, x, weight, bias=None, silu=True):
+        """One decode step of the convolution. Shapes: state (batch, dim, W);
+        x (batch, dim). Returns (y, state_new); the input state is not modified."""
+        state = _f64(state).copy()
+        x, weight, bias = _f64(x), _f64(weight), _f64(bias)
+        batch, dim, width = state.shape
+        assert x.shape == (batch, dim) and weight.shape == (dim, width)
+        y = np.zeros((batch, dim), dtype=np.float64)
+        rc = self.lib.oracle_conv1d_update(batch, dim, width, _ptr(state), _ptr(x), _ptr(weight),
+                                           _ptr(bias), _ptr(y), int(bool(silu)))
+        if rc != 0:
+            raise ValueError(f"oracle_conv1d_update rejected its arguments (status {rc})")
+        return y, state
 
 
 def get():

@@ -123,3 +123,79 @@ int oracle_state_update(int64_t batch, int64_t dim, int64_t dstate, double* h,
     return oracle_scan_fwd(batch, 1, dim, dstate, x, delta, A, Bm, Cm, Dskip, z,
                            h, y, h, 0, delta_bias, delta_softplus);
 }
+
+/*
+ * Short causal convolution of the Mamba block (page "Mamba and State Space
+ * Models", section "A State of Fixed Size": besides the SSM state each
+ * channel keeps a short convolution over its last 4 inputs; the podcast page
+ * and the dictionary page name the same short convolution as part of the
+ * block). The pages give no formula; the plainest reading, used here:
+ *
+ *   pre[b,t,d] = bias[d] + sum_{k=0}^{W-1} weight[d,k] * x[b, t-(W-1)+k, d]
+ *   y[b,t,d]   = silu(pre) if `silu`, else pre
+ *
+ * i.e. each channel is filtered on its own (depthwise) and only the current
+ * and the W-1 previous inputs are seen (causal); weight[d, W-1] multiplies
+ * the current token. Inputs before the first token come from `state_in`, the
+ * last W inputs of whatever preceded the sequence (state_in[b,d,W-1] is the
+ * newest), or are zero when it is NULL. `state_out` receives the last W
+ * inputs as the sequence leaves them, in the same layout, so the next call
+ * (or the next decode step) continues the sequence exactly.
+ *
+ * Layout: x, y (batch, L, dim), dim contiguous; weight (dim, W); bias (dim)
+ * or NULL; state_in, state_out (batch, dim, W) or NULL. Every array is fp64.
+ * state_out may alias state_in.
+ */
+static double conv_input(const double* x, const double* carried, int64_t b, int64_t s,
+                         int64_t d, int64_t seqlen, int64_t dim, int64_t width)
+{
+    /* input s of channel (b, d); s < 0 reaches into the W carried inputs */
+    if (s >= 0) return x[(b * seqlen + s) * dim + d];
+    return carried[width + s];
+}
+
+int oracle_conv1d_fwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t width,
+                      const double* x, const double* weight, const double* bias,
+                      const double* state_in, double* y, double* state_out, int silu)
+{
+    if (batch < 0 || seqlen < 0 || dim < 0 || width < 1 || width > 64) return -1;
+    if (batch == 0 || dim == 0) return 0;
+    if (!weight || (seqlen > 0 && (!x || !y))) return -1;
+
+    #pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t b = 0; b < batch; ++b) {
+        for (int64_t d = 0; d < dim; ++d) {
+            /* copied first, so state_out may alias state_in */
+            double carried[64];
+            for (int64_t k = 0; k < width; ++k)
+                carried[k] = state_in ? state_in[(b * dim + d) * width + k] : 0.0;
+
+            for (int64_t t = 0; t < seqlen; ++t) {
+                double pre = bias ? bias[d] : 0.0;
+                for (int64_t k = 0; k < width; ++k)
+                    pre += weight[d * width + k] *
+                           conv_input(x, carried, b, t - (width - 1) + k, d, seqlen, dim, width);
+                y[(b * seqlen + t) * dim + d] = silu ? pre / (1.0 + exp(-pre)) : pre;
+            }
+            if (state_out)
+                for (int64_t k = 0; k < width; ++k)
+                    state_out[(b * dim + d) * width + k] =
+                        conv_input(x, carried, b, seqlen - width + k, d, seqlen, dim, width);
+        }
+    }
+    return 0;
+}
+
+/*
+ * Decode step of the short convolution: the new input joins the W carried
+ * inputs (the oldest drops out) and one output is produced. By definition
+ * the forward convolution over one token with state_in = state_out = state.
+ * x, y (batch, dim); state (batch, dim, W), updated in place.
+ */
+int oracle_conv1d_update(int64_t batch, int64_t dim, int64_t width, double* state,
+                         const double* x, const double* weight, const double* bias,
+                         double* y, int silu)
+{
+    if (!state) return -1;
+    return oracle_conv1d_fwd(batch, 1, dim, width, x, weight, bias, state, y, state, silu);
+}

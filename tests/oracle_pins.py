@@ -31,6 +31,17 @@ when it disagrees with an independent statement of the result:
   A ~ 0 and x = B = C = 1 the first output is delta itself, which must equal
   softplus(delta_raw + bias) as numpy's logaddexp(0, .) computes it; and the
   Theorem 1 gate identity holds with the softplus applied inside the scan.
+- pin_conv_numpy: the short causal convolution (section "A State of Fixed
+  Size": the last 4 inputs of each channel) equals numpy's convolve of the
+  carried inputs followed by the sequence with the reversed taps, plus the
+  bias, through scipy's logistic silu; the state it hands on is the last W
+  inputs of that same concatenation.
+- pin_conv_impulse: a unit impulse at token t0 (zero carried state) reads
+  out the taps newest-first: pre[t0 + j] = bias + weight[W-1-j], bias
+  elsewhere.
+- pin_conv_split_and_decode: convolving [0, L) equals [0, m) then [m, L)
+  from the handed-on state, bit for bit, and T decode steps equal the
+  convolution over T tokens.
 
 silu(z) = z * sigmoid(z) is evaluated with scipy's logistic function.
 """
@@ -48,6 +59,8 @@ def _close(got, want, rtol=RTOL, what=""):
     got = np.asarray(got)
     want = np.asarray(want)
     assert got.shape == want.shape, f"{what}: shape {got.shape} != {want.shape}"
+    if want.size == 0:
+        return
     scale = max(1.0, float(np.max(np.abs(want))))
     err = float(np.max(np.abs(got - want))) if want.size else 0.0
     assert err <= rtol * scale, f"{what}: max abs error {err:.3e} > {rtol:.1e} * {scale:.3e}"
@@ -291,5 +304,70 @@ def pin_delta_activation(orc, seed=19):
     assert np.array_equal(yd, yo[:, 0]) and np.array_equal(hd, ho), "decode activation"
 
 
+def _conv_inputs(rng, batch, L, dim, width):
+    return dict(x=rng.standard_normal((batch, L, dim)),
+                weight=rng.standard_normal((dim, width)),
+                bias=rng.standard_normal(dim),
+                state_in=rng.standard_normal((batch, dim, width)))
+
+
+def pin_conv_numpy(orc, seed=21):
+    rng = np.random.default_rng(seed)
+    for width in (1, 2, 3, 4):
+        for L in (0, 1, 2, 3, 5, 17):
+            inp = _conv_inputs(rng, 2, L, 5, width)
+            for silu in (True, False):
+                for with_state in (True, False):
+                    args = dict(inp) if with_state else dict(inp, state_in=None)
+                    y, st = orc.conv1d_fwd(**args, silu=silu)
+                    want_y = np.empty((2, L, 5))
+                    want_s = np.empty((2, 5, width))
+                    for b in range(2):
+                        for d in range(5):
+                            carried = (inp["state_in"][b, d] if with_state else np.zeros(width))
+                            ext = np.concatenate([carried, inp["x"][b, :, d]])
+                            taps = inp["weight"][d]
+                            # valid[i] = sum_m ext[i + m] * taps[m]; token t is i = t + 1
+                            valid = np.convolve(ext, taps[::-1], mode="valid")
+                            pre = valid[1:] + inp["bias"][d]
+                            want_y[b, :, d] = _silu(pre) if silu else pre
+                            want_s[b, d] = ext[-width:]
+                    _close(y, want_y, what=f"conv numpy W={width} L={L} silu={silu}")
+                    assert np.array_equal(st, want_s), f"conv state W={width} L={L}"
+
+
+def pin_conv_impulse(orc, seed=22):
+    rng = np.random.default_rng(seed)
+    width, L, t0 = 4, 12, 5
+    w = rng.standard_normal((3, width))
+    bias = rng.standard_normal(3)
+    x = np.zeros((1, L, 3))
+    x[0, t0, :] = 1.0
+    y, st = orc.conv1d_fwd(x, w, bias, silu=False)
+    for d in range(3):
+        want = np.full(L, bias[d])
+        for j in range(width):
+            want[t0 + j] += w[d, width - 1 - j]
+        _close(y[0, :, d], want, rtol=1e-15, what="conv impulse response")
+
+
+def pin_conv_split_and_decode(orc, seed=23):
+    rng = np.random.default_rng(seed)
+    width = 4
+    inp = _conv_inputs(rng, 3, 23, 6, width)
+    y, st = orc.conv1d_fwd(**inp)
+    for m in (0, 1, 2, 3, 4, 10, 22, 23):
+        y1, s1 = orc.conv1d_fwd(**dict(inp, x=inp["x"][:, :m]))
+        y2, s2 = orc.conv1d_fwd(**dict(inp, x=inp["x"][:, m:], state_in=s1))
+        assert np.array_equal(np.concatenate([y1, y2], axis=1), y), f"conv split at {m}: y"
+        assert np.array_equal(s2, st), f"conv split at {m}: state"
+    s = inp["state_in"].copy()
+    for t in range(23):
+        yt, s = orc.conv1d_update(s, inp["x"][:, t], inp["weight"], inp["bias"])
+        assert np.array_equal(yt, y[:, t]), f"conv decode step {t}"
+    assert np.array_equal(s, st), "conv decode state"
+
+
 ALL_PINS = [pin_lti_convolution, pin_brute_force, pin_chunk_split, pin_theorem1,
-            pin_ssd_matrix, pin_limits, pin_structure, pin_decode, pin_delta_activation]
+            pin_ssd_matrix, pin_limits, pin_structure, pin_decode, pin_delta_activation,
+            pin_conv_numpy, pin_conv_impulse, pin_conv_split_and_decode]

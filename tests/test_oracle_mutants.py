@@ -45,6 +45,18 @@ MUTANTS = {
                            "hL[(b * dim + d) * dstate + n] = 0.5 * h[n];"),
     "zero-order hold sign": ("(Abar - 1.0) / a", "(1.0 - Abar) / a"),
     "skip uses the wrong channel": ("out += Dskip[d] * u;", "out += Dskip[dim - 1 - d] * u;"),
+    "conv taps reversed": ("pre += weight[d * width + k] *",
+                           "pre += weight[d * width + (width - 1 - k)] *"),
+    "conv taps shifted by one token": ("conv_input(x, carried, b, t - (width - 1) + k, d,",
+                                       "conv_input(x, carried, b, t - width + k, d,"),
+    "conv carried inputs newest first": ("return carried[width + s];", "return carried[-s - 1];"),
+    "conv silu dropped": ("silu ? pre / (1.0 + exp(-pre)) : pre;", "pre;"),
+    "conv bias dropped": ("double pre = bias ? bias[d] : 0.0;", "double pre = 0.0;"),
+    "conv state handed on one token early": ("conv_input(x, carried, b, seqlen - width + k, d,",
+                                             "conv_input(x, carried, b, seqlen - width + k - 1, d,"),
+    "conv carried state ignored": (
+        "carried[k] = state_in ? state_in[(b * dim + d) * width + k] : 0.0;",
+        "carried[k] = 0.0;"),
 }
 
 
