@@ -181,6 +181,10 @@ def main():
     if args.calibrate_copy:
         calibrate_copy()
         return
+    if args.workload in W.CONV_WORKLOADS:
+        cw = W.CONV_WORKLOADS[args.workload]
+        (bench_conv if cw.kind == "conv" else bench_conv_decode)(args, cw)
+        return
     w = W.WORKLOADS[args.workload]
     if w.kind == "decode":
         bench_decode(args, w)
@@ -360,6 +364,144 @@ def bench_decode(args, w):
         "cpu_baseline": None,
     }
     print(json.dumps(line), flush=True)
+
+
+def conv_bytes(w, state_in):
+    """Bytes one convolution call must move: x in and y out (I/O dtype), the
+    handed-on state out and, when there is one, the carried state in (I/O
+    dtype), weight and bias in (fp32)."""
+    s = 4 if w.io == "f32" else 2
+    b, l, d, k = w.batch, w.seqlen, w.dim, w.width
+    return 2 * b * l * d * s + b * d * k * s * (2 if state_in else 1) + d * k * 4 + d * 4
+
+
+def _time_steps(step, warmup, steps, stream):
+    import torch
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(steps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    return ev0.elapsed_time(ev1) / steps, time.perf_counter() - t0
+
+
+def bench_conv(args, w):
+    """One step = one causal_conv1d_fwd (+ silu) over the whole workload,
+    handing on the last W inputs; the convolution kernel and the small
+    state kernel are both inside the timed region."""
+    import torch
+
+    import selective_state_space_40_amd as ms
+    import ssm_workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    ms.load_library()
+    sets = [W.generate_conv(w, device=dev, seed=w.seed + 101 * i) for i in range(2)]
+    y = torch.empty_like(sets[0]["x"])
+    st = torch.empty(w.batch, w.dim, w.width, dtype=y.dtype, device=dev)
+
+    def step(i):
+        inp = sets[i % 2]
+        ms.conv1d_fwd(inp["x"], inp["weight"], inp["bias"], inp["state_in"], out=y, state_out=st)
+
+    ms_per_step, wall = _time_steps(step, args.warmup, args.steps, torch.cuda.current_stream(dev))
+    sec = ms_per_step / 1e3
+    elems = w.batch * w.seqlen * w.dim
+    nbytes = conv_bytes(w, sets[0]["state_in"] is not None)
+    gbps = nbytes / sec / 1e9
+    cpu = None if args.no_cpu_baseline else cpu_baseline_conv(w, sets[0])
+    line = {
+        "metric": "short causal convolution elements/s (B*L*D) and achieved HBM GB/s",
+        "value": elems / sec, "unit": "elements/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "seqlen": w.seqlen, "dim": w.dim,
+                   "width": w.width, "io_dtype": w.io, "silu": True,
+                   "parallelism": "single GPU"},
+        "achieved_GBps": round(gbps, 1), "wall_s": round(wall, 4),
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "conv1d_fwd_kernel + conv1d_state_out_kernel",
+                     "algorithmic_bytes": nbytes},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def bench_conv_decode(args, w):
+    """One step = one causal_conv1d_update per layer over all layers, each
+    with its own state, replayed as a HIP graph."""
+    import torch
+
+    import selective_state_space_40_amd as ms
+    import ssm_workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    ms.load_library()
+    layers = [W.generate_conv_decode_layer(w, l, device=dev) for l in range(w.layers)]
+    ys = [torch.empty_like(L["x"]) for L in layers]
+
+    def run():
+        for L, y in zip(layers, ys):
+            ms.conv1d_update(L["state"], L["x"], L["weight"], L["bias"], out=y)
+
+    stream = torch.cuda.Stream(dev)
+    stream.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(stream):
+        run()
+    torch.cuda.current_stream(dev).wait_stream(stream)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run()
+    ms_per_step, wall = _time_steps(lambda i: graph.replay(), args.warmup, args.steps,
+                                    torch.cuda.current_stream(dev))
+    sec = ms_per_step / 1e3
+    s = 4 if w.io == "f32" else 2
+    per_layer = (2 * w.batch * w.dim * w.width * s + 2 * w.batch * w.dim * s
+                 + w.dim * w.width * 4 + w.dim * 4)
+    nbytes = per_layer * w.layers
+    gbps = nbytes / sec / 1e9
+    line = {
+        "metric": "convolution decode elements/s (batch*D*layers per step) and achieved HBM GB/s",
+        "value": w.batch * w.dim * w.layers / sec, "unit": "elements/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "dim": w.dim, "width": w.width,
+                   "layers": w.layers, "io_dtype": w.io, "parallelism": "single GPU"},
+        "achieved_GBps": round(gbps, 1), "wall_s": round(wall, 4),
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "conv1d_update_kernel (64 launches per step, graph replay)",
+                     "algorithmic_bytes": nbytes},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline_conv(w, inp):
+    """The fp64 oracle's convolution on the host over the whole workload
+    (cheap enough to run in full)."""
+    import oracle
+
+    orc = oracle.get()
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    host = {k: (oracle._f64(v) if v is not None else None) for k, v in inp.items()}
+    t0 = time.perf_counter()
+    orc.conv1d_fwd(host["x"], host["weight"], host["bias"], host["state_in"])
+    dt = time.perf_counter() - t0
+    elems = w.batch * w.seqlen * w.dim
+    return {"value": elems / dt, "unit": "elements/s", "cores": threads, "kind": "oracle",
+            "sample": f"{w.name}: the whole workload, fp64, {dt:.2f} s"}
 
 
 def cpu_baseline(w, inp, channels, softplus=False):

@@ -56,7 +56,8 @@ typedef enum mamba_status {
     MAMBA_OK = 0,
     MAMBA_ERR_INVALID_ARG = -1,   /* negative size, NULL required pointer, bad dtype */
     MAMBA_ERR_UNSUPPORTED = -2,   /* dstate outside 1..MAMBA_SCAN_MAX_DSTATE, sizes too large,
-                                     a state split the kernels do not provide */
+                                     a state split the kernels do not provide, a
+                                     convolution width outside 1..MAMBA_CONV_MAX_WIDTH */
     MAMBA_ERR_MISALIGNED = -3,    /* a pointer is not 16-byte aligned */
     MAMBA_ERR_WORKSPACE = -4,     /* workspace NULL or smaller than required */
     MAMBA_ERR_HIP = -5            /* the HIP runtime reported an error */
@@ -172,6 +173,60 @@ int ssm_state_update(int64_t batch, int64_t dim, int dstate, int dtype, float* h
                      const void* x, const void* delta, const float* A,
                      const void* B, const void* C, const float* D, const void* z,
                      void* y, const mamba_scan_options* options, hipStream_t stream);
+
+/* Widest short convolution the library provides (the pages' width is 4). */
+#define MAMBA_CONV_MAX_WIDTH 4
+
+/*
+ * Short causal depthwise convolution of the Mamba block over whole
+ * sequences (page "Mamba and State Space Models", section "A State of Fixed
+ * Size": besides its SSM state each channel keeps the last 4 inputs of a
+ * short convolution). The pages give no formula; the library computes, per
+ * batch row b, channel d and token t,
+ *
+ *     pre[b,t,d] = bias[d] + sum_{k=0}^{W-1} weight[d,k] * x[b, t-(W-1)+k, d]
+ *     y[b,t,d]   = silu(pre) if silu != 0, else pre
+ *
+ * each channel filtered on its own and causally: weight[d, W-1] multiplies
+ * the current token. Inputs before token 0 come from state_in.
+ *
+ * x          (batch, seqlen, dim) I/O dtype   required when seqlen > 0
+ * weight     (dim, width) fp32                required; 1 <= width <= 4
+ * bias       (dim) fp32                       optional (NULL: no bias)
+ * state_in   (batch, dim, width) I/O dtype    optional: the last `width`
+ *                                             inputs before the sequence,
+ *                                             oldest first (NULL: zeros)
+ * y          (batch, seqlen, dim) I/O dtype   written
+ * state_out  (batch, dim, width) I/O dtype    optional: receives the last
+ *                                             `width` inputs of the sequence
+ *                                             (reaching into state_in when
+ *                                             seqlen < width); may be the
+ *                                             same buffer as state_in, but
+ *                                             must not partly overlap it
+ * The state holds inputs, so it is kept exactly in the I/O dtype. seqlen == 0
+ * copies state_in (or zeros) to state_out; batch == 0 or dim == 0 is a
+ * no-op. y must not overlap x or the states. Errors as for ssm_scan_fwd;
+ * a width outside 1..4 is MAMBA_ERR_UNSUPPORTED.
+ */
+int causal_conv1d_fwd(int64_t batch, int64_t seqlen, int64_t dim, int width, int dtype,
+                      const void* x, const float* weight, const float* bias,
+                      const void* state_in, void* y, void* state_out, int silu,
+                      hipStream_t stream);
+
+/*
+ * Decode step of the short convolution: the token's input joins the
+ * carried inputs (the oldest leaves) and one output is produced. Equivalent
+ * to causal_conv1d_fwd with seqlen = 1 and state_in = state_out = state.
+ *
+ * state      (batch, dim, width) I/O dtype    read and updated in place
+ * x          (batch, dim) I/O dtype           required
+ * weight     (dim, width) fp32                required
+ * bias       (dim) fp32                       optional
+ * y          (batch, dim) I/O dtype           written
+ */
+int causal_conv1d_update(int64_t batch, int64_t dim, int width, int dtype, void* state,
+                         const void* x, const float* weight, const float* bias, void* y,
+                         int silu, hipStream_t stream);
 
 /* Static, human-readable name of a mamba_status value. */
 const char* mamba_status_string(int status);

@@ -10,11 +10,15 @@ There is no other code path: without the built library every call raises.
                      delta_bias=None, delta_softplus=False)
     y = state_update(h, x, delta, A, B, C, D=None, z=None,
                      delta_bias=None, delta_softplus=False)   # h updated in place
+    y, state = conv1d_fwd(x, weight, bias=None, state_in=None, silu=True)
+    y = conv1d_update(state, x, weight, bias=None, silu=True)  # state updated in place
 
 Shapes (row-major, contiguous): x, delta, z, y (batch, L, dim); B, C
 (batch, L, N); A (dim, N) fp32; D and delta_bias (dim,) fp32; h0, hL
 (batch, dim, N) fp32. With delta_softplus the kernels use
-softplus(delta + delta_bias) in place of delta.
+softplus(delta + delta_bias) in place of delta. The short convolution takes
+x, y (batch, L, dim), weight (dim, W) fp32, bias (dim,) fp32 and a state of
+the last W inputs (batch, dim, W) in the dtype of x.
 x, delta, z, B and C share one dtype, float32 or bfloat16, and y has it too.
 """
 import ctypes
@@ -22,7 +26,7 @@ import os
 
 import torch
 
-__all__ = ["scan_fwd", "state_update", "workspace_size", "resolve_plan", "library_path",
+__all__ = ["scan_fwd", "state_update", "conv1d_fwd", "conv1d_update", "workspace_size", "resolve_plan", "library_path",
            "load_library", "MambaScanError", "MAX_DSTATE", "ScanPlan", "ScanOptions"]
 
 MAX_DSTATE = 16
@@ -76,6 +80,10 @@ def load_library():
     lib.ssm_scan_fwd.restype = i32
     lib.ssm_state_update.argtypes = [i64, i64, i32, i32] + [vp] * 9 + [po, vp]
     lib.ssm_state_update.restype = i32
+    lib.causal_conv1d_fwd.argtypes = [i64, i64, i64, i32, i32] + [vp] * 6 + [i32, vp]
+    lib.causal_conv1d_fwd.restype = i32
+    lib.causal_conv1d_update.argtypes = [i64, i64, i32, i32] + [vp] * 5 + [i32, vp]
+    lib.causal_conv1d_update.restype = i32
     lib.mamba_status_string.argtypes = [i32]
     lib.mamba_status_string.restype = ctypes.c_char_p
     _LIB = lib
@@ -225,4 +233,68 @@ def state_update(h, x, delta, A, B, C, D=None, z=None, *, delta_bias=None,
                                   _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(y),
                                   _options(delta_bias, delta_softplus), _stream(dev))
     _check(st, "ssm_state_update")
+    return y
+
+
+def conv1d_fwd(x, weight, bias=None, state_in=None, *, silu=True, return_state=True, out=None,
+               state_out=None):
+    """Short causal depthwise convolution over whole sequences; returns
+    (y, state_out) where state_out (batch, dim, W) holds the last W inputs
+    (None when return_state is False). state_in (batch, dim, W), in the dtype
+    of x, holds the W inputs before the sequence (None: zeros); state_out may
+    be the same tensor."""
+    lib = load_library()
+    if x.dim() != 3:
+        raise ValueError("x must be (batch, L, dim)")
+    batch, seqlen, dim = x.shape
+    if weight.dim() != 2 or weight.shape[0] != dim:
+        raise ValueError("weight must be (dim, W)")
+    width = weight.shape[1]
+    dev, dt = x.device, x.dtype
+    if dt not in _DTYPES:
+        raise ValueError(f"unsupported I/O dtype {dt}")
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU device")
+    _need(x, "x", (batch, seqlen, dim), dt, dev)
+    _need(weight, "weight", (dim, width), torch.float32, dev)
+    _need(bias, "bias", (dim,), torch.float32, dev)
+    _need(state_in, "state_in", (batch, dim, width), dt, dev)
+    y = out if out is not None else torch.empty_like(x)
+    _need(y, "out", (batch, seqlen, dim), dt, dev)
+    st = None
+    if return_state:
+        st = state_out if state_out is not None else torch.empty(batch, dim, width, dtype=dt,
+                                                                 device=dev)
+        _need(st, "state_out", (batch, dim, width), dt, dev)
+    with torch.cuda.device(dev):
+        rc = lib.causal_conv1d_fwd(batch, seqlen, dim, width, _DTYPES[dt], _ptr(x), _ptr(weight),
+                                   _ptr(bias), _ptr(state_in), _ptr(y), _ptr(st),
+                                   1 if silu else 0, _stream(dev))
+    _check(rc, "causal_conv1d_fwd")
+    return y, st
+
+
+def conv1d_update(state, x, weight, bias=None, *, silu=True, out=None):
+    """One decode step of the convolution: state (batch, dim, W), in the
+    dtype of x, is updated in place; returns y (batch, dim)."""
+    lib = load_library()
+    if state.dim() != 3:
+        raise ValueError("state must be (batch, dim, W)")
+    batch, dim, width = state.shape
+    dev, dt = x.device, x.dtype
+    if dt not in _DTYPES:
+        raise ValueError(f"unsupported I/O dtype {dt}")
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU device")
+    _need(state, "state", (batch, dim, width), dt, dev)
+    _need(x, "x", (batch, dim), dt, dev)
+    _need(weight, "weight", (dim, width), torch.float32, dev)
+    _need(bias, "bias", (dim,), torch.float32, dev)
+    y = out if out is not None else torch.empty_like(x)
+    _need(y, "out", (batch, dim), dt, dev)
+    with torch.cuda.device(dev):
+        rc = lib.causal_conv1d_update(batch, dim, width, _DTYPES[dt], _ptr(state), _ptr(x),
+                                      _ptr(weight), _ptr(bias), _ptr(y), 1 if silu else 0,
+                                      _stream(dev))
+    _check(rc, "causal_conv1d_update")
     return y

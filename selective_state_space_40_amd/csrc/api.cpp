@@ -17,6 +17,8 @@ namespace {
 
 using mamba::ScanPlan;
 
+static_assert(mamba::kConvMaxWidth == MAMBA_CONV_MAX_WIDTH, "convolution width limit");
+
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_cu_count[kMaxDevices];  // 0 = not queried yet
 
@@ -245,11 +247,74 @@ int ssm_state_update(int64_t batch, int64_t dim, int dstate, int dtype, float* h
     return mamba::launch_state_update(a, stream) == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP;
 }
 
+int causal_conv1d_fwd(int64_t batch, int64_t seqlen, int64_t dim, int width, int dtype,
+                      const void* x, const float* weight, const float* bias,
+                      const void* state_in, void* y, void* state_out, int silu,
+                      hipStream_t stream) {
+    int st = check_shape(batch, seqlen, dim, 1, dtype);
+    if (st != MAMBA_OK) return st;
+    if (width < 1 || width > MAMBA_CONV_MAX_WIDTH) return MAMBA_ERR_UNSUPPORTED;
+    if (batch == 0 || dim == 0) return MAMBA_OK;
+    if (weight == nullptr) return MAMBA_ERR_INVALID_ARG;
+    if (seqlen > 0 && (x == nullptr || y == nullptr)) return MAMBA_ERR_INVALID_ARG;
+    const void* ptrs[] = {x, weight, bias, state_in, y, state_out};
+    for (const void* p : ptrs)
+        if (p != nullptr && !aligned16(p)) return MAMBA_ERR_MISALIGNED;
+    if (seqlen == 0 && state_out == nullptr) return MAMBA_OK;
+
+    mamba::ConvArgs a;
+    a.batch = batch;
+    a.seqlen = seqlen;
+    a.dim = dim;
+    a.width = width;
+    a.io = dtype == MAMBA_DTYPE_F32 ? mamba::kIoF32 : mamba::kIoBF16;
+    a.silu = silu != 0;
+    a.x = x;
+    a.weight = weight;
+    a.bias = bias;
+    a.state_in = state_in;
+    a.y = y;
+    a.state_out = state_out;
+    a.fuse_state = 0;
+    return mamba::launch_conv1d(a, false, stream) == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP;
+}
+
+int causal_conv1d_update(int64_t batch, int64_t dim, int width, int dtype, void* state,
+                         const void* x, const float* weight, const float* bias, void* y,
+                         int silu, hipStream_t stream) {
+    int st = check_shape(batch, 1, dim, 1, dtype);
+    if (st != MAMBA_OK) return st;
+    if (width < 1 || width > MAMBA_CONV_MAX_WIDTH) return MAMBA_ERR_UNSUPPORTED;
+    if (batch == 0 || dim == 0) return MAMBA_OK;
+    if (state == nullptr || x == nullptr || weight == nullptr || y == nullptr)
+        return MAMBA_ERR_INVALID_ARG;
+    const void* ptrs[] = {state, x, weight, bias, y};
+    for (const void* p : ptrs)
+        if (p != nullptr && !aligned16(p)) return MAMBA_ERR_MISALIGNED;
+
+    mamba::ConvArgs a;
+    a.batch = batch;
+    a.seqlen = 1;
+    a.dim = dim;
+    a.width = width;
+    a.io = dtype == MAMBA_DTYPE_F32 ? mamba::kIoF32 : mamba::kIoBF16;
+    a.silu = silu != 0;
+    a.x = x;
+    a.weight = weight;
+    a.bias = bias;
+    a.state_in = state;
+    a.y = y;
+    a.state_out = state;
+    a.fuse_state = 0;
+    return mamba::launch_conv1d(a, true, stream) == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP;
+}
+
 const char* mamba_status_string(int status) {
     switch (status) {
         case MAMBA_OK: return "MAMBA_OK: success";
         case MAMBA_ERR_INVALID_ARG: return "MAMBA_ERR_INVALID_ARG: invalid argument";
-        case MAMBA_ERR_UNSUPPORTED: return "MAMBA_ERR_UNSUPPORTED: unsupported size or dstate";
+        case MAMBA_ERR_UNSUPPORTED:
+            return "MAMBA_ERR_UNSUPPORTED: unsupported size, dstate, split or width";
         case MAMBA_ERR_MISALIGNED: return "MAMBA_ERR_MISALIGNED: pointer not 16-byte aligned";
         case MAMBA_ERR_WORKSPACE: return "MAMBA_ERR_WORKSPACE: workspace missing or too small";
         case MAMBA_ERR_HIP: return "MAMBA_ERR_HIP: HIP runtime error";

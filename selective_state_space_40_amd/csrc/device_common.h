@@ -68,6 +68,20 @@ __device__ __forceinline__ float softplus_f32(float v) {
     return fmaxf(v, 0.0f) + l;
 }
 
+// Workgroups are handed to the chip's 8 XCDs in turn (workgroup i to XCD
+// i mod 8), and every XCD has its own L2. This maps the hardware workgroup
+// id to a logical one such that each XCD runs one contiguous range of
+// logical workgroups, so workgroups that are neighbours in the logical
+// order, and read neighbouring data, share an L2. It is a bijection on
+// [0, nblocks).
+constexpr int64_t kXcds = 8;
+
+__device__ __forceinline__ int64_t xcd_contiguous_block(int64_t bid, int64_t nblocks) {
+    const int64_t q = nblocks / kXcds, r = nblocks % kXcds;
+    const int64_t xcd = bid % kXcds, k = bid / kXcds;
+    return xcd < r ? xcd * (q + 1) + k : r * (q + 1) + (xcd - r) * q + k;
+}
+
 // Grid for the grid-stride kernels above: enough 256-thread blocks to cover
 // `count` items, capped well below the 32-bit grid limit.
 inline int64_t stride_blocks(int64_t count) {

@@ -74,6 +74,25 @@ struct DecodeArgs {
     int delta_softplus;
 };
 
+// Widest short convolution the kernels are built for.
+constexpr int kConvMaxWidth = 4;
+
+// Short causal convolution. For the decode step seqlen is 1 and state_in
+// and state_out are the same (batch, dim, width) buffer.
+struct ConvArgs {
+    int64_t batch, seqlen, dim;
+    int width;
+    int io;
+    int silu;
+    const void* x;
+    const float* weight;
+    const float* bias;
+    const void* state_in;
+    void* y;
+    void* state_out;
+    int fuse_state;  // set by the launcher: the forward kernel writes state_out itself
+};
+
 // Workspace layout for nchunks > 1: three fp32 arrays of
 // nchunks * batch * dim * dstate elements each: the state entering each
 // chunk, each chunk's end state from a zero start, and each chunk's decay
@@ -90,6 +109,10 @@ hipError_t launch_scan(const ScanArgs& a, const ScanPlan& plan, void* workspace,
 template <int IO, bool SP>
 hipError_t launch_scan_variant(const ScanArgs& a, const ScanPlan& plan, void* workspace,
                                hipStream_t stream);
+
+// Queue the convolution over whole sequences (update == false) or its
+// decode step (update == true). Arguments are already validated.
+hipError_t launch_conv1d(const ConvArgs& a, bool update, hipStream_t stream);
 
 // Queue the single-token update. Arguments are already validated.
 hipError_t launch_state_update(const DecodeArgs& a, hipStream_t stream);

@@ -32,7 +32,8 @@ from dataclasses import dataclass, field
 import torch
 
 __all__ = ["Workload", "WORKLOADS", "generate_scan", "generate_decode_layer",
-           "io_torch_dtype"]
+           "io_torch_dtype", "ConvWorkload", "CONV_WORKLOADS", "generate_conv",
+           "generate_conv_decode_layer"]
 
 
 @dataclass(frozen=True)
@@ -184,3 +185,80 @@ def generate_decode_layer(w, layer, device="cpu", batch=None, dim=None, raw_delt
     if raw_delta:
         out["delta_bias"] = _bias(dim, g, device, w.delta_shift)
     return out
+
+
+# ---------------------------------------------------------------------------
+# Short causal convolution workloads. The pages give the convolution's width
+# (the last 4 inputs of each channel, section "A State of Fixed Size") and
+# the Mamba-2.8B channel count, not its weights; the recipe:
+#   - weight (dim, W) and bias (dim,) fp32 ~ U(-1/sqrt(W), 1/sqrt(W)), the
+#     usual fan-in bound of a depthwise filter of W taps;
+#   - x ~ N(0, 1), drawn in fp32 and rounded to the I/O dtype;
+#   - carried state (batch, dim, W) in the I/O dtype: zeros for a sequence
+#     that starts fresh, N(0, 1) for decode.
+# Draw order: weight, bias, x, state.
+
+
+@dataclass(frozen=True)
+class ConvWorkload:
+    name: str
+    kind: str            # "conv" or "conv_decode"
+    batch: int
+    seqlen: int
+    dim: int
+    width: int
+    io: str
+    state: str           # "zero" or "normal": the carried inputs before the sequence
+    seed: int
+    layers: int = 1
+    note: str = field(default="", compare=False)
+
+    @property
+    def elements(self):
+        return self.batch * self.seqlen * self.dim * self.layers
+
+
+CONV_WORKLOADS = {
+    "conv_mamba28b_layer": ConvWorkload(
+        "conv_mamba28b_layer", "conv", 8, 2048, 5120, 4, "bf16", "zero", 5,
+        note="short convolution + silu over a Mamba-2.8B-shaped layer input"),
+    "conv_decode_64layer": ConvWorkload(
+        "conv_decode_64layer", "conv_decode", 256, 1, 5120, 4, "bf16", "normal", 6, layers=64,
+        note="convolution decode step, batch 256, 64 layers of D=5120"),
+}
+
+
+def _taps(w, g, device, dim):
+    bound = 1.0 / float(w.width) ** 0.5
+    weight = (torch.rand(dim, w.width, generator=g, device=device) * 2.0 - 1.0) * bound
+    bias = (torch.rand(dim, generator=g, device=device) * 2.0 - 1.0) * bound
+    return weight, bias
+
+
+def generate_conv(w, device="cpu", batch=None, seqlen=None, dim=None, seed=None, state=None):
+    """Inputs of one convolution call: x, weight, bias, state_in (None for a
+    fresh sequence)."""
+    batch = w.batch if batch is None else batch
+    seqlen = w.seqlen if seqlen is None else seqlen
+    dim = w.dim if dim is None else dim
+    seed = w.seed if seed is None else seed
+    state = w.state if state is None else state
+    dt = io_torch_dtype(w.io)
+    g = _gen(seed, device)
+    weight, bias = _taps(w, g, device, dim)
+    x = _normal((batch, seqlen, dim), g, device, dt)
+    st = _normal((batch, dim, w.width), g, device, dt) if state == "normal" else None
+    return dict(x=x, weight=weight, bias=bias, state_in=st)
+
+
+def generate_conv_decode_layer(w, layer, device="cpu", batch=None, dim=None):
+    """One layer of a convolution decode step: state (batch, dim, W), x
+    (batch, dim), weight, bias."""
+    batch = w.batch if batch is None else batch
+    dim = w.dim if dim is None else dim
+    dt = io_torch_dtype(w.io)
+    g = _gen(w.seed * 1000003 + layer, device)
+    weight, bias = _taps(w, g, device, dim)
+    x = _normal((batch, dim), g, device, dt)
+    st = _normal((batch, dim, w.width), g, device, dt)
+    return dict(state=st, x=x, weight=weight, bias=bias)

@@ -28,8 +28,8 @@ def lib():
 
 def test_library_exports_every_declared_symbol(lib):
     names = _declared_functions()
-    assert names == ["mamba_status_string", "ssm_scan_fwd", "ssm_scan_fwd_workspace_size",
-                     "ssm_state_update"]
+    assert names == ["causal_conv1d_fwd", "causal_conv1d_update", "mamba_status_string",
+                     "ssm_scan_fwd", "ssm_scan_fwd_workspace_size", "ssm_state_update"]
     for n in names:
         assert hasattr(lib, n), f"{n} missing from {ms.library_path()}"
 
@@ -149,3 +149,36 @@ def test_python_binding_requires_gpu_tensors():
     x = torch.zeros(1, 4, 8)
     with pytest.raises(ValueError):
         ms.scan_fwd(x, x, torch.zeros(8, 4), torch.zeros(1, 4, 4), torch.zeros(1, 4, 4))
+
+
+def test_conv_rejects_bad_arguments(lib):
+    def fwd(batch=2, seqlen=8, dim=64, width=4, dtype=1, silu=1, **kw):
+        p = dict(x=P, weight=P, bias=None, state_in=None, y=P, state_out=None)
+        p.update(kw)
+        return lib.causal_conv1d_fwd(batch, seqlen, dim, width, dtype, p["x"], p["weight"],
+                                     p["bias"], p["state_in"], p["y"], p["state_out"], silu, None)
+    assert fwd(batch=-1) == INVALID
+    assert fwd(seqlen=-1) == INVALID
+    assert fwd(dtype=5) == INVALID
+    assert fwd(width=0) == UNSUPPORTED
+    assert fwd(width=5) == UNSUPPORTED
+    for name in ("x", "weight", "y"):
+        assert fwd(**{name: None}) == INVALID, name
+    for name in ("x", "weight", "bias", "state_in", "y", "state_out"):
+        assert fwd(**{name: PM}) == MISALIGNED, name
+    assert fwd(batch=0) == OK and fwd(dim=0) == OK
+    # an empty sequence without a state to hand on has nothing to do
+    assert fwd(seqlen=0, x=None, y=None) == OK
+
+    def upd(batch=2, dim=64, width=4, dtype=1, **kw):
+        p = dict(state=P, x=P, weight=P, bias=None, y=P)
+        p.update(kw)
+        return lib.causal_conv1d_update(batch, dim, width, dtype, p["state"], p["x"],
+                                        p["weight"], p["bias"], p["y"], 1, None)
+    assert upd(batch=-2) == INVALID
+    assert upd(width=7) == UNSUPPORTED
+    for name in ("state", "x", "weight", "y"):
+        assert upd(**{name: None}) == INVALID, name
+    for name in ("state", "x", "weight", "bias", "y"):
+        assert upd(**{name: PM}) == MISALIGNED, name
+    assert upd(dim=0) == OK

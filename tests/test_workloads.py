@@ -63,3 +63,16 @@ def test_decode_layers_are_distinct():
     l1 = W.generate_decode_layer(w, 1, batch=4, dim=32)
     assert l0["h"].shape == (4, 32, 16) and l0["B"].shape == (4, 16)
     assert not torch.equal(l0["x"], l1["x"])
+
+
+def test_conv_workloads_keep_the_last_4_inputs_per_channel():
+    g = _golden()["state_size"]
+    for name in ("conv_mamba28b_layer", "conv_decode_64layer"):
+        w = W.CONV_WORKLOADS[name]
+        assert w.width == g["conv_inputs_per_channel"] and w.dim == g["channels"]
+    assert W.CONV_WORKLOADS["conv_decode_64layer"].layers == g["layers"]
+    a = W.generate_conv(W.CONV_WORKLOADS["conv_mamba28b_layer"], batch=1, seqlen=5, dim=8)
+    b = W.generate_conv(W.CONV_WORKLOADS["conv_mamba28b_layer"], batch=1, seqlen=5, dim=8)
+    assert torch.equal(a["x"], b["x"]) and torch.equal(a["weight"], b["weight"])
+    assert a["state_in"] is None and a["x"].dtype == torch.bfloat16
+    assert float(a["weight"].abs().max()) <= 0.5
