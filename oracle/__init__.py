@@ -38,6 +38,8 @@ def _load(path=None):
     lib.oracle_state_update.argtypes = [i64, i64, i64] + [dp] * 9 + [dp, ctypes.c_int]
     lib.oracle_state_update.restype = ctypes.c_int
     lib.oracle_max_dstate.restype = ctypes.c_int
+    lib.oracle_scan_bwd.argtypes = ([i64] * 4 + [dp] * 9 + [ctypes.c_int] + [dp] * 11)
+    lib.oracle_scan_bwd.restype = ctypes.c_int
     lib.oracle_conv1d_fwd.argtypes = [i64] * 4 + [dp] * 6 + [ctypes.c_int]
     lib.oracle_conv1d_fwd.restype = ctypes.c_int
     lib.oracle_conv1d_update.argtypes = [i64] * 3 + [dp] * 5 + [ctypes.c_int]
@@ -115,6 +117,37 @@ class Oracle:
             raise ValueError(f"oracle_state_update rejected its arguments (status {rc})")
         return y, h
 
+
+    def scan_bwd(self, x, delta, A, B, C, D=None, z=None, h0=None, dy=None, dhL=None,
+                 delta_bias=None, delta_softplus=False):
+        """Gradients of L = sum(dy * y) + sum(dhL * hL) with respect to every
+        input of scan_fwd (same shapes and options). Returns a dict of fp64
+        arrays: dx, ddelta, dz (batch, L, dim); dB, dC (batch, L, N); dA
+        (dim, N); dD, ddelta_bias (dim,); dh0 (batch, dim, N). Entries for
+        absent optional inputs (D, z, delta_bias) are None; dh0 is always
+        returned (the gradient at a zero initial state when h0 is None)."""
+        x, delta, A, B, C = (_f64(v) for v in (x, delta, A, B, C))
+        D, z, h0, bias = _f64(D), _f64(z), _f64(h0), _f64(delta_bias)
+        dy, dhL = _f64(dy), _f64(dhL)
+        batch, seqlen, dim = x.shape
+        dstate = A.shape[1]
+        assert delta.shape == x.shape and dy.shape == x.shape
+        assert B.shape == (batch, seqlen, dstate) and C.shape == B.shape
+        out = dict(dx=np.zeros_like(x), ddelta=np.zeros_like(x),
+                   dA=np.zeros((dim, dstate)), dB=np.zeros_like(B), dC=np.zeros_like(C),
+                   dD=None if D is None else np.zeros(dim),
+                   dz=None if z is None else np.zeros_like(x),
+                   dh0=np.zeros((batch, dim, dstate)),
+                   ddelta_bias=None if bias is None else np.zeros(dim))
+        rc = self.lib.oracle_scan_bwd(
+            batch, seqlen, dim, dstate, _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
+            _ptr(D), _ptr(z), _ptr(h0), _ptr(bias), int(bool(delta_softplus)), _ptr(dy),
+            _ptr(dhL), _ptr(out["dx"]), _ptr(out["ddelta"]), _ptr(out["dA"]), _ptr(out["dB"]),
+            _ptr(out["dC"]), _ptr(out["dD"]), _ptr(out["dz"]), _ptr(out["dh0"]),
+            _ptr(out["ddelta_bias"]))
+        if rc != 0:
+            raise ValueError(f"oracle_scan_bwd rejected its arguments (status {rc})")
+        return out
 
     def conv1d_fwd(self, x, weight, bias=None, state_in=None, silu=True, return_state=True):
         """Short causal depthwise convolution over whole sequences.

@@ -42,6 +42,8 @@
 #include <math.h>
 #include <stddef.h>
 #include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
 
 #define ORACLE_MAX_DSTATE 256
 
@@ -198,4 +200,163 @@ int oracle_conv1d_update(int64_t batch, int64_t dim, int64_t width, double* stat
 {
     if (!state) return -1;
     return oracle_conv1d_fwd(batch, 1, dim, width, x, weight, bias, state, y, state, silu);
+}
+
+/*
+ * Backward pass of the scan (page "Mamba and State Space Models", section
+ * "A Scan on the Chip": training's backward pass needs the intermediate
+ * states, which are computed again rather than stored). This oracle simply
+ * keeps every state of a channel while it runs the forward recurrence once
+ * more, then walks the sequence backwards applying the chain rule to each
+ * step of oracle_scan_fwd.
+ *
+ * The loss is L = sum(dy * y) + sum(dhL * hL): dy (batch, L, dim) is the
+ * gradient arriving at y, dhL (batch, dim, dstate) the one arriving at the
+ * final state (NULL: zero). With the state's adjoint
+ *   lam_t[n] = dL/dh_t[n] = C_t[n] * g_t + Abar_{t+1}[n] * lam_{t+1}[n],
+ *   lam_{L-1}[n] = C_{L-1}[n] * g_{L-1} + dhL[n],   g_t = dy_t * silu(z_t),
+ * the gradients of one step h_t = Abar_t h_{t-1} + dt_t B_t x_t,
+ * Abar_t = exp(dt_t A), are
+ *   dx_t     = D g_t + sum_n lam_t[n] dt_t B_t[n]
+ *   d dt_t   = sum_n lam_t[n] (A[n] Abar_t[n] h_{t-1}[n] + B_t[n] x_t)
+ *   dA[n]   += lam_t[n] dt_t Abar_t[n] h_{t-1}[n]
+ *   dB_t[n] += lam_t[n] dt_t x_t        (summed over channels)
+ *   dC_t[n] += g_t h_t[n]               (summed over channels)
+ *   dD      += g_t x_t
+ *   dz_t     = dy_t p_t silu'(z_t),  p_t = C_t . h_t + D x_t,
+ *              silu'(z) = s (1 + z (1 - s)), s = 1 / (1 + exp(-z))
+ *   dh0[n]   = Abar_0[n] lam_0[n]
+ * and with the fused activation dt = softplus(v), v = delta + bias:
+ *   d delta = d dt * sigmoid(v),  d bias += d delta.
+ * dA, dD and d bias sum over batch rows; dB and dC over channels. Outputs
+ * are fp64 and overwritten: dx, ddelta, dz (batch, L, dim); dB, dC
+ * (batch, L, dstate); dA (dim, dstate); dD, ddelta_bias (dim); dh0
+ * (batch, dim, dstate). dD, dz, dh0, ddelta_bias may be NULL (not wanted);
+ * dz must be NULL when z is, dD when Dskip is, ddelta_bias when delta_bias is.
+ * Batch rows run in parallel; everything within a row runs in order, and the
+ * sums over rows are taken in row order afterwards.
+ */
+static double sigmoid(double v) { return 1.0 / (1.0 + exp(-v)); }
+
+int oracle_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
+                    const double* x, const double* delta, const double* A,
+                    const double* Bm, const double* Cm, const double* Dskip,
+                    const double* z, const double* h0, const double* delta_bias,
+                    int delta_softplus, const double* dy, const double* dhL,
+                    double* dx, double* ddelta, double* dA, double* dB, double* dC,
+                    double* dD, double* dz, double* dh0, double* ddelta_bias)
+{
+    if (batch < 0 || seqlen < 0 || dim < 0 || dstate < 1 || dstate > ORACLE_MAX_DSTATE)
+        return -1;
+    if (!A || !dA) return -1;
+    if (seqlen > 0 && (!x || !delta || !Bm || !Cm || !dy || !dx || !ddelta || !dB || !dC))
+        return -1;
+    if ((dz && !z) || (dD && !Dskip) || (ddelta_bias && !delta_bias)) return -1;
+
+    const int64_t N = dstate;
+    memset(dA, 0, sizeof(double) * (size_t)(dim * N));
+    if (dD) memset(dD, 0, sizeof(double) * (size_t)dim);
+    if (ddelta_bias) memset(ddelta_bias, 0, sizeof(double) * (size_t)dim);
+    if (batch == 0 || dim == 0) return 0;
+    if (seqlen > 0) {
+        memset(dB, 0, sizeof(double) * (size_t)(batch * seqlen * N));
+        memset(dC, 0, sizeof(double) * (size_t)(batch * seqlen * N));
+    }
+    /* per-row partial sums of dA, dD, d bias, added up in row order below */
+    double* pA = calloc((size_t)(batch * dim * N), sizeof(double));
+    double* pD = calloc((size_t)(batch * dim), sizeof(double));
+    double* pBias = calloc((size_t)(batch * dim), sizeof(double));
+    if (!pA || !pD || !pBias) {
+        free(pA); free(pD); free(pBias);
+        return -2;
+    }
+    int failed = 0;
+
+    #pragma omp parallel for schedule(static)
+    for (int64_t b = 0; b < batch; ++b) {
+        /* hs[(t + 1) * N + n] = h_t[n]; hs[n] = h_{-1} = h0 */
+        double* hs = malloc(sizeof(double) * (size_t)((seqlen + 1) * N));
+        double* dts = malloc(sizeof(double) * (size_t)(seqlen > 0 ? seqlen : 1));
+        double* vs = malloc(sizeof(double) * (size_t)(seqlen > 0 ? seqlen : 1));
+        if (!hs || !dts || !vs) {
+            free(hs); free(dts); free(vs);
+            #pragma omp atomic write
+            failed = 1;
+            continue;
+        }
+        for (int64_t d = 0; d < dim; ++d) {
+            /* forward once more, keeping every state */
+            for (int64_t n = 0; n < N; ++n) hs[n] = h0 ? h0[(b * dim + d) * N + n] : 0.0;
+            for (int64_t t = 0; t < seqlen; ++t) {
+                const int64_t i_tok = (b * seqlen + t) * dim + d;
+                const int64_t i_bc = (b * seqlen + t) * N;
+                double v = delta[i_tok];
+                if (delta_bias) v += delta_bias[d];
+                const double dt = delta_softplus ? softplus(v) : v;
+                vs[t] = v;
+                dts[t] = dt;
+                for (int64_t n = 0; n < N; ++n)
+                    hs[(t + 1) * N + n] = exp(dt * A[d * N + n]) * hs[t * N + n] +
+                                          dt * Bm[i_bc + n] * x[i_tok];
+            }
+            /* backwards through the steps */
+            double lam[ORACLE_MAX_DSTATE];
+            double abar_next[ORACLE_MAX_DSTATE];
+            for (int64_t n = 0; n < N; ++n) {
+                lam[n] = dhL ? dhL[(b * dim + d) * N + n] : 0.0;
+                abar_next[n] = 1.0;
+            }
+            for (int64_t t = seqlen - 1; t >= 0; --t) {
+                const int64_t i_tok = (b * seqlen + t) * dim + d;
+                const int64_t i_bc = (b * seqlen + t) * N;
+                const double u = x[i_tok];
+                const double dt = dts[t];
+                const double* h_now = hs + (t + 1) * N;
+                const double* h_prev = hs + t * N;
+                double s = 1.0, zz = 0.0;
+                if (z) {
+                    zz = z[i_tok];
+                    s = sigmoid(zz);
+                }
+                const double gate = z ? zz * s : 1.0;
+                const double g = dy[i_tok] * gate;  /* dL/dp_t */
+                double p = Dskip ? Dskip[d] * u : 0.0;
+                double dxt = Dskip ? Dskip[d] * g : 0.0;
+                double ddt = 0.0;
+                for (int64_t n = 0; n < N; ++n) {
+                    const double a = A[d * N + n];
+                    const double abar = exp(dt * a);
+                    lam[n] = Cm[i_bc + n] * g + abar_next[n] * lam[n];
+                    p += Cm[i_bc + n] * h_now[n];
+                    dxt += lam[n] * dt * Bm[i_bc + n];
+                    ddt += lam[n] * (a * abar * h_prev[n] + Bm[i_bc + n] * u);
+                    pA[(b * dim + d) * N + n] += lam[n] * dt * abar * h_prev[n];
+                    dB[i_bc + n] += lam[n] * dt * u;
+                    dC[i_bc + n] += g * h_now[n];
+                    abar_next[n] = abar;
+                }
+                if (dD) pD[b * dim + d] += g * u;
+                if (dz) dz[i_tok] = dy[i_tok] * p * s * (1.0 + zz * (1.0 - s));
+                dx[i_tok] = dxt;
+                const double dv = delta_softplus ? ddt * sigmoid(vs[t]) : ddt;
+                ddelta[i_tok] = dv;
+                if (ddelta_bias) pBias[b * dim + d] += dv;
+            }
+            if (dh0)
+                for (int64_t n = 0; n < N; ++n) dh0[(b * dim + d) * N + n] = abar_next[n] * lam[n];
+        }
+        free(hs);
+        free(dts);
+        free(vs);
+    }
+    for (int64_t b = 0; b < batch; ++b)
+        for (int64_t d = 0; d < dim; ++d) {
+            for (int64_t n = 0; n < N; ++n) dA[d * N + n] += pA[(b * dim + d) * N + n];
+            if (dD) dD[d] += pD[b * dim + d];
+            if (ddelta_bias) ddelta_bias[d] += pBias[b * dim + d];
+        }
+    free(pA);
+    free(pD);
+    free(pBias);
+    return failed ? -2 : 0;
 }

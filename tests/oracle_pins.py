@@ -39,6 +39,13 @@ when it disagrees with an independent statement of the result:
 - pin_conv_impulse: a unit impulse at token t0 (zero carried state) reads
   out the taps newest-first: pre[t0 + j] = bias + weight[W-1-j], bias
   elsewhere.
+- pin_bwd_finite_differences: every gradient the backward pass returns
+  (x, delta, A, B, C, D, z, h0, and the raw delta and its bias under the
+  fused softplus) equals central differences of the forward scan's loss
+  sum(dy * y) + sum(dhL * hL) in fp64, entry by entry (section "A Scan on
+  the Chip": training runs a backward pass through the same recurrence).
+- pin_bwd_linearity: the gradients are linear in (dy, dhL), and with dy = 0
+  and dhL = 0 they all vanish.
 - pin_conv_split_and_decode: convolving [0, L) equals [0, m) then [m, L)
   from the handed-on state, bit for bit, and T decode steps equal the
   convolution over T tokens.
@@ -368,6 +375,79 @@ def pin_conv_split_and_decode(orc, seed=23):
     assert np.array_equal(s, st), "conv decode state"
 
 
+def _fd_grad(loss, arr, eps):
+    fd = np.zeros_like(arr)
+    it = np.nditer(arr, flags=["multi_index"])
+    for _ in it:
+        i = it.multi_index
+        a1 = arr.copy()
+        a1[i] += eps
+        a2 = arr.copy()
+        a2[i] -= eps
+        fd[i] = (loss(a1) - loss(a2)) / (2.0 * eps)
+    return fd
+
+
+def pin_bwd_finite_differences(orc, seed=24):
+    rng = np.random.default_rng(seed)
+    cases = [dict(softplus=False, opt=True), dict(softplus=True, opt=True),
+             dict(softplus=False, opt=False)]
+    for case in cases:
+        batch, L, dim, N = 2, 6, 3, 4
+        inp = _rand_inputs(rng, batch, L, dim, N, h0=case["opt"])
+        if not case["opt"]:
+            inp["D"] = None
+            inp["z"] = None
+        if case["softplus"]:
+            inp["delta"] = rng.standard_normal((batch, L, dim)) - 0.5
+            inp["delta_bias"] = rng.uniform(-1.0, 1.0, dim)
+        dy = rng.standard_normal((batch, L, dim))
+        dhL = rng.standard_normal((batch, dim, N)) if case["opt"] else None
+        sp = case["softplus"]
+        g = orc.scan_bwd(**inp, dy=dy, dhL=dhL, delta_softplus=sp)
+
+        def loss_of(name):
+            def f(v):
+                y, hL = orc.scan_fwd(**dict(inp, **{name: v}), delta_softplus=sp)
+                total = float(np.sum(dy * y))
+                if dhL is not None:
+                    total += float(np.sum(dhL * hL))
+                return total
+            return f
+        names = [("x", "dx"), ("delta", "ddelta"), ("A", "dA"), ("B", "dB"), ("C", "dC")]
+        if case["opt"]:
+            names += [("D", "dD"), ("z", "dz"), ("h0", "dh0")]
+        if sp:
+            names += [("delta_bias", "ddelta_bias")]
+        for name, key in names:
+            fd = _fd_grad(loss_of(name), inp[name], 1e-6)
+            _close(g[key], fd, rtol=1e-7, what=f"backward {key} vs finite differences ({case})")
+        if not case["opt"]:
+            # zero initial state: dh0 is still the gradient at h0 = 0
+            zero = np.zeros((batch, dim, N))
+            fd = _fd_grad(loss_of("h0"), zero, 1e-6)
+            _close(g["dh0"], fd, rtol=1e-7, what="backward dh0 at a zero start")
+            assert g["dD"] is None and g["dz"] is None
+
+
+def pin_bwd_linearity(orc, seed=25):
+    rng = np.random.default_rng(seed)
+    inp = _rand_inputs(rng, 2, 9, 4, 3)
+    dy1, dy2 = rng.standard_normal((2, 2, 9, 4))
+    dh1, dh2 = rng.standard_normal((2, 2, 4, 3))
+    g1 = orc.scan_bwd(**inp, dy=dy1, dhL=dh1)
+    g2 = orc.scan_bwd(**inp, dy=dy2, dhL=dh2)
+    g12 = orc.scan_bwd(**inp, dy=2.0 * dy1 - dy2, dhL=2.0 * dh1 - dh2)
+    for k in g1:
+        if g1[k] is not None:
+            _close(g12[k], 2.0 * g1[k] - g2[k], what=f"backward linear in (dy, dhL): {k}")
+    g0 = orc.scan_bwd(**inp, dy=np.zeros_like(dy1), dhL=None)
+    for k in g0:
+        if g0[k] is not None:
+            assert not np.any(g0[k]), f"backward {k} not zero for zero upstream gradients"
+
+
 ALL_PINS = [pin_lti_convolution, pin_brute_force, pin_chunk_split, pin_theorem1,
             pin_ssd_matrix, pin_limits, pin_structure, pin_decode, pin_delta_activation,
-            pin_conv_numpy, pin_conv_impulse, pin_conv_split_and_decode]
+            pin_conv_numpy, pin_conv_impulse, pin_conv_split_and_decode,
+            pin_bwd_finite_differences, pin_bwd_linearity]

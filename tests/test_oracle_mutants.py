@@ -14,7 +14,7 @@ import oracle_pins
 from oracle import build as oracle_build
 
 MUTANTS = {
-    "decay sign flipped": ("exp(dt * a)", "exp(-dt * a)"),
+    "decay sign flipped": ("const double Abar = exp(dt * a);", "const double Abar = exp(-dt * a);"),
     "delta dropped from Bbar": (": dt * Bm[i_bc + n];", ": Bm[i_bc + n];"),
     "decay of h dropped": ("Abar * h[n] + Bbar * u", "h[n] + Bbar * u"),
     "readout uses B": ("out += Cm[i_bc + n] * h[n];", "out += Bm[i_bc + n] * h[n];"),
@@ -29,8 +29,9 @@ MUTANTS = {
                                      "const int64_t i_bc = (b * seqlen + (t > 0 ? t - 1 : 0)) * dstate;"),
     "B, C ignore the batch": ("const int64_t i_bc = (b * seqlen + t) * dstate;",
                               "const int64_t i_bc = t * dstate;"),
-    "x from the previous token": ("const double u = x[i_tok];",
-                                  "const double u = x[i_tok - (t > 0 ? dim : 0)];"),
+    "x from the previous token": (
+        "const double u = x[i_tok];\n                if (delta_bias)",
+        "const double u = x[i_tok - (t > 0 ? dim : 0)];\n                if (delta_bias)"),
     "x and delta swapped": ("double dt = delta[i_tok];\n                const double u = x[i_tok];",
                             "double dt = x[i_tok];\n                const double u = delta[i_tok];"),
     "delta bias ignored": ("if (delta_bias) dt += delta_bias[d];", ""),
@@ -54,6 +55,25 @@ MUTANTS = {
     "conv bias dropped": ("double pre = bias ? bias[d] : 0.0;", "double pre = 0.0;"),
     "conv state handed on one token early": ("conv_input(x, carried, b, seqlen - width + k, d,",
                                              "conv_input(x, carried, b, seqlen - width + k - 1, d,"),
+    "bwd adjoint decays with this token's Abar": (
+        "lam[n] = Cm[i_bc + n] * g + abar_next[n] * lam[n];",
+        "lam[n] = Cm[i_bc + n] * g + abar * lam[n];"),
+    "bwd final-state gradient ignored": ("lam[n] = dhL ? dhL[(b * dim + d) * N + n] : 0.0;",
+                                         "lam[n] = 0.0;"),
+    "bwd delta gradient drops the decay term": (
+        "ddt += lam[n] * (a * abar * h_prev[n] + Bm[i_bc + n] * u);",
+        "ddt += lam[n] * (Bm[i_bc + n] * u);"),
+    "bwd dA uses the new state": ("pA[(b * dim + d) * N + n] += lam[n] * dt * abar * h_prev[n];",
+                                  "pA[(b * dim + d) * N + n] += lam[n] * dt * abar * h_now[n];"),
+    "bwd dB misses delta": ("dB[i_bc + n] += lam[n] * dt * u;", "dB[i_bc + n] += lam[n] * u;"),
+    "bwd dC uses the previous state": ("dC[i_bc + n] += g * h_now[n];",
+                                       "dC[i_bc + n] += g * h_prev[n];"),
+    "bwd gate derivative wrong": ("s * (1.0 + zz * (1.0 - s))", "s * (1.0 - s)"),
+    "bwd softplus derivative dropped": ("const double dv = delta_softplus ? ddt * sigmoid(vs[t]) : ddt;",
+                                        "const double dv = ddt;"),
+    "bwd dh0 misses the first decay": ("dh0[(b * dim + d) * N + n] = abar_next[n] * lam[n];",
+                                       "dh0[(b * dim + d) * N + n] = lam[n];"),
+    "bwd skip gradient dropped": ("double dxt = Dskip ? Dskip[d] * g : 0.0;", "double dxt = 0.0;"),
     "conv carried state ignored": (
         "carried[k] = state_in ? state_in[(b * dim + d) * width + k] : 0.0;",
         "carried[k] = 0.0;"),
