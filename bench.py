@@ -41,6 +41,9 @@ def parse():
     p.add_argument("--state-split", type=int, default=0, help="0 = the library's automatic plan")
     p.add_argument("--batch", type=int, default=0, help="override the workload's batch (0 = keep)")
     p.add_argument("--dim", type=int, default=0, help="override the workload's channels (0 = keep)")
+    p.add_argument("--backward", action="store_true",
+                   help="time ssm_scan_bwd (gradients of every input, states recomputed) "
+                        "instead of the forward scan")
     p.add_argument("--delta-softplus", action="store_true",
                    help="pass delta before its activation with a per-channel bias and let the "
                         "kernels apply bias and softplus")
@@ -188,6 +191,9 @@ def main():
     w = W.WORKLOADS[args.workload]
     if w.kind == "decode":
         bench_decode(args, w)
+        return
+    if args.backward:
+        bench_backward(args, w)
         return
     if args.batch or args.dim:
         import dataclasses
@@ -364,6 +370,122 @@ def bench_decode(args, w):
         "cpu_baseline": None,
     }
     print(json.dumps(line), flush=True)
+
+
+def backward_bytes(w, softplus=False):
+    """Bytes the backward pass must move: x, delta, z, dy in and dx, ddelta,
+    dz out (I/O dtype); B, C in (I/O dtype) and dB, dC out (fp32); A, D in,
+    dA, dD out and dh0 out (fp32); the initial state in when there is one;
+    with the fused activation the bias in and its gradient out."""
+    s = 4 if w.io == "f32" else 2
+    b, l, d, n = w.batch, w.seqlen, w.dim, w.dstate
+    total = 7 * b * l * d * s + 2 * b * l * n * (s + 4) + 2 * (d * n * 4 + d * 4) + b * d * n * 4
+    if w.h0 == "normal":
+        total += b * d * n * 4
+    if softplus:
+        total += 2 * d * 4
+    return total
+
+
+def backward_alu_ops(w, softplus=False):
+    """fp32 lane-operations the backward pass by recomputation must issue per
+    element: the forward state update twice (once for the checkpoints, once
+    to have every state while walking back: delta*A, exp, (delta*x)*B, FMA;
+    4 per state each), and per state the adjoint update (multiply, FMA), the
+    decay (multiply, exp), and the terms of dA (2 multiplies, FMA), d delta
+    (multiply, 2 FMA), dx (FMA), dB and dC (a multiply each) and the readout
+    for dz (FMA): 14 per state; per element about 20 more (delta*x, the gate
+    and its derivative, dx and readout skip terms, dD, conversions). The
+    fused activation adds softplus and its derivative (16)."""
+    n = w.dstate
+    per_elem = 8 * n + 14 * n + 20 + (16 if softplus else 0)
+    return per_elem * w.batch * w.seqlen * w.dim
+
+
+def bench_backward(args, w):
+    """One step = one ssm_scan_bwd over the whole workload: the checkpoint
+    passes, the reverse kernel and the reductions, all in the timed region."""
+    import torch
+
+    import selective_state_space_40_amd as ms
+    import ssm_workloads as W
+
+    if args.batch or args.dim:
+        import dataclasses
+        w = dataclasses.replace(w, batch=args.batch or w.batch, dim=args.dim or w.dim,
+                                name=f"{w.name} resized")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    ms.load_library()
+    sp = args.delta_softplus
+    sets = []
+    for i in range(2):
+        inp = W.generate_scan(w, device=dev, seed=w.seed + 101 * i, raw_delta=sp)
+        g = torch.Generator(device=dev).manual_seed(w.seed + 7 + i)
+        inp["dy"] = torch.randn(w.batch, w.seqlen, w.dim, generator=g, device=dev).to(
+            inp["x"].dtype)
+        sets.append(inp)
+
+    def step(i):
+        inp = sets[i % 2]
+        ms.scan_bwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"],
+                    inp["h0"], dy=inp["dy"], delta_bias=inp.get("delta_bias"),
+                    delta_softplus=sp)
+
+    ms_per_step, wall = _time_steps(step, args.warmup, args.steps, torch.cuda.current_stream(dev))
+    sec = ms_per_step / 1e3
+    elems = w.batch * w.seqlen * w.dim
+    nbytes = backward_bytes(w, sp)
+    ops = backward_alu_ops(w, sp)
+    tops = ops / sec / 1e12
+    gbps = nbytes / sec / 1e9
+    cpu = None if args.no_cpu_baseline else cpu_baseline_backward(w, sets[0], sp)
+    line = {
+        "metric": "backward scan elements/s (B*L*D, all input gradients, states recomputed)",
+        "value": elems / sec, "unit": "elements/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "seqlen": w.seqlen, "dim": w.dim,
+                   "dstate": w.dstate, "io_dtype": w.io, "checkpoint_every": 32,
+                   "delta_activation": "bias + softplus in the kernels" if sp else
+                                       "none (delta passed activated)",
+                   "parallelism": "single GPU"},
+        "achieved_GBps": round(gbps, 1), "wall_s": round(wall, 4),
+        "roofline": {"bound": "alu", "achieved": round(tops, 3), "peak": ALU_PEAK_TOPS,
+                     "unit": "Tops/s (fp32 lane-ops)", "frac": round(tops / ALU_PEAK_TOPS, 4),
+                     "traffic": None, "kernel": "ssm_scan_bwd step (all passes)",
+                     "algorithmic_bytes": nbytes, "algorithmic_ops": ops,
+                     "hbm_GBps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline_backward(w, inp, softplus):
+    """The fp64 oracle's backward pass on the host over a channel sample (the
+    per-channel work is independent; dB and dC come out as partial sums)."""
+    import torch
+
+    import oracle
+
+    orc = oracle.get()
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    channels = max(8, min(w.dim, int(3.0e6 * threads / (w.batch * w.seqlen))))
+    idx = torch.arange(channels, device=inp["x"].device)
+    sub = dict(x=inp["x"].index_select(2, idx), delta=inp["delta"].index_select(2, idx),
+               A=inp["A"].index_select(0, idx), B=inp["B"], C=inp["C"],
+               D=inp["D"].index_select(0, idx), z=inp["z"].index_select(2, idx), h0=None,
+               dy=inp["dy"].index_select(2, idx),
+               delta_bias=inp["delta_bias"].index_select(0, idx) if softplus else None)
+    host = {k: (oracle._f64(v) if v is not None else None) for k, v in sub.items()}
+    t0 = time.perf_counter()
+    orc.scan_bwd(**host, delta_softplus=softplus)
+    dt = time.perf_counter() - t0
+    elems = w.batch * w.seqlen * channels
+    return {"value": elems / dt, "unit": "elements/s",
+            "cores": min(threads, w.batch), "kind": "oracle",
+            "sample": f"{w.name}: all {w.batch} batch rows x {w.seqlen} tokens x first "
+                      f"{channels} of {w.dim} channels, fp64 (rows in parallel), {dt:.2f} s"}
 
 
 def conv_bytes(w, state_in):

@@ -174,6 +174,48 @@ int ssm_state_update(int64_t batch, int64_t dim, int dstate, int dtype, float* h
                      const void* B, const void* C, const float* D, const void* z,
                      void* y, const mamba_scan_options* options, hipStream_t stream);
 
+/*
+ * Backward pass of ssm_scan_fwd (page "Mamba and State Space Models",
+ * section "A Scan on the Chip": the states the backward pass needs are
+ * computed again rather than stored). Given the forward call's inputs and
+ * the gradients dy at y and dhL at the final state, it writes the gradients
+ * of L = sum(dy * y) + sum(dhL * hL) with respect to every input.
+ *
+ * x, delta, A, B, C, D, z, h0, options   as passed to ssm_scan_fwd
+ * dy           (batch, seqlen, dim) I/O dtype     required
+ * dhL          (batch, dim, dstate) fp32          optional (NULL: zero)
+ * dx, ddelta   (batch, seqlen, dim) I/O dtype     written; ddelta is the
+ *                                                 gradient at the delta input
+ *                                                 (before the activation when
+ *                                                 options apply one)
+ * dA           (dim, dstate) fp32                 written (summed over rows)
+ * dB, dC       (batch, seqlen, dstate) fp32       written (summed over channels)
+ * dD           (dim) fp32                         optional; must be NULL when D is
+ * dz           (batch, seqlen, dim) I/O dtype     optional; must be NULL when z is
+ * dh0          (batch, dim, dstate) fp32          optional: the gradient at the
+ *                                                 initial state (zero start when
+ *                                                 h0 is NULL)
+ * ddelta_bias  (dim) fp32                         optional; must be NULL when
+ *                                                 options carry no delta_bias
+ * workspace    at least ssm_scan_bwd_workspace_size bytes
+ *
+ * The intermediate states are recomputed from checkpoints every 32 tokens
+ * that the call itself computes into the workspace. Sums over channels and
+ * rows are taken in a fixed order, so results are reproducible bit for bit.
+ * seqlen == 0 writes zero dA, dD, ddelta_bias and dh0 = dhL. Outputs must
+ * not overlap inputs or each other. Errors as for ssm_scan_fwd.
+ */
+int ssm_scan_bwd_workspace_size(int64_t batch, int64_t seqlen, int64_t dim, int dstate,
+                                int dtype, size_t* bytes);
+
+int ssm_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int dstate, int dtype,
+                 const void* x, const void* delta, const float* A, const void* B,
+                 const void* C, const float* D, const void* z, const float* h0,
+                 const mamba_scan_options* options, const void* dy, const float* dhL,
+                 void* dx, void* ddelta, float* dA, float* dB, float* dC, float* dD,
+                 void* dz, float* dh0, float* ddelta_bias, void* workspace,
+                 size_t workspace_bytes, hipStream_t stream);
+
 /* Widest short convolution the library provides (the pages' width is 4). */
 #define MAMBA_CONV_MAX_WIDTH 4
 

@@ -10,6 +10,8 @@ There is no other code path: without the built library every call raises.
                      delta_bias=None, delta_softplus=False)
     y = state_update(h, x, delta, A, B, C, D=None, z=None,
                      delta_bias=None, delta_softplus=False)   # h updated in place
+    grads = scan_bwd(x, delta, A, B, C, D=None, z=None, h0=None, dy=dy, dhL=None,
+                     delta_bias=None, delta_softplus=False)      # dict of gradients
     y, state = conv1d_fwd(x, weight, bias=None, state_in=None, silu=True)
     y = conv1d_update(state, x, weight, bias=None, silu=True)  # state updated in place
 
@@ -26,7 +28,7 @@ import os
 
 import torch
 
-__all__ = ["scan_fwd", "state_update", "conv1d_fwd", "conv1d_update", "workspace_size", "resolve_plan", "library_path",
+__all__ = ["scan_fwd", "scan_bwd", "state_update", "conv1d_fwd", "conv1d_update", "workspace_size", "resolve_plan", "library_path",
            "load_library", "MambaScanError", "MAX_DSTATE", "ScanPlan", "ScanOptions"]
 
 MAX_DSTATE = 16
@@ -80,6 +82,12 @@ def load_library():
     lib.ssm_scan_fwd.restype = i32
     lib.ssm_state_update.argtypes = [i64, i64, i32, i32] + [vp] * 9 + [po, vp]
     lib.ssm_state_update.restype = i32
+    lib.ssm_scan_bwd_workspace_size.argtypes = [i64, i64, i64, i32, i32,
+                                                ctypes.POINTER(ctypes.c_size_t)]
+    lib.ssm_scan_bwd_workspace_size.restype = i32
+    lib.ssm_scan_bwd.argtypes = ([i64, i64, i64, i32, i32] + [vp] * 8 + [po] + [vp] * 11 +
+                                 [vp, ctypes.c_size_t, vp])
+    lib.ssm_scan_bwd.restype = i32
     lib.causal_conv1d_fwd.argtypes = [i64, i64, i64, i32, i32] + [vp] * 6 + [i32, vp]
     lib.causal_conv1d_fwd.restype = i32
     lib.causal_conv1d_update.argtypes = [i64, i64, i32, i32] + [vp] * 5 + [i32, vp]
@@ -145,10 +153,10 @@ def workspace_size(batch, seqlen, dim, dstate, dtype=torch.bfloat16, chunk_len=0
     return resolve_plan(batch, seqlen, dim, dstate, dtype, chunk_len, state_split)[2]
 
 
-def _workspace(device, nbytes):
+def _workspace(device, nbytes, kind="fwd"):
     if nbytes == 0:
         return None
-    key = (device, torch.cuda.current_stream(device).cuda_stream)
+    key = (device, torch.cuda.current_stream(device).cuda_stream, kind)
     buf = _WS.get(key)
     if buf is None or buf.numel() < nbytes:
         buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
@@ -202,6 +210,59 @@ def scan_fwd(x, delta, A, B, C, D=None, z=None, h0=None, *, delta_bias=None,
                               _ptr(ws), nbytes, _stream(dev))
     _check(st, "ssm_scan_fwd")
     return y, hL
+
+
+def scan_bwd(x, delta, A, B, C, D=None, z=None, h0=None, *, dy, dhL=None, delta_bias=None,
+             delta_softplus=False, want_dh0=True):
+    """Gradients of sum(dy * y) + sum(dhL * hL) for the scan_fwd call with the
+    same inputs. Returns a dict: dx, ddelta, dz (like x, I/O dtype); dB, dC
+    (batch, L, N) fp32; dA (dim, N) fp32; dD, ddelta_bias (dim,) fp32; dh0
+    (batch, dim, N) fp32. Entries of absent optional inputs are None."""
+    lib = load_library()
+    if x.dim() != 3:
+        raise ValueError("x must be (batch, L, dim)")
+    batch, seqlen, dim = x.shape
+    if A.dim() != 2 or A.shape[0] != dim:
+        raise ValueError("A must be (dim, N)")
+    dstate = A.shape[1]
+    dev, dt = x.device, x.dtype
+    if dt not in _DTYPES:
+        raise ValueError(f"unsupported I/O dtype {dt}")
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU device")
+    _need(x, "x", (batch, seqlen, dim), dt, dev)
+    _need(delta, "delta", (batch, seqlen, dim), dt, dev)
+    _need(A, "A", (dim, dstate), torch.float32, dev)
+    _need(B, "B", (batch, seqlen, dstate), dt, dev)
+    _need(C, "C", (batch, seqlen, dstate), dt, dev)
+    _need(D, "D", (dim,), torch.float32, dev)
+    _need(z, "z", (batch, seqlen, dim), dt, dev)
+    _need(h0, "h0", (batch, dim, dstate), torch.float32, dev)
+    _need(delta_bias, "delta_bias", (dim,), torch.float32, dev)
+    _need(dy, "dy", (batch, seqlen, dim), dt, dev)
+    _need(dhL, "dhL", (batch, dim, dstate), torch.float32, dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    g = dict(dx=torch.empty_like(x), ddelta=torch.empty_like(x),
+             dA=torch.empty(dim, dstate, **f32), dB=torch.empty(batch, seqlen, dstate, **f32),
+             dC=torch.empty(batch, seqlen, dstate, **f32),
+             dD=None if D is None else torch.empty(dim, **f32),
+             dz=None if z is None else torch.empty_like(x),
+             dh0=torch.empty(batch, dim, dstate, **f32) if want_dh0 else None,
+             ddelta_bias=None if delta_bias is None else torch.empty(dim, **f32))
+    with torch.cuda.device(dev):
+        nbytes = ctypes.c_size_t(0)
+        _check(lib.ssm_scan_bwd_workspace_size(batch, seqlen, dim, dstate, _DTYPES[dt],
+                                               ctypes.byref(nbytes)),
+               "ssm_scan_bwd_workspace_size")
+        ws = _workspace(dev, nbytes.value, "bwd")
+        st = lib.ssm_scan_bwd(batch, seqlen, dim, dstate, _DTYPES[dt], _ptr(x), _ptr(delta),
+                              _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0),
+                              _options(delta_bias, delta_softplus), _ptr(dy), _ptr(dhL),
+                              _ptr(g["dx"]), _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]),
+                              _ptr(g["dC"]), _ptr(g["dD"]), _ptr(g["dz"]), _ptr(g["dh0"]),
+                              _ptr(g["ddelta_bias"]), _ptr(ws), nbytes.value, _stream(dev))
+    _check(st, "ssm_scan_bwd")
+    return g
 
 
 def state_update(h, x, delta, A, B, C, D=None, z=None, *, delta_bias=None,

@@ -247,6 +247,83 @@ int ssm_state_update(int64_t batch, int64_t dim, int dstate, int dtype, float* h
     return mamba::launch_state_update(a, stream) == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP;
 }
 
+int ssm_scan_bwd_workspace_size(int64_t batch, int64_t seqlen, int64_t dim, int dstate,
+                                int dtype, size_t* bytes) {
+    if (bytes == nullptr) return MAMBA_ERR_INVALID_ARG;
+    const int st = check_shape(batch, seqlen, dim, dstate, dtype);
+    if (st != MAMBA_OK) return st;
+    *bytes = mamba::scan_bwd_workspace_bytes(batch, seqlen, dim, dstate);
+    return MAMBA_OK;
+}
+
+int ssm_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int dstate, int dtype,
+                 const void* x, const void* delta, const float* A, const void* B,
+                 const void* C, const float* D, const void* z, const float* h0,
+                 const mamba_scan_options* options, const void* dy, const float* dhL,
+                 void* dx, void* ddelta, float* dA, float* dB, float* dC, float* dD,
+                 void* dz, float* dh0, float* ddelta_bias, void* workspace,
+                 size_t workspace_bytes, hipStream_t stream) {
+    int st = check_shape(batch, seqlen, dim, dstate, dtype);
+    if (st != MAMBA_OK) return st;
+    const float* delta_bias = nullptr;
+    int delta_softplus = 0;
+    st = read_options(options, &delta_bias, &delta_softplus);
+    if (st != MAMBA_OK) return st;
+    if ((dD != nullptr && D == nullptr) || (dz != nullptr && z == nullptr) ||
+        (ddelta_bias != nullptr && delta_bias == nullptr))
+        return MAMBA_ERR_INVALID_ARG;
+    if (dim == 0) return MAMBA_OK;
+    if (A == nullptr || dA == nullptr) return MAMBA_ERR_INVALID_ARG;
+    if (batch > 0 && seqlen > 0 &&
+        (x == nullptr || delta == nullptr || B == nullptr || C == nullptr || dy == nullptr ||
+         dx == nullptr || ddelta == nullptr || dB == nullptr || dC == nullptr))
+        return MAMBA_ERR_INVALID_ARG;
+    const void* ptrs[] = {x, delta, A, B, C, D, z, h0, dy, dhL, dx, ddelta,
+                          dA, dB, dC, dD, dz, dh0, ddelta_bias, workspace};
+    for (const void* p : ptrs)
+        if (p != nullptr && !aligned16(p)) return MAMBA_ERR_MISALIGNED;
+    const size_t need = mamba::scan_bwd_workspace_bytes(batch, seqlen, dim, dstate);
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return MAMBA_ERR_WORKSPACE;
+    int split = 1;
+    for (int sp = kPreferredSplit; sp > 1; sp /= 2)
+        if (mamba::split_supported(dstate, sp)) {
+            split = sp;
+            break;
+        }
+
+    mamba::BwdArgs a;
+    a.fwd.batch = batch;
+    a.fwd.seqlen = seqlen;
+    a.fwd.dim = dim;
+    a.fwd.dstate = dstate;
+    a.fwd.io = dtype == MAMBA_DTYPE_F32 ? mamba::kIoF32 : mamba::kIoBF16;
+    a.fwd.x = x;
+    a.fwd.delta = delta;
+    a.fwd.A = A;
+    a.fwd.B = B;
+    a.fwd.C = C;
+    a.fwd.D = D;
+    a.fwd.z = z;
+    a.fwd.h0 = h0;
+    a.fwd.y = nullptr;
+    a.fwd.hL = nullptr;
+    a.fwd.delta_bias = delta_bias;
+    a.fwd.delta_softplus = delta_softplus;
+    a.dy = dy;
+    a.dhL = dhL;
+    a.dx = dx;
+    a.ddelta = ddelta;
+    a.dA = dA;
+    a.dB = dB;
+    a.dC = dC;
+    a.dD = dD;
+    a.dz = dz;
+    a.dh0 = dh0;
+    a.ddelta_bias = ddelta_bias;
+    return mamba::launch_scan_bwd(a, split, workspace, stream) == hipSuccess ? MAMBA_OK
+                                                                             : MAMBA_ERR_HIP;
+}
+
 int causal_conv1d_fwd(int64_t batch, int64_t seqlen, int64_t dim, int width, int dtype,
                       const void* x, const float* weight, const float* bias,
                       const void* state_in, void* y, void* state_out, int silu,

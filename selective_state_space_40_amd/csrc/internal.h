@@ -93,6 +93,32 @@ struct ConvArgs {
     int fuse_state;  // set by the launcher: the forward kernel writes state_out itself
 };
 
+// Backward pass of the scan. The forward inputs come in `fwd` (its y and hL
+// are not used); gradients of the loss sum(dy * y) + sum(dhL * hL).
+constexpr int kBwdChunk = 32;  // tokens between the backward pass's checkpoints
+
+struct BwdArgs {
+    ScanArgs fwd;
+    const void* dy;        // (batch, seqlen, dim) I/O dtype
+    const float* dhL;      // (batch, dim, dstate) or nullptr
+    void* dx;              // (batch, seqlen, dim) I/O dtype
+    void* ddelta;          // (batch, seqlen, dim) I/O dtype: gradient at the delta input
+    float* dA;             // (dim, dstate)
+    float* dB;             // (batch, seqlen, dstate)
+    float* dC;             // (batch, seqlen, dstate)
+    float* dD;             // (dim) or nullptr
+    void* dz;              // (batch, seqlen, dim) I/O dtype, or nullptr
+    float* dh0;            // (batch, dim, dstate) or nullptr
+    float* ddelta_bias;    // (dim) or nullptr
+};
+
+// Scratch bytes of the backward pass for this shape.
+size_t scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int dstate);
+
+// Queue the backward pass; `fwd_split` is the state split of the forward
+// summary pass that computes the checkpoints. Arguments are validated.
+hipError_t launch_scan_bwd(const BwdArgs& a, int fwd_split, void* workspace, hipStream_t stream);
+
 // Workspace layout for nchunks > 1: three fp32 arrays of
 // nchunks * batch * dim * dstate elements each: the state entering each
 // chunk, each chunk's end state from a zero start, and each chunk's decay
@@ -105,10 +131,12 @@ hipError_t launch_scan(const ScanArgs& a, const ScanPlan& plan, void* workspace,
                        hipStream_t stream);
 
 // The chunked scan for one (I/O dtype, delta softplus) pair; each pair is
-// compiled in its own translation unit (scan_variant.hip).
+// compiled in its own translation unit (scan_variant.hip). With states_only
+// it queues only the summary and carry passes, which leave the state
+// entering every chunk in the workspace (the backward pass's checkpoints).
 template <int IO, bool SP>
 hipError_t launch_scan_variant(const ScanArgs& a, const ScanPlan& plan, void* workspace,
-                               hipStream_t stream);
+                               hipStream_t stream, bool states_only);
 
 // Queue the convolution over whole sequences (update == false) or its
 // decode step (update == true). Arguments are already validated.

@@ -1,0 +1,514 @@
+// Backward pass of the selective scan by recomputation (page "Mamba and
+// State Space Models", world.lapla.si, section "A Scan on the Chip": the
+// states that training's backward pass needs are computed again instead of
+// being stored).
+//
+// For the loss sum(dy * y) + sum(dhL * hL), with g_t = dy_t * silu(z_t) and
+// the adjoint of the state
+//     lam_t[n] = C_t[n] g_t + Abar_{t+1}[n] lam_{t+1}[n],   lam_L = dhL,
+// one step h_t = Abar_t h_{t-1} + dt_t B_t x_t, Abar_t = exp(dt_t A), gives
+//     dx_t   = D g_t + sum_n lam_t dt_t B_t          d dt_t = sum_n lam_t (A Abar_t h_{t-1} + B_t x_t)
+//     dA    += lam_t dt_t Abar_t h_{t-1}             dB_t  += lam_t dt_t x_t   (over channels)
+//     dC_t  += g_t h_t          (over channels)      dD    += g_t x_t
+//     dz_t   = dy_t p_t silu'(z_t), p_t = C_t.h_t + D x_t
+//     dh0    = Abar_0 lam_0;  with dt = softplus(v): d delta = d dt sigmoid(v).
+//
+// Work plan. (1) The forward summary and carry passes of the chunked scan,
+// run with chunks of kBwdChunk = 32 tokens, leave the state entering every
+// chunk in the workspace: the checkpoints. (2) One workgroup per (batch row,
+// 64-channel group) walks the chunks from last to first, carrying lam in
+// registers. Its ceil(N/4) waves split the states, 4 per wave (padded with
+// inert states: A = B = C = 0). In a chunk it first runs forward over the 4
+// tiles of 8 tokens, keeping each tile's entering state in LDS, then takes
+// the tiles in reverse: it recomputes the tile's 8 states per lane into
+// registers from the kept entry and walks the tile backwards. Sums over
+// states (dx, d dt, p) go through LDS to the wave that finishes the token;
+// sums over channels (dB, dC) are reduced inside the wave by a butterfly of
+// lane exchanges that leaves one finished (token, state) sum in each lane,
+// written as this group's partial. (3) Small kernels add the partials over
+// channel groups (dB, dC) and batch rows (dA, dD, d bias) in a fixed order,
+// so results are bitwise reproducible.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "device_common.h"
+#include "internal.h"
+
+namespace mamba {
+namespace {
+
+constexpr int kBT = 8;                         // tokens per tile
+constexpr int kTilesPerChunk = kBwdChunk / kBT;
+constexpr int kNpw = 4;                        // states per wave
+constexpr int kVals = 2 * kBT * kNpw;          // dB and dC terms per lane per tile
+static_assert(kVals == kWave, "the butterfly leaves exactly one sum per lane");
+
+template <int S>
+struct BwdLds {
+    float2 dtx[kBT][kWave];                    // (delta as used, x) per token and channel
+    float g[kBT][kWave];                       // dy * silu(z)
+    float bc[2][kBT][kNpw * S];                // B and C rows of the tile, padded states 0
+    float tent[kTilesPerChunk][kNpw * S][kWave];  // state entering each tile of the chunk
+    float red[3][S][kBT][kWave];               // per-wave partial sums over states
+};
+
+// What the wave that finishes token j keeps from staging.
+struct Own {
+    float dy, z, v, x;
+};
+
+struct Place {
+    int64_t b, d;      // batch row, this lane's channel (clamped to dim-1)
+    int64_t grp;       // 64-channel group
+    bool valid;        // lane maps to a real channel
+    int w, n0;         // wave, first state of its slice
+    float dbias;
+};
+
+__device__ __forceinline__ float sigmoid_f32(float v) {
+    return fast_rcp(1.0f + fast_exp2(-v * kLog2e));
+}
+
+// Stage tile [t0, t0 + cnt): wave w converts the tokens j = w, w+S, ... of
+// the tile (delta activated once per (channel, token)); all threads stage
+// the tile's B and C rows.
+template <int S, int IO, bool SP, bool HAS_Z, bool WANT_G>
+__device__ __forceinline__ void stage_tile(const BwdArgs& a, const Place& pl, BwdLds<S>& lds,
+                                           int64_t t0, int cnt, Own (&own)[(kBT + S - 1) / S]) {
+    constexpr int OW = (kBT + S - 1) / S;
+    const ScanArgs& f = a.fwd;
+    const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+    for (int jj = 0; jj < OW; ++jj) {
+        const int j = jj * S + pl.w;
+        if (j < cnt) {
+            const int64_t idx = (pl.b * f.seqlen + t0 + j) * f.dim + pl.d;
+            float xf = raw_to_f32<IO>(load_raw<IO>(f.x, idx));
+            const float v = raw_to_f32<IO>(load_raw<IO>(f.delta, idx)) + pl.dbias;
+            const float dt = SP ? softplus_f32(v) : v;
+            if (!pl.valid) xf = 0.0f;  // a clamped lane contributes nothing
+            lds.dtx[j][lane] = make_float2(dt, xf);
+            if constexpr (WANT_G) {
+                const float dyf = raw_to_f32<IO>(load_raw<IO>(a.dy, idx));
+                const float zf = HAS_Z ? raw_to_f32<IO>(load_raw<IO>(f.z, idx)) : 0.0f;
+                float gg = HAS_Z ? dyf * silu(zf) : dyf;
+                if (!pl.valid) gg = 0.0f;
+                lds.g[j][lane] = gg;
+                own[jj] = Own{dyf, zf, v, xf};
+            }
+        }
+    }
+    constexpr int NP = kNpw * S;
+    const int N = f.dstate;
+    for (int e = threadIdx.x; e < 2 * kBT * NP; e += kWave * S) {
+        const int which = e / (kBT * NP);
+        const int r = e - which * kBT * NP;
+        const int j = r / NP;
+        const int n = r - j * NP;
+        float val = 0.0f;
+        if (j < cnt && n < N)
+            val = raw_to_f32<IO>(load_raw<IO>(which ? f.C : f.B, (pl.b * f.seqlen + t0 + j) * N + n));
+        lds.bc[which][j][n] = val;
+    }
+}
+
+// Sum of each of the 64 values over the 64 lanes. At the step of distance
+// k, pairs (vals[2i], vals[2i+1]) are folded into vals[i]: lanes with bit k
+// clear keep the first value and add their partner's copy of it, lanes with
+// bit k set the second. After the steps k = 32, 16, ..., 1, lane l holds the
+// full sum of the value whose index is l with its 6 bits reversed.
+__device__ __forceinline__ float lane_sums(float (&vals)[kVals]) {
+    const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+    for (int k = 32, cnt = kVals / 2; k >= 1; k /= 2, cnt /= 2) {
+        const bool hi = (lane & k) != 0;
+#pragma unroll
+        for (int i = 0; i < cnt; ++i) {
+            const float keep = hi ? vals[2 * i + 1] : vals[2 * i];
+            const float send = hi ? vals[2 * i] : vals[2 * i + 1];
+            vals[i] = keep + __shfl_xor(send, k, kWave);
+        }
+    }
+    return vals[0];
+}
+
+__device__ __forceinline__ int reverse6(int l) {
+    return ((l & 1) << 5) | ((l & 2) << 3) | ((l & 4) << 1) | ((l & 8) >> 1) | ((l & 16) >> 3) |
+           ((l & 32) >> 5);
+}
+
+template <int S, int IO, bool SP, bool HAS_D, bool HAS_Z>
+__global__ __launch_bounds__(kWave * S) void scan_bwd_kernel(BwdArgs a, int64_t ngroups,
+                                                             int64_t nchunks, const float* ckpt,
+                                                             float* part_bc, float* part_a,
+                                                             float* part_d, float* part_bias) {
+    constexpr int OW = (kBT + S - 1) / S;
+    __shared__ BwdLds<S> lds;
+    const ScanArgs& f = a.fwd;
+    const int N = f.dstate;
+    const int64_t L = f.seqlen;
+    const int lane = threadIdx.x & (kWave - 1);
+
+    Place pl;
+    pl.grp = blockIdx.x % ngroups;
+    pl.b = blockIdx.x / ngroups;
+    pl.w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
+    pl.n0 = pl.w * kNpw;
+    const int64_t d_raw = pl.grp * kWave + lane;
+    pl.valid = d_raw < f.dim;
+    pl.d = pl.valid ? d_raw : f.dim - 1;
+    pl.dbias = f.delta_bias != nullptr ? f.delta_bias[pl.d] : 0.0f;
+    const float dskip = HAS_D ? f.D[pl.d] : 0.0f;
+
+    bool sv[kNpw];      // state exists (not padding)
+    float A[kNpw], A2[kNpw], lam[kNpw], en[kNpw], dA[kNpw];
+#pragma unroll
+    for (int q = 0; q < kNpw; ++q) {
+        const int n = pl.n0 + q;
+        sv[q] = n < N;
+        A[q] = sv[q] ? f.A[pl.d * N + n] : 0.0f;
+        A2[q] = A[q] * kLog2e;
+        lam[q] = (sv[q] && a.dhL != nullptr) ? a.dhL[(pl.b * f.dim + pl.d) * N + n] : 0.0f;
+        en[q] = 1.0f;
+        dA[q] = 0.0f;
+    }
+    float dD_acc = 0.0f, dbias_acc = 0.0f;
+    Own own[OW];
+
+    for (int64_t k = nchunks - 1; k >= 0; --k) {
+        const int64_t cs = k * kBwdChunk;
+        const int64_t ce = min(L, cs + kBwdChunk);
+        const int ntile = static_cast<int>((ce - cs + kBT - 1) / kBT);
+
+        // (a) forward over the chunk from its checkpoint, keeping tile entries
+        float h[kNpw];
+#pragma unroll
+        for (int q = 0; q < kNpw; ++q) {
+            const int n = pl.n0 + q;
+            float v = 0.0f;
+            if (sv[q]) {
+                if (nchunks == 1)
+                    v = f.h0 != nullptr ? f.h0[(pl.b * f.dim + pl.d) * N + n] : 0.0f;
+                else
+                    v = ckpt[((k * f.batch + pl.b) * f.dim + pl.d) * N + n];
+            }
+            h[q] = v;
+        }
+        for (int i = 0; i < ntile; ++i) {
+            const int64_t t0 = cs + i * kBT;
+            const int cnt = static_cast<int>(min<int64_t>(kBT, ce - t0));
+            stage_tile<S, IO, SP, HAS_Z, false>(a, pl, lds, t0, cnt, own);
+            __syncthreads();
+#pragma unroll
+            for (int q = 0; q < kNpw; ++q) lds.tent[i][pl.n0 + q][lane] = h[q];
+#pragma unroll
+            for (int j = 0; j < kBT; ++j) {
+                if (j < cnt) {
+                    const float2 v = lds.dtx[j][lane];
+                    const float du = v.x * v.y;
+#pragma unroll
+                    for (int q = 0; q < kNpw; ++q)
+                        h[q] = fmaf(fast_exp2(v.x * A2[q]), h[q], du * lds.bc[0][j][pl.n0 + q]);
+                }
+            }
+            __syncthreads();
+        }
+
+        // (b) the tiles in reverse
+        for (int i = ntile - 1; i >= 0; --i) {
+            const int64_t t0 = cs + i * kBT;
+            const int cnt = static_cast<int>(min<int64_t>(kBT, ce - t0));
+            stage_tile<S, IO, SP, HAS_Z, true>(a, pl, lds, t0, cnt, own);
+            __syncthreads();
+
+            float he[kNpw], hs[kBT][kNpw];
+#pragma unroll
+            for (int q = 0; q < kNpw; ++q) he[q] = lds.tent[i][pl.n0 + q][lane];
+#pragma unroll
+            for (int q = 0; q < kNpw; ++q) h[q] = he[q];
+#pragma unroll
+            for (int j = 0; j < kBT; ++j) {
+                if (j < cnt) {
+                    const float2 v = lds.dtx[j][lane];
+                    const float du = v.x * v.y;
+#pragma unroll
+                    for (int q = 0; q < kNpw; ++q)
+                        h[q] = fmaf(fast_exp2(v.x * A2[q]), h[q], du * lds.bc[0][j][pl.n0 + q]);
+                }
+#pragma unroll
+                for (int q = 0; q < kNpw; ++q) hs[j][q] = h[q];
+            }
+
+            float vals[kVals];
+#pragma unroll
+            for (int e = 0; e < kVals; ++e) vals[e] = 0.0f;
+#pragma unroll
+            for (int j = kBT - 1; j >= 0; --j) {
+                if (j < cnt) {
+                    const float2 v = lds.dtx[j][lane];
+                    const float dt = v.x, x = v.y;
+                    const float gg = lds.g[j][lane];
+                    float dxp = 0.0f, ddp = 0.0f, pp = 0.0f;
+#pragma unroll
+                    for (int q = 0; q < kNpw; ++q) {
+                        const float Bq = lds.bc[0][j][pl.n0 + q];
+                        const float Cq = lds.bc[1][j][pl.n0 + q];
+                        lam[q] = fmaf(en[q], lam[q], Cq * gg);
+                        const float e = fast_exp2(dt * A2[q]);
+                        const float hprev = j > 0 ? hs[j > 0 ? j - 1 : 0][q] : he[q];
+                        const float eh = e * hprev;
+                        const float ldt = lam[q] * dt;
+                        dA[q] = fmaf(ldt, eh, dA[q]);
+                        ddp = fmaf(lam[q], fmaf(A[q], eh, Bq * x), ddp);
+                        dxp = fmaf(ldt, Bq, dxp);
+                        pp = fmaf(Cq, hs[j][q], pp);
+                        vals[j * kNpw + q] = ldt * x;
+                        vals[kBT * kNpw + j * kNpw + q] = gg * hs[j][q];
+                        en[q] = e;
+                    }
+                    lds.red[0][pl.w][j][lane] = dxp;
+                    lds.red[1][pl.w][j][lane] = ddp;
+                    lds.red[2][pl.w][j][lane] = pp;
+                }
+            }
+
+            // dB, dC of this tile summed over the group's channels
+            {
+                const float sum = lane_sums(vals);
+                const int v = reverse6(lane);
+                const int which = v / (kBT * kNpw);
+                const int r = v - which * kBT * kNpw;
+                const int j = r / kNpw;
+                const int n = pl.n0 + (r - j * kNpw);
+                if (j < cnt && n < N) {
+                    const int64_t per = f.batch * L * N;
+                    part_bc[(which * ngroups + pl.grp) * per + (pl.b * L + t0 + j) * N + n] = sum;
+                }
+            }
+            __syncthreads();
+
+            // finish this wave's tokens of the tile
+#pragma unroll
+            for (int jj = 0; jj < OW; ++jj) {
+                const int j = jj * S + pl.w;
+                if (j < cnt) {
+                    float dxs = 0.0f, dds = 0.0f, ps = 0.0f;
+#pragma unroll
+                    for (int u = 0; u < S; ++u) {
+                        dxs += lds.red[0][u][j][lane];
+                        dds += lds.red[1][u][j][lane];
+                        ps += lds.red[2][u][j][lane];
+                    }
+                    const Own o = own[jj];
+                    const float gg = lds.g[j][lane];
+                    if constexpr (HAS_D) {
+                        dxs = fmaf(dskip, gg, dxs);
+                        ps = fmaf(dskip, o.x, ps);
+                    }
+                    const float dv = SP ? dds * sigmoid_f32(o.v) : dds;
+                    dD_acc = fmaf(gg, o.x, dD_acc);
+                    dbias_acc += dv;
+                    if (pl.valid) {
+                        const int64_t idx = (pl.b * L + t0 + j) * f.dim + pl.d;
+                        store_io<IO>(a.dx, idx, dxs);
+                        store_io<IO>(a.ddelta, idx, dv);
+                        if constexpr (HAS_Z) {
+                            const float s = sigmoid_f32(o.z);
+                            store_io<IO>(a.dz, idx, o.dy * ps * (s * fmaf(o.z, 1.0f - s, 1.0f)));
+                        }
+                    }
+                }
+            }
+        }
+    }
+
+    // gradients at h0 and the per-row partials of dA, dD, d bias
+    if (pl.valid) {
+#pragma unroll
+        for (int q = 0; q < kNpw; ++q) {
+            if (sv[q]) {
+                const int64_t col = (pl.b * f.dim + pl.d) * N + pl.n0 + q;
+                if (a.dh0 != nullptr) a.dh0[col] = en[q] * lam[q];
+                part_a[col] = dA[q];
+            }
+        }
+    }
+    __syncthreads();
+    lds.red[0][pl.w][0][lane] = dD_acc;
+    lds.red[1][pl.w][0][lane] = dbias_acc;
+    __syncthreads();
+    if (pl.w == 0 && pl.valid) {
+        float sd = 0.0f, sb = 0.0f;
+#pragma unroll
+        for (int u = 0; u < S; ++u) {
+            sd += lds.red[0][u][0][lane];
+            sb += lds.red[1][u][0][lane];
+        }
+        part_d[pl.b * f.dim + pl.d] = sd;
+        part_bias[pl.b * f.dim + pl.d] = sb;
+    }
+}
+
+// dB and dC: the partials of all channel groups added in group order.
+__global__ __launch_bounds__(256) void bwd_bc_reduce_kernel(int64_t per, int64_t ngroups,
+                                                            const float* part, float* dB,
+                                                            float* dC) {
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < 2 * per;
+         i += stride) {
+        const int64_t which = i / per;
+        const int64_t r = i - which * per;
+        float s = 0.0f;
+        for (int64_t g = 0; g < ngroups; ++g) s += part[(which * ngroups + g) * per + r];
+        (which ? dC : dB)[r] = s;
+    }
+}
+
+// dA, dD, d bias: the per-row partials added in row order.
+__global__ __launch_bounds__(256) void bwd_param_reduce_kernel(int64_t batch, int64_t dim, int N,
+                                                               const float* part_a,
+                                                               const float* part_d,
+                                                               const float* part_bias, float* dA,
+                                                               float* dD, float* dbias) {
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+    const int64_t cols = dim * N;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < cols;
+         i += stride) {
+        float s = 0.0f;
+        for (int64_t b = 0; b < batch; ++b) s += part_a[b * cols + i];
+        dA[i] = s;
+        if (i < dim) {
+            float sd = 0.0f, sb = 0.0f;
+            for (int64_t b = 0; b < batch; ++b) {
+                sd += part_d[b * dim + i];
+                sb += part_bias[b * dim + i];
+            }
+            if (dD != nullptr) dD[i] = sd;
+            if (dbias != nullptr) dbias[i] = sb;
+        }
+    }
+}
+
+// Empty sequence or empty batch: dA, dD, d bias are zero and dh0 = dhL.
+__global__ __launch_bounds__(256) void bwd_degenerate_kernel(int64_t cols, int64_t dim,
+                                                             int64_t states, const float* dhL,
+                                                             float* dA, float* dD, float* dbias,
+                                                             float* dh0) {
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+    const int64_t n = cols > states ? cols : states;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+         i += stride) {
+        if (i < cols) dA[i] = 0.0f;
+        if (i < dim) {
+            if (dD != nullptr) dD[i] = 0.0f;
+            if (dbias != nullptr) dbias[i] = 0.0f;
+        }
+        if (i < states && dh0 != nullptr) dh0[i] = dhL != nullptr ? dhL[i] : 0.0f;
+    }
+}
+
+struct BwdLayout {
+    int64_t nchunks, ngroups;
+    size_t ckpt, part_bc, part_a, part_d, part_bias, total;  // float offsets / count
+};
+
+inline size_t round64(size_t v) { return (v + 63) / 64 * 64; }
+
+BwdLayout bwd_layout(int64_t batch, int64_t seqlen, int64_t dim, int dstate) {
+    BwdLayout l;
+    l.nchunks = (seqlen + kBwdChunk - 1) / kBwdChunk;
+    l.ngroups = (dim + kWave - 1) / kWave;
+    const size_t states = static_cast<size_t>(batch) * dim * dstate;
+    size_t off = 0;
+    l.ckpt = off;
+    off += round64(l.nchunks > 1 ? 3 * static_cast<size_t>(l.nchunks) * states : 0);
+    l.part_bc = off;
+    off += round64(2 * static_cast<size_t>(l.ngroups) * batch * seqlen * dstate);
+    l.part_a = off;
+    off += round64(states);
+    l.part_d = off;
+    off += round64(static_cast<size_t>(batch) * dim);
+    l.part_bias = off;
+    off += round64(static_cast<size_t>(batch) * dim);
+    l.total = off;
+    return l;
+}
+
+template <int S, int IO, bool SP>
+hipError_t launch_bwd_main(const BwdArgs& a, const BwdLayout& l, float* ws, hipStream_t s) {
+    const int64_t blocks = a.fwd.batch * l.ngroups;
+    const bool has_d = a.fwd.D != nullptr, has_z = a.fwd.z != nullptr;
+    auto go = [&](auto kernel) {
+        hipLaunchKernelGGL(kernel, dim3(blocks), dim3(kWave * S), 0, s, a, l.ngroups, l.nchunks,
+                           ws + l.ckpt, ws + l.part_bc, ws + l.part_a, ws + l.part_d,
+                           ws + l.part_bias);
+    };
+    if (has_d && has_z) go(scan_bwd_kernel<S, IO, SP, true, true>);
+    else if (has_d) go(scan_bwd_kernel<S, IO, SP, true, false>);
+    else if (has_z) go(scan_bwd_kernel<S, IO, SP, false, true>);
+    else go(scan_bwd_kernel<S, IO, SP, false, false>);
+    return hipGetLastError();
+}
+
+template <int IO, bool SP>
+hipError_t launch_bwd_io(const BwdArgs& a, int fwd_split, float* ws, hipStream_t s) {
+    const ScanArgs& f = a.fwd;
+    const BwdLayout l = bwd_layout(f.batch, f.seqlen, f.dim, f.dstate);
+    if (l.nchunks > 1) {
+        ScanPlan p;
+        p.chunk_len = kBwdChunk;
+        p.nchunks = l.nchunks;
+        p.state_split = fwd_split;
+        p.workspace_bytes = 0;
+        // the summary pass writes no output; y points at a real buffer all the same
+        ScanArgs fa = f;
+        fa.y = a.dx;
+        const hipError_t e = launch_scan_variant<IO, SP>(fa, p, ws + l.ckpt, s, true);
+        if (e != hipSuccess) return e;
+    }
+    hipError_t e;
+    switch ((f.dstate + kNpw - 1) / kNpw) {
+        case 1: e = launch_bwd_main<1, IO, SP>(a, l, ws, s); break;
+        case 2: e = launch_bwd_main<2, IO, SP>(a, l, ws, s); break;
+        case 3: e = launch_bwd_main<3, IO, SP>(a, l, ws, s); break;
+        case 4: e = launch_bwd_main<4, IO, SP>(a, l, ws, s); break;
+        default: return hipErrorInvalidValue;
+    }
+    if (e != hipSuccess) return e;
+    const int64_t per = f.batch * f.seqlen * f.dstate;
+    hipLaunchKernelGGL(bwd_bc_reduce_kernel, dim3(stride_blocks(2 * per)), dim3(256), 0, s, per,
+                       l.ngroups, ws + l.part_bc, a.dB, a.dC);
+    hipLaunchKernelGGL(bwd_param_reduce_kernel, dim3(stride_blocks(f.dim * f.dstate)), dim3(256),
+                       0, s, f.batch, f.dim, f.dstate, ws + l.part_a, ws + l.part_d,
+                       ws + l.part_bias, a.dA, a.dD, a.ddelta_bias);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+size_t scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int dstate) {
+    if (batch == 0 || seqlen == 0 || dim == 0) return 0;
+    return bwd_layout(batch, seqlen, dim, dstate).total * sizeof(float);
+}
+
+hipError_t launch_scan_bwd(const BwdArgs& a, int fwd_split, void* workspace, hipStream_t stream) {
+    const ScanArgs& f = a.fwd;
+    if (f.dim == 0) return hipSuccess;
+    if (f.batch == 0 || f.seqlen == 0) {
+        const int64_t cols = f.dim * f.dstate;
+        const int64_t states = f.batch * f.dim * f.dstate;
+        hipLaunchKernelGGL(bwd_degenerate_kernel,
+                           dim3(stride_blocks(cols > states ? cols : states)), dim3(256), 0,
+                           stream, cols, f.dim, states, a.dhL, a.dA, a.dD, a.ddelta_bias, a.dh0);
+        return hipGetLastError();
+    }
+    float* ws = static_cast<float*>(workspace);
+    const bool sp = f.delta_softplus != 0;
+    if (f.io == kIoF32)
+        return sp ? launch_bwd_io<kIoF32, true>(a, fwd_split, ws, stream)
+                  : launch_bwd_io<kIoF32, false>(a, fwd_split, ws, stream);
+    return sp ? launch_bwd_io<kIoBF16, true>(a, fwd_split, ws, stream)
+              : launch_bwd_io<kIoBF16, false>(a, fwd_split, ws, stream);
+}
+
+}  // namespace mamba

@@ -579,7 +579,8 @@ void chunk_output_kernel(ScanArgs a, ChunkGrid g, Carry c) {
 // ---------------------------------------------------------------------------
 // Host-side dispatch over the compile-time variants.
 template <int N, int S, int IO, bool SP>
-hipError_t launch_scan_ns(const ScanArgs& a, const ScanPlan& plan, void* ws, hipStream_t s) {
+hipError_t launch_scan_ns(const ScanArgs& a, const ScanPlan& plan, void* ws, hipStream_t s,
+                          bool states_only) {
     ChunkGrid g;
     g.nblk_d = (a.dim + kWave - 1) / kWave;
     g.nchunks = plan.nchunks;
@@ -602,6 +603,7 @@ hipError_t launch_scan_ns(const ScanArgs& a, const ScanPlan& plan, void* ws, hip
         hipLaunchKernelGGL(chunk_carry_kernel, dim3(stride_blocks(columns)), dim3(256), 0, s,
                            columns, plan.nchunks, c);
     }
+    if (states_only) return hipGetLastError();
     const int64_t blocks = g.nblk_d * plan.nchunks * a.batch;
     const dim3 grid(blocks), block(kWave * S);
     const bool has_d = a.D != nullptr, has_z = a.z != nullptr;
@@ -619,12 +621,13 @@ hipError_t launch_scan_ns(const ScanArgs& a, const ScanPlan& plan, void* ws, hip
 // The state split S is a compile-time parameter; every N supports S = 1 and
 // N = 16, 8 and 4 also support the splits that divide them (up to 8).
 template <int N, int IO, bool SP>
-hipError_t launch_scan_n(const ScanArgs& a, const ScanPlan& plan, void* ws, hipStream_t s) {
+hipError_t launch_scan_n(const ScanArgs& a, const ScanPlan& plan, void* ws, hipStream_t s,
+                         bool states_only) {
     switch (plan.state_split) {
-        case 1: return launch_scan_ns<N, 1, IO, SP>(a, plan, ws, s);
-        case 2: if constexpr (N % 2 == 0 && (N == 4 || N == 8 || N == 16)) return launch_scan_ns<N, 2, IO, SP>(a, plan, ws, s); break;
-        case 4: if constexpr (N % 4 == 0 && (N == 4 || N == 8 || N == 16)) return launch_scan_ns<N, 4, IO, SP>(a, plan, ws, s); break;
-        case 8: if constexpr (N % 8 == 0 && (N == 8 || N == 16)) return launch_scan_ns<N, 8, IO, SP>(a, plan, ws, s); break;
+        case 1: return launch_scan_ns<N, 1, IO, SP>(a, plan, ws, s, states_only);
+        case 2: if constexpr (N % 2 == 0 && (N == 4 || N == 8 || N == 16)) return launch_scan_ns<N, 2, IO, SP>(a, plan, ws, s, states_only); break;
+        case 4: if constexpr (N % 4 == 0 && (N == 4 || N == 8 || N == 16)) return launch_scan_ns<N, 4, IO, SP>(a, plan, ws, s, states_only); break;
+        case 8: if constexpr (N % 8 == 0 && (N == 8 || N == 16)) return launch_scan_ns<N, 8, IO, SP>(a, plan, ws, s, states_only); break;
         default: break;
     }
     return hipErrorInvalidValue;
@@ -633,9 +636,10 @@ hipError_t launch_scan_n(const ScanArgs& a, const ScanPlan& plan, void* ws, hipS
 }  // namespace
 
 template <int IO, bool SP>
-hipError_t launch_scan_variant(const ScanArgs& a, const ScanPlan& p, void* ws, hipStream_t s) {
+hipError_t launch_scan_variant(const ScanArgs& a, const ScanPlan& p, void* ws, hipStream_t s,
+                               bool states_only) {
     switch (a.dstate) {
-#define MAMBA_CASE(n) case n: return launch_scan_n<n, IO, SP>(a, p, ws, s);
+#define MAMBA_CASE(n) case n: return launch_scan_n<n, IO, SP>(a, p, ws, s, states_only);
         MAMBA_CASE(1) MAMBA_CASE(2) MAMBA_CASE(3) MAMBA_CASE(4) MAMBA_CASE(5) MAMBA_CASE(6)
         MAMBA_CASE(7) MAMBA_CASE(8) MAMBA_CASE(9) MAMBA_CASE(10) MAMBA_CASE(11) MAMBA_CASE(12)
         MAMBA_CASE(13) MAMBA_CASE(14) MAMBA_CASE(15) MAMBA_CASE(16)

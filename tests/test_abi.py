@@ -29,7 +29,8 @@ def lib():
 def test_library_exports_every_declared_symbol(lib):
     names = _declared_functions()
     assert names == ["causal_conv1d_fwd", "causal_conv1d_update", "mamba_status_string",
-                     "ssm_scan_fwd", "ssm_scan_fwd_workspace_size", "ssm_state_update"]
+                     "ssm_scan_bwd", "ssm_scan_bwd_workspace_size", "ssm_scan_fwd",
+                     "ssm_scan_fwd_workspace_size", "ssm_state_update"]
     for n in names:
         assert hasattr(lib, n), f"{n} missing from {ms.library_path()}"
 
@@ -182,3 +183,37 @@ def test_conv_rejects_bad_arguments(lib):
     for name in ("state", "x", "weight", "bias", "y"):
         assert upd(**{name: PM}) == MISALIGNED, name
     assert upd(dim=0) == OK
+
+
+def test_scan_bwd_rejects_bad_arguments(lib):
+    need = ctypes.c_size_t(0)
+    assert lib.ssm_scan_bwd_workspace_size(2, 64, 64, 16, 1, ctypes.byref(need)) == OK
+    assert need.value > 0
+    assert lib.ssm_scan_bwd_workspace_size(2, 64, 64, 17, 1, ctypes.byref(need)) == UNSUPPORTED
+    assert lib.ssm_scan_bwd_workspace_size(2, 64, 64, 16, 1, None) == INVALID
+    lib.ssm_scan_bwd_workspace_size(2, 64, 64, 16, 1, ctypes.byref(need))
+
+    def bwd(batch=2, seqlen=64, dim=64, dstate=16, dtype=1, opts=None, ws=P, wsb=None, **kw):
+        p = dict(x=P, delta=P, A=P, B=P, C=P, D=None, z=None, h0=None, dy=P, dhL=None, dx=P,
+                 ddelta=P, dA=P, dB=P, dC=P, dD=None, dz=None, dh0=None, ddelta_bias=None)
+        p.update(kw)
+        return lib.ssm_scan_bwd(batch, seqlen, dim, dstate, dtype, p["x"], p["delta"], p["A"],
+                                p["B"], p["C"], p["D"], p["z"], p["h0"], opts, p["dy"], p["dhL"],
+                                p["dx"], p["ddelta"], p["dA"], p["dB"], p["dC"], p["dD"],
+                                p["dz"], p["dh0"], p["ddelta_bias"], ws,
+                                need.value if wsb is None else wsb, None)
+    assert bwd(batch=-1) == INVALID
+    assert bwd(dstate=0) == UNSUPPORTED
+    assert bwd(dtype=9) == INVALID
+    for name in ("x", "delta", "A", "B", "C", "dy", "dx", "ddelta", "dA", "dB", "dC"):
+        assert bwd(**{name: None}) == INVALID, name
+    for name in ("x", "delta", "A", "B", "C", "dy", "dx", "ddelta", "dA", "dB", "dC"):
+        assert bwd(**{name: PM}) == MISALIGNED, name
+    # a gradient for an input that is absent
+    assert bwd(dD=P) == INVALID
+    assert bwd(dz=P) == INVALID
+    assert bwd(ddelta_bias=P) == INVALID
+    assert bwd(opts=_opts(reserved=3)) == INVALID
+    assert bwd(ws=None) == WORKSPACE
+    assert bwd(wsb=need.value - 4) == WORKSPACE
+    assert bwd(dim=0) == OK
