@@ -40,6 +40,8 @@ def _load(path=None):
     lib.oracle_max_dstate.restype = ctypes.c_int
     lib.oracle_scan_bwd.argtypes = ([i64] * 4 + [dp] * 9 + [ctypes.c_int] + [dp] * 11)
     lib.oracle_scan_bwd.restype = ctypes.c_int
+    lib.oracle_ssd_fwd.argtypes = [i64] * 5 + [dp] * 10 + [dp, ctypes.c_int]
+    lib.oracle_ssd_fwd.restype = ctypes.c_int
     lib.oracle_conv1d_fwd.argtypes = [i64] * 4 + [dp] * 6 + [ctypes.c_int]
     lib.oracle_conv1d_fwd.restype = ctypes.c_int
     lib.oracle_conv1d_update.argtypes = [i64] * 3 + [dp] * 5 + [ctypes.c_int]
@@ -148,6 +150,27 @@ class Oracle:
         if rc != 0:
             raise ValueError(f"oracle_scan_bwd rejected its arguments (status {rc})")
         return out
+
+    def ssd_fwd(self, x, dt, A, B, C, D=None, z=None, h0=None, headdim=64, dt_bias=None,
+                dt_softplus=False, return_state=True):
+        """Mamba-2 dual form with a scalar decay per head. Shapes: x, z
+        (batch, L, nheads*headdim); dt (batch, L, nheads); A, dt_bias
+        (nheads,); B, C (batch, L, N); D (nheads*headdim,); h0 (batch, nheads,
+        headdim, N). Returns (y, hL) as fp64 arrays."""
+        x, dt, A, B, C = (_f64(v) for v in (x, dt, A, B, C))
+        D, z, h0, bias = _f64(D), _f64(z), _f64(h0), _f64(dt_bias)
+        batch, seqlen, dim = x.shape
+        nheads = dt.shape[2]
+        assert dim == nheads * headdim and A.shape == (nheads,)
+        dstate = B.shape[2]
+        y = np.zeros((batch, seqlen, dim), dtype=np.float64)
+        hL = np.zeros((batch, nheads, headdim, dstate)) if return_state else None
+        rc = self.lib.oracle_ssd_fwd(batch, seqlen, nheads, headdim, dstate, _ptr(x), _ptr(dt),
+                                     _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0),
+                                     _ptr(y), _ptr(hL), _ptr(bias), int(bool(dt_softplus)))
+        if rc != 0:
+            raise ValueError(f"oracle_ssd_fwd rejected its arguments (status {rc})")
+        return y, hL
 
     def conv1d_fwd(self, x, weight, bias=None, state_in=None, silu=True, return_state=True):
         """Short causal depthwise convolution over whole sequences.

@@ -360,3 +360,68 @@ int oracle_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int64_t dstate,
     free(pBias);
     return failed ? -2 : 0;
 }
+
+/*
+ * Mamba-2's state space dual form (page "Mamba and State Space Models",
+ * section "Mamba-2: Two Algorithms"): A is a number times the identity, so
+ * the state of a channel decays by one factor exp(dt * a) for all its
+ * states. The channels come in heads of `headdim` channels that share that
+ * number a and the step dt, which is what lets a whole chunk be handled by
+ * matrix products; B and C are shared by all heads. The result is exactly
+ * the recurrence, so the oracle runs it token by token:
+ *
+ *   h[p,n] <- exp(dt a_h) h[p,n] + dt B[n] x[p],   y[p] = sum_n C[n] h[p,n]
+ *   y[p]   = (y[p] + D[p] x[p]) * silu(z[p])
+ *
+ * Layout: x, z, y (batch, L, nheads*headdim), channel h*headdim + p
+ * contiguous; dt (batch, L, nheads); A, dt_bias (nheads); B, C (batch, L,
+ * dstate); Dskip (nheads*headdim); h0, hL (batch, nheads, headdim, dstate).
+ * dt may arrive raw: dt_bias[h] is added and softplus applied when asked.
+ */
+int oracle_ssd_fwd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                   int64_t dstate, const double* x, const double* dt, const double* A,
+                   const double* Bm, const double* Cm, const double* Dskip, const double* z,
+                   const double* h0, double* y, double* hL, const double* dt_bias,
+                   int dt_softplus)
+{
+    if (batch < 0 || seqlen < 0 || nheads < 0 || headdim < 0 || dstate < 1 ||
+        dstate > ORACLE_MAX_DSTATE)
+        return -1;
+    if (!A) return -1;
+    if (batch == 0 || nheads == 0 || headdim == 0) return 0;
+    if (seqlen > 0 && (!x || !dt || !Bm || !Cm || !y)) return -1;
+    const int64_t dim = nheads * headdim;
+
+    #pragma omp parallel for collapse(3) schedule(static)
+    for (int64_t b = 0; b < batch; ++b) {
+        for (int64_t hd = 0; hd < nheads; ++hd) {
+            for (int64_t p = 0; p < headdim; ++p) {
+                const int64_t d = hd * headdim + p;
+                const int64_t row = (b * nheads + hd) * headdim + p;  /* (b, h, p) */
+                double h[ORACLE_MAX_DSTATE];
+                for (int64_t n = 0; n < dstate; ++n)
+                    h[n] = h0 ? h0[row * dstate + n] : 0.0;
+                for (int64_t t = 0; t < seqlen; ++t) {
+                    double step = dt[(b * seqlen + t) * nheads + hd];
+                    if (dt_bias) step += dt_bias[hd];
+                    if (dt_softplus) step = softplus(step);
+                    const double decay = exp(step * A[hd]);
+                    const int64_t i_tok = (b * seqlen + t) * dim + d;
+                    const int64_t i_bc = (b * seqlen + t) * dstate;
+                    const double u = x[i_tok];
+                    double out = 0.0;
+                    for (int64_t n = 0; n < dstate; ++n) {
+                        h[n] = decay * h[n] + step * Bm[i_bc + n] * u;
+                        out += Cm[i_bc + n] * h[n];
+                    }
+                    if (Dskip) out += Dskip[d] * u;
+                    if (z) out *= z[i_tok] / (1.0 + exp(-z[i_tok]));
+                    y[i_tok] = out;
+                }
+                if (hL)
+                    for (int64_t n = 0; n < dstate; ++n) hL[row * dstate + n] = h[n];
+            }
+        }
+    }
+    return 0;
+}

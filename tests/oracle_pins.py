@@ -46,6 +46,16 @@ when it disagrees with an independent statement of the result:
   the Chip": training runs a backward pass through the same recurrence).
 - pin_bwd_linearity: the gradients are linear in (dy, dhL), and with dy = 0
   and dhL = 0 they all vanish.
+- pin_ssd_dual_matrix: Mamba-2's form with one decay per head (section
+  "Mamba-2: Two Algorithms") equals the whole-sequence lower-triangular
+  matrix M[i, j] = (C_i . B_j) exp(a (S_i - S_j)), S the running sum of dt,
+  applied to dt * x as one numpy matmul per head ("masked attention" with C
+  as queries and B as keys), plus the decayed initial state.
+- pin_ssd_chunked: the same result from the chunked algorithm the section
+  describes: matrix products inside each chunk and only the state passed
+  from chunk to chunk, for several chunk lengths.
+- pin_ssd_heads_of_one: with one channel per head the dual form is the
+  selective scan with A[d, n] = a_d for every n.
 - pin_conv_split_and_decode: convolving [0, L) equals [0, m) then [m, L)
   from the handed-on state, bit for bit, and T decode steps equal the
   convolution over T tokens.
@@ -447,7 +457,103 @@ def pin_bwd_linearity(orc, seed=25):
             assert not np.any(g0[k]), f"backward {k} not zero for zero upstream gradients"
 
 
+def _ssd_inputs(rng, batch, L, nheads, headdim, N, h0=True):
+    dim = nheads * headdim
+    return dict(x=rng.standard_normal((batch, L, dim)),
+                dt=np.log1p(np.exp(rng.standard_normal((batch, L, nheads)) - 1.0)),
+                A=-np.exp(rng.uniform(-1.0, 1.0, nheads)),
+                B=rng.standard_normal((batch, L, N)), C=rng.standard_normal((batch, L, N)),
+                D=rng.standard_normal(dim), z=rng.standard_normal((batch, L, dim)),
+                h0=rng.standard_normal((batch, nheads, headdim, N)) if h0 else None)
+
+
+def _ssd_gate_skip(pre, inp, b, sl, cols):
+    out = pre + inp["D"][cols] * inp["x"][b, sl][:, cols]
+    return out * _silu(inp["z"][b, sl][:, cols])
+
+
+def pin_ssd_dual_matrix(orc, seed=26):
+    rng = np.random.default_rng(seed)
+    batch, L, H, P, N = 2, 29, 3, 4, 5
+    inp = _ssd_inputs(rng, batch, L, H, P, N)
+    y, hL = orc.ssd_fwd(**inp, headdim=P)
+    mask = np.tril(np.ones((L, L), dtype=bool))
+    for b in range(batch):
+        G = inp["C"][b] @ inp["B"][b].T                               # (L, L): C_i . B_j
+        for h in range(H):
+            a = inp["A"][h]
+            S = np.cumsum(inp["dt"][b, :, h])
+            M = np.where(mask, G * np.exp(a * (S[:, None] - S[None, :])), 0.0)
+            cols = slice(h * P, (h + 1) * P)
+            V = inp["dt"][b, :, h][:, None] * inp["x"][b, :, cols]   # (L, P)
+            h0 = inp["h0"][b, h]                                     # (P, N)
+            pre = M @ V + np.exp(a * S)[:, None] * (inp["C"][b] @ h0.T)
+            _close(y[b, :, cols], _ssd_gate_skip(pre, inp, b, slice(None), cols),
+                   what="SSD whole-sequence matrix y")
+            w = np.exp(a * (S[-1] - S)) * inp["dt"][b, :, h]
+            want_h = (inp["x"][b, :, cols] * w[:, None]).T @ inp["B"][b] + np.exp(a * S[-1]) * h0
+            _close(hL[b, h], want_h, what="SSD whole-sequence matrix hL")
+
+
+def _ssd_chunked(inp, P, Q):
+    """The chunked dual form: matmuls inside each chunk, state between chunks."""
+    x, dt, A, B, C = inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"]
+    batch, L, _ = x.shape
+    H = dt.shape[2]
+    N = B.shape[2]
+    pre = np.zeros_like(x)
+    state = np.zeros((batch, H, P, N)) if inp["h0"] is None else inp["h0"].copy()
+    for c0 in range(0, L, Q):
+        sl = slice(c0, min(L, c0 + Q))
+        q = sl.stop - sl.start
+        mask = np.tril(np.ones((q, q), dtype=bool))
+        for b in range(batch):
+            G = C[b, sl] @ B[b, sl].T
+            for h in range(H):
+                S = np.cumsum(dt[b, sl, h]) * A[h]                    # log decay inside the chunk
+                cols = slice(h * P, (h + 1) * P)
+                V = dt[b, sl, h][:, None] * x[b, sl, cols]
+                M = np.where(mask, G * np.exp(S[:, None] - S[None, :]), 0.0)
+                pre[b, sl, cols] = M @ V + np.exp(S)[:, None] * (C[b, sl] @ state[b, h].T)
+                w = np.exp(S[-1] - S)
+                state[b, h] = np.exp(S[-1]) * state[b, h] + (V * w[:, None]).T @ B[b, sl]
+    return pre, state
+
+
+def pin_ssd_chunked(orc, seed=27):
+    rng = np.random.default_rng(seed)
+    batch, L, H, P, N = 2, 23, 2, 3, 6
+    inp = _ssd_inputs(rng, batch, L, H, P, N)
+    y, hL = orc.ssd_fwd(**inp, headdim=P)
+    for Q in (1, 3, 7, 23, 40):
+        pre, state = _ssd_chunked(inp, P, Q)
+        want = np.empty_like(pre)
+        for b in range(batch):
+            want[b] = _ssd_gate_skip(pre[b], inp, b, slice(None), slice(None))
+        _close(y, want, what=f"SSD chunked y (Q={Q})")
+        _close(hL, state, what=f"SSD chunked hL (Q={Q})")
+    # raw dt through bias and softplus is the activated dt
+    raw = rng.standard_normal(inp["dt"].shape)
+    bias = rng.uniform(-2.0, 0.0, H)
+    y1, h1 = orc.ssd_fwd(**dict(inp, dt=raw), headdim=P, dt_bias=bias, dt_softplus=True)
+    y2, h2 = orc.ssd_fwd(**dict(inp, dt=np.logaddexp(0.0, raw + bias)), headdim=P)
+    _close(y1, y2, what="SSD fused dt activation y")
+    _close(h1, h2, what="SSD fused dt activation hL")
+
+
+def pin_ssd_heads_of_one(orc, seed=28):
+    rng = np.random.default_rng(seed)
+    batch, L, H, N = 2, 17, 5, 4
+    inp = _ssd_inputs(rng, batch, L, H, 1, N)
+    y, hL = orc.ssd_fwd(**inp, headdim=1)
+    ys, hs = orc.scan_fwd(inp["x"], inp["dt"], np.repeat(inp["A"][:, None], N, axis=1),
+                          inp["B"], inp["C"], D=inp["D"], z=inp["z"], h0=inp["h0"][:, :, 0, :])
+    _close(y, ys, what="SSD with one channel per head is the scan (y)")
+    _close(hL[:, :, 0, :], hs, what="SSD with one channel per head is the scan (hL)")
+
+
 ALL_PINS = [pin_lti_convolution, pin_brute_force, pin_chunk_split, pin_theorem1,
             pin_ssd_matrix, pin_limits, pin_structure, pin_decode, pin_delta_activation,
             pin_conv_numpy, pin_conv_impulse, pin_conv_split_and_decode,
-            pin_bwd_finite_differences, pin_bwd_linearity]
+            pin_bwd_finite_differences, pin_bwd_linearity, pin_ssd_dual_matrix,
+            pin_ssd_chunked, pin_ssd_heads_of_one]

@@ -17,18 +17,19 @@ MUTANTS = {
     "decay sign flipped": ("const double Abar = exp(dt * a);", "const double Abar = exp(-dt * a);"),
     "delta dropped from Bbar": (": dt * Bm[i_bc + n];", ": Bm[i_bc + n];"),
     "decay of h dropped": ("Abar * h[n] + Bbar * u", "h[n] + Bbar * u"),
-    "readout uses B": ("out += Cm[i_bc + n] * h[n];", "out += Bm[i_bc + n] * h[n];"),
+    "readout uses B": ("h[n] = Abar * h[n] + Bbar * u;\n                    out += Cm[i_bc + n] * h[n];",
+                       "h[n] = Abar * h[n] + Bbar * u;\n                    out += Bm[i_bc + n] * h[n];"),
     "A transposed": ("const double a = A[d * dstate + n];", "const double a = A[n * dim + d];"),
-    "skip term dropped": ("if (Dskip) out += Dskip[d] * u;", ""),
+    "skip term dropped": ("if (Dskip) out += Dskip[d] * u;\n                if (z) {", "if (z) {"),
     "gate sign flipped": ("out *= zz / (1.0 + exp(-zz));", "out *= zz / (1.0 + exp(zz));"),
     "h0 ignored": ("h[n] = h0 ? h0[(b * dim + d) * dstate + n] : 0.0;", "h[n] = 0.0;"),
     "readout before update": (
         "h[n] = Abar * h[n] + Bbar * u;\n                    out += Cm[i_bc + n] * h[n];",
         "out += Cm[i_bc + n] * h[n];\n                    h[n] = Abar * h[n] + Bbar * u;"),
-    "B, C from the previous token": ("const int64_t i_bc = (b * seqlen + t) * dstate;",
-                                     "const int64_t i_bc = (b * seqlen + (t > 0 ? t - 1 : 0)) * dstate;"),
-    "B, C ignore the batch": ("const int64_t i_bc = (b * seqlen + t) * dstate;",
-                              "const int64_t i_bc = t * dstate;"),
+    "B, C from the previous token": ("const int64_t i_bc = (b * seqlen + t) * dstate;    /*",
+                                     "const int64_t i_bc = (b * seqlen + (t > 0 ? t - 1 : 0)) * dstate;    /*"),
+    "B, C ignore the batch": ("const int64_t i_bc = (b * seqlen + t) * dstate;    /*",
+                              "const int64_t i_bc = t * dstate;    /*"),
     "x from the previous token": (
         "const double u = x[i_tok];\n                if (delta_bias)",
         "const double u = x[i_tok - (t > 0 ? dim : 0)];\n                if (delta_bias)"),
@@ -45,7 +46,8 @@ MUTANTS = {
     "final state scaled": ("hL[(b * dim + d) * dstate + n] = h[n];",
                            "hL[(b * dim + d) * dstate + n] = 0.5 * h[n];"),
     "zero-order hold sign": ("(Abar - 1.0) / a", "(1.0 - Abar) / a"),
-    "skip uses the wrong channel": ("out += Dskip[d] * u;", "out += Dskip[dim - 1 - d] * u;"),
+    "skip uses the wrong channel": ("if (Dskip) out += Dskip[d] * u;\n                if (z) {",
+                                    "if (Dskip) out += Dskip[dim - 1 - d] * u;\n                if (z) {"),
     "conv taps reversed": ("pre += weight[d * width + k] *",
                            "pre += weight[d * width + (width - 1 - k)] *"),
     "conv taps shifted by one token": ("conv_input(x, carried, b, t - (width - 1) + k, d,",
@@ -74,6 +76,17 @@ MUTANTS = {
     "bwd dh0 misses the first decay": ("dh0[(b * dim + d) * N + n] = abar_next[n] * lam[n];",
                                        "dh0[(b * dim + d) * N + n] = lam[n];"),
     "bwd skip gradient dropped": ("double dxt = Dskip ? Dskip[d] * g : 0.0;", "double dxt = 0.0;"),
+    "ssd decay from the next head": ("const double decay = exp(step * A[hd]);",
+                                     "const double decay = exp(step * A[(hd + 1) % nheads]);"),
+    "ssd dt from the first head": ("double step = dt[(b * seqlen + t) * nheads + hd];",
+                                   "double step = dt[(b * seqlen + t) * nheads];"),
+    "ssd B and C swapped": ("h[n] = decay * h[n] + step * Bm[i_bc + n] * u;\n                        out += Cm[i_bc + n] * h[n];",
+                            "h[n] = decay * h[n] + step * Cm[i_bc + n] * u;\n                        out += Bm[i_bc + n] * h[n];"),
+    "ssd state rows ignore the head": ("const int64_t row = (b * nheads + hd) * headdim + p;",
+                                       "const int64_t row = b * nheads * headdim + p;"),
+    "ssd decay applied twice": ("h[n] = decay * h[n] + step * Bm[i_bc + n] * u;",
+                                "h[n] = decay * decay * h[n] + step * Bm[i_bc + n] * u;"),
+    "ssd dt bias ignored": ("if (dt_bias) step += dt_bias[hd];", ""),
     "conv carried state ignored": (
         "carried[k] = state_in ? state_in[(b * dim + d) * width + k] : 0.0;",
         "carried[k] = 0.0;"),
