@@ -184,6 +184,9 @@ def main():
     if args.calibrate_copy:
         calibrate_copy()
         return
+    if args.workload in W.SSD_WORKLOADS:
+        bench_ssd(args, W.SSD_WORKLOADS[args.workload])
+        return
     if args.workload in W.CONV_WORKLOADS:
         cw = W.CONV_WORKLOADS[args.workload]
         (bench_conv if cw.kind == "conv" else bench_conv_decode)(args, cw)
@@ -486,6 +489,107 @@ def cpu_baseline_backward(w, inp, softplus):
             "cores": min(threads, w.batch), "kind": "oracle",
             "sample": f"{w.name}: all {w.batch} batch rows x {w.seqlen} tokens x first "
                       f"{channels} of {w.dim} channels, fp64 (rows in parallel), {dt:.2f} s"}
+
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix cores, MI355X
+
+
+def ssd_flops(w):
+    """Matrix-core flops the chunked dual form needs per chunk of Q = 64
+    tokens and head of P = 64 channels (2 flops per multiply-add): C B^T on
+    and below the diagonal (Q*Q*N/2), the masked matrix times x (Q*Q*P/2),
+    C times the carried state (Q*N*P) and the state update (P*Q*N)."""
+    q, p, n = 64, w.headdim, w.dstate
+    per_chunk_head = q * q * n / 2 + q * q * p / 2 + q * n * p + p * q * n
+    chunks = -(-w.seqlen // q)
+    return 2.0 * per_chunk_head * chunks * w.batch * w.nheads
+
+
+def ssd_bytes(w):
+    """x, z in and y out, dt in (bf16), B and C in (bf16), A and D in, the
+    final state out (fp32), the initial state in when there is one."""
+    b, l, d, h, n = w.batch, w.seqlen, w.dim, w.nheads, w.dstate
+    total = 3 * b * l * d * 2 + b * l * h * 2 + 2 * b * l * n * 2 + h * 4 + d * 4
+    total += b * h * w.headdim * n * 4 * (2 if w.h0 == "normal" else 1)
+    return total
+
+
+def bench_ssd(args, w):
+    """One step = one ssd_fwd over the whole workload (one launch)."""
+    import torch
+
+    import selective_state_space_40_amd as ms
+    import ssm_workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    ms.load_library()
+    sets = [W.generate_ssd(w, device=dev, seed=w.seed + 101 * i) for i in range(2)]
+    y = torch.empty_like(sets[0]["x"])
+    hL = torch.empty(w.batch, w.nheads, w.headdim, w.dstate, dtype=torch.float32, device=dev)
+
+    def step(i):
+        inp = sets[i % 2]
+        ms.ssd_fwd(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"],
+                   inp["h0"], out=y, state_out=hL)
+
+    ms_per_step, wall = _time_steps(step, args.warmup, args.steps, torch.cuda.current_stream(dev))
+    sec = ms_per_step / 1e3
+    flops = ssd_flops(w)
+    nbytes = ssd_bytes(w)
+    tflops = flops / sec / 1e12
+    gbps = nbytes / sec / 1e9
+    mfma_frac = tflops / MFMA_BF16_PEAK_TFLOPS
+    hbm_frac = gbps / HBM_PEAK_GBPS
+    bound = "mfma" if flops / (MFMA_BF16_PEAK_TFLOPS * 1e12) > nbytes / (HBM_PEAK_GBPS * 1e9) \
+        else "hbm"
+    cpu = None if args.no_cpu_baseline else cpu_baseline_ssd(w, sets[0])
+    line = {
+        "metric": "Mamba-2 dual-form scan elements/s (B*L*D) and achieved HBM GB/s",
+        "value": w.elements / sec, "unit": "elements/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "seqlen": w.seqlen, "nheads": w.nheads,
+                   "headdim": w.headdim, "dstate": w.dstate, "chunk": 64, "io_dtype": w.io,
+                   "parallelism": "single GPU"},
+        "achieved_GBps": round(gbps, 1), "wall_s": round(wall, 4),
+        "roofline": {"bound": bound,
+                     "achieved": round(gbps if bound == "hbm" else tflops, 3),
+                     "peak": HBM_PEAK_GBPS if bound == "hbm" else MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "GB/s" if bound == "hbm" else "TFLOP/s",
+                     "frac": round(hbm_frac if bound == "hbm" else mfma_frac, 4),
+                     "traffic": None, "kernel": "ssd_fwd_kernel",
+                     "algorithmic_bytes": nbytes, "algorithmic_flops": flops,
+                     "mfma_TFLOPs": round(tflops, 2), "mfma_frac": round(mfma_frac, 4),
+                     "hbm_frac": round(hbm_frac, 4)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline_ssd(w, inp):
+    """The fp64 oracle on the host over a sample of heads (heads are
+    independent), all rows and tokens."""
+    import torch
+
+    import oracle
+
+    orc = oracle.get()
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    nh = max(1, min(w.nheads, int(2.0e6 * threads / (w.batch * w.seqlen * w.headdim))))
+    hix = torch.arange(nh, device=inp["x"].device)
+    chans = torch.arange(nh * w.headdim, device=inp["x"].device)
+    sub = dict(x=inp["x"].index_select(2, chans), dt=inp["dt"].index_select(2, hix),
+               A=inp["A"].index_select(0, hix), B=inp["B"], C=inp["C"],
+               D=inp["D"].index_select(0, chans), z=inp["z"].index_select(2, chans), h0=None)
+    host = {k: (oracle._f64(v) if v is not None else None) for k, v in sub.items()}
+    t0 = time.perf_counter()
+    orc.ssd_fwd(**host, headdim=w.headdim)
+    dt = time.perf_counter() - t0
+    elems = w.batch * w.seqlen * nh * w.headdim
+    return {"value": elems / dt, "unit": "elements/s", "cores": threads, "kind": "oracle",
+            "sample": f"{w.name}: all {w.batch} rows x {w.seqlen} tokens x first {nh} of "
+                      f"{w.nheads} heads, fp64, {dt:.2f} s"}
 
 
 def conv_bytes(w, state_in):

@@ -216,6 +216,41 @@ int ssm_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int dstate, int dty
                  void* dz, float* dh0, float* ddelta_bias, void* workspace,
                  size_t workspace_bytes, hipStream_t stream);
 
+/* Channels per head of the dual form, and the state sizes it provides. */
+#define MAMBA_SSD_HEADDIM 64
+
+/*
+ * Mamba-2's state space dual form (page "Mamba and State Space Models",
+ * section "Mamba-2: Two Algorithms"): A is a number a_h times the identity,
+ * shared with the step dt by the 64 channels of a head, so a chunk of the
+ * sequence maps input to output through one lower-triangular matrix
+ * (entry i, j: C_i . B_j times the decay between) and the chunks are done
+ * with matrix products on the matrix cores, passing only the state on.
+ * The result is the recurrence, per batch row b, head h, channel p of the
+ * head (channel d = h*64 + p) and state n:
+ *
+ *     h[p,n] <- exp(dt[b,t,h] a_h) h[p,n] + dt[b,t,h] B[b,t,n] x[b,t,d]
+ *     y[b,t,d] = (sum_n C[b,t,n] h[p,n] + D[d] x[b,t,d]) * silu(z[b,t,d])
+ *
+ * x, z, y   (batch, seqlen, nheads*64) bf16      z optional
+ * dt        (batch, seqlen, nheads) bf16         positive, or raw with
+ *                                                options (delta_bias is then
+ *                                                (nheads) fp32, one per head)
+ * A         (nheads) fp32                        a_h < 0 (not checked)
+ * B, C      (batch, seqlen, dstate) bf16         shared by all heads
+ * D         (nheads*64) fp32                     optional
+ * h0, hL    (batch, nheads, 64, dstate) fp32     optional; hL may alias h0
+ *
+ * Requirements: headdim == MAMBA_SSD_HEADDIM, dstate 64 or 128, dtype
+ * MAMBA_DTYPE_BF16 (the products run in bf16 with fp32 accumulation);
+ * anything else is MAMBA_ERR_UNSUPPORTED. No workspace. Errors and
+ * ownership as for ssm_scan_fwd.
+ */
+int ssd_fwd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int dstate,
+            int dtype, const void* x, const void* dt, const float* A, const void* B,
+            const void* C, const float* D, const void* z, const float* h0, void* y, float* hL,
+            const mamba_scan_options* options, hipStream_t stream);
+
 /* Widest short convolution the library provides (the pages' width is 4). */
 #define MAMBA_CONV_MAX_WIDTH 4
 

@@ -12,6 +12,7 @@ There is no other code path: without the built library every call raises.
                      delta_bias=None, delta_softplus=False)   # h updated in place
     grads = scan_bwd(x, delta, A, B, C, D=None, z=None, h0=None, dy=dy, dhL=None,
                      delta_bias=None, delta_softplus=False)      # dict of gradients
+    y, hL = ssd_fwd(x, dt, A_heads, B, C, D=None, z=None, h0=None)   # Mamba-2 dual form
     y, state = conv1d_fwd(x, weight, bias=None, state_in=None, silu=True)
     y = conv1d_update(state, x, weight, bias=None, silu=True)  # state updated in place
 
@@ -28,7 +29,7 @@ import os
 
 import torch
 
-__all__ = ["scan_fwd", "scan_bwd", "state_update", "conv1d_fwd", "conv1d_update", "workspace_size", "resolve_plan", "library_path",
+__all__ = ["scan_fwd", "scan_bwd", "ssd_fwd", "state_update", "conv1d_fwd", "conv1d_update", "workspace_size", "resolve_plan", "library_path",
            "load_library", "MambaScanError", "MAX_DSTATE", "ScanPlan", "ScanOptions"]
 
 MAX_DSTATE = 16
@@ -88,6 +89,8 @@ def load_library():
     lib.ssm_scan_bwd.argtypes = ([i64, i64, i64, i32, i32] + [vp] * 8 + [po] + [vp] * 11 +
                                  [vp, ctypes.c_size_t, vp])
     lib.ssm_scan_bwd.restype = i32
+    lib.ssd_fwd.argtypes = [i64, i64, i64, i64, i32, i32] + [vp] * 10 + [po, vp]
+    lib.ssd_fwd.restype = i32
     lib.causal_conv1d_fwd.argtypes = [i64, i64, i64, i32, i32] + [vp] * 6 + [i32, vp]
     lib.causal_conv1d_fwd.restype = i32
     lib.causal_conv1d_update.argtypes = [i64, i64, i32, i32] + [vp] * 5 + [i32, vp]
@@ -359,3 +362,48 @@ def conv1d_update(state, x, weight, bias=None, *, silu=True, out=None):
                                       _stream(dev))
     _check(rc, "causal_conv1d_update")
     return y
+
+
+SSD_HEADDIM = 64
+
+
+def ssd_fwd(x, dt, A, B, C, D=None, z=None, h0=None, *, dt_bias=None, dt_softplus=False,
+            return_state=True, out=None, state_out=None):
+    """Mamba-2 dual form: heads of 64 channels share the step dt (batch, L,
+    nheads) and the decay a_h (A: (nheads,) fp32). x, z (batch, L, nheads*64)
+    and B, C (batch, L, N) are bf16; N is 64 or 128. Returns (y, hL) with
+    hL (batch, nheads, 64, N) fp32 (None when return_state is False)."""
+    lib = load_library()
+    if x.dim() != 3 or dt.dim() != 3:
+        raise ValueError("x must be (batch, L, nheads*64) and dt (batch, L, nheads)")
+    batch, seqlen, dim = x.shape
+    nheads = dt.shape[2]
+    if dim != nheads * SSD_HEADDIM:
+        raise ValueError(f"x has {dim} channels, expected nheads*{SSD_HEADDIM}")
+    dstate = B.shape[2]
+    dev, dtp = x.device, x.dtype
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU device")
+    _need(x, "x", (batch, seqlen, dim), dtp, dev)
+    _need(dt, "dt", (batch, seqlen, nheads), dtp, dev)
+    _need(A, "A", (nheads,), torch.float32, dev)
+    _need(B, "B", (batch, seqlen, dstate), dtp, dev)
+    _need(C, "C", (batch, seqlen, dstate), dtp, dev)
+    _need(D, "D", (dim,), torch.float32, dev)
+    _need(z, "z", (batch, seqlen, dim), dtp, dev)
+    _need(h0, "h0", (batch, nheads, SSD_HEADDIM, dstate), torch.float32, dev)
+    _need(dt_bias, "dt_bias", (nheads,), torch.float32, dev)
+    y = out if out is not None else torch.empty_like(x)
+    _need(y, "out", (batch, seqlen, dim), dtp, dev)
+    hL = None
+    if return_state:
+        hL = state_out if state_out is not None else torch.empty(
+            batch, nheads, SSD_HEADDIM, dstate, dtype=torch.float32, device=dev)
+        _need(hL, "state_out", (batch, nheads, SSD_HEADDIM, dstate), torch.float32, dev)
+    with torch.cuda.device(dev):
+        st = lib.ssd_fwd(batch, seqlen, nheads, SSD_HEADDIM, dstate, _DTYPES.get(dtp, -1),
+                         _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                         _ptr(h0), _ptr(y), _ptr(hL), _options(dt_bias, dt_softplus),
+                         _stream(dev))
+    _check(st, "ssd_fwd")
+    return y, hL

@@ -20,7 +20,7 @@ ARCH = "gfx950"
 
 # (object name, source, extra defines)
 UNITS = [("api", "api.cpp", ()), ("launch", "launch.hip", ()), ("conv1d", "conv1d.hip", ()),
-         ("scan_bwd", "scan_bwd.hip", ())] + [
+         ("scan_bwd", "scan_bwd.hip", ()), ("ssd", "ssd.hip", ())] + [
     (f"scan_io{io}_sp{sp}", "scan_variant.hip",
      (f"-DMAMBA_VARIANT_IO={io}", f"-DMAMBA_VARIANT_SP={sp}"))
     for io in (0, 1) for sp in (0, 1)]

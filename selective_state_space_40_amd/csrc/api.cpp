@@ -324,6 +324,53 @@ int ssm_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int dstate, int dty
                                                                              : MAMBA_ERR_HIP;
 }
 
+int ssd_fwd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int dstate,
+            int dtype, const void* x, const void* dt, const float* A, const void* B,
+            const void* C, const float* D, const void* z, const float* h0, void* y, float* hL,
+            const mamba_scan_options* options, hipStream_t stream) {
+    if (batch < 0 || seqlen < 0 || nheads < 0 || headdim < 0) return MAMBA_ERR_INVALID_ARG;
+    if (dtype != MAMBA_DTYPE_F32 && dtype != MAMBA_DTYPE_BF16) return MAMBA_ERR_INVALID_ARG;
+    if (headdim != MAMBA_SSD_HEADDIM || (dstate != 64 && dstate != 128) ||
+        dtype != MAMBA_DTYPE_BF16)
+        return MAMBA_ERR_UNSUPPORTED;
+    if (nheads > (int64_t(1) << 24)) return MAMBA_ERR_UNSUPPORTED;
+    int st = check_shape(batch, seqlen, nheads * headdim, 1, dtype);
+    if (st != MAMBA_OK) return st;
+    if (batch * nheads >= (int64_t(1) << 31)) return MAMBA_ERR_UNSUPPORTED;
+    const float* dt_bias = nullptr;
+    int dt_softplus = 0;
+    st = read_options(options, &dt_bias, &dt_softplus);
+    if (st != MAMBA_OK) return st;
+    if (batch == 0 || nheads == 0) return MAMBA_OK;
+    if (A == nullptr) return MAMBA_ERR_INVALID_ARG;
+    if (seqlen > 0 && (x == nullptr || dt == nullptr || B == nullptr || C == nullptr ||
+                       y == nullptr))
+        return MAMBA_ERR_INVALID_ARG;
+    const void* ptrs[] = {x, dt, A, B, C, D, z, h0, y, hL};
+    for (const void* p : ptrs)
+        if (p != nullptr && !aligned16(p)) return MAMBA_ERR_MISALIGNED;
+    if (seqlen == 0 && hL == nullptr) return MAMBA_OK;
+
+    mamba::SsdArgs a;
+    a.batch = batch;
+    a.seqlen = seqlen;
+    a.nheads = nheads;
+    a.dstate = dstate;
+    a.x = x;
+    a.dt = dt;
+    a.A = A;
+    a.B = B;
+    a.C = C;
+    a.D = D;
+    a.z = z;
+    a.h0 = h0;
+    a.y = y;
+    a.hL = hL;
+    a.dt_bias = dt_bias;
+    a.dt_softplus = dt_softplus;
+    return mamba::launch_ssd_fwd(a, stream) == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP;
+}
+
 int causal_conv1d_fwd(int64_t batch, int64_t seqlen, int64_t dim, int width, int dtype,
                       const void* x, const float* weight, const float* bias,
                       const void* state_in, void* y, void* state_out, int silu,

@@ -119,6 +119,26 @@ size_t scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int 
 // summary pass that computes the checkpoints. Arguments are validated.
 hipError_t launch_scan_bwd(const BwdArgs& a, int fwd_split, void* workspace, hipStream_t stream);
 
+// Mamba-2 dual form: heads of 64 channels sharing one decay and step.
+struct SsdArgs {
+    int64_t batch, seqlen, nheads;
+    int dstate;            // 64 or 128
+    const void* x;         // (batch, seqlen, nheads*64) bf16
+    const void* dt;        // (batch, seqlen, nheads) bf16
+    const float* A;        // (nheads)
+    const void* B;         // (batch, seqlen, dstate) bf16
+    const void* C;
+    const float* D;        // (nheads*64) or nullptr
+    const void* z;         // like x, or nullptr
+    const float* h0;       // (batch, nheads, 64, dstate) or nullptr
+    void* y;
+    float* hL;
+    const float* dt_bias;  // (nheads) or nullptr
+    int dt_softplus;
+};
+
+hipError_t launch_ssd_fwd(const SsdArgs& a, hipStream_t stream);
+
 // Workspace layout for nchunks > 1: three fp32 arrays of
 // nchunks * batch * dim * dstate elements each: the state entering each
 // chunk, each chunk's end state from a zero start, and each chunk's decay

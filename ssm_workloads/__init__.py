@@ -33,7 +33,7 @@ import torch
 
 __all__ = ["Workload", "WORKLOADS", "generate_scan", "generate_decode_layer",
            "io_torch_dtype", "ConvWorkload", "CONV_WORKLOADS", "generate_conv",
-           "generate_conv_decode_layer"]
+           "generate_conv_decode_layer", "SsdWorkload", "SSD_WORKLOADS", "generate_ssd"]
 
 
 @dataclass(frozen=True)
@@ -262,3 +262,82 @@ def generate_conv_decode_layer(w, layer, device="cpu", batch=None, dim=None):
     x = _normal((batch, dim), g, device, dt)
     st = _normal((batch, dim, w.width), g, device, dt)
     return dict(state=st, x=x, weight=weight, bias=bias)
+
+
+# ---------------------------------------------------------------------------
+# Mamba-2 dual-form workloads (section "Mamba-2: Two Algorithms": one decay
+# per head, 128 numbers of state per channel). The pages give the state size,
+# not the head size; heads of 64 channels are the reading used (the channel
+# count is the Mamba-2.8B layer's 5,120, so 80 heads). Recipe:
+#   - A (nheads,) fp32 = -U(1, 16), the -1 .. -16 range of section "Every
+#     Step the Same" spread over the heads;
+#   - dt (batch, L, nheads) = softplus(N(0, 1) * delta_std + delta_shift) in
+#     fp32, rounded to bf16; raw_dt=True gives N(0, 1) * delta_std and a
+#     per-head bias delta_shift + N(0, 1) * 0.5 (drawn last) instead;
+#   - x, z, B, C ~ N(0, 1) rounded to bf16; D (nheads*64,) fp32 ~ N(0, 1);
+#   - h0: zeros, or N(0, 1) fp32 (batch, nheads, 64, N).
+# Draw order: A, D, x, dt, z, B, C, h0.
+
+
+@dataclass(frozen=True)
+class SsdWorkload:
+    name: str
+    batch: int
+    seqlen: int
+    nheads: int
+    dstate: int
+    delta_shift: float
+    delta_std: float
+    h0: str
+    seed: int
+    headdim: int = 64
+    io: str = "bf16"
+    note: str = field(default="", compare=False)
+
+    @property
+    def dim(self):
+        return self.nheads * self.headdim
+
+    @property
+    def elements(self):
+        return self.batch * self.seqlen * self.dim
+
+
+SSD_WORKLOADS = {
+    "ssd_mamba2_layer": SsdWorkload(
+        "ssd_mamba2_layer", 8, 2048, 80, 128, -4.0, 0.5, "zero", 7,
+        note="Mamba-2 dual form over a 5,120-channel layer, 80 heads of 64, state 128"),
+}
+
+
+def generate_ssd(w, device="cpu", batch=None, seqlen=None, nheads=None, dstate=None, seed=None,
+                 h0=None, raw_dt=False):
+    """Inputs of one ssd_fwd call: x, dt, A, B, C, D, z, h0 (and dt_bias with
+    raw_dt=True)."""
+    batch = w.batch if batch is None else batch
+    seqlen = w.seqlen if seqlen is None else seqlen
+    nheads = w.nheads if nheads is None else nheads
+    dstate = w.dstate if dstate is None else dstate
+    seed = w.seed if seed is None else seed
+    h0 = w.h0 if h0 is None else h0
+    dt_ = io_torch_dtype(w.io)
+    dim = nheads * w.headdim
+    g = _gen(seed, device)
+    A = -(1.0 + 15.0 * torch.rand(nheads, generator=g, device=device, dtype=torch.float32))
+    D = torch.randn(dim, generator=g, device=device, dtype=torch.float32)
+    x = _normal((batch, seqlen, dim), g, device, dt_)
+    if raw_dt:
+        dt = _normal((batch, seqlen, nheads), g, device, dt_, std=w.delta_std)
+    else:
+        dt = _softplus_normal((batch, seqlen, nheads), g, device, dt_, w.delta_shift, w.delta_std)
+    z = _normal((batch, seqlen, dim), g, device, dt_)
+    B = _normal((batch, seqlen, dstate), g, device, dt_)
+    C = _normal((batch, seqlen, dstate), g, device, dt_)
+    hs = None
+    if h0 == "normal":
+        hs = torch.randn(batch, nheads, w.headdim, dstate, generator=g, device=device,
+                         dtype=torch.float32)
+    out = dict(x=x, dt=dt, A=A, B=B, C=C, D=D, z=z, h0=hs)
+    if raw_dt:
+        out["dt_bias"] = _bias(nheads, g, device, w.delta_shift)
+    return out

@@ -29,7 +29,7 @@ def lib():
 def test_library_exports_every_declared_symbol(lib):
     names = _declared_functions()
     assert names == ["causal_conv1d_fwd", "causal_conv1d_update", "mamba_status_string",
-                     "ssm_scan_bwd", "ssm_scan_bwd_workspace_size", "ssm_scan_fwd",
+                     "ssd_fwd", "ssm_scan_bwd", "ssm_scan_bwd_workspace_size", "ssm_scan_fwd",
                      "ssm_scan_fwd_workspace_size", "ssm_state_update"]
     for n in names:
         assert hasattr(lib, n), f"{n} missing from {ms.library_path()}"
@@ -217,3 +217,22 @@ def test_scan_bwd_rejects_bad_arguments(lib):
     assert bwd(ws=None) == WORKSPACE
     assert bwd(wsb=need.value - 4) == WORKSPACE
     assert bwd(dim=0) == OK
+
+
+def test_ssd_rejects_bad_arguments(lib):
+    def ssd(batch=2, seqlen=64, nheads=4, headdim=64, dstate=128, dtype=1, opts=None, **kw):
+        p = dict(x=P, dt=P, A=P, B=P, C=P, D=None, z=None, h0=None, y=P, hL=None)
+        p.update(kw)
+        return lib.ssd_fwd(batch, seqlen, nheads, headdim, dstate, dtype, p["x"], p["dt"], p["A"],
+                           p["B"], p["C"], p["D"], p["z"], p["h0"], p["y"], p["hL"], opts, None)
+    assert ssd(batch=-1) == INVALID
+    assert ssd(dtype=3) == INVALID
+    assert ssd(headdim=32) == UNSUPPORTED
+    assert ssd(dstate=16) == UNSUPPORTED
+    assert ssd(dtype=0) == UNSUPPORTED      # fp32 I/O: the products run in bf16
+    for name in ("x", "dt", "A", "B", "C", "y"):
+        assert ssd(**{name: None}) == INVALID, name
+    for name in ("x", "dt", "A", "B", "C", "D", "z", "h0", "y", "hL"):
+        assert ssd(**{name: PM}) == MISALIGNED, name
+    assert ssd(opts=_opts(reserved=1)) == INVALID
+    assert ssd(nheads=0) == OK and ssd(batch=0) == OK

@@ -1,0 +1,137 @@
+"""GPU parity of the Mamba-2 dual form (ssd_fwd through the C ABI, bf16
+matrix-core products) against the fp64 CPU oracle on the same seeded inputs.
+
+Tolerance: max abs error <= 2e-2 * max|oracle| per output tensor (bf16 I/O;
+the chunk matrix, the weighted inputs and the state are rounded to bf16 as
+matrix-core operands, with fp32 accumulation), on y and on the final state.
+"""
+import dataclasses
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import selective_state_space_40_amd as ms
+import ssm_workloads as W
+from parity_util import assert_close
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+TOL = 2e-2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    ms.load_library()
+    yield
+    torch.cuda.synchronize()
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+W0 = W.SSD_WORKLOADS["ssd_mamba2_layer"]
+
+
+def _run(inp, **kw):
+    sp = inp.get("dt_bias") is not None
+    y, hL = ms.ssd_fwd(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp.get("D"),
+                       inp.get("z"), inp.get("h0"), dt_bias=inp.get("dt_bias"), dt_softplus=sp,
+                       **kw)
+    torch.cuda.synchronize()
+    return y, hL
+
+
+def _oracle(orc, inp):
+    sp = inp.get("dt_bias") is not None
+    return orc.ssd_fwd(**inp, headdim=64, dt_softplus=sp)
+
+
+CASES = [
+    # (batch, seqlen, nheads, dstate)
+    (1, 1, 1, 64), (1, 5, 2, 128), (2, 63, 1, 64), (1, 64, 3, 128), (2, 65, 2, 64),
+    (1, 128, 1, 128), (2, 200, 3, 128), (1, 257, 2, 64), (3, 31, 1, 128),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "x".join(map(str, c)))
+def test_ssd_shapes(orc, case):
+    batch, seqlen, nheads, dstate = case
+    for h0 in ("zero", "normal"):
+        inp = W.generate_ssd(W0, device=DEV, batch=batch, seqlen=seqlen, nheads=nheads,
+                             dstate=dstate, seed=sum(case), h0=h0)
+        _say(f"case ssd {case} h0={h0}")
+        y, hL = _run(inp)
+        yo, ho = _oracle(orc, inp)
+        assert_close(y, yo, TOL, f"ssd {case} y")
+        assert_close(hL, ho, TOL, f"ssd {case} hL")
+
+
+def test_ssd_optional_inputs_and_fused_dt(orc):
+    base = W.generate_ssd(W0, device=DEV, batch=2, seqlen=150, nheads=2, dstate=128, seed=3,
+                          h0="normal")
+    for drop in (("D",), ("z",), ("D", "z", "h0")):
+        inp = dict(base)
+        for k in drop:
+            inp[k] = None
+        _say(f"case ssd without {drop}")
+        y, hL = _run(inp)
+        yo, ho = _oracle(orc, inp)
+        assert_close(y, yo, TOL, f"ssd without {drop} y")
+        assert_close(hL, ho, TOL, f"ssd without {drop} hL")
+    inp = W.generate_ssd(W0, device=DEV, batch=2, seqlen=150, nheads=2, dstate=64, seed=4,
+                         raw_dt=True)
+    _say("case ssd raw dt + bias + softplus")
+    y, hL = _run(inp)
+    yo, ho = _oracle(orc, inp)
+    assert_close(y, yo, TOL, "ssd fused dt y")
+    assert_close(hL, ho, TOL, "ssd fused dt hL")
+
+
+def test_ssd_full_size_sampled_heads(orc):
+    w = W0
+    inp = W.generate_ssd(w, device=DEV)
+    _say(f"case {w.name}: B={w.batch} L={w.seqlen} heads={w.nheads} N={w.dstate}")
+    y, hL = _run(inp)
+    heads = [0, 1, 39, 78, 79]
+    chans = torch.cat([torch.arange(h * 64, (h + 1) * 64) for h in heads]).to(DEV)
+    hix = torch.as_tensor(heads, device=DEV)
+    sub = dict(x=inp["x"].index_select(2, chans), dt=inp["dt"].index_select(2, hix),
+               A=inp["A"].index_select(0, hix), B=inp["B"], C=inp["C"],
+               D=inp["D"].index_select(0, chans), z=inp["z"].index_select(2, chans), h0=None)
+    _say(f"case {w.name}: oracle on heads {heads}")
+    yo, ho = orc.ssd_fwd(**sub, headdim=64)
+    assert_close(y.index_select(2, chans), yo, TOL, "full-size ssd y (sampled heads)")
+    assert_close(hL.index_select(1, hix), ho, TOL, "full-size ssd hL (sampled heads)")
+
+
+def test_ssd_resume_alias_empty_deterministic(orc):
+    inp = W.generate_ssd(W0, device=DEV, batch=2, seqlen=190, nheads=2, dstate=128, seed=5,
+                         h0="normal")
+    yo, ho = _oracle(orc, inp)
+    m = 77
+    first = {k: (v[:, :m].contiguous() if k in ("x", "dt", "B", "C", "z") else v)
+             for k, v in inp.items()}
+    second = {k: (v[:, m:].contiguous() if k in ("x", "dt", "B", "C", "z") else v)
+              for k, v in inp.items()}
+    state = inp["h0"].clone()
+    first["h0"] = state
+    _say("case ssd split at 77, state carried in place")
+    y1, _ = _run(first, state_out=state)
+    second["h0"] = state
+    y2, _ = _run(second, state_out=state)
+    assert_close(torch.cat([y1, y2], dim=1), yo, TOL, "ssd split y")
+    assert_close(state, ho, TOL, "ssd split state")
+    empty = {k: (v[:, :0].contiguous() if k in ("x", "dt", "B", "C", "z") else v)
+             for k, v in inp.items()}
+    y, hL = _run(empty)
+    assert y.shape[1] == 0 and torch.equal(hL, inp["h0"])
+    a1 = _run(inp)
+    a2 = _run(inp)
+    assert torch.equal(a1[0], a2[0]) and torch.equal(a1[1], a2[1])
