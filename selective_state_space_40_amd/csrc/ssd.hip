@@ -9,18 +9,23 @@
 //     Y      = M X + diag(exp(S_i)) C H^T              (Q x P)
 //     H     <- exp(S_last) H + (X * w)^T B,  w_j = exp(S_last - S_j) dt_j
 //     y      = (Y + D x) * silu(z)
-// All four products are bf16 MFMA (v_mfma_f32_32x32x16_bf16) with fp32
+// All products are bf16 MFMA (v_mfma_f32_16x16x32_bf16) with fp32
 // accumulation.
 //
 // Work mapping. One workgroup of 4 waves per (batch row, head) walks the
 // chunks in order, so the state never leaves the chip: it lives in the MFMA
-// accumulators, each wave holding a 32 x N/2 block of it in fp32, and is
-// rounded to bf16 in LDS only as the operand of C H^T. Each chunk's x, B and
-// C are staged once in LDS (rows padded by 16 bytes against bank conflicts)
-// and feed every product; wave w computes the (w/2, w%2) 32 x 32 block of G
-// (the block above the diagonal is zero and skipped), of Y, and its block of
-// the state update. The matrix M goes through LDS to change from the
-// accumulator layout to the operand layout. bf16 I/O, head size 64,
+// accumulators as H^T (N x P), wave w holding rows n of its quarter of N for
+// all 64 channels, in fp32; it is rounded to bf16 in LDS only as an operand.
+// Wave w owns tokens i in [16w, 16w + 16) of the chunk. It forms G^T for its
+// tokens (rows j <= its last token only) and turns it into M^T in its
+// accumulators; the accumulator of a 16 x 16 block holds, in each lane, one
+// column i and rows j = 4(lane / 16) + 0..3, and two such blocks are exactly
+// the K = 32 operand of the next product up to a fixed permutation of K, so
+// Y^T = X^T M^T takes M^T straight from the accumulators (X^T is read with
+// the same permutation) and M never goes through LDS. The chunk's x, B and C
+// are staged once in LDS (rows padded by 16 bytes), B also transposed and
+// scaled by w_j for the state update, and the next chunk's inputs are loaded
+// into registers while this one is computed. bf16 I/O, head size 64,
 // N = 64 or 128, Q = 64.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -36,194 +41,313 @@ constexpr int kP = 64;   // channels per head
 constexpr int kSsdThreads = 256;
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
-typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 
 template <int N>
 struct SsdLds {
     static constexpr int kRowN = N + 8;   // padded row of N bf16
     static constexpr int kRowQ = kQ + 8;  // padded row of 64 bf16
-    __bf16 C[kQ][kRowN];    // C rows of the chunk (i, n)
-    __bf16 B[kQ][kRowN];    // B rows (j, n)
-    __bf16 X[kQ][kRowQ];    // x of the head (j, p)
-    __bf16 Xw[kQ][kRowQ];   // x * w_j (j, p)
-    __bf16 M[kQ][kRowQ];    // the chunk's matrix (i, j)
-    __bf16 H[kP][kRowN];    // the state entering the chunk (p, n)
-    float dt[kQ];           // the step as used
-    float S[kQ];            // a * running sum of dt inside the chunk
+    __bf16 C[kQ][kRowN];     // C rows of the chunk (i, n)
+    __bf16 B[kQ][kRowN];     // B rows (j, n)
+    __bf16 Bt[N][kRowQ];     // B transposed (n, j)
+    __bf16 Xt[kP][kRowQ];    // x transposed (p, j)
+    __bf16 H[kP][kRowN];     // the state entering the chunk (p, n)
+    float dt[kQ];            // the step as used
+    float S[kQ];             // log2 of the decay from chunk start through token j
+    float w[kQ];             // exp(S_last - S_j) dt_j: weight of token j in the state update
 };
 
-__device__ __forceinline__ bf16x8 load8(const __bf16* p) {
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 lds8(const __bf16* p) {
     return *reinterpret_cast<const bf16x8*>(p);
 }
 
-// 8 values down a column of a row-major LDS array (k rows apart)
-__device__ __forceinline__ bf16x8 load8_col(const __bf16* p, int stride) {
+// Operand whose 8 K values are two runs of 4: p[0..3] and q[0..3].
+__device__ __forceinline__ bf16x8 lds4x2(const __bf16* p, const __bf16* q) {
+    typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+    const bf16x4 a = *reinterpret_cast<const bf16x4*>(p);
+    const bf16x4 b = *reinterpret_cast<const bf16x4*>(q);
     bf16x8 v;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = p[e * stride];
+    for (int e = 0; e < 4; ++e) {
+        v[e] = a[e];
+        v[e + 4] = b[e];
+    }
     return v;
 }
 
-__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+// The next chunk's inputs, held in registers between chunks. Threads
+// 0 .. 63 each hold an 8 x 8 block (8 tokens, 8 channels) of x, the next
+// N threads (N / 8 blocks per 8 tokens) an 8 x 8 block of B; all threads
+// hold a share of C.
+template <int N>
+struct Prefetch {
+    static constexpr int kXBlocks = (kQ / 8) * (kP / 8);
+    static constexpr int kBBlocks = (kQ / 8) * (N / 8);
+    static constexpr int kC = kQ * N / 8 / kSsdThreads;   // uint4 of C per thread
+    uint4 blk[8], c[kC];
+    float dt;
+};
+
+template <int N>
+__device__ __forceinline__ void fetch_chunk(const SsdArgs& a, int64_t bb, int64_t hd, int64_t t0,
+                                            int cnt, Prefetch<N>& f) {
+    const int tid = threadIdx.x;
+    const int64_t L = a.seqlen, dim = a.nheads * kP;
+    const uint16_t* src = nullptr;
+    int64_t stride = 0;
+    int jb = 0;
+    if (tid < Prefetch<N>::kXBlocks) {
+        jb = tid / (kP / 8);
+        src = static_cast<const uint16_t*>(a.x) + (bb * L + t0) * dim + hd * kP + 8 * (tid % (kP / 8));
+        stride = dim;
+    } else if (tid < Prefetch<N>::kXBlocks + Prefetch<N>::kBBlocks) {
+        const int e = tid - Prefetch<N>::kXBlocks;
+        jb = e / (N / 8);
+        src = static_cast<const uint16_t*>(a.B) + (bb * L + t0) * N + 8 * (e % (N / 8));
+        stride = N;
+    }
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+        const int j = 8 * jb + r;
+        f.blk[r] = (src != nullptr && j < cnt)
+                       ? *reinterpret_cast<const uint4*>(src + static_cast<int64_t>(j) * stride)
+                       : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < Prefetch<N>::kC; ++r) {
+        const int e = tid + r * kSsdThreads;
+        const int j = e / (N / 8), q = e % (N / 8);
+        f.c[r] = j < cnt ? *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.C) +
+                                                           (bb * L + t0 + j) * N + 8 * q)
+                         : make_uint4(0, 0, 0, 0);
+    }
+    const int lane = tid & (kWave - 1);
+    f.dt = (tid < kWave && lane < cnt)
+               ? raw_to_f32<kIoBF16>(load_raw<kIoBF16>(a.dt, (bb * L + t0 + lane) * a.nheads + hd))
+               : 0.0f;
 }
 
-// Row of element v of a lane's 32 x 32 accumulator block (its column is
-// lane % 32).
-__device__ __forceinline__ int acc_row(int v, int lane) {
-    return 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+// 8 x 8 bf16 transpose in registers: in[r] holds row r (8 values), out[f]
+// column f.
+__device__ __forceinline__ void transpose8(const uint4 (&in)[8], uint4 (&out)[8]) {
+    uint32_t iw[8][4];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+        iw[r][0] = in[r].x; iw[r][1] = in[r].y; iw[r][2] = in[r].z; iw[r][3] = in[r].w;
+    }
+#pragma unroll
+    for (int f = 0; f < 8; ++f) {
+        uint32_t o[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t lo = iw[2 * q][f >> 1], hi = iw[2 * q + 1][f >> 1];
+            o[q] = (f & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
+        }
+        out[f] = make_uint4(o[0], o[1], o[2], o[3]);
+    }
 }
 
 template <int N, bool SP, bool HAS_D, bool HAS_Z>
-__global__ __launch_bounds__(kSsdThreads) void ssd_fwd_kernel(SsdArgs a) {
-    constexpr int NT = N / 64;  // 32 x 32 state blocks per wave
+__global__ __launch_bounds__(kSsdThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void ssd_fwd_kernel(SsdArgs a) {
+    constexpr int NW = N / 4;        // state rows n per wave
+    constexpr int NTN = NW / 16;     // 16-row blocks of them
+    constexpr int RN = SsdLds<N>::kRowN, RQ = SsdLds<N>::kRowQ;
     __shared__ __attribute__((aligned(16))) SsdLds<N> lds;
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
-    const int64_t b = blockIdx.x / a.nheads;
-    const int64_t hd = blockIdx.x - b * a.nheads;
+    const int g = lane >> 4, c = lane & 15;
+    const int64_t bb = blockIdx.x / a.nheads;
+    const int64_t hd = blockIdx.x - bb * a.nheads;
     const int64_t L = a.seqlen;
     const int64_t dim = a.nheads * kP;
-    const float alog2 = a.A[hd] * kLog2e;   // log2 of the decay per unit of dt
+    const float alog2 = a.A[hd] * kLog2e;
     const float bias = a.dt_bias != nullptr ? a.dt_bias[hd] : 0.0f;
+    const int i = 16 * w + c;        // this lane's token of the chunk (as output column)
 
-    // the wave's blocks: rows r0 of G and Y, columns c0 of G (j) and Y (p);
-    // state rows p0, columns n0 + 32 t
-    const int r0 = 32 * (w >> 1), c0 = 32 * (w & 1);
-    const int p0 = 32 * (w >> 1), n0 = (N / 2) * (w & 1);
-    const int col = lane & 31;
-
-    f32x16 H[NT];
+    // state H^T: block (nt, pt) holds rows n = nw0 + 16 nt + 4 g + v, column p = 16 pt + c
+    const int nw0 = NW * w;
+    f32x4 H[NTN][4];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
+    for (int nt = 0; nt < NTN; ++nt)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int p = p0 + acc_row(v, lane), n = n0 + 32 * t + col;
-            H[t][v] = a.h0 != nullptr ? a.h0[((b * a.nheads + hd) * kP + p) * N + n] : 0.0f;
-        }
-    }
+        for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int n = nw0 + 16 * nt + 4 * g + v, p = 16 * pt + c;
+                H[nt][pt][v] = a.h0 != nullptr ? a.h0[((bb * a.nheads + hd) * kP + p) * N + n] : 0.0f;
+            }
 
     const int64_t nchunks = (L + kQ - 1) / kQ;
-    for (int64_t c = 0; c < nchunks; ++c) {
-        const int64_t t0 = c * kQ;
+    Prefetch<N> pf;
+    fetch_chunk<N>(a, bb, hd, 0, static_cast<int>(min<int64_t>(kQ, L)), pf);
+    for (int64_t ch = 0; ch < nchunks; ++ch) {
+        const int64_t t0 = ch * kQ;
         const int cnt = static_cast<int>(min<int64_t>(kQ, L - t0));
 
-        // (1) stage x, B, C of the chunk (tokens past the end as zeros) and
-        // the steps with their running sum
-        for (int e = tid; e < kQ * (kP / 8); e += kSsdThreads) {
-            const int j = e / (kP / 8), q = e - j * (kP / 8);
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (j < cnt)
-                v = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.x) +
-                                                    (b * L + t0 + j) * dim + hd * kP + 8 * q);
-            *reinterpret_cast<uint4*>(&lds.X[j][8 * q]) = v;
+        // (1) stage the chunk: x transposed, B as it is and transposed, C;
+        // the steps, their running sum and the token weights; the state
+        // entering the chunk as bf16 (p, n)
+        if (tid < Prefetch<N>::kXBlocks + Prefetch<N>::kBBlocks) {
+            uint4 tr[8];
+            transpose8(pf.blk, tr);
+            if (tid < Prefetch<N>::kXBlocks) {
+                const int jb = tid / (kP / 8), pb = tid % (kP / 8);
+#pragma unroll
+                for (int f = 0; f < 8; ++f) *reinterpret_cast<uint4*>(&lds.Xt[8 * pb + f][8 * jb]) = tr[f];
+            } else {
+                const int e = tid - Prefetch<N>::kXBlocks;
+                const int jb = e / (N / 8), nb = e % (N / 8);
+#pragma unroll
+                for (int f = 0; f < 8; ++f) {
+                    *reinterpret_cast<uint4*>(&lds.Bt[8 * nb + f][8 * jb]) = tr[f];
+                    *reinterpret_cast<uint4*>(&lds.B[8 * jb + f][8 * nb]) = pf.blk[f];
+                }
+            }
         }
-        for (int e = tid; e < 2 * kQ * (N / 8); e += kSsdThreads) {
-            const int which = e / (kQ * (N / 8));
-            const int r = e - which * kQ * (N / 8);
-            const int j = r / (N / 8), q = r - j * (N / 8);
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (j < cnt)
-                v = *reinterpret_cast<const uint4*>(
-                    static_cast<const uint16_t*>(which ? a.C : a.B) + (b * L + t0 + j) * N + 8 * q);
-            *reinterpret_cast<uint4*>(which ? &lds.C[j][8 * q] : &lds.B[j][8 * q]) = v;
+#pragma unroll
+        for (int r = 0; r < Prefetch<N>::kC; ++r) {
+            const int e = tid + r * kSsdThreads;
+            const int j = e / (N / 8), q = e % (N / 8);
+            *reinterpret_cast<uint4*>(&lds.C[j][8 * q]) = pf.c[r];
         }
         if (w == 0) {
-            float dtv = 0.0f;
-            if (lane < cnt) {
-                const float v = raw_to_f32<kIoBF16>(
-                    load_raw<kIoBF16>(a.dt, (b * L + t0 + lane) * a.nheads + hd)) + bias;
-                dtv = SP ? softplus_f32(v) : v;
-            }
-            float s = dtv;  // inclusive running sum over the chunk's lanes
+            const float v = pf.dt + bias;
+            const float dtv = lane < cnt ? (SP ? softplus_f32(v) : v) : 0.0f;
+            float s = dtv;
 #pragma unroll
             for (int k = 1; k < kWave; k *= 2) {
                 const float o = __shfl_up(s, k, kWave);
                 if (lane >= k) s += o;
             }
+            s *= alog2;
+            const float last = __shfl(s, kWave - 1, kWave);
             lds.dt[lane] = dtv;
-            lds.S[lane] = s * alog2;  // log2 of the decay from chunk start through token lane
+            lds.S[lane] = s;
+            lds.w[lane] = fast_exp2(last - s) * dtv;
         }
+#pragma unroll
+        for (int nt = 0; nt < NTN; ++nt)
+#pragma unroll
+            for (int pt = 0; pt < 4; ++pt) {
+                typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+                bf16x4 hv;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) hv[v] = static_cast<__bf16>(H[nt][pt][v]);
+                *reinterpret_cast<bf16x4*>(&lds.H[16 * pt + c][nw0 + 16 * nt + 4 * g]) = hv;
+            }
         __syncthreads();
 
-        // (2) x * w_j, the state as bf16, and the wave's block of M
+        // the next chunk's loads go out now and land during this chunk
+        if (ch + 1 < nchunks)
+            fetch_chunk<N>(a, bb, hd, t0 + kQ, static_cast<int>(min<int64_t>(kQ, L - t0 - kQ)), pf);
         const float s_last = lds.S[kQ - 1];
-        for (int e = tid; e < kQ * kP; e += kSsdThreads) {
-            const int j = e / kP, p = e - j * kP;
-            const float wj = fast_exp2(s_last - lds.S[j]) * lds.dt[j];
-            lds.Xw[j][p] = static_cast<__bf16>(static_cast<float>(lds.X[j][p]) * wj);
-        }
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-#pragma unroll
-            for (int v = 0; v < 16; ++v)
-                lds.H[p0 + acc_row(v, lane)][n0 + 32 * t + col] = static_cast<__bf16>(H[t][v]);
-        if (r0 >= c0) {  // the block above the diagonal is zero
-            f32x16 G = {};
-#pragma unroll
-            for (int k = 0; k < N; k += 16) {
-                const int kk = k + 8 * (lane >> 5);
-                G = mfma(load8(&lds.C[r0 + col][kk]), load8(&lds.B[c0 + col][kk]), G);
-            }
-            const int j = c0 + col;
-            const float sj = lds.S[j], dtj = lds.dt[j];
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int i = r0 + acc_row(v, lane);
-                const float m = i >= j ? G[v] * fast_exp2(lds.S[i] - sj) * dtj : 0.0f;
-                lds.M[i][j] = static_cast<__bf16>(m);
-            }
-        } else {
-#pragma unroll
-            for (int v = 0; v < 16; ++v) lds.M[r0 + acc_row(v, lane)][c0 + col] = static_cast<__bf16>(0.0f);
-        }
-        __syncthreads();
 
-        // (3) the wave's block of Y: M X (only j <= last row of the block)
-        // plus diag(exp(S)) C H^T; then skip, gate and store
-        {
-            f32x16 Yd = {}, Yo = {};
-            const int kmax = r0 + 32;
-            for (int k = 0; k < kmax; k += 16) {
-                const int kk = k + 8 * (lane >> 5);
-                Yd = mfma(load8(&lds.M[r0 + col][kk]), load8_col(&lds.X[kk][c0 + col], SsdLds<N>::kRowQ), Yd);
-            }
+        // (3) M^T for this wave's tokens: blocks jt = 0 .. w of G^T = B C^T
+        f32x4 Mt[4];
+        const float si = lds.S[i];
 #pragma unroll
-            for (int k = 0; k < N; k += 16) {
-                const int kk = k + 8 * (lane >> 5);
-                Yo = mfma(load8(&lds.C[r0 + col][kk]), load8(&lds.H[c0 + col][kk]), Yo);
-            }
-            const int p = c0 + col;
-            const int64_t chan = hd * kP + p;
-            const float dskip = HAS_D ? a.D[chan] : 0.0f;
+        for (int jt = 0; jt < 4; ++jt) {
+            Mt[jt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            if (jt <= w) {
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int i = r0 + acc_row(v, lane);
-                if (i < cnt) {
-                    float out = Yd[v] + fast_exp2(lds.S[i]) * Yo[v];
-                    const int64_t idx = (b * L + t0 + i) * dim + chan;
-                    if constexpr (HAS_D) out = fmaf(dskip, static_cast<float>(lds.X[i][p]), out);
-                    if constexpr (HAS_Z) out *= silu(raw_to_f32<kIoBF16>(load_raw<kIoBF16>(a.z, idx)));
-                    store_io<kIoBF16>(a.y, idx, out);
+                for (int k = 0; k < N; k += 32)
+                    Mt[jt] = mfma16(lds8(&lds.B[16 * jt + c][k + 8 * g]),
+                                    lds8(&lds.C[i][k + 8 * g]), Mt[jt]);
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int j = 16 * jt + 4 * g + v;
+                    Mt[jt][v] = j <= i ? Mt[jt][v] * fast_exp2(si - lds.S[j]) * lds.dt[j] : 0.0f;
                 }
             }
         }
+        // Y^T = X^T M^T + exp(S_i) H C^T: blocks pt (rows p = 16 pt + 4 g + v, column i)
+        f32x4 Yd[4], Yo[4];
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt) {
+            Yd[pt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            Yo[pt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        }
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+            if (2 * s2 <= w) {
+                // K = 32 tokens j: j = 32 s2 + 4 g + e (e < 4) and 32 s2 + 16 + 4 g + (e - 4)
+                bf16x8 mb;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    mb[e] = static_cast<__bf16>(Mt[2 * s2][e]);
+                    mb[e + 4] = static_cast<__bf16>(Mt[2 * s2 + 1][e]);
+                }
+#pragma unroll
+                for (int pt = 0; pt < 4; ++pt)
+                    Yd[pt] = mfma16(lds4x2(&lds.Xt[16 * pt + c][32 * s2 + 4 * g],
+                                           &lds.Xt[16 * pt + c][32 * s2 + 16 + 4 * g]),
+                                    mb, Yd[pt]);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < N; k += 32) {
+            const bf16x8 cb = lds8(&lds.C[i][k + 8 * g]);
+#pragma unroll
+            for (int pt = 0; pt < 4; ++pt)
+                Yo[pt] = mfma16(lds8(&lds.H[16 * pt + c][k + 8 * g]), cb, Yo[pt]);
+        }
+        if (i < cnt) {
+            const float eo = fast_exp2(si);
+            const int64_t row = (bb * L + t0 + i) * dim + hd * kP;
+#pragma unroll
+            for (int pt = 0; pt < 4; ++pt) {
+                const int p0 = 16 * pt + 4 * g;
+                float out[4];
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    out[v] = fmaf(eo, Yo[pt][v], Yd[pt][v]);
+                    if constexpr (HAS_D)
+                        out[v] = fmaf(a.D[hd * kP + p0 + v], static_cast<float>(lds.Xt[p0 + v][i]), out[v]);
+                }
+                if constexpr (HAS_Z) {
+                    const uint2 zr = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.z) + row + p0);
+                    out[0] *= silu(__uint_as_float(zr.x << 16));
+                    out[1] *= silu(__uint_as_float(zr.x & 0xffff0000u));
+                    out[2] *= silu(__uint_as_float(zr.y << 16));
+                    out[3] *= silu(__uint_as_float(zr.y & 0xffff0000u));
+                }
+                uint2 o;
+                o.x = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(out[0]))) |
+                      (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(out[1]))) << 16);
+                o.y = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(out[2]))) |
+                      (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(out[3]))) << 16);
+                *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.y) + row + p0) = o;
+            }
+        }
 
-        // (4) the state: H <- exp(S_last) H + (X w)^T B
-        {
-            const float decay = fast_exp2(s_last);
+        // (4) the state: H^T <- exp(S_last) H^T + (B w)^T X, w applied as the
+        // operand is read
+        const float decay = fast_exp2(s_last);
 #pragma unroll
-            for (int t = 0; t < NT; ++t)
+        for (int nt = 0; nt < NTN; ++nt)
 #pragma unroll
-                for (int v = 0; v < 16; ++v) H[t][v] *= decay;
+            for (int pt = 0; pt < 4; ++pt)
 #pragma unroll
-            for (int k = 0; k < kQ; k += 16) {
-                const int kk = k + 8 * (lane >> 5);
-                const bf16x8 xa = load8_col(&lds.Xw[kk][p0 + col], SsdLds<N>::kRowQ);
+                for (int v = 0; v < 4; ++v) H[nt][pt][v] *= decay;
 #pragma unroll
-                for (int t = 0; t < NT; ++t)
-                    H[t] = mfma(xa, load8_col(&lds.B[kk][n0 + 32 * t + col], SsdLds<N>::kRowN), H[t]);
+        for (int k = 0; k < kQ; k += 32) {
+            float wk[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) wk[e] = lds.w[k + 8 * g + e];
+#pragma unroll
+            for (int nt = 0; nt < NTN; ++nt) {
+                bf16x8 bw = lds8(&lds.Bt[nw0 + 16 * nt + c][k + 8 * g]);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) bw[e] = static_cast<__bf16>(static_cast<float>(bw[e]) * wk[e]);
+#pragma unroll
+                for (int pt = 0; pt < 4; ++pt)
+                    H[nt][pt] = mfma16(bw, lds8(&lds.Xt[16 * pt + c][k + 8 * g]), H[nt][pt]);
             }
         }
         __syncthreads();
@@ -231,12 +355,14 @@ __global__ __launch_bounds__(kSsdThreads) void ssd_fwd_kernel(SsdArgs a) {
 
     if (a.hL != nullptr) {
 #pragma unroll
-        for (int t = 0; t < NT; ++t)
+        for (int nt = 0; nt < NTN; ++nt)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int p = p0 + acc_row(v, lane), n = n0 + 32 * t + col;
-                a.hL[((b * a.nheads + hd) * kP + p) * N + n] = H[t][v];
-            }
+            for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int n = nw0 + 16 * nt + 4 * g + v, p = 16 * pt + c;
+                    a.hL[((bb * a.nheads + hd) * kP + p) * N + n] = H[nt][pt][v];
+                }
     }
 }
 
