@@ -199,7 +199,7 @@ int ssm_state_update(int64_t batch, int64_t dim, int dstate, int dtype, float* h
  *                                                 options carry no delta_bias
  * workspace    at least ssm_scan_bwd_workspace_size bytes
  *
- * The intermediate states are recomputed from checkpoints every 32 tokens
+ * The intermediate states are recomputed from checkpoints every 8 tokens
  * that the call itself computes into the workspace. Sums over channels and
  * rows are taken in a fixed order, so results are reproducible bit for bit.
  * seqlen == 0 writes zero dA, dD, ddelta_bias and dh0 = dhL. Outputs must

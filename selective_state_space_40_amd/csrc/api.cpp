@@ -284,13 +284,6 @@ int ssm_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int dstate, int dty
         if (p != nullptr && !aligned16(p)) return MAMBA_ERR_MISALIGNED;
     const size_t need = mamba::scan_bwd_workspace_bytes(batch, seqlen, dim, dstate);
     if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return MAMBA_ERR_WORKSPACE;
-    int split = 1;
-    for (int sp = kPreferredSplit; sp > 1; sp /= 2)
-        if (mamba::split_supported(dstate, sp)) {
-            split = sp;
-            break;
-        }
-
     mamba::BwdArgs a;
     a.fwd.batch = batch;
     a.fwd.seqlen = seqlen;
@@ -320,8 +313,7 @@ int ssm_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int dstate, int dty
     a.dz = dz;
     a.dh0 = dh0;
     a.ddelta_bias = ddelta_bias;
-    return mamba::launch_scan_bwd(a, split, workspace, stream) == hipSuccess ? MAMBA_OK
-                                                                             : MAMBA_ERR_HIP;
+    return mamba::launch_scan_bwd(a, workspace, stream) == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP;
 }
 
 int ssd_fwd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int dstate,

@@ -95,7 +95,6 @@ struct ConvArgs {
 
 // Backward pass of the scan. The forward inputs come in `fwd` (its y and hL
 // are not used); gradients of the loss sum(dy * y) + sum(dhL * hL).
-constexpr int kBwdChunk = 32;  // tokens between the backward pass's checkpoints
 
 struct BwdArgs {
     ScanArgs fwd;
@@ -115,9 +114,8 @@ struct BwdArgs {
 // Scratch bytes of the backward pass for this shape.
 size_t scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int dstate);
 
-// Queue the backward pass; `fwd_split` is the state split of the forward
-// summary pass that computes the checkpoints. Arguments are validated.
-hipError_t launch_scan_bwd(const BwdArgs& a, int fwd_split, void* workspace, hipStream_t stream);
+// Queue the backward pass. Arguments are validated.
+hipError_t launch_scan_bwd(const BwdArgs& a, void* workspace, hipStream_t stream);
 
 // Mamba-2 dual form: heads of 64 channels sharing one decay and step.
 struct SsdArgs {
@@ -153,7 +151,7 @@ hipError_t launch_scan(const ScanArgs& a, const ScanPlan& plan, void* workspace,
 // The chunked scan for one (I/O dtype, delta softplus) pair; each pair is
 // compiled in its own translation unit (scan_variant.hip). With states_only
 // it queues only the summary and carry passes, which leave the state
-// entering every chunk in the workspace (the backward pass's checkpoints).
+// entering every chunk in the workspace.
 template <int IO, bool SP>
 hipError_t launch_scan_variant(const ScanArgs& a, const ScanPlan& plan, void* workspace,
                                hipStream_t stream, bool states_only);

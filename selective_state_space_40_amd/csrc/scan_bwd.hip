@@ -13,15 +13,14 @@
 //     dz_t   = dy_t p_t silu'(z_t), p_t = C_t.h_t + D x_t
 //     dh0    = Abar_0 lam_0;  with dt = softplus(v): d delta = d dt sigmoid(v).
 //
-// Work plan. (1) The forward summary and carry passes of the chunked scan,
-// run with chunks of kBwdChunk = 32 tokens, leave the state entering every
-// chunk in the workspace: the checkpoints. (2) One workgroup per (batch row,
-// 64-channel group) walks the chunks from last to first, carrying lam in
-// registers. Its ceil(N/4) waves split the states, 4 per wave (padded with
-// inert states: A = B = C = 0). In a chunk it first runs forward over the 4
-// tiles of 8 tokens, keeping each tile's entering state in LDS, then takes
-// the tiles in reverse: it recomputes the tile's 8 states per lane into
-// registers from the kept entry and walks the tile backwards. Sums over
+// Work plan. One workgroup per (batch row, 64-channel group); its
+// ceil(N/4) waves split the states, 4 per wave (padded with inert states:
+// A = B = C = 0). (1) It runs forward over the whole sequence in tiles of 8
+// tokens and writes the state entering every tile to the workspace: the
+// checkpoints, 4 B per state and tile. (2) It takes the tiles from last to
+// first, carrying lam in registers: it reads the tile's checkpoint,
+// recomputes the tile's 8 states per lane into registers and walks the tile
+// backwards. Sums over
 // states (dx, d dt, p) go through LDS to the wave that finishes the token;
 // sums over channels (dB, dC) are reduced inside the wave by a butterfly of
 // lane exchanges that leaves one finished (token, state) sum in each lane,
@@ -38,7 +37,6 @@ namespace mamba {
 namespace {
 
 constexpr int kBT = 8;                         // tokens per tile
-constexpr int kTilesPerChunk = kBwdChunk / kBT;
 constexpr int kNpw = 4;                        // states per wave
 constexpr int kVals = 2 * kBT * kNpw;          // dB and dC terms per lane per tile
 static_assert(kVals == kWave, "the butterfly leaves exactly one sum per lane");
@@ -48,7 +46,6 @@ struct BwdLds {
     float2 dtx[kBT][kWave];                    // (delta as used, x) per token and channel
     float g[kBT][kWave];                       // dy * silu(z)
     float bc[2][kBT][kNpw * S];                // B and C rows of the tile, padded states 0
-    float tent[kTilesPerChunk][kNpw * S][kWave];  // state entering each tile of the chunk
     float red[3][S][kBT][kWave];               // per-wave partial sums over states
 };
 
@@ -69,28 +66,63 @@ __device__ __forceinline__ float sigmoid_f32(float v) {
     return fast_rcp(1.0f + fast_exp2(-v * kLog2e));
 }
 
-// Stage tile [t0, t0 + cnt): wave w converts the tokens j = w, w+S, ... of
-// the tile (delta activated once per (channel, token)); all threads stage
-// the tile's B and C rows.
-template <int S, int IO, bool SP, bool HAS_Z, bool WANT_G>
-__device__ __forceinline__ void stage_tile(const BwdArgs& a, const Place& pl, BwdLds<S>& lds,
-                                           int64_t t0, int cnt, Own (&own)[(kBT + S - 1) / S]) {
-    constexpr int OW = (kBT + S - 1) / S;
+// Raw inputs of one tile as this thread stages them: the tokens j = w,
+// w+S, ... of the tile for its lane's channel, and one element of the
+// tile's B and C rows (2 * kBT * 4S elements over 64S threads). Loaded a
+// tile ahead so the loads are in flight while the previous tile computes.
+template <int S>
+struct TileRaw {
+    static constexpr int OW = (kBT + S - 1) / S;
+    uint32_t x[OW], dl[OW], dy[OW], z[OW];
+    uint32_t bc;
+};
+
+template <int S, int IO, bool HAS_Z, bool WANT_G>
+__device__ __forceinline__ void fetch_tile(const BwdArgs& a, const Place& pl, int64_t t0, int cnt,
+                                           TileRaw<S>& r) {
     const ScanArgs& f = a.fwd;
-    const int lane = threadIdx.x & (kWave - 1);
 #pragma unroll
-    for (int jj = 0; jj < OW; ++jj) {
+    for (int jj = 0; jj < TileRaw<S>::OW; ++jj) {
         const int j = jj * S + pl.w;
         if (j < cnt) {
             const int64_t idx = (pl.b * f.seqlen + t0 + j) * f.dim + pl.d;
-            float xf = raw_to_f32<IO>(load_raw<IO>(f.x, idx));
-            const float v = raw_to_f32<IO>(load_raw<IO>(f.delta, idx)) + pl.dbias;
+            r.x[jj] = load_raw<IO>(f.x, idx);
+            r.dl[jj] = load_raw<IO>(f.delta, idx);
+            if constexpr (WANT_G) {
+                r.dy[jj] = load_raw<IO>(a.dy, idx);
+                r.z[jj] = HAS_Z ? load_raw<IO>(f.z, idx) : 0u;
+            }
+        }
+    }
+    constexpr int NP = kNpw * S;
+    const int e = threadIdx.x;  // exactly one B or C element per thread
+    const int which = e / (kBT * NP);
+    const int rr = e - which * kBT * NP;
+    const int j = rr / NP;
+    const int n = rr - j * NP;
+    r.bc = 0u;
+    if (j < cnt && n < f.dstate)
+        r.bc = load_raw<IO>(which ? f.C : f.B, (pl.b * f.seqlen + t0 + j) * f.dstate + n);
+}
+
+// Stage a fetched tile: wave w converts its tokens j = w, w+S, ... (delta
+// activated once per (channel, token)) and every thread its B or C element.
+template <int S, int IO, bool SP, bool HAS_Z, bool WANT_G>
+__device__ __forceinline__ void put_tile(const TileRaw<S>& r, const Place& pl, BwdLds<S>& lds,
+                                         int cnt, Own (&own)[(kBT + S - 1) / S]) {
+    const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+    for (int jj = 0; jj < TileRaw<S>::OW; ++jj) {
+        const int j = jj * S + pl.w;
+        if (j < cnt) {
+            float xf = raw_to_f32<IO>(r.x[jj]);
+            const float v = raw_to_f32<IO>(r.dl[jj]) + pl.dbias;
             const float dt = SP ? softplus_f32(v) : v;
             if (!pl.valid) xf = 0.0f;  // a clamped lane contributes nothing
             lds.dtx[j][lane] = make_float2(dt, xf);
             if constexpr (WANT_G) {
-                const float dyf = raw_to_f32<IO>(load_raw<IO>(a.dy, idx));
-                const float zf = HAS_Z ? raw_to_f32<IO>(load_raw<IO>(f.z, idx)) : 0.0f;
+                const float dyf = raw_to_f32<IO>(r.dy[jj]);
+                const float zf = HAS_Z ? raw_to_f32<IO>(r.z[jj]) : 0.0f;
                 float gg = HAS_Z ? dyf * silu(zf) : dyf;
                 if (!pl.valid) gg = 0.0f;
                 lds.g[j][lane] = gg;
@@ -99,17 +131,10 @@ __device__ __forceinline__ void stage_tile(const BwdArgs& a, const Place& pl, Bw
         }
     }
     constexpr int NP = kNpw * S;
-    const int N = f.dstate;
-    for (int e = threadIdx.x; e < 2 * kBT * NP; e += kWave * S) {
-        const int which = e / (kBT * NP);
-        const int r = e - which * kBT * NP;
-        const int j = r / NP;
-        const int n = r - j * NP;
-        float val = 0.0f;
-        if (j < cnt && n < N)
-            val = raw_to_f32<IO>(load_raw<IO>(which ? f.C : f.B, (pl.b * f.seqlen + t0 + j) * N + n));
-        lds.bc[which][j][n] = val;
-    }
+    const int e = threadIdx.x;
+    const int which = e / (kBT * NP);
+    const int rr = e - which * kBT * NP;
+    lds.bc[which][rr / NP][rr % NP] = raw_to_f32<IO>(r.bc);
 }
 
 // Sum of each of the 64 values over the 64 lanes. At the step of distance
@@ -138,8 +163,9 @@ __device__ __forceinline__ int reverse6(int l) {
 }
 
 template <int S, int IO, bool SP, bool HAS_D, bool HAS_Z>
-__global__ __launch_bounds__(kWave * S) void scan_bwd_kernel(BwdArgs a, int64_t ngroups,
-                                                             int64_t nchunks, const float* ckpt,
+__global__ __launch_bounds__(kWave * S) __attribute__((amdgpu_waves_per_eu(S == 4 ? 3 : 1)))
+void scan_bwd_kernel(BwdArgs a, int64_t ngroups,
+                                                             float* tent,
                                                              float* part_bc, float* part_a,
                                                              float* part_d, float* part_bias) {
     constexpr int OW = (kBT + S - 1) / S;
@@ -175,32 +201,30 @@ __global__ __launch_bounds__(kWave * S) void scan_bwd_kernel(BwdArgs a, int64_t 
     float dD_acc = 0.0f, dbias_acc = 0.0f;
     Own own[OW];
 
-    for (int64_t k = nchunks - 1; k >= 0; --k) {
-        const int64_t cs = k * kBwdChunk;
-        const int64_t ce = min(L, cs + kBwdChunk);
-        const int ntile = static_cast<int>((ce - cs + kBT - 1) / kBT);
-
-        // (a) forward over the chunk from its checkpoint, keeping tile entries
+    const int64_t ntiles = (L + kBT - 1) / kBT;
+    // (1) forward over the whole sequence, keeping the state entering every
+    // tile in the workspace (only real lanes and states write)
+    {
         float h[kNpw];
 #pragma unroll
-        for (int q = 0; q < kNpw; ++q) {
-            const int n = pl.n0 + q;
-            float v = 0.0f;
-            if (sv[q]) {
-                if (nchunks == 1)
-                    v = f.h0 != nullptr ? f.h0[(pl.b * f.dim + pl.d) * N + n] : 0.0f;
-                else
-                    v = ckpt[((k * f.batch + pl.b) * f.dim + pl.d) * N + n];
-            }
-            h[q] = v;
-        }
-        for (int i = 0; i < ntile; ++i) {
-            const int64_t t0 = cs + i * kBT;
-            const int cnt = static_cast<int>(min<int64_t>(kBT, ce - t0));
-            stage_tile<S, IO, SP, HAS_Z, false>(a, pl, lds, t0, cnt, own);
-            __syncthreads();
+        for (int q = 0; q < kNpw; ++q)
+            h[q] = (sv[q] && f.h0 != nullptr) ? f.h0[(pl.b * f.dim + pl.d) * N + pl.n0 + q] : 0.0f;
+        TileRaw<S> raw;
+        fetch_tile<S, IO, HAS_Z, false>(a, pl, 0, static_cast<int>(min<int64_t>(kBT, L)), raw);
+        for (int64_t i = 0; i < ntiles; ++i) {
+            const int64_t t0 = i * kBT;
+            const int cnt = static_cast<int>(min<int64_t>(kBT, L - t0));
+            if (pl.valid) {
+                float* row = tent + ((i * f.batch + pl.b) * f.dim + pl.d) * N + pl.n0;
 #pragma unroll
-            for (int q = 0; q < kNpw; ++q) lds.tent[i][pl.n0 + q][lane] = h[q];
+                for (int q = 0; q < kNpw; ++q)
+                    if (sv[q]) row[q] = h[q];
+            }
+            put_tile<S, IO, SP, HAS_Z, false>(raw, pl, lds, cnt, own);
+            __syncthreads();
+            if (i + 1 < ntiles)
+                fetch_tile<S, IO, HAS_Z, false>(a, pl, t0 + kBT,
+                                                static_cast<int>(min<int64_t>(kBT, L - t0 - kBT)), raw);
 #pragma unroll
             for (int j = 0; j < kBT; ++j) {
                 if (j < cnt) {
@@ -213,17 +237,31 @@ __global__ __launch_bounds__(kWave * S) void scan_bwd_kernel(BwdArgs a, int64_t 
             }
             __syncthreads();
         }
+    }
 
-        // (b) the tiles in reverse
-        for (int i = ntile - 1; i >= 0; --i) {
-            const int64_t t0 = cs + i * kBT;
-            const int cnt = static_cast<int>(min<int64_t>(kBT, ce - t0));
-            stage_tile<S, IO, SP, HAS_Z, true>(a, pl, lds, t0, cnt, own);
-            __syncthreads();
-
+    // (2) the tiles in reverse
+    {
+        float h[kNpw];
+        TileRaw<S> raw;
+        {
+            const int64_t tl = (ntiles - 1) * kBT;
+            fetch_tile<S, IO, HAS_Z, true>(a, pl, tl, static_cast<int>(L - tl), raw);
+        }
+        for (int64_t i = ntiles - 1; i >= 0; --i) {
+            const int64_t t0 = i * kBT;
+            const int cnt = static_cast<int>(min<int64_t>(kBT, L - t0));
+            // the tile's entering state; a lane past the last channel starts
+            // from zero (its x and g are zero too, so it contributes nothing)
             float he[kNpw], hs[kBT][kNpw];
+            {
+                const float* row = tent + ((i * f.batch + pl.b) * f.dim + pl.d) * N + pl.n0;
 #pragma unroll
-            for (int q = 0; q < kNpw; ++q) he[q] = lds.tent[i][pl.n0 + q][lane];
+                for (int q = 0; q < kNpw; ++q) he[q] = (pl.valid && sv[q]) ? row[q] : 0.0f;
+            }
+            put_tile<S, IO, SP, HAS_Z, true>(raw, pl, lds, cnt, own);
+            __syncthreads();
+            if (i > 0) fetch_tile<S, IO, HAS_Z, true>(a, pl, t0 - kBT, kBT, raw);
+
 #pragma unroll
             for (int q = 0; q < kNpw; ++q) h[q] = he[q];
 #pragma unroll
@@ -408,20 +446,20 @@ __global__ __launch_bounds__(256) void bwd_degenerate_kernel(int64_t cols, int64
 }
 
 struct BwdLayout {
-    int64_t nchunks, ngroups;
-    size_t ckpt, part_bc, part_a, part_d, part_bias, total;  // float offsets / count
+    int64_t ntiles, ngroups;
+    size_t tent, part_bc, part_a, part_d, part_bias, total;  // float offsets / count
 };
 
 inline size_t round64(size_t v) { return (v + 63) / 64 * 64; }
 
 BwdLayout bwd_layout(int64_t batch, int64_t seqlen, int64_t dim, int dstate) {
     BwdLayout l;
-    l.nchunks = (seqlen + kBwdChunk - 1) / kBwdChunk;
+    l.ntiles = (seqlen + kBT - 1) / kBT;
     l.ngroups = (dim + kWave - 1) / kWave;
     const size_t states = static_cast<size_t>(batch) * dim * dstate;
     size_t off = 0;
-    l.ckpt = off;
-    off += round64(l.nchunks > 1 ? 3 * static_cast<size_t>(l.nchunks) * states : 0);
+    l.tent = off;
+    off += round64(static_cast<size_t>(l.ntiles) * states);
     l.part_bc = off;
     off += round64(2 * static_cast<size_t>(l.ngroups) * batch * seqlen * dstate);
     l.part_a = off;
@@ -439,8 +477,8 @@ hipError_t launch_bwd_main(const BwdArgs& a, const BwdLayout& l, float* ws, hipS
     const int64_t blocks = a.fwd.batch * l.ngroups;
     const bool has_d = a.fwd.D != nullptr, has_z = a.fwd.z != nullptr;
     auto go = [&](auto kernel) {
-        hipLaunchKernelGGL(kernel, dim3(blocks), dim3(kWave * S), 0, s, a, l.ngroups, l.nchunks,
-                           ws + l.ckpt, ws + l.part_bc, ws + l.part_a, ws + l.part_d,
+        hipLaunchKernelGGL(kernel, dim3(blocks), dim3(kWave * S), 0, s, a, l.ngroups,
+                           ws + l.tent, ws + l.part_bc, ws + l.part_a, ws + l.part_d,
                            ws + l.part_bias);
     };
     if (has_d && has_z) go(scan_bwd_kernel<S, IO, SP, true, true>);
@@ -451,21 +489,9 @@ hipError_t launch_bwd_main(const BwdArgs& a, const BwdLayout& l, float* ws, hipS
 }
 
 template <int IO, bool SP>
-hipError_t launch_bwd_io(const BwdArgs& a, int fwd_split, float* ws, hipStream_t s) {
+hipError_t launch_bwd_io(const BwdArgs& a, float* ws, hipStream_t s) {
     const ScanArgs& f = a.fwd;
     const BwdLayout l = bwd_layout(f.batch, f.seqlen, f.dim, f.dstate);
-    if (l.nchunks > 1) {
-        ScanPlan p;
-        p.chunk_len = kBwdChunk;
-        p.nchunks = l.nchunks;
-        p.state_split = fwd_split;
-        p.workspace_bytes = 0;
-        // the summary pass writes no output; y points at a real buffer all the same
-        ScanArgs fa = f;
-        fa.y = a.dx;
-        const hipError_t e = launch_scan_variant<IO, SP>(fa, p, ws + l.ckpt, s, true);
-        if (e != hipSuccess) return e;
-    }
     hipError_t e;
     switch ((f.dstate + kNpw - 1) / kNpw) {
         case 1: e = launch_bwd_main<1, IO, SP>(a, l, ws, s); break;
@@ -491,7 +517,7 @@ size_t scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int 
     return bwd_layout(batch, seqlen, dim, dstate).total * sizeof(float);
 }
 
-hipError_t launch_scan_bwd(const BwdArgs& a, int fwd_split, void* workspace, hipStream_t stream) {
+hipError_t launch_scan_bwd(const BwdArgs& a, void* workspace, hipStream_t stream) {
     const ScanArgs& f = a.fwd;
     if (f.dim == 0) return hipSuccess;
     if (f.batch == 0 || f.seqlen == 0) {
@@ -505,10 +531,10 @@ hipError_t launch_scan_bwd(const BwdArgs& a, int fwd_split, void* workspace, hip
     float* ws = static_cast<float*>(workspace);
     const bool sp = f.delta_softplus != 0;
     if (f.io == kIoF32)
-        return sp ? launch_bwd_io<kIoF32, true>(a, fwd_split, ws, stream)
-                  : launch_bwd_io<kIoF32, false>(a, fwd_split, ws, stream);
-    return sp ? launch_bwd_io<kIoBF16, true>(a, fwd_split, ws, stream)
-              : launch_bwd_io<kIoBF16, false>(a, fwd_split, ws, stream);
+        return sp ? launch_bwd_io<kIoF32, true>(a, ws, stream)
+                  : launch_bwd_io<kIoF32, false>(a, ws, stream);
+    return sp ? launch_bwd_io<kIoBF16, true>(a, ws, stream)
+              : launch_bwd_io<kIoBF16, false>(a, ws, stream);
 }
 
 }  // namespace mamba
