@@ -242,8 +242,8 @@ int ssm_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int dstate, int dty
  * h0, hL    (batch, nheads, 64, dstate) fp32     optional; hL may alias h0
  *
  * Requirements: headdim == MAMBA_SSD_HEADDIM, dstate 64 or 128, dtype
- * MAMBA_DTYPE_BF16 (the products run in bf16 with fp32 accumulation);
- * anything else is MAMBA_ERR_UNSUPPORTED. No workspace. Errors and
+ * MAMBA_DTYPE_BF16 (the products run in bf16 with fp32 accumulation),
+ * nheads <= 65536; anything else is MAMBA_ERR_UNSUPPORTED. No workspace. Errors and
  * ownership as for ssm_scan_fwd.
  */
 int ssd_fwd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int dstate,

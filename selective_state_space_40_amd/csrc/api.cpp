@@ -325,7 +325,7 @@ int ssd_fwd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int 
     if (headdim != MAMBA_SSD_HEADDIM || (dstate != 64 && dstate != 128) ||
         dtype != MAMBA_DTYPE_BF16)
         return MAMBA_ERR_UNSUPPORTED;
-    if (nheads > (int64_t(1) << 24)) return MAMBA_ERR_UNSUPPORTED;
+    if (nheads > (int64_t(1) << 16)) return MAMBA_ERR_UNSUPPORTED;
     int st = check_shape(batch, seqlen, nheads * headdim, 1, dtype);
     if (st != MAMBA_OK) return st;
     if (batch * nheads >= (int64_t(1) << 31)) return MAMBA_ERR_UNSUPPORTED;

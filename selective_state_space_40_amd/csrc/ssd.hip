@@ -22,11 +22,14 @@
 // column i and rows j = 4(lane / 16) + 0..3, and two such blocks are exactly
 // the K = 32 operand of the next product up to a fixed permutation of K, so
 // Y^T = X^T M^T takes M^T straight from the accumulators (X^T is read with
-// the same permutation) and M never goes through LDS. The chunk's x, B and C
-// are staged once in LDS (rows padded by 16 bytes), B also transposed and
-// scaled by w_j for the state update, and the next chunk's inputs are loaded
-// into registers while this one is computed. bf16 I/O, head size 64,
-// N = 64 or 128, Q = 64.
+// the same permutation) and M never goes through LDS. C is read only by the
+// wave that owns the token, so each lane keeps its token's C row in
+// registers in operand layout. The chunk's x and B are staged once in LDS
+// (rows padded by 16 bytes), B also transposed for the state update, and the
+// next chunk's inputs (x, B, C, z and the steps) are loaded into registers
+// while this one is computed; nothing in the chunk waits on global memory
+// until the next chunk is staged. bf16 I/O, head size 64, N = 64 or 128,
+// Q = 64.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -47,15 +50,24 @@ template <int N>
 struct SsdLds {
     static constexpr int kRowN = N + 8;   // padded row of N bf16
     static constexpr int kRowQ = kQ + 8;  // padded row of 64 bf16
-    __bf16 C[kQ][kRowN];     // C rows of the chunk (i, n)
     __bf16 B[kQ][kRowN];     // B rows (j, n)
-    __bf16 Bt[N][kRowQ];     // B transposed (n, j)
-    __bf16 Xt[kP][kRowQ];    // x transposed (p, j)
+    __bf16 Bt[N][kRowQ];     // B transposed (n, j), 8-value runs of j swizzled (tcol)
+    __bf16 Xt[kP][kRowQ];    // x transposed (p, j), swizzled the same way
     __bf16 H[kP][kRowN];     // the state entering the chunk (p, n)
-    float dt[kQ];            // the step as used
+    alignas(16) float dt[kQ];  // the step as used
     float S[kQ];             // log2 of the decay from chunk start through token j
     float w[kQ];             // exp(S_last - S_j) dt_j: weight of token j in the state update
+    alignas(16) float D[kP];   // the skip weights of the head's channels
+    float Y[4][16][kP + 4];    // per wave: its 16 tokens' outputs before the gate (i, p)
 };
+
+// Column of element (row, col) of a transposed tile: the 16-byte run of 8
+// columns is XOR-ed with bits 3..5 of the row, so the 8 rows that the staging
+// lanes write together land in 8 different bank groups. A run of 8 (or of 4
+// starting at a multiple of 4) stays contiguous.
+__device__ __forceinline__ int tcol(int row, int col) {
+    return ((((col >> 3) ^ (row >> 3)) & 7) << 3) | (col & 7);
+}
 
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -81,54 +93,97 @@ __device__ __forceinline__ bf16x8 lds4x2(const __bf16* p, const __bf16* q) {
 
 // The next chunk's inputs, held in registers between chunks. Threads
 // 0 .. 63 each hold an 8 x 8 block (8 tokens, 8 channels) of x, the next
-// N threads (N / 8 blocks per 8 tokens) an 8 x 8 block of B; all threads
-// hold a share of C.
+// N threads (N / 8 blocks per 8 tokens) an 8 x 8 block of B. Every lane
+// holds the C row of its own token i as the products read it (8 values of n
+// at 8 g + 32 k for k < N / 32), and the gate z and input x of 8 channels of
+// two of its wave's tokens in row order (see the output step); lanes of wave
+// 0 hold the raw step of token `lane`. Values stay raw until the chunk
+// is staged, so issuing the loads never waits for them.
 template <int N>
 struct Prefetch {
     static constexpr int kXBlocks = (kQ / 8) * (kP / 8);
     static constexpr int kBBlocks = (kQ / 8) * (N / 8);
-    static constexpr int kC = kQ * N / 8 / kSsdThreads;   // uint4 of C per thread
-    uint4 blk[8], c[kC];
-    float dt;
+    static constexpr int kCk = N / 32;   // K steps of 32 over n
+    uint4 blk[8], c[kCk];
+    uint4 z[2], xd[2];
+    uint32_t dt;
 };
 
-template <int N>
+// Buffer resource over `bytes` bytes from p (raw addressing, gfx9 word 3):
+// a load whose offset lies at or past the end returns zeros, so the tokens
+// of a ragged last chunk need no branch.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t chunk_rsrc(const void* p, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, bytes, 0x00020000);
+}
+
+__device__ __forceinline__ uint4 ld128(__amdgpu_buffer_rsrc_t r, int off) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+
+// Issues the loads of chunk [t0, t0 + cnt) of row bb, head hd. Every
+// resource starts at the chunk's first token and ends after its last valid
+// one; lane offsets are the same for every chunk. Offsets fit 31 bits since
+// the library caps nheads at 2^16 (64 rows of 2^22 channels).
+template <int N, bool HAS_D, bool HAS_Z>
 __device__ __forceinline__ void fetch_chunk(const SsdArgs& a, int64_t bb, int64_t hd, int64_t t0,
                                             int cnt, Prefetch<N>& f) {
     const int tid = threadIdx.x;
-    const int64_t L = a.seqlen, dim = a.nheads * kP;
-    const uint16_t* src = nullptr;
-    int64_t stride = 0;
-    int jb = 0;
-    if (tid < Prefetch<N>::kXBlocks) {
-        jb = tid / (kP / 8);
-        src = static_cast<const uint16_t*>(a.x) + (bb * L + t0) * dim + hd * kP + 8 * (tid % (kP / 8));
-        stride = dim;
-    } else if (tid < Prefetch<N>::kXBlocks + Prefetch<N>::kBBlocks) {
-        const int e = tid - Prefetch<N>::kXBlocks;
-        jb = e / (N / 8);
-        src = static_cast<const uint16_t*>(a.B) + (bb * L + t0) * N + 8 * (e % (N / 8));
-        stride = N;
-    }
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-        const int j = 8 * jb + r;
-        f.blk[r] = (src != nullptr && j < cnt)
-                       ? *reinterpret_cast<const uint4*>(src + static_cast<int64_t>(j) * stride)
-                       : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int r = 0; r < Prefetch<N>::kC; ++r) {
-        const int e = tid + r * kSsdThreads;
-        const int j = e / (N / 8), q = e % (N / 8);
-        f.c[r] = j < cnt ? *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.C) +
-                                                           (bb * L + t0 + j) * N + 8 * q)
-                         : make_uint4(0, 0, 0, 0);
-    }
     const int lane = tid & (kWave - 1);
-    f.dt = (tid < kWave && lane < cnt)
-               ? raw_to_f32<kIoBF16>(load_raw<kIoBF16>(a.dt, (bb * L + t0 + lane) * a.nheads + hd))
-               : 0.0f;
+    const int dim = static_cast<int>(a.nheads) * kP;
+    const int64_t row0 = bb * a.seqlen + t0;
+    const int span = ((cnt - 1) * dim + kP) * 2;   // bytes of a head's channels over the chunk
+    const __amdgpu_buffer_rsrc_t rx =
+        chunk_rsrc(static_cast<const uint16_t*>(a.x) + row0 * dim + hd * kP, span);
+    if (tid < Prefetch<N>::kXBlocks) {
+        const int jb = tid / (kP / 8), col = 8 * (tid % (kP / 8));
+#pragma unroll
+        for (int r = 0; r < 8; ++r) f.blk[r] = ld128(rx, ((8 * jb + r) * dim + col) * 2);
+    } else if (tid < Prefetch<N>::kXBlocks + Prefetch<N>::kBBlocks) {
+        const __amdgpu_buffer_rsrc_t rb = chunk_rsrc(static_cast<const uint16_t*>(a.B) + row0 * N, cnt * N * 2);
+        const int e = tid - Prefetch<N>::kXBlocks;
+        const int jb = e / (N / 8), col = 8 * (e % (N / 8));
+#pragma unroll
+        for (int r = 0; r < 8; ++r) f.blk[r] = ld128(rb, ((8 * jb + r) * N + col) * 2);
+    }
+    const int i = 16 * (tid / kWave) + (lane & 15), g = lane >> 4;
+    const __amdgpu_buffer_rsrc_t rc = chunk_rsrc(static_cast<const uint16_t*>(a.C) + row0 * N, cnt * N * 2);
+#pragma unroll
+    for (int k = 0; k < Prefetch<N>::kCk; ++k) f.c[k] = ld128(rc, (i * N + 8 * g + 32 * k) * 2);
+    // rows 16 w + (lane / 8) + 8 h, channels 8 (lane % 8) .. + 8
+    const int orow = 16 * (tid / kWave) + (lane >> 3), ocol = 8 * (lane & 7);
+    if constexpr (HAS_Z) {
+        const __amdgpu_buffer_rsrc_t rz =
+            chunk_rsrc(static_cast<const uint16_t*>(a.z) + row0 * dim + hd * kP, span);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) f.z[h] = ld128(rz, ((orow + 8 * h) * dim + ocol) * 2);
+    }
+    if constexpr (HAS_D) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) f.xd[h] = ld128(rx, ((orow + 8 * h) * dim + ocol) * 2);
+    }
+    const int nh = static_cast<int>(a.nheads);
+    const __amdgpu_buffer_rsrc_t rdt =
+        chunk_rsrc(static_cast<const uint16_t*>(a.dt) + row0 * nh + hd, ((cnt - 1) * nh + 1) * 2);
+    f.dt = static_cast<uint16_t>(__builtin_amdgcn_raw_buffer_load_b16(rdt, lane * nh * 2, 0, 0));
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave with DPP: shifts by 1, 2,
+// 4 and 8 within rows of 16 lanes, then the row totals are carried with the
+// row broadcasts of lanes 15 and 31.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_add(float x) {
+    return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROW_MASK, 0xf, false));
+}
+
+__device__ __forceinline__ float wave_prefix_sum(float v) {
+    v = dpp_add<0x111, 0xf>(v);   // row_shr:1
+    v = dpp_add<0x112, 0xf>(v);   // row_shr:2
+    v = dpp_add<0x114, 0xf>(v);   // row_shr:4
+    v = dpp_add<0x118, 0xf>(v);   // row_shr:8
+    v = dpp_add<0x142, 0xa>(v);   // row_bcast:15 into rows 1 and 3
+    v = dpp_add<0x143, 0xc>(v);   // row_bcast:31 into rows 2 and 3
+    return v;
 }
 
 // 8 x 8 bf16 transpose in registers: in[r] holds row r (8 values), out[f]
@@ -168,10 +223,12 @@ void ssd_fwd_kernel(SsdArgs a) {
     const int64_t dim = a.nheads * kP;
     const float alog2 = a.A[hd] * kLog2e;
     const float bias = a.dt_bias != nullptr ? a.dt_bias[hd] : 0.0f;
-    const int i = 16 * w + c;        // this lane's token of the chunk (as output column)
+    const int tb = w;                // this wave's block of 16 tokens
+    const int i = 16 * tb + c;       // this lane's token of the chunk (as output column)
 
     // state H^T: block (nt, pt) holds rows n = nw0 + 16 nt + 4 g + v, column p = 16 pt + c
     const int nw0 = NW * w;
+    if (tid < kP) lds.D[tid] = HAS_D ? a.D[hd * kP + tid] : 0.0f;
     f32x4 H[NTN][4];
 #pragma unroll
     for (int nt = 0; nt < NTN; ++nt)
@@ -185,48 +242,46 @@ void ssd_fwd_kernel(SsdArgs a) {
 
     const int64_t nchunks = (L + kQ - 1) / kQ;
     Prefetch<N> pf;
-    fetch_chunk<N>(a, bb, hd, 0, static_cast<int>(min<int64_t>(kQ, L)), pf);
+    fetch_chunk<N, HAS_D, HAS_Z>(a, bb, hd, 0, static_cast<int>(min<int64_t>(kQ, L)), pf);
     for (int64_t ch = 0; ch < nchunks; ++ch) {
         const int64_t t0 = ch * kQ;
         const int cnt = static_cast<int>(min<int64_t>(kQ, L - t0));
 
-        // (1) stage the chunk: x transposed, B as it is and transposed, C;
-        // the steps, their running sum and the token weights; the state
-        // entering the chunk as bf16 (p, n)
+        // (1) stage the chunk: x transposed, B as it is and transposed; the
+        // steps, their running sum and the token weights; the state entering
+        // the chunk as bf16 (p, n). C and z move to this chunk's registers.
         if (tid < Prefetch<N>::kXBlocks + Prefetch<N>::kBBlocks) {
             uint4 tr[8];
             transpose8(pf.blk, tr);
             if (tid < Prefetch<N>::kXBlocks) {
                 const int jb = tid / (kP / 8), pb = tid % (kP / 8);
 #pragma unroll
-                for (int f = 0; f < 8; ++f) *reinterpret_cast<uint4*>(&lds.Xt[8 * pb + f][8 * jb]) = tr[f];
+                for (int f = 0; f < 8; ++f)
+                    *reinterpret_cast<uint4*>(&lds.Xt[8 * pb + f][tcol(8 * pb + f, 8 * jb)]) = tr[f];
             } else {
                 const int e = tid - Prefetch<N>::kXBlocks;
                 const int jb = e / (N / 8), nb = e % (N / 8);
 #pragma unroll
                 for (int f = 0; f < 8; ++f) {
-                    *reinterpret_cast<uint4*>(&lds.Bt[8 * nb + f][8 * jb]) = tr[f];
+                    *reinterpret_cast<uint4*>(&lds.Bt[8 * nb + f][tcol(8 * nb + f, 8 * jb)]) = tr[f];
                     *reinterpret_cast<uint4*>(&lds.B[8 * jb + f][8 * nb]) = pf.blk[f];
                 }
             }
         }
+        bf16x8 cop[Prefetch<N>::kCk];
 #pragma unroll
-        for (int r = 0; r < Prefetch<N>::kC; ++r) {
-            const int e = tid + r * kSsdThreads;
-            const int j = e / (N / 8), q = e % (N / 8);
-            *reinterpret_cast<uint4*>(&lds.C[j][8 * q]) = pf.c[r];
+        for (int k = 0; k < Prefetch<N>::kCk; ++k) cop[k] = __builtin_bit_cast(bf16x8, pf.c[k]);
+        uint4 zc[2], xc[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            zc[h] = pf.z[h];
+            xc[h] = pf.xd[h];
         }
         if (w == 0) {
-            const float v = pf.dt + bias;
+            const float v = raw_to_f32<kIoBF16>(pf.dt) + bias;
             const float dtv = lane < cnt ? (SP ? softplus_f32(v) : v) : 0.0f;
-            float s = dtv;
-#pragma unroll
-            for (int k = 1; k < kWave; k *= 2) {
-                const float o = __shfl_up(s, k, kWave);
-                if (lane >= k) s += o;
-            }
-            s *= alog2;
-            const float last = __shfl(s, kWave - 1, kWave);
+            const float s = wave_prefix_sum(dtv) * alog2;
+            const float last = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s), kWave - 1));
             lds.dt[lane] = dtv;
             lds.S[lane] = s;
             lds.w[lane] = fast_exp2(last - s) * dtv;
@@ -245,7 +300,7 @@ void ssd_fwd_kernel(SsdArgs a) {
 
         // the next chunk's loads go out now and land during this chunk
         if (ch + 1 < nchunks)
-            fetch_chunk<N>(a, bb, hd, t0 + kQ, static_cast<int>(min<int64_t>(kQ, L - t0 - kQ)), pf);
+            fetch_chunk<N, HAS_D, HAS_Z>(a, bb, hd, t0 + kQ, static_cast<int>(min<int64_t>(kQ, L - t0 - kQ)), pf);
         const float s_last = lds.S[kQ - 1];
 
         // (3) M^T for this wave's tokens: blocks jt = 0 .. w of G^T = B C^T
@@ -254,15 +309,18 @@ void ssd_fwd_kernel(SsdArgs a) {
 #pragma unroll
         for (int jt = 0; jt < 4; ++jt) {
             Mt[jt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-            if (jt <= w) {
+            if (jt <= tb) {
 #pragma unroll
                 for (int k = 0; k < N; k += 32)
-                    Mt[jt] = mfma16(lds8(&lds.B[16 * jt + c][k + 8 * g]),
-                                    lds8(&lds.C[i][k + 8 * g]), Mt[jt]);
+                    Mt[jt] = mfma16(lds8(&lds.B[16 * jt + c][k + 8 * g]), cop[k / 32], Mt[jt]);
+                // token j = 16 jt + 4 g + v; above the diagonal (j > i) the
+                // factor may overflow and is discarded by the select
+                const f32x4 sj = *reinterpret_cast<const f32x4*>(&lds.S[16 * jt + 4 * g]);
+                const f32x4 dj = *reinterpret_cast<const f32x4*>(&lds.dt[16 * jt + 4 * g]);
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
-                    const int j = 16 * jt + 4 * g + v;
-                    Mt[jt][v] = j <= i ? Mt[jt][v] * fast_exp2(si - lds.S[j]) * lds.dt[j] : 0.0f;
+                    const float e = fast_exp2(si - sj[v]) * dj[v];
+                    Mt[jt][v] = (jt < tb || 4 * g + v <= c) ? Mt[jt][v] * e : 0.0f;
                 }
             }
         }
@@ -275,7 +333,7 @@ void ssd_fwd_kernel(SsdArgs a) {
         }
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
-            if (2 * s2 <= w) {
+            if (2 * s2 <= tb) {
                 // K = 32 tokens j: j = 32 s2 + 4 g + e (e < 4) and 32 s2 + 16 + 4 g + (e - 4)
                 bf16x8 mb;
 #pragma unroll
@@ -285,44 +343,72 @@ void ssd_fwd_kernel(SsdArgs a) {
                 }
 #pragma unroll
                 for (int pt = 0; pt < 4; ++pt)
-                    Yd[pt] = mfma16(lds4x2(&lds.Xt[16 * pt + c][32 * s2 + 4 * g],
-                                           &lds.Xt[16 * pt + c][32 * s2 + 16 + 4 * g]),
+                    Yd[pt] = mfma16(lds4x2(&lds.Xt[16 * pt + c][tcol(16 * pt + c, 32 * s2 + 4 * g)],
+                                           &lds.Xt[16 * pt + c][tcol(16 * pt + c, 32 * s2 + 16 + 4 * g)]),
                                     mb, Yd[pt]);
             }
         }
 #pragma unroll
         for (int k = 0; k < N; k += 32) {
-            const bf16x8 cb = lds8(&lds.C[i][k + 8 * g]);
 #pragma unroll
             for (int pt = 0; pt < 4; ++pt)
-                Yo[pt] = mfma16(lds8(&lds.H[16 * pt + c][k + 8 * g]), cb, Yo[pt]);
+                Yo[pt] = mfma16(lds8(&lds.H[16 * pt + c][k + 8 * g]), cop[k / 32], Yo[pt]);
         }
-        if (i < cnt) {
+        // (5) output: the wave's 16 x 64 block leaves the accumulators through
+        // LDS so that the gate and input are read, and y written, as whole
+        // rows (16 bytes per lane, 8 lanes per row); rows past the sequence
+        // end fall outside the chunk's buffer range and are not stored.
+        {
             const float eo = fast_exp2(si);
-            const int64_t row = (bb * L + t0 + i) * dim + hd * kP;
 #pragma unroll
             for (int pt = 0; pt < 4; ++pt) {
-                const int p0 = 16 * pt + 4 * g;
-                float out[4];
+                f32x4 o;
 #pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    out[v] = fmaf(eo, Yo[pt][v], Yd[pt][v]);
-                    if constexpr (HAS_D)
-                        out[v] = fmaf(a.D[hd * kP + p0 + v], static_cast<float>(lds.Xt[p0 + v][i]), out[v]);
+                for (int v = 0; v < 4; ++v) o[v] = fmaf(eo, Yo[pt][v], Yd[pt][v]);
+                *reinterpret_cast<f32x4*>(&lds.Y[w][c][16 * pt + 4 * g]) = o;
+            }
+            // lanes of this wave read what other lanes of it wrote
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            const int orow = lane >> 3, ocol = 8 * (lane & 7);
+            const __amdgpu_buffer_rsrc_t ry =
+                chunk_rsrc(static_cast<uint16_t*>(a.y) + (bb * L + t0) * dim + hd * kP,
+                           ((cnt - 1) * static_cast<int>(dim) + kP) * 2);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int r = orow + 8 * h;
+                const f32x4 y0 = *reinterpret_cast<const f32x4*>(&lds.Y[w][r][ocol]);
+                const f32x4 y1 = *reinterpret_cast<const f32x4*>(&lds.Y[w][r][ocol + 4]);
+                float out[8] = {y0[0], y0[1], y0[2], y0[3], y1[0], y1[1], y1[2], y1[3]};
+                if constexpr (HAS_D) {
+                    const f32x4 d0 = *reinterpret_cast<const f32x4*>(&lds.D[ocol]);
+                    const f32x4 d1 = *reinterpret_cast<const f32x4*>(&lds.D[ocol + 4]);
+                    const uint32_t xw[4] = {xc[h].x, xc[h].y, xc[h].z, xc[h].w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        out[2 * e] = fmaf(e < 2 ? d0[2 * e] : d1[2 * e - 4], __uint_as_float(xw[e] << 16), out[2 * e]);
+                        out[2 * e + 1] = fmaf(e < 2 ? d0[2 * e + 1] : d1[2 * e - 3],
+                                              __uint_as_float(xw[e] & 0xffff0000u), out[2 * e + 1]);
+                    }
                 }
                 if constexpr (HAS_Z) {
-                    const uint2 zr = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.z) + row + p0);
-                    out[0] *= silu(__uint_as_float(zr.x << 16));
-                    out[1] *= silu(__uint_as_float(zr.x & 0xffff0000u));
-                    out[2] *= silu(__uint_as_float(zr.y << 16));
-                    out[3] *= silu(__uint_as_float(zr.y & 0xffff0000u));
+                    const uint32_t zw[4] = {zc[h].x, zc[h].y, zc[h].z, zc[h].w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        out[2 * e] *= silu(__uint_as_float(zw[e] << 16));
+                        out[2 * e + 1] *= silu(__uint_as_float(zw[e] & 0xffff0000u));
+                    }
                 }
-                uint2 o;
-                o.x = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(out[0]))) |
-                      (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(out[1]))) << 16);
-                o.y = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(out[2]))) |
-                      (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(out[3]))) << 16);
-                *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.y) + row + p0) = o;
+                uint32_t ow[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    ow[e] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(out[2 * e]))) |
+                            (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(out[2 * e + 1]))) << 16);
+                __builtin_amdgcn_raw_buffer_store_b128(
+                    __builtin_bit_cast(__attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t,
+                                       make_uint4(ow[0], ow[1], ow[2], ow[3])),
+                    ry, ((16 * tb + r) * static_cast<int>(dim) + ocol) * 2, 0, 0);
             }
         }
 
@@ -342,12 +428,12 @@ void ssd_fwd_kernel(SsdArgs a) {
             for (int e = 0; e < 8; ++e) wk[e] = lds.w[k + 8 * g + e];
 #pragma unroll
             for (int nt = 0; nt < NTN; ++nt) {
-                bf16x8 bw = lds8(&lds.Bt[nw0 + 16 * nt + c][k + 8 * g]);
+                bf16x8 bw = lds8(&lds.Bt[nw0 + 16 * nt + c][tcol(nw0 + 16 * nt + c, k + 8 * g)]);
 #pragma unroll
                 for (int e = 0; e < 8; ++e) bw[e] = static_cast<__bf16>(static_cast<float>(bw[e]) * wk[e]);
 #pragma unroll
                 for (int pt = 0; pt < 4; ++pt)
-                    H[nt][pt] = mfma16(bw, lds8(&lds.Xt[16 * pt + c][k + 8 * g]), H[nt][pt]);
+                    H[nt][pt] = mfma16(bw, lds8(&lds.Xt[16 * pt + c][tcol(16 * pt + c, k + 8 * g)]), H[nt][pt]);
             }
         }
         __syncthreads();
