@@ -135,16 +135,21 @@ __device__ __forceinline__ void fetch_chunk(const SsdArgs& a, int64_t bb, int64_
     const int span = ((cnt - 1) * dim + kP) * 2;   // bytes of a head's channels over the chunk
     const __amdgpu_buffer_rsrc_t rx =
         chunk_rsrc(static_cast<const uint16_t*>(a.x) + row0 * dim + hd * kP, span);
-    if (tid < Prefetch<N>::kXBlocks) {
-        const int jb = tid / (kP / 8), col = 8 * (tid % (kP / 8));
-#pragma unroll
-        for (int r = 0; r < 8; ++r) f.blk[r] = ld128(rx, ((8 * jb + r) * dim + col) * 2);
-    } else if (tid < Prefetch<N>::kXBlocks + Prefetch<N>::kBBlocks) {
-        const __amdgpu_buffer_rsrc_t rb = chunk_rsrc(static_cast<const uint16_t*>(a.B) + row0 * N, cnt * N * 2);
+    // one load sequence for every wave (a branch per tensor would merge the
+    // loaded registers through copies that wait for the loads): wave 0 loads
+    // x blocks, the next waves B blocks, any other wave an empty range
+    {
+        const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);
+        const bool isx = wv == 0, isb = wv > 0 && wv * kWave < Prefetch<N>::kXBlocks + Prefetch<N>::kBBlocks;
+        const __amdgpu_buffer_rsrc_t rb =
+            chunk_rsrc(static_cast<const uint16_t*>(a.B) + row0 * N, isb ? cnt * N * 2 : 0);
         const int e = tid - Prefetch<N>::kXBlocks;
-        const int jb = e / (N / 8), col = 8 * (e % (N / 8));
+        const int off = isx ? ((tid / (kP / 8)) * 8 * dim + 8 * (tid % (kP / 8))) * 2
+                            : ((e / (N / 8)) * 8 * N + 8 * (e % (N / 8))) * 2;
+        const int step = isx ? dim * 2 : N * 2;
+        const __amdgpu_buffer_rsrc_t rblk = isx ? rx : rb;
 #pragma unroll
-        for (int r = 0; r < 8; ++r) f.blk[r] = ld128(rb, ((8 * jb + r) * N + col) * 2);
+        for (int r = 0; r < 8; ++r) f.blk[r] = ld128(rblk, off + r * step);
     }
     const int i = 16 * (tid / kWave) + (lane & 15), g = lane >> 4;
     const __amdgpu_buffer_rsrc_t rc = chunk_rsrc(static_cast<const uint16_t*>(a.C) + row0 * N, cnt * N * 2);

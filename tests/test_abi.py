@@ -230,6 +230,7 @@ def test_ssd_rejects_bad_arguments(lib):
     assert ssd(headdim=32) == UNSUPPORTED
     assert ssd(dstate=16) == UNSUPPORTED
     assert ssd(dtype=0) == UNSUPPORTED      # fp32 I/O: the products run in bf16
+    assert ssd(nheads=65537) == UNSUPPORTED  # buffer offsets of a chunk must fit 31 bits
     for name in ("x", "dt", "A", "B", "C", "y"):
         assert ssd(**{name: None}) == INVALID, name
     for name in ("x", "dt", "A", "B", "C", "D", "z", "h0", "y", "hL"):
