@@ -18,6 +18,9 @@ constexpr int kScanChannelsPerGroup = kWave;
 #define MAMBA_TOKEN_TILE 8
 #endif
 constexpr int kTokenTile = MAMBA_TOKEN_TILE;
+// Tokens of a tile whose LDS inputs the scan reads together, ahead of their
+// arithmetic (a divisor of kTokenTile).
+constexpr int kLdsGroup = 2;
 
 enum IoType : int { kIoF32 = 0, kIoBF16 = 1 };
 
