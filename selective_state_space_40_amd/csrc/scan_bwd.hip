@@ -36,6 +36,8 @@
 namespace mamba {
 namespace {
 
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+
 constexpr int kBT = 8;                         // tokens per tile
 constexpr int kNpw = 4;                        // states per wave
 constexpr int kVals = 2 * kBT * kNpw;          // dB and dC terms per lane per tile
@@ -45,7 +47,7 @@ template <int S>
 struct BwdLds {
     float2 dtx[kBT][kWave];                    // (delta as used, x) per token and channel
     float g[kBT][kWave];                       // dy * silu(z)
-    float bc[2][kBT][kNpw * S];                // B and C rows of the tile, padded states 0
+    alignas(16) float bc[2][kBT][kNpw * S];    // B and C rows of the tile, padded states 0
     float red[3][S][kBT][kWave];               // per-wave partial sums over states
 };
 
@@ -67,49 +69,58 @@ __device__ __forceinline__ float sigmoid_f32(float v) {
 }
 
 // Raw inputs of one tile as this thread stages them: the tokens j = w,
-// w+S, ... of the tile for its lane's channel, and one element of the
-// tile's B and C rows (2 * kBT * 4S elements over 64S threads). Loaded a
-// tile ahead so the loads are in flight while the previous tile computes.
+// w+S, ... of the tile for its lane's channel, one element of the tile's B
+// and C rows (2 * kBT * 4S elements over 64S threads) and, walking
+// backwards, the tile's checkpointed entering state of the lane's states.
+// Loaded a tile ahead so the loads are in flight while the previous tile
+// computes. Every load is issued unconditionally with its token and state
+// clamped into range (the clamped values are never used): conditional loads
+// leave the compiler unable to count the loads in flight, and the wait
+// before the first use of an older load then also waits for these.
 template <int S>
 struct TileRaw {
     static constexpr int OW = (kBT + S - 1) / S;
     uint32_t x[OW], dl[OW], dy[OW], z[OW];
     uint32_t bc;
+    float he[kNpw];
 };
 
 template <int S, int IO, bool HAS_Z, bool WANT_G>
-__device__ __forceinline__ void fetch_tile(const BwdArgs& a, const Place& pl, int64_t t0, int cnt,
-                                           TileRaw<S>& r) {
+__device__ __forceinline__ void fetch_tile(const BwdArgs& a, const Place& pl, const float* tent,
+                                           int64_t tile, int cnt, TileRaw<S>& r) {
     const ScanArgs& f = a.fwd;
+    const int64_t t0 = tile * kBT;
 #pragma unroll
     for (int jj = 0; jj < TileRaw<S>::OW; ++jj) {
-        const int j = jj * S + pl.w;
-        if (j < cnt) {
-            const int64_t idx = (pl.b * f.seqlen + t0 + j) * f.dim + pl.d;
-            r.x[jj] = load_raw<IO>(f.x, idx);
-            r.dl[jj] = load_raw<IO>(f.delta, idx);
-            if constexpr (WANT_G) {
-                r.dy[jj] = load_raw<IO>(a.dy, idx);
-                r.z[jj] = HAS_Z ? load_raw<IO>(f.z, idx) : 0u;
-            }
+        const int j = min(jj * S + pl.w, cnt - 1);
+        const int64_t idx = (pl.b * f.seqlen + t0 + j) * f.dim + pl.d;
+        r.x[jj] = load_raw<IO>(f.x, idx);
+        r.dl[jj] = load_raw<IO>(f.delta, idx);
+        if constexpr (WANT_G) {
+            r.dy[jj] = load_raw<IO>(a.dy, idx);
+            r.z[jj] = HAS_Z ? load_raw<IO>(f.z, idx) : 0u;
         }
     }
     constexpr int NP = kNpw * S;
     const int e = threadIdx.x;  // exactly one B or C element per thread
     const int which = e / (kBT * NP);
     const int rr = e - which * kBT * NP;
-    const int j = rr / NP;
-    const int n = rr - j * NP;
-    r.bc = 0u;
-    if (j < cnt && n < f.dstate)
-        r.bc = load_raw<IO>(which ? f.C : f.B, (pl.b * f.seqlen + t0 + j) * f.dstate + n);
+    const int j = min(rr / NP, cnt - 1);
+    const int n = min(rr % NP, f.dstate - 1);
+    r.bc = load_raw<IO>(which ? f.C : f.B, (pl.b * f.seqlen + t0 + j) * f.dstate + n);
+    if constexpr (WANT_G) {
+        const int N = f.dstate;
+        const float* row = tent + ((tile * f.batch + pl.b) * f.dim + pl.d) * N;
+#pragma unroll
+        for (int q = 0; q < kNpw; ++q) r.he[q] = row[min(pl.n0 + q, N - 1)];
+    }
 }
 
 // Stage a fetched tile: wave w converts its tokens j = w, w+S, ... (delta
 // activated once per (channel, token)) and every thread its B or C element.
 template <int S, int IO, bool SP, bool HAS_Z, bool WANT_G>
 __device__ __forceinline__ void put_tile(const TileRaw<S>& r, const Place& pl, BwdLds<S>& lds,
-                                         int cnt, Own (&own)[(kBT + S - 1) / S]) {
+                                         int cnt, int nstate, Own (&own)[(kBT + S - 1) / S]) {
     const int lane = threadIdx.x & (kWave - 1);
 #pragma unroll
     for (int jj = 0; jj < TileRaw<S>::OW; ++jj) {
@@ -134,26 +145,50 @@ __device__ __forceinline__ void put_tile(const TileRaw<S>& r, const Place& pl, B
     const int e = threadIdx.x;
     const int which = e / (kBT * NP);
     const int rr = e - which * kBT * NP;
-    lds.bc[which][rr / NP][rr % NP] = raw_to_f32<IO>(r.bc);
+    const bool in = rr / NP < cnt && rr % NP < nstate;   // padding states and tokens read as 0
+    lds.bc[which][rr / NP][rr % NP] = in ? raw_to_f32<IO>(r.bc) : 0.0f;
 }
 
 // Sum of each of the 64 values over the 64 lanes. At the step of distance
 // k, pairs (vals[2i], vals[2i+1]) are folded into vals[i]: lanes with bit k
-// clear keep the first value and add their partner's copy of it, lanes with
-// bit k set the second. After the steps k = 32, 16, ..., 1, lane l holds the
-// full sum of the value whose index is l with its 6 bits reversed.
+// clear keep the first value and add their partner's (lane ^ k) copy of it,
+// lanes with bit k set the second. After the steps k = 32, 16, ..., 1, lane l
+// holds the full sum of the value whose index is l with its 6 bits reversed.
+// All exchanges stay in the VALU: for k = 32 and 16 one lane swap of the pair
+// (v_permlane32_swap / v_permlane16_swap exchange the upper half of the
+// first register's 32- or 16-lane blocks with the lower half of the
+// second's) leaves each lane exactly its own kept value and its partner's,
+// so their sum is the step; for k <= 8 DPP row shifts bring lane l + k and
+// l - k within the 16-lane row.
+template <int K>
+__device__ __forceinline__ void fold_dpp(float (&vals)[kVals], int cnt, int lane) {
+    const bool hi = (lane & K) != 0;
+    for (int i = 0; i < cnt; ++i) {
+        const float a = vals[2 * i], b = vals[2 * i + 1];
+        const float up = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(a), 0x100 + K, 0xf, 0xf, false));
+        const float dn = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(b), 0x110 + K, 0xf, 0xf, false));
+        vals[i] = hi ? b + dn : a + up;   // row_shl:K reads lane l + K, row_shr:K lane l - K
+    }
+}
+
 __device__ __forceinline__ float lane_sums(float (&vals)[kVals]) {
     const int lane = threadIdx.x & (kWave - 1);
 #pragma unroll
-    for (int k = 32, cnt = kVals / 2; k >= 1; k /= 2, cnt /= 2) {
-        const bool hi = (lane & k) != 0;
-#pragma unroll
-        for (int i = 0; i < cnt; ++i) {
-            const float keep = hi ? vals[2 * i + 1] : vals[2 * i];
-            const float send = hi ? vals[2 * i] : vals[2 * i + 1];
-            vals[i] = keep + __shfl_xor(send, k, kWave);
-        }
+    for (int i = 0; i < 32; ++i) {
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(vals[2 * i]),
+                                                        __float_as_uint(vals[2 * i + 1]), false, false);
+        vals[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
     }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(vals[2 * i]),
+                                                        __float_as_uint(vals[2 * i + 1]), false, false);
+        vals[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+    fold_dpp<8>(vals, 8, lane);
+    fold_dpp<4>(vals, 4, lane);
+    fold_dpp<2>(vals, 2, lane);
+    fold_dpp<1>(vals, 1, lane);
     return vals[0];
 }
 
@@ -210,7 +245,7 @@ void scan_bwd_kernel(BwdArgs a, int64_t ngroups,
         for (int q = 0; q < kNpw; ++q)
             h[q] = (sv[q] && f.h0 != nullptr) ? f.h0[(pl.b * f.dim + pl.d) * N + pl.n0 + q] : 0.0f;
         TileRaw<S> raw;
-        fetch_tile<S, IO, HAS_Z, false>(a, pl, 0, static_cast<int>(min<int64_t>(kBT, L)), raw);
+        fetch_tile<S, IO, HAS_Z, false>(a, pl, tent, 0, static_cast<int>(min<int64_t>(kBT, L)), raw);
         for (int64_t i = 0; i < ntiles; ++i) {
             const int64_t t0 = i * kBT;
             const int cnt = static_cast<int>(min<int64_t>(kBT, L - t0));
@@ -220,19 +255,32 @@ void scan_bwd_kernel(BwdArgs a, int64_t ngroups,
                 for (int q = 0; q < kNpw; ++q)
                     if (sv[q]) row[q] = h[q];
             }
-            put_tile<S, IO, SP, HAS_Z, false>(raw, pl, lds, cnt, own);
+            put_tile<S, IO, SP, HAS_Z, false>(raw, pl, lds, cnt, N, own);
             __syncthreads();
-            if (i + 1 < ntiles)
-                fetch_tile<S, IO, HAS_Z, false>(a, pl, t0 + kBT,
-                                                static_cast<int>(min<int64_t>(kBT, L - t0 - kBT)), raw);
+            {
+                // the last tile fetches itself again (unused)
+                const int64_t nx = min(i + 1, ntiles - 1);
+                fetch_tile<S, IO, HAS_Z, false>(a, pl, tent, nx,
+                                                static_cast<int>(min<int64_t>(kBT, L - nx * kBT)), raw);
+            }
 #pragma unroll
-            for (int j = 0; j < kBT; ++j) {
-                if (j < cnt) {
-                    const float2 v = lds.dtx[j][lane];
-                    const float du = v.x * v.y;
+            for (int j0 = 0; j0 < kBT; j0 += 2) {
+                float2 v[2];
+                f32x4 bq[2];
 #pragma unroll
-                    for (int q = 0; q < kNpw; ++q)
-                        h[q] = fmaf(fast_exp2(v.x * A2[q]), h[q], du * lds.bc[0][j][pl.n0 + q]);
+                for (int jj = 0; jj < 2; ++jj) {
+                    v[jj] = lds.dtx[j0 + jj][lane];
+                    bq[jj] = *reinterpret_cast<const f32x4*>(&lds.bc[0][j0 + jj][pl.n0]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int jj = 0; jj < 2; ++jj) {
+                    if (j0 + jj < cnt) {
+                        const float du = v[jj].x * v[jj].y;
+#pragma unroll
+                        for (int q = 0; q < kNpw; ++q)
+                            h[q] = fmaf(fast_exp2(v[jj].x * A2[q]), h[q], du * bq[jj][q]);
+                    }
                 }
             }
             __syncthreads();
@@ -243,54 +291,76 @@ void scan_bwd_kernel(BwdArgs a, int64_t ngroups,
     {
         float h[kNpw];
         TileRaw<S> raw;
-        {
-            const int64_t tl = (ntiles - 1) * kBT;
-            fetch_tile<S, IO, HAS_Z, true>(a, pl, tl, static_cast<int>(L - tl), raw);
-        }
+        fetch_tile<S, IO, HAS_Z, true>(a, pl, tent, ntiles - 1,
+                                       static_cast<int>(L - (ntiles - 1) * kBT), raw);
         for (int64_t i = ntiles - 1; i >= 0; --i) {
             const int64_t t0 = i * kBT;
             const int cnt = static_cast<int>(min<int64_t>(kBT, L - t0));
             // the tile's entering state; a lane past the last channel starts
             // from zero (its x and g are zero too, so it contributes nothing)
             float he[kNpw], hs[kBT][kNpw];
-            {
-                const float* row = tent + ((i * f.batch + pl.b) * f.dim + pl.d) * N + pl.n0;
 #pragma unroll
-                for (int q = 0; q < kNpw; ++q) he[q] = (pl.valid && sv[q]) ? row[q] : 0.0f;
-            }
-            put_tile<S, IO, SP, HAS_Z, true>(raw, pl, lds, cnt, own);
+            for (int q = 0; q < kNpw; ++q) he[q] = (pl.valid && sv[q]) ? raw.he[q] : 0.0f;
+            put_tile<S, IO, SP, HAS_Z, true>(raw, pl, lds, cnt, N, own);
             __syncthreads();
-            if (i > 0) fetch_tile<S, IO, HAS_Z, true>(a, pl, t0 - kBT, kBT, raw);
+            // tile 0 fetches itself again (unused)
+            fetch_tile<S, IO, HAS_Z, true>(a, pl, tent, i > 0 ? i - 1 : 0, kBT < L ? kBT : static_cast<int>(L), raw);
 
 #pragma unroll
             for (int q = 0; q < kNpw; ++q) h[q] = he[q];
 #pragma unroll
-            for (int j = 0; j < kBT; ++j) {
-                if (j < cnt) {
-                    const float2 v = lds.dtx[j][lane];
-                    const float du = v.x * v.y;
+            for (int j0 = 0; j0 < kBT; j0 += 2) {
+                float2 v[2];
+                f32x4 bq[2];
 #pragma unroll
-                    for (int q = 0; q < kNpw; ++q)
-                        h[q] = fmaf(fast_exp2(v.x * A2[q]), h[q], du * lds.bc[0][j][pl.n0 + q]);
+                for (int jj = 0; jj < 2; ++jj) {
+                    v[jj] = lds.dtx[j0 + jj][lane];
+                    bq[jj] = *reinterpret_cast<const f32x4*>(&lds.bc[0][j0 + jj][pl.n0]);
                 }
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int q = 0; q < kNpw; ++q) hs[j][q] = h[q];
+                for (int jj = 0; jj < 2; ++jj) {
+                    const int j = j0 + jj;
+                    if (j < cnt) {
+                        const float du = v[jj].x * v[jj].y;
+#pragma unroll
+                        for (int q = 0; q < kNpw; ++q)
+                            h[q] = fmaf(fast_exp2(v[jj].x * A2[q]), h[q], du * bq[jj][q]);
+                    }
+#pragma unroll
+                    for (int q = 0; q < kNpw; ++q) hs[j][q] = h[q];
+                }
             }
 
             float vals[kVals];
 #pragma unroll
             for (int e = 0; e < kVals; ++e) vals[e] = 0.0f;
 #pragma unroll
-            for (int j = kBT - 1; j >= 0; --j) {
+            for (int j1 = kBT - 1; j1 >= 0; j1 -= 2) {
+              // the LDS inputs of tokens j1 and j1 - 1 are read before either
+              // token's arithmetic (as in the forward kernel)
+              float2 vv[2];
+              float gq[2];
+              f32x4 bq[2], cq[2];
+#pragma unroll
+              for (int jj = 0; jj < 2; ++jj) {
+                  vv[jj] = lds.dtx[j1 - jj][lane];
+                  gq[jj] = lds.g[j1 - jj][lane];
+                  bq[jj] = *reinterpret_cast<const f32x4*>(&lds.bc[0][j1 - jj][pl.n0]);
+                  cq[jj] = *reinterpret_cast<const f32x4*>(&lds.bc[1][j1 - jj][pl.n0]);
+              }
+              __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+              for (int jj = 0; jj < 2; ++jj) {
+                const int j = j1 - jj;
                 if (j < cnt) {
-                    const float2 v = lds.dtx[j][lane];
-                    const float dt = v.x, x = v.y;
-                    const float gg = lds.g[j][lane];
+                    const float dt = vv[jj].x, x = vv[jj].y;
+                    const float gg = gq[jj];
                     float dxp = 0.0f, ddp = 0.0f, pp = 0.0f;
 #pragma unroll
                     for (int q = 0; q < kNpw; ++q) {
-                        const float Bq = lds.bc[0][j][pl.n0 + q];
-                        const float Cq = lds.bc[1][j][pl.n0 + q];
+                        const float Bq = bq[jj][q];
+                        const float Cq = cq[jj][q];
                         lam[q] = fmaf(en[q], lam[q], Cq * gg);
                         const float e = fast_exp2(dt * A2[q]);
                         const float hprev = j > 0 ? hs[j > 0 ? j - 1 : 0][q] : he[q];
@@ -308,6 +378,7 @@ void scan_bwd_kernel(BwdArgs a, int64_t ngroups,
                     lds.red[1][pl.w][j][lane] = ddp;
                     lds.red[2][pl.w][j][lane] = pp;
                 }
+              }
             }
 
             // dB, dC of this tile summed over the group's channels
