@@ -449,7 +449,7 @@ def bench_backward(args, w):
         "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "seqlen": w.seqlen, "dim": w.dim,
-                   "dstate": w.dstate, "io_dtype": w.io, "checkpoint_every": 32,
+                   "dstate": w.dstate, "io_dtype": w.io, "checkpoint_every": 8,
                    "delta_activation": "bias + softplus in the kernels" if sp else
                                        "none (delta passed activated)",
                    "parallelism": "single GPU"},
