@@ -128,12 +128,41 @@ __device__ __forceinline__ uint32_t to_raw(float v) {
 template <int W, int VEC>
 __device__ __forceinline__ void load_taps(const ConvArgs& a, int64_t c0, float (&wt)[VEC][W],
                                           float (&bs)[VEC]) {
-    // weight rows of VEC adjacent channels are VEC*W contiguous floats
+    // weight rows of VEC adjacent channels are VEC*W contiguous floats; when
+    // VEC*W is a multiple of 4 they start 16-byte aligned (the weight pointer
+    // is, and c0*W is a multiple of VEC*W), and likewise the bias run
+    if constexpr ((VEC * W) % 4 == 0) {
+        const float4* wp = reinterpret_cast<const float4*>(a.weight + c0 * W);
 #pragma unroll
-    for (int v = 0; v < VEC; ++v) {
+        for (int q = 0; q < VEC * W / 4; ++q) {
+            const float4 v = wp[q];
+            const float e[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-        for (int k = 0; k < W; ++k) wt[v][k] = a.weight[(c0 + v) * W + k];
-        bs[v] = a.bias != nullptr ? a.bias[c0 + v] : 0.0f;
+            for (int u = 0; u < 4; ++u) wt[(4 * q + u) / W][(4 * q + u) % W] = e[u];
+        }
+    } else {
+#pragma unroll
+        for (int v = 0; v < VEC; ++v)
+#pragma unroll
+            for (int k = 0; k < W; ++k) wt[v][k] = a.weight[(c0 + v) * W + k];
+    }
+    if constexpr (VEC % 4 == 0) {
+#pragma unroll
+        for (int q = 0; q < VEC / 4; ++q) {
+            const float4 v = a.bias != nullptr ? reinterpret_cast<const float4*>(a.bias + c0)[q]
+                                               : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            bs[4 * q] = v.x; bs[4 * q + 1] = v.y; bs[4 * q + 2] = v.z; bs[4 * q + 3] = v.w;
+        }
+    } else if constexpr (VEC % 2 == 0) {
+#pragma unroll
+        for (int q = 0; q < VEC / 2; ++q) {
+            const float2 v = a.bias != nullptr ? reinterpret_cast<const float2*>(a.bias + c0)[q]
+                                               : make_float2(0.0f, 0.0f);
+            bs[2 * q] = v.x; bs[2 * q + 1] = v.y;
+        }
+    } else {
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) bs[v] = a.bias != nullptr ? a.bias[c0 + v] : 0.0f;
     }
 }
 
@@ -318,8 +347,14 @@ hipError_t launch_conv_wv(const ConvArgs& a, bool update, hipStream_t s) {
     return hipGetLastError();
 }
 
+// The decode step moves so few bytes per thread that more threads beat wider
+// accesses: 2 channels per thread measured 524.6 us for 64 layers of
+// 256 x 5120 against 558.1 (1 channel), 560.1 (4) and 750.3 (8).
 template <int W, int IO>
 hipError_t launch_conv_w(const ConvArgs& a, bool update, hipStream_t s) {
+    if (update)
+        return a.dim % 2 == 0 ? launch_conv_wv<W, IO, 2>(a, update, s)
+                              : launch_conv_wv<W, IO, 1>(a, update, s);
     return a.dim % 4 == 0 ? launch_conv_wv<W, IO, 4>(a, update, s)
                           : launch_conv_wv<W, IO, 1>(a, update, s);
 }
