@@ -271,6 +271,7 @@ def main():
         "hbm_frac": round(hbm_frac, 4),
     }
 
+    clock = gpu_clock_sample(step)
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, sets[0], args.cpu_sample_channels, sp)
@@ -297,6 +298,7 @@ def main():
         "achieved_GBps": round(gbps, 1),
         "wall_s": round(wall, 4),
         "roofline": roofline,
+        "gpu_clock": clock,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
@@ -358,6 +360,7 @@ def bench_decode(args, w):
     elems = w.batch * w.dim * w.layers
     bytes_step = decode_bytes(w) * w.layers
     gbps = bytes_step / sec / 1e9
+    clock = gpu_clock_sample(lambda i: graph.replay())
     line = {
         "metric": "decode state-update elements/s (batch*D*layers per step) and achieved HBM GB/s",
         "value": elems / sec, "unit": "elements/s", "n_gpus": 1, "steps": args.steps,
@@ -370,6 +373,7 @@ def bench_decode(args, w):
                      "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
                      "kernel": "state_update_kernel (64 launches per step, graph replay)",
                      "algorithmic_bytes": bytes_step},
+        "gpu_clock": clock,
         "cpu_baseline": None,
     }
     print(json.dumps(line), flush=True)
@@ -443,6 +447,7 @@ def bench_backward(args, w):
     tops = ops / sec / 1e12
     gbps = nbytes / sec / 1e9
     cpu = None if args.no_cpu_baseline else cpu_baseline_backward(w, sets[0], sp)
+    clock = gpu_clock_sample(step)
     line = {
         "metric": "backward scan elements/s (B*L*D, all input gradients, states recomputed)",
         "value": elems / sec, "unit": "elements/s", "n_gpus": 1, "steps": args.steps,
@@ -459,6 +464,7 @@ def bench_backward(args, w):
                      "traffic": None, "kernel": "ssm_scan_bwd step (all passes)",
                      "algorithmic_bytes": nbytes, "algorithmic_ops": ops,
                      "hbm_GBps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4)},
+        "gpu_clock": clock,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
@@ -544,6 +550,7 @@ def bench_ssd(args, w):
     bound = "mfma" if flops / (MFMA_BF16_PEAK_TFLOPS * 1e12) > nbytes / (HBM_PEAK_GBPS * 1e9) \
         else "hbm"
     cpu = None if args.no_cpu_baseline else cpu_baseline_ssd(w, sets[0])
+    clock = gpu_clock_sample(step)
     line = {
         "metric": "Mamba-2 dual-form scan elements/s (B*L*D) and achieved HBM GB/s",
         "value": w.elements / sec, "unit": "elements/s", "n_gpus": 1, "steps": args.steps,
@@ -562,6 +569,7 @@ def bench_ssd(args, w):
                      "algorithmic_bytes": nbytes, "algorithmic_flops": flops,
                      "mfma_TFLOPs": round(tflops, 2), "mfma_frac": round(mfma_frac, 4),
                      "hbm_frac": round(hbm_frac, 4)},
+        "gpu_clock": clock,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
@@ -599,6 +607,57 @@ def conv_bytes(w, state_in):
     s = 4 if w.io == "f32" else 2
     b, l, d, k = w.batch, w.seqlen, w.dim, w.width
     return 2 * b * l * d * s + b * d * k * s * (2 if state_in else 1) + d * k * 4 + d * 4
+
+
+def gpu_clock_sample(step, max_seconds=2.5):
+    """The GFX clock the step runs at, for the record. The GPU's metrics
+    table (read through amdsmi) is refreshed by the firmware about once a
+    second, so after the timed region the step keeps running, untimed (eight
+    steps between readings, the queue drained after each), until the table
+    has been refreshed twice while it ran or `max_seconds` pass; the per-XCD
+    current GFX clocks of the refreshed tables are reported. Returns None
+    when amdsmi is missing, sees more than one GPU or no refresh comes."""
+    import torch
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+    except Exception:
+        return None
+    try:
+        handles = amdsmi.amdsmi_get_processor_handles()
+        if len(handles) != 1:
+            return None
+        stamp = amdsmi.amdsmi_get_gpu_metrics_info(handles[0]).get("system_clock_counter")
+        tables = []
+        i = 0
+        t_end = time.perf_counter() + max_seconds
+        while time.perf_counter() < t_end and len(tables) < 2:
+            for _ in range(8):
+                step(i)
+                i += 1
+            m = amdsmi.amdsmi_get_gpu_metrics_info(handles[0])
+            if m.get("system_clock_counter") != stamp:
+                stamp = m.get("system_clock_counter")
+                xcd = [int(c) for c in (m.get("current_gfxclks") or [])
+                       if isinstance(c, (int, float)) and c > 0]
+                if xcd:
+                    tables.append(xcd)
+            torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        if not tables:
+            return None
+        flat = [c for t in tables for c in t]
+        return {"mean_MHz": round(sum(flat) / len(flat)), "min_MHz": min(flat),
+                "max_MHz": max(flat), "xcd_MHz_last": tables[-1], "tables": len(tables),
+                "how": "amdsmi metrics tables refreshed while the step repeated untimed "
+                       "right after the timed region"}
+    except Exception:
+        return None
+    finally:
+        try:
+            amdsmi.amdsmi_shut_down()
+        except Exception:
+            pass
 
 
 def _time_steps(step, warmup, steps, stream):
@@ -643,6 +702,7 @@ def bench_conv(args, w):
     nbytes = conv_bytes(w, sets[0]["state_in"] is not None)
     gbps = nbytes / sec / 1e9
     cpu = None if args.no_cpu_baseline else cpu_baseline_conv(w, sets[0])
+    clock = gpu_clock_sample(step)
     line = {
         "metric": "short causal convolution elements/s (B*L*D) and achieved HBM GB/s",
         "value": elems / sec, "unit": "elements/s", "n_gpus": 1, "steps": args.steps,
@@ -656,6 +716,7 @@ def bench_conv(args, w):
                      "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
                      "kernel": "conv1d_fwd_kernel + conv1d_state_out_kernel",
                      "algorithmic_bytes": nbytes},
+        "gpu_clock": clock,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
@@ -696,6 +757,7 @@ def bench_conv_decode(args, w):
                  + w.dim * w.width * 4 + w.dim * 4)
     nbytes = per_layer * w.layers
     gbps = nbytes / sec / 1e9
+    clock = gpu_clock_sample(lambda i: graph.replay())
     line = {
         "metric": "convolution decode elements/s (batch*D*layers per step) and achieved HBM GB/s",
         "value": w.batch * w.dim * w.layers / sec, "unit": "elements/s", "n_gpus": 1,
@@ -709,6 +771,7 @@ def bench_conv_decode(args, w):
                      "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
                      "kernel": "conv1d_update_kernel (64 launches per step, graph replay)",
                      "algorithmic_bytes": nbytes},
+        "gpu_clock": clock,
         "cpu_baseline": None,
     }
     print(json.dumps(line), flush=True)
