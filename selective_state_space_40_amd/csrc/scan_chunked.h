@@ -239,11 +239,20 @@ __device__ __forceinline__ void fetch_tile(const ChunkIo& io, int tile, int w, i
     }
 }
 
+// What the wave that finishes token j of a tile keeps from staging it: the
+// skip term D*x and the gate silu(z). Holding these instead of the raw x and
+// z frees the raw tile as soon as it is staged.
+template <int S>
+struct Epilogue {
+    float skip[TT / S], gate[TT / S];
+};
+
 // LDS layout of the staged per-token inputs: [token j][lane] float2 (delta,
-// delta*x). Writes the wave's own tokens and returns D*x of them.
-template <int S, int IO, bool SP, bool HAS_D>
+// delta*x). Writes the wave's own tokens and keeps their skip terms and
+// gates for its epilogue.
+template <int S, int IO, bool SP, bool HAS_D, bool HAS_Z>
 __device__ __forceinline__ void stage_tokens(float2* dtdu, int w, const Tile<S>& r, float dbias,
-                                             float dskip, float (&skip)[TT / S]) {
+                                             float dskip, Epilogue<S>& e) {
     const int lane = threadIdx.x & (kWave - 1);
     float dt[TT / S];
     delta_tile<S, IO, SP>(r, dbias, dt);
@@ -251,7 +260,8 @@ __device__ __forceinline__ void stage_tokens(float2* dtdu, int w, const Tile<S>&
     for (int jj = 0; jj < TT / S; ++jj) {
         const float u = raw_to_f32<IO>(r.x[jj]);
         dtdu[(jj * S + w) * kWave + lane] = make_float2(dt[jj], dt[jj] * u);
-        skip[jj] = HAS_D ? dskip * u : 0.0f;
+        e.skip[jj] = HAS_D ? dskip * u : 0.0f;
+        e.gate[jj] = HAS_Z ? silu(raw_to_f32<IO>(r.z[jj])) : 1.0f;
     }
 }
 
@@ -354,8 +364,7 @@ __device__ __forceinline__ void compute_tile(const ChunkIo& io, const float* bcs
 // and the store.
 template <int S, int IO, bool HAS_Z, bool FULL>
 __device__ __forceinline__ void finalize_tile(const ChunkIo& io, const float* red_tile, int w,
-                                              int tile, int cnt, const Tile<S>& r,
-                                              const float (&skip)[TT / S]) {
+                                              int tile, int cnt, const Epilogue<S>& e) {
     const int lane = threadIdx.x & (kWave - 1);
 #pragma unroll
     for (int jj = 0; jj < TT / S; ++jj) {
@@ -365,8 +374,8 @@ __device__ __forceinline__ void finalize_tile(const ChunkIo& io, const float* re
             float acc = col[0];
 #pragma unroll
             for (int v = 1; v < S; ++v) acc += col[v * TT * kWave];
-            acc += skip[jj];
-            if constexpr (HAS_Z) acc *= silu(raw_to_f32<IO>(r.z[jj]));
+            acc += e.skip[jj];
+            if constexpr (HAS_Z) acc *= e.gate[jj];
             // Lanes past the last channel were clamped onto channel dim-1 and
             // computed its value bit for bit, so they store the same bits to
             // the same address; the store needs no lane mask.
@@ -385,19 +394,24 @@ struct ScanLds {
     float red[2][S > 1 ? S * TT * kWave : 1];
 };
 
-// All `ntok` tokens of one chunk for one wave. Two register tiles alternate:
-// while one tile is computed the next one (this wave's x, delta, z and its
-// share of the raw B/C run) is already in flight, and the tiles swap roles
-// without register copies. Fetches are unconditional and clamp their tokens
-// to the chunk, and the full tiles run in pairs inside a loop with a single
-// exit, so every path into a compute step has the same loads in flight and
-// the waits before it stay exact. A ragged last tile runs once after the loop.
+// All `ntok` tokens of one chunk for one wave. Two register tiles alternate
+// and swap roles without register copies. With S > 1 a tile's raw inputs
+// (this wave's x, delta, z and its share of the raw B/C run) are fetched two
+// tiles before the tile is computed: a raw tile is free once staged (the
+// epilogue keeps D*x and silu(z) instead), so step i refills the registers
+// that held tile i with tile i+2 while tile i+1's raw inputs, fetched a whole
+// step earlier, are staged. With S == 1 the single wave computes from the
+// raw tile itself, so it fetches one tile ahead. Fetches are unconditional
+// and clamp their tiles and tokens to the chunk, and the full tiles run in
+// pairs inside a loop with a single exit, so every path into a compute step
+// has the same loads in flight and the waits before it stay exact. A ragged
+// last tile runs once after the loop.
 //
-// Per tile, in order: fetch tile i+1; compute tile i from LDS buffers i&1
-// and store the partial readouts; stage tile i+1's B/C and per-token inputs
-// into LDS buffers (i+1)&1; barrier; finalise this wave's tokens of tile i.
-// Every LDS buffer is rewritten only after a barrier that follows its last
-// read.
+// Per tile, in order: fetch tile i+2 (S > 1) or i+1; compute tile i from LDS
+// buffers i&1 and store the partial readouts; stage tile i+1's B/C and
+// per-token inputs into LDS buffers (i+1)&1; barrier; finalise this wave's
+// tokens of tile i. Every LDS buffer is rewritten only after a barrier that
+// follows its last read.
 template <int N, int S, int IO, bool SP, bool OUTPUT, bool HAS_D, bool HAS_Z>
 __device__ __forceinline__ void scan_chunk(const ChunkIo& io, const BcIo& bcio, float dbias,
                                            int ntok, int w, int n0,
@@ -410,20 +424,24 @@ __device__ __forceinline__ void scan_chunk(const ChunkIo& io, const BcIo& bcio, 
     const int ntiles = (ntok + TT - 1) / TT;
     const int nfull = ntok / TT;
     const int lane = threadIdx.x & (kWave - 1);
+    constexpr int AHEAD = S > 1 ? 2 : 1;  // tiles between fetching a tile and computing it
     Tile<S> ta, tb;
-    float ska[TT / S], skb[TT / S];
-    uint32_t bra[KP], cra[KP];
+    Epilogue<S> ea, eb;
+    uint32_t bra[KP], cra[KP], brb[KP], crb[KP];
 
-    auto step = [&](auto full_tag, int i, const Tile<S>& cur, const float (&skc)[TT / S],
-                    Tile<S>& nxt, float (&skn)[TT / S]) {
+    // bf/cf receive the B/C run fetched in this step; bs/cs hold tile i+1's,
+    // staged at its end (the same registers when AHEAD == 1)
+    auto step = [&](auto full_tag, int i, Tile<S>& cur, const Epilogue<S>& ec, Tile<S>& nxt,
+                    Epilogue<S>& en, uint32_t (&bf)[KP], uint32_t (&cf)[KP],
+                    const uint32_t (&bs)[KP], const uint32_t (&cs)[KP]) {
         constexpr bool FULL = decltype(full_tag)::value;
-        const int inext = min(i + 1, ntiles - 1);
+        const int ifetch = min(i + AHEAD, ntiles - 1);
         // The B/C run is issued first and kept first (scheduling fences), so
-        // staging it at the end of this step waits only for loads older than
-        // the next tile's token inputs, which stay in flight a little longer.
-        fetch_bc<N, S, IO>(bcio, inext, min(TT, ntok - inext * TT), bra, cra);
+        // with AHEAD == 1 staging it at the end of this step waits only for
+        // loads older than the next tile's token inputs.
+        fetch_bc<N, S, IO>(bcio, ifetch, min(TT, ntok - ifetch * TT), bf, cf);
         __builtin_amdgcn_sched_barrier(0);
-        fetch_tile<S, IO, LOAD_Z>(io, inext, w, ntok, nxt);
+        fetch_tile<S, IO, LOAD_Z>(io, ifetch, w, ntok, AHEAD == 2 ? cur : nxt);
         __builtin_amdgcn_sched_barrier(0);
         const int cnt = FULL ? TT : ntok - i * TT;
         float part[TT], dtv[TT / S];
@@ -436,34 +454,51 @@ __device__ __forceinline__ void scan_chunk(const ChunkIo& io, const BcIo& bcio, 
 #pragma unroll
             for (int j = 0; j < TT; ++j) mine[j * kWave] = part[j];
         }
-        stage_bc<N, S, IO>(lds.bcs[(i + 1) & 1], bra, cra);
+        stage_bc<N, S, IO>(lds.bcs[(i + 1) & 1], bs, cs);
         if constexpr (S > 1)
-            stage_tokens<S, IO, SP, OUTPUT && HAS_D>(lds.dtdu[(i + 1) & 1], w, nxt, dbias, dskip,
-                                                     skn);
+            stage_tokens<S, IO, SP, OUTPUT && HAS_D, OUTPUT && HAS_Z>(lds.dtdu[(i + 1) & 1], w,
+                                                                      nxt, dbias, dskip, en);
         __syncthreads();
         if constexpr (OUTPUT && S > 1)
-            finalize_tile<S, IO, HAS_Z, FULL>(io, lds.red[i & 1], w, i, cnt, cur, skc);
+            finalize_tile<S, IO, HAS_Z, FULL>(io, lds.red[i & 1], w, i, cnt, ec);
+    };
+    // even steps fetch into (bra, cra) and stage (brb, crb), odd steps the
+    // other way round; with AHEAD == 1 every step fetches and stages (bra, cra)
+    auto even = [&](auto tag, int i) {
+        if constexpr (AHEAD == 2) step(tag, i, ta, ea, tb, eb, bra, cra, brb, crb);
+        else step(tag, i, ta, ea, tb, eb, bra, cra, bra, cra);
+    };
+    auto odd = [&](auto tag, int i) {
+        if constexpr (AHEAD == 2) step(tag, i, tb, eb, ta, ea, brb, crb, bra, cra);
+        else step(tag, i, tb, eb, ta, ea, bra, cra, bra, cra);
     };
     using Full = std::integral_constant<bool, true>;
     using Ragged = std::integral_constant<bool, false>;
 
-    // prologue: tile 0's B/C and token inputs into LDS buffers 0
+    // prologue: tile 0's B/C and token inputs into LDS buffers 0 (and, two
+    // tiles ahead, tile 1's raw inputs into the second registers)
     fetch_bc<N, S, IO>(bcio, 0, min(TT, ntok), bra, cra);
     fetch_tile<S, IO, LOAD_Z>(io, 0, w, ntok, ta);
+    if constexpr (AHEAD == 2) {
+        const int i1 = min(1, ntiles - 1);
+        fetch_bc<N, S, IO>(bcio, i1, min(TT, ntok - i1 * TT), brb, crb);
+        fetch_tile<S, IO, LOAD_Z>(io, i1, w, ntok, tb);
+    }
     stage_bc<N, S, IO>(lds.bcs[0], bra, cra);
     if constexpr (S > 1)
-        stage_tokens<S, IO, SP, OUTPUT && HAS_D>(lds.dtdu[0], w, ta, dbias, dskip, ska);
+        stage_tokens<S, IO, SP, OUTPUT && HAS_D, OUTPUT && HAS_Z>(lds.dtdu[0], w, ta, dbias,
+                                                                  dskip, ea);
     __syncthreads();
     int i = 0;
     for (; i + 2 <= nfull; i += 2) {
-        step(Full{}, i, ta, ska, tb, skb);
-        step(Full{}, i + 1, tb, skb, ta, ska);
+        even(Full{}, i);
+        odd(Full{}, i + 1);
     }
     if (i < nfull) {
-        step(Full{}, i, ta, ska, tb, skb);
-        if (nfull < ntiles) step(Ragged{}, i + 1, tb, skb, ta, ska);
+        even(Full{}, i);
+        if (nfull < ntiles) odd(Ragged{}, i + 1);
     } else if (nfull < ntiles) {
-        step(Ragged{}, i, ta, ska, tb, skb);
+        even(Ragged{}, i);
     }
 }
 
