@@ -47,6 +47,9 @@ def parse():
     p.add_argument("--delta-softplus", action="store_true",
                    help="pass delta before its activation with a per-channel bias and let the "
                         "kernels apply bias and softplus")
+    p.add_argument("--spin-up", type=float, default=0.3,
+                   help="seconds the step runs untimed before the warm-up steps, so the GPU "
+                        "clock has left idle (0 = none)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-channels", type=int, default=0,
                    help="channels of the CPU-baseline sample (0 = sized to ~10 s)")
@@ -217,6 +220,7 @@ def main():
                     inp["h0"], delta_bias=inp.get("delta_bias"), delta_softplus=sp,
                     chunk_len=args.chunk_len, state_split=args.state_split, out=y, state_out=hL)
 
+    _spin_up(step, args.spin_up)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -299,6 +303,7 @@ def main():
         "wall_s": round(wall, 4),
         "roofline": roofline,
         "gpu_clock": clock,
+        "spin_up": dict(SPIN_UP),
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
@@ -342,6 +347,7 @@ def bench_decode(args, w):
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         step()
+    _spin_up(lambda i: graph.replay(), args.spin_up)
     for _ in range(args.warmup):
         graph.replay()
     torch.cuda.synchronize()
@@ -374,6 +380,7 @@ def bench_decode(args, w):
                      "kernel": "state_update_kernel (64 launches per step, graph replay)",
                      "algorithmic_bytes": bytes_step},
         "gpu_clock": clock,
+        "spin_up": dict(SPIN_UP),
         "cpu_baseline": None,
     }
     print(json.dumps(line), flush=True)
@@ -439,7 +446,8 @@ def bench_backward(args, w):
                     inp["h0"], dy=inp["dy"], delta_bias=inp.get("delta_bias"),
                     delta_softplus=sp)
 
-    ms_per_step, wall = _time_steps(step, args.warmup, args.steps, torch.cuda.current_stream(dev))
+    ms_per_step, wall = _time_steps(step, args.warmup, args.steps, torch.cuda.current_stream(dev),
+                                      args.spin_up)
     sec = ms_per_step / 1e3
     elems = w.batch * w.seqlen * w.dim
     nbytes = backward_bytes(w, sp)
@@ -465,6 +473,7 @@ def bench_backward(args, w):
                      "algorithmic_bytes": nbytes, "algorithmic_ops": ops,
                      "hbm_GBps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4)},
         "gpu_clock": clock,
+        "spin_up": dict(SPIN_UP),
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
@@ -539,7 +548,8 @@ def bench_ssd(args, w):
         ms.ssd_fwd(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"],
                    inp["h0"], out=y, state_out=hL)
 
-    ms_per_step, wall = _time_steps(step, args.warmup, args.steps, torch.cuda.current_stream(dev))
+    ms_per_step, wall = _time_steps(step, args.warmup, args.steps, torch.cuda.current_stream(dev),
+                                      args.spin_up)
     sec = ms_per_step / 1e3
     flops = ssd_flops(w)
     nbytes = ssd_bytes(w)
@@ -570,6 +580,7 @@ def bench_ssd(args, w):
                      "mfma_TFLOPs": round(tflops, 2), "mfma_frac": round(mfma_frac, 4),
                      "hbm_frac": round(hbm_frac, 4)},
         "gpu_clock": clock,
+        "spin_up": dict(SPIN_UP),
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
@@ -660,8 +671,29 @@ def gpu_clock_sample(step, max_seconds=2.5):
             pass
 
 
-def _time_steps(step, warmup, steps, stream):
+# Untimed steps run before the warm-up ones: the GFX clock climbs from idle
+# over tens of milliseconds of load, and 50 steps timed after only 5 warm-up
+# steps of the Mamba-2.8B layer ran 9% slower (368-374 us) than after 100
+# (341 us). Filled in by _spin_up and reported on every bench line.
+SPIN_UP = {"seconds": 0.0, "steps": 0}
+
+
+def _spin_up(step, seconds):
     import torch
+    n = 0
+    t_end = time.perf_counter() + seconds
+    while time.perf_counter() < t_end:
+        for _ in range(4):
+            step(n)
+            n += 1
+        torch.cuda.synchronize()
+    SPIN_UP.update(seconds=seconds, steps=n)
+    return n
+
+
+def _time_steps(step, warmup, steps, stream, spin_up=0.0):
+    import torch
+    _spin_up(step, spin_up)
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
@@ -696,7 +728,8 @@ def bench_conv(args, w):
         inp = sets[i % 2]
         ms.conv1d_fwd(inp["x"], inp["weight"], inp["bias"], inp["state_in"], out=y, state_out=st)
 
-    ms_per_step, wall = _time_steps(step, args.warmup, args.steps, torch.cuda.current_stream(dev))
+    ms_per_step, wall = _time_steps(step, args.warmup, args.steps, torch.cuda.current_stream(dev),
+                                      args.spin_up)
     sec = ms_per_step / 1e3
     elems = w.batch * w.seqlen * w.dim
     nbytes = conv_bytes(w, sets[0]["state_in"] is not None)
@@ -717,6 +750,7 @@ def bench_conv(args, w):
                      "kernel": "conv1d_fwd_kernel + conv1d_state_out_kernel",
                      "algorithmic_bytes": nbytes},
         "gpu_clock": clock,
+        "spin_up": dict(SPIN_UP),
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
@@ -750,7 +784,7 @@ def bench_conv_decode(args, w):
     with torch.cuda.graph(graph):
         run()
     ms_per_step, wall = _time_steps(lambda i: graph.replay(), args.warmup, args.steps,
-                                    torch.cuda.current_stream(dev))
+                                    torch.cuda.current_stream(dev), args.spin_up)
     sec = ms_per_step / 1e3
     s = 4 if w.io == "f32" else 2
     per_layer = (2 * w.batch * w.dim * w.width * s + 2 * w.batch * w.dim * s
@@ -772,6 +806,7 @@ def bench_conv_decode(args, w):
                      "kernel": "conv1d_update_kernel (64 launches per step, graph replay)",
                      "algorithmic_bytes": nbytes},
         "gpu_clock": clock,
+        "spin_up": dict(SPIN_UP),
         "cpu_baseline": None,
     }
     print(json.dumps(line), flush=True)
