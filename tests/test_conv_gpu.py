@@ -108,17 +108,19 @@ def test_conv_state_aliasing_and_split(orc):
 
 
 def test_conv_decode_steps_equal_forward(orc):
+    # even channel counts take the 2-channels-per-thread decode kernel, odd
+    # ones the single-channel kernel; every width of both
     for io in ("f32", "bf16"):
-        for width in (4, 3, 1):
-            inp = _inputs(3, 12, 70, width, io, seed=width)
+        for width, dim in ((4, 70), (3, 70), (2, 70), (1, 70), (4, 37), (3, 37), (2, 37), (1, 37)):
+            inp = _inputs(3, 12, dim, width, io, seed=width + dim)
             yo, so = orc.conv1d_fwd(inp["x"], inp["weight"], inp["bias"], inp["state_in"])
             state = inp["state_in"].clone()
-            _say(f"case conv decode W={width} {io}")
+            _say(f"case conv decode W={width} D={dim} {io}")
             ys = [ms.conv1d_update(state, inp["x"][:, t].contiguous(), inp["weight"],
                                    inp["bias"]) for t in range(12)]
             torch.cuda.synchronize()
-            assert_close(torch.stack(ys, dim=1), yo, TOL[io], f"conv decode W={width} y")
-            _state_equal(state, so, f"conv decode W={width}")
+            assert_close(torch.stack(ys, dim=1), yo, TOL[io], f"conv decode W={width} D={dim} y")
+            _state_equal(state, so, f"conv decode W={width} D={dim}")
 
 
 @pytest.mark.parametrize("layer", [0, 41])
