@@ -91,22 +91,18 @@ __device__ __forceinline__ bf16x8 lds4x2(const __bf16* p, const __bf16* q) {
     return v;
 }
 
-// The next chunk's inputs, held in registers between chunks. Threads
-// 0 .. 63 each hold an 8 x 8 block (8 tokens, 8 channels) of x, the next
-// N threads (N / 8 blocks per 8 tokens) an 8 x 8 block of B. Every lane
-// holds the C row of its own token i as the products read it (8 values of n
-// at 8 g + 32 k for k < N / 32), and the gate z and input x of 8 channels of
-// two of its wave's tokens in row order (see the output step); lanes of wave
-// 0 hold the raw step of token `lane`. Values stay raw until the chunk
-// is staged, so issuing the loads never waits for them.
+// How the chunk's inputs are spread over the threads. Threads 0 .. 63 each
+// load an 8 x 8 block (8 tokens, 8 channels) of x, the next N threads (N / 8
+// blocks per 8 tokens) an 8 x 8 block of B; lanes of wave 0 load the raw
+// step of token `lane`. Every lane loads the C row of its own token i as the
+// products read it (8 values of n at 8 g + 32 k for k < N / 32), and the gate
+// z and input x of 8 channels of two of its wave's tokens in row order (see
+// the output step).
 template <int N>
-struct Prefetch {
+struct Layout {
     static constexpr int kXBlocks = (kQ / 8) * (kP / 8);
     static constexpr int kBBlocks = (kQ / 8) * (N / 8);
     static constexpr int kCk = N / 32;   // K steps of 32 over n
-    uint4 blk[8], c[kCk];
-    uint4 z[2], xd[2];
-    uint32_t dt;
 };
 
 // Buffer resource over `bytes` bytes from p (raw addressing, gfx9 word 3):
@@ -121,56 +117,80 @@ __device__ __forceinline__ uint4 ld128(__amdgpu_buffer_rsrc_t r, int off) {
 }
 
 
-// Issues the loads of chunk [t0, t0 + cnt) of row bb, head hd. Every
-// resource starts at the chunk's first token and ends after its last valid
-// one; lane offsets are the same for every chunk. Offsets fit 31 bits since
-// the library caps nheads at 2^16 (64 rows of 2^22 channels).
-template <int N, bool HAS_D, bool HAS_Z>
-__device__ __forceinline__ void fetch_chunk(const SsdArgs& a, int64_t bb, int64_t hd, int64_t t0,
-                                            int cnt, Prefetch<N>& f) {
+// The loads of chunk [t0, t0 + cnt) of row bb, head hd, in three groups
+// issued at different points of the previous chunk: each group goes into
+// the registers that held the previous chunk's values right after their last
+// use, so no registers are copied between chunks. Every resource starts at
+// the chunk's first token and ends after its last valid one; lane offsets
+// are the same for every chunk. Offsets fit 31 bits since the library caps
+// nheads at 2^16 (64 rows of 2^22 channels).
+struct ChunkPos {
+    int64_t row0;   // bb * seqlen + t0
+    int cnt;        // valid tokens
+};
+
+// x and B blocks and the step, consumed when the chunk is staged. One load
+// sequence for every wave (a branch per tensor would merge the loaded
+// registers through copies that wait for the loads): wave 0 loads x blocks,
+// the next waves B blocks, any other wave an empty range.
+template <int N>
+__device__ __forceinline__ void fetch_tiles(const SsdArgs& a, int64_t hd, ChunkPos c,
+                                            uint4 (&blk)[8], uint32_t& dt) {
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int dim = static_cast<int>(a.nheads) * kP;
-    const int64_t row0 = bb * a.seqlen + t0;
-    const int span = ((cnt - 1) * dim + kP) * 2;   // bytes of a head's channels over the chunk
-    const __amdgpu_buffer_rsrc_t rx =
-        chunk_rsrc(static_cast<const uint16_t*>(a.x) + row0 * dim + hd * kP, span);
-    // one load sequence for every wave (a branch per tensor would merge the
-    // loaded registers through copies that wait for the loads): wave 0 loads
-    // x blocks, the next waves B blocks, any other wave an empty range
-    {
-        const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);
-        const bool isx = wv == 0, isb = wv > 0 && wv * kWave < Prefetch<N>::kXBlocks + Prefetch<N>::kBBlocks;
-        const __amdgpu_buffer_rsrc_t rb =
-            chunk_rsrc(static_cast<const uint16_t*>(a.B) + row0 * N, isb ? cnt * N * 2 : 0);
-        const int e = tid - Prefetch<N>::kXBlocks;
-        const int off = isx ? ((tid / (kP / 8)) * 8 * dim + 8 * (tid % (kP / 8))) * 2
-                            : ((e / (N / 8)) * 8 * N + 8 * (e % (N / 8))) * 2;
-        const int step = isx ? dim * 2 : N * 2;
-        const __amdgpu_buffer_rsrc_t rblk = isx ? rx : rb;
+    const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const bool isx = wv == 0, isb = wv > 0 && wv * kWave < Layout<N>::kXBlocks + Layout<N>::kBBlocks;
+    const __amdgpu_buffer_rsrc_t rx = chunk_rsrc(
+        static_cast<const uint16_t*>(a.x) + c.row0 * dim + hd * kP, ((c.cnt - 1) * dim + kP) * 2);
+    const __amdgpu_buffer_rsrc_t rb =
+        chunk_rsrc(static_cast<const uint16_t*>(a.B) + c.row0 * N, isb ? c.cnt * N * 2 : 0);
+    const int e = tid - Layout<N>::kXBlocks;
+    const int off = isx ? ((tid / (kP / 8)) * 8 * dim + 8 * (tid % (kP / 8))) * 2
+                        : ((e / (N / 8)) * 8 * N + 8 * (e % (N / 8))) * 2;
+    const int step = isx ? dim * 2 : N * 2;
+    const __amdgpu_buffer_rsrc_t rblk = isx ? rx : rb;
 #pragma unroll
-        for (int r = 0; r < 8; ++r) f.blk[r] = ld128(rblk, off + r * step);
-    }
-    const int i = 16 * (tid / kWave) + (lane & 15), g = lane >> 4;
-    const __amdgpu_buffer_rsrc_t rc = chunk_rsrc(static_cast<const uint16_t*>(a.C) + row0 * N, cnt * N * 2);
+    for (int r = 0; r < 8; ++r) blk[r] = ld128(rblk, off + r * step);
+    const int nh = static_cast<int>(a.nheads);
+    const __amdgpu_buffer_rsrc_t rdt = chunk_rsrc(static_cast<const uint16_t*>(a.dt) + c.row0 * nh + hd,
+                                                  ((c.cnt - 1) * nh + 1) * 2);
+    dt = static_cast<uint16_t>(__builtin_amdgcn_raw_buffer_load_b16(rdt, lane * nh * 2, 0, 0));
+}
+
+// This lane's C row as the products read it; last used by the H C^T product.
+template <int N>
+__device__ __forceinline__ void fetch_c(const SsdArgs& a, ChunkPos c, bf16x8 (&cop)[Layout<N>::kCk]) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int i = 16 * (threadIdx.x / kWave) + (lane & 15), g = lane >> 4;
+    const __amdgpu_buffer_rsrc_t rc =
+        chunk_rsrc(static_cast<const uint16_t*>(a.C) + c.row0 * N, c.cnt * N * 2);
 #pragma unroll
-    for (int k = 0; k < Prefetch<N>::kCk; ++k) f.c[k] = ld128(rc, (i * N + 8 * g + 32 * k) * 2);
-    // rows 16 w + (lane / 8) + 8 h, channels 8 (lane % 8) .. + 8
-    const int orow = 16 * (tid / kWave) + (lane >> 3), ocol = 8 * (lane & 7);
+    for (int k = 0; k < Layout<N>::kCk; ++k)
+        cop[k] = __builtin_bit_cast(bf16x8, ld128(rc, (i * N + 8 * g + 32 * k) * 2));
+}
+
+// The gate and input rows of the output step (rows 16 w + (lane / 8) + 8 h,
+// channels 8 (lane % 8) .. + 8); last used by the output step.
+template <bool HAS_D, bool HAS_Z>
+__device__ __forceinline__ void fetch_out(const SsdArgs& a, int64_t hd, ChunkPos c, uint4 (&zc)[2],
+                                          uint4 (&xc)[2]) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int dim = static_cast<int>(a.nheads) * kP;
+    const int span = ((c.cnt - 1) * dim + kP) * 2;
+    const int orow = 16 * (threadIdx.x / kWave) + (lane >> 3), ocol = 8 * (lane & 7);
     if constexpr (HAS_Z) {
         const __amdgpu_buffer_rsrc_t rz =
-            chunk_rsrc(static_cast<const uint16_t*>(a.z) + row0 * dim + hd * kP, span);
+            chunk_rsrc(static_cast<const uint16_t*>(a.z) + c.row0 * dim + hd * kP, span);
 #pragma unroll
-        for (int h = 0; h < 2; ++h) f.z[h] = ld128(rz, ((orow + 8 * h) * dim + ocol) * 2);
+        for (int h = 0; h < 2; ++h) zc[h] = ld128(rz, ((orow + 8 * h) * dim + ocol) * 2);
     }
     if constexpr (HAS_D) {
+        const __amdgpu_buffer_rsrc_t rx =
+            chunk_rsrc(static_cast<const uint16_t*>(a.x) + c.row0 * dim + hd * kP, span);
 #pragma unroll
-        for (int h = 0; h < 2; ++h) f.xd[h] = ld128(rx, ((orow + 8 * h) * dim + ocol) * 2);
+        for (int h = 0; h < 2; ++h) xc[h] = ld128(rx, ((orow + 8 * h) * dim + ocol) * 2);
     }
-    const int nh = static_cast<int>(a.nheads);
-    const __amdgpu_buffer_rsrc_t rdt =
-        chunk_rsrc(static_cast<const uint16_t*>(a.dt) + row0 * nh + hd, ((cnt - 1) * nh + 1) * 2);
-    f.dt = static_cast<uint16_t>(__builtin_amdgcn_raw_buffer_load_b16(rdt, lane * nh * 2, 0, 0));
 }
 
 // Inclusive prefix sum over the 64 lanes of a wave with DPP: shifts by 1, 2,
@@ -246,44 +266,46 @@ void ssd_fwd_kernel(SsdArgs a) {
             }
 
     const int64_t nchunks = (L + kQ - 1) / kQ;
-    Prefetch<N> pf;
-    fetch_chunk<N, HAS_D, HAS_Z>(a, bb, hd, 0, static_cast<int>(min<int64_t>(kQ, L)), pf);
+    // the chunk whose loads a step issues: the next one, the last one
+    // loading itself again (unused) so that every iteration issues the same
+    // loads and the waits before each use stay exact
+    auto pos = [&](int64_t k) {
+        k = min(k, nchunks - 1);
+        return ChunkPos{bb * L + k * kQ, static_cast<int>(min<int64_t>(kQ, L - k * kQ))};
+    };
+    uint4 blk[8], zc[2], xc[2];
+    uint32_t dtr;
+    bf16x8 cop[Layout<N>::kCk];
+    fetch_tiles<N>(a, hd, pos(0), blk, dtr);
+    fetch_c<N>(a, pos(0), cop);
+    fetch_out<HAS_D, HAS_Z>(a, hd, pos(0), zc, xc);
     for (int64_t ch = 0; ch < nchunks; ++ch) {
         const int64_t t0 = ch * kQ;
         const int cnt = static_cast<int>(min<int64_t>(kQ, L - t0));
 
         // (1) stage the chunk: x transposed, B as it is and transposed; the
         // steps, their running sum and the token weights; the state entering
-        // the chunk as bf16 (p, n). C and z move to this chunk's registers.
-        if (tid < Prefetch<N>::kXBlocks + Prefetch<N>::kBBlocks) {
+        // the chunk as bf16 (p, n)
+        if (tid < Layout<N>::kXBlocks + Layout<N>::kBBlocks) {
             uint4 tr[8];
-            transpose8(pf.blk, tr);
-            if (tid < Prefetch<N>::kXBlocks) {
+            transpose8(blk, tr);
+            if (tid < Layout<N>::kXBlocks) {
                 const int jb = tid / (kP / 8), pb = tid % (kP / 8);
 #pragma unroll
                 for (int f = 0; f < 8; ++f)
                     *reinterpret_cast<uint4*>(&lds.Xt[8 * pb + f][tcol(8 * pb + f, 8 * jb)]) = tr[f];
             } else {
-                const int e = tid - Prefetch<N>::kXBlocks;
+                const int e = tid - Layout<N>::kXBlocks;
                 const int jb = e / (N / 8), nb = e % (N / 8);
 #pragma unroll
                 for (int f = 0; f < 8; ++f) {
                     *reinterpret_cast<uint4*>(&lds.Bt[8 * nb + f][tcol(8 * nb + f, 8 * jb)]) = tr[f];
-                    *reinterpret_cast<uint4*>(&lds.B[8 * jb + f][8 * nb]) = pf.blk[f];
+                    *reinterpret_cast<uint4*>(&lds.B[8 * jb + f][8 * nb]) = blk[f];
                 }
             }
         }
-        bf16x8 cop[Prefetch<N>::kCk];
-#pragma unroll
-        for (int k = 0; k < Prefetch<N>::kCk; ++k) cop[k] = __builtin_bit_cast(bf16x8, pf.c[k]);
-        uint4 zc[2], xc[2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            zc[h] = pf.z[h];
-            xc[h] = pf.xd[h];
-        }
         if (w == 0) {
-            const float v = raw_to_f32<kIoBF16>(pf.dt) + bias;
+            const float v = raw_to_f32<kIoBF16>(dtr) + bias;
             const float dtv = lane < cnt ? (SP ? softplus_f32(v) : v) : 0.0f;
             const float s = wave_prefix_sum(dtv) * alog2;
             const float last = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s), kWave - 1));
@@ -303,9 +325,8 @@ void ssd_fwd_kernel(SsdArgs a) {
             }
         __syncthreads();
 
-        // the next chunk's loads go out now and land during this chunk
-        if (ch + 1 < nchunks)
-            fetch_chunk<N, HAS_D, HAS_Z>(a, bb, hd, t0 + kQ, static_cast<int>(min<int64_t>(kQ, L - t0 - kQ)), pf);
+        // the next chunk's tiles and steps go out now and land during this one
+        fetch_tiles<N>(a, hd, pos(ch + 1), blk, dtr);
         const float s_last = lds.S[kQ - 1];
 
         // (3) M^T for this wave's tokens: blocks jt = 0 .. w of G^T = B C^T
@@ -359,6 +380,8 @@ void ssd_fwd_kernel(SsdArgs a) {
             for (int pt = 0; pt < 4; ++pt)
                 Yo[pt] = mfma16(lds8(&lds.H[16 * pt + c][k + 8 * g]), cop[k / 32], Yo[pt]);
         }
+        // this chunk's C is no longer needed: the next chunk's goes out
+        fetch_c<N>(a, pos(ch + 1), cop);
         // (5) output: the wave's 16 x 64 block leaves the accumulators through
         // LDS so that the gate and input are read, and y written, as whole
         // rows (16 bytes per lane, 8 lanes per row); rows past the sequence
@@ -416,6 +439,8 @@ void ssd_fwd_kernel(SsdArgs a) {
                     ry, ((16 * tb + r) * static_cast<int>(dim) + ocol) * 2, 0, 0);
             }
         }
+        // nor this chunk's gate and input
+        fetch_out<HAS_D, HAS_Z>(a, hd, pos(ch + 1), zc, xc);
 
         // (4) the state: H^T <- exp(S_last) H^T + (B w)^T X, w applied as the
         // operand is read
