@@ -3,10 +3,11 @@ the fp64 CPU oracle's backward pass on the same seeded inputs.
 
 Tolerance, per gradient tensor: max abs error <= tol * max|oracle| with
 tol = 1e-4 for fp32 I/O and 2e-2 for bf16 I/O. The fp32 bound is looser than
-the forward's 1e-5: each gradient is a sum over up to 32 tokens of
-recomputed states (sums over channels and batch rows follow), through the
-hardware exp2 (about 1 ulp) and fp32 accumulation, and dA, dB and dC add
-thousands of such terms. bf16 I/O keeps the forward's 2e-2 (dx, ddelta, dz
+the forward's 1e-5: each gradient combines states recomputed in fp32 (a
+forward pass over the whole sequence to the checkpoints, then up to 8 tokens
+from a checkpoint) with an adjoint carried back over the whole sequence,
+through the hardware exp2 (about 1 ulp) and fp32 accumulation, and dA, dB
+and dC add thousands of such terms. bf16 I/O keeps the forward's 2e-2 (dx, ddelta, dz
 are rounded to bf16 on output).
 """
 import dataclasses
