@@ -34,6 +34,27 @@ namespace {
 
 constexpr int kConvTokens = 16;  // tokens per thread of the forward kernel
 constexpr int kConvBlock = 256;
+// The decode state streams through once per step: non-temporal loads and
+// stores keep it from displacing cached data (64 layers of 256 x 5120, W=4:
+// 461 us against 523 us with ordinary accesses).
+constexpr bool kConvStateNt = true;
+
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+
+// Word loads and stores, non-temporal when NT (data that streams through
+// once and should not displace cached data).
+template <bool NT, typename T>
+__device__ __forceinline__ T ld_words(const T* p) {
+    if constexpr (NT) return __builtin_nontemporal_load(p);
+    else return *p;
+}
+
+template <bool NT, typename T>
+__device__ __forceinline__ void st_words(T v, T* p) {
+    if constexpr (NT) __builtin_nontemporal_store(v, p);
+    else *p = v;
+}
 
 // K consecutive I/O elements held as raw 32-bit words and moved with the
 // widest accesses their size allows (callers guarantee that alignment).
@@ -44,6 +65,7 @@ struct Run {
     static constexpr int kN = kWords ? kBytes / 4 : K;  // words, or single elements
     uint32_t w[kN];
 
+    template <bool NT = false>
     __device__ __forceinline__ void load(const void* base, int64_t elem) {
         if constexpr (!kWords) {
 #pragma unroll
@@ -53,22 +75,23 @@ struct Run {
             if constexpr (kBytes % 16 == 0) {
 #pragma unroll
                 for (int q = 0; q < kN / 4; ++q) {
-                    const uint4 v = reinterpret_cast<const uint4*>(p)[q];
+                    const v4u v = ld_words<NT>(reinterpret_cast<const v4u*>(p) + q);
                     w[4 * q] = v.x; w[4 * q + 1] = v.y; w[4 * q + 2] = v.z; w[4 * q + 3] = v.w;
                 }
             } else if constexpr (kBytes % 8 == 0) {
 #pragma unroll
                 for (int q = 0; q < kN / 2; ++q) {
-                    const uint2 v = reinterpret_cast<const uint2*>(p)[q];
+                    const v2u v = ld_words<NT>(reinterpret_cast<const v2u*>(p) + q);
                     w[2 * q] = v.x; w[2 * q + 1] = v.y;
                 }
             } else {
 #pragma unroll
-                for (int q = 0; q < kN; ++q) w[q] = reinterpret_cast<const uint32_t*>(p)[q];
+                for (int q = 0; q < kN; ++q) w[q] = ld_words<NT>(reinterpret_cast<const uint32_t*>(p) + q);
             }
         }
     }
 
+    template <bool NT = false>
     __device__ __forceinline__ void store(void* base, int64_t elem) const {
         if constexpr (!kWords) {
 #pragma unroll
@@ -83,15 +106,15 @@ struct Run {
             if constexpr (kBytes % 16 == 0) {
 #pragma unroll
                 for (int q = 0; q < kN / 4; ++q)
-                    reinterpret_cast<uint4*>(p)[q] =
-                        make_uint4(w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]);
+                    st_words<NT>(v4u{w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]},
+                                 reinterpret_cast<v4u*>(p) + q);
             } else if constexpr (kBytes % 8 == 0) {
 #pragma unroll
                 for (int q = 0; q < kN / 2; ++q)
-                    reinterpret_cast<uint2*>(p)[q] = make_uint2(w[2 * q], w[2 * q + 1]);
+                    st_words<NT>(v2u{w[2 * q], w[2 * q + 1]}, reinterpret_cast<v2u*>(p) + q);
             } else {
 #pragma unroll
-                for (int q = 0; q < kN; ++q) reinterpret_cast<uint32_t*>(p)[q] = w[q];
+                for (int q = 0; q < kN; ++q) st_words<NT>(w[q], reinterpret_cast<uint32_t*>(p) + q);
             }
         }
     }
@@ -264,7 +287,7 @@ __global__ __launch_bounds__(kConvBlock) void conv1d_update_kernel(ConvArgs a, i
     const int64_t b = gid / ncg;
     const int64_t c0 = cg * VEC;
     Run<IO, VEC * W> st;
-    st.load(a.state_in, (b * a.dim + c0) * W);
+    st.template load<kConvStateNt>(a.state_in, (b * a.dim + c0) * W);
     Run<IO, VEC> xin;
     xin.load(a.x, b * a.dim + c0);
     float wt[VEC][W], bs[VEC];
@@ -282,7 +305,7 @@ __global__ __launch_bounds__(kConvBlock) void conv1d_update_kernel(ConvArgs a, i
         for (int k = 0; k < W; ++k) pre = fmaf(wt[v][k], st.f32(v * W + k), pre);
         o.set(v, to_raw<IO>(conv_act<SILU>(pre)));
     }
-    st.store(a.state_out, (b * a.dim + c0) * W);
+    st.template store<kConvStateNt>(a.state_out, (b * a.dim + c0) * W);
     o.store(a.y, b * a.dim + c0);
 }
 
