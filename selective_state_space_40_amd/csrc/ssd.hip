@@ -42,6 +42,9 @@ namespace {
 constexpr int kQ = 64;   // tokens per chunk
 constexpr int kP = 64;   // channels per head
 constexpr int kSsdThreads = 256;
+// Cache policy of the y stores: non-temporal (y is written once and not
+// read back here).
+constexpr int kStoreNt = 2;
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
@@ -436,7 +439,7 @@ void ssd_fwd_kernel(SsdArgs a) {
                 __builtin_amdgcn_raw_buffer_store_b128(
                     __builtin_bit_cast(__attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t,
                                        make_uint4(ow[0], ow[1], ow[2], ow[3])),
-                    ry, ((16 * tb + r) * static_cast<int>(dim) + ocol) * 2, 0, 0);
+                    ry, ((16 * tb + r) * static_cast<int>(dim) + ocol) * 2, 0, kStoreNt);
             }
         }
         // nor this chunk's gate and input
