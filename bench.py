@@ -53,6 +53,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-channels", type=int, default=0,
                    help="channels of the CPU-baseline sample (0 = sized to ~10 s)")
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="the CPU baseline repeats its sample until this much wall time has "
+                        "gone by (a sample that takes longer runs once)")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="run only a plain 1 GiB device-to-device copy, for counter calibration")
     p.add_argument("--record-traffic", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV",
@@ -278,7 +281,7 @@ def main():
     clock = gpu_clock_sample(step)
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, sets[0], args.cpu_sample_channels, sp)
+        cpu = cpu_baseline(w, sets[0], args.cpu_sample_channels, sp, args.cpu_seconds)
 
     line = {
         "metric": METRIC,
@@ -454,7 +457,7 @@ def bench_backward(args, w):
     ops = backward_alu_ops(w, sp)
     tops = ops / sec / 1e12
     gbps = nbytes / sec / 1e9
-    cpu = None if args.no_cpu_baseline else cpu_baseline_backward(w, sets[0], sp)
+    cpu = None if args.no_cpu_baseline else cpu_baseline_backward(w, sets[0], sp, args.cpu_seconds)
     clock = gpu_clock_sample(step)
     line = {
         "metric": "backward scan elements/s (B*L*D, all input gradients, states recomputed)",
@@ -479,7 +482,23 @@ def bench_backward(args, w):
     print(json.dumps(line), flush=True)
 
 
-def cpu_baseline_backward(w, inp, softplus):
+def _oracle_passes(run, seconds):
+    """Run one oracle pass over the sample, then more until `seconds` of wall
+    time have gone by; returns (passes, seconds taken)."""
+    passes, t0 = 0, time.perf_counter()
+    while True:
+        run()
+        passes += 1
+        dt = time.perf_counter() - t0
+        if dt >= seconds:
+            return passes, dt
+
+
+def _passes_text(passes, dt):
+    return f"{passes} pass{'es' if passes > 1 else ''} in {dt:.1f} s"
+
+
+def cpu_baseline_backward(w, inp, softplus, seconds):
     """The fp64 oracle's backward pass on the host over a channel sample (the
     per-channel work is independent; dB and dC come out as partial sums)."""
     import torch
@@ -488,7 +507,9 @@ def cpu_baseline_backward(w, inp, softplus):
 
     orc = oracle.get()
     threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
-    channels = max(8, min(w.dim, int(3.0e6 * threads / (w.batch * w.seqlen))))
+    # one pass sized to at most ~`seconds` at ~2e6 elements/s per core
+    per_pass = max(seconds, 1.0) * 2.0e6 * threads
+    channels = max(8, min(w.dim, int(per_pass / (w.batch * w.seqlen))))
     idx = torch.arange(channels, device=inp["x"].device)
     sub = dict(x=inp["x"].index_select(2, idx), delta=inp["delta"].index_select(2, idx),
                A=inp["A"].index_select(0, idx), B=inp["B"], C=inp["C"],
@@ -496,14 +517,13 @@ def cpu_baseline_backward(w, inp, softplus):
                dy=inp["dy"].index_select(2, idx),
                delta_bias=inp["delta_bias"].index_select(0, idx) if softplus else None)
     host = {k: (oracle._f64(v) if v is not None else None) for k, v in sub.items()}
-    t0 = time.perf_counter()
-    orc.scan_bwd(**host, delta_softplus=softplus)
-    dt = time.perf_counter() - t0
-    elems = w.batch * w.seqlen * channels
+    passes, dt = _oracle_passes(lambda: orc.scan_bwd(**host, delta_softplus=softplus), seconds)
+    elems = w.batch * w.seqlen * channels * passes
     return {"value": elems / dt, "unit": "elements/s",
             "cores": min(threads, w.batch), "kind": "oracle",
             "sample": f"{w.name}: all {w.batch} batch rows x {w.seqlen} tokens x first "
-                      f"{channels} of {w.dim} channels, fp64 (rows in parallel), {dt:.2f} s"}
+                      f"{channels} of {w.dim} channels, fp64 (rows in parallel), "
+                      f"{_passes_text(passes, dt)}"}
 
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix cores, MI355X
@@ -559,7 +579,7 @@ def bench_ssd(args, w):
     hbm_frac = gbps / HBM_PEAK_GBPS
     bound = "mfma" if flops / (MFMA_BF16_PEAK_TFLOPS * 1e12) > nbytes / (HBM_PEAK_GBPS * 1e9) \
         else "hbm"
-    cpu = None if args.no_cpu_baseline else cpu_baseline_ssd(w, sets[0])
+    cpu = None if args.no_cpu_baseline else cpu_baseline_ssd(w, sets[0], args.cpu_seconds)
     clock = gpu_clock_sample(step)
     line = {
         "metric": "Mamba-2 dual-form scan elements/s (B*L*D) and achieved HBM GB/s",
@@ -586,7 +606,7 @@ def bench_ssd(args, w):
     print(json.dumps(line), flush=True)
 
 
-def cpu_baseline_ssd(w, inp):
+def cpu_baseline_ssd(w, inp, seconds):
     """The fp64 oracle on the host over a sample of heads (heads are
     independent), all rows and tokens."""
     import torch
@@ -595,20 +615,20 @@ def cpu_baseline_ssd(w, inp):
 
     orc = oracle.get()
     threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
-    nh = max(1, min(w.nheads, int(2.0e6 * threads / (w.batch * w.seqlen * w.headdim))))
+    # one pass sized to at most ~`seconds` at ~4e6 elements/s per core
+    per_pass = max(seconds, 1.0) * 4.0e6 * threads
+    nh = max(1, min(w.nheads, int(per_pass / (w.batch * w.seqlen * w.headdim))))
     hix = torch.arange(nh, device=inp["x"].device)
     chans = torch.arange(nh * w.headdim, device=inp["x"].device)
     sub = dict(x=inp["x"].index_select(2, chans), dt=inp["dt"].index_select(2, hix),
                A=inp["A"].index_select(0, hix), B=inp["B"], C=inp["C"],
                D=inp["D"].index_select(0, chans), z=inp["z"].index_select(2, chans), h0=None)
     host = {k: (oracle._f64(v) if v is not None else None) for k, v in sub.items()}
-    t0 = time.perf_counter()
-    orc.ssd_fwd(**host, headdim=w.headdim)
-    dt = time.perf_counter() - t0
-    elems = w.batch * w.seqlen * nh * w.headdim
+    passes, dt = _oracle_passes(lambda: orc.ssd_fwd(**host, headdim=w.headdim), seconds)
+    elems = w.batch * w.seqlen * nh * w.headdim * passes
     return {"value": elems / dt, "unit": "elements/s", "cores": threads, "kind": "oracle",
             "sample": f"{w.name}: all {w.batch} rows x {w.seqlen} tokens x first {nh} of "
-                      f"{w.nheads} heads, fp64, {dt:.2f} s"}
+                      f"{w.nheads} heads, fp64, {_passes_text(passes, dt)}"}
 
 
 def conv_bytes(w, state_in):
@@ -734,7 +754,7 @@ def bench_conv(args, w):
     elems = w.batch * w.seqlen * w.dim
     nbytes = conv_bytes(w, sets[0]["state_in"] is not None)
     gbps = nbytes / sec / 1e9
-    cpu = None if args.no_cpu_baseline else cpu_baseline_conv(w, sets[0])
+    cpu = None if args.no_cpu_baseline else cpu_baseline_conv(w, sets[0], args.cpu_seconds)
     clock = gpu_clock_sample(step)
     line = {
         "metric": "short causal convolution elements/s (B*L*D) and achieved HBM GB/s",
@@ -812,7 +832,7 @@ def bench_conv_decode(args, w):
     print(json.dumps(line), flush=True)
 
 
-def cpu_baseline_conv(w, inp):
+def cpu_baseline_conv(w, inp, seconds):
     """The fp64 oracle's convolution on the host over the whole workload
     (cheap enough to run in full)."""
     import oracle
@@ -820,15 +840,15 @@ def cpu_baseline_conv(w, inp):
     orc = oracle.get()
     threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
     host = {k: (oracle._f64(v) if v is not None else None) for k, v in inp.items()}
-    t0 = time.perf_counter()
-    orc.conv1d_fwd(host["x"], host["weight"], host["bias"], host["state_in"])
-    dt = time.perf_counter() - t0
-    elems = w.batch * w.seqlen * w.dim
+    passes, dt = _oracle_passes(
+        lambda: orc.conv1d_fwd(host["x"], host["weight"], host["bias"], host["state_in"]),
+        seconds)
+    elems = w.batch * w.seqlen * w.dim * passes
     return {"value": elems / dt, "unit": "elements/s", "cores": threads, "kind": "oracle",
-            "sample": f"{w.name}: the whole workload, fp64, {dt:.2f} s"}
+            "sample": f"{w.name}: the whole workload, fp64, {_passes_text(passes, dt)}"}
 
 
-def cpu_baseline(w, inp, channels, softplus=False):
+def cpu_baseline(w, inp, channels, softplus=False, seconds=10.0):
     """The fp64 oracle, as it is, on the host over a channel sample of the
     same workload (all batch rows, all tokens)."""
     import numpy as np
@@ -839,9 +859,9 @@ def cpu_baseline(w, inp, channels, softplus=False):
     orc = oracle.get()
     threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
     if channels <= 0:
-        # about 10 s at ~1e7 elements/s per core
+        # one pass sized to at most ~`seconds` at ~1e7 elements/s per core
         per_core = 1.0e7
-        channels = int(10.0 * per_core * threads / (w.batch * w.seqlen))
+        channels = int(max(seconds, 1.0) * per_core * threads / (w.batch * w.seqlen))
         channels = max(8, min(w.dim, channels))
     idx = torch.arange(channels, device=inp["x"].device)
     sub = {k: v for k, v in dict(
@@ -850,13 +870,11 @@ def cpu_baseline(w, inp, channels, softplus=False):
         z=inp["z"].index_select(2, idx), h0=None,
         delta_bias=inp["delta_bias"].index_select(0, idx) if softplus else None).items()}
     host = {k: (oracle._f64(v) if v is not None else None) for k, v in sub.items()}
-    t0 = time.perf_counter()
-    orc.scan_fwd(**host, delta_softplus=softplus)
-    dt = time.perf_counter() - t0
-    elems = w.batch * w.seqlen * channels
+    passes, dt = _oracle_passes(lambda: orc.scan_fwd(**host, delta_softplus=softplus), seconds)
+    elems = w.batch * w.seqlen * channels * passes
     return {"value": elems / dt, "unit": "elements/s", "cores": threads, "kind": "oracle",
             "sample": f"{w.name}: all {w.batch} batch rows x {w.seqlen} tokens x first "
-                      f"{channels} of {w.dim} channels, fp64, {dt:.2f} s"}
+                      f"{channels} of {w.dim} channels, fp64, {_passes_text(passes, dt)}"}
 
 
 if __name__ == "__main__":
