@@ -39,6 +39,8 @@ def parse():
     p.add_argument("--workload", default="mamba28b_layer")
     p.add_argument("--chunk-len", type=int, default=0, help="0 = the library's automatic plan")
     p.add_argument("--state-split", type=int, default=0, help="0 = the library's automatic plan")
+    p.add_argument("--carry", choices=("auto", "rerun", "repair"), default="auto",
+                   help="how chunks of a cut sequence join (auto = the library's plan)")
     p.add_argument("--batch", type=int, default=0, help="override the workload's batch (0 = keep)")
     p.add_argument("--dim", type=int, default=0, help="override the workload's channels (0 = keep)")
     p.add_argument("--backward", action="store_true",
@@ -216,12 +218,14 @@ def main():
     sets = [W.generate_scan(w, device=dev, seed=w.seed + 101 * i, raw_delta=sp) for i in range(2)]
     y = torch.empty_like(sets[0]["x"])
     hL = torch.empty(w.batch, w.dim, w.dstate, dtype=torch.float32, device=dev)
+    carry = {"auto": ms.CARRY_AUTO, "rerun": ms.CARRY_RERUN, "repair": ms.CARRY_REPAIR}[args.carry]
 
     def step(i):
         inp = sets[i % 2]
         ms.scan_fwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"],
                     inp["h0"], delta_bias=inp.get("delta_bias"), delta_softplus=sp,
-                    chunk_len=args.chunk_len, state_split=args.state_split, out=y, state_out=hL)
+                    chunk_len=args.chunk_len, state_split=args.state_split, carry=carry,
+                    out=y, state_out=hL)
 
     _spin_up(step, args.spin_up)
     for i in range(args.warmup):
@@ -242,9 +246,9 @@ def main():
     ms_per_step = ev0.elapsed_time(ev1) / args.steps
 
     # the plan the library chose, for the record
-    chunk_len, split, _ = ms.resolve_plan(w.batch, w.seqlen, w.dim, w.dstate,
-                                          W.io_torch_dtype(w.io), args.chunk_len,
-                                          args.state_split)
+    plan = ms.resolve_plan(w.batch, w.seqlen, w.dim, w.dstate, W.io_torch_dtype(w.io),
+                           args.chunk_len, args.state_split, carry)
+    chunk_len, split = plan.chunk_len, plan.state_split
     nchunks = -(-w.seqlen // chunk_len)
 
     elems = w.batch * w.seqlen * w.dim
@@ -258,7 +262,8 @@ def main():
     # Dominant kernel: the output pass (chunk_output_kernel). With a single
     # chunk the step is exactly that one launch, so the event time per step
     # is its launch duration; with several chunks the step also holds the
-    # summary and carry passes and the figure covers the whole step.
+    # carry pass and either the summary pass or the head reruns, and the
+    # figure covers the whole step.
     hbm_frac = gbps / HBM_PEAK_GBPS
     alu_frac = tops / ALU_PEAK_TOPS
     bound = "alu" if ops / (ALU_PEAK_TOPS * 1e12) > bytes_alg / (HBM_PEAK_GBPS * 1e9) else "hbm"
@@ -299,6 +304,8 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "seqlen": w.seqlen, "dim": w.dim,
                    "dstate": w.dstate, "io_dtype": w.io, "chunk_len": int(chunk_len),
                    "nchunks": int(nchunks), "state_split": int(split),
+                   "carry": (None if nchunks == 1 else
+                             {ms.CARRY_RERUN: "rerun", ms.CARRY_REPAIR: "repair"}[plan.carry]),
                    "delta_activation": "bias + softplus in the kernels" if sp else
                                        "none (delta passed activated)",
                    "parallelism": "single GPU"},

@@ -69,28 +69,54 @@ typedef enum mamba_dtype {
 } mamba_dtype;
 
 /*
+ * How chunks of a cut sequence learn the state entering them.
+ *
+ * MAMBA_CARRY_RERUN   a summary pass computes every chunk's (decay product,
+ *                     end state) pair, an associative combine of the pairs
+ *                     gives the state entering each chunk (the "parallel
+ *                     scan" of section "A Scan on the Chip"), and the output
+ *                     pass reruns every chunk from its entering state.
+ * MAMBA_CARRY_REPAIR  every chunk runs once from a zero state (the first
+ *                     from h0), writing y and its pair; the combine gives the
+ *                     entering states and hL; each later chunk then reruns
+ *                     from its entering state only until exp(A * sum of
+ *                     delta since the chunk start) is at most 2^-32 for every
+ *                     state of its 64-channel group, and keeps the zero-start
+ *                     y after that. The outputs it keeps differ from the
+ *                     rerun ones by less than 2^-32 * sum_n |C[n] h_in[n]|
+ *                     (h_in: the entering state), below fp32 rounding of
+ *                     that readout. The rerun length depends on the data: a
+ *                     chunk whose decay never gets there (A >= 0, delta = 0,
+ *                     a non-finite entering state) is rerun whole.
+ */
+typedef enum mamba_carry {
+    MAMBA_CARRY_AUTO = 0,
+    MAMBA_CARRY_RERUN = 1,
+    MAMBA_CARRY_REPAIR = 2
+} mamba_carry;
+
+/*
  * How ssm_scan_fwd divides its work over the GPU. A NULL plan, or a zero
  * field, lets the library choose from the shape and the current device's
- * compute-unit count; every choice gives the same result up to rounding.
+ * compute-unit count; every choice gives the same result up to rounding
+ * (and, with MAMBA_CARRY_REPAIR, the bound stated above).
  *
  * chunk_len    tokens per parallel chunk. Each sequence is cut into chunks
- *              that run in parallel; a summary pass computes every chunk's
- *              (decay product, end state) pair, an associative combine of the
- *              pairs gives the state entering each chunk (the "parallel scan"
- *              of section "A Scan on the Chip"), and the output pass reruns
- *              each chunk from its entering state. A chunk_len of seqlen or
- *              more means one chunk and a single pass. The library may
- *              shorten a chunk so a chunk of one channel group spans less
- *              than 4 GiB.
+ *              that run in parallel and are joined as `carry` says. A
+ *              chunk_len of seqlen or more means one chunk and a single
+ *              pass. The library may shorten a chunk so a chunk of one
+ *              channel group spans less than 4 GiB.
  * state_split  waves sharing the dstate states of each channel: 1, 2, 4 or
  *              8. Values above 1 need dstate of 4, 8 or 16 divisible by the
  *              split.
- * reserved     must be 0.
+ * carry        a mamba_carry value; automatic picks MAMBA_CARRY_REPAIR for
+ *              chunks of 4096 tokens or more, MAMBA_CARRY_RERUN otherwise.
+ *              Ignored with one chunk. Other values: MAMBA_ERR_INVALID_ARG.
  */
 typedef struct mamba_scan_plan {
     int64_t chunk_len;
     int32_t state_split;
-    int32_t reserved;
+    int32_t carry;
 } mamba_scan_plan;
 
 /*

@@ -24,13 +24,15 @@ x, y (batch, L, dim), weight (dim, W) fp32, bias (dim,) fp32 and a state of
 the last W inputs (batch, dim, W) in the dtype of x.
 x, delta, z, B and C share one dtype, float32 or bfloat16, and y has it too.
 """
+import collections
 import ctypes
 import os
 
 import torch
 
 __all__ = ["scan_fwd", "scan_bwd", "ssd_fwd", "state_update", "conv1d_fwd", "conv1d_update", "workspace_size", "resolve_plan", "library_path",
-           "load_library", "MambaScanError", "MAX_DSTATE", "ScanPlan", "ScanOptions"]
+           "load_library", "MambaScanError", "MAX_DSTATE", "ScanPlan", "ScanOptions", "Plan",
+           "CARRY_AUTO", "CARRY_RERUN", "CARRY_REPAIR"]
 
 MAX_DSTATE = 16
 _DTYPES = {torch.float32: 0, torch.bfloat16: 1}
@@ -39,11 +41,20 @@ _LIB = None
 _WS = {}
 
 
+CARRY_AUTO, CARRY_RERUN, CARRY_REPAIR = 0, 1, 2
+
+
 class ScanPlan(ctypes.Structure):
-    """mamba_scan_plan: chunk_len (tokens per parallel chunk) and state_split
-    (waves sharing one channel's states); 0 means automatic."""
+    """mamba_scan_plan: chunk_len (tokens per parallel chunk), state_split
+    (waves sharing one channel's states) and carry (CARRY_RERUN: summary pass
+    and a rerun of every chunk; CARRY_REPAIR: one pass from zero states and a
+    rerun of each chunk's head while the entering state still counts); 0
+    means automatic."""
     _fields_ = [("chunk_len", ctypes.c_int64), ("state_split", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("carry", ctypes.c_int32)]
+
+
+Plan = collections.namedtuple("Plan", "chunk_len state_split carry workspace_bytes")
 
 
 class ScanOptions(ctypes.Structure):
@@ -137,23 +148,26 @@ def _options(delta_bias, delta_softplus):
                                     1 if delta_softplus else 0, 0))
 
 
-def resolve_plan(batch, seqlen, dim, dstate, dtype=torch.bfloat16, chunk_len=0, state_split=0):
-    """The plan ssm_scan_fwd uses for this shape, and its scratch bytes:
-    returns (chunk_len, state_split, workspace_bytes). Automatic fields query
-    the current device."""
-    req = ScanPlan(chunk_len, state_split, 0)
+def resolve_plan(batch, seqlen, dim, dstate, dtype=torch.bfloat16, chunk_len=0, state_split=0,
+                 carry=CARRY_AUTO):
+    """The plan ssm_scan_fwd uses for this shape, and its scratch bytes, as a
+    Plan (chunk_len, state_split, carry, workspace_bytes). Automatic fields
+    query the current device."""
+    req = ScanPlan(chunk_len, state_split, carry)
     out = ScanPlan(0, 0, 0)
     nbytes = ctypes.c_size_t(0)
     _check(load_library().ssm_scan_fwd_workspace_size(batch, seqlen, dim, dstate, _DTYPES[dtype],
                                                       ctypes.byref(req), ctypes.byref(out),
                                                       ctypes.byref(nbytes)),
            "ssm_scan_fwd_workspace_size")
-    return out.chunk_len, out.state_split, nbytes.value
+    return Plan(out.chunk_len, out.state_split, out.carry, nbytes.value)
 
 
-def workspace_size(batch, seqlen, dim, dstate, dtype=torch.bfloat16, chunk_len=0, state_split=0):
+def workspace_size(batch, seqlen, dim, dstate, dtype=torch.bfloat16, chunk_len=0, state_split=0,
+                   carry=CARRY_AUTO):
     """Scratch bytes ssm_scan_fwd needs for this shape and plan."""
-    return resolve_plan(batch, seqlen, dim, dstate, dtype, chunk_len, state_split)[2]
+    return resolve_plan(batch, seqlen, dim, dstate, dtype, chunk_len, state_split,
+                        carry).workspace_bytes
 
 
 def _workspace(device, nbytes, kind="fwd"):
@@ -168,13 +182,14 @@ def _workspace(device, nbytes, kind="fwd"):
 
 
 def scan_fwd(x, delta, A, B, C, D=None, z=None, h0=None, *, delta_bias=None,
-             delta_softplus=False, chunk_len=0, state_split=0, return_state=True, out=None,
-             state_out=None):
+             delta_softplus=False, chunk_len=0, state_split=0, carry=CARRY_AUTO,
+             return_state=True, out=None, state_out=None):
     """Selective scan over whole sequences; returns (y, hL) (hL is None when
     return_state is False). `delta_bias` (dim,) fp32 is added to delta and
     `delta_softplus` applies softplus after it, inside the kernels.
-    `chunk_len` > 0 forces the parallel chunk length and `state_split` > 0
-    the number of waves sharing a channel's states."""
+    `chunk_len` > 0 forces the parallel chunk length, `state_split` > 0 the
+    number of waves sharing a channel's states and `carry` how chunks join
+    (CARRY_RERUN or CARRY_REPAIR)."""
     lib = load_library()
     if x.dim() != 3:
         raise ValueError("x must be (batch, L, dim)")
@@ -203,9 +218,9 @@ def scan_fwd(x, delta, A, B, C, D=None, z=None, h0=None, *, delta_bias=None,
         hL = state_out if state_out is not None else torch.empty(batch, dim, dstate,
                                                                  dtype=torch.float32, device=dev)
         _need(hL, "state_out", (batch, dim, dstate), torch.float32, dev)
-    plan = ScanPlan(chunk_len, state_split, 0)
+    plan = ScanPlan(chunk_len, state_split, carry)
     with torch.cuda.device(dev):
-        nbytes = workspace_size(batch, seqlen, dim, dstate, dt, chunk_len, state_split)
+        nbytes = workspace_size(batch, seqlen, dim, dstate, dt, chunk_len, state_split, carry)
         ws = _workspace(dev, nbytes)
         st = lib.ssm_scan_fwd(batch, seqlen, dim, dstate, _DTYPES[dt], _ptr(x), _ptr(delta),
                               _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0), _ptr(y),

@@ -79,7 +79,17 @@ int check_shape(int64_t batch, int64_t seqlen, int64_t dim, int dstate, int dtyp
 // per SIMD is the sequence cut, into enough chunks for about six waves per
 // SIMD. Chunks are never shorter than kMinChunk tokens. (Measured on MI355X
 // for the Mamba-130M and Mamba-2.8B layer shapes.)
+//
+// Chunks of kRepairMinChunk tokens or more join through the repaired carry:
+// its rerun covers only a chunk's head while the entering state still
+// counts, which on long chunks is a small part of the summary pass it
+// replaces (the million-token scan: about 1,100 of 21,848 tokens). Short
+// chunks keep the summary pass, since a rerun that covers the whole chunk
+// costs more than the summary.
 constexpr int kPreferredSplit = 4;
+constexpr int64_t kRepairMinChunk = 4096;
+static_assert(mamba::kCarryRerun == MAMBA_CARRY_RERUN && mamba::kCarryRepair == MAMBA_CARRY_REPAIR,
+              "internal carry codes follow the public enum");
 constexpr int64_t kWavesPerSimdNoChunk = 2;
 constexpr int64_t kWavesPerSimdChunked = 6;
 constexpr int64_t kMinChunk = 64;
@@ -88,13 +98,16 @@ int make_plan(int64_t batch, int64_t seqlen, int64_t dim, int dstate, int dtype,
               const mamba_scan_plan* req, ScanPlan* plan) {
     int64_t len = req ? req->chunk_len : 0;
     int split = req ? req->state_split : 0;
-    if (req && req->reserved != 0) return MAMBA_ERR_INVALID_ARG;
+    const int carry = req ? req->carry : MAMBA_CARRY_AUTO;
+    if (carry != MAMBA_CARRY_AUTO && carry != MAMBA_CARRY_RERUN && carry != MAMBA_CARRY_REPAIR)
+        return MAMBA_ERR_INVALID_ARG;
     if (len < 0 || split < 0) return MAMBA_ERR_INVALID_ARG;
     if (split != 0 && !mamba::split_supported(dstate, split)) return MAMBA_ERR_UNSUPPORTED;
     if (seqlen == 0 || batch == 0 || dim == 0) {
         plan->chunk_len = seqlen;
         plan->nchunks = 1;
         plan->state_split = split ? split : 1;
+        plan->carry = carry != MAMBA_CARRY_AUTO ? carry : MAMBA_CARRY_RERUN;
         plan->workspace_bytes = 0;
         return MAMBA_OK;
     }
@@ -135,6 +148,10 @@ int make_plan(int64_t batch, int64_t seqlen, int64_t dim, int dstate, int dtype,
     plan->chunk_len = len;
     plan->nchunks = nchunks;
     plan->state_split = split;
+    plan->carry = carry != MAMBA_CARRY_AUTO
+                      ? carry
+                      : (nchunks > 1 && len >= kRepairMinChunk ? MAMBA_CARRY_REPAIR
+                                                               : MAMBA_CARRY_RERUN);
     plan->workspace_bytes = mamba::scan_workspace_bytes(batch, dim, dstate, nchunks);
     return MAMBA_OK;
 }
@@ -156,7 +173,7 @@ int ssm_scan_fwd_workspace_size(int64_t batch, int64_t seqlen, int64_t dim, int 
     if (resolved != nullptr) {
         resolved->chunk_len = plan.chunk_len;
         resolved->state_split = plan.state_split;
-        resolved->reserved = 0;
+        resolved->carry = plan.carry;
     }
     return MAMBA_OK;
 }

@@ -26,10 +26,18 @@ enum IoType : int { kIoF32 = 0, kIoBF16 = 1 };
 
 // How one ssm_scan_fwd call is split: the sequence is cut into `nchunks`
 // chunks of `chunk_len` tokens (the last one may be shorter).
+// How chunks learn the state entering them (mamba_carry in the public
+// header): a summary pass and a rerun of every chunk, or one pass from zero
+// states and a rerun of each chunk's head only while the entering state
+// still counts.
+constexpr int kCarryRerun = 1;
+constexpr int kCarryRepair = 2;
+
 struct ScanPlan {
     int64_t chunk_len = 0;
     int64_t nchunks = 1;
     int state_split = 1;         // waves sharing the states of one channel
+    int carry = kCarryRerun;     // kCarryRerun or kCarryRepair (nchunks > 1)
     size_t workspace_bytes = 0;  // 0 when nchunks == 1
 };
 
@@ -152,12 +160,10 @@ hipError_t launch_scan(const ScanArgs& a, const ScanPlan& plan, void* workspace,
                        hipStream_t stream);
 
 // The chunked scan for one (I/O dtype, delta softplus) pair; each pair is
-// compiled in its own translation unit (scan_variant.hip). With states_only
-// it queues only the summary and carry passes, which leave the state
-// entering every chunk in the workspace.
+// compiled in its own translation unit (scan_variant.hip).
 template <int IO, bool SP>
 hipError_t launch_scan_variant(const ScanArgs& a, const ScanPlan& plan, void* workspace,
-                               hipStream_t stream, bool states_only);
+                               hipStream_t stream);
 
 // Queue the convolution over whole sequences (update == false) or its
 // decode step (update == true). Arguments are already validated.

@@ -171,10 +171,10 @@ hipError_t launch_scan(const ScanArgs& a, const ScanPlan& plan, void* workspace,
     }
     const bool sp = a.delta_softplus != 0;
     if (a.io == kIoF32)
-        return sp ? launch_scan_variant<kIoF32, true>(a, plan, workspace, stream, false)
-                  : launch_scan_variant<kIoF32, false>(a, plan, workspace, stream, false);
-    return sp ? launch_scan_variant<kIoBF16, true>(a, plan, workspace, stream, false)
-              : launch_scan_variant<kIoBF16, false>(a, plan, workspace, stream, false);
+        return sp ? launch_scan_variant<kIoF32, true>(a, plan, workspace, stream)
+                  : launch_scan_variant<kIoF32, false>(a, plan, workspace, stream);
+    return sp ? launch_scan_variant<kIoBF16, true>(a, plan, workspace, stream)
+              : launch_scan_variant<kIoBF16, false>(a, plan, workspace, stream);
 }
 
 hipError_t launch_state_update(const DecodeArgs& a, hipStream_t stream) {

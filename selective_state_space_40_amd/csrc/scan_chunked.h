@@ -37,6 +37,20 @@
 // of section "A Scan on the Chip"). P is formed from a chunk-local sum of
 // delta, never from differences of long prefix sums.
 //
+// With long chunks the carry can instead be repaired where it matters. Pass
+// 1 then runs every chunk once from a zero state (chunk 0 from h0) and
+// writes y as well as the summary pair; the carry pass folds the pairs
+// through the last chunk, which gives hL too. The true state of a chunk
+// differs from its zero-start state by P_t (.) h_in, where P_t =
+// exp(A * sum of delta since the chunk start) only shrinks along the chunk
+// (delta > 0, A < 0), so pass 2 reruns each later chunk from its entering
+// state only until P_t <= 2^-32 for every state of the workgroup, and the
+// zero-start outputs stand from there on: what they leave out is below
+// 2^-32 * sum_n |C[n] h_in[n]|, under the fp32 rounding of that readout.
+// The stopping test is made on the data, so the cost depends on the decay;
+// where the weight never falls (A >= 0, delta = 0, NaN) pass 2 reruns the
+// whole chunk, as the two-pass form does.
+//
 // This header is the body of scan_variant.hip, which is compiled once per
 // (I/O dtype, delta activation) pair so the variants build in parallel.
 #pragma once
@@ -270,9 +284,9 @@ __device__ __forceinline__ void stage_tokens(float2* dtdu, int w, const Tile<S>&
 // per-token inputs come from LDS and the readout over the wave's states is
 // kept per token in part[]; with S == 1 the wave holds every state, takes
 // its inputs straight from its registers (delta already activated in dtv)
-// and finishes and stores each token right away. Without OUTPUT the sum of
-// delta accumulates in dsum.
-template <int N, int S, int IO, bool OUTPUT, bool HAS_D, bool HAS_Z, bool FULL>
+// and finishes and stores each token right away. With SUM (always without
+// OUTPUT) the sum of delta accumulates in dsum.
+template <int N, int S, int IO, bool OUTPUT, bool SUM, bool HAS_D, bool HAS_Z, bool FULL>
 __device__ __forceinline__ void compute_tile(const ChunkIo& io, const float* bcs_w,
                                              const float2* dtdu, const Tile<S>& r,
                                              const float (&dtv)[TT / S], int tile, int cnt, const float (&A2)[Split<N, S>::NPW],
@@ -336,6 +350,7 @@ __device__ __forceinline__ void compute_tile(const ChunkIo& io, const float* bcs
                                       static_cast<uint32_t>(tile * TT + j) * io.row_bytes, p);
                     }
                     part[j] = p;
+                    if constexpr (SUM) dsum += dt;
                 } else {
 #pragma unroll
                     for (int k = 0; k < NPW; ++k) {
@@ -392,7 +407,20 @@ struct ScanLds {
     float bcs[2][2 * BcStage<N, S>::kSlots];
     float2 dtdu[2][S > 1 ? TT * kWave : 1];
     float red[2][S > 1 ? S * TT * kWave : 1];
+    int vote[2][S];  // pass 2 of the repaired carry: wave w's lanes are all done
 };
+
+// What one run over a chunk computes.
+enum Pass : int {
+    kPassSummary = 0,  // end state and sum of delta, no y
+    kPassOutput = 1,   // y from the given entering state
+    kPassLocal = 2,    // y, and the sum of delta for the chunk's decay product
+    kPassFixup = 3,    // y until the entering state's weight is negligible
+};
+
+// Pass 2 of the repaired carry stops once exp2(A2 * sum of delta) is at most
+// 2^-kFixupLog2 for every state of the workgroup.
+constexpr float kFixupLog2 = 32.0f;
 
 // All `ntok` tokens of one chunk for one wave. Two register tiles alternate
 // and swap roles without register copies. With S > 1 a tile's raw inputs
@@ -412,13 +440,23 @@ struct ScanLds {
 // per-token inputs into LDS buffers (i+1)&1; barrier; finalise this wave's
 // tokens of tile i. Every LDS buffer is rewritten only after a barrier that
 // follows its last read.
-template <int N, int S, int IO, bool SP, bool OUTPUT, bool HAS_D, bool HAS_Z>
+//
+// kPassFixup also votes per tile: before the barrier each wave records in
+// vote[i&1] whether all its lanes have exp2(a2max * dsum) <= 2^-kFixupLog2
+// (a2max: the lane's largest A2), and after it every wave reads all S votes
+// and the whole workgroup leaves together once they agree; the loads still
+// in flight are dropped. Without kPassFixup the steps return false at
+// compile time and the loop is as before.
+template <int N, int S, int IO, bool SP, int PASS, bool HAS_D, bool HAS_Z>
 __device__ __forceinline__ void scan_chunk(const ChunkIo& io, const BcIo& bcio, float dbias,
                                            int ntok, int w, int n0,
                                            ScanLds<N, S>& lds,
                                            const float (&A2)[Split<N, S>::NPW],
                                            float (&h)[Split<N, S>::NPW], float dskip,
-                                           float& dsum) {
+                                           float a2max, float& dsum) {
+    constexpr bool OUTPUT = PASS != kPassSummary;
+    constexpr bool SUM = PASS != kPassOutput;
+    constexpr bool FIX = PASS == kPassFixup;
     constexpr bool LOAD_Z = OUTPUT && HAS_Z;
     constexpr int KP = BcStage<N, S>::kPerLane;
     const int ntiles = (ntok + TT - 1) / TT;
@@ -433,7 +471,7 @@ __device__ __forceinline__ void scan_chunk(const ChunkIo& io, const BcIo& bcio, 
     // staged at its end (the same registers when AHEAD == 1)
     auto step = [&](auto full_tag, int i, Tile<S>& cur, const Epilogue<S>& ec, Tile<S>& nxt,
                     Epilogue<S>& en, uint32_t (&bf)[KP], uint32_t (&cf)[KP],
-                    const uint32_t (&bs)[KP], const uint32_t (&cs)[KP]) {
+                    const uint32_t (&bs)[KP], const uint32_t (&cs)[KP]) -> bool {
         constexpr bool FULL = decltype(full_tag)::value;
         const int ifetch = min(i + AHEAD, ntiles - 1);
         // The B/C run is issued first and kept first (scheduling fences), so
@@ -446,13 +484,18 @@ __device__ __forceinline__ void scan_chunk(const ChunkIo& io, const BcIo& bcio, 
         const int cnt = FULL ? TT : ntok - i * TT;
         float part[TT], dtv[TT / S];
         if constexpr (S == 1) delta_tile<S, IO, SP>(cur, dbias, dtv);
-        compute_tile<N, S, IO, OUTPUT, HAS_D, HAS_Z, FULL>(io, lds.bcs[i & 1] + n0,
-                                                           lds.dtdu[i & 1], cur, dtv, i, cnt, A2,
-                                                           h, dskip, part, dsum);
+        compute_tile<N, S, IO, OUTPUT, SUM, HAS_D, HAS_Z, FULL>(io, lds.bcs[i & 1] + n0,
+                                                                lds.dtdu[i & 1], cur, dtv, i, cnt,
+                                                                A2, h, dskip, part, dsum);
         if constexpr (OUTPUT && S > 1) {
             float* mine = lds.red[i & 1] + w * TT * kWave + lane;
 #pragma unroll
             for (int j = 0; j < TT; ++j) mine[j * kWave] = part[j];
+        }
+        if constexpr (FIX) {
+            // a NaN sum compares false and keeps the lane going
+            const bool done = dsum * a2max <= -kFixupLog2;
+            lds.vote[i & 1][w] = __builtin_amdgcn_ballot_w64(!done) == 0 ? 1 : 0;
         }
         stage_bc<N, S, IO>(lds.bcs[(i + 1) & 1], bs, cs);
         if constexpr (S > 1)
@@ -461,16 +504,24 @@ __device__ __forceinline__ void scan_chunk(const ChunkIo& io, const BcIo& bcio, 
         __syncthreads();
         if constexpr (OUTPUT && S > 1)
             finalize_tile<S, IO, HAS_Z, FULL>(io, lds.red[i & 1], w, i, cnt, ec);
+        if constexpr (FIX) {
+            int all = 1;
+#pragma unroll
+            for (int v = 0; v < S; ++v) all &= lds.vote[i & 1][v];
+            return all != 0;
+        } else {
+            return false;
+        }
     };
     // even steps fetch into (bra, cra) and stage (brb, crb), odd steps the
     // other way round; with AHEAD == 1 every step fetches and stages (bra, cra)
-    auto even = [&](auto tag, int i) {
-        if constexpr (AHEAD == 2) step(tag, i, ta, ea, tb, eb, bra, cra, brb, crb);
-        else step(tag, i, ta, ea, tb, eb, bra, cra, bra, cra);
+    auto even = [&](auto tag, int i) -> bool {
+        if constexpr (AHEAD == 2) return step(tag, i, ta, ea, tb, eb, bra, cra, brb, crb);
+        else return step(tag, i, ta, ea, tb, eb, bra, cra, bra, cra);
     };
-    auto odd = [&](auto tag, int i) {
-        if constexpr (AHEAD == 2) step(tag, i, tb, eb, ta, ea, brb, crb, bra, cra);
-        else step(tag, i, tb, eb, ta, ea, bra, cra, bra, cra);
+    auto odd = [&](auto tag, int i) -> bool {
+        if constexpr (AHEAD == 2) return step(tag, i, tb, eb, ta, ea, brb, crb, bra, cra);
+        else return step(tag, i, tb, eb, ta, ea, bra, cra, bra, cra);
     };
     using Full = std::integral_constant<bool, true>;
     using Ragged = std::integral_constant<bool, false>;
@@ -491,11 +542,11 @@ __device__ __forceinline__ void scan_chunk(const ChunkIo& io, const BcIo& bcio, 
     __syncthreads();
     int i = 0;
     for (; i + 2 <= nfull; i += 2) {
-        even(Full{}, i);
-        odd(Full{}, i + 1);
+        if (even(Full{}, i)) return;
+        if (odd(Full{}, i + 1)) return;
     }
     if (i < nfull) {
-        even(Full{}, i);
+        if (even(Full{}, i)) return;
         if (nfull < ntiles) odd(Ragged{}, i + 1);
     } else if (nfull < ntiles) {
         even(Ragged{}, i);
@@ -503,9 +554,10 @@ __device__ __forceinline__ void scan_chunk(const ChunkIo& io, const BcIo& bcio, 
 }
 
 struct ChunkGrid {
-    int64_t nblk_d;     // channel groups per batch row
-    int64_t nchunks;    // chunks per sequence
-    int64_t chunk_len;  // tokens per chunk
+    int64_t nblk_d;           // channel groups per batch row
+    int64_t nchunks;          // chunks per sequence the grid covers
+    int64_t chunk_len;        // tokens per chunk
+    int64_t first_chunk = 0;  // sequence chunk of the grid's chunk 0
 };
 
 __device__ __forceinline__ void decode_block(const ChunkGrid& g, int64_t blk, int64_t& dblk,
@@ -540,6 +592,7 @@ __device__ __forceinline__ WaveSlot wave_slot(const ScanArgs& a, const ChunkGrid
     WaveSlot s;
     int64_t dblk;
     decode_block(g, blockIdx.x, dblk, s.k, s.b);
+    s.k += g.first_chunk;
     s.w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
     s.n0 = s.w * Split<N, S>::NPW;
     const int lane = threadIdx.x & (kWave - 1);
@@ -587,8 +640,8 @@ void chunk_summary_kernel(ScanArgs a, ChunkGrid g, Carry c) {
     }
     __shared__ ScanLds<N, S> lds;
     float dsum = 0.0f;
-    scan_chunk<N, S, IO, SP, false, false, false>(s.io, s.bc, s.dbias, s.ntok, s.w, s.n0, lds,
-                                                  A2, h, 0.0f, dsum);
+    scan_chunk<N, S, IO, SP, kPassSummary, false, false>(s.io, s.bc, s.dbias, s.ntok, s.w, s.n0,
+                                                         lds, A2, h, 0.0f, 0.0f, dsum);
 #pragma unroll
     for (int q = 0; q < NPW; ++q) {
         c.end[srow + q] = h[q];
@@ -597,17 +650,22 @@ void chunk_summary_kernel(ScanArgs a, ChunkGrid g, Carry c) {
 }
 
 // Carry pass: one thread per (b, d, n) column folds the chunk summaries in
-// order and writes the state entering chunks 1 .. nchunks-1.
+// order and writes the state entering chunks 1 .. nchunks-1. With hL (the
+// repaired carry, whose pass 1 summarises the last chunk too) it folds
+// through the last chunk and writes the final state, whose (b, d, n) layout
+// is the column index.
 __global__ __launch_bounds__(256) void chunk_carry_kernel(int64_t columns, int64_t nchunks,
-                                                          Carry c) {
+                                                          Carry c, float* hL) {
     const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
     for (int64_t col = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; col < columns;
          col += stride) {
         float H = c.end[col];  // exact end state of chunk 0
         for (int64_t k = 1; k < nchunks; ++k) {
             c.start[k * columns + col] = H;
-            if (k + 1 < nchunks) H = fmaf(c.decay[k * columns + col], H, c.end[k * columns + col]);
+            if (k + 1 < nchunks || hL != nullptr)
+                H = fmaf(c.decay[k * columns + col], H, c.end[k * columns + col]);
         }
+        if (hL != nullptr) hL[col] = H;
     }
 }
 
@@ -633,19 +691,90 @@ void chunk_output_kernel(ScanArgs a, ChunkGrid g, Carry c) {
     }
     const float dskip = HAS_D ? a.D[s.d] : 0.0f;
     float dsum = 0.0f;
-    scan_chunk<N, S, IO, SP, true, HAS_D, HAS_Z>(s.io, s.bc, s.dbias, s.ntok, s.w, s.n0, lds, A2,
-                                                 h, dskip, dsum);
+    scan_chunk<N, S, IO, SP, kPassOutput, HAS_D, HAS_Z>(s.io, s.bc, s.dbias, s.ntok, s.w, s.n0,
+                                                        lds, A2, h, dskip, 0.0f, dsum);
     if (s.k == g.nchunks - 1 && a.hL != nullptr) {
 #pragma unroll
         for (int q = 0; q < NPW; ++q) a.hL[(s.b * a.dim + s.d) * N + s.n0 + q] = h[q];
     }
 }
 
+// Repaired carry, pass 1: every chunk from a zero state (chunk 0 from h0)
+// writes y and its (end state, decay product) pair, the last chunk's
+// included.
+template <int N, int S, int IO, bool SP, bool HAS_D, bool HAS_Z>
+__global__ __launch_bounds__(kWave * S) __attribute__((amdgpu_waves_per_eu(S <= 2 ? 2 : 4)))
+void chunk_local_kernel(ScanArgs a, ChunkGrid g, Carry c) {
+    constexpr int NPW = Split<N, S>::NPW;
+    __shared__ ScanLds<N, S> lds;
+    const WaveSlot s = wave_slot<N, S, IO>(a, g);
+    float A2[NPW], h[NPW];
+    const int64_t srow = ((s.k * a.batch + s.b) * a.dim + s.d) * N + s.n0;
+#pragma unroll
+    for (int q = 0; q < NPW; ++q) {
+        A2[q] = a.A[s.d * N + s.n0 + q] * kLog2e;
+        h[q] = (s.k == 0 && a.h0 != nullptr) ? a.h0[(s.b * a.dim + s.d) * N + s.n0 + q] : 0.0f;
+    }
+    const float dskip = HAS_D ? a.D[s.d] : 0.0f;
+    float dsum = 0.0f;
+    scan_chunk<N, S, IO, SP, kPassLocal, HAS_D, HAS_Z>(s.io, s.bc, s.dbias, s.ntok, s.w, s.n0,
+                                                       lds, A2, h, dskip, 0.0f, dsum);
+#pragma unroll
+    for (int q = 0; q < NPW; ++q) {
+        c.end[srow + q] = h[q];
+        c.decay[srow + q] = fast_exp2(A2[q] * dsum);
+    }
+}
+
+// Repaired carry, pass 2: chunks 1 .. nchunks-1 rerun from their true
+// entering state and overwrite y until the entering state's weight has
+// fallen below 2^-kFixupLog2 for every state of the workgroup.
+template <int N, int S, int IO, bool SP, bool HAS_D, bool HAS_Z>
+__global__ __launch_bounds__(kWave * S) __attribute__((amdgpu_waves_per_eu(S <= 2 ? 2 : 4)))
+void chunk_fixup_kernel(ScanArgs a, ChunkGrid g, Carry c) {
+    constexpr int NPW = Split<N, S>::NPW;
+    __shared__ ScanLds<N, S> lds;
+    const WaveSlot s = wave_slot<N, S, IO>(a, g);
+    float A2[NPW], h[NPW];
+    const int64_t srow = ((s.k * a.batch + s.b) * a.dim + s.d) * N + s.n0;
+    float a2max = -__builtin_inff();
+    bool finite = true;
+#pragma unroll
+    for (int q = 0; q < NPW; ++q) {
+        A2[q] = a.A[s.d * N + s.n0 + q] * kLog2e;
+        h[q] = c.start[srow + q];
+        a2max = fmaxf(a2max, A2[q]);
+        finite = finite && __builtin_isfinite(h[q]);
+    }
+    // an infinite or NaN entering state reaches every later output, as in
+    // the two-pass form: its lanes never vote done
+    if (!finite) a2max = __builtin_nanf("");
+    const float dskip = HAS_D ? a.D[s.d] : 0.0f;
+    float dsum = 0.0f;
+    scan_chunk<N, S, IO, SP, kPassFixup, HAS_D, HAS_Z>(s.io, s.bc, s.dbias, s.ntok, s.w, s.n0,
+                                                       lds, A2, h, dskip, a2max, dsum);
+}
+
 // ---------------------------------------------------------------------------
 // Host-side dispatch over the compile-time variants.
+template <int N, int S, int IO, bool SP, bool HAS_D, bool HAS_Z>
+hipError_t launch_repaired(const ScanArgs& a, const ChunkGrid& g, const Carry& c,
+                           int64_t columns, hipStream_t s) {
+    const dim3 block(kWave * S);
+    hipLaunchKernelGGL((chunk_local_kernel<N, S, IO, SP, HAS_D, HAS_Z>),
+                       dim3(g.nblk_d * g.nchunks * a.batch), block, 0, s, a, g, c);
+    hipLaunchKernelGGL(chunk_carry_kernel, dim3(stride_blocks(columns)), dim3(256), 0, s, columns,
+                       g.nchunks, c, a.hL);
+    ChunkGrid g2 = g;
+    g2.nchunks = g.nchunks - 1;
+    g2.first_chunk = 1;
+    hipLaunchKernelGGL((chunk_fixup_kernel<N, S, IO, SP, HAS_D, HAS_Z>),
+                       dim3(g.nblk_d * g2.nchunks * a.batch), block, 0, s, a, g2, c);
+    return hipGetLastError();
+}
+
 template <int N, int S, int IO, bool SP>
-hipError_t launch_scan_ns(const ScanArgs& a, const ScanPlan& plan, void* ws, hipStream_t s,
-                          bool states_only) {
+hipError_t launch_scan_ns(const ScanArgs& a, const ScanPlan& plan, void* ws, hipStream_t s) {
     ChunkGrid g;
     g.nblk_d = (a.dim + kWave - 1) / kWave;
     g.nchunks = plan.nchunks;
@@ -657,6 +786,15 @@ hipError_t launch_scan_ns(const ScanArgs& a, const ScanPlan& plan, void* ws, hip
         c.start = base;
         c.end = base + plan.nchunks * columns;
         c.decay = base + 2 * plan.nchunks * columns;
+    }
+    const bool has_d = a.D != nullptr, has_z = a.z != nullptr;
+    if (plan.nchunks > 1 && plan.carry == kCarryRepair) {
+        if (has_d && has_z) return launch_repaired<N, S, IO, SP, true, true>(a, g, c, columns, s);
+        if (has_d) return launch_repaired<N, S, IO, SP, true, false>(a, g, c, columns, s);
+        if (has_z) return launch_repaired<N, S, IO, SP, false, true>(a, g, c, columns, s);
+        return launch_repaired<N, S, IO, SP, false, false>(a, g, c, columns, s);
+    }
+    if (plan.nchunks > 1) {
         // Pass 1 covers chunks 0 .. nchunks-2: its grid describes nchunks-1
         // chunks of the same length, so block indices map onto exactly those;
         // the workspace rows keep the full nchunks stride through `columns`.
@@ -666,12 +804,10 @@ hipError_t launch_scan_ns(const ScanArgs& a, const ScanPlan& plan, void* ws, hip
         hipLaunchKernelGGL((chunk_summary_kernel<N, S, IO, SP>), dim3(blocks1), dim3(kWave * S), 0, s,
                            a, g1, c);
         hipLaunchKernelGGL(chunk_carry_kernel, dim3(stride_blocks(columns)), dim3(256), 0, s,
-                           columns, plan.nchunks, c);
+                           columns, plan.nchunks, c, nullptr);
     }
-    if (states_only) return hipGetLastError();
     const int64_t blocks = g.nblk_d * plan.nchunks * a.batch;
     const dim3 grid(blocks), block(kWave * S);
-    const bool has_d = a.D != nullptr, has_z = a.z != nullptr;
     if (has_d && has_z)
         hipLaunchKernelGGL((chunk_output_kernel<N, S, IO, SP, true, true>), grid, block, 0, s, a, g, c);
     else if (has_d)
@@ -686,13 +822,12 @@ hipError_t launch_scan_ns(const ScanArgs& a, const ScanPlan& plan, void* ws, hip
 // The state split S is a compile-time parameter; every N supports S = 1 and
 // N = 16, 8 and 4 also support the splits that divide them (up to 8).
 template <int N, int IO, bool SP>
-hipError_t launch_scan_n(const ScanArgs& a, const ScanPlan& plan, void* ws, hipStream_t s,
-                         bool states_only) {
+hipError_t launch_scan_n(const ScanArgs& a, const ScanPlan& plan, void* ws, hipStream_t s) {
     switch (plan.state_split) {
-        case 1: return launch_scan_ns<N, 1, IO, SP>(a, plan, ws, s, states_only);
-        case 2: if constexpr (N % 2 == 0 && (N == 4 || N == 8 || N == 16)) return launch_scan_ns<N, 2, IO, SP>(a, plan, ws, s, states_only); break;
-        case 4: if constexpr (N % 4 == 0 && (N == 4 || N == 8 || N == 16)) return launch_scan_ns<N, 4, IO, SP>(a, plan, ws, s, states_only); break;
-        case 8: if constexpr (N % 8 == 0 && (N == 8 || N == 16)) return launch_scan_ns<N, 8, IO, SP>(a, plan, ws, s, states_only); break;
+        case 1: return launch_scan_ns<N, 1, IO, SP>(a, plan, ws, s);
+        case 2: if constexpr (N % 2 == 0 && (N == 4 || N == 8 || N == 16)) return launch_scan_ns<N, 2, IO, SP>(a, plan, ws, s); break;
+        case 4: if constexpr (N % 4 == 0 && (N == 4 || N == 8 || N == 16)) return launch_scan_ns<N, 4, IO, SP>(a, plan, ws, s); break;
+        case 8: if constexpr (N % 8 == 0 && (N == 8 || N == 16)) return launch_scan_ns<N, 8, IO, SP>(a, plan, ws, s); break;
         default: break;
     }
     return hipErrorInvalidValue;
@@ -701,10 +836,9 @@ hipError_t launch_scan_n(const ScanArgs& a, const ScanPlan& plan, void* ws, hipS
 }  // namespace
 
 template <int IO, bool SP>
-hipError_t launch_scan_variant(const ScanArgs& a, const ScanPlan& p, void* ws, hipStream_t s,
-                               bool states_only) {
+hipError_t launch_scan_variant(const ScanArgs& a, const ScanPlan& p, void* ws, hipStream_t s) {
     switch (a.dstate) {
-#define MAMBA_CASE(n) case n: return launch_scan_n<n, IO, SP>(a, p, ws, s, states_only);
+#define MAMBA_CASE(n) case n: return launch_scan_n<n, IO, SP>(a, p, ws, s);
         MAMBA_CASE(1) MAMBA_CASE(2) MAMBA_CASE(3) MAMBA_CASE(4) MAMBA_CASE(5) MAMBA_CASE(6)
         MAMBA_CASE(7) MAMBA_CASE(8) MAMBA_CASE(9) MAMBA_CASE(10) MAMBA_CASE(11) MAMBA_CASE(12)
         MAMBA_CASE(13) MAMBA_CASE(14) MAMBA_CASE(15) MAMBA_CASE(16)

@@ -10,5 +10,5 @@
 
 namespace mamba {
 template hipError_t launch_scan_variant<MAMBA_VARIANT_IO, (MAMBA_VARIANT_SP != 0)>(
-    const ScanArgs&, const ScanPlan&, void*, hipStream_t, bool);
+    const ScanArgs&, const ScanPlan&, void*, hipStream_t);
 }  // namespace mamba

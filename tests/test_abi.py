@@ -48,8 +48,8 @@ P = ctypes.c_void_p(0x10000)
 PM = ctypes.c_void_p(0x10008)  # not 16-byte aligned
 
 
-def _plan(chunk_len=0, split=0, reserved=0):
-    return ctypes.byref(ms.ScanPlan(chunk_len, split, reserved))
+def _plan(chunk_len=0, split=0, carry=0):
+    return ctypes.byref(ms.ScanPlan(chunk_len, split, carry))
 
 
 def _opts(bias=None, softplus=0, reserved=0):
@@ -70,7 +70,8 @@ def test_scan_rejects_bad_shapes(lib):
     assert _scan(lib, seqlen=-3) == INVALID
     assert _scan(lib, dim=-1) == INVALID
     assert _scan(lib, plan=_plan(chunk_len=-8, split=1)) == INVALID
-    assert _scan(lib, plan=_plan(chunk_len=8, split=1, reserved=1)) == INVALID
+    assert _scan(lib, plan=_plan(chunk_len=8, split=1, carry=3)) == INVALID
+    assert _scan(lib, plan=_plan(chunk_len=8, split=1, carry=-1)) == INVALID
     assert _scan(lib, plan=_plan(chunk_len=8, split=3)) == UNSUPPORTED
     assert _scan(lib, plan=_plan(chunk_len=8, split=16)) == UNSUPPORTED
     assert _scan(lib, dstate=4, plan=_plan(chunk_len=8, split=8)) == UNSUPPORTED
@@ -117,6 +118,27 @@ def test_scan_workspace_check(lib):
     assert lib.ssm_scan_fwd_workspace_size(1, 1 << 20, 1 << 14, 16, 0, _plan(1 << 20, 1),
                                            ctypes.byref(got), ctypes.byref(need)) == OK
     assert got.chunk_len * (1 << 14) * 4 < (1 << 32)
+
+
+def test_scan_carry_choice(lib):
+    """Automatic carry: the head rerun from 4096-token chunks up, the summary
+    pass below; a forced choice is kept; both need the same scratch."""
+    got = ms.ScanPlan(0, 0, 0)
+    need = ctypes.c_size_t(0)
+
+    def resolve(seqlen, chunk_len, carry=0):
+        assert lib.ssm_scan_fwd_workspace_size(1, seqlen, 64, 16, 1, _plan(chunk_len, 4, carry),
+                                               ctypes.byref(got), ctypes.byref(need)) == OK
+        return got.carry, need.value
+
+    assert resolve(1 << 14, 4095)[0] == ms.CARRY_RERUN
+    assert resolve(1 << 14, 4096)[0] == ms.CARRY_REPAIR
+    assert resolve(1 << 14, 4096, ms.CARRY_RERUN)[0] == ms.CARRY_RERUN
+    assert resolve(1 << 14, 256, ms.CARRY_REPAIR)[0] == ms.CARRY_REPAIR
+    assert resolve(1 << 14, 4096, ms.CARRY_REPAIR)[1] == resolve(1 << 14, 4096,
+                                                                  ms.CARRY_RERUN)[1] > 0
+    # one chunk: no carry at all, reported as the rerun form
+    assert resolve(4096, 4096) == (ms.CARRY_RERUN, 0)
 
 
 def test_scan_empty_shapes_are_noops(lib):
