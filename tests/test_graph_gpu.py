@@ -9,6 +9,7 @@ kernels on the same inputs give the same bits). Nothing captured may record
 a memset or allocate outside the capture's pool; a failure here means a
 captured node does not do on replay what it did when captured.
 """
+import dataclasses
 import sys
 
 import pytest
@@ -112,39 +113,55 @@ def test_graph_decode_layers_replay_bitwise():
 
 
 def test_graph_chunked_scan_and_ssd_replay_bitwise():
-    """A scan forced into several chunks (summary, carry and output passes
-    with a workspace allocated while capturing) and a dual-form call."""
+    """A scan forced into several chunks, once with the summary-pass carry and
+    once with the repaired carry (whose head reruns stop on the data), each
+    with a workspace allocated while capturing, and a dual-form call."""
     w = W.WORKLOADS["mamba130m_layer"]
     inp = {k: (v.to(DEV) if v is not None else None)
            for k, v in W.generate_scan(w, batch=2, seqlen=300, dim=192, seed=11).items()}
+    # delta ~ softplus(N(0,1)): the repaired carry's head reruns stop inside
+    # the 104-token chunks
+    fast = {k: (v.to(DEV) if v is not None else None)
+            for k, v in W.generate_scan(dataclasses.replace(w, delta_shift=0.0), batch=2,
+                                        seqlen=300, dim=192, seed=13).items()}
     sw = W.SSD_WORKLOADS["ssd_mamba2_layer"]
     sinp = {k: (v.to(DEV) if v is not None else None)
             for k, v in W.generate_ssd(sw, batch=2, seqlen=150, nheads=2, dstate=128,
                                        seed=12).items()}
     y = torch.empty_like(inp["x"])
     hL = torch.empty(2, 192, w.dstate, dtype=torch.float32, device=DEV)
+    ry = torch.empty_like(inp["x"])
+    rhL = torch.empty_like(hL)
     sy = torch.empty_like(sinp["x"])
     shL = torch.empty(2, 2, 64, 128, dtype=torch.float32, device=DEV)
 
     def step():
         ms.scan_fwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"],
                     inp["h0"], chunk_len=64, out=y, state_out=hL)
+        ms.scan_fwd(fast["x"], fast["delta"], fast["A"], fast["B"], fast["C"], fast["D"],
+                    fast["z"], fast["h0"], chunk_len=104, carry=ms.CARRY_REPAIR, out=ry,
+                    state_out=rhL)
         ms.ssd_fwd(sinp["x"], sinp["dt"], sinp["A"], sinp["B"], sinp["C"], sinp["D"], sinp["z"],
                    sinp["h0"], out=sy, state_out=shL)
 
     graph = _capture(step)
     y_ref, h_ref = ms.scan_fwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"],
                                inp["z"], inp["h0"], chunk_len=64)
+    ry_ref, rh_ref = ms.scan_fwd(fast["x"], fast["delta"], fast["A"], fast["B"], fast["C"],
+                                 fast["D"], fast["z"], fast["h0"], chunk_len=104,
+                                 carry=ms.CARRY_REPAIR)
     sy_ref, sh_ref = ms.ssd_fwd(sinp["x"], sinp["dt"], sinp["A"], sinp["B"], sinp["C"],
                                 sinp["D"], sinp["z"], sinp["h0"])
     torch.cuda.synchronize()
     for r in range(REPLAYS):
         _say(f"case graph chunked scan + ssd: replay {r}")
         y.zero_()
+        ry.zero_()
         sy.zero_()
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(y, y_ref) and torch.equal(hL, h_ref), f"chunked scan, replay {r}"
+        assert torch.equal(ry, ry_ref) and torch.equal(rhL, rh_ref), f"repaired carry, replay {r}"
         assert torch.equal(sy, sy_ref) and torch.equal(shL, sh_ref), f"ssd, replay {r}"
         _eager_noise(r)
