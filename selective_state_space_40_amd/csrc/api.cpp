@@ -85,13 +85,16 @@ int check_shape(int64_t batch, int64_t seqlen, int64_t dim, int dstate, int dtyp
 // counts, which on long chunks is a small part of the summary pass it
 // replaces (the million-token scan: about 1,100 of 21,848 tokens). Short
 // chunks keep the summary pass, since a rerun that covers the whole chunk
-// costs more than the summary.
+// costs more than the summary. Without a summary pass more chunks cost only
+// their head reruns, so such plans aim at about eight waves per SIMD (the
+// million-token scan: 7.99 ms with 64 chunks against 8.16 ms with 48).
 constexpr int kPreferredSplit = 4;
 constexpr int64_t kRepairMinChunk = 4096;
 static_assert(mamba::kCarryRerun == MAMBA_CARRY_RERUN && mamba::kCarryRepair == MAMBA_CARRY_REPAIR,
               "internal carry codes follow the public enum");
 constexpr int64_t kWavesPerSimdNoChunk = 2;
 constexpr int64_t kWavesPerSimdChunked = 6;
+constexpr int64_t kWavesPerSimdRepaired = 8;
 constexpr int64_t kMinChunk = 64;
 
 int make_plan(int64_t batch, int64_t seqlen, int64_t dim, int dstate, int dtype,
@@ -127,14 +130,21 @@ int make_plan(int64_t batch, int64_t seqlen, int64_t dim, int dstate, int dtype,
         }
         if (len == 0) {
             const int64_t waves = groups * split;
-            int64_t n = 1;
-            if (waves < kWavesPerSimdNoChunk * simds)
-                n = (kWavesPerSimdChunked * simds + waves - 1) / waves;
             const int64_t nmax = seqlen / kMinChunk;
-            if (n > nmax) n = nmax;
-            if (n < 1) n = 1;
-            len = (seqlen + n - 1) / n;
-            len = (len + mamba::kTokenTile - 1) / mamba::kTokenTile * mamba::kTokenTile;
+            auto chunk_for = [&](int64_t per_simd) {
+                int64_t n = 1;
+                if (waves < kWavesPerSimdNoChunk * simds) n = (per_simd * simds + waves - 1) / waves;
+                if (n > nmax) n = nmax;
+                if (n < 1) n = 1;
+                const int64_t c = (seqlen + n - 1) / n;
+                return (c + mamba::kTokenTile - 1) / mamba::kTokenTile * mamba::kTokenTile;
+            };
+            len = chunk_for(kWavesPerSimdChunked);
+            // chunks that will join through the repaired carry: more of them
+            if (len < seqlen && carry != MAMBA_CARRY_RERUN) {
+                const int64_t shorter = chunk_for(kWavesPerSimdRepaired);
+                if (shorter >= kRepairMinChunk) len = shorter;
+            }
         }
     }
     if (len > seqlen) len = seqlen;
