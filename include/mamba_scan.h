@@ -87,7 +87,11 @@ typedef enum mamba_dtype {
  *                     (h_in: the entering state), below fp32 rounding of
  *                     that readout. The rerun length depends on the data: a
  *                     chunk whose decay never gets there (A >= 0, delta = 0,
- *                     a non-finite entering state) is rerun whole.
+ *                     a non-finite entering state) is rerun whole. The bound
+ *                     rests on the weight only shrinking, i.e. on the
+ *                     positive delta the scan requires (after the bias and
+ *                     activation, when fused); with negative deltas only
+ *                     MAMBA_CARRY_RERUN keeps the plain recurrence.
  */
 typedef enum mamba_carry {
     MAMBA_CARRY_AUTO = 0,
