@@ -653,17 +653,34 @@ void chunk_summary_kernel(ScanArgs a, ChunkGrid g, Carry c) {
 // order and writes the state entering chunks 1 .. nchunks-1. With hL (the
 // repaired carry, whose pass 1 summarises the last chunk too) it folds
 // through the last chunk and writes the final state, whose (b, d, n) layout
-// is the column index.
+// is the column index. The pairs are loaded kCarryBatch chunks at a time
+// before they are folded, so a thread waits for memory once per batch rather
+// than once per chunk (the fold itself is one FMA per chunk).
+constexpr int kCarryBatch = 8;
+
 __global__ __launch_bounds__(256) void chunk_carry_kernel(int64_t columns, int64_t nchunks,
                                                           Carry c, float* hL) {
     const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+    // chunks whose pair is folded: 1 .. last - 1 (the last one only with hL)
+    const int64_t last = hL != nullptr ? nchunks : nchunks - 1;
     for (int64_t col = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; col < columns;
          col += stride) {
         float H = c.end[col];  // exact end state of chunk 0
-        for (int64_t k = 1; k < nchunks; ++k) {
-            c.start[k * columns + col] = H;
-            if (k + 1 < nchunks || hL != nullptr)
-                H = fmaf(c.decay[k * columns + col], H, c.end[k * columns + col]);
+        for (int64_t k0 = 1; k0 < nchunks; k0 += kCarryBatch) {
+            float P[kCarryBatch], E[kCarryBatch];
+#pragma unroll
+            for (int u = 0; u < kCarryBatch; ++u) {
+                // clamped into range; the pairs past `last` are never used
+                const int64_t k = min(k0 + u, nchunks - 1);
+                P[u] = c.decay[k * columns + col];
+                E[u] = c.end[k * columns + col];
+            }
+#pragma unroll
+            for (int u = 0; u < kCarryBatch; ++u) {
+                const int64_t k = k0 + u;
+                if (k < nchunks) c.start[k * columns + col] = H;
+                if (k < last) H = fmaf(P[u], H, E[u]);
+            }
         }
         if (hL != nullptr) hL[col] = H;
     }
