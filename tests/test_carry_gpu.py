@@ -221,3 +221,21 @@ def test_repaired_carry_with_fused_softplus(orc):
     yo, ho = orc.scan_fwd(**inp, delta_softplus=True)
     assert_close(y, yo, TOL["bf16"], "repaired softplus y")
     assert_close(hL, ho, TOL["bf16"], "repaired softplus hL")
+
+
+def _splits(dstate):
+    # the splits the kernels are built for at this state size (besides 1)
+    return [1] + [s for s in (2, 4, 8) if dstate in (4, 8, 16) and dstate % s == 0]
+
+
+@pytest.mark.parametrize("dstate", list(range(1, ms.MAX_DSTATE + 1)))
+def test_repaired_carry_every_state_size(orc, dstate):
+    # every compiled state size and split of the local and fix-up kernels:
+    # 5 chunks of 160 tokens (the last ragged), 70 channels (a ragged group)
+    inp = _inputs(1, 700, 70, dstate, "f32", seed=40 + dstate)
+    yo, ho = orc.scan_fwd(**inp)
+    for split in _splits(dstate):
+        _say(f"case repaired carry N={dstate} split={split}")
+        y, hL = _run(inp, chunk_len=160, state_split=split, carry=REPAIR)
+        assert_close(y, yo, TOL["f32"], f"repaired N={dstate} split={split} y")
+        assert_close(hL, ho, TOL["f32"], f"repaired N={dstate} split={split} hL")
