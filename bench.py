@@ -41,6 +41,9 @@ def parse():
     p.add_argument("--state-split", type=int, default=0, help="0 = the library's automatic plan")
     p.add_argument("--carry", choices=("auto", "rerun", "repair"), default="auto",
                    help="how chunks of a cut sequence join (auto = the library's plan)")
+    p.add_argument("--halves", type=int, default=0,
+                   help="channel groups run as two 32-channel halves (0 = the library's plan, "
+                        "-1 = none, k = the last k groups)")
     p.add_argument("--batch", type=int, default=0, help="override the workload's batch (0 = keep)")
     p.add_argument("--dim", type=int, default=0, help="override the workload's channels (0 = keep)")
     p.add_argument("--backward", action="store_true",
@@ -225,7 +228,7 @@ def main():
         ms.scan_fwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"],
                     inp["h0"], delta_bias=inp.get("delta_bias"), delta_softplus=sp,
                     chunk_len=args.chunk_len, state_split=args.state_split, carry=carry,
-                    out=y, state_out=hL)
+                    halves=args.halves, out=y, state_out=hL)
 
     _spin_up(step, args.spin_up)
     for i in range(args.warmup):
@@ -247,7 +250,7 @@ def main():
 
     # the plan the library chose, for the record
     plan = ms.resolve_plan(w.batch, w.seqlen, w.dim, w.dstate, W.io_torch_dtype(w.io),
-                           args.chunk_len, args.state_split, carry)
+                           args.chunk_len, args.state_split, carry, args.halves)
     chunk_len, split = plan.chunk_len, plan.state_split
     nchunks = -(-w.seqlen // chunk_len)
 
@@ -306,6 +309,7 @@ def main():
                    "nchunks": int(nchunks), "state_split": int(split),
                    "carry": (None if nchunks == 1 else
                              {ms.CARRY_RERUN: "rerun", ms.CARRY_REPAIR: "repair"}[plan.carry]),
+                   "half_groups": int(plan.halves),
                    "delta_activation": "bias + softplus in the kernels" if sp else
                                        "none (delta passed activated)",
                    "parallelism": "single GPU"},

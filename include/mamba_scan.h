@@ -116,11 +116,26 @@ typedef enum mamba_carry {
  * carry        a mamba_carry value; automatic picks MAMBA_CARRY_REPAIR for
  *              chunks of 4096 tokens or more, MAMBA_CARRY_RERUN otherwise.
  *              Ignored with one chunk. Other values: MAMBA_ERR_INVALID_ARG.
+ * halves       channel groups (64 channels of one batch row) run as two
+ *              halves of 32 channels, each channel's states then spread over
+ *              8 lanes: the last `halves` groups in (row, group) order. It
+ *              evens out the work per compute unit when the groups do not
+ *              divide over the units (G groups on C units, G mod C <= C/2:
+ *              every unit then holds G div C groups and at most one half).
+ *              0: automatic (exactly that case); -1: none; k > 0: the last
+ *              k groups (k at most the number of groups, else
+ *              MAMBA_ERR_INVALID_ARG). Halves need one chunk, state_split 4
+ *              and dstate 8 or 16; k > 0 on any other plan returns
+ *              MAMBA_ERR_UNSUPPORTED, and automatic means none there.
+ *              A resolved plan reports the number of groups split.
+ * reserved     must be 0.
  */
 typedef struct mamba_scan_plan {
     int64_t chunk_len;
     int32_t state_split;
     int32_t carry;
+    int32_t halves;
+    int32_t reserved;
 } mamba_scan_plan;
 
 /*

@@ -32,7 +32,7 @@ import torch
 
 __all__ = ["scan_fwd", "scan_bwd", "ssd_fwd", "state_update", "conv1d_fwd", "conv1d_update", "workspace_size", "resolve_plan", "library_path",
            "load_library", "MambaScanError", "MAX_DSTATE", "ScanPlan", "ScanOptions", "Plan",
-           "CARRY_AUTO", "CARRY_RERUN", "CARRY_REPAIR"]
+           "CARRY_AUTO", "CARRY_RERUN", "CARRY_REPAIR", "HALVES_AUTO", "HALVES_NONE"]
 
 MAX_DSTATE = 16
 _DTYPES = {torch.float32: 0, torch.bfloat16: 1}
@@ -44,17 +44,22 @@ _WS = {}
 CARRY_AUTO, CARRY_RERUN, CARRY_REPAIR = 0, 1, 2
 
 
+HALVES_AUTO, HALVES_NONE = 0, -1
+
+
 class ScanPlan(ctypes.Structure):
     """mamba_scan_plan: chunk_len (tokens per parallel chunk), state_split
-    (waves sharing one channel's states) and carry (CARRY_RERUN: summary pass
+    (waves sharing one channel's states), carry (CARRY_RERUN: summary pass
     and a rerun of every chunk; CARRY_REPAIR: one pass from zero states and a
-    rerun of each chunk's head while the entering state still counts); 0
-    means automatic."""
+    rerun of each chunk's head while the entering state still counts) and
+    halves (the last channel groups run as two 32-channel halves; -1 none,
+    k > 0 the last k groups); 0 means automatic."""
     _fields_ = [("chunk_len", ctypes.c_int64), ("state_split", ctypes.c_int32),
-                ("carry", ctypes.c_int32)]
+                ("carry", ctypes.c_int32), ("halves", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 
-Plan = collections.namedtuple("Plan", "chunk_len state_split carry workspace_bytes")
+Plan = collections.namedtuple("Plan", "chunk_len state_split carry halves workspace_bytes")
 
 
 class ScanOptions(ctypes.Structure):
@@ -149,25 +154,26 @@ def _options(delta_bias, delta_softplus):
 
 
 def resolve_plan(batch, seqlen, dim, dstate, dtype=torch.bfloat16, chunk_len=0, state_split=0,
-                 carry=CARRY_AUTO):
+                 carry=CARRY_AUTO, halves=HALVES_AUTO):
     """The plan ssm_scan_fwd uses for this shape, and its scratch bytes, as a
-    Plan (chunk_len, state_split, carry, workspace_bytes). Automatic fields
-    query the current device."""
-    req = ScanPlan(chunk_len, state_split, carry)
-    out = ScanPlan(0, 0, 0)
+    Plan (chunk_len, state_split, carry, halves, workspace_bytes); halves is
+    the number of channel groups split. Automatic fields query the current
+    device."""
+    req = ScanPlan(chunk_len, state_split, carry, halves, 0)
+    out = ScanPlan(0, 0, 0, 0, 0)
     nbytes = ctypes.c_size_t(0)
     _check(load_library().ssm_scan_fwd_workspace_size(batch, seqlen, dim, dstate, _DTYPES[dtype],
                                                       ctypes.byref(req), ctypes.byref(out),
                                                       ctypes.byref(nbytes)),
            "ssm_scan_fwd_workspace_size")
-    return Plan(out.chunk_len, out.state_split, out.carry, nbytes.value)
+    return Plan(out.chunk_len, out.state_split, out.carry, out.halves, nbytes.value)
 
 
 def workspace_size(batch, seqlen, dim, dstate, dtype=torch.bfloat16, chunk_len=0, state_split=0,
-                   carry=CARRY_AUTO):
+                   carry=CARRY_AUTO, halves=HALVES_AUTO):
     """Scratch bytes ssm_scan_fwd needs for this shape and plan."""
-    return resolve_plan(batch, seqlen, dim, dstate, dtype, chunk_len, state_split,
-                        carry).workspace_bytes
+    return resolve_plan(batch, seqlen, dim, dstate, dtype, chunk_len, state_split, carry,
+                        halves).workspace_bytes
 
 
 def _workspace(device, nbytes, kind="fwd"):
@@ -183,13 +189,14 @@ def _workspace(device, nbytes, kind="fwd"):
 
 def scan_fwd(x, delta, A, B, C, D=None, z=None, h0=None, *, delta_bias=None,
              delta_softplus=False, chunk_len=0, state_split=0, carry=CARRY_AUTO,
-             return_state=True, out=None, state_out=None):
+             halves=HALVES_AUTO, return_state=True, out=None, state_out=None):
     """Selective scan over whole sequences; returns (y, hL) (hL is None when
     return_state is False). `delta_bias` (dim,) fp32 is added to delta and
     `delta_softplus` applies softplus after it, inside the kernels.
     `chunk_len` > 0 forces the parallel chunk length, `state_split` > 0 the
-    number of waves sharing a channel's states and `carry` how chunks join
-    (CARRY_RERUN or CARRY_REPAIR)."""
+    number of waves sharing a channel's states, `carry` how chunks join
+    (CARRY_RERUN or CARRY_REPAIR) and `halves` how many of the last channel
+    groups run as two 32-channel halves (HALVES_NONE: none)."""
     lib = load_library()
     if x.dim() != 3:
         raise ValueError("x must be (batch, L, dim)")
@@ -218,9 +225,10 @@ def scan_fwd(x, delta, A, B, C, D=None, z=None, h0=None, *, delta_bias=None,
         hL = state_out if state_out is not None else torch.empty(batch, dim, dstate,
                                                                  dtype=torch.float32, device=dev)
         _need(hL, "state_out", (batch, dim, dstate), torch.float32, dev)
-    plan = ScanPlan(chunk_len, state_split, carry)
+    plan = ScanPlan(chunk_len, state_split, carry, halves, 0)
     with torch.cuda.device(dev):
-        nbytes = workspace_size(batch, seqlen, dim, dstate, dt, chunk_len, state_split, carry)
+        nbytes = workspace_size(batch, seqlen, dim, dstate, dt, chunk_len, state_split, carry,
+                                halves)
         ws = _workspace(dev, nbytes)
         st = lib.ssm_scan_fwd(batch, seqlen, dim, dstate, _DTYPES[dt], _ptr(x), _ptr(delta),
                               _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0), _ptr(y),

@@ -102,8 +102,10 @@ int make_plan(int64_t batch, int64_t seqlen, int64_t dim, int dstate, int dtype,
     int64_t len = req ? req->chunk_len : 0;
     int split = req ? req->state_split : 0;
     const int carry = req ? req->carry : MAMBA_CARRY_AUTO;
+    const int64_t halves = req ? req->halves : 0;
     if (carry != MAMBA_CARRY_AUTO && carry != MAMBA_CARRY_RERUN && carry != MAMBA_CARRY_REPAIR)
         return MAMBA_ERR_INVALID_ARG;
+    if ((req && req->reserved != 0) || halves < -1) return MAMBA_ERR_INVALID_ARG;
     if (len < 0 || split < 0) return MAMBA_ERR_INVALID_ARG;
     if (split != 0 && !mamba::split_supported(dstate, split)) return MAMBA_ERR_UNSUPPORTED;
     if (seqlen == 0 || batch == 0 || dim == 0) {
@@ -111,6 +113,7 @@ int make_plan(int64_t batch, int64_t seqlen, int64_t dim, int dstate, int dtype,
         plan->nchunks = 1;
         plan->state_split = split ? split : 1;
         plan->carry = carry != MAMBA_CARRY_AUTO ? carry : MAMBA_CARRY_RERUN;
+        plan->halves = 0;  // nothing runs: any request is moot
         plan->workspace_bytes = 0;
         return MAMBA_OK;
     }
@@ -163,6 +166,22 @@ int make_plan(int64_t batch, int64_t seqlen, int64_t dim, int dstate, int dtype,
                       : (nchunks > 1 && len >= kRepairMinChunk ? MAMBA_CARRY_REPAIR
                                                                : MAMBA_CARRY_RERUN);
     plan->workspace_bytes = mamba::scan_workspace_bytes(batch, dim, dstate, nchunks);
+    // whole and half channel groups
+    plan->halves = 0;
+    const bool halvable = nchunks == 1 && split == 4 && (dstate == 8 || dstate == 16);
+    if (halves > 0) {
+        if (!halvable) return MAMBA_ERR_UNSUPPORTED;
+        if (halves > groups) return MAMBA_ERR_INVALID_ARG;
+        plan->halves = halves;
+    } else if (halves == 0 && halvable) {
+        int cu = 0;
+        const int st = current_cu_count(&cu);
+        if (st != MAMBA_OK) return st;
+        const int64_t surplus = groups % cu;
+        if (surplus > 0 && 2 * surplus <= cu) plan->halves = surplus;
+    }
+    // the launch holds the whole groups and two blocks per split group
+    if (groups + plan->halves > (int64_t(1) << 31)) return MAMBA_ERR_UNSUPPORTED;
     return MAMBA_OK;
 }
 
@@ -184,6 +203,8 @@ int ssm_scan_fwd_workspace_size(int64_t batch, int64_t seqlen, int64_t dim, int 
         resolved->chunk_len = plan.chunk_len;
         resolved->state_split = plan.state_split;
         resolved->carry = plan.carry;
+        resolved->halves = static_cast<int32_t>(plan.halves);
+        resolved->reserved = 0;
     }
     return MAMBA_OK;
 }

@@ -38,6 +38,7 @@ struct ScanPlan {
     int64_t nchunks = 1;
     int state_split = 1;         // waves sharing the states of one channel
     int carry = kCarryRerun;     // kCarryRerun or kCarryRepair (nchunks > 1)
+    int64_t halves = 0;          // last channel groups split into two 32-channel halves
     size_t workspace_bytes = 0;  // 0 when nchunks == 1
 };
 

@@ -587,11 +587,12 @@ struct WaveSlot {
 };
 
 template <int N, int S, int IO>
-__device__ __forceinline__ WaveSlot wave_slot(const ScanArgs& a, const ChunkGrid& g) {
+__device__ __forceinline__ WaveSlot wave_slot(const ScanArgs& a, const ChunkGrid& g,
+                                              int64_t blk) {
     constexpr int64_t esz = IO == kIoF32 ? 4 : 2;
     WaveSlot s;
     int64_t dblk;
-    decode_block(g, blockIdx.x, dblk, s.k, s.b);
+    decode_block(g, blk, dblk, s.k, s.b);
     s.k += g.first_chunk;
     s.w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
     s.n0 = s.w * Split<N, S>::NPW;
@@ -626,7 +627,7 @@ template <int N, int S, int IO, bool SP>
 __global__ __launch_bounds__(kWave * S) __attribute__((amdgpu_waves_per_eu(S == 1 ? 4 : 6)))
 void chunk_summary_kernel(ScanArgs a, ChunkGrid g, Carry c) {
     constexpr int NPW = Split<N, S>::NPW;
-    const WaveSlot s = wave_slot<N, S, IO>(a, g);
+    const WaveSlot s = wave_slot<N, S, IO>(a, g, blockIdx.x);
     float A2[NPW], h[NPW];
     const int64_t srow = ((s.k * a.batch + s.b) * a.dim + s.d) * N + s.n0;
 #pragma unroll
@@ -689,11 +690,10 @@ __global__ __launch_bounds__(256) void chunk_carry_kernel(int64_t columns, int64
 // Pass 2 (or the only pass when nchunks == 1): scan each chunk from its true
 // entering state and write y; the last chunk writes hL.
 template <int N, int S, int IO, bool SP, bool HAS_D, bool HAS_Z>
-__global__ __launch_bounds__(kWave * S) __attribute__((amdgpu_waves_per_eu(S <= 2 ? 2 : 4)))
-void chunk_output_kernel(ScanArgs a, ChunkGrid g, Carry c) {
+__device__ __forceinline__ void output_group(const ScanArgs& a, const ChunkGrid& g,
+                                             const Carry& c, int64_t blk, ScanLds<N, S>& lds) {
     constexpr int NPW = Split<N, S>::NPW;
-    __shared__ ScanLds<N, S> lds;
-    const WaveSlot s = wave_slot<N, S, IO>(a, g);
+    const WaveSlot s = wave_slot<N, S, IO>(a, g, blk);
     float A2[NPW], h[NPW];
 #pragma unroll
     for (int q = 0; q < NPW; ++q) A2[q] = a.A[s.d * N + s.n0 + q] * kLog2e;
@@ -716,6 +716,238 @@ void chunk_output_kernel(ScanArgs a, ChunkGrid g, Carry c) {
     }
 }
 
+template <int N, int S, int IO, bool SP, bool HAS_D, bool HAS_Z>
+__global__ __launch_bounds__(kWave * S) __attribute__((amdgpu_waves_per_eu(S <= 2 ? 2 : 4)))
+void chunk_output_kernel(ScanArgs a, ChunkGrid g, Carry c) {
+    __shared__ ScanLds<N, S> lds;
+    output_group<N, S, IO, SP, HAS_D, HAS_Z>(a, g, c, blockIdx.x, lds);
+}
+
+// ---------------------------------------------------------------------------
+// Half channel groups (single-chunk scans of split 4). A launch of G channel
+// groups on C compute units leaves some units with one workgroup more than
+// others unless G is a multiple of C; on the Mamba-2.8B layer (640 groups,
+// 2.5 per unit) the units holding three set the time while the others idle.
+// The plan can split the last groups in two halves of 32 channels each, so
+// that every unit holds its share of whole groups plus at most one half.
+// A half workgroup has the same 4 waves and 256 lanes as a whole one, but
+// each wave holds two 32-lane rows: lanes 0..31 and 32..63 of wave w take
+// state split v = 2w and 2w + 1 of 8 (N/8 states each) for the same 32
+// channels. Every channel's states are spread over 8 lanes, a lane does half
+// the state work of a whole group's lane, and a token's readout sums 8
+// partials. Split v also owns token v of every 8-token tile: it loads,
+// converts and stages that token's inputs for its 32 channels and finishes
+// that token's outputs, so every (channel, token) is converted and finished
+// once. The tile pipeline is the whole group's (inputs two tiles ahead, B/C
+// staged in LDS, one barrier per tile, double-buffered LDS); only the token
+// a lane loads or stores differs per lane, so its row offset goes into the
+// per-lane buffer offset.
+constexpr int kHalf = 32;  // channels of a half group
+constexpr int kSplitsHalf = 8;
+
+template <int N>
+struct HalfLds {
+    float bcs[2][2 * BcStage<N, 4>::kSlots];
+    float2 dtdu[2][TT * kHalf];               // (delta, delta*x) per token and channel
+    float red[2][kSplitsHalf * TT * kHalf];   // partial readouts per split, token, channel
+};
+
+template <int IO>
+__device__ __forceinline__ uint32_t buf_load_lane(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    if constexpr (IO == kIoF32) {
+        return __builtin_amdgcn_raw_buffer_load_b32(r, static_cast<int>(off), 0, 0);
+    } else {
+        return __builtin_amdgcn_raw_buffer_load_b16(r, static_cast<int>(off), 0, 0);
+    }
+}
+
+template <int N, int IO, bool SP, bool HAS_D, bool HAS_Z>
+__device__ __forceinline__ void half_group(const ScanArgs& a, int64_t b, int64_t d0,
+                                           HalfLds<N>& lds) {
+    constexpr int NPS = N / kSplitsHalf;  // states per lane
+    static_assert(N % kSplitsHalf == 0 && TT == kSplitsHalf, "one token per split and tile");
+    constexpr int KP = BcStage<N, 4>::kPerLane;
+    constexpr int P = BcStage<N, 4>::kSlots;
+    constexpr int64_t esz = IO == kIoF32 ? 4 : 2;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int ch = lane & (kHalf - 1);
+    const int v = 2 * (static_cast<int>(threadIdx.x) / kWave) + (lane >> 5);
+    const int n0 = v * NPS;
+    // lanes past the last channel work on channel dim-1 (as in a whole group)
+    const int64_t d = min(d0 + ch, a.dim - 1);
+    const int64_t L = a.seqlen;
+    const int ntok = static_cast<int>(L);
+    const int ntiles = (ntok + TT - 1) / TT;
+    const int nfull = ntok / TT;
+    const float dbias = a.delta_bias != nullptr ? a.delta_bias[d] : 0.0f;
+    const float dskip = HAS_D ? a.D[d] : 0.0f;
+    float A2[NPS], h[NPS];
+#pragma unroll
+    for (int q = 0; q < NPS; ++q) {
+        A2[q] = a.A[d * N + n0 + q] * kLog2e;
+        h[q] = a.h0 != nullptr ? a.h0[(b * a.dim + d) * N + n0 + q] : 0.0f;
+    }
+    // the row from (b, 0, d0) to the end of (b, L-1, dim-1): below 2^32 bytes
+    // because the plan only splits groups of single-chunk scans
+    const int64_t first = b * L * a.dim + d0;
+    const uint32_t extent = static_cast<uint32_t>((L * a.dim - d0) * esz);
+    const uint32_t row_bytes = static_cast<uint32_t>(a.dim * esz);
+    const uint32_t lane_bytes = static_cast<uint32_t>((d - d0) * esz);
+    const auto rx = make_rsrc(static_cast<const char*>(a.x) + first * esz, extent);
+    const auto rdt = make_rsrc(static_cast<const char*>(a.delta) + first * esz, extent);
+    const auto rz = make_rsrc(a.z != nullptr ? static_cast<const char*>(a.z) + first * esz : nullptr,
+                              extent);
+    const auto ry = make_rsrc(static_cast<char*>(a.y) + first * esz, extent);
+    BcIo bcio;
+    bcio.B = make_rsrc(static_cast<const char*>(a.B) + b * L * N * esz,
+                       static_cast<uint32_t>(L * N * esz));
+    bcio.C = make_rsrc(static_cast<const char*>(a.C) + b * L * N * esz,
+                       static_cast<uint32_t>(L * N * esz));
+
+    struct Raw {
+        uint32_t x, dt, z;
+    };
+    struct Epi {
+        float skip, gate;
+    };
+    // this lane's token of tile `tile`, clamped to the sequence (unused copies)
+    auto fetch = [&](int tile, Raw& r) {
+        const int tok = min(tile * TT + v, ntok - 1);
+        const uint32_t off = lane_bytes + static_cast<uint32_t>(tok) * row_bytes;
+        r.x = buf_load_lane<IO>(rx, off);
+        r.dt = buf_load_lane<IO>(rdt, off);
+        r.z = HAS_Z ? buf_load_lane<IO>(rz, off) : 0u;
+    };
+    auto stage = [&](float2* dtdu, const Raw& r, Epi& e) {
+        float dt = raw_to_f32<IO>(r.dt) + dbias;
+        if constexpr (SP) dt = softplus_f32(dt);
+        const float u = raw_to_f32<IO>(r.x);
+        dtdu[v * kHalf + ch] = make_float2(dt, dt * u);
+        e.skip = HAS_D ? dskip * u : 0.0f;
+        e.gate = HAS_Z ? silu(raw_to_f32<IO>(r.z)) : 1.0f;
+    };
+    auto step = [&](auto full_tag, int i, Raw& cur, const Epi& ec, Raw& nxt, Epi& en,
+                    uint32_t (&bf)[KP], uint32_t (&cf)[KP], const uint32_t (&bs)[KP],
+                    const uint32_t (&cs)[KP]) {
+        constexpr bool FULL = decltype(full_tag)::value;
+        const int ifetch = min(i + 2, ntiles - 1);
+        fetch_bc<N, 4, IO>(bcio, ifetch, min(TT, ntok - ifetch * TT), bf, cf);
+        __builtin_amdgcn_sched_barrier(0);
+        fetch(ifetch, cur);
+        __builtin_amdgcn_sched_barrier(0);
+        const int cnt = FULL ? TT : ntok - i * TT;
+        const float* bcs = lds.bcs[i & 1];
+        const float2* dtdu = lds.dtdu[i & 1];
+        float* red = lds.red[i & 1] + v * TT * kHalf + ch;
+        // tokens in pairs: both tokens' LDS inputs before their arithmetic
+#pragma unroll
+        for (int j0 = 0; j0 < TT; j0 += 2) {
+            float2 du[2];
+            float Bq[2][NPS], Cq[2][NPS];
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) {
+                du[jj] = dtdu[(j0 + jj) * kHalf + ch];
+                read_slice<NPS>(bcs + (j0 + jj) * N + n0, Bq[jj]);
+                read_slice<NPS>(bcs + P + (j0 + jj) * N + n0, Cq[jj]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) {
+                const int j = j0 + jj;
+                if (FULL || j < cnt) {
+                    float p = 0.0f;
+#pragma unroll
+                    for (int q = 0; q < NPS; ++q) {
+                        const float e = fast_exp2(du[jj].x * A2[q]);
+                        h[q] = fmaf(e, h[q], du[jj].y * Bq[jj][q]);
+                        p = fmaf(Cq[jj][q], h[q], p);
+                    }
+                    red[j * kHalf] = p;
+                }
+            }
+        }
+        stage_bc<N, 4, IO>(lds.bcs[(i + 1) & 1], bs, cs);
+        stage(lds.dtdu[(i + 1) & 1], nxt, en);
+        __syncthreads();
+        // finish this lane's token of tile i: the 8 partials in split order
+        if (FULL || v < cnt) {
+            const float* col = lds.red[i & 1] + v * kHalf + ch;
+            float acc = col[0];
+#pragma unroll
+            for (int u = 1; u < kSplitsHalf; ++u) acc += col[u * TT * kHalf];
+            acc += ec.skip;
+            if constexpr (HAS_Z) acc *= ec.gate;
+            const uint32_t off = lane_bytes + static_cast<uint32_t>(i * TT + v) * row_bytes;
+            if constexpr (IO == kIoF32) {
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc), ry, static_cast<int>(off),
+                                                      0, 0);
+            } else {
+                const __bf16 hv = static_cast<__bf16>(acc);  // round to nearest even
+                __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, hv), ry,
+                                                      static_cast<int>(off), 0, 0);
+            }
+        }
+    };
+
+    Raw ra, rb;
+    Epi ea, eb;
+    uint32_t bra[KP], cra[KP], brb[KP], crb[KP];
+    fetch_bc<N, 4, IO>(bcio, 0, min(TT, ntok), bra, cra);
+    fetch(0, ra);
+    {
+        const int i1 = min(1, ntiles - 1);
+        fetch_bc<N, 4, IO>(bcio, i1, min(TT, ntok - i1 * TT), brb, crb);
+        fetch(i1, rb);
+    }
+    stage_bc<N, 4, IO>(lds.bcs[0], bra, cra);
+    stage(lds.dtdu[0], ra, ea);
+    __syncthreads();
+    using Full = std::integral_constant<bool, true>;
+    using Ragged = std::integral_constant<bool, false>;
+    // even steps fetch into (ra, bra, cra) and stage (rb, brb, crb), odd steps
+    // the other way round
+    int i = 0;
+    for (; i + 2 <= nfull; i += 2) {
+        step(Full{}, i, ra, ea, rb, eb, bra, cra, brb, crb);
+        step(Full{}, i + 1, rb, eb, ra, ea, brb, crb, bra, cra);
+    }
+    if (i < nfull) {
+        step(Full{}, i, ra, ea, rb, eb, bra, cra, brb, crb);
+        if (nfull < ntiles) step(Ragged{}, i + 1, rb, eb, ra, ea, brb, crb, bra, cra);
+    } else if (nfull < ntiles) {
+        step(Ragged{}, i, ra, ea, rb, eb, bra, cra, brb, crb);
+    }
+    if (a.hL != nullptr) {
+#pragma unroll
+        for (int q = 0; q < NPS; ++q) a.hL[(b * a.dim + d) * N + n0 + q] = h[q];
+    }
+}
+
+// One launch of whole and half groups (single chunk, split 4): blocks
+// [0, nwhole) are whole groups 0 .. nwhole-1 in (row, group) order, the
+// blocks after them the two halves of each remaining group.
+template <int N, int IO, bool SP, bool HAS_D, bool HAS_Z>
+__global__ __launch_bounds__(kWave * 4) __attribute__((amdgpu_waves_per_eu(4)))
+void chunk_mixed_kernel(ScanArgs a, ChunkGrid g, int64_t nwhole) {
+    __shared__ union {
+        ScanLds<N, 4> whole;
+        HalfLds<N> half;
+    } lds;
+    const int64_t blk = blockIdx.x;
+    if (blk < nwhole) {
+        output_group<N, 4, IO, SP, HAS_D, HAS_Z>(a, g, Carry{nullptr, nullptr, nullptr}, blk,
+                                                 lds.whole);
+    } else {
+        const int64_t hb = blk - nwhole;
+        const int64_t grp = nwhole + hb / 2;
+        const int64_t d0 = (grp % g.nblk_d) * kWave + (hb % 2) * kHalf;
+        // a second half wholly past the last channel has nothing to do (the
+        // whole workgroup leaves before its first barrier)
+        if (d0 >= a.dim) return;
+        half_group<N, IO, SP, HAS_D, HAS_Z>(a, grp / g.nblk_d, d0, lds.half);
+    }
+}
+
 // Repaired carry, pass 1: every chunk from a zero state (chunk 0 from h0)
 // writes y and its (end state, decay product) pair, the last chunk's
 // included.
@@ -724,7 +956,7 @@ __global__ __launch_bounds__(kWave * S) __attribute__((amdgpu_waves_per_eu(S <= 
 void chunk_local_kernel(ScanArgs a, ChunkGrid g, Carry c) {
     constexpr int NPW = Split<N, S>::NPW;
     __shared__ ScanLds<N, S> lds;
-    const WaveSlot s = wave_slot<N, S, IO>(a, g);
+    const WaveSlot s = wave_slot<N, S, IO>(a, g, blockIdx.x);
     float A2[NPW], h[NPW];
     const int64_t srow = ((s.k * a.batch + s.b) * a.dim + s.d) * N + s.n0;
 #pragma unroll
@@ -751,7 +983,7 @@ __global__ __launch_bounds__(kWave * S) __attribute__((amdgpu_waves_per_eu(S <= 
 void chunk_fixup_kernel(ScanArgs a, ChunkGrid g, Carry c) {
     constexpr int NPW = Split<N, S>::NPW;
     __shared__ ScanLds<N, S> lds;
-    const WaveSlot s = wave_slot<N, S, IO>(a, g);
+    const WaveSlot s = wave_slot<N, S, IO>(a, g, blockIdx.x);
     float A2[NPW], h[NPW];
     const int64_t srow = ((s.k * a.batch + s.b) * a.dim + s.d) * N + s.n0;
     float a2max = -__builtin_inff();
@@ -805,6 +1037,21 @@ hipError_t launch_scan_ns(const ScanArgs& a, const ScanPlan& plan, void* ws, hip
         c.decay = base + 2 * plan.nchunks * columns;
     }
     const bool has_d = a.D != nullptr, has_z = a.z != nullptr;
+    if constexpr (S == 4 && N % kSplitsHalf == 0) {
+        if (plan.nchunks == 1 && plan.halves > 0) {
+            const int64_t nwhole = g.nblk_d * a.batch - plan.halves;
+            const dim3 grid(nwhole + 2 * plan.halves), block(kWave * S);
+            if (has_d && has_z)
+                hipLaunchKernelGGL((chunk_mixed_kernel<N, IO, SP, true, true>), grid, block, 0, s, a, g, nwhole);
+            else if (has_d)
+                hipLaunchKernelGGL((chunk_mixed_kernel<N, IO, SP, true, false>), grid, block, 0, s, a, g, nwhole);
+            else if (has_z)
+                hipLaunchKernelGGL((chunk_mixed_kernel<N, IO, SP, false, true>), grid, block, 0, s, a, g, nwhole);
+            else
+                hipLaunchKernelGGL((chunk_mixed_kernel<N, IO, SP, false, false>), grid, block, 0, s, a, g, nwhole);
+            return hipGetLastError();
+        }
+    }
     if (plan.nchunks > 1 && plan.carry == kCarryRepair) {
         if (has_d && has_z) return launch_repaired<N, S, IO, SP, true, true>(a, g, c, columns, s);
         if (has_d) return launch_repaired<N, S, IO, SP, true, false>(a, g, c, columns, s);

@@ -48,8 +48,8 @@ P = ctypes.c_void_p(0x10000)
 PM = ctypes.c_void_p(0x10008)  # not 16-byte aligned
 
 
-def _plan(chunk_len=0, split=0, carry=0):
-    return ctypes.byref(ms.ScanPlan(chunk_len, split, carry))
+def _plan(chunk_len=0, split=0, carry=0, halves=0, reserved=0):
+    return ctypes.byref(ms.ScanPlan(chunk_len, split, carry, halves, reserved))
 
 
 def _opts(bias=None, softplus=0, reserved=0):
@@ -137,8 +137,41 @@ def test_scan_carry_choice(lib):
     assert resolve(1 << 14, 256, ms.CARRY_REPAIR)[0] == ms.CARRY_REPAIR
     assert resolve(1 << 14, 4096, ms.CARRY_REPAIR)[1] == resolve(1 << 14, 4096,
                                                                   ms.CARRY_RERUN)[1] > 0
-    # one chunk: no carry at all, reported as the rerun form
-    assert resolve(4096, 4096) == (ms.CARRY_RERUN, 0)
+    # one chunk: no carry at all, reported as the rerun form (halves off: an
+    # automatic choice of them would query the device)
+    assert lib.ssm_scan_fwd_workspace_size(1, 4096, 64, 16, 1, _plan(4096, 4, 0, -1),
+                                           ctypes.byref(got), ctypes.byref(need)) == OK
+    assert (got.carry, need.value) == (ms.CARRY_RERUN, 0)
+
+
+def test_scan_halves_choice(lib):
+    """Half channel groups: only one chunk, split 4, dstate 8 or 16; at most
+    the number of groups; reported as the number of groups split."""
+    got = ms.ScanPlan(0, 0, 0, 0, 0)
+    need = ctypes.c_size_t(0)
+
+    def resolve(batch=2, seqlen=64, dim=200, dstate=16, chunk_len=64, split=4, halves=0,
+                reserved=0):
+        st = lib.ssm_scan_fwd_workspace_size(batch, seqlen, dim, dstate, 1,
+                                             _plan(chunk_len, split, 0, halves, reserved),
+                                             ctypes.byref(got), ctypes.byref(need))
+        return st, got.halves
+
+    # 2 rows x 4 groups of 64 channels = 8 groups
+    assert resolve(halves=3) == (OK, 3)
+    assert resolve(halves=8) == (OK, 8)
+    assert resolve(halves=-1) == (OK, 0)
+    assert resolve(dstate=8, halves=2) == (OK, 2)
+    assert resolve(halves=9)[0] == INVALID
+    assert resolve(halves=-2)[0] == INVALID
+    assert resolve(halves=-1, reserved=1)[0] == INVALID
+    assert resolve(chunk_len=32, halves=1)[0] == UNSUPPORTED      # two chunks
+    assert resolve(split=2, halves=1)[0] == UNSUPPORTED
+    assert resolve(dstate=4, halves=1)[0] == UNSUPPORTED
+    assert resolve(dstate=12, split=1, halves=1)[0] == UNSUPPORTED
+    # an empty scan runs nothing: the request is moot
+    assert resolve(seqlen=0, halves=5) == (OK, 0)
+    assert _scan(lib, plan=_plan(8, 4, 0, 0, 1)) == INVALID
 
 
 def test_scan_empty_shapes_are_noops(lib):
