@@ -100,7 +100,14 @@ def algorithmic_alu_ops(w, softplus=False):
 
 
 COPY_BYTES = 1 << 30
-DOMINANT = "chunk_output_kernel"
+# The kernel of a single-chunk scan: one launch of whole channel groups, or
+# of whole and half groups when the plan splits some.
+KERNEL_WHOLE = "chunk_output_kernel"
+KERNEL_MIXED = "chunk_mixed_kernel"
+
+
+def dominant_kernel(plan):
+    return KERNEL_MIXED if plan.halves > 0 else KERNEL_WHOLE
 KERNEL_SOURCES = [os.path.join(ROOT, "selective_state_space_40_amd", "csrc", f)
                   for f in ("internal.h", "device_common.h", "scan_chunked.h", "scan_variant.hip")]
 
@@ -134,14 +141,17 @@ def record_traffic(args):
     """HBM bytes per launch of the dominant kernel from FETCH_SIZE and
     WRITE_SIZE (KiB per dispatch), each scaled by what the same counter reads
     for a plain copy of COPY_BYTES (read COPY_BYTES, write COPY_BYTES)."""
+    import csv
     fetch_csv, write_csv, cfetch_csv, cwrite_csv = args.record_traffic
-    fetch = _counter_per_dispatch(fetch_csv, "FETCH_SIZE", DOMINANT)
-    write = _counter_per_dispatch(write_csv, "WRITE_SIZE", DOMINANT)
+    names = {r["Kernel_Name"] for r in csv.DictReader(open(fetch_csv))}
+    kernel = KERNEL_MIXED if any(KERNEL_MIXED in n for n in names) else KERNEL_WHOLE
+    fetch = _counter_per_dispatch(fetch_csv, "FETCH_SIZE", kernel)
+    write = _counter_per_dispatch(write_csv, "WRITE_SIZE", kernel)
     cfetch = _counter_per_dispatch(cfetch_csv, "FETCH_SIZE", "copy")
     cwrite = _counter_per_dispatch(cwrite_csv, "WRITE_SIZE", "copy")
     fetch_scale = COPY_BYTES / cfetch
     write_scale = COPY_BYTES / cwrite
-    out = {"workload": args.workload, "kernel": DOMINANT, "source_sha256_16": source_hash(),
+    out = {"workload": args.workload, "kernel": kernel, "source_sha256_16": source_hash(),
            "fetch_bytes": fetch * fetch_scale, "write_bytes": write * write_scale,
            "traffic_bytes": fetch * fetch_scale + write * write_scale,
            "fetch_kib_raw": fetch, "write_kib_raw": write,
@@ -163,15 +173,15 @@ def calibrate_copy():
     print(json.dumps({"calibration_copy_bytes": COPY_BYTES, "launches": 3}))
 
 
-def recorded_traffic(workload):
-    """Measured HBM bytes per launch, or None when not recorded or recorded
-    for a different kernel source."""
+def recorded_traffic(workload, kernel):
+    """Measured HBM bytes per launch, or None when not recorded, recorded
+    for another kernel or recorded for a different kernel source."""
     try:
         with open(traffic_path(workload)) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("source_sha256_16") != source_hash():
+    if rec.get("source_sha256_16") != source_hash() or rec.get("kernel") != kernel:
         return None
     return rec.get("traffic_bytes")
 
@@ -262,16 +272,19 @@ def main():
     ops = algorithmic_alu_ops(w, sp)
     tops = ops / sec / 1e12
 
-    # Dominant kernel: the output pass (chunk_output_kernel). With a single
+    # Dominant kernel: the output pass (chunk_output_kernel, or
+    # chunk_mixed_kernel when the plan splits channel groups). With a single
     # chunk the step is exactly that one launch, so the event time per step
     # is its launch duration; with several chunks the step also holds the
     # carry pass and either the summary pass or the head reruns, and the
-    # figure covers the whole step.
+    # figure covers the whole step. Recorded traffic is used only for the
+    # workload's own automatic plan.
     hbm_frac = gbps / HBM_PEAK_GBPS
     alu_frac = tops / ALU_PEAK_TOPS
     bound = "alu" if ops / (ALU_PEAK_TOPS * 1e12) > bytes_alg / (HBM_PEAK_GBPS * 1e9) else "hbm"
-    plain = not (args.batch or args.dim or sp)
-    traffic = recorded_traffic(w.name) if nchunks == 1 and plain else None
+    plain = not (args.batch or args.dim or sp or args.chunk_len or args.state_split or args.halves
+                 or args.carry != "auto")
+    traffic = recorded_traffic(w.name, dominant_kernel(plan)) if nchunks == 1 and plain else None
     roofline = {
         "bound": bound,
         "achieved": round(tops if bound == "alu" else gbps, 3),
@@ -279,7 +292,7 @@ def main():
         "unit": "Tops/s (fp32 lane-ops)" if bound == "alu" else "GB/s",
         "frac": round(alu_frac if bound == "alu" else hbm_frac, 4),
         "traffic": traffic,
-        "kernel": DOMINANT if nchunks == 1 else "ssm_scan_fwd step (all passes)",
+        "kernel": dominant_kernel(plan) if nchunks == 1 else "ssm_scan_fwd step (all passes)",
         "algorithmic_bytes": bytes_alg,
         "algorithmic_ops": ops,
         "hbm_GBps": round(gbps, 1),

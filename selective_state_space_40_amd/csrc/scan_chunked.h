@@ -925,7 +925,15 @@ __device__ __forceinline__ void half_group(const ScanArgs& a, int64_t b, int64_t
 
 // One launch of whole and half groups (single chunk, split 4): blocks
 // [0, nwhole) are whole groups 0 .. nwhole-1 in (row, group) order, the
-// blocks after them the two halves of each remaining group.
+// blocks after them the two halves of each remaining group. The two halves
+// of a group read the two 64-byte halves of the same 128-byte rows of x,
+// delta and z, so they are placed 8 blocks apart: blocks go to the chip's 8
+// XCDs in turn (block i to XCD i mod 8) and each XCD has its own L2, which
+// then fetches those rows once for both (consecutive halves on two XCDs
+// read the split groups' rows twice from HBM: +100 MB per Mamba-2.8B
+// layer). Within every 16 half blocks, block r < 8 is half 0 and block
+// 8 + r half 1 of the same group; a last partial run of blocks pairs
+// neighbours.
 template <int N, int IO, bool SP, bool HAS_D, bool HAS_Z>
 __global__ __launch_bounds__(kWave * 4) __attribute__((amdgpu_waves_per_eu(4)))
 void chunk_mixed_kernel(ScanArgs a, ChunkGrid g, int64_t nwhole) {
@@ -939,8 +947,18 @@ void chunk_mixed_kernel(ScanArgs a, ChunkGrid g, int64_t nwhole) {
                                                  lds.whole);
     } else {
         const int64_t hb = blk - nwhole;
-        const int64_t grp = nwhole + hb / 2;
-        const int64_t d0 = (grp % g.nblk_d) * kWave + (hb % 2) * kHalf;
+        const int64_t nhb = static_cast<int64_t>(gridDim.x) - nwhole;
+        const int64_t run = hb / 16, r = hb % 16;
+        int64_t pair, side;
+        if ((run + 1) * 16 <= nhb) {
+            pair = run * 8 + r % 8;
+            side = r / 8;
+        } else {
+            pair = hb / 2;
+            side = hb % 2;
+        }
+        const int64_t grp = nwhole + pair;
+        const int64_t d0 = (grp % g.nblk_d) * kWave + side * kHalf;
         // a second half wholly past the last channel has nothing to do (the
         // whole workgroup leaves before its first barrier)
         if (d0 >= a.dim) return;
