@@ -471,7 +471,7 @@ def bench_backward(args, w):
         inp = sets[i % 2]
         ms.scan_bwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"],
                     inp["h0"], dy=inp["dy"], delta_bias=inp.get("delta_bias"),
-                    delta_softplus=sp)
+                    delta_softplus=sp, halves=args.halves)
 
     ms_per_step, wall = _time_steps(step, args.warmup, args.steps, torch.cuda.current_stream(dev),
                                       args.spin_up)
@@ -490,6 +490,7 @@ def bench_backward(args, w):
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "seqlen": w.seqlen, "dim": w.dim,
                    "dstate": w.dstate, "io_dtype": w.io, "checkpoint_every": 8,
+                   "half_groups": bwd_half_groups(w, args.halves),
                    "delta_activation": "bias + softplus in the kernels" if sp else
                                        "none (delta passed activated)",
                    "parallelism": "single GPU"},
@@ -520,6 +521,19 @@ def _oracle_passes(run, seconds):
 
 def _passes_text(passes, dt):
     return f"{passes} pass{'es' if passes > 1 else ''} in {dt:.1f} s"
+
+
+def bwd_half_groups(w, requested):
+    """Channel groups the backward pass runs as halves: the count asked for,
+    or the library's automatic rule (the groups whole rounds of the chip's
+    compute units leave over, when at most half a round; dstate 13..16)."""
+    import torch
+    if requested != 0 or not 13 <= w.dstate <= 16:
+        return max(requested, 0) if 13 <= w.dstate <= 16 else 0
+    cu = torch.cuda.get_device_properties(0).multi_processor_count
+    groups = w.batch * -(-w.dim // 64)
+    surplus = groups % cu
+    return surplus if 0 < surplus and 2 * surplus <= cu else 0
 
 
 def cpu_baseline_backward(w, inp, softplus, seconds):

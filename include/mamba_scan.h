@@ -242,6 +242,11 @@ int ssm_state_update(int64_t batch, int64_t dim, int dstate, int dtype, float* h
  *                                                 h0 is NULL)
  * ddelta_bias  (dim) fp32                         optional; must be NULL when
  *                                                 options carry no delta_bias
+ * plan         may be NULL (automatic). Only `halves` applies (see
+ *              mamba_scan_plan: channel groups run as two 32-channel halves,
+ *              available for dstate 13..16, automatic by the same rule as
+ *              the forward scan); chunk_len, state_split, carry and reserved
+ *              must be 0.
  * workspace    at least ssm_scan_bwd_workspace_size bytes
  *
  * The intermediate states are recomputed from checkpoints every 8 tokens
@@ -256,7 +261,8 @@ int ssm_scan_bwd_workspace_size(int64_t batch, int64_t seqlen, int64_t dim, int 
 int ssm_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int dstate, int dtype,
                  const void* x, const void* delta, const float* A, const void* B,
                  const void* C, const float* D, const void* z, const float* h0,
-                 const mamba_scan_options* options, const void* dy, const float* dhL,
+                 const mamba_scan_options* options, const mamba_scan_plan* plan,
+                 const void* dy, const float* dhL,
                  void* dx, void* ddelta, float* dA, float* dB, float* dC, float* dD,
                  void* dz, float* dh0, float* ddelta_bias, void* workspace,
                  size_t workspace_bytes, hipStream_t stream);

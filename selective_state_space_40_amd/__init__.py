@@ -102,7 +102,7 @@ def load_library():
     lib.ssm_scan_bwd_workspace_size.argtypes = [i64, i64, i64, i32, i32,
                                                 ctypes.POINTER(ctypes.c_size_t)]
     lib.ssm_scan_bwd_workspace_size.restype = i32
-    lib.ssm_scan_bwd.argtypes = ([i64, i64, i64, i32, i32] + [vp] * 8 + [po] + [vp] * 11 +
+    lib.ssm_scan_bwd.argtypes = ([i64, i64, i64, i32, i32] + [vp] * 8 + [po, pp] + [vp] * 11 +
                                  [vp, ctypes.c_size_t, vp])
     lib.ssm_scan_bwd.restype = i32
     lib.ssd_fwd.argtypes = [i64, i64, i64, i64, i32, i32] + [vp] * 10 + [po, vp]
@@ -239,11 +239,13 @@ def scan_fwd(x, delta, A, B, C, D=None, z=None, h0=None, *, delta_bias=None,
 
 
 def scan_bwd(x, delta, A, B, C, D=None, z=None, h0=None, *, dy, dhL=None, delta_bias=None,
-             delta_softplus=False, want_dh0=True):
+             delta_softplus=False, want_dh0=True, halves=HALVES_AUTO):
     """Gradients of sum(dy * y) + sum(dhL * hL) for the scan_fwd call with the
     same inputs. Returns a dict: dx, ddelta, dz (like x, I/O dtype); dB, dC
     (batch, L, N) fp32; dA (dim, N) fp32; dD, ddelta_bias (dim,) fp32; dh0
-    (batch, dim, N) fp32. Entries of absent optional inputs are None."""
+    (batch, dim, N) fp32. Entries of absent optional inputs are None.
+    `halves` is the number of the last channel groups run as two 32-channel
+    halves (HALVES_AUTO: the library's choice, HALVES_NONE: none; N 13..16)."""
     lib = load_library()
     if x.dim() != 3:
         raise ValueError("x must be (batch, L, dim)")
@@ -283,7 +285,8 @@ def scan_bwd(x, delta, A, B, C, D=None, z=None, h0=None, *, dy, dhL=None, delta_
         ws = _workspace(dev, nbytes.value, "bwd")
         st = lib.ssm_scan_bwd(batch, seqlen, dim, dstate, _DTYPES[dt], _ptr(x), _ptr(delta),
                               _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0),
-                              _options(delta_bias, delta_softplus), _ptr(dy), _ptr(dhL),
+                              _options(delta_bias, delta_softplus),
+                              ctypes.byref(ScanPlan(0, 0, 0, halves, 0)), _ptr(dy), _ptr(dhL),
                               _ptr(g["dx"]), _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]),
                               _ptr(g["dC"]), _ptr(g["dD"]), _ptr(g["dz"]), _ptr(g["dh0"]),
                               _ptr(g["ddelta_bias"]), _ptr(ws), nbytes.value, _stream(dev))

@@ -307,12 +307,23 @@ int ssm_scan_bwd_workspace_size(int64_t batch, int64_t seqlen, int64_t dim, int 
 int ssm_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int dstate, int dtype,
                  const void* x, const void* delta, const float* A, const void* B,
                  const void* C, const float* D, const void* z, const float* h0,
-                 const mamba_scan_options* options, const void* dy, const float* dhL,
+                 const mamba_scan_options* options, const mamba_scan_plan* plan,
+                 const void* dy, const float* dhL,
                  void* dx, void* ddelta, float* dA, float* dB, float* dC, float* dD,
                  void* dz, float* dh0, float* ddelta_bias, void* workspace,
                  size_t workspace_bytes, hipStream_t stream) {
     int st = check_shape(batch, seqlen, dim, dstate, dtype);
     if (st != MAMBA_OK) return st;
+    // only `halves` applies to the backward pass
+    if (plan != nullptr && (plan->chunk_len != 0 || plan->state_split != 0 || plan->carry != 0 ||
+                            plan->reserved != 0 || plan->halves < -1))
+        return MAMBA_ERR_INVALID_ARG;
+    const int64_t halves_req = plan != nullptr ? plan->halves : 0;
+    const int64_t groups = batch * ((dim + mamba::kWave - 1) / mamba::kWave);
+    const bool runs = batch > 0 && seqlen > 0 && dim > 0;  // else any request is moot
+    if (runs && halves_req > 0 && !mamba::bwd_halves_supported(dstate))
+        return MAMBA_ERR_UNSUPPORTED;
+    if (runs && halves_req > groups) return MAMBA_ERR_INVALID_ARG;
     const float* delta_bias = nullptr;
     int delta_softplus = 0;
     st = read_options(options, &delta_bias, &delta_softplus);
@@ -333,6 +344,21 @@ int ssm_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int dstate, int dty
     const size_t need = mamba::scan_bwd_workspace_bytes(batch, seqlen, dim, dstate);
     if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return MAMBA_ERR_WORKSPACE;
     mamba::BwdArgs a;
+    a.halves = 0;
+    if (runs && mamba::bwd_halves_supported(dstate)) {
+        if (halves_req > 0) {
+            a.halves = halves_req;
+        } else if (halves_req == 0) {
+            // as the forward plan: the groups whole rounds leave over, when
+            // they are at most half a round
+            int cu = 0;
+            st = current_cu_count(&cu);
+            if (st != MAMBA_OK) return st;
+            const int64_t surplus = groups % cu;
+            if (surplus > 0 && 2 * surplus <= cu) a.halves = surplus;
+        }
+        if (groups + a.halves > (int64_t(1) << 31)) return MAMBA_ERR_UNSUPPORTED;
+    }
     a.fwd.batch = batch;
     a.fwd.seqlen = seqlen;
     a.fwd.dim = dim;

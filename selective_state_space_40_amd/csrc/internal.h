@@ -121,7 +121,12 @@ struct BwdArgs {
     void* dz;              // (batch, seqlen, dim) I/O dtype, or nullptr
     float* dh0;            // (batch, dim, dstate) or nullptr
     float* ddelta_bias;    // (dim) or nullptr
+    int64_t halves = 0;    // last channel groups run as two 32-channel halves (dstate 13..16)
 };
+
+// The backward pass can split channel groups into halves when a channel's
+// states fill 4 waves of 4 (dstate 13..16).
+inline bool bwd_halves_supported(int dstate) { return dstate >= 13 && dstate <= 16; }
 
 // Scratch bytes of the backward pass for this shape.
 size_t scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int dstate);

@@ -160,8 +160,8 @@ __device__ __forceinline__ void put_tile(const TileRaw<S>& r, const Place& pl, B
 // second's) leaves each lane exactly its own kept value and its partner's,
 // so their sum is the step; for k <= 8 DPP row shifts bring lane l + k and
 // l - k within the 16-lane row.
-template <int K>
-__device__ __forceinline__ void fold_dpp(float (&vals)[kVals], int cnt, int lane) {
+template <int K, int M>
+__device__ __forceinline__ void fold_dpp(float (&vals)[M], int cnt, int lane) {
     const bool hi = (lane & K) != 0;
     for (int i = 0; i < cnt; ++i) {
         const float a = vals[2 * i], b = vals[2 * i + 1];
@@ -192,27 +192,62 @@ __device__ __forceinline__ float lane_sums(float (&vals)[kVals]) {
     return vals[0];
 }
 
+// The same over the 32 lanes of each half of the wave (the rows of a half
+// group, which hold different states): 32 values, steps k = 16, ..., 1; lane
+// l holds the sum of value reverse5(l mod 32) over its 32-lane half.
+__device__ __forceinline__ float lane_sums32(float (&vals)[kWave / 2]) {
+    const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(vals[2 * i]),
+                                                        __float_as_uint(vals[2 * i + 1]), false, false);
+        vals[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+    fold_dpp<8>(vals, 8, lane);
+    fold_dpp<4>(vals, 4, lane);
+    fold_dpp<2>(vals, 2, lane);
+    fold_dpp<1>(vals, 1, lane);
+    return vals[0];
+}
+
+__device__ __forceinline__ int reverse5(int l) {
+    return ((l & 1) << 4) | ((l & 2) << 2) | (l & 4) | ((l & 8) >> 2) | ((l & 16) >> 4);
+}
+
 __device__ __forceinline__ int reverse6(int l) {
     return ((l & 1) << 5) | ((l & 2) << 3) | ((l & 4) << 1) | ((l & 8) >> 1) | ((l & 16) >> 3) |
            ((l & 32) >> 5);
 }
 
+// Workspace pointers of the main kernel. part_bc holds nslots partial dB/dC
+// slots per (row, token, state): slot g for channel group g (its first half
+// when split), slot ngroups + g for the second half of a split group g.
+struct BwdWs {
+    float* tent;
+    float* part_bc;
+    float* part_a;
+    float* part_d;
+    float* part_bias;
+    int64_t nslots;
+};
+
 template <int S, int IO, bool SP, bool HAS_D, bool HAS_Z>
-__global__ __launch_bounds__(kWave * S) __attribute__((amdgpu_waves_per_eu(S == 4 ? 3 : 1)))
-void scan_bwd_kernel(BwdArgs a, int64_t ngroups,
-                                                             float* tent,
-                                                             float* part_bc, float* part_a,
-                                                             float* part_d, float* part_bias) {
+__device__ __forceinline__ void bwd_whole_group(const BwdArgs& a, int64_t ngroups, int64_t blk,
+                                                const BwdWs& ws, BwdLds<S>& lds) {
     constexpr int OW = (kBT + S - 1) / S;
-    __shared__ BwdLds<S> lds;
+    float* const tent = ws.tent;
+    float* const part_bc = ws.part_bc;
+    float* const part_a = ws.part_a;
+    float* const part_d = ws.part_d;
+    float* const part_bias = ws.part_bias;
     const ScanArgs& f = a.fwd;
     const int N = f.dstate;
     const int64_t L = f.seqlen;
     const int lane = threadIdx.x & (kWave - 1);
 
     Place pl;
-    pl.grp = blockIdx.x % ngroups;
-    pl.b = blockIdx.x / ngroups;
+    pl.grp = blk % ngroups;
+    pl.b = blk / ngroups;
     pl.w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
     pl.n0 = pl.w * kNpw;
     const int64_t d_raw = pl.grp * kWave + lane;
@@ -391,7 +426,7 @@ void scan_bwd_kernel(BwdArgs a, int64_t ngroups,
                 const int n = pl.n0 + (r - j * kNpw);
                 if (j < cnt && n < N) {
                     const int64_t per = f.batch * L * N;
-                    part_bc[(which * ngroups + pl.grp) * per + (pl.b * L + t0 + j) * N + n] = sum;
+                    part_bc[(which * ws.nslots + pl.grp) * per + (pl.b * L + t0 + j) * N + n] = sum;
                 }
             }
             __syncthreads();
@@ -458,17 +493,380 @@ void scan_bwd_kernel(BwdArgs a, int64_t ngroups,
     }
 }
 
-// dB and dC: the partials of all channel groups added in group order.
-__global__ __launch_bounds__(256) void bwd_bc_reduce_kernel(int64_t per, int64_t ngroups,
-                                                            const float* part, float* dB,
-                                                            float* dC) {
+// ---------------------------------------------------------------------------
+// Half channel groups (dstate 13..16, 4 waves). As in the forward scan, a
+// launch of G groups on C compute units leaves some units a workgroup more
+// than others unless C divides G, and the plan can run the last groups as
+// two halves of 32 channels: lanes 0..31 and 32..63 of wave w take state
+// split v = 2w and 2w + 1 of 8 (2 states each, padded past dstate) for the
+// same 32 channels, so a lane does half a whole lane's state work. Split v
+// also stages and finishes token v of every 8-token tile. Per-token sums over
+// states go through LDS as 8 partials, and dB, dC are summed over the 32
+// channels of each half-wave row by lane_sums32; a group's second half
+// writes them to its own slot, which the reduction adds for split groups.
+constexpr int kHalfCh = 32;     // channels of a half group
+constexpr int kHalfSplits = 8;  // state splits of a half group
+constexpr int kHalfNps = 2;     // states per lane of a half group
+constexpr int kHalfVals = 2 * kBT * kHalfNps;
+static_assert(kHalfVals == kWave / 2, "the half butterfly leaves one sum per lane");
+
+struct BwdHalfLds {
+    float2 dtx[kBT][kHalfCh];
+    float g[kBT][kHalfCh];
+    alignas(16) float bc[2][kBT][kHalfSplits * kHalfNps];
+    float red[3][kHalfSplits][kBT][kHalfCh];
+};
+
+template <int IO, bool SP, bool HAS_D, bool HAS_Z>
+__device__ __forceinline__ void bwd_half_group(const BwdArgs& a, int64_t ngroups, int64_t b,
+                                               int64_t grp, int side, const BwdWs& ws,
+                                               BwdHalfLds& lds) {
+    constexpr int NP = kHalfSplits * kHalfNps;  // 16 padded states
+    const ScanArgs& f = a.fwd;
+    const int N = f.dstate;
+    const int64_t L = f.seqlen;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int ch = lane & (kHalfCh - 1);
+    const int v = 2 * (static_cast<int>(threadIdx.x) / kWave) + (lane >> 5);
+    const int n0 = v * kHalfNps;
+    const int64_t d_raw = grp * kWave + side * kHalfCh + ch;
+    const bool valid = d_raw < f.dim;
+    const int64_t d = valid ? d_raw : f.dim - 1;
+    const float dbias = f.delta_bias != nullptr ? f.delta_bias[d] : 0.0f;
+    const float dskip = HAS_D ? f.D[d] : 0.0f;
+    const int64_t slot = side == 0 ? grp : ngroups + grp;
+
+    bool sv[kHalfNps];
+    float A[kHalfNps], A2[kHalfNps], lam[kHalfNps], en[kHalfNps], dA[kHalfNps];
+#pragma unroll
+    for (int q = 0; q < kHalfNps; ++q) {
+        const int n = n0 + q;
+        sv[q] = n < N;
+        A[q] = sv[q] ? f.A[d * N + n] : 0.0f;
+        A2[q] = A[q] * kLog2e;
+        lam[q] = (sv[q] && a.dhL != nullptr) ? a.dhL[(b * f.dim + d) * N + n] : 0.0f;
+        en[q] = 1.0f;
+        dA[q] = 0.0f;
+    }
+    float dD_acc = 0.0f, dbias_acc = 0.0f;
+    Own own;
+
+    struct Raw {
+        uint32_t x, dl, dy, z, bc;
+        float he[kHalfNps];
+    };
+    // token v of tile `tile` for this lane's channel, one B or C element per
+    // thread and, walking backwards, the tile's checkpointed states; every
+    // index clamped into range (the clamped values are never used)
+    auto fetch = [&](auto want_g, int64_t tile, int cnt, Raw& r) {
+        constexpr bool WANT_G = decltype(want_g)::value;
+        const int64_t t0 = tile * kBT;
+        const int j = min(v, cnt - 1);
+        const int64_t idx = (b * L + t0 + j) * f.dim + d;
+        r.x = load_raw<IO>(f.x, idx);
+        r.dl = load_raw<IO>(f.delta, idx);
+        if constexpr (WANT_G) {
+            r.dy = load_raw<IO>(a.dy, idx);
+            r.z = HAS_Z ? load_raw<IO>(f.z, idx) : 0u;
+        }
+        const int e = threadIdx.x;  // exactly one B or C element per thread
+        const int which = e / (kBT * NP);
+        const int rr = e - which * kBT * NP;
+        const int jb = min(rr / NP, cnt - 1);
+        const int n = min(rr % NP, N - 1);
+        r.bc = load_raw<IO>(which ? f.C : f.B, (b * L + t0 + jb) * N + n);
+        if constexpr (WANT_G) {
+            const float* row = ws.tent + ((tile * f.batch + b) * f.dim + d) * N;
+#pragma unroll
+            for (int q = 0; q < kHalfNps; ++q) r.he[q] = row[min(n0 + q, N - 1)];
+        }
+    };
+    auto put = [&](auto want_g, const Raw& r, int cnt) {
+        constexpr bool WANT_G = decltype(want_g)::value;
+        if (v < cnt) {
+            float xf = raw_to_f32<IO>(r.x);
+            const float vv = raw_to_f32<IO>(r.dl) + dbias;
+            const float dt = SP ? softplus_f32(vv) : vv;
+            if (!valid) xf = 0.0f;  // a clamped lane contributes nothing
+            lds.dtx[v][ch] = make_float2(dt, xf);
+            if constexpr (WANT_G) {
+                const float dyf = raw_to_f32<IO>(r.dy);
+                const float zf = HAS_Z ? raw_to_f32<IO>(r.z) : 0.0f;
+                float gg = HAS_Z ? dyf * silu(zf) : dyf;
+                if (!valid) gg = 0.0f;
+                lds.g[v][ch] = gg;
+                own = Own{dyf, zf, vv, xf};
+            }
+        }
+        const int e = threadIdx.x;
+        const int which = e / (kBT * NP);
+        const int rr = e - which * kBT * NP;
+        const bool in = rr / NP < cnt && rr % NP < N;  // padding states and tokens read as 0
+        lds.bc[which][rr / NP][rr % NP] = in ? raw_to_f32<IO>(r.bc) : 0.0f;
+    };
+    using No = std::integral_constant<bool, false>;
+    using Yes = std::integral_constant<bool, true>;
+
+    const int64_t ntiles = (L + kBT - 1) / kBT;
+    // (1) forward over the whole sequence, keeping the state entering every
+    // tile (only real lanes and states write)
+    {
+        float h[kHalfNps];
+#pragma unroll
+        for (int q = 0; q < kHalfNps; ++q)
+            h[q] = (sv[q] && f.h0 != nullptr) ? f.h0[(b * f.dim + d) * N + n0 + q] : 0.0f;
+        Raw raw;
+        fetch(No{}, 0, static_cast<int>(min<int64_t>(kBT, L)), raw);
+        for (int64_t i = 0; i < ntiles; ++i) {
+            const int64_t t0 = i * kBT;
+            const int cnt = static_cast<int>(min<int64_t>(kBT, L - t0));
+            if (valid) {
+                float* row = ws.tent + ((i * f.batch + b) * f.dim + d) * N + n0;
+#pragma unroll
+                for (int q = 0; q < kHalfNps; ++q)
+                    if (sv[q]) row[q] = h[q];
+            }
+            put(No{}, raw, cnt);
+            __syncthreads();
+            {
+                const int64_t nx = min(i + 1, ntiles - 1);
+                fetch(No{}, nx, static_cast<int>(min<int64_t>(kBT, L - nx * kBT)), raw);
+            }
+#pragma unroll
+            for (int j0 = 0; j0 < kBT; j0 += 2) {
+                float2 vq[2], bq[2];
+#pragma unroll
+                for (int jj = 0; jj < 2; ++jj) {
+                    vq[jj] = lds.dtx[j0 + jj][ch];
+                    bq[jj] = *reinterpret_cast<const float2*>(&lds.bc[0][j0 + jj][n0]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int jj = 0; jj < 2; ++jj) {
+                    if (j0 + jj < cnt) {
+                        const float du = vq[jj].x * vq[jj].y;
+                        h[0] = fmaf(fast_exp2(vq[jj].x * A2[0]), h[0], du * bq[jj].x);
+                        h[1] = fmaf(fast_exp2(vq[jj].x * A2[1]), h[1], du * bq[jj].y);
+                    }
+                }
+            }
+            __syncthreads();
+        }
+    }
+
+    // (2) the tiles in reverse
+    {
+        Raw raw;
+        fetch(Yes{}, ntiles - 1, static_cast<int>(L - (ntiles - 1) * kBT), raw);
+        for (int64_t i = ntiles - 1; i >= 0; --i) {
+            const int64_t t0 = i * kBT;
+            const int cnt = static_cast<int>(min<int64_t>(kBT, L - t0));
+            float he[kHalfNps], hs[kBT][kHalfNps], h[kHalfNps];
+#pragma unroll
+            for (int q = 0; q < kHalfNps; ++q) he[q] = (valid && sv[q]) ? raw.he[q] : 0.0f;
+            put(Yes{}, raw, cnt);
+            __syncthreads();
+            fetch(Yes{}, i > 0 ? i - 1 : 0, kBT < L ? kBT : static_cast<int>(L), raw);
+
+#pragma unroll
+            for (int q = 0; q < kHalfNps; ++q) h[q] = he[q];
+#pragma unroll
+            for (int j0 = 0; j0 < kBT; j0 += 2) {
+                float2 vq[2], bq[2];
+#pragma unroll
+                for (int jj = 0; jj < 2; ++jj) {
+                    vq[jj] = lds.dtx[j0 + jj][ch];
+                    bq[jj] = *reinterpret_cast<const float2*>(&lds.bc[0][j0 + jj][n0]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int jj = 0; jj < 2; ++jj) {
+                    const int j = j0 + jj;
+                    if (j < cnt) {
+                        const float du = vq[jj].x * vq[jj].y;
+                        h[0] = fmaf(fast_exp2(vq[jj].x * A2[0]), h[0], du * bq[jj].x);
+                        h[1] = fmaf(fast_exp2(vq[jj].x * A2[1]), h[1], du * bq[jj].y);
+                    }
+                    hs[j][0] = h[0];
+                    hs[j][1] = h[1];
+                }
+            }
+
+            float vals[kHalfVals];
+#pragma unroll
+            for (int e = 0; e < kHalfVals; ++e) vals[e] = 0.0f;
+#pragma unroll
+            for (int j1 = kBT - 1; j1 >= 0; j1 -= 2) {
+                float2 vv[2], bq[2], cq[2];
+                float gq[2];
+#pragma unroll
+                for (int jj = 0; jj < 2; ++jj) {
+                    vv[jj] = lds.dtx[j1 - jj][ch];
+                    gq[jj] = lds.g[j1 - jj][ch];
+                    bq[jj] = *reinterpret_cast<const float2*>(&lds.bc[0][j1 - jj][n0]);
+                    cq[jj] = *reinterpret_cast<const float2*>(&lds.bc[1][j1 - jj][n0]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int jj = 0; jj < 2; ++jj) {
+                    const int j = j1 - jj;
+                    if (j < cnt) {
+                        const float dt = vv[jj].x, x = vv[jj].y;
+                        const float gg = gq[jj];
+                        const float Bv[kHalfNps] = {bq[jj].x, bq[jj].y};
+                        const float Cv[kHalfNps] = {cq[jj].x, cq[jj].y};
+                        float dxp = 0.0f, ddp = 0.0f, pp = 0.0f;
+#pragma unroll
+                        for (int q = 0; q < kHalfNps; ++q) {
+                            lam[q] = fmaf(en[q], lam[q], Cv[q] * gg);
+                            const float e = fast_exp2(dt * A2[q]);
+                            const float hprev = j > 0 ? hs[j > 0 ? j - 1 : 0][q] : he[q];
+                            const float eh = e * hprev;
+                            const float ldt = lam[q] * dt;
+                            dA[q] = fmaf(ldt, eh, dA[q]);
+                            ddp = fmaf(lam[q], fmaf(A[q], eh, Bv[q] * x), ddp);
+                            dxp = fmaf(ldt, Bv[q], dxp);
+                            pp = fmaf(Cv[q], hs[j][q], pp);
+                            vals[j * kHalfNps + q] = ldt * x;
+                            vals[kBT * kHalfNps + j * kHalfNps + q] = gg * hs[j][q];
+                            en[q] = e;
+                        }
+                        lds.red[0][v][j][ch] = dxp;
+                        lds.red[1][v][j][ch] = ddp;
+                        lds.red[2][v][j][ch] = pp;
+                    }
+                }
+            }
+
+            // dB, dC of this tile summed over the half's 32 channels
+            {
+                const float sum = lane_sums32(vals);
+                const int r5 = reverse5(ch);
+                const int which = r5 / (kBT * kHalfNps);
+                const int r = r5 - which * kBT * kHalfNps;
+                const int j = r / kHalfNps;
+                const int n = n0 + (r - j * kHalfNps);
+                if (j < cnt && n < N) {
+                    const int64_t per = f.batch * L * N;
+                    ws.part_bc[(which * ws.nslots + slot) * per + (b * L + t0 + j) * N + n] = sum;
+                }
+            }
+            __syncthreads();
+
+            // finish this lane's token v of the tile: the 8 split partials
+            if (v < cnt) {
+                float dxs = 0.0f, dds = 0.0f, ps = 0.0f;
+#pragma unroll
+                for (int u = 0; u < kHalfSplits; ++u) {
+                    dxs += lds.red[0][u][v][ch];
+                    dds += lds.red[1][u][v][ch];
+                    ps += lds.red[2][u][v][ch];
+                }
+                const float gg = lds.g[v][ch];
+                if constexpr (HAS_D) {
+                    dxs = fmaf(dskip, gg, dxs);
+                    ps = fmaf(dskip, own.x, ps);
+                }
+                const float dv = SP ? dds * sigmoid_f32(own.v) : dds;
+                dD_acc = fmaf(gg, own.x, dD_acc);
+                dbias_acc += dv;
+                if (valid) {
+                    const int64_t idx = (b * L + t0 + v) * f.dim + d;
+                    store_io<IO>(a.dx, idx, dxs);
+                    store_io<IO>(a.ddelta, idx, dv);
+                    if constexpr (HAS_Z) {
+                        const float sg = sigmoid_f32(own.z);
+                        store_io<IO>(a.dz, idx, own.dy * ps * (sg * fmaf(own.z, 1.0f - sg, 1.0f)));
+                    }
+                }
+            }
+        }
+    }
+
+    // gradients at h0 and the per-row partials of dA, dD, d bias
+    if (valid) {
+#pragma unroll
+        for (int q = 0; q < kHalfNps; ++q) {
+            if (sv[q]) {
+                const int64_t col = (b * f.dim + d) * N + n0 + q;
+                if (a.dh0 != nullptr) a.dh0[col] = en[q] * lam[q];
+                ws.part_a[col] = dA[q];
+            }
+        }
+    }
+    __syncthreads();
+    lds.red[0][v][0][ch] = dD_acc;
+    lds.red[1][v][0][ch] = dbias_acc;
+    __syncthreads();
+    if (v == 0 && valid) {
+        float sd = 0.0f, sb = 0.0f;
+#pragma unroll
+        for (int u = 0; u < kHalfSplits; ++u) {
+            sd += lds.red[0][u][0][ch];
+            sb += lds.red[1][u][0][ch];
+        }
+        ws.part_d[b * f.dim + d] = sd;
+        ws.part_bias[b * f.dim + d] = sb;
+    }
+}
+
+// One launch of whole and half groups (dstate 13..16): blocks [0, nwhole)
+// are whole groups in (row, group) order, the blocks after them the two
+// halves of each remaining group, a group's halves 8 blocks apart so one
+// XCD's L2 serves the rows they share (as in the forward scan).
+template <int IO, bool SP, bool HAS_D, bool HAS_Z>
+__global__ __launch_bounds__(kWave * 4) __attribute__((amdgpu_waves_per_eu(3)))
+void scan_bwd_mixed_kernel(BwdArgs a, int64_t ngroups, int64_t nwhole, BwdWs ws) {
+    __shared__ union {
+        BwdLds<4> whole;
+        BwdHalfLds half;
+    } lds;
+    const int64_t blk = blockIdx.x;
+    if (blk < nwhole) {
+        bwd_whole_group<4, IO, SP, HAS_D, HAS_Z>(a, ngroups, blk, ws, lds.whole);
+    } else {
+        const int64_t hb = blk - nwhole;
+        const int64_t nhb = static_cast<int64_t>(gridDim.x) - nwhole;
+        const int64_t run = hb / 16, r = hb % 16;
+        int64_t pair, side;
+        if ((run + 1) * 16 <= nhb) {
+            pair = run * 8 + r % 8;
+            side = r / 8;
+        } else {
+            pair = hb / 2;
+            side = hb % 2;
+        }
+        const int64_t gi = nwhole + pair;  // (row, group) index of the split group
+        bwd_half_group<IO, SP, HAS_D, HAS_Z>(a, ngroups, gi / ngroups, gi % ngroups,
+                                             static_cast<int>(side), ws, lds.half);
+    }
+}
+
+template <int S, int IO, bool SP, bool HAS_D, bool HAS_Z>
+__global__ __launch_bounds__(kWave * S) __attribute__((amdgpu_waves_per_eu(S == 4 ? 3 : 1)))
+void scan_bwd_kernel(BwdArgs a, int64_t ngroups, BwdWs ws) {
+    __shared__ BwdLds<S> lds;
+    bwd_whole_group<S, IO, SP, HAS_D, HAS_Z>(a, ngroups, blockIdx.x, ws, lds);
+}
+
+// dB and dC: the partials of all channel groups added in group order, a
+// split group's second half right after its first. Groups of row b from
+// index nwhole on in (row, group) order are split.
+__global__ __launch_bounds__(256) void bwd_bc_reduce_kernel(int64_t per, int64_t row,
+                                                            int64_t ngroups, int64_t nslots,
+                                                            int64_t nwhole, const float* part,
+                                                            float* dB, float* dC) {
     const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
     for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < 2 * per;
          i += stride) {
         const int64_t which = i / per;
         const int64_t r = i - which * per;
+        const int64_t first_split = nwhole - (r / row) * ngroups;  // groups of this row
         float s = 0.0f;
-        for (int64_t g = 0; g < ngroups; ++g) s += part[(which * ngroups + g) * per + r];
+        for (int64_t g = 0; g < ngroups; ++g) {
+            s += part[(which * nslots + g) * per + r];
+            if (g >= first_split) s += part[(which * nslots + ngroups + g) * per + r];
+        }
         (which ? dC : dB)[r] = s;
     }
 }
@@ -517,9 +915,13 @@ __global__ __launch_bounds__(256) void bwd_degenerate_kernel(int64_t cols, int64
 }
 
 struct BwdLayout {
-    int64_t ntiles, ngroups;
+    int64_t ntiles, ngroups, nslots;
     size_t tent, part_bc, part_a, part_d, part_bias, total;  // float offsets / count
 };
+
+// Half groups need 4 waves of states (dstate 13..16).
+inline bool bwd_halvable(int dstate) { return bwd_halves_supported(dstate); }
+static_assert(kNpw * 4 == 16, "dstate 13..16 fills 4 waves");
 
 inline size_t round64(size_t v) { return (v + 63) / 64 * 64; }
 
@@ -527,12 +929,15 @@ BwdLayout bwd_layout(int64_t batch, int64_t seqlen, int64_t dim, int dstate) {
     BwdLayout l;
     l.ntiles = (seqlen + kBT - 1) / kBT;
     l.ngroups = (dim + kWave - 1) / kWave;
+    // slots for the second halves of split groups whenever the shape allows
+    // splitting, so the size needs no knowledge of the device
+    l.nslots = bwd_halvable(dstate) ? 2 * l.ngroups : l.ngroups;
     const size_t states = static_cast<size_t>(batch) * dim * dstate;
     size_t off = 0;
     l.tent = off;
     off += round64(static_cast<size_t>(l.ntiles) * states);
     l.part_bc = off;
-    off += round64(2 * static_cast<size_t>(l.ngroups) * batch * seqlen * dstate);
+    off += round64(2 * static_cast<size_t>(l.nslots) * batch * seqlen * dstate);
     l.part_a = off;
     off += round64(states);
     l.part_d = off;
@@ -545,12 +950,26 @@ BwdLayout bwd_layout(int64_t batch, int64_t seqlen, int64_t dim, int dstate) {
 
 template <int S, int IO, bool SP>
 hipError_t launch_bwd_main(const BwdArgs& a, const BwdLayout& l, float* ws, hipStream_t s) {
-    const int64_t blocks = a.fwd.batch * l.ngroups;
+    const int64_t groups = a.fwd.batch * l.ngroups;
     const bool has_d = a.fwd.D != nullptr, has_z = a.fwd.z != nullptr;
+    const BwdWs w{ws + l.tent, ws + l.part_bc, ws + l.part_a, ws + l.part_d, ws + l.part_bias,
+                  l.nslots};
+    if constexpr (S == 4) {
+        if (a.halves > 0) {
+            const int64_t nwhole = groups - a.halves;
+            const dim3 grid(nwhole + 2 * a.halves), block(kWave * S);
+            auto go = [&](auto kernel) {
+                hipLaunchKernelGGL(kernel, grid, block, 0, s, a, l.ngroups, nwhole, w);
+            };
+            if (has_d && has_z) go(scan_bwd_mixed_kernel<IO, SP, true, true>);
+            else if (has_d) go(scan_bwd_mixed_kernel<IO, SP, true, false>);
+            else if (has_z) go(scan_bwd_mixed_kernel<IO, SP, false, true>);
+            else go(scan_bwd_mixed_kernel<IO, SP, false, false>);
+            return hipGetLastError();
+        }
+    }
     auto go = [&](auto kernel) {
-        hipLaunchKernelGGL(kernel, dim3(blocks), dim3(kWave * S), 0, s, a, l.ngroups,
-                           ws + l.tent, ws + l.part_bc, ws + l.part_a, ws + l.part_d,
-                           ws + l.part_bias);
+        hipLaunchKernelGGL(kernel, dim3(groups), dim3(kWave * S), 0, s, a, l.ngroups, w);
     };
     if (has_d && has_z) go(scan_bwd_kernel<S, IO, SP, true, true>);
     else if (has_d) go(scan_bwd_kernel<S, IO, SP, true, false>);
@@ -573,8 +992,10 @@ hipError_t launch_bwd_io(const BwdArgs& a, float* ws, hipStream_t s) {
     }
     if (e != hipSuccess) return e;
     const int64_t per = f.batch * f.seqlen * f.dstate;
+    const int64_t nwhole = f.batch * l.ngroups - (bwd_halvable(f.dstate) ? a.halves : 0);
     hipLaunchKernelGGL(bwd_bc_reduce_kernel, dim3(stride_blocks(2 * per)), dim3(256), 0, s, per,
-                       l.ngroups, ws + l.part_bc, a.dB, a.dC);
+                       f.seqlen * f.dstate, l.ngroups, l.nslots, nwhole, ws + l.part_bc, a.dB,
+                       a.dC);
     hipLaunchKernelGGL(bwd_param_reduce_kernel, dim3(stride_blocks(f.dim * f.dstate)), dim3(256),
                        0, s, f.batch, f.dim, f.dstate, ws + l.part_a, ws + l.part_d,
                        ws + l.part_bias, a.dA, a.dD, a.ddelta_bias);

@@ -248,12 +248,14 @@ def test_scan_bwd_rejects_bad_arguments(lib):
     assert lib.ssm_scan_bwd_workspace_size(2, 64, 64, 16, 1, None) == INVALID
     lib.ssm_scan_bwd_workspace_size(2, 64, 64, 16, 1, ctypes.byref(need))
 
-    def bwd(batch=2, seqlen=64, dim=64, dstate=16, dtype=1, opts=None, ws=P, wsb=None, **kw):
+    def bwd(batch=2, seqlen=64, dim=64, dstate=16, dtype=1, opts=None, plan=None, ws=P, wsb=None,
+            **kw):
         p = dict(x=P, delta=P, A=P, B=P, C=P, D=None, z=None, h0=None, dy=P, dhL=None, dx=P,
                  ddelta=P, dA=P, dB=P, dC=P, dD=None, dz=None, dh0=None, ddelta_bias=None)
         p.update(kw)
         return lib.ssm_scan_bwd(batch, seqlen, dim, dstate, dtype, p["x"], p["delta"], p["A"],
-                                p["B"], p["C"], p["D"], p["z"], p["h0"], opts, p["dy"], p["dhL"],
+                                p["B"], p["C"], p["D"], p["z"], p["h0"], opts, plan, p["dy"],
+                                p["dhL"],
                                 p["dx"], p["ddelta"], p["dA"], p["dB"], p["dC"], p["dD"],
                                 p["dz"], p["dh0"], p["ddelta_bias"], ws,
                                 need.value if wsb is None else wsb, None)
@@ -269,6 +271,16 @@ def test_scan_bwd_rejects_bad_arguments(lib):
     assert bwd(dz=P) == INVALID
     assert bwd(ddelta_bias=P) == INVALID
     assert bwd(opts=_opts(reserved=3)) == INVALID
+    # only the plan's halves field applies: 2 rows x 1 group here
+    assert bwd(plan=_plan(chunk_len=8)) == INVALID
+    assert bwd(plan=_plan(split=4)) == INVALID
+    assert bwd(plan=_plan(carry=1)) == INVALID
+    assert bwd(plan=_plan(halves=-1, reserved=1)) == INVALID
+    assert bwd(plan=_plan(halves=-2)) == INVALID
+    assert bwd(plan=_plan(halves=3)) == INVALID
+    assert bwd(plan=_plan(halves=1), dstate=8) == UNSUPPORTED
+    assert bwd(plan=_plan(halves=1), ws=None) == WORKSPACE
+    assert bwd(plan=_plan(halves=5), dim=0) == OK   # nothing runs
     assert bwd(ws=None) == WORKSPACE
     assert bwd(wsb=need.value - 4) == WORKSPACE
     assert bwd(dim=0) == OK

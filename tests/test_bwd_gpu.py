@@ -57,11 +57,11 @@ def _inputs(batch, seqlen, dim, dstate, io, seed, h0=True, D=True, z=True, softp
     return inp, dy, dhL
 
 
-def _compare(orc, inp, dy, dhL, io, what, keys=KEYS):
+def _compare(orc, inp, dy, dhL, io, what, keys=KEYS, halves=ms.HALVES_AUTO):
     sp = inp.get("delta_bias") is not None
     got = ms.scan_bwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp.get("D"),
                       inp.get("z"), inp.get("h0"), dy=dy, dhL=dhL,
-                      delta_bias=inp.get("delta_bias"), delta_softplus=sp)
+                      delta_bias=inp.get("delta_bias"), delta_softplus=sp, halves=halves)
     torch.cuda.synchronize()
     want = orc.scan_bwd(**inp, dy=dy, dhL=dhL, delta_softplus=sp)
     for k in keys:
@@ -87,6 +87,52 @@ def test_bwd_shapes(orc, case):
     inp, dy, dhL = _inputs(*case, seed=sum(case[:4]))
     _say(f"case bwd {case}")
     _compare(orc, inp, dy, dhL, io, f"bwd {case}")
+
+
+HALF_CASES = [
+    # (batch, seqlen, dim, dstate, io): dim 70 leaves the second half of its
+    # last group wholly past the last channel, dim 100 a half with 4 real
+    # channels; N = 13 pads the last split's states
+    (2, 31, 65, 16, "f32"), (3, 45, 100, 16, "f32"), (2, 50, 70, 13, "f32"),
+    (2, 129, 128, 16, "bf16"), (1, 257, 96, 14, "f32"),
+]
+
+
+@pytest.mark.parametrize("case", HALF_CASES, ids=lambda c: "x".join(map(str, c)))
+def test_bwd_half_groups(orc, case):
+    # every split group count: none, one, half of them, all
+    batch, seqlen, dim, dstate, io = case
+    inp, dy, dhL = _inputs(*case, seed=sum(case[:4]) + 1)
+    G = batch * ((dim + 63) // 64)
+    for halves in sorted({ms.HALVES_NONE, 1, max(1, G // 2), G}):
+        _say(f"case bwd halves={halves} of {G} groups {case}")
+        _compare(orc, inp, dy, dhL, io, f"bwd halves={halves} {case}", halves=halves)
+
+
+def test_bwd_half_groups_options_and_softplus(orc):
+    for h0, D, z, use_dhL in ((False, True, True, True), (True, False, False, False)):
+        inp, dy, dhL = _inputs(2, 70, 80, 16, "f32", seed=5, h0=h0, D=D, z=z)
+        _say(f"case bwd halves=all h0={h0} D={D} z={z} dhL={use_dhL}")
+        _compare(orc, inp, dy, dhL if use_dhL else None, "f32",
+                 f"bwd halves h0={h0} D={D} z={z} dhL={use_dhL}", halves=4)
+    for io in ("f32", "bf16"):
+        inp, dy, dhL = _inputs(2, 90, 100, 16, io, seed=6, softplus=True)
+        _say(f"case bwd halves softplus {io}")
+        _compare(orc, inp, dy, dhL, io, f"bwd halves softplus {io}", halves=3)
+
+
+def test_bwd_half_groups_bitwise_run_to_run():
+    inp, dy, dhL = _inputs(2, 60, 150, 16, "bf16", seed=8)
+
+    def run():
+        g = ms.scan_bwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"],
+                        inp["h0"], dy=dy, dhL=dhL, halves=4)
+        torch.cuda.synchronize()
+        return g
+    a, b = run(), run()
+    for k in KEYS:
+        if a[k] is not None:
+            assert torch.equal(a[k], b[k]), k
 
 
 def test_bwd_optional_inputs(orc):
