@@ -862,10 +862,26 @@ __global__ __launch_bounds__(256) void bwd_bc_reduce_kernel(int64_t per, int64_t
         const int64_t which = i / per;
         const int64_t r = i - which * per;
         const int64_t first_split = nwhole - (r / row) * ngroups;  // groups of this row
+        const bool halves = first_split < ngroups;
+        // 8 groups' partials are loaded before they are added (in group order),
+        // so a thread waits for memory once per 8 groups
         float s = 0.0f;
-        for (int64_t g = 0; g < ngroups; ++g) {
-            s += part[(which * nslots + g) * per + r];
-            if (g >= first_split) s += part[(which * nslots + ngroups + g) * per + r];
+        for (int64_t g0 = 0; g0 < ngroups; g0 += 8) {
+            float p[8], e[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int64_t g = min(g0 + u, ngroups - 1);  // clamped, the copy is unused
+                p[u] = part[(which * nslots + g) * per + r];
+                e[u] = halves ? part[(which * nslots + ngroups + g) * per + r] : 0.0f;
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int64_t g = g0 + u;
+                if (g < ngroups) {
+                    s += p[u];
+                    if (g >= first_split) s += e[u];  // only split groups' second halves
+                }
+            }
         }
         (which ? dC : dB)[r] = s;
     }
