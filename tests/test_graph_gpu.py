@@ -115,7 +115,8 @@ def test_graph_decode_layers_replay_bitwise():
 def test_graph_chunked_scan_and_ssd_replay_bitwise():
     """A scan forced into several chunks, once with the summary-pass carry and
     once with the repaired carry (whose head reruns stop on the data), each
-    with a workspace allocated while capturing, and a dual-form call."""
+    with a workspace allocated while capturing, a single-chunk scan with
+    whole and half channel groups, and a dual-form call."""
     w = W.WORKLOADS["mamba130m_layer"]
     inp = {k: (v.to(DEV) if v is not None else None)
            for k, v in W.generate_scan(w, batch=2, seqlen=300, dim=192, seed=11).items()}
@@ -132,6 +133,8 @@ def test_graph_chunked_scan_and_ssd_replay_bitwise():
     hL = torch.empty(2, 192, w.dstate, dtype=torch.float32, device=DEV)
     ry = torch.empty_like(inp["x"])
     rhL = torch.empty_like(hL)
+    my = torch.empty_like(inp["x"])
+    mhL = torch.empty_like(hL)
     sy = torch.empty_like(sinp["x"])
     shL = torch.empty(2, 2, 64, 128, dtype=torch.float32, device=DEV)
 
@@ -141,6 +144,9 @@ def test_graph_chunked_scan_and_ssd_replay_bitwise():
         ms.scan_fwd(fast["x"], fast["delta"], fast["A"], fast["B"], fast["C"], fast["D"],
                     fast["z"], fast["h0"], chunk_len=104, carry=ms.CARRY_REPAIR, out=ry,
                     state_out=rhL)
+        # one chunk, whole and half channel groups in one launch
+        ms.scan_fwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"],
+                    inp["h0"], chunk_len=300, state_split=4, halves=3, out=my, state_out=mhL)
         ms.ssd_fwd(sinp["x"], sinp["dt"], sinp["A"], sinp["B"], sinp["C"], sinp["D"], sinp["z"],
                    sinp["h0"], out=sy, state_out=shL)
 
@@ -150,6 +156,8 @@ def test_graph_chunked_scan_and_ssd_replay_bitwise():
     ry_ref, rh_ref = ms.scan_fwd(fast["x"], fast["delta"], fast["A"], fast["B"], fast["C"],
                                  fast["D"], fast["z"], fast["h0"], chunk_len=104,
                                  carry=ms.CARRY_REPAIR)
+    my_ref, mh_ref = ms.scan_fwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"],
+                                 inp["z"], inp["h0"], chunk_len=300, state_split=4, halves=3)
     sy_ref, sh_ref = ms.ssd_fwd(sinp["x"], sinp["dt"], sinp["A"], sinp["B"], sinp["C"],
                                 sinp["D"], sinp["z"], sinp["h0"])
     torch.cuda.synchronize()
@@ -157,11 +165,13 @@ def test_graph_chunked_scan_and_ssd_replay_bitwise():
         _say(f"case graph chunked scan + ssd: replay {r}")
         y.zero_()
         ry.zero_()
+        my.zero_()
         sy.zero_()
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(y, y_ref) and torch.equal(hL, h_ref), f"chunked scan, replay {r}"
         assert torch.equal(ry, ry_ref) and torch.equal(rhL, rh_ref), f"repaired carry, replay {r}"
+        assert torch.equal(my, my_ref) and torch.equal(mhL, mh_ref), f"half groups, replay {r}"
         assert torch.equal(sy, sy_ref) and torch.equal(shL, sh_ref), f"ssd, replay {r}"
         _eager_noise(r)
