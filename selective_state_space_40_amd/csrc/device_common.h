@@ -68,6 +68,30 @@ __device__ __forceinline__ float softplus_f32(float v) {
     return fmaxf(v, 0.0f) + l;
 }
 
+// Half channel groups (the forward scan's and the backward pass's): the
+// last channel groups of a launch can run as two halves of 32 channels, each
+// channel's states spread over 8 lanes (two 32-lane rows per wave).
+constexpr int kHalfChannels = 32;
+constexpr int kHalfSplits = 8;
+
+// Which split group and which half block `hb` of `nhb` half blocks runs.
+// The two halves of a group read the two 64-byte halves of the same
+// 128-byte rows, so they are placed 8 blocks apart, on one XCD (block i
+// goes to XCD i mod 8) whose L2 then fetches those rows once: within every
+// 16 half blocks, block r < 8 is half 0 and block 8 + r half 1 of the same
+// group; a last partial run of blocks pairs neighbours.
+__device__ __forceinline__ void half_block_pair(int64_t hb, int64_t nhb, int64_t& pair,
+                                                int& side) {
+    const int64_t run = hb / 16, r = hb % 16;
+    if ((run + 1) * 16 <= nhb) {
+        pair = run * 8 + r % 8;
+        side = static_cast<int>(r / 8);
+    } else {
+        pair = hb / 2;
+        side = static_cast<int>(hb % 2);
+    }
+}
+
 // Workgroups are handed to the chip's 8 XCDs in turn (workgroup i to XCD
 // i mod 8), and every XCD has its own L2. This maps the hardware workgroup
 // id to a logical one such that each XCD runs one contiguous range of

@@ -504,9 +504,8 @@ __device__ __forceinline__ void bwd_whole_group(const BwdArgs& a, int64_t ngroup
 // states go through LDS as 8 partials, and dB, dC are summed over the 32
 // channels of each half-wave row by lane_sums32; a group's second half
 // writes them to its own slot, which the reduction adds for split groups.
-constexpr int kHalfCh = 32;     // channels of a half group
-constexpr int kHalfSplits = 8;  // state splits of a half group
-constexpr int kHalfNps = 2;     // states per lane of a half group
+constexpr int kHalfCh = kHalfChannels;
+constexpr int kHalfNps = 16 / kHalfSplits;  // states per lane of a half group
 constexpr int kHalfVals = 2 * kBT * kHalfNps;
 static_assert(kHalfVals == kWave / 2, "the half butterfly leaves one sum per lane");
 
@@ -812,8 +811,7 @@ __device__ __forceinline__ void bwd_half_group(const BwdArgs& a, int64_t ngroups
 
 // One launch of whole and half groups (dstate 13..16): blocks [0, nwhole)
 // are whole groups in (row, group) order, the blocks after them the two
-// halves of each remaining group, a group's halves 8 blocks apart so one
-// XCD's L2 serves the rows they share (as in the forward scan).
+// halves of each remaining group, placed by half_block_pair.
 template <int IO, bool SP, bool HAS_D, bool HAS_Z>
 __global__ __launch_bounds__(kWave * 4) __attribute__((amdgpu_waves_per_eu(3)))
 void scan_bwd_mixed_kernel(BwdArgs a, int64_t ngroups, int64_t nwhole, BwdWs ws) {
@@ -825,20 +823,12 @@ void scan_bwd_mixed_kernel(BwdArgs a, int64_t ngroups, int64_t nwhole, BwdWs ws)
     if (blk < nwhole) {
         bwd_whole_group<4, IO, SP, HAS_D, HAS_Z>(a, ngroups, blk, ws, lds.whole);
     } else {
-        const int64_t hb = blk - nwhole;
-        const int64_t nhb = static_cast<int64_t>(gridDim.x) - nwhole;
-        const int64_t run = hb / 16, r = hb % 16;
-        int64_t pair, side;
-        if ((run + 1) * 16 <= nhb) {
-            pair = run * 8 + r % 8;
-            side = r / 8;
-        } else {
-            pair = hb / 2;
-            side = hb % 2;
-        }
+        int64_t pair;
+        int side;
+        half_block_pair(blk - nwhole, static_cast<int64_t>(gridDim.x) - nwhole, pair, side);
         const int64_t gi = nwhole + pair;  // (row, group) index of the split group
-        bwd_half_group<IO, SP, HAS_D, HAS_Z>(a, ngroups, gi / ngroups, gi % ngroups,
-                                             static_cast<int>(side), ws, lds.half);
+        bwd_half_group<IO, SP, HAS_D, HAS_Z>(a, ngroups, gi / ngroups, gi % ngroups, side, ws,
+                                             lds.half);
     }
 }
 

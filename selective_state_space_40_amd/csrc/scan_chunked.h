@@ -742,8 +742,8 @@ void chunk_output_kernel(ScanArgs a, ChunkGrid g, Carry c) {
 // staged in LDS, one barrier per tile, double-buffered LDS); only the token
 // a lane loads or stores differs per lane, so its row offset goes into the
 // per-lane buffer offset.
-constexpr int kHalf = 32;  // channels of a half group
-constexpr int kSplitsHalf = 8;
+constexpr int kHalf = kHalfChannels;
+constexpr int kSplitsHalf = kHalfSplits;
 
 template <int N>
 struct HalfLds {
@@ -925,15 +925,10 @@ __device__ __forceinline__ void half_group(const ScanArgs& a, int64_t b, int64_t
 
 // One launch of whole and half groups (single chunk, split 4): blocks
 // [0, nwhole) are whole groups 0 .. nwhole-1 in (row, group) order, the
-// blocks after them the two halves of each remaining group. The two halves
-// of a group read the two 64-byte halves of the same 128-byte rows of x,
-// delta and z, so they are placed 8 blocks apart: blocks go to the chip's 8
-// XCDs in turn (block i to XCD i mod 8) and each XCD has its own L2, which
-// then fetches those rows once for both (consecutive halves on two XCDs
-// read the split groups' rows twice from HBM: +100 MB per Mamba-2.8B
-// layer). Within every 16 half blocks, block r < 8 is half 0 and block
-// 8 + r half 1 of the same group; a last partial run of blocks pairs
-// neighbours.
+// blocks after them the two halves of each remaining group, placed by
+// half_block_pair so that one XCD's L2 fetches the rows of x, delta and z a
+// group's halves share (as neighbours on two XCDs they read those rows
+// twice from HBM: +100 MB per Mamba-2.8B layer).
 template <int N, int IO, bool SP, bool HAS_D, bool HAS_Z>
 __global__ __launch_bounds__(kWave * 4) __attribute__((amdgpu_waves_per_eu(4)))
 void chunk_mixed_kernel(ScanArgs a, ChunkGrid g, int64_t nwhole) {
@@ -946,17 +941,9 @@ void chunk_mixed_kernel(ScanArgs a, ChunkGrid g, int64_t nwhole) {
         output_group<N, 4, IO, SP, HAS_D, HAS_Z>(a, g, Carry{nullptr, nullptr, nullptr}, blk,
                                                  lds.whole);
     } else {
-        const int64_t hb = blk - nwhole;
-        const int64_t nhb = static_cast<int64_t>(gridDim.x) - nwhole;
-        const int64_t run = hb / 16, r = hb % 16;
-        int64_t pair, side;
-        if ((run + 1) * 16 <= nhb) {
-            pair = run * 8 + r % 8;
-            side = r / 8;
-        } else {
-            pair = hb / 2;
-            side = hb % 2;
-        }
+        int64_t pair;
+        int side;
+        half_block_pair(blk - nwhole, static_cast<int64_t>(gridDim.x) - nwhole, pair, side);
         const int64_t grp = nwhole + pair;
         const int64_t d0 = (grp % g.nblk_d) * kWave + side * kHalf;
         // a second half wholly past the last channel has nothing to do (the
