@@ -19,8 +19,11 @@
 // tokens and writes the state entering every tile to the workspace: the
 // checkpoints, 4 B per state and tile. (2) It takes the tiles from last to
 // first, carrying lam in registers: it reads the tile's checkpoint,
-// recomputes the tile's 8 states per lane into registers and walks the tile
-// backwards. Sums over
+// recomputes the tile's 8 states per lane into registers (whole groups also
+// keep the tile's decay factors in LDS, so the walk back does not evaluate
+// them again) and walks the tile backwards. Tokens past the end of the
+// sequence are staged as inert ones (delta = x = g = 0, zero B and C), so the
+// forward loops need no per-token test. Sums over
 // states (dx, d dt, p) go through LDS to the wave that finishes the token;
 // sums over channels (dB, dC) are reduced inside the wave by a butterfly of
 // lane exchanges that leaves one finished (token, state) sum in each lane,
@@ -43,12 +46,22 @@ constexpr int kNpw = 4;                        // states per wave
 constexpr int kVals = 2 * kBT * kNpw;          // dB and dC terms per lane per tile
 static_assert(kVals == kWave, "the butterfly leaves exactly one sum per lane");
 
+// One slot per (wave, token) of a tile: first the decay factors
+// exp(dt A) of the wave's states that the tile's recomputation evaluates
+// (kNpw per lane, lane-major), then, once the wave walking backwards has
+// read a token's factors, its three partial sums over states for that token
+// (dx, d dt, C.h; kWave each). A slot is only ever written by its own wave,
+// and the sums it writes depend on the factors it read there, so the read
+// comes first.
+constexpr int kSlot = kNpw * kWave;
+static_assert(3 * kWave <= kSlot, "the partial sums fit in the slot of the factors");
+
 template <int S>
 struct BwdLds {
     float2 dtx[kBT][kWave];                    // (delta as used, x) per token and channel
     float g[kBT][kWave];                       // dy * silu(z)
     alignas(16) float bc[2][kBT][kNpw * S];    // B and C rows of the tile, padded states 0
-    float red[3][S][kBT][kWave];               // per-wave partial sums over states
+    alignas(16) float slot[S][kBT][kSlot];
 };
 
 // What the wave that finishes token j keeps from staging.
@@ -139,6 +152,11 @@ __device__ __forceinline__ void put_tile(const TileRaw<S>& r, const Place& pl, B
                 lds.g[j][lane] = gg;
                 own[jj] = Own{dyf, zf, v, xf};
             }
+        } else if (j < kBT) {
+            // a token past the end of the sequence: inert (delta = x = g = 0
+            // and zero B, C rows leave the state and every sum unchanged)
+            lds.dtx[j][lane] = make_float2(0.0f, 0.0f);
+            if constexpr (WANT_G) lds.g[j][lane] = 0.0f;
         }
     }
     constexpr int NP = kNpw * S;
@@ -310,12 +328,10 @@ __device__ __forceinline__ void bwd_whole_group(const BwdArgs& a, int64_t ngroup
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int jj = 0; jj < 2; ++jj) {
-                    if (j0 + jj < cnt) {
-                        const float du = v[jj].x * v[jj].y;
+                    const float du = v[jj].x * v[jj].y;
 #pragma unroll
-                        for (int q = 0; q < kNpw; ++q)
-                            h[q] = fmaf(fast_exp2(v[jj].x * A2[q]), h[q], du * bq[jj][q]);
-                    }
+                    for (int q = 0; q < kNpw; ++q)
+                        h[q] = fmaf(fast_exp2(v[jj].x * A2[q]), h[q], du * bq[jj][q]);
                 }
             }
             __syncthreads();
@@ -356,12 +372,14 @@ __device__ __forceinline__ void bwd_whole_group(const BwdArgs& a, int64_t ngroup
 #pragma unroll
                 for (int jj = 0; jj < 2; ++jj) {
                     const int j = j0 + jj;
-                    if (j < cnt) {
-                        const float du = v[jj].x * v[jj].y;
+                    const float du = v[jj].x * v[jj].y;
+                    f32x4 ev;
 #pragma unroll
-                        for (int q = 0; q < kNpw; ++q)
-                            h[q] = fmaf(fast_exp2(v[jj].x * A2[q]), h[q], du * bq[jj][q]);
+                    for (int q = 0; q < kNpw; ++q) {
+                        ev[q] = fast_exp2(v[jj].x * A2[q]);
+                        h[q] = fmaf(ev[q], h[q], du * bq[jj][q]);
                     }
+                    reinterpret_cast<f32x4*>(lds.slot[pl.w][j])[lane] = ev;
 #pragma unroll
                     for (int q = 0; q < kNpw; ++q) hs[j][q] = h[q];
                 }
@@ -376,13 +394,14 @@ __device__ __forceinline__ void bwd_whole_group(const BwdArgs& a, int64_t ngroup
               // token's arithmetic (as in the forward kernel)
               float2 vv[2];
               float gq[2];
-              f32x4 bq[2], cq[2];
+              f32x4 bq[2], cq[2], eq[2];
 #pragma unroll
               for (int jj = 0; jj < 2; ++jj) {
                   vv[jj] = lds.dtx[j1 - jj][lane];
                   gq[jj] = lds.g[j1 - jj][lane];
                   bq[jj] = *reinterpret_cast<const f32x4*>(&lds.bc[0][j1 - jj][pl.n0]);
                   cq[jj] = *reinterpret_cast<const f32x4*>(&lds.bc[1][j1 - jj][pl.n0]);
+                  eq[jj] = reinterpret_cast<const f32x4*>(lds.slot[pl.w][j1 - jj])[lane];
               }
               __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -397,7 +416,7 @@ __device__ __forceinline__ void bwd_whole_group(const BwdArgs& a, int64_t ngroup
                         const float Bq = bq[jj][q];
                         const float Cq = cq[jj][q];
                         lam[q] = fmaf(en[q], lam[q], Cq * gg);
-                        const float e = fast_exp2(dt * A2[q]);
+                        const float e = eq[jj][q];
                         const float hprev = j > 0 ? hs[j > 0 ? j - 1 : 0][q] : he[q];
                         const float eh = e * hprev;
                         const float ldt = lam[q] * dt;
@@ -409,9 +428,9 @@ __device__ __forceinline__ void bwd_whole_group(const BwdArgs& a, int64_t ngroup
                         vals[kBT * kNpw + j * kNpw + q] = gg * hs[j][q];
                         en[q] = e;
                     }
-                    lds.red[0][pl.w][j][lane] = dxp;
-                    lds.red[1][pl.w][j][lane] = ddp;
-                    lds.red[2][pl.w][j][lane] = pp;
+                    lds.slot[pl.w][j][lane] = dxp;
+                    lds.slot[pl.w][j][kWave + lane] = ddp;
+                    lds.slot[pl.w][j][2 * kWave + lane] = pp;
                 }
               }
             }
@@ -439,9 +458,9 @@ __device__ __forceinline__ void bwd_whole_group(const BwdArgs& a, int64_t ngroup
                     float dxs = 0.0f, dds = 0.0f, ps = 0.0f;
 #pragma unroll
                     for (int u = 0; u < S; ++u) {
-                        dxs += lds.red[0][u][j][lane];
-                        dds += lds.red[1][u][j][lane];
-                        ps += lds.red[2][u][j][lane];
+                        dxs += lds.slot[u][j][lane];
+                        dds += lds.slot[u][j][kWave + lane];
+                        ps += lds.slot[u][j][2 * kWave + lane];
                     }
                     const Own o = own[jj];
                     const float gg = lds.g[j][lane];
@@ -478,15 +497,15 @@ __device__ __forceinline__ void bwd_whole_group(const BwdArgs& a, int64_t ngroup
         }
     }
     __syncthreads();
-    lds.red[0][pl.w][0][lane] = dD_acc;
-    lds.red[1][pl.w][0][lane] = dbias_acc;
+    lds.slot[pl.w][0][lane] = dD_acc;
+    lds.slot[pl.w][0][kWave + lane] = dbias_acc;
     __syncthreads();
     if (pl.w == 0 && pl.valid) {
         float sd = 0.0f, sb = 0.0f;
 #pragma unroll
         for (int u = 0; u < S; ++u) {
-            sd += lds.red[0][u][0][lane];
-            sb += lds.red[1][u][0][lane];
+            sd += lds.slot[u][0][lane];
+            sb += lds.slot[u][0][kWave + lane];
         }
         part_d[pl.b * f.dim + pl.d] = sd;
         part_bias[pl.b * f.dim + pl.d] = sb;
@@ -596,6 +615,10 @@ __device__ __forceinline__ void bwd_half_group(const BwdArgs& a, int64_t ngroups
                 lds.g[v][ch] = gg;
                 own = Own{dyf, zf, vv, xf};
             }
+        } else {
+            // past the end of the sequence: inert, as in whole groups
+            lds.dtx[v][ch] = make_float2(0.0f, 0.0f);
+            if constexpr (WANT_G) lds.g[v][ch] = 0.0f;
         }
         const int e = threadIdx.x;
         const int which = e / (kBT * NP);
@@ -642,11 +665,9 @@ __device__ __forceinline__ void bwd_half_group(const BwdArgs& a, int64_t ngroups
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int jj = 0; jj < 2; ++jj) {
-                    if (j0 + jj < cnt) {
-                        const float du = vq[jj].x * vq[jj].y;
-                        h[0] = fmaf(fast_exp2(vq[jj].x * A2[0]), h[0], du * bq[jj].x);
-                        h[1] = fmaf(fast_exp2(vq[jj].x * A2[1]), h[1], du * bq[jj].y);
-                    }
+                    const float du = vq[jj].x * vq[jj].y;
+                    h[0] = fmaf(fast_exp2(vq[jj].x * A2[0]), h[0], du * bq[jj].x);
+                    h[1] = fmaf(fast_exp2(vq[jj].x * A2[1]), h[1], du * bq[jj].y);
                 }
             }
             __syncthreads();
@@ -681,11 +702,9 @@ __device__ __forceinline__ void bwd_half_group(const BwdArgs& a, int64_t ngroups
 #pragma unroll
                 for (int jj = 0; jj < 2; ++jj) {
                     const int j = j0 + jj;
-                    if (j < cnt) {
-                        const float du = vq[jj].x * vq[jj].y;
-                        h[0] = fmaf(fast_exp2(vq[jj].x * A2[0]), h[0], du * bq[jj].x);
-                        h[1] = fmaf(fast_exp2(vq[jj].x * A2[1]), h[1], du * bq[jj].y);
-                    }
+                    const float du = vq[jj].x * vq[jj].y;
+                    h[0] = fmaf(fast_exp2(vq[jj].x * A2[0]), h[0], du * bq[jj].x);
+                    h[1] = fmaf(fast_exp2(vq[jj].x * A2[1]), h[1], du * bq[jj].y);
                     hs[j][0] = h[0];
                     hs[j][1] = h[1];
                 }
