@@ -198,3 +198,33 @@ def test_bwd_empty_and_deterministic(orc):
     for k in a:
         if a[k] is not None:
             assert torch.equal(a[k], b[k]), f"{k} not reproducible"
+
+
+@pytest.mark.parametrize("halves", [ms.HALVES_AUTO, ms.HALVES_NONE], ids=["halves", "whole"])
+def test_bwd_nan_propagates_like_the_oracle(orc, halves):
+    # a NaN in one x: every gradient is NaN exactly where the oracle's is
+    # (d delta, dz and dC from that token on, dB at that token, dA and dD of
+    # that channel), finite entries within tolerance; dx and dh0 stay finite
+    inp, dy, dhL = _inputs(2, 37, 70, 16, "f32", seed=41)
+    t, d = 20, 5
+    inp["x"][1, t, d] = float("nan")
+    _say(f"case backward with a NaN input, halves={halves}")
+    got = ms.scan_bwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"],
+                      inp["h0"], dy=dy, dhL=dhL, halves=halves)
+    torch.cuda.synchronize()
+    want = orc.scan_bwd(**inp, dy=dy, dhL=dhL)
+    for k in KEYS:
+        if want[k] is None:
+            continue
+        g = got[k].double().cpu().numpy()
+        w = np.asarray(want[k], dtype=np.float64)
+        assert np.array_equal(np.isnan(g), np.isnan(w)), f"{k}: NaN positions differ"
+        fin = np.isfinite(w)
+        assert np.all(np.isfinite(g[fin])), f"{k}: non-finite where the oracle is finite"
+        scale = float(np.max(np.abs(w[fin]))) if fin.any() else 0.0
+        err = float(np.max(np.abs(g[fin] - w[fin]))) if fin.any() else 0.0
+        assert err <= TOL_BWD["f32"] * scale, f"{k}: max abs error {err:.3e} vs {scale:.3e}"
+    wnan = {k: np.isnan(np.asarray(want[k], dtype=np.float64)) for k in KEYS if want[k] is not None}
+    assert wnan["ddelta"][1, t:, d].all() and not wnan["ddelta"][1, :t, d].any()
+    assert wnan["dz"][1, t:, d].all() and wnan["dC"][1, t:].all() and wnan["dB"][1, t].all()
+    assert wnan["dA"][d].all() and wnan["dD"][d] and not wnan["dx"].any() and not wnan["dh0"].any()
