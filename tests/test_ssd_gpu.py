@@ -135,3 +135,34 @@ def test_ssd_resume_alias_empty_deterministic(orc):
     a1 = _run(inp)
     a2 = _run(inp)
     assert torch.equal(a1[0], a2[0]) and torch.equal(a1[1], a2[1])
+
+
+def test_ssd_nan_stays_in_its_channel(orc):
+    # the chunk products multiply the causal mask's zeros by every input of
+    # a 16-token block, so a NaN input may also reach the earlier tokens of
+    # its own block; it never leaves its channel or reaches an earlier block,
+    # and everything finite agrees with the oracle
+    inp = W.generate_ssd(W0, device=DEV, batch=1, seqlen=100, nheads=2, dstate=128, seed=5,
+                         h0="normal")
+    t, p = 37, 5
+    inp["x"][0, t, p] = float("nan")
+    _say("case ssd with a NaN input")
+    y, hL = _run(inp)
+    yo, ho = _oracle(orc, inp)
+    g = y.double().cpu().numpy()
+    w = np.asarray(yo, dtype=np.float64)
+    assert np.isnan(g[0, t:, p]).all() and np.isnan(w[0, t:, p]).all()
+    block = (t // 16) * 16
+    assert np.isfinite(g[0, :block, p]).all()
+    others = np.ones(g.shape[2], dtype=bool)
+    others[p] = False
+    assert np.isfinite(g[0][:, others]).all() and np.isfinite(w[0][:, others]).all()
+    fin = np.isfinite(g)
+    scale = float(np.max(np.abs(w[fin])))
+    assert float(np.max(np.abs(g[fin] - w[fin]))) <= TOL * scale
+    gh = hL.double().cpu().numpy()
+    wh = np.asarray(ho, dtype=np.float64)
+    assert np.array_equal(np.isnan(gh), np.isnan(wh))
+    assert np.isnan(wh).sum() == wh.shape[-1]   # the channel's states only
+    hf = np.isfinite(wh)
+    assert float(np.max(np.abs(gh[hf] - wh[hf]))) <= TOL * float(np.max(np.abs(wh[hf])))
