@@ -295,7 +295,9 @@ int ssm_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int dstate, int dty
  * Requirements: headdim == MAMBA_SSD_HEADDIM, dstate 64 or 128, dtype
  * MAMBA_DTYPE_BF16 (the products run in bf16 with fp32 accumulation),
  * nheads <= 65536; anything else is MAMBA_ERR_UNSUPPORTED. No workspace. Errors and
- * ownership as for ssm_scan_fwd.
+ * ownership as for ssm_scan_fwd. A NaN or infinite input stays in its channel
+ * but, since the chunk products multiply the causal mask's zeros by it, also
+ * reaches the earlier outputs of its own 16-token block.
  */
 int ssd_fwd(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int dstate,
             int dtype, const void* x, const void* dt, const float* A, const void* B,
