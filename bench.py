@@ -471,7 +471,7 @@ def bench_backward(args, w):
         inp = sets[i % 2]
         ms.scan_bwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"],
                     inp["h0"], dy=inp["dy"], delta_bias=inp.get("delta_bias"),
-                    delta_softplus=sp, halves=args.halves)
+                    delta_softplus=sp, halves=args.halves, chunk_len=args.chunk_len)
 
     ms_per_step, wall = _time_steps(step, args.warmup, args.steps, torch.cuda.current_stream(dev),
                                       args.spin_up)
@@ -483,6 +483,8 @@ def bench_backward(args, w):
     gbps = nbytes / sec / 1e9
     cpu = None if args.no_cpu_baseline else cpu_baseline_backward(w, sets[0], sp, args.cpu_seconds)
     clock = gpu_clock_sample(step)
+    plan = ms.resolve_bwd_plan(w.batch, w.seqlen, w.dim, w.dstate, W.io_torch_dtype(w.io),
+                               args.chunk_len, args.halves)
     line = {
         "metric": "backward scan elements/s (B*L*D, all input gradients, states recomputed)",
         "value": elems / sec, "unit": "elements/s", "n_gpus": 1, "steps": args.steps,
@@ -490,7 +492,9 @@ def bench_backward(args, w):
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "seqlen": w.seqlen, "dim": w.dim,
                    "dstate": w.dstate, "io_dtype": w.io, "checkpoint_every": 8,
-                   "half_groups": bwd_half_groups(w, args.halves),
+                   "chunk_len": int(plan.chunk_len),
+                   "nchunks": int(-(-w.seqlen // plan.chunk_len)),
+                   "half_groups": int(plan.halves),
                    "delta_activation": "bias + softplus in the kernels" if sp else
                                        "none (delta passed activated)",
                    "parallelism": "single GPU"},
@@ -521,19 +525,6 @@ def _oracle_passes(run, seconds):
 
 def _passes_text(passes, dt):
     return f"{passes} pass{'es' if passes > 1 else ''} in {dt:.1f} s"
-
-
-def bwd_half_groups(w, requested):
-    """Channel groups the backward pass runs as halves: the count asked for,
-    or the library's automatic rule (the groups whole rounds of the chip's
-    compute units leave over, when at most half a round; dstate 13..16)."""
-    import torch
-    if requested != 0 or not 13 <= w.dstate <= 16:
-        return max(requested, 0) if 13 <= w.dstate <= 16 else 0
-    cu = torch.cuda.get_device_properties(0).multi_processor_count
-    groups = w.batch * -(-w.dim // 64)
-    surplus = groups % cu
-    return surplus if 0 < surplus and 2 * surplus <= cu else 0
 
 
 def cpu_baseline_backward(w, inp, softplus, seconds):

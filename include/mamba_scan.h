@@ -242,21 +242,36 @@ int ssm_state_update(int64_t batch, int64_t dim, int dstate, int dtype, float* h
  *                                                 h0 is NULL)
  * ddelta_bias  (dim) fp32                         optional; must be NULL when
  *                                                 options carry no delta_bias
- * plan         may be NULL (automatic). Only `halves` applies (see
+ * plan         may be NULL (automatic). `chunk_len` (0: automatic, else a
+ *              multiple of 8) cuts the sequence into chunks that run in
+ *              parallel; the automatic plan cuts it only when the channel
+ *              groups alone hold fewer than two waves per SIMD, into chunks
+ *              of at least 64 tokens for about six. `halves` (see
  *              mamba_scan_plan: channel groups run as two 32-channel halves,
- *              available for dstate 13..16, automatic by the same rule as
- *              the forward scan); chunk_len, state_split, carry and reserved
- *              must be 0.
- * workspace    at least ssm_scan_bwd_workspace_size bytes
+ *              dstate 13..16, automatic by the same rule as the forward
+ *              scan) needs one chunk: forcing both is MAMBA_ERR_UNSUPPORTED.
+ *              state_split, carry and reserved must be 0.
+ * workspace    at least the bytes ssm_scan_bwd_workspace_size reports for the
+ *              same shape and plan
  *
  * The intermediate states are recomputed from checkpoints every 8 tokens
- * that the call itself computes into the workspace. Sums over channels and
- * rows are taken in a fixed order, so results are reproducible bit for bit.
- * seqlen == 0 writes zero dA, dD, ddelta_bias and dh0 = dhL. Outputs must
- * not overlap inputs or each other. Errors as for ssm_scan_fwd.
+ * that the call itself computes into the workspace. A chunked sequence first
+ * summarises every chunk but one twice, the state forward from a zero start
+ * and the adjoint back from a zero start, and folds the summaries in chunk
+ * order into each chunk's entering state and adjoint (the same combine as
+ * the forward chunks'), so each chunk's gradients follow from its own
+ * tokens. Sums over channels and rows are taken in a fixed order, so
+ * results are reproducible bit for bit for a given plan. seqlen == 0 writes
+ * zero dA, dD, ddelta_bias and dh0 = dhL. Outputs must not overlap inputs or
+ * each other. Errors as for ssm_scan_fwd.
+ *
+ * ssm_scan_bwd_workspace_size: scratch bytes for the shape and plan; with
+ * `resolved` non-NULL it also reports the plan decided (chunk_len: the
+ * chunk length, the whole sequence when uncut; halves: the groups split).
  */
 int ssm_scan_bwd_workspace_size(int64_t batch, int64_t seqlen, int64_t dim, int dstate,
-                                int dtype, size_t* bytes);
+                                int dtype, const mamba_scan_plan* plan,
+                                mamba_scan_plan* resolved, size_t* bytes);
 
 int ssm_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int dstate, int dtype,
                  const void* x, const void* delta, const float* A, const void* B,

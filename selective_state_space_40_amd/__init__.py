@@ -99,7 +99,7 @@ def load_library():
     lib.ssm_scan_fwd.restype = i32
     lib.ssm_state_update.argtypes = [i64, i64, i32, i32] + [vp] * 9 + [po, vp]
     lib.ssm_state_update.restype = i32
-    lib.ssm_scan_bwd_workspace_size.argtypes = [i64, i64, i64, i32, i32,
+    lib.ssm_scan_bwd_workspace_size.argtypes = [i64, i64, i64, i32, i32, pp, pp,
                                                 ctypes.POINTER(ctypes.c_size_t)]
     lib.ssm_scan_bwd_workspace_size.restype = i32
     lib.ssm_scan_bwd.argtypes = ([i64, i64, i64, i32, i32] + [vp] * 8 + [po, pp] + [vp] * 11 +
@@ -167,6 +167,21 @@ def resolve_plan(batch, seqlen, dim, dstate, dtype=torch.bfloat16, chunk_len=0, 
                                                       ctypes.byref(nbytes)),
            "ssm_scan_fwd_workspace_size")
     return Plan(out.chunk_len, out.state_split, out.carry, out.halves, nbytes.value)
+
+
+def resolve_bwd_plan(batch, seqlen, dim, dstate, dtype=torch.bfloat16, chunk_len=0,
+                     halves=HALVES_AUTO):
+    """The plan ssm_scan_bwd uses for this shape, and its scratch bytes, as a
+    Plan (chunk_len: the chunk length, the whole sequence when uncut; halves:
+    the channel groups split; state_split and carry 0)."""
+    req = ScanPlan(chunk_len, 0, 0, halves, 0)
+    out = ScanPlan(0, 0, 0, 0, 0)
+    nbytes = ctypes.c_size_t(0)
+    _check(load_library().ssm_scan_bwd_workspace_size(batch, seqlen, dim, dstate, _DTYPES[dtype],
+                                                      ctypes.byref(req), ctypes.byref(out),
+                                                      ctypes.byref(nbytes)),
+           "ssm_scan_bwd_workspace_size")
+    return Plan(out.chunk_len, 0, 0, out.halves, nbytes.value)
 
 
 def workspace_size(batch, seqlen, dim, dstate, dtype=torch.bfloat16, chunk_len=0, state_split=0,
@@ -239,13 +254,15 @@ def scan_fwd(x, delta, A, B, C, D=None, z=None, h0=None, *, delta_bias=None,
 
 
 def scan_bwd(x, delta, A, B, C, D=None, z=None, h0=None, *, dy, dhL=None, delta_bias=None,
-             delta_softplus=False, want_dh0=True, halves=HALVES_AUTO):
+             delta_softplus=False, want_dh0=True, halves=HALVES_AUTO, chunk_len=0):
     """Gradients of sum(dy * y) + sum(dhL * hL) for the scan_fwd call with the
     same inputs. Returns a dict: dx, ddelta, dz (like x, I/O dtype); dB, dC
     (batch, L, N) fp32; dA (dim, N) fp32; dD, ddelta_bias (dim,) fp32; dh0
     (batch, dim, N) fp32. Entries of absent optional inputs are None.
     `halves` is the number of the last channel groups run as two 32-channel
-    halves (HALVES_AUTO: the library's choice, HALVES_NONE: none; N 13..16)."""
+    halves (HALVES_AUTO: the library's choice, HALVES_NONE: none; N 13..16);
+    `chunk_len` > 0 (a multiple of 8) cuts the sequence into chunks that run
+    in parallel (0: the library's choice)."""
     lib = load_library()
     if x.dim() != 3:
         raise ValueError("x must be (batch, L, dim)")
@@ -278,15 +295,16 @@ def scan_bwd(x, delta, A, B, C, D=None, z=None, h0=None, *, dy, dhL=None, delta_
              dh0=torch.empty(batch, dim, dstate, **f32) if want_dh0 else None,
              ddelta_bias=None if delta_bias is None else torch.empty(dim, **f32))
     with torch.cuda.device(dev):
+        plan = ScanPlan(chunk_len, 0, 0, halves, 0)
         nbytes = ctypes.c_size_t(0)
         _check(lib.ssm_scan_bwd_workspace_size(batch, seqlen, dim, dstate, _DTYPES[dt],
-                                               ctypes.byref(nbytes)),
+                                               ctypes.byref(plan), None, ctypes.byref(nbytes)),
                "ssm_scan_bwd_workspace_size")
         ws = _workspace(dev, nbytes.value, "bwd")
         st = lib.ssm_scan_bwd(batch, seqlen, dim, dstate, _DTYPES[dt], _ptr(x), _ptr(delta),
                               _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0),
                               _options(delta_bias, delta_softplus),
-                              ctypes.byref(ScanPlan(0, 0, 0, halves, 0)), _ptr(dy), _ptr(dhL),
+                              ctypes.byref(plan), _ptr(dy), _ptr(dhL),
                               _ptr(g["dx"]), _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]),
                               _ptr(g["dC"]), _ptr(g["dD"]), _ptr(g["dz"]), _ptr(g["dh0"]),
                               _ptr(g["ddelta_bias"]), _ptr(ws), nbytes.value, _stream(dev))

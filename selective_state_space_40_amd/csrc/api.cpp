@@ -295,12 +295,98 @@ int ssm_state_update(int64_t batch, int64_t dim, int dstate, int dtype, float* h
     return mamba::launch_state_update(a, stream) == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP;
 }
 
-int ssm_scan_bwd_workspace_size(int64_t batch, int64_t seqlen, int64_t dim, int dstate,
-                                int dtype, size_t* bytes) {
-    if (bytes == nullptr) return MAMBA_ERR_INVALID_ARG;
-    const int st = check_shape(batch, seqlen, dim, dstate, dtype);
+namespace {
+
+// Work decomposition of the backward pass. One workgroup of ceil(N/4) waves
+// walks one (chunk, batch row, 64-channel group). The sequence stays whole
+// unless the groups' waves fill less than kWavesPerSimdNoChunk waves per
+// SIMD; it is then cut into chunks of at least kMinChunk tokens for about
+// kBwdWavesPerSimd waves per SIMD (two rounds of the three the kernel holds
+// per SIMD), at the price of a state and an adjoint summary over every chunk
+// but one. (Measured on MI355X: the Mamba-130M layer 759 us with 8 chunks,
+// 774 with 4, 1028 with 2, 1185 whole; the million-token scan 61.4 ms with
+// 48 chunks, 65.8 with 24, 88.4 with 12.) Halves
+// (the last groups as two 32-channel halves, as in the forward plan) need
+// a whole sequence: forced halves keep it whole.
+constexpr int64_t kBwdWavesPerSimd = 6;
+
+// The checks of a requested backward plan that need no device.
+int check_bwd_plan(int64_t batch, int64_t seqlen, int64_t dim, int dstate,
+                   const mamba_scan_plan* req) {
+    if (req == nullptr) return MAMBA_OK;
+    if (req->state_split != 0 || req->carry != 0 || req->reserved != 0 || req->halves < -1 ||
+        req->chunk_len < 0 || req->chunk_len % 8 != 0)
+        return MAMBA_ERR_INVALID_ARG;
+    if (batch <= 0 || seqlen <= 0 || dim <= 0) return MAMBA_OK;  // nothing runs: moot
+    const int64_t groups = batch * ((dim + mamba::kWave - 1) / mamba::kWave);
+    if (req->halves > 0 && !mamba::bwd_halves_supported(dstate)) return MAMBA_ERR_UNSUPPORTED;
+    if (req->halves > groups) return MAMBA_ERR_INVALID_ARG;
+    const bool chunked = req->chunk_len > 0 && req->chunk_len < seqlen;
+    if (chunked && req->halves > 0) return MAMBA_ERR_UNSUPPORTED;
+    return MAMBA_OK;
+}
+
+// The backward plan: chunk length (0: one chunk) and halves. Automatic
+// fields query the current device.
+int make_bwd_plan(int64_t batch, int64_t seqlen, int64_t dim, int dstate,
+                  const mamba_scan_plan* req, int64_t* chunk_len, int64_t* halves) {
+    const int st = check_bwd_plan(batch, seqlen, dim, dstate, req);
     if (st != MAMBA_OK) return st;
-    *bytes = mamba::scan_bwd_workspace_bytes(batch, seqlen, dim, dstate);
+    const int64_t len_req = req != nullptr ? req->chunk_len : 0;
+    const int64_t halves_req = req != nullptr ? req->halves : 0;
+    *chunk_len = 0;
+    *halves = 0;
+    if (batch <= 0 || seqlen <= 0 || dim <= 0) return MAMBA_OK;
+    const int64_t groups = batch * ((dim + mamba::kWave - 1) / mamba::kWave);
+    int cu = 0;
+    if (len_req == 0 || halves_req == 0) {
+        const int st = current_cu_count(&cu);
+        if (st != MAMBA_OK) return st;
+    }
+    int64_t len = len_req;
+    if (len == 0 && halves_req <= 0) {  // forced halves keep the sequence whole
+        const int64_t waves = groups * ((dstate + 3) / 4);
+        const int64_t simds = int64_t(cu) * 4;
+        if (waves < kWavesPerSimdNoChunk * simds) {
+            int64_t n = (kBwdWavesPerSimd * simds + waves - 1) / waves;
+            if (n > seqlen / kMinChunk) n = seqlen / kMinChunk;
+            if (n >= 2) len = ((seqlen + n - 1) / n + 7) / 8 * 8;
+        }
+    }
+    if (len >= seqlen) len = 0;  // one chunk
+    const int64_t nchunks = len > 0 ? (seqlen + len - 1) / len : 1;
+    if (nchunks > 1 && halves_req > 0) return MAMBA_ERR_UNSUPPORTED;
+    if (nchunks == 1 && mamba::bwd_halves_supported(dstate)) {
+        if (halves_req > 0) {
+            *halves = halves_req;
+        } else if (halves_req == 0) {
+            // the groups whole rounds leave over, when at most half a round
+            const int64_t surplus = groups % cu;
+            if (surplus > 0 && 2 * surplus <= cu) *halves = surplus;
+        }
+    }
+    if (nchunks * groups + *halves > (int64_t(1) << 31)) return MAMBA_ERR_UNSUPPORTED;
+    *chunk_len = len;
+    return MAMBA_OK;
+}
+
+}  // namespace
+
+int ssm_scan_bwd_workspace_size(int64_t batch, int64_t seqlen, int64_t dim, int dstate,
+                                int dtype, const mamba_scan_plan* plan,
+                                mamba_scan_plan* resolved, size_t* bytes) {
+    if (bytes == nullptr) return MAMBA_ERR_INVALID_ARG;
+    int st = check_shape(batch, seqlen, dim, dstate, dtype);
+    if (st != MAMBA_OK) return st;
+    int64_t chunk_len = 0, halves = 0;
+    st = make_bwd_plan(batch, seqlen, dim, dstate, plan, &chunk_len, &halves);
+    if (st != MAMBA_OK) return st;
+    *bytes = mamba::scan_bwd_workspace_bytes(batch, seqlen, dim, dstate, chunk_len);
+    if (resolved != nullptr) {
+        *resolved = mamba_scan_plan{};
+        resolved->chunk_len = chunk_len > 0 ? chunk_len : seqlen;
+        resolved->halves = halves;
+    }
     return MAMBA_OK;
 }
 
@@ -314,16 +400,8 @@ int ssm_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int dstate, int dty
                  size_t workspace_bytes, hipStream_t stream) {
     int st = check_shape(batch, seqlen, dim, dstate, dtype);
     if (st != MAMBA_OK) return st;
-    // only `halves` applies to the backward pass
-    if (plan != nullptr && (plan->chunk_len != 0 || plan->state_split != 0 || plan->carry != 0 ||
-                            plan->reserved != 0 || plan->halves < -1))
-        return MAMBA_ERR_INVALID_ARG;
-    const int64_t halves_req = plan != nullptr ? plan->halves : 0;
-    const int64_t groups = batch * ((dim + mamba::kWave - 1) / mamba::kWave);
-    const bool runs = batch > 0 && seqlen > 0 && dim > 0;  // else any request is moot
-    if (runs && halves_req > 0 && !mamba::bwd_halves_supported(dstate))
-        return MAMBA_ERR_UNSUPPORTED;
-    if (runs && halves_req > groups) return MAMBA_ERR_INVALID_ARG;
+    st = check_bwd_plan(batch, seqlen, dim, dstate, plan);
+    if (st != MAMBA_OK) return st;
     const float* delta_bias = nullptr;
     int delta_softplus = 0;
     st = read_options(options, &delta_bias, &delta_softplus);
@@ -341,24 +419,14 @@ int ssm_scan_bwd(int64_t batch, int64_t seqlen, int64_t dim, int dstate, int dty
                           dA, dB, dC, dD, dz, dh0, ddelta_bias, workspace};
     for (const void* p : ptrs)
         if (p != nullptr && !aligned16(p)) return MAMBA_ERR_MISALIGNED;
-    const size_t need = mamba::scan_bwd_workspace_bytes(batch, seqlen, dim, dstate);
+    int64_t chunk_len = 0, halves = 0;
+    st = make_bwd_plan(batch, seqlen, dim, dstate, plan, &chunk_len, &halves);
+    if (st != MAMBA_OK) return st;
+    const size_t need = mamba::scan_bwd_workspace_bytes(batch, seqlen, dim, dstate, chunk_len);
     if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return MAMBA_ERR_WORKSPACE;
     mamba::BwdArgs a;
-    a.halves = 0;
-    if (runs && mamba::bwd_halves_supported(dstate)) {
-        if (halves_req > 0) {
-            a.halves = halves_req;
-        } else if (halves_req == 0) {
-            // as the forward plan: the groups whole rounds leave over, when
-            // they are at most half a round
-            int cu = 0;
-            st = current_cu_count(&cu);
-            if (st != MAMBA_OK) return st;
-            const int64_t surplus = groups % cu;
-            if (surplus > 0 && 2 * surplus <= cu) a.halves = surplus;
-        }
-        if (groups + a.halves > (int64_t(1) << 31)) return MAMBA_ERR_UNSUPPORTED;
-    }
+    a.halves = halves;
+    a.chunk_len = chunk_len;
     a.fwd.batch = batch;
     a.fwd.seqlen = seqlen;
     a.fwd.dim = dim;

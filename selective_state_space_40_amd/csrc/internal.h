@@ -122,14 +122,17 @@ struct BwdArgs {
     float* dh0;            // (batch, dim, dstate) or nullptr
     float* ddelta_bias;    // (dim) or nullptr
     int64_t halves = 0;    // last channel groups run as two 32-channel halves (dstate 13..16)
+    int64_t chunk_len = 0; // tokens per chunk (a multiple of 8); 0: one chunk, no halves
 };
 
 // The backward pass can split channel groups into halves when a channel's
 // states fill 4 waves of 4 (dstate 13..16).
 inline bool bwd_halves_supported(int dstate) { return dstate >= 13 && dstate <= 16; }
 
-// Scratch bytes of the backward pass for this shape.
-size_t scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int dstate);
+// Scratch bytes of the backward pass for this shape cut into chunks of
+// chunk_len tokens (0: one chunk).
+size_t scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int dstate,
+                                int64_t chunk_len);
 
 // Queue the backward pass. Arguments are validated.
 hipError_t launch_scan_bwd(const BwdArgs& a, void* workspace, hipStream_t stream);

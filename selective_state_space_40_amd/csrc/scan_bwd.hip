@@ -243,11 +243,36 @@ __device__ __forceinline__ int reverse6(int l) {
 struct BwdWs {
     float* tent;
     float* part_bc;
-    float* part_a;
-    float* part_d;
-    float* part_bias;
+    float* part_a;        // [chunk][b][d][n]
+    float* part_d;        // [chunk][b][d]
+    float* part_bias;     // [chunk][b][d]
     int64_t nslots;
+    // A sequence cut into nchunks chunks of chunk_len tokens (one chunk:
+    // chunk_len covers the whole sequence). hin[c] is the state entering
+    // chunk c >= 1 and rho[nchunks - 1 - c] the adjoint entering chunk
+    // c <= nchunks - 2 from its right, Abar_{t1} lam_{t1} with t1 the first
+    // token after the chunk; both [.][b][d][n].
+    int64_t nchunks;
+    int64_t chunk_len;
+    const float* hin;
+    const float* rho;
 };
+
+// Place of a whole-group thread: batch row and channel group from the
+// workgroup's index within its chunk, its wave's states, its channel.
+__device__ __forceinline__ Place make_place(const ScanArgs& f, int64_t ngroups, int64_t in_chunk) {
+    const int lane = threadIdx.x & (kWave - 1);
+    Place pl;
+    pl.grp = in_chunk % ngroups;
+    pl.b = in_chunk / ngroups;
+    pl.w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
+    pl.n0 = pl.w * kNpw;
+    const int64_t d_raw = pl.grp * kWave + lane;
+    pl.valid = d_raw < f.dim;
+    pl.d = pl.valid ? d_raw : f.dim - 1;
+    pl.dbias = f.delta_bias != nullptr ? f.delta_bias[pl.d] : 0.0f;
+    return pl;
+}
 
 template <int S, int IO, bool SP, bool HAS_D, bool HAS_Z>
 __device__ __forceinline__ void bwd_whole_group(const BwdArgs& a, int64_t ngroups, int64_t blk,
@@ -263,17 +288,20 @@ __device__ __forceinline__ void bwd_whole_group(const BwdArgs& a, int64_t ngroup
     const int64_t L = f.seqlen;
     const int lane = threadIdx.x & (kWave - 1);
 
-    Place pl;
-    pl.grp = blk % ngroups;
-    pl.b = blk / ngroups;
-    pl.w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
-    pl.n0 = pl.w * kNpw;
-    const int64_t d_raw = pl.grp * kWave + lane;
-    pl.valid = d_raw < f.dim;
-    pl.d = pl.valid ? d_raw : f.dim - 1;
-    pl.dbias = f.delta_bias != nullptr ? f.delta_bias[pl.d] : 0.0f;
+    // block -> (chunk, batch row, channel group); the chunk's tiles
+    const int64_t rows = f.batch * ngroups;
+    const int64_t chunk = blk / rows;
+    const int64_t in_chunk = blk - chunk * rows;
+    const bool last_chunk = chunk == ws.nchunks - 1;
+    const int64_t i_first = chunk * (ws.chunk_len / kBT);
+    const int64_t i_end = last_chunk ? (L + kBT - 1) / kBT : i_first + ws.chunk_len / kBT;
+    const Place pl = make_place(f, ngroups, in_chunk);
     const float dskip = HAS_D ? f.D[pl.d] : 0.0f;
 
+    // the adjoint entering the chunk from its right: dhL for the last chunk
+    const int64_t col0 = (pl.b * f.dim + pl.d) * N;
+    const float* lam_in = last_chunk ? a.dhL
+                                     : ws.rho + (ws.nchunks - 1 - chunk) * f.batch * f.dim * N;
     bool sv[kNpw];      // state exists (not padding)
     float A[kNpw], A2[kNpw], lam[kNpw], en[kNpw], dA[kNpw];
 #pragma unroll
@@ -282,24 +310,25 @@ __device__ __forceinline__ void bwd_whole_group(const BwdArgs& a, int64_t ngroup
         sv[q] = n < N;
         A[q] = sv[q] ? f.A[pl.d * N + n] : 0.0f;
         A2[q] = A[q] * kLog2e;
-        lam[q] = (sv[q] && a.dhL != nullptr) ? a.dhL[(pl.b * f.dim + pl.d) * N + n] : 0.0f;
+        lam[q] = (sv[q] && lam_in != nullptr) ? lam_in[col0 + n] : 0.0f;
         en[q] = 1.0f;
         dA[q] = 0.0f;
     }
     float dD_acc = 0.0f, dbias_acc = 0.0f;
     Own own[OW];
 
-    const int64_t ntiles = (L + kBT - 1) / kBT;
-    // (1) forward over the whole sequence, keeping the state entering every
-    // tile in the workspace (only real lanes and states write)
+    // (1) forward over the chunk from its entering state, keeping the state
+    // entering every tile in the workspace (only real lanes and states write)
     {
+        const float* h_in = chunk == 0 ? f.h0 : ws.hin + chunk * f.batch * f.dim * N;
         float h[kNpw];
 #pragma unroll
         for (int q = 0; q < kNpw; ++q)
-            h[q] = (sv[q] && f.h0 != nullptr) ? f.h0[(pl.b * f.dim + pl.d) * N + pl.n0 + q] : 0.0f;
+            h[q] = (sv[q] && h_in != nullptr) ? h_in[col0 + pl.n0 + q] : 0.0f;
         TileRaw<S> raw;
-        fetch_tile<S, IO, HAS_Z, false>(a, pl, tent, 0, static_cast<int>(min<int64_t>(kBT, L)), raw);
-        for (int64_t i = 0; i < ntiles; ++i) {
+        fetch_tile<S, IO, HAS_Z, false>(a, pl, tent, i_first,
+                                        static_cast<int>(min<int64_t>(kBT, L - i_first * kBT)), raw);
+        for (int64_t i = i_first; i < i_end; ++i) {
             const int64_t t0 = i * kBT;
             const int cnt = static_cast<int>(min<int64_t>(kBT, L - t0));
             if (pl.valid) {
@@ -312,7 +341,7 @@ __device__ __forceinline__ void bwd_whole_group(const BwdArgs& a, int64_t ngroup
             __syncthreads();
             {
                 // the last tile fetches itself again (unused)
-                const int64_t nx = min(i + 1, ntiles - 1);
+                const int64_t nx = min(i + 1, i_end - 1);
                 fetch_tile<S, IO, HAS_Z, false>(a, pl, tent, nx,
                                                 static_cast<int>(min<int64_t>(kBT, L - nx * kBT)), raw);
             }
@@ -342,9 +371,10 @@ __device__ __forceinline__ void bwd_whole_group(const BwdArgs& a, int64_t ngroup
     {
         float h[kNpw];
         TileRaw<S> raw;
-        fetch_tile<S, IO, HAS_Z, true>(a, pl, tent, ntiles - 1,
-                                       static_cast<int>(L - (ntiles - 1) * kBT), raw);
-        for (int64_t i = ntiles - 1; i >= 0; --i) {
+        fetch_tile<S, IO, HAS_Z, true>(a, pl, tent, i_end - 1,
+                                       static_cast<int>(min<int64_t>(kBT, L - (i_end - 1) * kBT)),
+                                       raw);
+        for (int64_t i = i_end - 1; i >= i_first; --i) {
             const int64_t t0 = i * kBT;
             const int cnt = static_cast<int>(min<int64_t>(kBT, L - t0));
             // the tile's entering state; a lane past the last channel starts
@@ -354,8 +384,12 @@ __device__ __forceinline__ void bwd_whole_group(const BwdArgs& a, int64_t ngroup
             for (int q = 0; q < kNpw; ++q) he[q] = (pl.valid && sv[q]) ? raw.he[q] : 0.0f;
             put_tile<S, IO, SP, HAS_Z, true>(raw, pl, lds, cnt, N, own);
             __syncthreads();
-            // tile 0 fetches itself again (unused)
-            fetch_tile<S, IO, HAS_Z, true>(a, pl, tent, i > 0 ? i - 1 : 0, kBT < L ? kBT : static_cast<int>(L), raw);
+            // the chunk's first tile fetches itself again (unused)
+            {
+                const int64_t pv = i > i_first ? i - 1 : i_first;
+                fetch_tile<S, IO, HAS_Z, true>(a, pl, tent, pv,
+                                               static_cast<int>(min<int64_t>(kBT, L - pv * kBT)), raw);
+            }
 
 #pragma unroll
             for (int q = 0; q < kNpw; ++q) h[q] = he[q];
@@ -485,14 +519,17 @@ __device__ __forceinline__ void bwd_whole_group(const BwdArgs& a, int64_t ngroup
         }
     }
 
-    // gradients at h0 and the per-row partials of dA, dD, d bias
+    // the gradient at h0 (first chunk; later chunks' en * lam is what their
+    // left neighbour takes in, already folded by the carry) and the
+    // per-(chunk, row) partials of dA, dD, d bias
+    const int64_t prow = chunk * f.batch + pl.b;
     if (pl.valid) {
 #pragma unroll
         for (int q = 0; q < kNpw; ++q) {
             if (sv[q]) {
                 const int64_t col = (pl.b * f.dim + pl.d) * N + pl.n0 + q;
-                if (a.dh0 != nullptr) a.dh0[col] = en[q] * lam[q];
-                part_a[col] = dA[q];
+                if (chunk == 0 && a.dh0 != nullptr) a.dh0[col] = en[q] * lam[q];
+                part_a[(prow * f.dim + pl.d) * N + pl.n0 + q] = dA[q];
             }
         }
     }
@@ -507,8 +544,183 @@ __device__ __forceinline__ void bwd_whole_group(const BwdArgs& a, int64_t ngroup
             sd += lds.slot[u][0][lane];
             sb += lds.slot[u][0][kWave + lane];
         }
-        part_d[pl.b * f.dim + pl.d] = sd;
-        part_bias[pl.b * f.dim + pl.d] = sb;
+        part_d[prow * f.dim + pl.d] = sd;
+        part_bias[prow * f.dim + pl.d] = sb;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// A sequence cut into chunks, for shapes whose channel groups alone do not
+// fill the chip. Each (chunk, row, group) workgroup of the main kernel walks
+// only its chunk and needs the state entering it and the adjoint entering it
+// from the right. Both are first-order linear recurrences over the chunks:
+// the state after chunk c is P_c h + e_c with e_c the chunk's end state from
+// a zero start and P_c = exp(A * sum of delta over the chunk); the adjoint
+// the chunk hands to its left neighbour, Abar of its first token times lam
+// there, is P_c rho + l_c with rho what it takes in and l_c the same walked
+// back from zero. Each chunk is summarised, and the summaries are folded in
+// order (forward for the states, from the last chunk back for the adjoint).
+
+// State summary of chunks 0 .. nchunks-2 (whole tiles): end state from a
+// zero start (chunk 0 from h0) and decay product, [chunk][b][d][n].
+template <int S, int IO, bool SP>
+__global__ __launch_bounds__(kWave * S) void bwd_state_summary_kernel(BwdArgs a, int64_t ngroups,
+                                                                      BwdWs ws, float* end,
+                                                                      float* decay) {
+    __shared__ BwdLds<S> lds;
+    const ScanArgs& f = a.fwd;
+    const int N = f.dstate;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t rows = f.batch * ngroups;
+    const int64_t chunk = blockIdx.x / rows;
+    const Place pl = make_place(f, ngroups, blockIdx.x - chunk * rows);
+    const int64_t i_first = chunk * (ws.chunk_len / kBT), i_end = i_first + ws.chunk_len / kBT;
+    const int64_t col0 = (pl.b * f.dim + pl.d) * N;
+    bool sv[kNpw];
+    float A2[kNpw], h[kNpw];
+#pragma unroll
+    for (int q = 0; q < kNpw; ++q) {
+        const int n = pl.n0 + q;
+        sv[q] = n < N;
+        A2[q] = sv[q] ? f.A[pl.d * N + n] * kLog2e : 0.0f;
+        h[q] = (chunk == 0 && sv[q] && f.h0 != nullptr) ? f.h0[col0 + n] : 0.0f;
+    }
+    float dsum = 0.0f;
+    Own own[(kBT + S - 1) / S];
+    TileRaw<S> raw;
+    fetch_tile<S, IO, false, false>(a, pl, ws.tent, i_first, kBT, raw);
+    for (int64_t i = i_first; i < i_end; ++i) {
+        put_tile<S, IO, SP, false, false>(raw, pl, lds, kBT, N, own);
+        __syncthreads();
+        fetch_tile<S, IO, false, false>(a, pl, ws.tent, min(i + 1, i_end - 1), kBT, raw);
+#pragma unroll
+        for (int j0 = 0; j0 < kBT; j0 += 2) {
+            float2 v[2];
+            f32x4 bq[2];
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) {
+                v[jj] = lds.dtx[j0 + jj][lane];
+                bq[jj] = *reinterpret_cast<const f32x4*>(&lds.bc[0][j0 + jj][pl.n0]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) {
+                const float du = v[jj].x * v[jj].y;
+                dsum += v[jj].x;
+#pragma unroll
+                for (int q = 0; q < kNpw; ++q)
+                    h[q] = fmaf(fast_exp2(v[jj].x * A2[q]), h[q], du * bq[jj][q]);
+            }
+        }
+        __syncthreads();
+    }
+    if (pl.valid) {
+        const int64_t at = chunk * f.batch * f.dim * N + col0 + pl.n0;
+#pragma unroll
+        for (int q = 0; q < kNpw; ++q) {
+            if (sv[q]) {
+                end[at + q] = h[q];
+                decay[at + q] = fast_exp2(A2[q] * dsum);
+            }
+        }
+    }
+}
+
+// Adjoint summary of chunks 1 .. nchunks-1, walked back from a zero adjoint
+// (the last chunk from dhL): what the chunk hands to its left neighbour and
+// its decay product, stored at [nchunks - 1 - chunk][b][d][n] so that the
+// same in-order fold gives the adjoints.
+template <int S, int IO, bool SP, bool HAS_Z>
+__global__ __launch_bounds__(kWave * S) void bwd_adjoint_summary_kernel(BwdArgs a, int64_t ngroups,
+                                                                        BwdWs ws, float* end,
+                                                                        float* decay) {
+    __shared__ BwdLds<S> lds;
+    const ScanArgs& f = a.fwd;
+    const int N = f.dstate;
+    const int64_t L = f.seqlen;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t rows = f.batch * ngroups;
+    const int64_t chunk = 1 + blockIdx.x / rows;
+    const Place pl = make_place(f, ngroups, blockIdx.x - (chunk - 1) * rows);
+    const bool last_chunk = chunk == ws.nchunks - 1;
+    const int64_t i_first = chunk * (ws.chunk_len / kBT);
+    const int64_t i_end = last_chunk ? (L + kBT - 1) / kBT : i_first + ws.chunk_len / kBT;
+    const int64_t col0 = (pl.b * f.dim + pl.d) * N;
+    bool sv[kNpw];
+    float A2[kNpw], lam[kNpw], en[kNpw];
+#pragma unroll
+    for (int q = 0; q < kNpw; ++q) {
+        const int n = pl.n0 + q;
+        sv[q] = n < N;
+        A2[q] = sv[q] ? f.A[pl.d * N + n] * kLog2e : 0.0f;
+        lam[q] = (last_chunk && sv[q] && a.dhL != nullptr) ? a.dhL[col0 + n] : 0.0f;
+        en[q] = 1.0f;
+    }
+    float dsum = 0.0f;
+    Own own[(kBT + S - 1) / S];
+    TileRaw<S> raw;
+    fetch_tile<S, IO, HAS_Z, true>(a, pl, ws.tent, i_end - 1,
+                                   static_cast<int>(min<int64_t>(kBT, L - (i_end - 1) * kBT)), raw);
+    for (int64_t i = i_end - 1; i >= i_first; --i) {
+        // tokens past the end of the sequence are staged inert (g = delta = 0,
+        // zero C rows): they leave lam, en and the sum unchanged
+        put_tile<S, IO, SP, HAS_Z, true>(raw, pl, lds, static_cast<int>(min<int64_t>(kBT, L - i * kBT)),
+                                         N, own);
+        __syncthreads();
+        {
+            const int64_t pv = i > i_first ? i - 1 : i_first;
+            fetch_tile<S, IO, HAS_Z, true>(a, pl, ws.tent, pv,
+                                           static_cast<int>(min<int64_t>(kBT, L - pv * kBT)), raw);
+        }
+#pragma unroll
+        for (int j1 = kBT - 1; j1 >= 0; j1 -= 2) {
+            float2 vv[2];
+            float gq[2];
+            f32x4 cq[2];
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) {
+                vv[jj] = lds.dtx[j1 - jj][lane];
+                gq[jj] = lds.g[j1 - jj][lane];
+                cq[jj] = *reinterpret_cast<const f32x4*>(&lds.bc[1][j1 - jj][pl.n0]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) {
+                dsum += vv[jj].x;
+#pragma unroll
+                for (int q = 0; q < kNpw; ++q) {
+                    lam[q] = fmaf(en[q], lam[q], cq[jj][q] * gq[jj]);
+                    en[q] = fast_exp2(vv[jj].x * A2[q]);
+                }
+            }
+        }
+        __syncthreads();
+    }
+    if (pl.valid) {
+        const int64_t at = (ws.nchunks - 1 - chunk) * f.batch * f.dim * N + col0 + pl.n0;
+#pragma unroll
+        for (int q = 0; q < kNpw; ++q) {
+            if (sv[q]) {
+                end[at + q] = en[q] * lam[q];
+                decay[at + q] = fast_exp2(A2[q] * dsum);
+            }
+        }
+    }
+}
+
+// One thread per (b, d, n) column folds the summaries in order: start[k] =
+// what enters summary k, k = 1 .. nchunks-1 (entry 0 is the first one's own).
+__global__ __launch_bounds__(256) void bwd_fold_kernel(int64_t columns, int64_t nchunks,
+                                                       const float* end, const float* decay,
+                                                       float* start) {
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+    for (int64_t col = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; col < columns;
+         col += stride) {
+        float H = end[col];
+        for (int64_t k = 1; k < nchunks; ++k) {
+            start[k * columns + col] = H;
+            if (k < nchunks - 1) H = fmaf(decay[k * columns + col], H, end[k * columns + col]);
+        }
     }
 }
 
@@ -896,8 +1108,12 @@ __global__ __launch_bounds__(256) void bwd_bc_reduce_kernel(int64_t per, int64_t
     }
 }
 
-// dA, dD, d bias: the per-row partials added in row order.
-__global__ __launch_bounds__(256) void bwd_param_reduce_kernel(int64_t batch, int64_t dim, int N,
+// dA, dD, d bias: the per-row partials (rows: chunks x batch rows) added in
+// row order, loading kParamBatch rows before adding them so a thread waits
+// for memory once per batch of rows.
+constexpr int kParamBatch = 8;
+
+__global__ __launch_bounds__(256) void bwd_param_reduce_kernel(int64_t rows, int64_t dim, int N,
                                                                const float* part_a,
                                                                const float* part_d,
                                                                const float* part_bias, float* dA,
@@ -907,13 +1123,33 @@ __global__ __launch_bounds__(256) void bwd_param_reduce_kernel(int64_t batch, in
     for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < cols;
          i += stride) {
         float s = 0.0f;
-        for (int64_t b = 0; b < batch; ++b) s += part_a[b * cols + i];
+        for (int64_t b0 = 0; b0 < rows; b0 += kParamBatch) {
+            float v[kParamBatch];
+#pragma unroll
+            for (int u = 0; u < kParamBatch; ++u)
+                v[u] = part_a[min(b0 + u, rows - 1) * cols + i];  // clamped: unused past rows
+#pragma unroll
+            for (int u = 0; u < kParamBatch; ++u)
+                if (b0 + u < rows) s += v[u];
+        }
         dA[i] = s;
         if (i < dim) {
             float sd = 0.0f, sb = 0.0f;
-            for (int64_t b = 0; b < batch; ++b) {
-                sd += part_d[b * dim + i];
-                sb += part_bias[b * dim + i];
+            for (int64_t b0 = 0; b0 < rows; b0 += kParamBatch) {
+                float vd[kParamBatch], vb[kParamBatch];
+#pragma unroll
+                for (int u = 0; u < kParamBatch; ++u) {
+                    const int64_t b = min(b0 + u, rows - 1);
+                    vd[u] = part_d[b * dim + i];
+                    vb[u] = part_bias[b * dim + i];
+                }
+#pragma unroll
+                for (int u = 0; u < kParamBatch; ++u) {
+                    if (b0 + u < rows) {
+                        sd += vd[u];
+                        sb += vb[u];
+                    }
+                }
             }
             if (dD != nullptr) dD[i] = sd;
             if (dbias != nullptr) dbias[i] = sb;
@@ -940,8 +1176,10 @@ __global__ __launch_bounds__(256) void bwd_degenerate_kernel(int64_t cols, int64
 }
 
 struct BwdLayout {
-    int64_t ntiles, ngroups, nslots;
-    size_t tent, part_bc, part_a, part_d, part_bias, total;  // float offsets / count
+    int64_t ntiles, ngroups, nslots, nchunks, chunk_len;
+    size_t tent, part_bc, part_a, part_d, part_bias;          // float offsets
+    size_t fend, fdecay, fstart, rend, rdecay, rstart;        // chunk carries (nchunks > 1)
+    size_t total;                                             // float count
 };
 
 // Half groups need 4 waves of states (dstate 13..16).
@@ -950,10 +1188,12 @@ static_assert(kNpw * 4 == 16, "dstate 13..16 fills 4 waves");
 
 inline size_t round64(size_t v) { return (v + 63) / 64 * 64; }
 
-BwdLayout bwd_layout(int64_t batch, int64_t seqlen, int64_t dim, int dstate) {
+BwdLayout bwd_layout(int64_t batch, int64_t seqlen, int64_t dim, int dstate, int64_t chunk_len) {
     BwdLayout l;
     l.ntiles = (seqlen + kBT - 1) / kBT;
     l.ngroups = (dim + kWave - 1) / kWave;
+    l.chunk_len = chunk_len > 0 ? chunk_len : l.ntiles * kBT;
+    l.nchunks = chunk_len > 0 ? (seqlen + chunk_len - 1) / chunk_len : 1;
     // slots for the second halves of split groups whenever the shape allows
     // splitting, so the size needs no knowledge of the device
     l.nslots = bwd_halvable(dstate) ? 2 * l.ngroups : l.ngroups;
@@ -963,12 +1203,26 @@ BwdLayout bwd_layout(int64_t batch, int64_t seqlen, int64_t dim, int dstate) {
     off += round64(static_cast<size_t>(l.ntiles) * states);
     l.part_bc = off;
     off += round64(2 * static_cast<size_t>(l.nslots) * batch * seqlen * dstate);
+    const size_t nc = static_cast<size_t>(l.nchunks);
     l.part_a = off;
-    off += round64(states);
+    off += round64(nc * states);
     l.part_d = off;
-    off += round64(static_cast<size_t>(batch) * dim);
+    off += round64(nc * batch * dim);
     l.part_bias = off;
-    off += round64(static_cast<size_t>(batch) * dim);
+    off += round64(nc * batch * dim);
+    const size_t carry = l.nchunks > 1 ? round64(nc * states) : 0;
+    l.fend = off;
+    off += carry;
+    l.fdecay = off;
+    off += carry;
+    l.fstart = off;
+    off += carry;
+    l.rend = off;
+    off += carry;
+    l.rdecay = off;
+    off += carry;
+    l.rstart = off;
+    off += carry;
     l.total = off;
     return l;
 }
@@ -978,7 +1232,7 @@ hipError_t launch_bwd_main(const BwdArgs& a, const BwdLayout& l, float* ws, hipS
     const int64_t groups = a.fwd.batch * l.ngroups;
     const bool has_d = a.fwd.D != nullptr, has_z = a.fwd.z != nullptr;
     const BwdWs w{ws + l.tent, ws + l.part_bc, ws + l.part_a, ws + l.part_d, ws + l.part_bias,
-                  l.nslots};
+                  l.nslots, l.nchunks, l.chunk_len, ws + l.fstart, ws + l.rstart};
     if constexpr (S == 4) {
         if (a.halves > 0) {
             const int64_t nwhole = groups - a.halves;
@@ -993,8 +1247,26 @@ hipError_t launch_bwd_main(const BwdArgs& a, const BwdLayout& l, float* ws, hipS
             return hipGetLastError();
         }
     }
+    if (l.nchunks > 1) {
+        // the chunk carries: states forward, adjoints backward
+        const int64_t columns = a.fwd.batch * a.fwd.dim * a.fwd.dstate;
+        const dim3 grid((l.nchunks - 1) * groups), block(kWave * S);
+        hipLaunchKernelGGL((bwd_state_summary_kernel<S, IO, SP>), grid, block, 0, s, a, l.ngroups, w,
+                           ws + l.fend, ws + l.fdecay);
+        hipLaunchKernelGGL(bwd_fold_kernel, dim3(stride_blocks(columns)), dim3(256), 0, s, columns,
+                           l.nchunks, ws + l.fend, ws + l.fdecay, ws + l.fstart);
+        if (has_z)
+            hipLaunchKernelGGL((bwd_adjoint_summary_kernel<S, IO, SP, true>), grid, block, 0, s, a,
+                               l.ngroups, w, ws + l.rend, ws + l.rdecay);
+        else
+            hipLaunchKernelGGL((bwd_adjoint_summary_kernel<S, IO, SP, false>), grid, block, 0, s, a,
+                               l.ngroups, w, ws + l.rend, ws + l.rdecay);
+        hipLaunchKernelGGL(bwd_fold_kernel, dim3(stride_blocks(columns)), dim3(256), 0, s, columns,
+                           l.nchunks, ws + l.rend, ws + l.rdecay, ws + l.rstart);
+    }
     auto go = [&](auto kernel) {
-        hipLaunchKernelGGL(kernel, dim3(groups), dim3(kWave * S), 0, s, a, l.ngroups, w);
+        hipLaunchKernelGGL(kernel, dim3(l.nchunks * groups), dim3(kWave * S), 0, s, a, l.ngroups,
+                           w);
     };
     if (has_d && has_z) go(scan_bwd_kernel<S, IO, SP, true, true>);
     else if (has_d) go(scan_bwd_kernel<S, IO, SP, true, false>);
@@ -1006,7 +1278,7 @@ hipError_t launch_bwd_main(const BwdArgs& a, const BwdLayout& l, float* ws, hipS
 template <int IO, bool SP>
 hipError_t launch_bwd_io(const BwdArgs& a, float* ws, hipStream_t s) {
     const ScanArgs& f = a.fwd;
-    const BwdLayout l = bwd_layout(f.batch, f.seqlen, f.dim, f.dstate);
+    const BwdLayout l = bwd_layout(f.batch, f.seqlen, f.dim, f.dstate, a.chunk_len);
     hipError_t e;
     switch ((f.dstate + kNpw - 1) / kNpw) {
         case 1: e = launch_bwd_main<1, IO, SP>(a, l, ws, s); break;
@@ -1022,16 +1294,17 @@ hipError_t launch_bwd_io(const BwdArgs& a, float* ws, hipStream_t s) {
                        f.seqlen * f.dstate, l.ngroups, l.nslots, nwhole, ws + l.part_bc, a.dB,
                        a.dC);
     hipLaunchKernelGGL(bwd_param_reduce_kernel, dim3(stride_blocks(f.dim * f.dstate)), dim3(256),
-                       0, s, f.batch, f.dim, f.dstate, ws + l.part_a, ws + l.part_d,
+                       0, s, l.nchunks * f.batch, f.dim, f.dstate, ws + l.part_a, ws + l.part_d,
                        ws + l.part_bias, a.dA, a.dD, a.ddelta_bias);
     return hipGetLastError();
 }
 
 }  // namespace
 
-size_t scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int dstate) {
+size_t scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t dim, int dstate,
+                                int64_t chunk_len) {
     if (batch == 0 || seqlen == 0 || dim == 0) return 0;
-    return bwd_layout(batch, seqlen, dim, dstate).total * sizeof(float);
+    return bwd_layout(batch, seqlen, dim, dstate, chunk_len).total * sizeof(float);
 }
 
 hipError_t launch_scan_bwd(const BwdArgs& a, void* workspace, hipStream_t stream) {

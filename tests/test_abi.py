@@ -241,14 +241,24 @@ def test_conv_rejects_bad_arguments(lib):
 
 
 def test_scan_bwd_rejects_bad_arguments(lib):
+    # a plan that needs no device: one chunk (chunk_len = seqlen), no halves
+    whole = _plan(chunk_len=64, halves=-1)
     need = ctypes.c_size_t(0)
-    assert lib.ssm_scan_bwd_workspace_size(2, 64, 64, 16, 1, ctypes.byref(need)) == OK
+    assert lib.ssm_scan_bwd_workspace_size(2, 64, 64, 16, 1, whole, None, ctypes.byref(need)) == OK
     assert need.value > 0
-    assert lib.ssm_scan_bwd_workspace_size(2, 64, 64, 17, 1, ctypes.byref(need)) == UNSUPPORTED
-    assert lib.ssm_scan_bwd_workspace_size(2, 64, 64, 16, 1, None) == INVALID
-    lib.ssm_scan_bwd_workspace_size(2, 64, 64, 16, 1, ctypes.byref(need))
+    assert lib.ssm_scan_bwd_workspace_size(2, 64, 64, 17, 1, whole, None,
+                                           ctypes.byref(need)) == UNSUPPORTED
+    assert lib.ssm_scan_bwd_workspace_size(2, 64, 64, 16, 1, whole, None, None) == INVALID
+    # chunks of 16 tokens: the same scratch plus the chunk carries and
+    # per-chunk partials; the resolved plan reports the chunk length
+    chunked = ctypes.c_size_t(0)
+    res = ms.ScanPlan(0, 0, 0, 0, 0)
+    assert lib.ssm_scan_bwd_workspace_size(2, 64, 64, 16, 1, _plan(chunk_len=16, halves=-1),
+                                           ctypes.byref(res), ctypes.byref(chunked)) == OK
+    assert chunked.value > need.value and (res.chunk_len, res.halves) == (16, 0)
+    lib.ssm_scan_bwd_workspace_size(2, 64, 64, 16, 1, whole, None, ctypes.byref(need))
 
-    def bwd(batch=2, seqlen=64, dim=64, dstate=16, dtype=1, opts=None, plan=None, ws=P, wsb=None,
+    def bwd(batch=2, seqlen=64, dim=64, dstate=16, dtype=1, opts=None, plan=whole, ws=P, wsb=None,
             **kw):
         p = dict(x=P, delta=P, A=P, B=P, C=P, D=None, z=None, h0=None, dy=P, dhL=None, dx=P,
                  ddelta=P, dA=P, dB=P, dC=P, dD=None, dz=None, dh0=None, ddelta_bias=None)
@@ -271,15 +281,17 @@ def test_scan_bwd_rejects_bad_arguments(lib):
     assert bwd(dz=P) == INVALID
     assert bwd(ddelta_bias=P) == INVALID
     assert bwd(opts=_opts(reserved=3)) == INVALID
-    # only the plan's halves field applies: 2 rows x 1 group here
-    assert bwd(plan=_plan(chunk_len=8)) == INVALID
+    # the plan's chunk_len and halves apply: 2 rows x 1 group here
+    assert bwd(plan=_plan(chunk_len=12)) == INVALID     # not a multiple of 8
+    assert bwd(plan=_plan(chunk_len=-8)) == INVALID
+    assert bwd(plan=_plan(chunk_len=16, halves=1)) == UNSUPPORTED   # halves need one chunk
     assert bwd(plan=_plan(split=4)) == INVALID
     assert bwd(plan=_plan(carry=1)) == INVALID
     assert bwd(plan=_plan(halves=-1, reserved=1)) == INVALID
     assert bwd(plan=_plan(halves=-2)) == INVALID
     assert bwd(plan=_plan(halves=3)) == INVALID
     assert bwd(plan=_plan(halves=1), dstate=8) == UNSUPPORTED
-    assert bwd(plan=_plan(halves=1), ws=None) == WORKSPACE
+    assert bwd(plan=_plan(chunk_len=64, halves=1), ws=None) == WORKSPACE
     assert bwd(plan=_plan(halves=5), dim=0) == OK   # nothing runs
     assert bwd(ws=None) == WORKSPACE
     assert bwd(wsb=need.value - 4) == WORKSPACE

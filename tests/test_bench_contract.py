@@ -43,11 +43,3 @@ def test_roofline_names_the_planned_kernel():
     mixed = ms.Plan(2048, 4, ms.CARRY_RERUN, 128, 0)
     assert bench.dominant_kernel(whole) == "chunk_output_kernel"
     assert bench.dominant_kernel(mixed) == "chunk_mixed_kernel"
-
-
-def test_backward_half_groups_reported_when_forced():
-    w = W.WORKLOADS["mamba28b_layer"]
-    assert bench.bwd_half_groups(w, 5) == 5
-    assert bench.bwd_half_groups(w, -1) == 0
-    small = W.WORKLOADS["tiny_f32"]            # dstate 4: the backward cannot split
-    assert bench.bwd_half_groups(small, 3) == 0

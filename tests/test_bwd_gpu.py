@@ -57,11 +57,12 @@ def _inputs(batch, seqlen, dim, dstate, io, seed, h0=True, D=True, z=True, softp
     return inp, dy, dhL
 
 
-def _compare(orc, inp, dy, dhL, io, what, keys=KEYS, halves=ms.HALVES_AUTO):
+def _compare(orc, inp, dy, dhL, io, what, keys=KEYS, halves=ms.HALVES_AUTO, chunk_len=0):
     sp = inp.get("delta_bias") is not None
     got = ms.scan_bwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp.get("D"),
                       inp.get("z"), inp.get("h0"), dy=dy, dhL=dhL,
-                      delta_bias=inp.get("delta_bias"), delta_softplus=sp, halves=halves)
+                      delta_bias=inp.get("delta_bias"), delta_softplus=sp, halves=halves,
+                      chunk_len=chunk_len)
     torch.cuda.synchronize()
     want = orc.scan_bwd(**inp, dy=dy, dhL=dhL, delta_softplus=sp)
     for k in keys:
@@ -228,3 +229,67 @@ def test_bwd_nan_propagates_like_the_oracle(orc, halves):
     assert wnan["ddelta"][1, t:, d].all() and not wnan["ddelta"][1, :t, d].any()
     assert wnan["dz"][1, t:, d].all() and wnan["dC"][1, t:].all() and wnan["dB"][1, t].all()
     assert wnan["dA"][d].all() and wnan["dD"][d] and not wnan["dx"].any() and not wnan["dh0"].any()
+
+
+# ---------------------------------------------------------------------------
+# sequences cut into chunks: state and adjoint summaries folded across chunks
+
+CHUNK_CASES = [
+    # (batch, seqlen, dim, dstate, io, chunk_len)
+    (1, 257, 70, 16, "f32", 64),     # ragged last chunk and tile, 5 chunks
+    (2, 300, 130, 12, "bf16", 72),   # chunk not a power of two, 3 waves
+    (1, 200, 64, 5, "f32", 64),      # 2 waves
+    (1, 129, 33, 2, "f32", 8),       # one tile per chunk, 17 chunks
+    (3, 100, 20, 4, "f32", 24),
+    (2, 64, 64, 16, "f32", 64),      # chunk_len == seqlen: one chunk
+]
+
+
+@pytest.mark.parametrize("case", CHUNK_CASES, ids=lambda c: "x".join(map(str, c)))
+def test_bwd_chunked(orc, case):
+    batch, seqlen, dim, dstate, io, cl = case
+    inp, dy, dhL = _inputs(batch, seqlen, dim, dstate, io, seed=seqlen + dim + cl)
+    _say(f"case backward chunked {case}")
+    _compare(orc, inp, dy, dhL, io, f"chunked {case}", chunk_len=cl)
+
+
+def test_bwd_chunked_options_and_softplus(orc):
+    inp, dy, dhL = _inputs(2, 150, 96, 16, "f32", seed=61, h0=False, D=False, z=False)
+    _say("case backward chunked without D, z, h0, dhL")
+    _compare(orc, inp, dy, None, "f32", "chunked bare", chunk_len=40)
+    inp, dy, dhL = _inputs(2, 150, 96, 16, "bf16", seed=62, softplus=True)
+    _say("case backward chunked with fused softplus")
+    _compare(orc, inp, dy, dhL, "bf16", "chunked softplus", chunk_len=48)
+
+
+def test_bwd_chunked_agrees_with_one_chunk():
+    inp, dy, dhL = _inputs(1, 500, 192, 16, "f32", seed=63)
+    args = (inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"], inp["h0"])
+    one = ms.scan_bwd(*args, dy=dy, dhL=dhL, chunk_len=0, halves=ms.HALVES_NONE)
+    cut = ms.scan_bwd(*args, dy=dy, dhL=dhL, chunk_len=96)
+    again = ms.scan_bwd(*args, dy=dy, dhL=dhL, chunk_len=96)
+    torch.cuda.synchronize()
+    for k in KEYS:
+        if one[k] is None:
+            continue
+        assert_close(cut[k], one[k], 2e-5, f"chunked vs one chunk {k}")
+        assert torch.equal(cut[k], again[k]), f"chunked run to run {k}"
+
+
+def test_bwd_automatic_plan_cuts_small_batch(orc):
+    # one row of 130 channels: 3 groups cannot fill the chip, so the plan
+    # cuts the sequence; the result still matches the oracle
+    plan = ms.resolve_bwd_plan(1, 2048, 130, 16, torch.float32)
+    assert 64 <= plan.chunk_len < 2048 and plan.chunk_len % 8 == 0 and plan.halves == 0
+    big = ms.resolve_bwd_plan(8, 2048, 5120, 16, torch.bfloat16)
+    assert big.chunk_len == 2048          # the Mamba-2.8B layer stays whole
+    inp, dy, dhL = _inputs(1, 2048, 130, 16, "f32", seed=64)
+    _say(f"case backward automatic plan, chunks of {plan.chunk_len}")
+    _compare(orc, inp, dy, dhL, "f32", "automatic chunks")
+
+
+def test_bwd_chunks_and_halves_together_rejected():
+    inp, dy, dhL = _inputs(1, 128, 64, 16, "f32", seed=65)
+    with pytest.raises(ms.MambaScanError):
+        ms.scan_bwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"],
+                    inp["h0"], dy=dy, dhL=dhL, chunk_len=64, halves=1)
