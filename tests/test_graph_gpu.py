@@ -175,3 +175,43 @@ def test_graph_chunked_scan_and_ssd_replay_bitwise():
         assert torch.equal(my, my_ref) and torch.equal(mhL, mh_ref), f"half groups, replay {r}"
         assert torch.equal(sy, sy_ref) and torch.equal(shL, sh_ref), f"ssd, replay {r}"
         _eager_noise(r)
+
+
+def test_graph_backward_replay_bitwise():
+    """The backward pass captured twice: a sequence cut into chunks (state
+    and adjoint summaries, their folds, the reverse kernel, the reductions;
+    workspace allocated while capturing) and a whole sequence with half
+    channel groups."""
+    w = dataclasses.replace(W.WORKLOADS["mamba130m_layer"], h0="normal")
+    inp = {k: (v.to(DEV) if v is not None else None)
+           for k, v in W.generate_scan(w, batch=2, seqlen=300, dim=192, seed=21).items()}
+    g = torch.Generator(device=DEV).manual_seed(22)
+    dy = torch.randn(2, 300, 192, generator=g, device=DEV).to(inp["x"].dtype)
+    dhL = torch.randn(2, 192, w.dstate, generator=g, device=DEV)
+    args = (inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"], inp["h0"])
+    out = {}
+
+    def step():
+        out["cut"] = ms.scan_bwd(*args, dy=dy, dhL=dhL, chunk_len=64)
+        out["half"] = ms.scan_bwd(*args, dy=dy, dhL=dhL, chunk_len=304, halves=3)
+
+    graph = _capture(step)
+    ref = {"cut": ms.scan_bwd(*args, dy=dy, dhL=dhL, chunk_len=64),
+           "half": ms.scan_bwd(*args, dy=dy, dhL=dhL, chunk_len=304, halves=3)}
+    torch.cuda.synchronize()
+    for r in range(REPLAYS):
+        _say(f"case graph backward: replay {r}")
+        for grads in out.values():
+            for v in grads.values():
+                if v is not None:
+                    v.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for kind, grads in out.items():
+            for k, v in grads.items():
+                if v is None:
+                    assert ref[kind][k] is None
+                    continue
+                assert torch.equal(v, ref[kind][k]), f"backward {kind} {k}, replay {r}"
+        _eager_noise(r)
