@@ -365,7 +365,8 @@ int make_bwd_plan(int64_t batch, int64_t seqlen, int64_t dim, int dstate,
             if (surplus > 0 && 2 * surplus <= cu) *halves = surplus;
         }
     }
-    if (nchunks * groups + *halves > (int64_t(1) << 31)) return MAMBA_ERR_UNSUPPORTED;
+    // the largest launch: both chunk summaries together, or the main kernel
+    if (2 * nchunks * groups + *halves > (int64_t(1) << 31)) return MAMBA_ERR_UNSUPPORTED;
     *chunk_len = len;
     return MAMBA_OK;
 }

@@ -564,16 +564,15 @@ __device__ __forceinline__ void bwd_whole_group(const BwdArgs& a, int64_t ngroup
 // State summary of chunks 0 .. nchunks-2 (whole tiles): end state from a
 // zero start (chunk 0 from h0) and decay product, [chunk][b][d][n].
 template <int S, int IO, bool SP>
-__global__ __launch_bounds__(kWave * S) void bwd_state_summary_kernel(BwdArgs a, int64_t ngroups,
-                                                                      BwdWs ws, float* end,
-                                                                      float* decay) {
-    __shared__ BwdLds<S> lds;
+__device__ __forceinline__ void bwd_state_summary(const BwdArgs& a, int64_t ngroups,
+                                                  const BwdWs& ws, float* end, float* decay,
+                                                  int64_t blk, BwdLds<S>& lds) {
     const ScanArgs& f = a.fwd;
     const int N = f.dstate;
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t rows = f.batch * ngroups;
-    const int64_t chunk = blockIdx.x / rows;
-    const Place pl = make_place(f, ngroups, blockIdx.x - chunk * rows);
+    const int64_t chunk = blk / rows;
+    const Place pl = make_place(f, ngroups, blk - chunk * rows);
     const int64_t i_first = chunk * (ws.chunk_len / kBT), i_end = i_first + ws.chunk_len / kBT;
     const int64_t col0 = (pl.b * f.dim + pl.d) * N;
     bool sv[kNpw];
@@ -631,17 +630,16 @@ __global__ __launch_bounds__(kWave * S) void bwd_state_summary_kernel(BwdArgs a,
 // its decay product, stored at [nchunks - 1 - chunk][b][d][n] so that the
 // same in-order fold gives the adjoints.
 template <int S, int IO, bool SP, bool HAS_Z>
-__global__ __launch_bounds__(kWave * S) void bwd_adjoint_summary_kernel(BwdArgs a, int64_t ngroups,
-                                                                        BwdWs ws, float* end,
-                                                                        float* decay) {
-    __shared__ BwdLds<S> lds;
+__device__ __forceinline__ void bwd_adjoint_summary(const BwdArgs& a, int64_t ngroups,
+                                                    const BwdWs& ws, float* end, float* decay,
+                                                    int64_t blk, BwdLds<S>& lds) {
     const ScanArgs& f = a.fwd;
     const int N = f.dstate;
     const int64_t L = f.seqlen;
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t rows = f.batch * ngroups;
-    const int64_t chunk = 1 + blockIdx.x / rows;
-    const Place pl = make_place(f, ngroups, blockIdx.x - (chunk - 1) * rows);
+    const int64_t chunk = 1 + blk / rows;
+    const Place pl = make_place(f, ngroups, blk - (chunk - 1) * rows);
     const bool last_chunk = chunk == ws.nchunks - 1;
     const int64_t i_first = chunk * (ws.chunk_len / kBT);
     const int64_t i_end = last_chunk ? (L + kBT - 1) / kBT : i_first + ws.chunk_len / kBT;
@@ -708,14 +706,37 @@ __global__ __launch_bounds__(kWave * S) void bwd_adjoint_summary_kernel(BwdArgs 
     }
 }
 
+// Both summaries in one launch (they are independent): blocks [0, per)
+// summarise the states of chunks 0 .. nchunks-2, blocks [per, 2 per) the
+// adjoints of chunks 1 .. nchunks-1.
+struct BwdCarry {
+    float *fend, *fdecay, *fstart, *rend, *rdecay, *rstart;
+};
+
+template <int S, int IO, bool SP, bool HAS_Z>
+__global__ __launch_bounds__(kWave * S) void bwd_summary_kernel(BwdArgs a, int64_t ngroups,
+                                                                BwdWs ws, BwdCarry c, int64_t per) {
+    __shared__ BwdLds<S> lds;
+    const int64_t blk = blockIdx.x;
+    if (blk < per)
+        bwd_state_summary<S, IO, SP>(a, ngroups, ws, c.fend, c.fdecay, blk, lds);
+    else
+        bwd_adjoint_summary<S, IO, SP, HAS_Z>(a, ngroups, ws, c.rend, c.rdecay, blk - per, lds);
+}
+
 // One thread per (b, d, n) column folds the summaries in order: start[k] =
-// what enters summary k, k = 1 .. nchunks-1 (entry 0 is the first one's own).
+// what enters summary k, k = 1 .. nchunks-1 (entry 0 is the first one's own);
+// threads [0, columns) fold the states, [columns, 2 columns) the adjoints.
 __global__ __launch_bounds__(256) void bwd_fold_kernel(int64_t columns, int64_t nchunks,
-                                                       const float* end, const float* decay,
-                                                       float* start) {
+                                                       BwdCarry c) {
     const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
-    for (int64_t col = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; col < columns;
-         col += stride) {
+    for (int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+         t < 2 * columns; t += stride) {
+        const bool adj = t >= columns;
+        const int64_t col = adj ? t - columns : t;
+        const float* end = adj ? c.rend : c.fend;
+        const float* decay = adj ? c.rdecay : c.fdecay;
+        float* start = adj ? c.rstart : c.fstart;
         float H = end[col];
         for (int64_t k = 1; k < nchunks; ++k) {
             start[k * columns + col] = H;
@@ -1250,19 +1271,18 @@ hipError_t launch_bwd_main(const BwdArgs& a, const BwdLayout& l, float* ws, hipS
     if (l.nchunks > 1) {
         // the chunk carries: states forward, adjoints backward
         const int64_t columns = a.fwd.batch * a.fwd.dim * a.fwd.dstate;
-        const dim3 grid((l.nchunks - 1) * groups), block(kWave * S);
-        hipLaunchKernelGGL((bwd_state_summary_kernel<S, IO, SP>), grid, block, 0, s, a, l.ngroups, w,
-                           ws + l.fend, ws + l.fdecay);
-        hipLaunchKernelGGL(bwd_fold_kernel, dim3(stride_blocks(columns)), dim3(256), 0, s, columns,
-                           l.nchunks, ws + l.fend, ws + l.fdecay, ws + l.fstart);
+        const int64_t per = (l.nchunks - 1) * groups;
+        const BwdCarry c{ws + l.fend, ws + l.fdecay, ws + l.fstart,
+                         ws + l.rend, ws + l.rdecay, ws + l.rstart};
+        const dim3 grid(2 * per), block(kWave * S);
         if (has_z)
-            hipLaunchKernelGGL((bwd_adjoint_summary_kernel<S, IO, SP, true>), grid, block, 0, s, a,
-                               l.ngroups, w, ws + l.rend, ws + l.rdecay);
+            hipLaunchKernelGGL((bwd_summary_kernel<S, IO, SP, true>), grid, block, 0, s, a,
+                               l.ngroups, w, c, per);
         else
-            hipLaunchKernelGGL((bwd_adjoint_summary_kernel<S, IO, SP, false>), grid, block, 0, s, a,
-                               l.ngroups, w, ws + l.rend, ws + l.rdecay);
-        hipLaunchKernelGGL(bwd_fold_kernel, dim3(stride_blocks(columns)), dim3(256), 0, s, columns,
-                           l.nchunks, ws + l.rend, ws + l.rdecay, ws + l.rstart);
+            hipLaunchKernelGGL((bwd_summary_kernel<S, IO, SP, false>), grid, block, 0, s, a,
+                               l.ngroups, w, c, per);
+        hipLaunchKernelGGL(bwd_fold_kernel, dim3(stride_blocks(2 * columns)), dim3(256), 0, s,
+                           columns, l.nchunks, c);
     }
     auto go = [&](auto kernel) {
         hipLaunchKernelGGL(kernel, dim3(l.nchunks * groups), dim3(kWave * S), 0, s, a, l.ngroups,
