@@ -293,3 +293,32 @@ def test_bwd_chunks_and_halves_together_rejected():
     with pytest.raises(ms.MambaScanError):
         ms.scan_bwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"],
                     inp["h0"], dy=dy, dhL=dhL, chunk_len=64, halves=1)
+
+
+def test_bwd_million_length_sampled(orc):
+    # one row of 2048 channels over 2^20 tokens: the plan cuts the sequence
+    # into chunks; per-channel gradients on sampled channels against the
+    # oracle over the whole sequence (dB and dC, sums over every channel, are
+    # checked on the smaller chunked cases)
+    w = W.WORKLOADS["million_length"]
+    plan = ms.resolve_bwd_plan(w.batch, w.seqlen, w.dim, w.dstate, torch.bfloat16)
+    assert plan.chunk_len < w.seqlen
+    inp = W.generate_scan(w, device=DEV)
+    g = torch.Generator(device=DEV).manual_seed(98)
+    dy = torch.randn(w.batch, w.seqlen, w.dim, generator=g, device=DEV).to(torch.bfloat16)
+    _say(f"case bwd {w.name} full size, chunks of {plan.chunk_len}")
+    got = ms.scan_bwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"],
+                      inp["h0"], dy=dy)
+    torch.cuda.synchronize()
+    idx = sample_channels(w.dim, count=6, seed=w.seed)
+    ix = torch.as_tensor(idx, device=DEV)
+    sub = dict(x=inp["x"].index_select(2, ix), delta=inp["delta"].index_select(2, ix),
+               A=inp["A"].index_select(0, ix), B=inp["B"], C=inp["C"],
+               D=inp["D"].index_select(0, ix), z=inp["z"].index_select(2, ix), h0=None)
+    _say(f"case bwd {w.name}: oracle on {len(idx)} channels")
+    want = orc.scan_bwd(**sub, dy=dy.index_select(2, ix))
+    for k in ("dx", "ddelta", "dz"):
+        assert_close(got[k].index_select(2, ix), want[k], TOL_BWD["bf16"], f"million {k}")
+    assert_close(got["dA"].index_select(0, ix), want["dA"], TOL_BWD["bf16"], "million dA")
+    assert_close(got["dD"].index_select(0, ix), want["dD"], TOL_BWD["bf16"], "million dD")
+    assert_close(got["dh0"].index_select(1, ix), want["dh0"], TOL_BWD["bf16"], "million dh0")
