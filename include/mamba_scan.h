@@ -100,10 +100,11 @@ typedef enum mamba_carry {
 } mamba_carry;
 
 /*
- * How ssm_scan_fwd divides its work over the GPU. A NULL plan, or a zero
- * field, lets the library choose from the shape and the current device's
- * compute-unit count; every choice gives the same result up to rounding
- * (and, with MAMBA_CARRY_REPAIR, the bound stated above).
+ * How ssm_scan_fwd divides its work over the GPU (ssm_scan_bwd takes the
+ * same struct and uses chunk_len and halves, as documented there). A NULL
+ * plan, or a zero field, lets the library choose from the shape and the
+ * current device's compute-unit count; every choice gives the same result
+ * up to rounding (and, with MAMBA_CARRY_REPAIR, the bound stated above).
  *
  * chunk_len    tokens per parallel chunk. Each sequence is cut into chunks
  *              that run in parallel and are joined as `carry` says. A
