@@ -152,9 +152,12 @@ template <int N, int S>
 struct BcStage {
     static constexpr int kVals = TT * N;                                // per tensor per tile
     static constexpr int kPerLane = (kVals + kWave * S - 1) / (kWave * S);
-    // LDS floats per tensor: every lane of every pass gets a slot, so lanes
-    // past the tile's values write padding instead of taking a branch
-    static constexpr int kSlots = kPerLane * kWave * S;
+    // LDS floats per tensor: the tile's values, rounded up to whole 16-byte
+    // runs so the C run starts aligned. Lanes past the values wrap around:
+    // they load and store the same value as the lane kVals below them, so
+    // every lane issues the same loads and stores without a branch.
+    static constexpr int kSlots = (kVals + 3) / 4 * 4;
+    __device__ static int slot(int q, int tid) { return (q * kWave * S + tid) % kVals; }
 };
 
 struct BcIo {
@@ -170,7 +173,7 @@ __device__ __forceinline__ void fetch_bc(const BcIo& bc, int tile, int cnt,
 #pragma unroll
     for (int q = 0; q < BcStage<N, S>::kPerLane; ++q) {
         // values past the tile's last token are clamped onto it (in bounds, unused)
-        const int idx = min(q * kWave * S + tid, cnt * N - 1);
+        const int idx = min(BcStage<N, S>::slot(q, tid), cnt * N - 1);
         const uint32_t off = static_cast<uint32_t>((tile * TT * N + idx) * esz);
         braw[q] = buf_load<IO>(bc.B, off, 0);
         craw[q] = buf_load<IO>(bc.C, off, 0);
@@ -186,7 +189,8 @@ __device__ __forceinline__ void stage_bc(float* bcs, const uint32_t (&braw)[BcSt
     const int tid = threadIdx.x;
 #pragma unroll
     for (int q = 0; q < BcStage<N, S>::kPerLane; ++q) {
-        const int idx = q * kWave * S + tid;
+        // a wrapped-around lane writes the value its twin writes
+        const int idx = BcStage<N, S>::slot(q, tid);
         bcs[idx] = raw_to_f32<IO>(braw[q]);
         bcs[P + idx] = raw_to_f32<IO>(craw[q]);
     }
@@ -401,12 +405,14 @@ __device__ __forceinline__ void finalize_tile(const ChunkIo& io, const float* re
 }
 
 // LDS of one workgroup: B/C tiles, per-token inputs and partial readouts,
-// each double-buffered by tile parity.
-template <int N, int S>
+// each double-buffered by tile parity. A pass without outputs (OUT false:
+// the chunk summaries) has no readouts, and the smaller footprint lets more
+// of its workgroups share a compute unit.
+template <int N, int S, bool OUT = true>
 struct ScanLds {
     float bcs[2][2 * BcStage<N, S>::kSlots];
     float2 dtdu[2][S > 1 ? TT * kWave : 1];
-    float red[2][S > 1 ? S * TT * kWave : 1];
+    float red[2][OUT && S > 1 ? S * TT * kWave : 1];
     int vote[2][S];  // pass 2 of the repaired carry: wave w's lanes are all done
 };
 
@@ -450,7 +456,7 @@ constexpr float kFixupLog2 = 32.0f;
 template <int N, int S, int IO, bool SP, int PASS, bool HAS_D, bool HAS_Z>
 __device__ __forceinline__ void scan_chunk(const ChunkIo& io, const BcIo& bcio, float dbias,
                                            int ntok, int w, int n0,
-                                           ScanLds<N, S>& lds,
+                                           ScanLds<N, S, PASS != kPassSummary>& lds,
                                            const float (&A2)[Split<N, S>::NPW],
                                            float (&h)[Split<N, S>::NPW], float dskip,
                                            float a2max, float& dsum) {
@@ -558,7 +564,14 @@ struct ChunkGrid {
     int64_t nchunks;          // chunks per sequence the grid covers
     int64_t chunk_len;        // tokens per chunk
     int64_t first_chunk = 0;  // sequence chunk of the grid's chunk 0
+    int fold = 0;             // output pass: fold the chunk summaries itself (no carry pass)
 };
+
+// Sequences of at most this many chunks skip the carry pass of the rerun
+// carry: each output workgroup folds the summaries of the chunks before its
+// own in its prologue (at most kFoldMaxChunks - 1 pairs per state, loaded
+// together), which costs less than a launch of its own.
+constexpr int64_t kFoldMaxChunks = 16;
 
 __device__ __forceinline__ void decode_block(const ChunkGrid& g, int64_t blk, int64_t& dblk,
                                              int64_t& k, int64_t& b) {
@@ -639,7 +652,7 @@ void chunk_summary_kernel(ScanArgs a, ChunkGrid g, Carry c) {
 #pragma unroll
         for (int q = 0; q < NPW; ++q) c.start[srow + q] = h[q];
     }
-    __shared__ ScanLds<N, S> lds;
+    __shared__ ScanLds<N, S, false> lds;
     float dsum = 0.0f;
     scan_chunk<N, S, IO, SP, kPassSummary, false, false>(s.io, s.bc, s.dbias, s.ntok, s.w, s.n0,
                                                          lds, A2, h, 0.0f, 0.0f, dsum);
@@ -697,10 +710,40 @@ __device__ __forceinline__ void output_group(const ScanArgs& a, const ChunkGrid&
     float A2[NPW], h[NPW];
 #pragma unroll
     for (int q = 0; q < NPW; ++q) A2[q] = a.A[s.d * N + s.n0 + q] * kLog2e;
-    if (g.nchunks == 1) {
+    if (g.nchunks == 1 || (g.fold && s.k == 0)) {
 #pragma unroll
         for (int q = 0; q < NPW; ++q)
             h[q] = a.h0 != nullptr ? a.h0[(s.b * a.dim + s.d) * N + s.n0 + q] : 0.0f;
+    } else if (g.fold) {
+        // The state entering chunk k: chunk 0's end state (exact: it started
+        // from h0) folded with the pairs of chunks 1 .. k-1 in order, the
+        // carry pass's arithmetic (so the same bits). The pairs of
+        // kFoldBatch chunks are loaded before they are folded.
+        constexpr int kFoldBatch = 4;
+        const int64_t cols = a.batch * a.dim * N;
+        const int64_t col = (s.b * a.dim + s.d) * N + s.n0;
+#pragma unroll
+        for (int q = 0; q < NPW; ++q) h[q] = c.end[col + q];
+        for (int64_t j0 = 1; j0 < s.k; j0 += kFoldBatch) {
+            float P[kFoldBatch][NPW], E[kFoldBatch][NPW];
+#pragma unroll
+            for (int u = 0; u < kFoldBatch; ++u) {
+                // clamped into range; pairs from chunk k on are never used
+                const int64_t row = min(j0 + u, s.k - 1) * cols + col;
+#pragma unroll
+                for (int q = 0; q < NPW; ++q) {
+                    P[u][q] = c.decay[row + q];
+                    E[u][q] = c.end[row + q];
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < kFoldBatch; ++u) {
+                if (j0 + u < s.k) {
+#pragma unroll
+                    for (int q = 0; q < NPW; ++q) h[q] = fmaf(P[u][q], h[q], E[u][q]);
+                }
+            }
+        }
     } else {
         const int64_t srow = ((s.k * a.batch + s.b) * a.dim + s.d) * N + s.n0;
 #pragma unroll
@@ -1072,8 +1115,12 @@ hipError_t launch_scan_ns(const ScanArgs& a, const ScanPlan& plan, void* ws, hip
         const int64_t blocks1 = g.nblk_d * g1.nchunks * a.batch;
         hipLaunchKernelGGL((chunk_summary_kernel<N, S, IO, SP>), dim3(blocks1), dim3(kWave * S), 0, s,
                            a, g1, c);
-        hipLaunchKernelGGL(chunk_carry_kernel, dim3(stride_blocks(columns)), dim3(256), 0, s,
-                           columns, plan.nchunks, c, nullptr);
+        if (plan.nchunks <= kFoldMaxChunks) {
+            g.fold = 1;
+        } else {
+            hipLaunchKernelGGL(chunk_carry_kernel, dim3(stride_blocks(columns)), dim3(256), 0, s,
+                               columns, plan.nchunks, c, nullptr);
+        }
     }
     const int64_t blocks = g.nblk_d * plan.nchunks * a.batch;
     const dim3 grid(blocks), block(kWave * S);
