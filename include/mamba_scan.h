@@ -201,6 +201,36 @@ int ssm_scan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int dstate, int dty
                  const mamba_scan_options* options, const mamba_scan_plan* plan,
                  void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Scratch bytes each GPU holds for ssm_scan_fwd_noalloc (32 MiB). */
+#define MAMBA_NOALLOC_SCRATCH_BYTES (32u * 1024u * 1024u)
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * ssm_scan_fwd without a workspace argument. It allocates nothing (no
+ * hipMalloc, hipFree or allocating library call). A plan that needs scratch
+ * (a chunked sequence) takes it from a fixed array of
+ * MAMBA_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs
+ * on until the process ends; the first such call on a device looks up that
+ * array's device address (hipGetSymbolAddress), later calls reuse it.
+ *
+ * Arguments, plan, results and errors are those of ssm_scan_fwd (same
+ * kernels, bit for bit the same outputs for the same plan), except:
+ *   - a plan whose workspace (ssm_scan_fwd_workspace_size) exceeds
+ *     MAMBA_NOALLOC_SCRATCH_BYTES returns MAMBA_ERR_WORKSPACE before any
+ *     HIP call; a smaller chunk count (a longer chunk_len) may fit;
+ *   - every call on one GPU shares that array, so calls that overlap on one
+ *     GPU (on different streams or from different threads) race and give
+ *     undefined results: callers serialise them, e.g. on one stream. The
+ *     array keeps the last call's contents; no call needs it cleared.
+ */
+int ssm_scan_fwd_noalloc(int64_t batch, int64_t seqlen, int64_t dim, int dstate, int dtype,
+                         const void* x, const void* delta, const float* A,
+                         const void* B, const void* C, const float* D, const void* z,
+                         const float* h0, void* y, float* hL,
+                         const mamba_scan_options* options, const mamba_scan_plan* plan,
+                         hipStream_t stream);
+
 /*
  * Single-token decode update (section "Taken Apart": one token moves the
  * state once). Equivalent to ssm_scan_fwd with seqlen = 1 and h0 = hL = h.

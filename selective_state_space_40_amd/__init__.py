@@ -8,6 +8,7 @@ There is no other code path: without the built library every call raises.
 
     y, hL = scan_fwd(x, delta, A, B, C, D=None, z=None, h0=None,
                      delta_bias=None, delta_softplus=False)
+    scan_fwd_noalloc(x, delta, A, B, C, D, z, h0, y=y, hL=hL)  # outputs given, nothing allocated
     y = state_update(h, x, delta, A, B, C, D=None, z=None,
                      delta_bias=None, delta_softplus=False)   # h updated in place
     grads = scan_bwd(x, delta, A, B, C, D=None, z=None, h0=None, dy=dy, dhL=None,
@@ -30,11 +31,12 @@ import os
 
 import torch
 
-__all__ = ["scan_fwd", "scan_bwd", "ssd_fwd", "state_update", "conv1d_fwd", "conv1d_update", "workspace_size", "resolve_plan", "library_path",
+__all__ = ["scan_fwd", "scan_fwd_noalloc", "NOALLOC_SCRATCH_BYTES", "scan_bwd", "ssd_fwd", "state_update", "conv1d_fwd", "conv1d_update", "workspace_size", "resolve_plan", "library_path",
            "load_library", "MambaScanError", "MAX_DSTATE", "ScanPlan", "ScanOptions", "Plan",
            "CARRY_AUTO", "CARRY_RERUN", "CARRY_REPAIR", "HALVES_AUTO", "HALVES_NONE"]
 
 MAX_DSTATE = 16
+NOALLOC_SCRATCH_BYTES = 32 * 1024 * 1024  # MAMBA_NOALLOC_SCRATCH_BYTES
 _DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -97,6 +99,8 @@ def load_library():
     lib.ssm_scan_fwd.argtypes = ([i64, i64, i64, i32, i32] + [vp] * 10 +
                                  [po, pp, vp, ctypes.c_size_t, vp])
     lib.ssm_scan_fwd.restype = i32
+    lib.ssm_scan_fwd_noalloc.argtypes = [i64, i64, i64, i32, i32] + [vp] * 10 + [po, pp, vp]
+    lib.ssm_scan_fwd_noalloc.restype = i32
     lib.ssm_state_update.argtypes = [i64, i64, i32, i32] + [vp] * 9 + [po, vp]
     lib.ssm_state_update.restype = i32
     lib.ssm_scan_bwd_workspace_size.argtypes = [i64, i64, i64, i32, i32, pp, pp,
@@ -250,6 +254,50 @@ def scan_fwd(x, delta, A, B, C, D=None, z=None, h0=None, *, delta_bias=None,
                               _ptr(hL), _options(delta_bias, delta_softplus), ctypes.byref(plan),
                               _ptr(ws), nbytes, _stream(dev))
     _check(st, "ssm_scan_fwd")
+    return y, hL
+
+
+def scan_fwd_noalloc(x, delta, A, B, C, D=None, z=None, h0=None, *, y, hL=None,
+                     delta_bias=None, delta_softplus=False, chunk_len=0, state_split=0,
+                     carry=CARRY_AUTO, halves=HALVES_AUTO):
+    """scan_fwd through ssm_scan_fwd_noalloc: the caller passes the outputs
+    y (like x) and hL ((batch, dim, N) fp32 or None) and nothing is
+    allocated, on the device or by torch; a chunked plan uses the library's
+    fixed per-GPU scratch (NOALLOC_SCRATCH_BYTES), which calls that overlap
+    on one GPU share. Returns (y, hL)."""
+    lib = load_library()
+    if x.dim() != 3:
+        raise ValueError("x must be (batch, L, dim)")
+    batch, seqlen, dim = x.shape
+    if A.dim() != 2 or A.shape[0] != dim:
+        raise ValueError("A must be (dim, N)")
+    dstate = A.shape[1]
+    dev, dt = x.device, x.dtype
+    if dt not in _DTYPES:
+        raise ValueError(f"unsupported I/O dtype {dt}")
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU device")
+    _need(x, "x", (batch, seqlen, dim), dt, dev)
+    _need(delta, "delta", (batch, seqlen, dim), dt, dev)
+    _need(A, "A", (dim, dstate), torch.float32, dev)
+    _need(B, "B", (batch, seqlen, dstate), dt, dev)
+    _need(C, "C", (batch, seqlen, dstate), dt, dev)
+    _need(D, "D", (dim,), torch.float32, dev)
+    _need(z, "z", (batch, seqlen, dim), dt, dev)
+    _need(h0, "h0", (batch, dim, dstate), torch.float32, dev)
+    _need(delta_bias, "delta_bias", (dim,), torch.float32, dev)
+    if y is None:
+        raise ValueError("y (the output) is required")
+    _need(y, "y", (batch, seqlen, dim), dt, dev)
+    _need(hL, "hL", (batch, dim, dstate), torch.float32, dev)
+    plan = ScanPlan(chunk_len, state_split, carry, halves, 0)
+    with torch.cuda.device(dev):
+        st = lib.ssm_scan_fwd_noalloc(batch, seqlen, dim, dstate, _DTYPES[dt], _ptr(x),
+                                      _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                                      _ptr(h0), _ptr(y), _ptr(hL),
+                                      _options(delta_bias, delta_softplus), ctypes.byref(plan),
+                                      _stream(dev))
+    _check(st, "ssm_scan_fwd_noalloc")
     return y, hL
 
 

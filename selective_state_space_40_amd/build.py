@@ -19,7 +19,8 @@ BUILD_DIR = os.path.join(HERE, "_build")
 ARCH = "gfx950"
 
 # (object name, source, extra defines)
-UNITS = [("api", "api.cpp", ()), ("launch", "launch.hip", ()), ("conv1d", "conv1d.hip", ()),
+UNITS = [("api", "api.cpp", ()), ("noalloc", "noalloc.hip", ()), ("launch", "launch.hip", ()),
+         ("conv1d", "conv1d.hip", ()),
          ("scan_bwd", "scan_bwd.hip", ()), ("ssd", "ssd.hip", ())] + [
     (f"scan_io{io}_sp{sp}", "scan_variant.hip",
      (f"-DMAMBA_VARIANT_IO={io}", f"-DMAMBA_VARIANT_SP={sp}"))

@@ -1,10 +1,13 @@
 // C ABI of the selective-scan library: argument checks, the chunk plan and
-// error mapping around the HIP kernels of scan_kernels.hip.
+// error mapping around the HIP kernels (scan_variant.hip, launch.hip,
+// scan_bwd.hip, ssd.hip, conv1d.hip).
 //
 // Every check runs on the host before any HIP call, so a rejected call
 // queues nothing and leaves the device untouched. The only HIP calls outside
 // the launches are the device and compute-unit-count queries of the
-// automatic chunk plan.
+// automatic chunk plan; the compute-unit count of each device is queried
+// once and kept for the life of the process (the only state the library
+// holds besides the fixed scratch of ssm_scan_fwd_noalloc, noalloc.hip).
 #include <hip/hip_runtime_api.h>
 
 #include <atomic>
@@ -209,12 +212,19 @@ int ssm_scan_fwd_workspace_size(int64_t batch, int64_t seqlen, int64_t dim, int 
     return MAMBA_OK;
 }
 
-int ssm_scan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int dstate, int dtype,
-                 const void* x, const void* delta, const float* A, const void* B,
-                 const void* C, const float* D, const void* z, const float* h0, void* y,
-                 float* hL, const mamba_scan_options* options,
-                 const mamba_scan_plan* plan_req, void* workspace, size_t workspace_bytes,
-                 hipStream_t stream) {
+}  // extern "C"
+
+namespace mamba {
+
+// ssm_scan_fwd's checks, plan and launch. With `scratch` the workspace is
+// not an argument: once the plan is known and needs one, scratch() is asked
+// for it (after every argument check, so a rejected call makes no HIP call).
+int scan_fwd_call(int64_t batch, int64_t seqlen, int64_t dim, int dstate, int dtype,
+                  const void* x, const void* delta, const float* A, const void* B,
+                  const void* C, const float* D, const void* z, const float* h0, void* y,
+                  float* hL, const mamba_scan_options* options,
+                  const mamba_scan_plan* plan_req, void* workspace, size_t workspace_bytes,
+                  ScratchSource scratch, hipStream_t stream) {
     int st = check_shape(batch, seqlen, dim, dstate, dtype);
     if (st != MAMBA_OK) return st;
     const float* delta_bias = nullptr;
@@ -234,15 +244,20 @@ int ssm_scan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int dstate, int dty
     ScanPlan plan;
     st = make_plan(batch, seqlen, dim, dstate, dtype, plan_req, &plan);
     if (st != MAMBA_OK) return st;
+    if (scratch != nullptr && plan.workspace_bytes > 0) {
+        st = scratch(plan.workspace_bytes, &workspace);
+        if (st != MAMBA_OK) return st;
+        workspace_bytes = plan.workspace_bytes;
+    }
     if (plan.workspace_bytes > 0 && (workspace == nullptr || workspace_bytes < plan.workspace_bytes))
         return MAMBA_ERR_WORKSPACE;
 
-    mamba::ScanArgs a;
+    ScanArgs a;
     a.batch = batch;
     a.seqlen = seqlen;
     a.dim = dim;
     a.dstate = dstate;
-    a.io = dtype == MAMBA_DTYPE_F32 ? mamba::kIoF32 : mamba::kIoBF16;
+    a.io = dtype == MAMBA_DTYPE_F32 ? kIoF32 : kIoBF16;
     a.x = x;
     a.delta = delta;
     a.A = A;
@@ -255,7 +270,22 @@ int ssm_scan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int dstate, int dty
     a.hL = hL;
     a.delta_bias = delta_bias;
     a.delta_softplus = delta_softplus;
-    return mamba::launch_scan(a, plan, workspace, stream) == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP;
+    return launch_scan(a, plan, workspace, stream) == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP;
+}
+
+}  // namespace mamba
+
+extern "C" {
+
+int ssm_scan_fwd(int64_t batch, int64_t seqlen, int64_t dim, int dstate, int dtype,
+                 const void* x, const void* delta, const float* A, const void* B,
+                 const void* C, const float* D, const void* z, const float* h0, void* y,
+                 float* hL, const mamba_scan_options* options,
+                 const mamba_scan_plan* plan_req, void* workspace, size_t workspace_bytes,
+                 hipStream_t stream) {
+    return mamba::scan_fwd_call(batch, seqlen, dim, dstate, dtype, x, delta, A, B, C, D, z, h0,
+                                y, hL, options, plan_req, workspace, workspace_bytes, nullptr,
+                                stream);
 }
 
 int ssm_state_update(int64_t batch, int64_t dim, int dstate, int dtype, float* h,

@@ -1,10 +1,14 @@
-// Internal interface between the C ABI layer (api.cpp) and the HIP kernels
-// (scan_kernels.hip). Not installed; not part of the public ABI.
+// Internal interface between the C ABI layer (api.cpp, noalloc.hip) and the
+// HIP kernels (scan_variant.hip, launch.hip, scan_bwd.hip, ssd.hip,
+// conv1d.hip). Not installed; not part of the public ABI.
 #pragma once
 
 #include <stddef.h>
 #include <stdint.h>
 #include <hip/hip_runtime_api.h>
+
+struct mamba_scan_options;
+struct mamba_scan_plan;
 
 namespace mamba {
 
@@ -180,5 +184,19 @@ hipError_t launch_conv1d(const ConvArgs& a, bool update, hipStream_t stream);
 
 // Queue the single-token update. Arguments are already validated.
 hipError_t launch_state_update(const DecodeArgs& a, hipStream_t stream);
+
+// Where a forward scan without a workspace argument gets its scratch: asked
+// for `bytes` once the plan is known (only when the plan needs scratch), it
+// returns a mamba_status and sets *ws.
+using ScratchSource = int (*)(size_t bytes, void** ws);
+
+// ssm_scan_fwd's argument checks, plan and launch (api.cpp). With `scratch`
+// non-null the workspace comes from it instead of the arguments.
+int scan_fwd_call(int64_t batch, int64_t seqlen, int64_t dim, int dstate, int dtype,
+                  const void* x, const void* delta, const float* A, const void* B,
+                  const void* C, const float* D, const void* z, const float* h0, void* y,
+                  float* hL, const mamba_scan_options* options,
+                  const mamba_scan_plan* plan_req, void* workspace, size_t workspace_bytes,
+                  ScratchSource scratch, hipStream_t stream);
 
 }  // namespace mamba

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol(lib):
     names = _declared_functions()
     assert names == ["causal_conv1d_fwd", "causal_conv1d_update", "mamba_status_string",
                      "ssd_fwd", "ssm_scan_bwd", "ssm_scan_bwd_workspace_size", "ssm_scan_fwd",
-                     "ssm_scan_fwd_workspace_size", "ssm_state_update"]
+                     "ssm_scan_fwd_noalloc", "ssm_scan_fwd_workspace_size", "ssm_state_update"]
     for n in names:
         assert hasattr(lib, n), f"{n} missing from {ms.library_path()}"
 
@@ -118,6 +118,44 @@ def test_scan_workspace_check(lib):
     assert lib.ssm_scan_fwd_workspace_size(1, 1 << 20, 1 << 14, 16, 0, _plan(1 << 20, 1),
                                            ctypes.byref(got), ctypes.byref(need)) == OK
     assert got.chunk_len * (1 << 14) * 4 < (1 << 32)
+
+
+def _scan_noalloc(lib, batch=2, seqlen=8, dim=64, dstate=16, dtype=1, ptrs=None, plan=None,
+                  opts=None):
+    p = dict(x=P, delta=P, A=P, B=P, C=P, D=None, z=None, h0=None, y=P, hL=None)
+    p.update(ptrs or {})
+    return lib.ssm_scan_fwd_noalloc(batch, seqlen, dim, dstate, dtype, p["x"], p["delta"], p["A"],
+                                    p["B"], p["C"], p["D"], p["z"], p["h0"], p["y"], p["hL"], opts,
+                                    plan, None)
+
+
+def test_scan_noalloc_checks(lib):
+    """The no-allocation scan makes ssm_scan_fwd's checks, and rejects a plan
+    whose scratch exceeds its fixed per-GPU array before any HIP call."""
+    limit = ms.NOALLOC_SCRATCH_BYTES
+    header = open(HEADER).read()
+    assert re.search(r"#define MAMBA_NOALLOC_SCRATCH_BYTES \(32u \* 1024u \* 1024u\)", header)
+    assert limit == 32 * 1024 * 1024
+    assert _scan_noalloc(lib, batch=-1) == INVALID
+    assert _scan_noalloc(lib, dstate=17) == UNSUPPORTED
+    assert _scan_noalloc(lib, ptrs={"x": None}) == INVALID
+    assert _scan_noalloc(lib, ptrs={"y": PM}) == MISALIGNED
+    assert _scan_noalloc(lib, opts=_opts(reserved=1)) == INVALID
+    assert _scan_noalloc(lib, batch=0) == OK
+    # 64 chunks over 8 rows x 5120 channels: 3 x 64 x 8 x 5120 x 16 x 4 bytes
+    need = ctypes.c_size_t(0)
+    plan = _plan(64, 4, 1)
+    assert lib.ssm_scan_fwd_workspace_size(8, 4096, 5120, 16, 1, plan, None,
+                                           ctypes.byref(need)) == OK
+    assert need.value == 3 * 64 * 8 * 5120 * 16 * 4 > limit
+    assert _scan_noalloc(lib, batch=8, seqlen=4096, dim=5120, plan=plan) == WORKSPACE
+    # just over the limit with the same row count
+    rows = 8
+    over = (limit // (3 * rows * 16 * 4 * 2)) + 1  # channels: 2 chunks need just over the limit
+    assert lib.ssm_scan_fwd_workspace_size(rows, 128, over, 16, 1, _plan(64, 4, 1), None,
+                                           ctypes.byref(need)) == OK
+    assert need.value > limit
+    assert _scan_noalloc(lib, batch=rows, seqlen=128, dim=over, plan=_plan(64, 4, 1)) == WORKSPACE
 
 
 def test_scan_carry_choice(lib):
