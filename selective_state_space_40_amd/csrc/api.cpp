@@ -325,6 +325,8 @@ int ssm_state_update(int64_t batch, int64_t dim, int dstate, int dtype, float* h
     return mamba::launch_state_update(a, stream) == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP;
 }
 
+}  // extern "C"
+
 namespace {
 
 // Work decomposition of the backward pass. One workgroup of ceil(N/4) waves
@@ -402,6 +404,8 @@ int make_bwd_plan(int64_t batch, int64_t seqlen, int64_t dim, int dstate,
 }
 
 }  // namespace
+
+extern "C" {
 
 int ssm_scan_bwd_workspace_size(int64_t batch, int64_t seqlen, int64_t dim, int dstate,
                                 int dtype, const mamba_scan_plan* plan,
