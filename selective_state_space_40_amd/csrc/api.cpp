@@ -77,11 +77,29 @@ int check_shape(int64_t batch, int64_t seqlen, int64_t dim, int dstate, int dtyp
 // of one batch row over one chunk. The automatic plan splits every channel's
 // states over four waves where the kernels allow it (dstate 4, 8 or 16):
 // that multiplies the waves by four for about a sixth more vector work, far
-// cheaper than cutting the sequence, where every chunk but the last pays a
-// summary pass. Only when the split launch still holds fewer than two waves
-// per SIMD is the sequence cut, into enough chunks for about six waves per
-// SIMD. Chunks are never shorter than kMinChunk tokens. (Measured on MI355X
-// for the Mamba-130M and Mamba-2.8B layer shapes.)
+// cheaper than cutting the sequence, where every chunk but the first and the
+// last pays a summary pass. Only when the split launch still holds fewer
+// than two waves per SIMD is the sequence cut. Chunks are never shorter than
+// kMinChunk tokens. (Measured on MI355X for the Mamba-130M and Mamba-2.8B
+// layer shapes.)
+//
+// How many chunks (rerun carry). Pass 1 (chunk 0's outputs and the
+// summaries of chunks 1 .. n-2) and pass 2 (the outputs of chunks 1 .. n-1)
+// each hold n-1 layers of the G channel groups. Both are bound by vector
+// issue, so a pass takes about as long as its busiest compute unit: m =
+// ceil((n-1) G / CU) workgroups of one chunk each, a summary costing about
+// kSummaryCost of an output pass per token, and every workgroup some
+// kChunkFixedTokens' worth of fixed cost (pipeline fill, prologue). Fewer
+// than six resident workgroups per unit issue less often: measured on the
+// Mamba-130M layer, three ran at 0.83 and four at 0.91 of the rate of six,
+// taken as (m + 12) / 18. The plan takes the n that minimises
+// (chunk_len + kChunkFixedTokens) * (m * kSummaryCost + (1 - kSummaryCost)
+// + m) / rate(m) among those that leave both passes at least
+// kWavesPerSimdChunked waves per SIMD, preferring fewer chunks unless more
+// cost at least 1% less. (Mamba-130M layer, 192 groups on 256 units: 9
+// chunks, six workgroups per unit in either pass, 142 us, against 150 us for
+// 8 chunks, whose pass 1 left a quarter of the units a workgroup short, and
+// 146 us for 5.)
 //
 // Chunks of kRepairMinChunk tokens or more join through the repaired carry:
 // its rerun covers only a chunk's head while the entering state still
@@ -96,9 +114,49 @@ constexpr int64_t kRepairMinChunk = 4096;
 static_assert(mamba::kCarryRerun == MAMBA_CARRY_RERUN && mamba::kCarryRepair == MAMBA_CARRY_REPAIR,
               "internal carry codes follow the public enum");
 constexpr int64_t kWavesPerSimdNoChunk = 2;
-constexpr int64_t kWavesPerSimdChunked = 6;
+constexpr int64_t kWavesPerSimdChunked = 3;
 constexpr int64_t kWavesPerSimdRepaired = 8;
 constexpr int64_t kMinChunk = 64;
+constexpr double kSummaryCost = 0.75;
+constexpr double kChunkFixedTokens = 32.0;
+
+// Chunk length of `n` chunks over seqlen tokens, a whole number of tiles.
+int64_t chunk_len_for(int64_t seqlen, int64_t n) {
+    const int64_t c = (seqlen + n - 1) / n;
+    return (c + mamba::kTokenTile - 1) / mamba::kTokenTile * mamba::kTokenTile;
+}
+
+// The rerun carry's chunk length by the balance rule above. When no count
+// leaves enough waves per SIMD (very few channel groups), the most chunks
+// the minimum length allows: the passes are then bound by latency, which
+// shorter chunks cut.
+int64_t rerun_chunk_len(int64_t seqlen, int64_t groups, int split, int cu) {
+    const int64_t nmax = seqlen / kMinChunk;
+    int64_t best_len = chunk_len_for(seqlen, nmax);
+    double best = -1.0;
+    // counts below n0 leave too few waves per SIMD; the cost repeats its
+    // pattern every CU / gcd(G, CU) counts, so a window of 4 CU counts past
+    // n0 holds the minimum
+    const int64_t need = kWavesPerSimdChunked * 4 * int64_t(cu);
+    const int64_t n0 = 1 + (need + groups * split - 1) / (groups * split);
+    const int64_t n1 = nmax < n0 + 4 * int64_t(cu) ? nmax : n0 + 4 * int64_t(cu);
+    for (int64_t n = n0 > 2 ? n0 : 2; n <= n1; ++n) {
+        const int64_t len = chunk_len_for(seqlen, n);
+        const int64_t chunks = (seqlen + len - 1) / len;
+        if (chunks != n) continue;  // rounding to whole tiles merged two counts
+        const int64_t layers = (n - 1) * groups;
+        if (layers * split < kWavesPerSimdNoChunk * 4 * int64_t(cu)) continue;
+        const double m = static_cast<double>((layers + cu - 1) / cu);
+        const double rate = m >= 6.0 ? 1.0 : (m + 12.0) / 18.0;
+        const double cost = (static_cast<double>(len) + kChunkFixedTokens) *
+                            (m * kSummaryCost + (1.0 - kSummaryCost) + m) / rate;
+        if (best < 0.0 || cost < 0.99 * best) {
+            best = cost;
+            best_len = len;
+        }
+    }
+    return best_len;
+}
 
 int make_plan(int64_t batch, int64_t seqlen, int64_t dim, int dstate, int dtype,
               const mamba_scan_plan* req, ScanPlan* plan) {
@@ -137,26 +195,27 @@ int make_plan(int64_t batch, int64_t seqlen, int64_t dim, int dstate, int dtype,
         if (len == 0) {
             const int64_t waves = groups * split;
             const int64_t nmax = seqlen / kMinChunk;
-            auto chunk_for = [&](int64_t per_simd) {
-                int64_t n = 1;
-                if (waves < kWavesPerSimdNoChunk * simds) n = (per_simd * simds + waves - 1) / waves;
-                if (n > nmax) n = nmax;
-                if (n < 1) n = 1;
-                const int64_t c = (seqlen + n - 1) / n;
-                return (c + mamba::kTokenTile - 1) / mamba::kTokenTile * mamba::kTokenTile;
-            };
-            len = chunk_for(kWavesPerSimdChunked);
-            // chunks that will join through the repaired carry: more of them
-            if (len < seqlen && carry != MAMBA_CARRY_RERUN) {
-                const int64_t shorter = chunk_for(kWavesPerSimdRepaired);
-                if (shorter >= kRepairMinChunk) len = shorter;
+            len = seqlen;
+            if (waves < kWavesPerSimdNoChunk * simds && nmax >= 2) {
+                len = rerun_chunk_len(seqlen, groups, split, cu);
+                // chunks that will join through the repaired carry: about
+                // eight waves per SIMD, when that keeps them long
+                if (carry != MAMBA_CARRY_RERUN) {
+                    int64_t n = (kWavesPerSimdRepaired * simds + waves - 1) / waves;
+                    if (n > nmax) n = nmax;
+                    const int64_t longer = chunk_len_for(seqlen, n < 1 ? 1 : n);
+                    if (longer >= kRepairMinChunk && longer < seqlen) len = longer;
+                }
             }
         }
     }
     if (len > seqlen) len = seqlen;
-    // a chunk's x/delta/z/y rows are addressed with 32-bit byte offsets
+    // a chunk's x/delta/z/y rows (dim per token) and B/C rows (dstate per
+    // token) are addressed with 32-bit byte offsets: its extent over the
+    // wider of the two stays below 2^32 bytes
     const int64_t esz = dtype == MAMBA_DTYPE_F32 ? 4 : 2;
-    const int64_t max_len = ((int64_t(1) << 32) - 1) / (dim * esz);
+    const int64_t row = dim > dstate ? dim : dstate;
+    const int64_t max_len = ((int64_t(1) << 32) - 1) / (row * esz);
     if (max_len < 1) return MAMBA_ERR_UNSUPPORTED;
     if (len > max_len) len = max_len;
     const int64_t nchunks = (seqlen + len - 1) / len;

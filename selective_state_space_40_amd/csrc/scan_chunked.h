@@ -174,7 +174,9 @@ __device__ __forceinline__ void fetch_bc(const BcIo& bc, int tile, int cnt,
     for (int q = 0; q < BcStage<N, S>::kPerLane; ++q) {
         // values past the tile's last token are clamped onto it (in bounds, unused)
         const int idx = min(BcStage<N, S>::slot(q, tid), cnt * N - 1);
-        const uint32_t off = static_cast<uint32_t>((tile * TT * N + idx) * esz);
+        // below 2^32 by the plan, which may exceed a signed int: unsigned math
+        const uint32_t off = (static_cast<uint32_t>(tile) * (TT * N) + static_cast<uint32_t>(idx)) *
+                             static_cast<uint32_t>(esz);
         braw[q] = buf_load<IO>(bc.B, off, 0);
         craw[q] = buf_load<IO>(bc.C, off, 0);
     }
@@ -290,7 +292,8 @@ __device__ __forceinline__ void stage_tokens(float2* dtdu, int w, const Tile<S>&
 // its inputs straight from its registers (delta already activated in dtv)
 // and finishes and stores each token right away. With SUM (always without
 // OUTPUT) the sum of delta accumulates in dsum.
-template <int N, int S, int IO, bool OUTPUT, bool SUM, bool HAS_D, bool HAS_Z, bool FULL>
+template <int N, int S, int IO, bool OUTPUT, bool SUM, bool HAS_D, bool HAS_Z, bool FULL,
+          bool PIPE>
 __device__ __forceinline__ void compute_tile(const ChunkIo& io, const float* bcs_w,
                                              const float2* dtdu, const Tile<S>& r,
                                              const float (&dtv)[TT / S], int tile, int cnt, const float (&A2)[Split<N, S>::NPW],
@@ -366,15 +369,29 @@ __device__ __forceinline__ void compute_tile(const ChunkIo& io, const float* bcs
             }
         }
     };
+    if constexpr (PIPE && G > 1 && NG > 1) {
+        // software-pipelined: the next group's LDS reads go out before this
+        // group's arithmetic, so its latency hides behind that arithmetic
+        // (a second group of registers; kernels with registers to spare)
+        Group q[2];
+        read_group(0, q[0]);
 #pragma unroll
-    for (int g = 0; g < NG; ++g) {
-        Group q;
-        read_group(g * G, q);
-        // keeps the group's reads ahead of its arithmetic: left alone, the
-        // scheduler issues each token's reads just before their use and
-        // every token then waits out the LDS latency
-        if constexpr (G > 1) __builtin_amdgcn_sched_barrier(0);
-        compute_group(g * G, q);
+        for (int g = 0; g < NG; ++g) {
+            if (g + 1 < NG) read_group((g + 1) * G, q[(g + 1) & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+            compute_group(g * G, q[g & 1]);
+        }
+    } else {
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+            Group q;
+            read_group(g * G, q);
+            // keeps the group's reads ahead of its arithmetic: left alone, the
+            // scheduler issues each token's reads just before their use and
+            // every token then waits out the LDS latency
+            if constexpr (G > 1) __builtin_amdgcn_sched_barrier(0);
+            compute_group(g * G, q);
+        }
     }
 }
 
@@ -407,13 +424,23 @@ __device__ __forceinline__ void finalize_tile(const ChunkIo& io, const float* re
 // LDS of one workgroup: B/C tiles, per-token inputs and partial readouts,
 // each double-buffered by tile parity. A pass without outputs (OUT false:
 // the chunk summaries) has no readouts, and the smaller footprint lets more
-// of its workgroups share a compute unit.
-template <int N, int S, bool OUT = true>
-struct ScanLds {
+// of its workgroups share a compute unit; only the repaired carry's second
+// pass (VOTE) needs the vote flags. LDS is allocated to a workgroup in whole
+// kilobytes here: the output pass of split 4 and 16 states takes exactly 26
+// KB, so six of its workgroups share a compute unit's 160 KB (a few bytes
+// more and only five do).
+template <bool VOTE, int S>
+struct VoteLds {
+    int vote[2][S];  // wave w's lanes are all done
+};
+template <int S>
+struct VoteLds<false, S> {};
+
+template <int N, int S, bool OUT = true, bool VOTE = false>
+struct ScanLds : VoteLds<VOTE, S> {
     float bcs[2][2 * BcStage<N, S>::kSlots];
     float2 dtdu[2][S > 1 ? TT * kWave : 1];
     float red[2][OUT && S > 1 ? S * TT * kWave : 1];
-    int vote[2][S];  // pass 2 of the repaired carry: wave w's lanes are all done
 };
 
 // What one run over a chunk computes.
@@ -427,6 +454,26 @@ enum Pass : int {
 // Pass 2 of the repaired carry stops once exp2(A2 * sum of delta) is at most
 // 2^-kFixupLog2 for every state of the workgroup.
 constexpr float kFixupLog2 = 32.0f;
+
+// Which kernels read a tile's LDS inputs one token group ahead of the
+// arithmetic (compute_tile): those whose occupancy the extra registers do
+// not lower.
+#ifndef MAMBA_PIPE_SUMMARY
+#define MAMBA_PIPE_SUMMARY 1
+#endif
+#ifndef MAMBA_PIPE_OUTPUT
+#define MAMBA_PIPE_OUTPUT 0
+#endif
+#ifndef MAMBA_PIPE_MIXED
+#define MAMBA_PIPE_MIXED 1
+#endif
+#ifndef MAMBA_PIPE_LOCAL
+#define MAMBA_PIPE_LOCAL 0
+#endif
+constexpr bool kPipeSummary = MAMBA_PIPE_SUMMARY;
+constexpr bool kPipeOutput = MAMBA_PIPE_OUTPUT;
+constexpr bool kPipeMixed = MAMBA_PIPE_MIXED;
+constexpr bool kPipeLocal = MAMBA_PIPE_LOCAL;
 
 // All `ntok` tokens of one chunk for one wave. Two register tiles alternate
 // and swap roles without register copies. With S > 1 a tile's raw inputs
@@ -453,10 +500,10 @@ constexpr float kFixupLog2 = 32.0f;
 // and the whole workgroup leaves together once they agree; the loads still
 // in flight are dropped. Without kPassFixup the steps return false at
 // compile time and the loop is as before.
-template <int N, int S, int IO, bool SP, int PASS, bool HAS_D, bool HAS_Z>
+template <int N, int S, int IO, bool SP, int PASS, bool HAS_D, bool HAS_Z, bool PIPE = false>
 __device__ __forceinline__ void scan_chunk(const ChunkIo& io, const BcIo& bcio, float dbias,
                                            int ntok, int w, int n0,
-                                           ScanLds<N, S, PASS != kPassSummary>& lds,
+                                           ScanLds<N, S, PASS != kPassSummary, PASS == kPassFixup>& lds,
                                            const float (&A2)[Split<N, S>::NPW],
                                            float (&h)[Split<N, S>::NPW], float dskip,
                                            float a2max, float& dsum) {
@@ -490,7 +537,7 @@ __device__ __forceinline__ void scan_chunk(const ChunkIo& io, const BcIo& bcio, 
         const int cnt = FULL ? TT : ntok - i * TT;
         float part[TT], dtv[TT / S];
         if constexpr (S == 1) delta_tile<S, IO, SP>(cur, dbias, dtv);
-        compute_tile<N, S, IO, OUTPUT, SUM, HAS_D, HAS_Z, FULL>(io, lds.bcs[i & 1] + n0,
+        compute_tile<N, S, IO, OUTPUT, SUM, HAS_D, HAS_Z, FULL, PIPE>(io, lds.bcs[i & 1] + n0,
                                                                 lds.dtdu[i & 1], cur, dtv, i, cnt,
                                                                 A2, h, dskip, part, dsum);
         if constexpr (OUTPUT && S > 1) {
@@ -564,6 +611,7 @@ struct ChunkGrid {
     int64_t nchunks;          // chunks per sequence the grid covers
     int64_t chunk_len;        // tokens per chunk
     int64_t first_chunk = 0;  // sequence chunk of the grid's chunk 0
+    int64_t seq_chunks = 1;   // chunks of the whole sequence (the last one writes hL)
     int fold = 0;             // output pass: fold the chunk summaries itself (no carry pass)
 };
 
@@ -634,27 +682,23 @@ __device__ __forceinline__ WaveSlot wave_slot(const ScanArgs& a, const ChunkGrid
     return s;
 }
 
-// Pass 1: per-chunk summaries (end state, decay product), all chunks but the
-// last. Chunk 0 starts from h0, so its end state is already exact.
+// The summary of one chunk from a zero entering state: its end state and its
+// decay product exp(A * sum of delta), the pair the carry folds.
 template <int N, int S, int IO, bool SP>
-__global__ __launch_bounds__(kWave * S) __attribute__((amdgpu_waves_per_eu(S == 1 ? 4 : 6)))
-void chunk_summary_kernel(ScanArgs a, ChunkGrid g, Carry c) {
+__device__ __forceinline__ void summary_group(const ScanArgs& a, const ChunkGrid& g,
+                                              const Carry& c, int64_t blk,
+                                              ScanLds<N, S, false>& lds) {
     constexpr int NPW = Split<N, S>::NPW;
-    const WaveSlot s = wave_slot<N, S, IO>(a, g, blockIdx.x);
+    const WaveSlot s = wave_slot<N, S, IO>(a, g, blk);
     float A2[NPW], h[NPW];
     const int64_t srow = ((s.k * a.batch + s.b) * a.dim + s.d) * N + s.n0;
 #pragma unroll
     for (int q = 0; q < NPW; ++q) {
         A2[q] = a.A[s.d * N + s.n0 + q] * kLog2e;
-        h[q] = (s.k == 0 && a.h0 != nullptr) ? a.h0[(s.b * a.dim + s.d) * N + s.n0 + q] : 0.0f;
+        h[q] = 0.0f;
     }
-    if (s.k == 0) {
-#pragma unroll
-        for (int q = 0; q < NPW; ++q) c.start[srow + q] = h[q];
-    }
-    __shared__ ScanLds<N, S, false> lds;
     float dsum = 0.0f;
-    scan_chunk<N, S, IO, SP, kPassSummary, false, false>(s.io, s.bc, s.dbias, s.ntok, s.w, s.n0,
+    scan_chunk<N, S, IO, SP, kPassSummary, false, false, kPipeSummary>(s.io, s.bc, s.dbias, s.ntok, s.w, s.n0,
                                                          lds, A2, h, 0.0f, 0.0f, dsum);
 #pragma unroll
     for (int q = 0; q < NPW; ++q) {
@@ -702,7 +746,8 @@ __global__ __launch_bounds__(256) void chunk_carry_kernel(int64_t columns, int64
 
 // Pass 2 (or the only pass when nchunks == 1): scan each chunk from its true
 // entering state and write y; the last chunk writes hL.
-template <int N, int S, int IO, bool SP, bool HAS_D, bool HAS_Z>
+template <int N, int S, int IO, bool SP, bool HAS_D, bool HAS_Z, bool PIPE,
+          bool STORE_END = false>
 __device__ __forceinline__ void output_group(const ScanArgs& a, const ChunkGrid& g,
                                              const Carry& c, int64_t blk, ScanLds<N, S>& lds) {
     constexpr int NPW = Split<N, S>::NPW;
@@ -710,7 +755,7 @@ __device__ __forceinline__ void output_group(const ScanArgs& a, const ChunkGrid&
     float A2[NPW], h[NPW];
 #pragma unroll
     for (int q = 0; q < NPW; ++q) A2[q] = a.A[s.d * N + s.n0 + q] * kLog2e;
-    if (g.nchunks == 1 || (g.fold && s.k == 0)) {
+    if (s.k == 0) {
 #pragma unroll
         for (int q = 0; q < NPW; ++q)
             h[q] = a.h0 != nullptr ? a.h0[(s.b * a.dim + s.d) * N + s.n0 + q] : 0.0f;
@@ -751,9 +796,15 @@ __device__ __forceinline__ void output_group(const ScanArgs& a, const ChunkGrid&
     }
     const float dskip = HAS_D ? a.D[s.d] : 0.0f;
     float dsum = 0.0f;
-    scan_chunk<N, S, IO, SP, kPassOutput, HAS_D, HAS_Z>(s.io, s.bc, s.dbias, s.ntok, s.w, s.n0,
+    scan_chunk<N, S, IO, SP, kPassOutput, HAS_D, HAS_Z, PIPE>(s.io, s.bc, s.dbias, s.ntok, s.w, s.n0,
                                                         lds, A2, h, dskip, 0.0f, dsum);
-    if (s.k == g.nchunks - 1 && a.hL != nullptr) {
+    if constexpr (STORE_END) {
+        // chunk 0 of a cut sequence: its end state, exact since it started
+        // from h0, is the state entering chunk 1 and where the fold starts
+        const int64_t srow = ((s.k * a.batch + s.b) * a.dim + s.d) * N + s.n0;
+#pragma unroll
+        for (int q = 0; q < NPW; ++q) c.end[srow + q] = h[q];
+    } else if (s.k == g.seq_chunks - 1 && a.hL != nullptr) {
 #pragma unroll
         for (int q = 0; q < NPW; ++q) a.hL[(s.b * a.dim + s.d) * N + s.n0 + q] = h[q];
     }
@@ -763,7 +814,29 @@ template <int N, int S, int IO, bool SP, bool HAS_D, bool HAS_Z>
 __global__ __launch_bounds__(kWave * S) __attribute__((amdgpu_waves_per_eu(S <= 2 ? 2 : 4)))
 void chunk_output_kernel(ScanArgs a, ChunkGrid g, Carry c) {
     __shared__ ScanLds<N, S> lds;
-    output_group<N, S, IO, SP, HAS_D, HAS_Z>(a, g, c, blockIdx.x, lds);
+    output_group<N, S, IO, SP, HAS_D, HAS_Z, kPipeOutput>(a, g, c, blockIdx.x, lds);
+}
+
+// Rerun carry, pass 1, over chunks 0 .. nchunks-2. Chunk 0 starts from h0,
+// so it runs the output pass straight away: its y is final and its end state
+// is the exact state entering chunk 1. The other chunks store their summary
+// pairs. Pass 2 then covers chunks 1 .. nchunks-1 only, so each launch holds
+// nchunks-1 layers of channel groups; the plan picks the chunk count that
+// spreads those workgroups evenly over the compute units.
+template <int N, int S, int IO, bool SP, bool HAS_D, bool HAS_Z>
+__global__ __launch_bounds__(kWave * S) __attribute__((amdgpu_waves_per_eu(S <= 2 ? 2 : 4)))
+void chunk_head_kernel(ScanArgs a, ChunkGrid g, Carry c) {
+    __shared__ union {
+        ScanLds<N, S> out;
+        ScanLds<N, S, false> sum;
+    } lds;
+    const int64_t blk = blockIdx.x;
+    int64_t dblk, k, b;
+    decode_block(g, blk, dblk, k, b);
+    if (k + g.first_chunk == 0)
+        output_group<N, S, IO, SP, HAS_D, HAS_Z, kPipeOutput, true>(a, g, c, blk, lds.out);
+    else
+        summary_group<N, S, IO, SP>(a, g, c, blk, lds.sum);
 }
 
 // ---------------------------------------------------------------------------
@@ -883,17 +956,20 @@ __device__ __forceinline__ void half_group(const ScanArgs& a, int64_t b, int64_t
         const float2* dtdu = lds.dtdu[i & 1];
         float* red = lds.red[i & 1] + v * TT * kHalf + ch;
         // tokens in pairs: both tokens' LDS inputs before their arithmetic
-#pragma unroll
-        for (int j0 = 0; j0 < TT; j0 += 2) {
+        // (with kPipeMixed the next pair's inputs before this pair's)
+        struct Pair {
             float2 du[2];
             float Bq[2][NPS], Cq[2][NPS];
+        };
+        auto read_pair = [&](int j0, Pair& pr) {
 #pragma unroll
             for (int jj = 0; jj < 2; ++jj) {
-                du[jj] = dtdu[(j0 + jj) * kHalf + ch];
-                read_slice<NPS>(bcs + (j0 + jj) * N + n0, Bq[jj]);
-                read_slice<NPS>(bcs + P + (j0 + jj) * N + n0, Cq[jj]);
+                pr.du[jj] = dtdu[(j0 + jj) * kHalf + ch];
+                read_slice<NPS>(bcs + (j0 + jj) * N + n0, pr.Bq[jj]);
+                read_slice<NPS>(bcs + P + (j0 + jj) * N + n0, pr.Cq[jj]);
             }
-            __builtin_amdgcn_sched_barrier(0);
+        };
+        auto compute_pair = [&](int j0, const Pair& pr) {
 #pragma unroll
             for (int jj = 0; jj < 2; ++jj) {
                 const int j = j0 + jj;
@@ -901,12 +977,30 @@ __device__ __forceinline__ void half_group(const ScanArgs& a, int64_t b, int64_t
                     float p = 0.0f;
 #pragma unroll
                     for (int q = 0; q < NPS; ++q) {
-                        const float e = fast_exp2(du[jj].x * A2[q]);
-                        h[q] = fmaf(e, h[q], du[jj].y * Bq[jj][q]);
-                        p = fmaf(Cq[jj][q], h[q], p);
+                        const float e = fast_exp2(pr.du[jj].x * A2[q]);
+                        h[q] = fmaf(e, h[q], pr.du[jj].y * pr.Bq[jj][q]);
+                        p = fmaf(pr.Cq[jj][q], h[q], p);
                     }
                     red[j * kHalf] = p;
                 }
+            }
+        };
+        if constexpr (kPipeMixed) {
+            Pair pr[2];
+            read_pair(0, pr[0]);
+#pragma unroll
+            for (int j0 = 0; j0 < TT; j0 += 2) {
+                if (j0 + 2 < TT) read_pair(j0 + 2, pr[((j0 >> 1) + 1) & 1]);
+                __builtin_amdgcn_sched_barrier(0);
+                compute_pair(j0, pr[(j0 >> 1) & 1]);
+            }
+        } else {
+#pragma unroll
+            for (int j0 = 0; j0 < TT; j0 += 2) {
+                Pair pr;
+                read_pair(j0, pr);
+                __builtin_amdgcn_sched_barrier(0);
+                compute_pair(j0, pr);
             }
         }
         stage_bc<N, 4, IO>(lds.bcs[(i + 1) & 1], bs, cs);
@@ -981,7 +1075,7 @@ void chunk_mixed_kernel(ScanArgs a, ChunkGrid g, int64_t nwhole) {
     } lds;
     const int64_t blk = blockIdx.x;
     if (blk < nwhole) {
-        output_group<N, 4, IO, SP, HAS_D, HAS_Z>(a, g, Carry{nullptr, nullptr, nullptr}, blk,
+        output_group<N, 4, IO, SP, HAS_D, HAS_Z, kPipeMixed>(a, g, Carry{nullptr, nullptr, nullptr}, blk,
                                                  lds.whole);
     } else {
         int64_t pair;
@@ -1014,7 +1108,7 @@ void chunk_local_kernel(ScanArgs a, ChunkGrid g, Carry c) {
     }
     const float dskip = HAS_D ? a.D[s.d] : 0.0f;
     float dsum = 0.0f;
-    scan_chunk<N, S, IO, SP, kPassLocal, HAS_D, HAS_Z>(s.io, s.bc, s.dbias, s.ntok, s.w, s.n0,
+    scan_chunk<N, S, IO, SP, kPassLocal, HAS_D, HAS_Z, kPipeLocal>(s.io, s.bc, s.dbias, s.ntok, s.w, s.n0,
                                                        lds, A2, h, dskip, 0.0f, dsum);
 #pragma unroll
     for (int q = 0; q < NPW; ++q) {
@@ -1030,7 +1124,7 @@ template <int N, int S, int IO, bool SP, bool HAS_D, bool HAS_Z>
 __global__ __launch_bounds__(kWave * S) __attribute__((amdgpu_waves_per_eu(S <= 2 ? 2 : 4)))
 void chunk_fixup_kernel(ScanArgs a, ChunkGrid g, Carry c) {
     constexpr int NPW = Split<N, S>::NPW;
-    __shared__ ScanLds<N, S> lds;
+    __shared__ ScanLds<N, S, true, true> lds;
     const WaveSlot s = wave_slot<N, S, IO>(a, g, blockIdx.x);
     float A2[NPW], h[NPW];
     const int64_t srow = ((s.k * a.batch + s.b) * a.dim + s.d) * N + s.n0;
@@ -1070,11 +1164,37 @@ hipError_t launch_repaired(const ScanArgs& a, const ChunkGrid& g, const Carry& c
     return hipGetLastError();
 }
 
+// Rerun carry: pass 1 (chunk 0's outputs and the summaries of chunks 1 ..
+// n-2), the carry fold (inside pass 2 for up to kFoldMaxChunks chunks, else
+// its own launch), pass 2 (the outputs of chunks 1 .. n-1). Both passes
+// describe n-1 chunks; the workspace rows keep the full n stride through
+// `columns`.
+template <int N, int S, int IO, bool SP, bool HAS_D, bool HAS_Z>
+hipError_t launch_rerun(const ScanArgs& a, const ChunkGrid& g, const Carry& c, int64_t columns,
+                        hipStream_t s) {
+    const dim3 block(kWave * S);
+    ChunkGrid g1 = g;
+    g1.nchunks = g.seq_chunks - 1;
+    const dim3 grid(g.nblk_d * g1.nchunks * a.batch);
+    hipLaunchKernelGGL((chunk_head_kernel<N, S, IO, SP, HAS_D, HAS_Z>), grid, block, 0, s, a, g1, c);
+    ChunkGrid g2 = g1;
+    g2.first_chunk = 1;
+    if (g.seq_chunks <= kFoldMaxChunks) {
+        g2.fold = 1;
+    } else {
+        hipLaunchKernelGGL(chunk_carry_kernel, dim3(stride_blocks(columns)), dim3(256), 0, s,
+                           columns, g.seq_chunks, c, nullptr);
+    }
+    hipLaunchKernelGGL((chunk_output_kernel<N, S, IO, SP, HAS_D, HAS_Z>), grid, block, 0, s, a, g2, c);
+    return hipGetLastError();
+}
+
 template <int N, int S, int IO, bool SP>
 hipError_t launch_scan_ns(const ScanArgs& a, const ScanPlan& plan, void* ws, hipStream_t s) {
     ChunkGrid g;
     g.nblk_d = (a.dim + kWave - 1) / kWave;
     g.nchunks = plan.nchunks;
+    g.seq_chunks = plan.nchunks;
     g.chunk_len = plan.chunk_len;
     Carry c{nullptr, nullptr, nullptr};
     const int64_t columns = a.batch * a.dim * N;
@@ -1107,23 +1227,12 @@ hipError_t launch_scan_ns(const ScanArgs& a, const ScanPlan& plan, void* ws, hip
         return launch_repaired<N, S, IO, SP, false, false>(a, g, c, columns, s);
     }
     if (plan.nchunks > 1) {
-        // Pass 1 covers chunks 0 .. nchunks-2: its grid describes nchunks-1
-        // chunks of the same length, so block indices map onto exactly those;
-        // the workspace rows keep the full nchunks stride through `columns`.
-        ChunkGrid g1 = g;
-        g1.nchunks = plan.nchunks - 1;
-        const int64_t blocks1 = g.nblk_d * g1.nchunks * a.batch;
-        hipLaunchKernelGGL((chunk_summary_kernel<N, S, IO, SP>), dim3(blocks1), dim3(kWave * S), 0, s,
-                           a, g1, c);
-        if (plan.nchunks <= kFoldMaxChunks) {
-            g.fold = 1;
-        } else {
-            hipLaunchKernelGGL(chunk_carry_kernel, dim3(stride_blocks(columns)), dim3(256), 0, s,
-                               columns, plan.nchunks, c, nullptr);
-        }
+        if (has_d && has_z) return launch_rerun<N, S, IO, SP, true, true>(a, g, c, columns, s);
+        if (has_d) return launch_rerun<N, S, IO, SP, true, false>(a, g, c, columns, s);
+        if (has_z) return launch_rerun<N, S, IO, SP, false, true>(a, g, c, columns, s);
+        return launch_rerun<N, S, IO, SP, false, false>(a, g, c, columns, s);
     }
-    const int64_t blocks = g.nblk_d * plan.nchunks * a.batch;
-    const dim3 grid(blocks), block(kWave * S);
+    const dim3 grid(g.nblk_d * a.batch), block(kWave * S);
     if (has_d && has_z)
         hipLaunchKernelGGL((chunk_output_kernel<N, S, IO, SP, true, true>), grid, block, 0, s, a, g, c);
     else if (has_d)

@@ -118,6 +118,17 @@ def test_scan_workspace_check(lib):
     assert lib.ssm_scan_fwd_workspace_size(1, 1 << 20, 1 << 14, 16, 0, _plan(1 << 20, 1),
                                            ctypes.byref(got), ctypes.byref(need)) == OK
     assert got.chunk_len * (1 << 14) * 4 < (1 << 32)
+    # the same holds for the B/C rows when dstate is wider than dim: a forced
+    # chunk of the whole sequence is shortened so chunk_len * dstate * esz
+    # stays below 2^32 too (fp32 and bf16)
+    for dtype, esz in ((0, 4), (1, 2)):
+        for dim in (1, 3, 15):
+            seqlen = (1 << 32) // (16 * esz) + 1000
+            assert lib.ssm_scan_fwd_workspace_size(1, seqlen, dim, 16, dtype, _plan(seqlen, 1),
+                                                   ctypes.byref(got), ctypes.byref(need)) == OK
+            assert got.chunk_len * 16 * esz < (1 << 32), (dtype, dim, got.chunk_len)
+            assert got.chunk_len * dim * esz < (1 << 32)
+            assert need.value > 0  # now cut into chunks
 
 
 def _scan_noalloc(lib, batch=2, seqlen=8, dim=64, dstate=16, dtype=1, ptrs=None, plan=None,
