@@ -1216,8 +1216,9 @@ BwdLayout bwd_layout(int64_t batch, int64_t seqlen, int64_t dim, int dstate, int
     l.chunk_len = chunk_len > 0 ? chunk_len : l.ntiles * kBT;
     l.nchunks = chunk_len > 0 ? (seqlen + chunk_len - 1) / chunk_len : 1;
     // slots for the second halves of split groups whenever the shape allows
-    // splitting, so the size needs no knowledge of the device
-    l.nslots = bwd_halvable(dstate) ? 2 * l.ngroups : l.ngroups;
+    // splitting, so the size needs no knowledge of the device; a chunked
+    // plan never splits groups (halves need the whole sequence)
+    l.nslots = bwd_halvable(dstate) && l.nchunks == 1 ? 2 * l.ngroups : l.ngroups;
     const size_t states = static_cast<size_t>(batch) * dim * dstate;
     size_t off = 0;
     l.tent = off;

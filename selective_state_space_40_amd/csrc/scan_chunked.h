@@ -164,7 +164,7 @@ struct BcIo {
     __amdgpu_buffer_rsrc_t B, C;  // base: B[b, t0, 0] / C[b, t0, 0], extent: the chunk's rows
 };
 
-template <int N, int S, int IO>
+template <int N, int S, int IO, bool WANT_C = true>
 __device__ __forceinline__ void fetch_bc(const BcIo& bc, int tile, int cnt,
                                          uint32_t (&braw)[BcStage<N, S>::kPerLane],
                                          uint32_t (&craw)[BcStage<N, S>::kPerLane]) {
@@ -178,13 +178,13 @@ __device__ __forceinline__ void fetch_bc(const BcIo& bc, int tile, int cnt,
         const uint32_t off = (static_cast<uint32_t>(tile) * (TT * N) + static_cast<uint32_t>(idx)) *
                              static_cast<uint32_t>(esz);
         braw[q] = buf_load<IO>(bc.B, off, 0);
-        craw[q] = buf_load<IO>(bc.C, off, 0);
+        craw[q] = WANT_C ? buf_load<IO>(bc.C, off, 0) : 0u;
     }
 }
 
 // LDS layout of one staged tile: [tensor B, C][token j][state n], fp32,
 // each tensor padded to kSlots floats.
-template <int N, int S, int IO>
+template <int N, int S, int IO, bool WANT_C = true>
 __device__ __forceinline__ void stage_bc(float* bcs, const uint32_t (&braw)[BcStage<N, S>::kPerLane],
                                          const uint32_t (&craw)[BcStage<N, S>::kPerLane]) {
     constexpr int P = BcStage<N, S>::kSlots;
@@ -194,7 +194,7 @@ __device__ __forceinline__ void stage_bc(float* bcs, const uint32_t (&braw)[BcSt
         // a wrapped-around lane writes the value its twin writes
         const int idx = BcStage<N, S>::slot(q, tid);
         bcs[idx] = raw_to_f32<IO>(braw[q]);
-        bcs[P + idx] = raw_to_f32<IO>(craw[q]);
+        if constexpr (WANT_C) bcs[P + idx] = raw_to_f32<IO>(craw[q]);
     }
 }
 
@@ -270,9 +270,14 @@ struct Epilogue {
 // LDS layout of the staged per-token inputs: [token j][lane] float2 (delta,
 // delta*x). Writes the wave's own tokens and keeps their skip terms and
 // gates for its epilogue.
-template <int S, int IO, bool SP, bool HAS_D, bool HAS_Z>
+//
+// With STAGED_SUM the wave also adds the deltas of the tile's tokens it
+// stages (j < cnt: the tile's valid tokens) to its partial sum `dsum`; the S
+// partials are added in wave order at the chunk's end (scan_chunk).
+template <int S, int IO, bool SP, bool HAS_D, bool HAS_Z, bool STAGED_SUM = false>
 __device__ __forceinline__ void stage_tokens(float2* dtdu, int w, const Tile<S>& r, float dbias,
-                                             float dskip, Epilogue<S>& e) {
+                                             float dskip, Epilogue<S>& e, int cnt = 0,
+                                             float* dsum = nullptr) {
     const int lane = threadIdx.x & (kWave - 1);
     float dt[TT / S];
     delta_tile<S, IO, SP>(r, dbias, dt);
@@ -282,6 +287,9 @@ __device__ __forceinline__ void stage_tokens(float2* dtdu, int w, const Tile<S>&
         dtdu[(jj * S + w) * kWave + lane] = make_float2(dt[jj], dt[jj] * u);
         e.skip[jj] = HAS_D ? dskip * u : 0.0f;
         e.gate[jj] = HAS_Z ? silu(raw_to_f32<IO>(r.z[jj])) : 1.0f;
+        if constexpr (STAGED_SUM) {
+            if (jj * S + w < cnt) *dsum += dt[jj];
+        }
     }
 }
 
@@ -364,7 +372,7 @@ __device__ __forceinline__ void compute_tile(const ChunkIo& io, const float* bcs
                         const float e = fast_exp2(dt * A2[k]);
                         h[k] = fmaf(e, h[k], du * q.B[jj][k]);
                     }
-                    dsum += dt;
+                    if constexpr (SUM) dsum += dt;
                 }
             }
         }
@@ -440,7 +448,9 @@ template <int N, int S, bool OUT = true, bool VOTE = false>
 struct ScanLds : VoteLds<VOTE, S> {
     float bcs[2][2 * BcStage<N, S>::kSlots];
     float2 dtdu[2][S > 1 ? TT * kWave : 1];
-    float red[2][OUT && S > 1 ? S * TT * kWave : 1];
+    // readout partials; the summary pass keeps only the S wave partials of
+    // the delta sum here (at its end)
+    float red[2][S > 1 ? (OUT ? S * TT : S) * kWave : 1];
 };
 
 // What one run over a chunk computes.
@@ -475,6 +485,31 @@ constexpr bool kPipeOutput = MAMBA_PIPE_OUTPUT;
 constexpr bool kPipeMixed = MAMBA_PIPE_MIXED;
 constexpr bool kPipeLocal = MAMBA_PIPE_LOCAL;
 
+// Issue priority by progress. A SIMD's scheduler prefers the oldest of its
+// ready waves, so the waves sharing it finish one after the other and the
+// last ones run alone, issuing far less often than a full SIMD would. A wave
+// of the chunked passes lowers its own priority (s_setprio) as it passes a
+// quarter, half and three quarters of its tiles, so the waves behind are
+// preferred and the SIMD's waves finish together (Mamba-130M layer, 9
+// chunks: 143 -> 134 us; million-token scan 8.1 -> 7.7 ms). The single-chunk
+// mixed launch keeps the default order: its whole and half waves, balanced
+// per SIMD by the plan, gained nothing from it.
+template <bool ON>
+struct ProgressPrio {
+    int b1, b2, b3;  // tile indices (even) where the priority drops
+    __device__ explicit ProgressPrio(int nfull)
+        : b1((nfull / 4) & ~1), b2((nfull / 2) & ~1), b3((3 * nfull / 4) & ~1) {
+        if constexpr (ON) __builtin_amdgcn_s_setprio(3);
+    }
+    __device__ void at(int i) const {
+        if constexpr (ON) {
+            if (i == b1) __builtin_amdgcn_s_setprio(2);
+            else if (i == b2) __builtin_amdgcn_s_setprio(1);
+            else if (i == b3) __builtin_amdgcn_s_setprio(0);
+        }
+    }
+};
+
 // All `ntok` tokens of one chunk for one wave. Two register tiles alternate
 // and swap roles without register copies. With S > 1 a tile's raw inputs
 // (this wave's x, delta, z and its share of the raw B/C run) are fetched two
@@ -500,7 +535,8 @@ constexpr bool kPipeLocal = MAMBA_PIPE_LOCAL;
 // and the whole workgroup leaves together once they agree; the loads still
 // in flight are dropped. Without kPassFixup the steps return false at
 // compile time and the loop is as before.
-template <int N, int S, int IO, bool SP, int PASS, bool HAS_D, bool HAS_Z, bool PIPE = false>
+template <int N, int S, int IO, bool SP, int PASS, bool HAS_D, bool HAS_Z, bool PIPE = false,
+          bool PRIO = true>
 __device__ __forceinline__ void scan_chunk(const ChunkIo& io, const BcIo& bcio, float dbias,
                                            int ntok, int w, int n0,
                                            ScanLds<N, S, PASS != kPassSummary, PASS == kPassFixup>& lds,
@@ -511,6 +547,13 @@ __device__ __forceinline__ void scan_chunk(const ChunkIo& io, const BcIo& bcio, 
     constexpr bool SUM = PASS != kPassOutput;
     constexpr bool FIX = PASS == kPassFixup;
     constexpr bool LOAD_Z = OUTPUT && HAS_Z;
+    // The passes that only need the chunk's total delta (the summary and
+    // local passes: the decay product) have each wave add only the tokens it
+    // stages and combine the S partials at the end, in wave order (the same
+    // order in both passes, so their decay products agree bit for bit). The
+    // repaired carry's second pass keeps a running sum in every wave: its
+    // vote after each tile needs it.
+    constexpr bool STAGED_SUM = S > 1 && (PASS == kPassSummary || PASS == kPassLocal);
     constexpr int KP = BcStage<N, S>::kPerLane;
     const int ntiles = (ntok + TT - 1) / TT;
     const int nfull = ntok / TT;
@@ -530,14 +573,14 @@ __device__ __forceinline__ void scan_chunk(const ChunkIo& io, const BcIo& bcio, 
         // The B/C run is issued first and kept first (scheduling fences), so
         // with AHEAD == 1 staging it at the end of this step waits only for
         // loads older than the next tile's token inputs.
-        fetch_bc<N, S, IO>(bcio, ifetch, min(TT, ntok - ifetch * TT), bf, cf);
+        fetch_bc<N, S, IO, OUTPUT>(bcio, ifetch, min(TT, ntok - ifetch * TT), bf, cf);
         __builtin_amdgcn_sched_barrier(0);
         fetch_tile<S, IO, LOAD_Z>(io, ifetch, w, ntok, AHEAD == 2 ? cur : nxt);
         __builtin_amdgcn_sched_barrier(0);
         const int cnt = FULL ? TT : ntok - i * TT;
         float part[TT], dtv[TT / S];
         if constexpr (S == 1) delta_tile<S, IO, SP>(cur, dbias, dtv);
-        compute_tile<N, S, IO, OUTPUT, SUM, HAS_D, HAS_Z, FULL, PIPE>(io, lds.bcs[i & 1] + n0,
+        compute_tile<N, S, IO, OUTPUT, SUM && !STAGED_SUM, HAS_D, HAS_Z, FULL, PIPE>(io, lds.bcs[i & 1] + n0,
                                                                 lds.dtdu[i & 1], cur, dtv, i, cnt,
                                                                 A2, h, dskip, part, dsum);
         if constexpr (OUTPUT && S > 1) {
@@ -550,10 +593,10 @@ __device__ __forceinline__ void scan_chunk(const ChunkIo& io, const BcIo& bcio, 
             const bool done = dsum * a2max <= -kFixupLog2;
             lds.vote[i & 1][w] = __builtin_amdgcn_ballot_w64(!done) == 0 ? 1 : 0;
         }
-        stage_bc<N, S, IO>(lds.bcs[(i + 1) & 1], bs, cs);
+        stage_bc<N, S, IO, OUTPUT>(lds.bcs[(i + 1) & 1], bs, cs);
         if constexpr (S > 1)
-            stage_tokens<S, IO, SP, OUTPUT && HAS_D, OUTPUT && HAS_Z>(lds.dtdu[(i + 1) & 1], w,
-                                                                      nxt, dbias, dskip, en);
+            stage_tokens<S, IO, SP, OUTPUT && HAS_D, OUTPUT && HAS_Z, STAGED_SUM>(
+                lds.dtdu[(i + 1) & 1], w, nxt, dbias, dskip, en, ntok - (i + 1) * TT, &dsum);
         __syncthreads();
         if constexpr (OUTPUT && S > 1)
             finalize_tile<S, IO, HAS_Z, FULL>(io, lds.red[i & 1], w, i, cnt, ec);
@@ -581,20 +624,22 @@ __device__ __forceinline__ void scan_chunk(const ChunkIo& io, const BcIo& bcio, 
 
     // prologue: tile 0's B/C and token inputs into LDS buffers 0 (and, two
     // tiles ahead, tile 1's raw inputs into the second registers)
-    fetch_bc<N, S, IO>(bcio, 0, min(TT, ntok), bra, cra);
+    fetch_bc<N, S, IO, OUTPUT>(bcio, 0, min(TT, ntok), bra, cra);
     fetch_tile<S, IO, LOAD_Z>(io, 0, w, ntok, ta);
     if constexpr (AHEAD == 2) {
         const int i1 = min(1, ntiles - 1);
-        fetch_bc<N, S, IO>(bcio, i1, min(TT, ntok - i1 * TT), brb, crb);
+        fetch_bc<N, S, IO, OUTPUT>(bcio, i1, min(TT, ntok - i1 * TT), brb, crb);
         fetch_tile<S, IO, LOAD_Z>(io, i1, w, ntok, tb);
     }
-    stage_bc<N, S, IO>(lds.bcs[0], bra, cra);
+    stage_bc<N, S, IO, OUTPUT>(lds.bcs[0], bra, cra);
     if constexpr (S > 1)
-        stage_tokens<S, IO, SP, OUTPUT && HAS_D, OUTPUT && HAS_Z>(lds.dtdu[0], w, ta, dbias,
-                                                                  dskip, ea);
+        stage_tokens<S, IO, SP, OUTPUT && HAS_D, OUTPUT && HAS_Z, STAGED_SUM>(
+            lds.dtdu[0], w, ta, dbias, dskip, ea, ntok, &dsum);
     __syncthreads();
+    const ProgressPrio<PRIO> prio(nfull);
     int i = 0;
     for (; i + 2 <= nfull; i += 2) {
+        prio.at(i);
         if (even(Full{}, i)) return;
         if (odd(Full{}, i + 1)) return;
     }
@@ -603,6 +648,17 @@ __device__ __forceinline__ void scan_chunk(const ChunkIo& io, const BcIo& bcio, 
         if (nfull < ntiles) odd(Ragged{}, i + 1);
     } else if (nfull < ntiles) {
         even(Ragged{}, i);
+    }
+    if constexpr (STAGED_SUM) {
+        // the waves' partial delta sums, added in wave order; the barrier
+        // first lets every wave finish reading the last tile's readouts
+        float* part = &lds.red[0][0];
+        __syncthreads();
+        part[w * kWave + lane] = dsum;
+        __syncthreads();
+        dsum = part[lane];
+#pragma unroll
+        for (int v = 1; v < S; ++v) dsum += part[v * kWave + lane];
     }
 }
 
@@ -747,7 +803,7 @@ __global__ __launch_bounds__(256) void chunk_carry_kernel(int64_t columns, int64
 // Pass 2 (or the only pass when nchunks == 1): scan each chunk from its true
 // entering state and write y; the last chunk writes hL.
 template <int N, int S, int IO, bool SP, bool HAS_D, bool HAS_Z, bool PIPE,
-          bool STORE_END = false>
+          bool STORE_END = false, bool PRIO = true>
 __device__ __forceinline__ void output_group(const ScanArgs& a, const ChunkGrid& g,
                                              const Carry& c, int64_t blk, ScanLds<N, S>& lds) {
     constexpr int NPW = Split<N, S>::NPW;
@@ -796,7 +852,7 @@ __device__ __forceinline__ void output_group(const ScanArgs& a, const ChunkGrid&
     }
     const float dskip = HAS_D ? a.D[s.d] : 0.0f;
     float dsum = 0.0f;
-    scan_chunk<N, S, IO, SP, kPassOutput, HAS_D, HAS_Z, PIPE>(s.io, s.bc, s.dbias, s.ntok, s.w, s.n0,
+    scan_chunk<N, S, IO, SP, kPassOutput, HAS_D, HAS_Z, PIPE, PRIO>(s.io, s.bc, s.dbias, s.ntok, s.w, s.n0,
                                                         lds, A2, h, dskip, 0.0f, dsum);
     if constexpr (STORE_END) {
         // chunk 0 of a cut sequence: its end state, exact since it started
@@ -1075,7 +1131,7 @@ void chunk_mixed_kernel(ScanArgs a, ChunkGrid g, int64_t nwhole) {
     } lds;
     const int64_t blk = blockIdx.x;
     if (blk < nwhole) {
-        output_group<N, 4, IO, SP, HAS_D, HAS_Z, kPipeMixed>(a, g, Carry{nullptr, nullptr, nullptr}, blk,
+        output_group<N, 4, IO, SP, HAS_D, HAS_Z, kPipeMixed, false, false>(a, g, Carry{nullptr, nullptr, nullptr}, blk,
                                                  lds.whole);
     } else {
         int64_t pair;

@@ -305,6 +305,22 @@ def test_scan_bwd_rejects_bad_arguments(lib):
     assert lib.ssm_scan_bwd_workspace_size(2, 64, 64, 16, 1, _plan(chunk_len=16, halves=-1),
                                            ctypes.byref(res), ctypes.byref(chunked)) == OK
     assert chunked.value > need.value and (res.chunk_len, res.halves) == (16, 0)
+    # Every workspace part scales with dstate except the half groups' extra
+    # dB/dC slots, reserved for dstate 13..16 only when the sequence stays
+    # whole (a chunked plan never splits groups). So over dstate 8, 12, 16 the
+    # size grows in equal steps for a chunked plan, and by more from 12 to 16
+    # for a whole one. (At this shape every part is a whole number of the
+    # 64-float alignment, so the steps are exact.)
+    def ws(dstate, chunk_len):
+        out = ctypes.c_size_t(0)
+        assert lib.ssm_scan_bwd_workspace_size(2, 64, 64, dstate, 1,
+                                               _plan(chunk_len=chunk_len, halves=-1), None,
+                                               ctypes.byref(out)) == OK
+        return out.value
+    c8, c12, c16 = ws(8, 16), ws(12, 16), ws(16, 16)
+    assert c16 - c12 == c12 - c8 > 0
+    w8, w12, w16 = ws(8, 64), ws(12, 64), ws(16, 64)
+    assert w16 - w12 == (w12 - w8) + 2 * 2 * 64 * 16 * 4   # + one slot of dB and of dC
     lib.ssm_scan_bwd_workspace_size(2, 64, 64, 16, 1, whole, None, ctypes.byref(need))
 
     def bwd(batch=2, seqlen=64, dim=64, dstate=16, dtype=1, opts=None, plan=whole, ws=P, wsb=None,

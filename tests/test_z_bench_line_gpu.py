@@ -1,10 +1,11 @@
 """GPU: one short run of bench.py and the fields of its JSON line.
 
 The benchmark prints one line for the Mamba-2.8B-shaped layer scan (B=8,
-L=2048, D=5120, N=16, bf16 I/O): throughput in elements/s, the roofline of
-the kernel the plan launches (achieved, peak, their ratio, the HBM traffic
-recorded from counters for this kernel's sources) and the fp64 oracle timed
-on the host as a reported baseline.
+L=2048, D=5120, N=16, bf16 I/O): throughput in elements/s, the HBM roofline
+of the kernel the plan launches (algorithmic bytes per step against 8 TB/s,
+the 60% target, the HBM traffic recorded from counters for this kernel's
+sources), the vector issue fraction beside it, and the fp64 oracle timed on
+the host as a reported baseline.
 """
 import json
 import os
@@ -48,10 +49,25 @@ def test_default_bench_line():
     assert d["value"] == pytest.approx(elems / (d["ms_per_step"] / 1e3), rel=1e-9)
 
     r = d["roofline"]
-    assert r["bound"] == "alu" and r["peak"] == bench.ALU_PEAK_TOPS
+    # the HBM roofline the target is stated against: algorithmic bytes per
+    # step over 8 TB/s
+    w = bench_workload()
+    nbytes = bench.algorithmic_bytes(w)
+    assert r["bound"] == "hbm" and r["peak"] == 8000.0 and r["unit"] == "GB/s"
+    assert r["algorithmic_bytes"] == nbytes
+    hbm = nbytes / (d["ms_per_step"] / 1e3) / 8e12
+    assert r["frac"] == pytest.approx(hbm, abs=1e-4)
     assert r["frac"] == pytest.approx(r["achieved"] / r["peak"], abs=1e-3)
+    assert r["target_frac"] == 0.60 and r["target_met"] == (r["frac"] >= 0.60)
     assert 0.0 < r["frac"] < 1.0
-    assert r["algorithmic_bytes"] == bench.algorithmic_bytes(bench_workload())
+    # beside it the vector issue fraction, a transcendental at two slots
+    iss = r["issue"]
+    slots = bench.algorithmic_alu_ops(w) + bench.transcendentals(w) * elems
+    assert iss["algorithmic_slots"] == slots == (89 + 18) * elems
+    assert iss["frac"] == pytest.approx(slots / (d["ms_per_step"] / 1e3) / 39.3216e12, abs=1e-3)
+    assert 0.0 < iss["frac"] < 1.0
+    assert iss["hbm_frac_at_full_issue"] == pytest.approx(
+        (nbytes / 8e12) / (slots / 39.3216e12), abs=1e-3)
     assert r["kernel"] in ("chunk_mixed_kernel", "chunk_output_kernel")
     # traffic comes from the counters recorded for this kernel's sources, or
     # is null once those sources have changed
