@@ -31,7 +31,11 @@
  * returns and allocates no device memory; ssm_scan_fwd takes its scratch
  * space from the caller's workspace. Work is queued on `stream` (0 = the
  * null stream) and the call returns before it finishes, so buffers must
- * outlive the queued work. Calls on different streams do not share state.
+ * outlive the queued work. Calls on different streams do not share state,
+ * with two exceptions: the automatic plans query each device's compute-unit
+ * count once and keep it for the life of the process (a per-device cache
+ * that threads may fill concurrently; it never changes), and
+ * ssm_scan_fwd_noalloc's fixed scratch (see there).
  *
  * Errors: shape, dtype, null-pointer, alignment and workspace checks run on
  * the host before any HIP call and return a negative mamba_status; nothing
@@ -71,11 +75,13 @@ typedef enum mamba_dtype {
 /*
  * How chunks of a cut sequence learn the state entering them.
  *
- * MAMBA_CARRY_RERUN   a summary pass computes every chunk's (decay product,
- *                     end state) pair, an associative combine of the pairs
- *                     gives the state entering each chunk (the "parallel
- *                     scan" of section "A Scan on the Chip"), and the output
- *                     pass reruns every chunk from its entering state.
+ * MAMBA_CARRY_RERUN   a first pass runs chunk 0 to its outputs (from h0, so
+ *                     its end state is exact) and summarises chunks 1 ..
+ *                     n-2 from a zero state as (decay product, end state)
+ *                     pairs; an associative combine of the pairs gives the
+ *                     state entering each later chunk (the "parallel scan"
+ *                     of section "A Scan on the Chip"), and a second pass
+ *                     reruns chunks 1 .. n-1 from their entering states.
  * MAMBA_CARRY_REPAIR  every chunk runs once from a zero state (the first
  *                     from h0), writing y and its pair; the combine gives the
  *                     entering states and hL; each later chunk then reruns

@@ -2,8 +2,8 @@
 
 Each translation unit is compiled to an object on its own, in parallel,
 and the objects are linked into one shared library. The chunked-scan
-kernels are compiled four times from scan_variant.hip, once per
-(I/O dtype, delta softplus) pair.
+kernels are compiled eight times from scan_variant.hip, once per
+(I/O dtype, delta softplus, half of the dstate range).
 """
 import os
 import shutil
@@ -22,9 +22,9 @@ ARCH = "gfx950"
 UNITS = [("api", "api.cpp", ()), ("noalloc", "noalloc.hip", ()), ("launch", "launch.hip", ()),
          ("conv1d", "conv1d.hip", ()),
          ("scan_bwd", "scan_bwd.hip", ()), ("ssd", "ssd.hip", ())] + [
-    (f"scan_io{io}_sp{sp}", "scan_variant.hip",
-     (f"-DMAMBA_VARIANT_IO={io}", f"-DMAMBA_VARIANT_SP={sp}"))
-    for io in (0, 1) for sp in (0, 1)]
+    (f"scan_io{io}_sp{sp}_n{part}", "scan_variant.hip",
+     (f"-DMAMBA_VARIANT_IO={io}", f"-DMAMBA_VARIANT_SP={sp}", f"-DMAMBA_VARIANT_PART={part}"))
+    for io in (0, 1) for sp in (0, 1) for part in (0, 1)]
 
 
 def hipcc():

@@ -172,9 +172,10 @@ size_t scan_workspace_bytes(int64_t batch, int64_t dim, int dstate, int64_t nchu
 hipError_t launch_scan(const ScanArgs& a, const ScanPlan& plan, void* workspace,
                        hipStream_t stream);
 
-// The chunked scan for one (I/O dtype, delta softplus) pair; each pair is
-// compiled in its own translation unit (scan_variant.hip).
-template <int IO, bool SP>
+// The chunked scan for one (I/O dtype, delta softplus) pair and half of the
+// dstate range (PART 0: 1..8, PART 1: 9..16); each is compiled in its own
+// translation unit (scan_variant.hip).
+template <int IO, bool SP, int PART>
 hipError_t launch_scan_variant(const ScanArgs& a, const ScanPlan& plan, void* workspace,
                                hipStream_t stream);
 

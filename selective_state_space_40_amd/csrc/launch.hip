@@ -170,11 +170,18 @@ hipError_t launch_scan(const ScanArgs& a, const ScanPlan& plan, void* workspace,
         return hipGetLastError();
     }
     const bool sp = a.delta_softplus != 0;
+    if (a.dstate <= 8) {
+        if (a.io == kIoF32)
+            return sp ? launch_scan_variant<kIoF32, true, 0>(a, plan, workspace, stream)
+                      : launch_scan_variant<kIoF32, false, 0>(a, plan, workspace, stream);
+        return sp ? launch_scan_variant<kIoBF16, true, 0>(a, plan, workspace, stream)
+                  : launch_scan_variant<kIoBF16, false, 0>(a, plan, workspace, stream);
+    }
     if (a.io == kIoF32)
-        return sp ? launch_scan_variant<kIoF32, true>(a, plan, workspace, stream)
-                  : launch_scan_variant<kIoF32, false>(a, plan, workspace, stream);
-    return sp ? launch_scan_variant<kIoBF16, true>(a, plan, workspace, stream)
-              : launch_scan_variant<kIoBF16, false>(a, plan, workspace, stream);
+        return sp ? launch_scan_variant<kIoF32, true, 1>(a, plan, workspace, stream)
+                  : launch_scan_variant<kIoF32, false, 1>(a, plan, workspace, stream);
+    return sp ? launch_scan_variant<kIoBF16, true, 1>(a, plan, workspace, stream)
+              : launch_scan_variant<kIoBF16, false, 1>(a, plan, workspace, stream);
 }
 
 hipError_t launch_state_update(const DecodeArgs& a, hipStream_t stream) {

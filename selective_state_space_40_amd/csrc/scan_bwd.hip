@@ -81,6 +81,39 @@ __device__ __forceinline__ float sigmoid_f32(float v) {
     return fast_rcp(1.0f + fast_exp2(-v * kLog2e));
 }
 
+// Issue priority by progress. The scheduler prefers the oldest ready wave of
+// a SIMD, so its waves finish one after the other and the last ones run
+// alone; each wave here lowers its own priority (s_setprio) as it gets
+// through its work so that the waves behind are preferred and all finish
+// together. Priority 3 for the forward phase, then 2, 1 and 0 over thirds of
+// the walk back; the chunk summaries step down over quarters.
+#ifndef MAMBA_BWD_PRIO
+#define MAMBA_BWD_PRIO 1
+#endif
+__device__ __forceinline__ void set_prio(int p) {
+    if constexpr (MAMBA_BWD_PRIO) {
+        if (p >= 3) __builtin_amdgcn_s_setprio(3);
+        else if (p == 2) __builtin_amdgcn_s_setprio(2);
+        else if (p == 1) __builtin_amdgcn_s_setprio(1);
+        else __builtin_amdgcn_s_setprio(0);
+    }
+}
+
+// Priority `top` at the first of n tiles, one lower after each of `top`
+// equal parts (`top` 2: thirds, 3: quarters).
+struct PrioSteps {
+    int64_t b1, b2, b3;
+    __device__ PrioSteps(int64_t n, int top)
+        : b1(top >= 2 ? n / (top + 1) : n), b2(top >= 2 ? 2 * n / (top + 1) : n),
+          b3(top >= 3 ? 3 * n / (top + 1) : n) {}
+    __device__ void at(int64_t done, int top) const {
+        if (done == 0) set_prio(top);
+        else if (done == b1) set_prio(top - 1);
+        else if (done == b2) set_prio(top - 2);
+        else if (done == b3) set_prio(top - 3);
+    }
+};
+
 // Raw inputs of one tile as this thread stages them: the tokens j = w,
 // w+S, ... of the tile for its lane's channel, one element of the tile's B
 // and C rows (2 * kBT * 4S elements over 64S threads) and, walking
@@ -328,6 +361,7 @@ __device__ __forceinline__ void bwd_whole_group(const BwdArgs& a, int64_t ngroup
         TileRaw<S> raw;
         fetch_tile<S, IO, HAS_Z, false>(a, pl, tent, i_first,
                                         static_cast<int>(min<int64_t>(kBT, L - i_first * kBT)), raw);
+        set_prio(3);
         for (int64_t i = i_first; i < i_end; ++i) {
             const int64_t t0 = i * kBT;
             const int cnt = static_cast<int>(min<int64_t>(kBT, L - t0));
@@ -374,7 +408,9 @@ __device__ __forceinline__ void bwd_whole_group(const BwdArgs& a, int64_t ngroup
         fetch_tile<S, IO, HAS_Z, true>(a, pl, tent, i_end - 1,
                                        static_cast<int>(min<int64_t>(kBT, L - (i_end - 1) * kBT)),
                                        raw);
+        const PrioSteps prio(i_end - i_first, 2);
         for (int64_t i = i_end - 1; i >= i_first; --i) {
+            prio.at(i_end - 1 - i, 2);
             const int64_t t0 = i * kBT;
             const int cnt = static_cast<int>(min<int64_t>(kBT, L - t0));
             // the tile's entering state; a lane past the last channel starts
@@ -588,7 +624,9 @@ __device__ __forceinline__ void bwd_state_summary(const BwdArgs& a, int64_t ngro
     Own own[(kBT + S - 1) / S];
     TileRaw<S> raw;
     fetch_tile<S, IO, false, false>(a, pl, ws.tent, i_first, kBT, raw);
+    const PrioSteps prio(i_end - i_first, 3);
     for (int64_t i = i_first; i < i_end; ++i) {
+        prio.at(i - i_first, 3);
         put_tile<S, IO, SP, false, false>(raw, pl, lds, kBT, N, own);
         __syncthreads();
         fetch_tile<S, IO, false, false>(a, pl, ws.tent, min(i + 1, i_end - 1), kBT, raw);
@@ -659,7 +697,9 @@ __device__ __forceinline__ void bwd_adjoint_summary(const BwdArgs& a, int64_t ng
     TileRaw<S> raw;
     fetch_tile<S, IO, HAS_Z, true>(a, pl, ws.tent, i_end - 1,
                                    static_cast<int>(min<int64_t>(kBT, L - (i_end - 1) * kBT)), raw);
+    const PrioSteps prio(i_end - i_first, 3);
     for (int64_t i = i_end - 1; i >= i_first; --i) {
+        prio.at(i_end - 1 - i, 3);
         // tokens past the end of the sequence are staged inert (g = delta = 0,
         // zero C rows): they leave lam, en and the sum unchanged
         put_tile<S, IO, SP, HAS_Z, true>(raw, pl, lds, static_cast<int>(min<int64_t>(kBT, L - i * kBT)),
@@ -872,6 +912,7 @@ __device__ __forceinline__ void bwd_half_group(const BwdArgs& a, int64_t ngroups
             h[q] = (sv[q] && f.h0 != nullptr) ? f.h0[(b * f.dim + d) * N + n0 + q] : 0.0f;
         Raw raw;
         fetch(No{}, 0, static_cast<int>(min<int64_t>(kBT, L)), raw);
+        set_prio(3);
         for (int64_t i = 0; i < ntiles; ++i) {
             const int64_t t0 = i * kBT;
             const int cnt = static_cast<int>(min<int64_t>(kBT, L - t0));
@@ -911,7 +952,9 @@ __device__ __forceinline__ void bwd_half_group(const BwdArgs& a, int64_t ngroups
     {
         Raw raw;
         fetch(Yes{}, ntiles - 1, static_cast<int>(L - (ntiles - 1) * kBT), raw);
+        const PrioSteps prio(ntiles, 2);
         for (int64_t i = ntiles - 1; i >= 0; --i) {
+            prio.at(ntiles - 1 - i, 2);
             const int64_t t0 = i * kBT;
             const int cnt = static_cast<int>(min<int64_t>(kBT, L - t0));
             float he[kHalfNps], hs[kBT][kHalfNps], h[kHalfNps];

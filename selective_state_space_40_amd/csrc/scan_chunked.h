@@ -52,7 +52,8 @@
 // whole chunk, as the two-pass form does.
 //
 // This header is the body of scan_variant.hip, which is compiled once per
-// (I/O dtype, delta activation) pair so the variants build in parallel.
+// (I/O dtype, delta activation, dstate half) so the variants build in
+// parallel.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -259,12 +260,13 @@ __device__ __forceinline__ void fetch_tile(const ChunkIo& io, int tile, int w, i
     }
 }
 
-// What the wave that finishes token j of a tile keeps from staging it: the
-// skip term D*x and the gate silu(z). Holding these instead of the raw x and
-// z frees the raw tile as soon as it is staged.
+// What the wave that finishes token j of a tile keeps from staging it: x as
+// fp32 (the skip term D*x is one FMA at the finish) and the gate silu(z).
+// Holding these instead of the raw x and z frees the raw tile as soon as it
+// is staged.
 template <int S>
 struct Epilogue {
-    float skip[TT / S], gate[TT / S];
+    float u[TT / S], gate[TT / S];
 };
 
 // LDS layout of the staged per-token inputs: [token j][lane] float2 (delta,
@@ -285,7 +287,7 @@ __device__ __forceinline__ void stage_tokens(float2* dtdu, int w, const Tile<S>&
     for (int jj = 0; jj < TT / S; ++jj) {
         const float u = raw_to_f32<IO>(r.x[jj]);
         dtdu[(jj * S + w) * kWave + lane] = make_float2(dt[jj], dt[jj] * u);
-        e.skip[jj] = HAS_D ? dskip * u : 0.0f;
+        e.u[jj] = HAS_D ? u : 0.0f;
         e.gate[jj] = HAS_Z ? silu(raw_to_f32<IO>(r.z[jj])) : 1.0f;
         if constexpr (STAGED_SUM) {
             if (jj * S + w < cnt) *dsum += dt[jj];
@@ -406,9 +408,10 @@ __device__ __forceinline__ void compute_tile(const ChunkIo& io, const float* bcs
 // Wave w finishes its tokens j = w, w+S, ... of the tile: the S partial
 // readouts summed in a fixed wave order, the skip term, the gate, rounding
 // and the store.
-template <int S, int IO, bool HAS_Z, bool FULL>
+template <int S, int IO, bool HAS_D, bool HAS_Z, bool FULL>
 __device__ __forceinline__ void finalize_tile(const ChunkIo& io, const float* red_tile, int w,
-                                              int tile, int cnt, const Epilogue<S>& e) {
+                                              int tile, int cnt, const Epilogue<S>& e,
+                                              float dskip) {
     const int lane = threadIdx.x & (kWave - 1);
 #pragma unroll
     for (int jj = 0; jj < TT / S; ++jj) {
@@ -418,7 +421,7 @@ __device__ __forceinline__ void finalize_tile(const ChunkIo& io, const float* re
             float acc = col[0];
 #pragma unroll
             for (int v = 1; v < S; ++v) acc += col[v * TT * kWave];
-            acc += e.skip[jj];
+            if constexpr (HAS_D) acc = fmaf(dskip, e.u[jj], acc);
             if constexpr (HAS_Z) acc *= e.gate[jj];
             // Lanes past the last channel were clamped onto channel dim-1 and
             // computed its value bit for bit, so they store the same bits to
@@ -599,7 +602,7 @@ __device__ __forceinline__ void scan_chunk(const ChunkIo& io, const BcIo& bcio, 
                 lds.dtdu[(i + 1) & 1], w, nxt, dbias, dskip, en, ntok - (i + 1) * TT, &dsum);
         __syncthreads();
         if constexpr (OUTPUT && S > 1)
-            finalize_tile<S, IO, HAS_Z, FULL>(io, lds.red[i & 1], w, i, cnt, ec);
+            finalize_tile<S, IO, HAS_D, HAS_Z, FULL>(io, lds.red[i & 1], w, i, cnt, ec, dskip);
         if constexpr (FIX) {
             int all = 1;
 #pragma unroll
@@ -980,7 +983,7 @@ __device__ __forceinline__ void half_group(const ScanArgs& a, int64_t b, int64_t
         uint32_t x, dt, z;
     };
     struct Epi {
-        float skip, gate;
+        float u, gate;  // x as fp32 (skip term: one FMA at the finish), silu(z)
     };
     // this lane's token of tile `tile`, clamped to the sequence (unused copies)
     auto fetch = [&](int tile, Raw& r) {
@@ -995,7 +998,7 @@ __device__ __forceinline__ void half_group(const ScanArgs& a, int64_t b, int64_t
         if constexpr (SP) dt = softplus_f32(dt);
         const float u = raw_to_f32<IO>(r.x);
         dtdu[v * kHalf + ch] = make_float2(dt, dt * u);
-        e.skip = HAS_D ? dskip * u : 0.0f;
+        e.u = HAS_D ? u : 0.0f;
         e.gate = HAS_Z ? silu(raw_to_f32<IO>(r.z)) : 1.0f;
     };
     auto step = [&](auto full_tag, int i, Raw& cur, const Epi& ec, Raw& nxt, Epi& en,
@@ -1068,7 +1071,7 @@ __device__ __forceinline__ void half_group(const ScanArgs& a, int64_t b, int64_t
             float acc = col[0];
 #pragma unroll
             for (int u = 1; u < kSplitsHalf; ++u) acc += col[u * TT * kHalf];
-            acc += ec.skip;
+            if constexpr (HAS_D) acc = fmaf(dskip, ec.u, acc);
             if constexpr (HAS_Z) acc *= ec.gate;
             const uint32_t off = lane_bytes + static_cast<uint32_t>(i * TT + v) * row_bytes;
             if constexpr (IO == kIoF32) {
@@ -1316,16 +1319,21 @@ hipError_t launch_scan_n(const ScanArgs& a, const ScanPlan& plan, void* ws, hipS
 
 }  // namespace
 
-template <int IO, bool SP>
+template <int IO, bool SP, int PART>
 hipError_t launch_scan_variant(const ScanArgs& a, const ScanPlan& p, void* ws, hipStream_t s) {
+    // PART 0 holds dstate 1..8, PART 1 dstate 9..16 (two objects per variant)
     switch (a.dstate) {
-#define MAMBA_CASE(n) case n: return launch_scan_n<n, IO, SP>(a, p, ws, s);
+#define MAMBA_CASE(n)                                                    \
+    case n:                                                              \
+        if constexpr ((n > 8) == (PART == 1)) return launch_scan_n<n, IO, SP>(a, p, ws, s); \
+        break;
         MAMBA_CASE(1) MAMBA_CASE(2) MAMBA_CASE(3) MAMBA_CASE(4) MAMBA_CASE(5) MAMBA_CASE(6)
         MAMBA_CASE(7) MAMBA_CASE(8) MAMBA_CASE(9) MAMBA_CASE(10) MAMBA_CASE(11) MAMBA_CASE(12)
         MAMBA_CASE(13) MAMBA_CASE(14) MAMBA_CASE(15) MAMBA_CASE(16)
 #undef MAMBA_CASE
-        default: return hipErrorInvalidValue;
+        default: break;
     }
+    return hipErrorInvalidValue;
 }
 
 }  // namespace mamba

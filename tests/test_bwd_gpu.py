@@ -155,7 +155,7 @@ def test_bwd_fused_softplus(orc, io):
 
 def test_bwd_full_size_sampled(orc):
     # the Mamba-2.8B layer shape: per-channel gradients on sampled channels
-    # over all rows, and dB/dC (sums over all channels) on batch row 0
+    # over all rows, and dB/dC (sums over all channels) on every row
     w = W.WORKLOADS["mamba28b_layer"]
     inp = W.generate_scan(w, device=DEV)
     g = torch.Generator(device=DEV).manual_seed(99)
@@ -176,11 +176,42 @@ def test_bwd_full_size_sampled(orc):
     assert_close(got["dA"].index_select(0, ix), want["dA"], TOL_BWD["bf16"], "full dA")
     assert_close(got["dD"].index_select(0, ix), want["dD"], TOL_BWD["bf16"], "full dD")
     assert_close(got["dh0"].index_select(1, ix), want["dh0"], TOL_BWD["bf16"], "full dh0")
-    _say(f"case bwd {w.name}: oracle on batch row 0, all channels")
-    row = {k: (v[:1] if k in ("x", "delta", "B", "C", "z") else v) for k, v in inp.items()}
-    want0 = orc.scan_bwd(**row, dy=dy[:1])
-    assert_close(got["dB"][:1], want0["dB"], TOL_BWD["bf16"], "full dB (row 0)")
-    assert_close(got["dC"][:1], want0["dC"], TOL_BWD["bf16"], "full dC (row 0)")
+    # dB and dC sum over all 5,120 channels: the oracle over every row and
+    # channel, one row at a time
+    for b in range(w.batch):
+        _say(f"case bwd {w.name}: oracle on batch row {b}, all channels")
+        row = {k: (v[b:b + 1] if k in ("x", "delta", "B", "C", "z") else v)
+               for k, v in inp.items()}
+        want_b = orc.scan_bwd(**row, dy=dy[b:b + 1])
+        assert_close(got["dB"][b:b + 1], want_b["dB"], TOL_BWD["bf16"], f"full dB (row {b})")
+        assert_close(got["dC"][b:b + 1], want_b["dC"], TOL_BWD["bf16"], f"full dC (row {b})")
+    _check_projections(inp, dy, got, range(0, w.seqlen, 1), "full")
+
+
+def _check_projections(inp, dy, got, tokens, what):
+    """Two identities that hold at any size, for the sums over channels:
+    y = silu(z) (C.h + D x) gives sum_n C[t,n] dC[t,n] = sum_d dy (y - silu(z) D x),
+    and dx = delta sum_n lam B + D dy silu(z) gives
+    sum_n B[t,n] dB[t,n] = sum_d x (dx - D dy silu(z)) (lam: the adjoint of the
+    state after token t). y comes from the forward scan of the same inputs
+    (checked against the oracle elsewhere); every side in fp64; the bound is
+    relative to the sum of the magnitudes of each side's terms."""
+    y, _ = ms.scan_fwd(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"],
+                       inp["z"], inp["h0"])
+    torch.cuda.synchronize()
+    t = torch.as_tensor(list(tokens), device=DEV)
+    f = lambda v: v.index_select(1, t).double()
+    x, z, dyt, yt, dx = f(inp["x"]), f(inp["z"]), f(dy), f(y), f(got["dx"])
+    Bt, Ct, dB, dC = f(inp["B"]), f(inp["C"]), f(got["dB"]), f(got["dC"])
+    g = z * torch.sigmoid(z)
+    Dx = inp["D"].double() * x
+    for lhs_terms, rhs_terms, name in (
+            (Ct * dC, dyt * (yt - g * Dx), "C.dC"),
+            (Bt * dB, x * (dx - inp["D"].double() * dyt * g), "B.dB")):
+        lhs, rhs = lhs_terms.sum(-1), rhs_terms.sum(-1)
+        scale = lhs_terms.abs().sum(-1) + rhs_terms.abs().sum(-1)
+        err = ((lhs - rhs).abs() / scale.clamp_min(1e-30)).max().item()
+        assert err <= TOL_BWD["bf16"], f"{what}: {name} identity off by {err:.3e} (relative)"
 
 
 def test_bwd_empty_and_deterministic(orc):
@@ -298,8 +329,8 @@ def test_bwd_chunks_and_halves_together_rejected():
 def test_bwd_million_length_sampled(orc):
     # one row of 2048 channels over 2^20 tokens: the plan cuts the sequence
     # into chunks; per-channel gradients on sampled channels against the
-    # oracle over the whole sequence (dB and dC, sums over every channel, are
-    # checked on the smaller chunked cases)
+    # oracle over the whole sequence; dB and dC (sums over every channel)
+    # through two identities that hold at any size (_check_projections)
     w = W.WORKLOADS["million_length"]
     plan = ms.resolve_bwd_plan(w.batch, w.seqlen, w.dim, w.dstate, torch.bfloat16)
     assert plan.chunk_len < w.seqlen
@@ -322,3 +353,10 @@ def test_bwd_million_length_sampled(orc):
     assert_close(got["dA"].index_select(0, ix), want["dA"], TOL_BWD["bf16"], "million dA")
     assert_close(got["dD"].index_select(0, ix), want["dD"], TOL_BWD["bf16"], "million dD")
     assert_close(got["dh0"].index_select(1, ix), want["dh0"], TOL_BWD["bf16"], "million dh0")
+    # dB and dC (sums over all 2,048 channels) through the identities, on
+    # every 64th token and on the tokens around every chunk boundary
+    _say(f"case bwd {w.name}: dB/dC identities")
+    toks = set(range(0, w.seqlen, 64))
+    for c in range(plan.chunk_len, w.seqlen, plan.chunk_len):
+        toks.update(range(max(0, c - 8), min(w.seqlen, c + 8)))
+    _check_projections(inp, dy, got, sorted(toks), "million")
