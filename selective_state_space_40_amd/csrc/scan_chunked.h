@@ -302,8 +302,7 @@ __device__ __forceinline__ void stage_tokens(float2* dtdu, int w, const Tile<S>&
 // its inputs straight from its registers (delta already activated in dtv)
 // and finishes and stores each token right away. With SUM (always without
 // OUTPUT) the sum of delta accumulates in dsum.
-template <int N, int S, int IO, bool OUTPUT, bool SUM, bool HAS_D, bool HAS_Z, bool FULL,
-          bool PIPE>
+template <int N, int S, int IO, bool OUTPUT, bool SUM, bool HAS_D, bool HAS_Z, bool FULL>
 __device__ __forceinline__ void compute_tile(const ChunkIo& io, const float* bcs_w,
                                              const float2* dtdu, const Tile<S>& r,
                                              const float (&dtv)[TT / S], int tile, int cnt, const float (&A2)[Split<N, S>::NPW],
@@ -343,6 +342,15 @@ __device__ __forceinline__ void compute_tile(const ChunkIo& io, const float* bcs
         }
     };
     auto compute_group = [&](int j0, const Group& q) {
+        // the decays of the group's tokens first: they do not depend on the
+        // state, so their exponentials are in flight before the state
+        // updates consume them
+        float ex[G][NPW];
+#pragma unroll
+        for (int jj = 0; jj < G; ++jj) {
+#pragma unroll
+            for (int k = 0; k < NPW; ++k) ex[jj][k] = fast_exp2(q.dt[jj] * A2[k]);
+        }
 #pragma unroll
         for (int jj = 0; jj < G; ++jj) {
             const int j = j0 + jj;
@@ -353,8 +361,7 @@ __device__ __forceinline__ void compute_tile(const ChunkIo& io, const float* bcs
                     float p = 0.0f;
 #pragma unroll
                     for (int k = 0; k < NPW; ++k) {
-                        const float e = fast_exp2(dt * A2[k]);
-                        h[k] = fmaf(e, h[k], du * q.B[jj][k]);
+                        h[k] = fmaf(ex[jj][k], h[k], du * q.B[jj][k]);
                         p = fmaf(q.C[jj][k], h[k], p);
                     }
                     if constexpr (S == 1) {
@@ -370,38 +377,23 @@ __device__ __forceinline__ void compute_tile(const ChunkIo& io, const float* bcs
                     if constexpr (SUM) dsum += dt;
                 } else {
 #pragma unroll
-                    for (int k = 0; k < NPW; ++k) {
-                        const float e = fast_exp2(dt * A2[k]);
-                        h[k] = fmaf(e, h[k], du * q.B[jj][k]);
-                    }
+                    for (int k = 0; k < NPW; ++k) h[k] = fmaf(ex[jj][k], h[k], du * q.B[jj][k]);
                     if constexpr (SUM) dsum += dt;
                 }
             }
         }
     };
-    if constexpr (PIPE && G > 1 && NG > 1) {
-        // software-pipelined: the next group's LDS reads go out before this
-        // group's arithmetic, so its latency hides behind that arithmetic
-        // (a second group of registers; kernels with registers to spare)
-        Group q[2];
-        read_group(0, q[0]);
 #pragma unroll
-        for (int g = 0; g < NG; ++g) {
-            if (g + 1 < NG) read_group((g + 1) * G, q[(g + 1) & 1]);
-            __builtin_amdgcn_sched_barrier(0);
-            compute_group(g * G, q[g & 1]);
-        }
-    } else {
-#pragma unroll
-        for (int g = 0; g < NG; ++g) {
-            Group q;
-            read_group(g * G, q);
-            // keeps the group's reads ahead of its arithmetic: left alone, the
-            // scheduler issues each token's reads just before their use and
-            // every token then waits out the LDS latency
-            if constexpr (G > 1) __builtin_amdgcn_sched_barrier(0);
-            compute_group(g * G, q);
-        }
+    for (int g = 0; g < NG; ++g) {
+        Group q;
+        read_group(g * G, q);
+        // keeps the group's reads ahead of its arithmetic: left alone, the
+        // scheduler issues each token's reads just before their use and
+        // every token then waits out the LDS latency (reading the next
+        // group's inputs before this group's arithmetic as well measured no
+        // faster and took 12-22 more registers)
+        if constexpr (G > 1) __builtin_amdgcn_sched_barrier(0);
+        compute_group(g * G, q);
     }
 }
 
@@ -468,26 +460,6 @@ enum Pass : int {
 // 2^-kFixupLog2 for every state of the workgroup.
 constexpr float kFixupLog2 = 32.0f;
 
-// Which kernels read a tile's LDS inputs one token group ahead of the
-// arithmetic (compute_tile): those whose occupancy the extra registers do
-// not lower.
-#ifndef MAMBA_PIPE_SUMMARY
-#define MAMBA_PIPE_SUMMARY 1
-#endif
-#ifndef MAMBA_PIPE_OUTPUT
-#define MAMBA_PIPE_OUTPUT 0
-#endif
-#ifndef MAMBA_PIPE_MIXED
-#define MAMBA_PIPE_MIXED 1
-#endif
-#ifndef MAMBA_PIPE_LOCAL
-#define MAMBA_PIPE_LOCAL 0
-#endif
-constexpr bool kPipeSummary = MAMBA_PIPE_SUMMARY;
-constexpr bool kPipeOutput = MAMBA_PIPE_OUTPUT;
-constexpr bool kPipeMixed = MAMBA_PIPE_MIXED;
-constexpr bool kPipeLocal = MAMBA_PIPE_LOCAL;
-
 // Issue priority by progress. A SIMD's scheduler prefers the oldest of its
 // ready waves, so the waves sharing it finish one after the other and the
 // last ones run alone, issuing far less often than a full SIMD would. A wave
@@ -538,8 +510,7 @@ struct ProgressPrio {
 // and the whole workgroup leaves together once they agree; the loads still
 // in flight are dropped. Without kPassFixup the steps return false at
 // compile time and the loop is as before.
-template <int N, int S, int IO, bool SP, int PASS, bool HAS_D, bool HAS_Z, bool PIPE = false,
-          bool PRIO = true>
+template <int N, int S, int IO, bool SP, int PASS, bool HAS_D, bool HAS_Z, bool PRIO = true>
 __device__ __forceinline__ void scan_chunk(const ChunkIo& io, const BcIo& bcio, float dbias,
                                            int ntok, int w, int n0,
                                            ScanLds<N, S, PASS != kPassSummary, PASS == kPassFixup>& lds,
@@ -583,7 +554,7 @@ __device__ __forceinline__ void scan_chunk(const ChunkIo& io, const BcIo& bcio, 
         const int cnt = FULL ? TT : ntok - i * TT;
         float part[TT], dtv[TT / S];
         if constexpr (S == 1) delta_tile<S, IO, SP>(cur, dbias, dtv);
-        compute_tile<N, S, IO, OUTPUT, SUM && !STAGED_SUM, HAS_D, HAS_Z, FULL, PIPE>(io, lds.bcs[i & 1] + n0,
+        compute_tile<N, S, IO, OUTPUT, SUM && !STAGED_SUM, HAS_D, HAS_Z, FULL>(io, lds.bcs[i & 1] + n0,
                                                                 lds.dtdu[i & 1], cur, dtv, i, cnt,
                                                                 A2, h, dskip, part, dsum);
         if constexpr (OUTPUT && S > 1) {
@@ -757,7 +728,7 @@ __device__ __forceinline__ void summary_group(const ScanArgs& a, const ChunkGrid
         h[q] = 0.0f;
     }
     float dsum = 0.0f;
-    scan_chunk<N, S, IO, SP, kPassSummary, false, false, kPipeSummary>(s.io, s.bc, s.dbias, s.ntok, s.w, s.n0,
+    scan_chunk<N, S, IO, SP, kPassSummary, false, false>(s.io, s.bc, s.dbias, s.ntok, s.w, s.n0,
                                                          lds, A2, h, 0.0f, 0.0f, dsum);
 #pragma unroll
     for (int q = 0; q < NPW; ++q) {
@@ -805,8 +776,8 @@ __global__ __launch_bounds__(256) void chunk_carry_kernel(int64_t columns, int64
 
 // Pass 2 (or the only pass when nchunks == 1): scan each chunk from its true
 // entering state and write y; the last chunk writes hL.
-template <int N, int S, int IO, bool SP, bool HAS_D, bool HAS_Z, bool PIPE,
-          bool STORE_END = false, bool PRIO = true>
+template <int N, int S, int IO, bool SP, bool HAS_D, bool HAS_Z, bool STORE_END = false,
+          bool PRIO = true>
 __device__ __forceinline__ void output_group(const ScanArgs& a, const ChunkGrid& g,
                                              const Carry& c, int64_t blk, ScanLds<N, S>& lds) {
     constexpr int NPW = Split<N, S>::NPW;
@@ -855,7 +826,7 @@ __device__ __forceinline__ void output_group(const ScanArgs& a, const ChunkGrid&
     }
     const float dskip = HAS_D ? a.D[s.d] : 0.0f;
     float dsum = 0.0f;
-    scan_chunk<N, S, IO, SP, kPassOutput, HAS_D, HAS_Z, PIPE, PRIO>(s.io, s.bc, s.dbias, s.ntok, s.w, s.n0,
+    scan_chunk<N, S, IO, SP, kPassOutput, HAS_D, HAS_Z, PRIO>(s.io, s.bc, s.dbias, s.ntok, s.w, s.n0,
                                                         lds, A2, h, dskip, 0.0f, dsum);
     if constexpr (STORE_END) {
         // chunk 0 of a cut sequence: its end state, exact since it started
@@ -873,7 +844,7 @@ template <int N, int S, int IO, bool SP, bool HAS_D, bool HAS_Z>
 __global__ __launch_bounds__(kWave * S) __attribute__((amdgpu_waves_per_eu(S <= 2 ? 2 : 4)))
 void chunk_output_kernel(ScanArgs a, ChunkGrid g, Carry c) {
     __shared__ ScanLds<N, S> lds;
-    output_group<N, S, IO, SP, HAS_D, HAS_Z, kPipeOutput>(a, g, c, blockIdx.x, lds);
+    output_group<N, S, IO, SP, HAS_D, HAS_Z>(a, g, c, blockIdx.x, lds);
 }
 
 // Rerun carry, pass 1, over chunks 0 .. nchunks-2. Chunk 0 starts from h0,
@@ -893,7 +864,7 @@ void chunk_head_kernel(ScanArgs a, ChunkGrid g, Carry c) {
     int64_t dblk, k, b;
     decode_block(g, blk, dblk, k, b);
     if (k + g.first_chunk == 0)
-        output_group<N, S, IO, SP, HAS_D, HAS_Z, kPipeOutput, true>(a, g, c, blk, lds.out);
+        output_group<N, S, IO, SP, HAS_D, HAS_Z, true>(a, g, c, blk, lds.out);
     else
         summary_group<N, S, IO, SP>(a, g, c, blk, lds.sum);
 }
@@ -1015,7 +986,6 @@ __device__ __forceinline__ void half_group(const ScanArgs& a, int64_t b, int64_t
         const float2* dtdu = lds.dtdu[i & 1];
         float* red = lds.red[i & 1] + v * TT * kHalf + ch;
         // tokens in pairs: both tokens' LDS inputs before their arithmetic
-        // (with kPipeMixed the next pair's inputs before this pair's)
         struct Pair {
             float2 du[2];
             float Bq[2][NPS], Cq[2][NPS];
@@ -1029,6 +999,12 @@ __device__ __forceinline__ void half_group(const ScanArgs& a, int64_t b, int64_t
             }
         };
         auto compute_pair = [&](int j0, const Pair& pr) {
+            float ex[2][NPS];  // the pair's decays first (see compute_tile)
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) {
+#pragma unroll
+                for (int q = 0; q < NPS; ++q) ex[jj][q] = fast_exp2(pr.du[jj].x * A2[q]);
+            }
 #pragma unroll
             for (int jj = 0; jj < 2; ++jj) {
                 const int j = j0 + jj;
@@ -1036,31 +1012,19 @@ __device__ __forceinline__ void half_group(const ScanArgs& a, int64_t b, int64_t
                     float p = 0.0f;
 #pragma unroll
                     for (int q = 0; q < NPS; ++q) {
-                        const float e = fast_exp2(pr.du[jj].x * A2[q]);
-                        h[q] = fmaf(e, h[q], pr.du[jj].y * pr.Bq[jj][q]);
+                        h[q] = fmaf(ex[jj][q], h[q], pr.du[jj].y * pr.Bq[jj][q]);
                         p = fmaf(pr.Cq[jj][q], h[q], p);
                     }
                     red[j * kHalf] = p;
                 }
             }
         };
-        if constexpr (kPipeMixed) {
-            Pair pr[2];
-            read_pair(0, pr[0]);
 #pragma unroll
-            for (int j0 = 0; j0 < TT; j0 += 2) {
-                if (j0 + 2 < TT) read_pair(j0 + 2, pr[((j0 >> 1) + 1) & 1]);
-                __builtin_amdgcn_sched_barrier(0);
-                compute_pair(j0, pr[(j0 >> 1) & 1]);
-            }
-        } else {
-#pragma unroll
-            for (int j0 = 0; j0 < TT; j0 += 2) {
-                Pair pr;
-                read_pair(j0, pr);
-                __builtin_amdgcn_sched_barrier(0);
-                compute_pair(j0, pr);
-            }
+        for (int j0 = 0; j0 < TT; j0 += 2) {
+            Pair pr;
+            read_pair(j0, pr);
+            __builtin_amdgcn_sched_barrier(0);
+            compute_pair(j0, pr);
         }
         stage_bc<N, 4, IO>(lds.bcs[(i + 1) & 1], bs, cs);
         stage(lds.dtdu[(i + 1) & 1], nxt, en);
@@ -1134,7 +1098,7 @@ void chunk_mixed_kernel(ScanArgs a, ChunkGrid g, int64_t nwhole) {
     } lds;
     const int64_t blk = blockIdx.x;
     if (blk < nwhole) {
-        output_group<N, 4, IO, SP, HAS_D, HAS_Z, kPipeMixed, false, false>(a, g, Carry{nullptr, nullptr, nullptr}, blk,
+        output_group<N, 4, IO, SP, HAS_D, HAS_Z, false, false>(a, g, Carry{nullptr, nullptr, nullptr}, blk,
                                                  lds.whole);
     } else {
         int64_t pair;
@@ -1167,7 +1131,7 @@ void chunk_local_kernel(ScanArgs a, ChunkGrid g, Carry c) {
     }
     const float dskip = HAS_D ? a.D[s.d] : 0.0f;
     float dsum = 0.0f;
-    scan_chunk<N, S, IO, SP, kPassLocal, HAS_D, HAS_Z, kPipeLocal>(s.io, s.bc, s.dbias, s.ntok, s.w, s.n0,
+    scan_chunk<N, S, IO, SP, kPassLocal, HAS_D, HAS_Z>(s.io, s.bc, s.dbias, s.ntok, s.w, s.n0,
                                                        lds, A2, h, dskip, 0.0f, dsum);
 #pragma unroll
     for (int q = 0; q < NPW; ++q) {

@@ -60,14 +60,17 @@ def test_default_bench_line():
     assert r["frac"] == pytest.approx(r["achieved"] / r["peak"], abs=1e-3)
     assert r["target_frac"] == 0.60 and r["target_met"] == (r["frac"] >= 0.60)
     assert 0.0 < r["frac"] < 1.0
-    # beside it the vector issue fraction, a transcendental at two slots
+    # beside it the vector issue fraction, one slot per fp32 operation, and
+    # the HBM fraction at full issue (transcendentals at one slot and at two)
     iss = r["issue"]
-    slots = bench.algorithmic_alu_ops(w) + bench.transcendentals(w) * elems
-    assert iss["algorithmic_slots"] == slots == (89 + 18) * elems
+    slots = bench.algorithmic_alu_ops(w)
+    assert iss["algorithmic_slots"] == slots == 89 * elems
     assert iss["frac"] == pytest.approx(slots / (d["ms_per_step"] / 1e3) / 39.3216e12, abs=1e-3)
     assert 0.0 < iss["frac"] < 1.0
     assert iss["hbm_frac_at_full_issue"] == pytest.approx(
         (nbytes / 8e12) / (slots / 39.3216e12), abs=1e-3)
+    assert iss["hbm_frac_at_full_issue_trans_at_2"] == pytest.approx(
+        (nbytes / 8e12) / ((89 + 18) * elems / 39.3216e12), abs=1e-3)
     assert r["kernel"] in ("chunk_mixed_kernel", "chunk_output_kernel")
     # traffic comes from the counters recorded for this kernel's sources, or
     # is null once those sources have changed
