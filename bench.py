@@ -471,24 +471,25 @@ def backward_alu_ops(w, softplus=False):
     """fp32 lane-operations the backward pass by recomputation must issue per
     element: the forward state update twice (once for the checkpoints, once
     to have every state while walking back: delta*A, exp, (delta*x)*B, FMA;
-    4 per state each), and per state the adjoint update (multiply, FMA), the
-    decay (multiply, exp), and the terms of dA (2 multiplies, FMA), d delta
-    (multiply, 2 FMA), dx (FMA), dB and dC (a multiply each) and the readout
-    for dz (FMA): 14 per state; per element about 20 more (delta*x, the gate
-    and its derivative, dx and readout skip terms, dD, conversions). The
-    fused activation adds softplus and its derivative (16)."""
+    4 per state each), and per state 9 in the walk back: the adjoint (FMA),
+    its decayed hand-back Abar*lam (multiply), lam*Abar*h_prev (multiply),
+    dA (FMA), the A term of d delta (FMA), sum of lam*B (FMA), the readout
+    for dz (FMA), the dB and dC terms (a multiply each); per element about
+    22 more (delta*x, dx and d delta from the sum of lam*B, the gate and its
+    derivative, dx and readout skip terms, dD, conversions). The fused
+    activation adds softplus and its derivative (16)."""
     n = w.dstate
-    per_elem = 8 * n + 14 * n + 20 + (16 if softplus else 0)
+    per_elem = 8 * n + 9 * n + 22 + (16 if softplus else 0)
     return per_elem * w.batch * w.seqlen * w.dim
 
 
 def backward_transcendentals(w, softplus=False):
     """Transcendental lane-operations per element among backward_alu_ops: the
-    exponential of each state update (twice) and of the adjoint's decay, and
-    the gate's exponential and reciprocal (sigmoid and silu share them); with
-    the fused activation softplus's exponential, logarithm and reciprocal and
-    its derivative's."""
-    return 3 * w.dstate + 2 + (4 if softplus else 0)
+    exponential of each state update (twice; the walk back reuses the
+    recomputation's decay factors), and the gate's exponential and
+    reciprocal (sigmoid and silu share them); with the fused activation
+    softplus's exponential, logarithm and reciprocal and its derivative's."""
+    return 2 * w.dstate + 2 + (4 if softplus else 0)
 
 
 def bench_backward(args, w):

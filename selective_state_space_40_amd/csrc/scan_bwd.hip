@@ -21,9 +21,14 @@
 // first, carrying lam in registers: it reads the tile's checkpoint,
 // recomputes the tile's 8 states per lane into registers (whole groups also
 // keep the tile's decay factors in LDS, so the walk back does not evaluate
-// them again) and walks the tile backwards. Tokens past the end of the
-// sequence are staged as inert ones (delta = x = g = 0, zero B and C), so the
-// forward loops need no per-token test. Sums over
+// them again) and walks the tile backwards. Walking back, the adjoint is
+// carried as m = Abar lam, what a token hands to the one before it: then
+// lam_t = C_t g_t + m is one FMA, and with lb = sum_n lam B the per-state
+// work is 9 operations (dx = D g + dt lb, d dt = sum_n A lam Abar h_{t-1} +
+// x lb). A sequence cut into chunks runs (1) for every chunk in a launch of
+// its own, from zero states, and (2) after the chunk carries are folded.
+// Tokens past the end of the sequence are staged as inert ones (delta = x =
+// g = 0, zero B and C), so the forward loops need no per-token test. Sums over
 // states (dx, d dt, p) go through LDS to the wave that finishes the token;
 // sums over channels (dB, dC) are reduced inside the wave by a butterfly of
 // lane exchanges that leaves one finished (token, state) sum in each lane,
@@ -42,6 +47,10 @@ namespace {
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 
 constexpr int kBT = 8;                         // tokens per tile
+#ifndef MAMBA_BWD_AHEAD
+#define MAMBA_BWD_AHEAD 4
+#endif
+constexpr int kAhead = MAMBA_BWD_AHEAD;        // tiles in flight in the forward passes
 constexpr int kNpw = 4;                        // states per wave
 constexpr int kVals = 2 * kBT * kNpw;          // dB and dC terms per lane per tile
 static_assert(kVals == kWave, "the butterfly leaves exactly one sum per lane");
@@ -86,7 +95,7 @@ __device__ __forceinline__ float sigmoid_f32(float v) {
 // alone; each wave here lowers its own priority (s_setprio) as it gets
 // through its work so that the waves behind are preferred and all finish
 // together. Priority 3 for the forward phase, then 2, 1 and 0 over thirds of
-// the walk back; the chunk summaries step down over quarters.
+// the walk back.
 #ifndef MAMBA_BWD_PRIO
 #define MAMBA_BWD_PRIO 1
 #endif
@@ -100,7 +109,7 @@ __device__ __forceinline__ void set_prio(int p) {
 }
 
 // Priority `top` at the first of n tiles, one lower after each of `top`
-// equal parts (`top` 2: thirds, 3: quarters).
+// equal parts (`top` 2: thirds).
 struct PrioSteps {
     int64_t b1, b2, b3;
     __device__ PrioSteps(int64_t n, int top)
@@ -129,11 +138,24 @@ struct TileRaw {
     uint32_t x[OW], dl[OW], dy[OW], z[OW];
     uint32_t bc;
     float he[kNpw];
+    float dp;   // sum of delta over the chunk before the tile (chunked walk only)
 };
 
-template <int S, int IO, bool HAS_Z, bool WANT_G>
+// Checkpoints are laid out [tile][batch row][group of 4 states][channel][4]:
+// the 64 lanes of a wave (64 channels, one group of states) write and read
+// one tile's checkpoint as 1 KB of contiguous memory, 16 bytes per lane.
+// Index of the checkpoint of states n0 .. of channel d (n0 % 4 plus the
+// count read stays within the group).
+__device__ __forceinline__ int64_t tent_index(const ScanArgs& f, int64_t tile, int64_t b, int64_t d,
+                                              int n0) {
+    const int64_t groups = (f.dstate + 3) / 4;
+    return (((tile * f.batch + b) * groups + n0 / 4) * f.dim + d) * 4 + (n0 & 3);
+}
+
+template <int S, int IO, bool HAS_Z, bool WANT_G, bool CORR = false, bool WANT_H = WANT_G>
 __device__ __forceinline__ void fetch_tile(const BwdArgs& a, const Place& pl, const float* tent,
-                                           int64_t tile, int cnt, TileRaw<S>& r) {
+                                           int64_t tile, int cnt, TileRaw<S>& r,
+                                           const float* dpre = nullptr) {
     const ScanArgs& f = a.fwd;
     const int64_t t0 = tile * kBT;
 #pragma unroll
@@ -154,11 +176,11 @@ __device__ __forceinline__ void fetch_tile(const BwdArgs& a, const Place& pl, co
     const int j = min(rr / NP, cnt - 1);
     const int n = min(rr % NP, f.dstate - 1);
     r.bc = load_raw<IO>(which ? f.C : f.B, (pl.b * f.seqlen + t0 + j) * f.dstate + n);
-    if constexpr (WANT_G) {
-        const int N = f.dstate;
-        const float* row = tent + ((tile * f.batch + pl.b) * f.dim + pl.d) * N;
+    if constexpr (WANT_H) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(tent + tent_index(f, tile, pl.b, pl.d, pl.n0));
 #pragma unroll
-        for (int q = 0; q < kNpw; ++q) r.he[q] = row[min(pl.n0 + q, N - 1)];
+        for (int q = 0; q < kNpw; ++q) r.he[q] = v[q];
+        if constexpr (CORR) r.dp = dpre[(tile * f.batch + pl.b) * f.dim + pl.d];
     }
 }
 
@@ -289,7 +311,20 @@ struct BwdWs {
     int64_t chunk_len;
     const float* hin;
     const float* rho;
+    // the split chunked plan: the forward pass from zero states writes each
+    // chunk's end state and decay product (chunks 0 .. nchunks-2) for the
+    // fold, and per tile the sum of delta over the chunk before it
+    float* fend;
+    float* fdecay;
+    float* dpre;
 };
+
+// What a whole-group workgroup runs: the forward pass and the walk back (a
+// whole sequence), the forward pass alone from a zero state, or the walk
+// back alone over checkpoints that the chunk's entering state still has to
+// be added to (a chunked sequence, whose forward passes run in an earlier
+// launch).
+enum BwdMode { kBwdBoth = 0, kBwdForward = 1, kBwdWalk = 2 };
 
 // Place of a whole-group thread: batch row and channel group from the
 // workgroup's index within its chunk, its wave's states, its channel.
@@ -307,7 +342,7 @@ __device__ __forceinline__ Place make_place(const ScanArgs& f, int64_t ngroups, 
     return pl;
 }
 
-template <int S, int IO, bool SP, bool HAS_D, bool HAS_Z>
+template <int S, int IO, bool SP, bool HAS_D, bool HAS_Z, int MODE = kBwdBoth>
 __device__ __forceinline__ void bwd_whole_group(const BwdArgs& a, int64_t ngroups, int64_t blk,
                                                 const BwdWs& ws, BwdLds<S>& lds) {
     constexpr int OW = (kBT + S - 1) / S;
@@ -336,78 +371,119 @@ __device__ __forceinline__ void bwd_whole_group(const BwdArgs& a, int64_t ngroup
     const float* lam_in = last_chunk ? a.dhL
                                      : ws.rho + (ws.nchunks - 1 - chunk) * f.batch * f.dim * N;
     bool sv[kNpw];      // state exists (not padding)
-    float A[kNpw], A2[kNpw], lam[kNpw], en[kNpw], dA[kNpw];
+    // m: Abar lam of the token after the one being walked (what that token
+    // hands back), at the chunk's end the adjoint taken in from the right
+    float A[kNpw], A2[kNpw], m[kNpw], dA[kNpw];
 #pragma unroll
     for (int q = 0; q < kNpw; ++q) {
         const int n = pl.n0 + q;
         sv[q] = n < N;
         A[q] = sv[q] ? f.A[pl.d * N + n] : 0.0f;
         A2[q] = A[q] * kLog2e;
-        lam[q] = (sv[q] && lam_in != nullptr) ? lam_in[col0 + n] : 0.0f;
-        en[q] = 1.0f;
+        m[q] = (sv[q] && lam_in != nullptr) ? lam_in[col0 + n] : 0.0f;
         dA[q] = 0.0f;
     }
     float dD_acc = 0.0f, dbias_acc = 0.0f;
     Own own[OW];
 
-    // (1) forward over the chunk from its entering state, keeping the state
-    // entering every tile in the workspace (only real lanes and states write)
-    {
-        const float* h_in = chunk == 0 ? f.h0 : ws.hin + chunk * f.batch * f.dim * N;
+    // (1) forward over the chunk from its entering state (alone: from a zero
+    // state after chunk 0), keeping the state entering every tile in the
+    // workspace (only real lanes and states write)
+    if constexpr (MODE != kBwdWalk) {
+        const float* h_in = chunk == 0 ? f.h0
+                          : MODE == kBwdForward ? nullptr
+                                                : ws.hin + chunk * f.batch * f.dim * N;
         float h[kNpw];
 #pragma unroll
         for (int q = 0; q < kNpw; ++q)
             h[q] = (sv[q] && h_in != nullptr) ? h_in[col0 + pl.n0 + q] : 0.0f;
-        TileRaw<S> raw;
-        fetch_tile<S, IO, HAS_Z, false>(a, pl, tent, i_first,
-                                        static_cast<int>(min<int64_t>(kBT, L - i_first * kBT)), raw);
+        float dsum = 0.0f;
+        // tiles are fetched kAhead ahead: the pass does little arithmetic per
+        // tile, so one tile of it does not cover the latency of HBM
+        TileRaw<S> raw[kAhead];
+#pragma unroll
+        for (int u = 0; u < kAhead; ++u) {
+            const int64_t nx = min(i_first + u, i_end - 1);
+            fetch_tile<S, IO, HAS_Z, false>(a, pl, tent, nx,
+                                            static_cast<int>(min<int64_t>(kBT, L - nx * kBT)), raw[u]);
+        }
         set_prio(3);
-        for (int64_t i = i_first; i < i_end; ++i) {
-            const int64_t t0 = i * kBT;
-            const int cnt = static_cast<int>(min<int64_t>(kBT, L - t0));
-            if (pl.valid) {
-                float* row = tent + ((i * f.batch + pl.b) * f.dim + pl.d) * N + pl.n0;
+        for (int64_t i0 = i_first; i0 < i_end; i0 += kAhead) {
 #pragma unroll
-                for (int q = 0; q < kNpw; ++q)
-                    if (sv[q]) row[q] = h[q];
-            }
-            put_tile<S, IO, SP, HAS_Z, false>(raw, pl, lds, cnt, N, own);
-            __syncthreads();
-            {
-                // the last tile fetches itself again (unused)
-                const int64_t nx = min(i + 1, i_end - 1);
-                fetch_tile<S, IO, HAS_Z, false>(a, pl, tent, nx,
-                                                static_cast<int>(min<int64_t>(kBT, L - nx * kBT)), raw);
-            }
-#pragma unroll
-            for (int j0 = 0; j0 < kBT; j0 += 2) {
-                float2 v[2];
-                f32x4 bq[2];
-#pragma unroll
-                for (int jj = 0; jj < 2; ++jj) {
-                    v[jj] = lds.dtx[j0 + jj][lane];
-                    bq[jj] = *reinterpret_cast<const f32x4*>(&lds.bc[0][j0 + jj][pl.n0]);
+            for (int u = 0; u < kAhead; ++u) {
+                const int64_t i = i0 + u;
+                if (i >= i_end) break;
+                const int64_t t0 = i * kBT;
+                const int cnt = static_cast<int>(min<int64_t>(kBT, L - t0));
+                if (pl.valid) {
+                    // padding states hold zero
+                    *reinterpret_cast<f32x4*>(tent + tent_index(f, i, pl.b, pl.d, pl.n0)) =
+                        f32x4{h[0], h[1], h[2], h[3]};
+                    if constexpr (MODE == kBwdForward)
+                        if (pl.w == 0) ws.dpre[(i * f.batch + pl.b) * f.dim + pl.d] = dsum;
                 }
-                __builtin_amdgcn_sched_barrier(0);
+                put_tile<S, IO, SP, HAS_Z, false>(raw[u], pl, lds, cnt, N, own);
+                __syncthreads();
+                {
+                    // the last tiles fetch the last one again (unused)
+                    const int64_t nx = min(i + kAhead, i_end - 1);
+                    fetch_tile<S, IO, HAS_Z, false>(a, pl, tent, nx,
+                                                    static_cast<int>(min<int64_t>(kBT, L - nx * kBT)),
+                                                    raw[u]);
+                }
 #pragma unroll
-                for (int jj = 0; jj < 2; ++jj) {
-                    const float du = v[jj].x * v[jj].y;
+                for (int j0 = 0; j0 < kBT; j0 += 2) {
+                    float2 v[2];
+                    f32x4 bq[2];
 #pragma unroll
-                    for (int q = 0; q < kNpw; ++q)
-                        h[q] = fmaf(fast_exp2(v[jj].x * A2[q]), h[q], du * bq[jj][q]);
+                    for (int jj = 0; jj < 2; ++jj) {
+                        v[jj] = lds.dtx[j0 + jj][lane];
+                        bq[jj] = *reinterpret_cast<const f32x4*>(&lds.bc[0][j0 + jj][pl.n0]);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int jj = 0; jj < 2; ++jj) {
+                        const float du = v[jj].x * v[jj].y;
+                        if constexpr (MODE == kBwdForward) dsum += v[jj].x;
+#pragma unroll
+                        for (int q = 0; q < kNpw; ++q)
+                            h[q] = fmaf(fast_exp2(v[jj].x * A2[q]), h[q], du * bq[jj][q]);
+                    }
+                }
+                __syncthreads();
+            }
+        }
+        if constexpr (MODE == kBwdForward) {
+            // the chunk's summary for the fold: end state from the zero (or
+            // initial) state and decay product
+            if (!last_chunk && pl.valid) {
+                const int64_t at = chunk * f.batch * f.dim * N + col0 + pl.n0;
+#pragma unroll
+                for (int q = 0; q < kNpw; ++q) {
+                    if (sv[q]) {
+                        ws.fend[at + q] = h[q];
+                        ws.fdecay[at + q] = fast_exp2(A2[q] * dsum);
+                    }
                 }
             }
-            __syncthreads();
+            return;
         }
     }
 
-    // (2) the tiles in reverse
+    // (2) the tiles in reverse. Walking alone, a chunk after the first adds
+    // its entering state, decayed to the tile, to each checkpoint.
     {
+        constexpr bool CORR = MODE == kBwdWalk;
+        float hin[kNpw];
+#pragma unroll
+        for (int q = 0; q < kNpw; ++q)
+            hin[q] = (CORR && chunk > 0 && sv[q] && pl.valid) ? ws.hin[chunk * f.batch * f.dim * N + col0 + pl.n0 + q]
+                                                  : 0.0f;
         float h[kNpw];
         TileRaw<S> raw;
-        fetch_tile<S, IO, HAS_Z, true>(a, pl, tent, i_end - 1,
-                                       static_cast<int>(min<int64_t>(kBT, L - (i_end - 1) * kBT)),
-                                       raw);
+        fetch_tile<S, IO, HAS_Z, true, CORR>(a, pl, tent, i_end - 1,
+                                             static_cast<int>(min<int64_t>(kBT, L - (i_end - 1) * kBT)),
+                                             raw, ws.dpre);
         const PrioSteps prio(i_end - i_first, 2);
         for (int64_t i = i_end - 1; i >= i_first; --i) {
             prio.at(i_end - 1 - i, 2);
@@ -418,13 +494,20 @@ __device__ __forceinline__ void bwd_whole_group(const BwdArgs& a, int64_t ngroup
             float he[kNpw], hs[kBT][kNpw];
 #pragma unroll
             for (int q = 0; q < kNpw; ++q) he[q] = (pl.valid && sv[q]) ? raw.he[q] : 0.0f;
+            if constexpr (CORR) {
+                if (chunk > 0) {
+#pragma unroll
+                    for (int q = 0; q < kNpw; ++q) he[q] = fmaf(fast_exp2(A2[q] * raw.dp), hin[q], he[q]);
+                }
+            }
             put_tile<S, IO, SP, HAS_Z, true>(raw, pl, lds, cnt, N, own);
             __syncthreads();
             // the chunk's first tile fetches itself again (unused)
             {
                 const int64_t pv = i > i_first ? i - 1 : i_first;
-                fetch_tile<S, IO, HAS_Z, true>(a, pl, tent, pv,
-                                               static_cast<int>(min<int64_t>(kBT, L - pv * kBT)), raw);
+                fetch_tile<S, IO, HAS_Z, true, CORR>(a, pl, tent, pv,
+                                                     static_cast<int>(min<int64_t>(kBT, L - pv * kBT)),
+                                                     raw, ws.dpre);
             }
 
 #pragma unroll
@@ -480,26 +563,26 @@ __device__ __forceinline__ void bwd_whole_group(const BwdArgs& a, int64_t ngroup
                 if (j < cnt) {
                     const float dt = vv[jj].x, x = vv[jj].y;
                     const float gg = gq[jj];
-                    float dxp = 0.0f, ddp = 0.0f, pp = 0.0f;
+                    const float dtx = dt * x;
+                    float lb = 0.0f, dap = 0.0f, pp = 0.0f;
 #pragma unroll
                     for (int q = 0; q < kNpw; ++q) {
                         const float Bq = bq[jj][q];
                         const float Cq = cq[jj][q];
-                        lam[q] = fmaf(en[q], lam[q], Cq * gg);
-                        const float e = eq[jj][q];
+                        const float lam = fmaf(Cq, gg, m[q]);
                         const float hprev = j > 0 ? hs[j > 0 ? j - 1 : 0][q] : he[q];
-                        const float eh = e * hprev;
-                        const float ldt = lam[q] * dt;
-                        dA[q] = fmaf(ldt, eh, dA[q]);
-                        ddp = fmaf(lam[q], fmaf(A[q], eh, Bq * x), ddp);
-                        dxp = fmaf(ldt, Bq, dxp);
+                        m[q] = eq[jj][q] * lam;
+                        const float le = m[q] * hprev;   // lam Abar h_{t-1}
+                        dA[q] = fmaf(dt, le, dA[q]);
+                        dap = fmaf(A[q], le, dap);
+                        lb = fmaf(lam, Bq, lb);
                         pp = fmaf(Cq, hs[j][q], pp);
-                        vals[j * kNpw + q] = ldt * x;
+                        vals[j * kNpw + q] = lam * dtx;
                         vals[kBT * kNpw + j * kNpw + q] = gg * hs[j][q];
-                        en[q] = e;
                     }
-                    lds.slot[pl.w][j][lane] = dxp;
-                    lds.slot[pl.w][j][kWave + lane] = ddp;
+                    // sum_n lam dt B = dt lb; sum_n lam (A Abar h_{t-1} + B x) = dap + x lb
+                    lds.slot[pl.w][j][lane] = dt * lb;
+                    lds.slot[pl.w][j][kWave + lane] = fmaf(x, lb, dap);
                     lds.slot[pl.w][j][2 * kWave + lane] = pp;
                 }
               }
@@ -564,7 +647,7 @@ __device__ __forceinline__ void bwd_whole_group(const BwdArgs& a, int64_t ngroup
         for (int q = 0; q < kNpw; ++q) {
             if (sv[q]) {
                 const int64_t col = (pl.b * f.dim + pl.d) * N + pl.n0 + q;
-                if (chunk == 0 && a.dh0 != nullptr) a.dh0[col] = en[q] * lam[q];
+                if (chunk == 0 && a.dh0 != nullptr) a.dh0[col] = m[q];
                 part_a[(prow * f.dim + pl.d) * N + pl.n0 + q] = dA[q];
             }
         }
@@ -596,72 +679,11 @@ __device__ __forceinline__ void bwd_whole_group(const BwdArgs& a, int64_t ngroup
 // there, is P_c rho + l_c with rho what it takes in and l_c the same walked
 // back from zero. Each chunk is summarised, and the summaries are folded in
 // order (forward for the states, from the last chunk back for the adjoint).
-
-// State summary of chunks 0 .. nchunks-2 (whole tiles): end state from a
-// zero start (chunk 0 from h0) and decay product, [chunk][b][d][n].
-template <int S, int IO, bool SP>
-__device__ __forceinline__ void bwd_state_summary(const BwdArgs& a, int64_t ngroups,
-                                                  const BwdWs& ws, float* end, float* decay,
-                                                  int64_t blk, BwdLds<S>& lds) {
-    const ScanArgs& f = a.fwd;
-    const int N = f.dstate;
-    const int lane = threadIdx.x & (kWave - 1);
-    const int64_t rows = f.batch * ngroups;
-    const int64_t chunk = blk / rows;
-    const Place pl = make_place(f, ngroups, blk - chunk * rows);
-    const int64_t i_first = chunk * (ws.chunk_len / kBT), i_end = i_first + ws.chunk_len / kBT;
-    const int64_t col0 = (pl.b * f.dim + pl.d) * N;
-    bool sv[kNpw];
-    float A2[kNpw], h[kNpw];
-#pragma unroll
-    for (int q = 0; q < kNpw; ++q) {
-        const int n = pl.n0 + q;
-        sv[q] = n < N;
-        A2[q] = sv[q] ? f.A[pl.d * N + n] * kLog2e : 0.0f;
-        h[q] = (chunk == 0 && sv[q] && f.h0 != nullptr) ? f.h0[col0 + n] : 0.0f;
-    }
-    float dsum = 0.0f;
-    Own own[(kBT + S - 1) / S];
-    TileRaw<S> raw;
-    fetch_tile<S, IO, false, false>(a, pl, ws.tent, i_first, kBT, raw);
-    const PrioSteps prio(i_end - i_first, 3);
-    for (int64_t i = i_first; i < i_end; ++i) {
-        prio.at(i - i_first, 3);
-        put_tile<S, IO, SP, false, false>(raw, pl, lds, kBT, N, own);
-        __syncthreads();
-        fetch_tile<S, IO, false, false>(a, pl, ws.tent, min(i + 1, i_end - 1), kBT, raw);
-#pragma unroll
-        for (int j0 = 0; j0 < kBT; j0 += 2) {
-            float2 v[2];
-            f32x4 bq[2];
-#pragma unroll
-            for (int jj = 0; jj < 2; ++jj) {
-                v[jj] = lds.dtx[j0 + jj][lane];
-                bq[jj] = *reinterpret_cast<const f32x4*>(&lds.bc[0][j0 + jj][pl.n0]);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int jj = 0; jj < 2; ++jj) {
-                const float du = v[jj].x * v[jj].y;
-                dsum += v[jj].x;
-#pragma unroll
-                for (int q = 0; q < kNpw; ++q)
-                    h[q] = fmaf(fast_exp2(v[jj].x * A2[q]), h[q], du * bq[jj][q]);
-            }
-        }
-        __syncthreads();
-    }
-    if (pl.valid) {
-        const int64_t at = chunk * f.batch * f.dim * N + col0 + pl.n0;
-#pragma unroll
-        for (int q = 0; q < kNpw; ++q) {
-            if (sv[q]) {
-                end[at + q] = h[q];
-                decay[at + q] = fast_exp2(A2[q] * dsum);
-            }
-        }
-    }
-}
+// The state summaries come from the forward pass itself: it runs every chunk
+// from a zero state, so its checkpoints lack the entering state h, which at
+// the checkpoint of tile i has decayed to exp(A * s_i) h, s_i the sum of
+// delta over the chunk before the tile; the walk back, launched after the
+// folds, adds that term to each checkpoint it reads.
 
 // Adjoint summary of chunks 1 .. nchunks-1, walked back from a zero adjoint
 // (the last chunk from dhL): what the chunk hands to its left neighbour and
@@ -694,45 +716,55 @@ __device__ __forceinline__ void bwd_adjoint_summary(const BwdArgs& a, int64_t ng
     }
     float dsum = 0.0f;
     Own own[(kBT + S - 1) / S];
-    TileRaw<S> raw;
-    fetch_tile<S, IO, HAS_Z, true>(a, pl, ws.tent, i_end - 1,
-                                   static_cast<int>(min<int64_t>(kBT, L - (i_end - 1) * kBT)), raw);
-    const PrioSteps prio(i_end - i_first, 3);
-    for (int64_t i = i_end - 1; i >= i_first; --i) {
-        prio.at(i_end - 1 - i, 3);
-        // tokens past the end of the sequence are staged inert (g = delta = 0,
-        // zero C rows): they leave lam, en and the sum unchanged
-        put_tile<S, IO, SP, HAS_Z, true>(raw, pl, lds, static_cast<int>(min<int64_t>(kBT, L - i * kBT)),
-                                         N, own);
-        __syncthreads();
-        {
-            const int64_t pv = i > i_first ? i - 1 : i_first;
-            fetch_tile<S, IO, HAS_Z, true>(a, pl, ws.tent, pv,
-                                           static_cast<int>(min<int64_t>(kBT, L - pv * kBT)), raw);
-        }
+    // tiles fetched kAhead ahead, as in the forward pass (without the
+    // checkpoints, which the summary does not read)
+    TileRaw<S> raw[kAhead];
 #pragma unroll
-        for (int j1 = kBT - 1; j1 >= 0; j1 -= 2) {
-            float2 vv[2];
-            float gq[2];
-            f32x4 cq[2];
+    for (int u = 0; u < kAhead; ++u) {
+        const int64_t pv = max(i_end - 1 - u, i_first);
+        fetch_tile<S, IO, HAS_Z, true, false, false>(
+            a, pl, ws.tent, pv, static_cast<int>(min<int64_t>(kBT, L - pv * kBT)), raw[u]);
+    }
+    for (int64_t i0 = i_end - 1; i0 >= i_first; i0 -= kAhead) {
 #pragma unroll
-            for (int jj = 0; jj < 2; ++jj) {
-                vv[jj] = lds.dtx[j1 - jj][lane];
-                gq[jj] = lds.g[j1 - jj][lane];
-                cq[jj] = *reinterpret_cast<const f32x4*>(&lds.bc[1][j1 - jj][pl.n0]);
+        for (int u = 0; u < kAhead; ++u) {
+            const int64_t i = i0 - u;
+            if (i < i_first) break;
+            // tokens past the end of the sequence are staged inert (g = delta
+            // = 0, zero C rows): they leave lam, en and the sum unchanged
+            put_tile<S, IO, SP, HAS_Z, true>(raw[u], pl, lds,
+                                             static_cast<int>(min<int64_t>(kBT, L - i * kBT)), N, own);
+            __syncthreads();
+            {
+                // the first tiles fetch the first one again (unused)
+                const int64_t pv = max(i - kAhead, i_first);
+                fetch_tile<S, IO, HAS_Z, true, false, false>(
+                    a, pl, ws.tent, pv, static_cast<int>(min<int64_t>(kBT, L - pv * kBT)), raw[u]);
             }
-            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int jj = 0; jj < 2; ++jj) {
-                dsum += vv[jj].x;
+            for (int j1 = kBT - 1; j1 >= 0; j1 -= 2) {
+                float2 vv[2];
+                float gq[2];
+                f32x4 cq[2];
 #pragma unroll
-                for (int q = 0; q < kNpw; ++q) {
-                    lam[q] = fmaf(en[q], lam[q], cq[jj][q] * gq[jj]);
-                    en[q] = fast_exp2(vv[jj].x * A2[q]);
+                for (int jj = 0; jj < 2; ++jj) {
+                    vv[jj] = lds.dtx[j1 - jj][lane];
+                    gq[jj] = lds.g[j1 - jj][lane];
+                    cq[jj] = *reinterpret_cast<const f32x4*>(&lds.bc[1][j1 - jj][pl.n0]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int jj = 0; jj < 2; ++jj) {
+                    dsum += vv[jj].x;
+#pragma unroll
+                    for (int q = 0; q < kNpw; ++q) {
+                        lam[q] = fmaf(en[q], lam[q], cq[jj][q] * gq[jj]);
+                        en[q] = fast_exp2(vv[jj].x * A2[q]);
+                    }
                 }
             }
+            __syncthreads();
         }
-        __syncthreads();
     }
     if (pl.valid) {
         const int64_t at = (ws.nchunks - 1 - chunk) * f.batch * f.dim * N + col0 + pl.n0;
@@ -746,23 +778,9 @@ __device__ __forceinline__ void bwd_adjoint_summary(const BwdArgs& a, int64_t ng
     }
 }
 
-// Both summaries in one launch (they are independent): blocks [0, per)
-// summarise the states of chunks 0 .. nchunks-2, blocks [per, 2 per) the
-// adjoints of chunks 1 .. nchunks-1.
 struct BwdCarry {
     float *fend, *fdecay, *fstart, *rend, *rdecay, *rstart;
 };
-
-template <int S, int IO, bool SP, bool HAS_Z>
-__global__ __launch_bounds__(kWave * S) void bwd_summary_kernel(BwdArgs a, int64_t ngroups,
-                                                                BwdWs ws, BwdCarry c, int64_t per) {
-    __shared__ BwdLds<S> lds;
-    const int64_t blk = blockIdx.x;
-    if (blk < per)
-        bwd_state_summary<S, IO, SP>(a, ngroups, ws, c.fend, c.fdecay, blk, lds);
-    else
-        bwd_adjoint_summary<S, IO, SP, HAS_Z>(a, ngroups, ws, c.rend, c.rdecay, blk - per, lds);
-}
 
 // One thread per (b, d, n) column folds the summaries in order: start[k] =
 // what enters summary k, k = 1 .. nchunks-1 (entry 0 is the first one's own);
@@ -828,15 +846,15 @@ __device__ __forceinline__ void bwd_half_group(const BwdArgs& a, int64_t ngroups
     const int64_t slot = side == 0 ? grp : ngroups + grp;
 
     bool sv[kHalfNps];
-    float A[kHalfNps], A2[kHalfNps], lam[kHalfNps], en[kHalfNps], dA[kHalfNps];
+    // m: Abar lam of the token after the one being walked, dhL at the end
+    float A[kHalfNps], A2[kHalfNps], m[kHalfNps], dA[kHalfNps];
 #pragma unroll
     for (int q = 0; q < kHalfNps; ++q) {
         const int n = n0 + q;
         sv[q] = n < N;
         A[q] = sv[q] ? f.A[d * N + n] : 0.0f;
         A2[q] = A[q] * kLog2e;
-        lam[q] = (sv[q] && a.dhL != nullptr) ? a.dhL[(b * f.dim + d) * N + n] : 0.0f;
-        en[q] = 1.0f;
+        m[q] = (sv[q] && a.dhL != nullptr) ? a.dhL[(b * f.dim + d) * N + n] : 0.0f;
         dA[q] = 0.0f;
     }
     float dD_acc = 0.0f, dbias_acc = 0.0f;
@@ -867,9 +885,9 @@ __device__ __forceinline__ void bwd_half_group(const BwdArgs& a, int64_t ngroups
         const int n = min(rr % NP, N - 1);
         r.bc = load_raw<IO>(which ? f.C : f.B, (b * L + t0 + jb) * N + n);
         if constexpr (WANT_G) {
-            const float* row = ws.tent + ((tile * f.batch + b) * f.dim + d) * N;
-#pragma unroll
-            for (int q = 0; q < kHalfNps; ++q) r.he[q] = row[min(n0 + q, N - 1)];
+            const float2 v = *reinterpret_cast<const float2*>(ws.tent + tent_index(f, tile, b, d, n0));
+            r.he[0] = v.x;
+            r.he[1] = v.y;
         }
     };
     auto put = [&](auto want_g, const Raw& r, int cnt) {
@@ -916,12 +934,8 @@ __device__ __forceinline__ void bwd_half_group(const BwdArgs& a, int64_t ngroups
         for (int64_t i = 0; i < ntiles; ++i) {
             const int64_t t0 = i * kBT;
             const int cnt = static_cast<int>(min<int64_t>(kBT, L - t0));
-            if (valid) {
-                float* row = ws.tent + ((i * f.batch + b) * f.dim + d) * N + n0;
-#pragma unroll
-                for (int q = 0; q < kHalfNps; ++q)
-                    if (sv[q]) row[q] = h[q];
-            }
+            if (valid)   // padding states hold zero
+                *reinterpret_cast<float2*>(ws.tent + tent_index(f, i, b, d, n0)) = make_float2(h[0], h[1]);
             put(No{}, raw, cnt);
             __syncthreads();
             {
@@ -1009,24 +1023,23 @@ __device__ __forceinline__ void bwd_half_group(const BwdArgs& a, int64_t ngroups
                         const float gg = gq[jj];
                         const float Bv[kHalfNps] = {bq[jj].x, bq[jj].y};
                         const float Cv[kHalfNps] = {cq[jj].x, cq[jj].y};
-                        float dxp = 0.0f, ddp = 0.0f, pp = 0.0f;
+                        const float dtx = dt * x;
+                        float lb = 0.0f, dap = 0.0f, pp = 0.0f;
 #pragma unroll
                         for (int q = 0; q < kHalfNps; ++q) {
-                            lam[q] = fmaf(en[q], lam[q], Cv[q] * gg);
-                            const float e = fast_exp2(dt * A2[q]);
+                            const float lam = fmaf(Cv[q], gg, m[q]);
                             const float hprev = j > 0 ? hs[j > 0 ? j - 1 : 0][q] : he[q];
-                            const float eh = e * hprev;
-                            const float ldt = lam[q] * dt;
-                            dA[q] = fmaf(ldt, eh, dA[q]);
-                            ddp = fmaf(lam[q], fmaf(A[q], eh, Bv[q] * x), ddp);
-                            dxp = fmaf(ldt, Bv[q], dxp);
+                            m[q] = fast_exp2(dt * A2[q]) * lam;
+                            const float le = m[q] * hprev;
+                            dA[q] = fmaf(dt, le, dA[q]);
+                            dap = fmaf(A[q], le, dap);
+                            lb = fmaf(lam, Bv[q], lb);
                             pp = fmaf(Cv[q], hs[j][q], pp);
-                            vals[j * kHalfNps + q] = ldt * x;
+                            vals[j * kHalfNps + q] = lam * dtx;
                             vals[kBT * kHalfNps + j * kHalfNps + q] = gg * hs[j][q];
-                            en[q] = e;
                         }
-                        lds.red[0][v][j][ch] = dxp;
-                        lds.red[1][v][j][ch] = ddp;
+                        lds.red[0][v][j][ch] = dt * lb;
+                        lds.red[1][v][j][ch] = fmaf(x, lb, dap);
                         lds.red[2][v][j][ch] = pp;
                     }
                 }
@@ -1083,7 +1096,7 @@ __device__ __forceinline__ void bwd_half_group(const BwdArgs& a, int64_t ngroups
         for (int q = 0; q < kHalfNps; ++q) {
             if (sv[q]) {
                 const int64_t col = (b * f.dim + d) * N + n0 + q;
-                if (a.dh0 != nullptr) a.dh0[col] = en[q] * lam[q];
+                if (a.dh0 != nullptr) a.dh0[col] = m[q];
                 ws.part_a[col] = dA[q];
             }
         }
@@ -1127,11 +1140,28 @@ void scan_bwd_mixed_kernel(BwdArgs a, int64_t ngroups, int64_t nwhole, BwdWs ws)
     }
 }
 
-template <int S, int IO, bool SP, bool HAS_D, bool HAS_Z>
+template <int S, int IO, bool SP, bool HAS_D, bool HAS_Z, int MODE>
 __global__ __launch_bounds__(kWave * S) __attribute__((amdgpu_waves_per_eu(S == 4 ? 3 : 1)))
 void scan_bwd_kernel(BwdArgs a, int64_t ngroups, BwdWs ws) {
     __shared__ BwdLds<S> lds;
-    bwd_whole_group<S, IO, SP, HAS_D, HAS_Z>(a, ngroups, blockIdx.x, ws, lds);
+    bwd_whole_group<S, IO, SP, HAS_D, HAS_Z, MODE>(a, ngroups, blockIdx.x, ws, lds);
+}
+
+// A chunked sequence, first launch: blocks [0, nfwd) run the forward pass of
+// every (chunk, row, group) from a zero state (chunk 0 from h0), writing the
+// checkpoints, the tiles' delta sums and the chunk summaries of the states;
+// the blocks after them summarise the adjoints of chunks 1 .. nchunks-1.
+// Both are independent of the carries, which are folded after this launch.
+template <int S, int IO, bool SP, bool HAS_Z>
+__global__ __launch_bounds__(kWave * S) void bwd_forward_kernel(BwdArgs a, int64_t ngroups,
+                                                                BwdWs ws, BwdCarry c,
+                                                                int64_t nfwd) {
+    __shared__ BwdLds<S> lds;
+    const int64_t blk = blockIdx.x;
+    if (blk < nfwd)
+        bwd_whole_group<S, IO, SP, false, false, kBwdForward>(a, ngroups, blk, ws, lds);
+    else
+        bwd_adjoint_summary<S, IO, SP, HAS_Z>(a, ngroups, ws, c.rend, c.rdecay, blk - nfwd, lds);
 }
 
 // dB and dC: the partials of all channel groups added in group order, a
@@ -1243,6 +1273,7 @@ struct BwdLayout {
     int64_t ntiles, ngroups, nslots, nchunks, chunk_len;
     size_t tent, part_bc, part_a, part_d, part_bias;          // float offsets
     size_t fend, fdecay, fstart, rend, rdecay, rstart;        // chunk carries (nchunks > 1)
+    size_t dpre;                                              // [tile][b][d] (nchunks > 1)
     size_t total;                                             // float count
 };
 
@@ -1264,8 +1295,8 @@ BwdLayout bwd_layout(int64_t batch, int64_t seqlen, int64_t dim, int dstate, int
     l.nslots = bwd_halvable(dstate) && l.nchunks == 1 ? 2 * l.ngroups : l.ngroups;
     const size_t states = static_cast<size_t>(batch) * dim * dstate;
     size_t off = 0;
-    l.tent = off;
-    off += round64(static_cast<size_t>(l.ntiles) * states);
+    l.tent = off;   // states padded to whole groups of 4
+    off += round64(static_cast<size_t>(l.ntiles) * batch * dim * ((dstate + 3) / 4 * 4));
     l.part_bc = off;
     off += round64(2 * static_cast<size_t>(l.nslots) * batch * seqlen * dstate);
     const size_t nc = static_cast<size_t>(l.nchunks);
@@ -1288,6 +1319,8 @@ BwdLayout bwd_layout(int64_t batch, int64_t seqlen, int64_t dim, int dstate, int
     off += carry;
     l.rstart = off;
     off += carry;
+    l.dpre = off;
+    off += l.nchunks > 1 ? round64(static_cast<size_t>(l.ntiles) * batch * dim) : 0;
     l.total = off;
     return l;
 }
@@ -1297,7 +1330,8 @@ hipError_t launch_bwd_main(const BwdArgs& a, const BwdLayout& l, float* ws, hipS
     const int64_t groups = a.fwd.batch * l.ngroups;
     const bool has_d = a.fwd.D != nullptr, has_z = a.fwd.z != nullptr;
     const BwdWs w{ws + l.tent, ws + l.part_bc, ws + l.part_a, ws + l.part_d, ws + l.part_bias,
-                  l.nslots, l.nchunks, l.chunk_len, ws + l.fstart, ws + l.rstart};
+                  l.nslots, l.nchunks, l.chunk_len, ws + l.fstart, ws + l.rstart,
+                  ws + l.fend, ws + l.fdecay, ws + l.dpre};
     if constexpr (S == 4) {
         if (a.halves > 0) {
             const int64_t nwhole = groups - a.halves;
@@ -1312,30 +1346,39 @@ hipError_t launch_bwd_main(const BwdArgs& a, const BwdLayout& l, float* ws, hipS
             return hipGetLastError();
         }
     }
-    if (l.nchunks > 1) {
-        // the chunk carries: states forward, adjoints backward
-        const int64_t columns = a.fwd.batch * a.fwd.dim * a.fwd.dstate;
-        const int64_t per = (l.nchunks - 1) * groups;
-        const BwdCarry c{ws + l.fend, ws + l.fdecay, ws + l.fstart,
-                         ws + l.rend, ws + l.rdecay, ws + l.rstart};
-        const dim3 grid(2 * per), block(kWave * S);
-        if (has_z)
-            hipLaunchKernelGGL((bwd_summary_kernel<S, IO, SP, true>), grid, block, 0, s, a,
-                               l.ngroups, w, c, per);
-        else
-            hipLaunchKernelGGL((bwd_summary_kernel<S, IO, SP, false>), grid, block, 0, s, a,
-                               l.ngroups, w, c, per);
-        hipLaunchKernelGGL(bwd_fold_kernel, dim3(stride_blocks(2 * columns)), dim3(256), 0, s,
-                           columns, l.nchunks, c);
-    }
     auto go = [&](auto kernel) {
         hipLaunchKernelGGL(kernel, dim3(l.nchunks * groups), dim3(kWave * S), 0, s, a, l.ngroups,
                            w);
     };
-    if (has_d && has_z) go(scan_bwd_kernel<S, IO, SP, true, true>);
-    else if (has_d) go(scan_bwd_kernel<S, IO, SP, true, false>);
-    else if (has_z) go(scan_bwd_kernel<S, IO, SP, false, true>);
-    else go(scan_bwd_kernel<S, IO, SP, false, false>);
+    if (l.nchunks == 1) {
+        if (has_d && has_z) go(scan_bwd_kernel<S, IO, SP, true, true, kBwdBoth>);
+        else if (has_d) go(scan_bwd_kernel<S, IO, SP, true, false, kBwdBoth>);
+        else if (has_z) go(scan_bwd_kernel<S, IO, SP, false, true, kBwdBoth>);
+        else go(scan_bwd_kernel<S, IO, SP, false, false, kBwdBoth>);
+        return hipGetLastError();
+    }
+    // a chunked sequence: the forward pass of every chunk from a zero state
+    // and the adjoint summaries, the two folds (states forward, adjoints
+    // backward), then the walk back of every chunk, which adds the folded
+    // entering state to its checkpoints
+    const int64_t columns = a.fwd.batch * a.fwd.dim * a.fwd.dstate;
+    const int64_t nfwd = l.nchunks * groups;
+    const int64_t nadj = (l.nchunks - 1) * groups;
+    const BwdCarry c{ws + l.fend, ws + l.fdecay, ws + l.fstart,
+                     ws + l.rend, ws + l.rdecay, ws + l.rstart};
+    const dim3 grid(nfwd + nadj), block(kWave * S);
+    if (has_z)
+        hipLaunchKernelGGL((bwd_forward_kernel<S, IO, SP, true>), grid, block, 0, s, a, l.ngroups,
+                           w, c, nfwd);
+    else
+        hipLaunchKernelGGL((bwd_forward_kernel<S, IO, SP, false>), grid, block, 0, s, a, l.ngroups,
+                           w, c, nfwd);
+    hipLaunchKernelGGL(bwd_fold_kernel, dim3(stride_blocks(2 * columns)), dim3(256), 0, s, columns,
+                       l.nchunks, c);
+    if (has_d && has_z) go(scan_bwd_kernel<S, IO, SP, true, true, kBwdWalk>);
+    else if (has_d) go(scan_bwd_kernel<S, IO, SP, true, false, kBwdWalk>);
+    else if (has_z) go(scan_bwd_kernel<S, IO, SP, false, true, kBwdWalk>);
+    else go(scan_bwd_kernel<S, IO, SP, false, false, kBwdWalk>);
     return hipGetLastError();
 }
 

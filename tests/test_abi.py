@@ -307,9 +307,10 @@ def test_scan_bwd_rejects_bad_arguments(lib):
     assert chunked.value > need.value and (res.chunk_len, res.halves) == (16, 0)
     # Every workspace part scales with dstate except the half groups' extra
     # dB/dC slots, reserved for dstate 13..16 only when the sequence stays
-    # whole (a chunked plan never splits groups). So over dstate 8, 12, 16 the
-    # size grows in equal steps for a chunked plan, and by more from 12 to 16
-    # for a whole one. (At this shape every part is a whole number of the
+    # whole (a chunked plan never splits groups), and the chunked plan's
+    # per-tile delta sums, which do not depend on dstate. So over dstate 8,
+    # 12, 16 the size grows in equal steps for a chunked plan, and by more
+    # from 12 to 16 for a whole one. (At this shape every part is a whole number of the
     # 64-float alignment, so the steps are exact.)
     def ws(dstate, chunk_len):
         out = ctypes.c_size_t(0)
