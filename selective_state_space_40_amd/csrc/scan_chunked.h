@@ -712,6 +712,16 @@ __device__ __forceinline__ WaveSlot wave_slot(const ScanArgs& a, const ChunkGrid
     return s;
 }
 
+// The chunk carries (end states, decay products, entering states) are laid
+// out [chunk][batch row][state][channel]: the lanes of a wave hold 64
+// consecutive channels, so each of its per-state reads and writes is one
+// contiguous run of 256 bytes. Index of state n of channel d in chunk k;
+// the next state is `dim` floats on.
+__device__ __forceinline__ int64_t carry_at(const ScanArgs& a, int N, int64_t k, int64_t b,
+                                            int64_t d, int n) {
+    return ((k * a.batch + b) * N + n) * a.dim + d;
+}
+
 // The summary of one chunk from a zero entering state: its end state and its
 // decay product exp(A * sum of delta), the pair the carry folds.
 template <int N, int S, int IO, bool SP>
@@ -721,7 +731,7 @@ __device__ __forceinline__ void summary_group(const ScanArgs& a, const ChunkGrid
     constexpr int NPW = Split<N, S>::NPW;
     const WaveSlot s = wave_slot<N, S, IO>(a, g, blk);
     float A2[NPW], h[NPW];
-    const int64_t srow = ((s.k * a.batch + s.b) * a.dim + s.d) * N + s.n0;
+    const int64_t srow = carry_at(a, N, s.k, s.b, s.d, s.n0);
 #pragma unroll
     for (int q = 0; q < NPW; ++q) {
         A2[q] = a.A[s.d * N + s.n0 + q] * kLog2e;
@@ -732,22 +742,22 @@ __device__ __forceinline__ void summary_group(const ScanArgs& a, const ChunkGrid
                                                          lds, A2, h, 0.0f, 0.0f, dsum);
 #pragma unroll
     for (int q = 0; q < NPW; ++q) {
-        c.end[srow + q] = h[q];
-        c.decay[srow + q] = fast_exp2(A2[q] * dsum);
+        c.end[srow + q * a.dim] = h[q];
+        c.decay[srow + q * a.dim] = fast_exp2(A2[q] * dsum);
     }
 }
 
-// Carry pass: one thread per (b, d, n) column folds the chunk summaries in
+// Carry pass: one thread per (b, n, d) column folds the chunk summaries in
 // order and writes the state entering chunks 1 .. nchunks-1. With hL (the
 // repaired carry, whose pass 1 summarises the last chunk too) it folds
-// through the last chunk and writes the final state, whose (b, d, n) layout
-// is the column index. The pairs are loaded kCarryBatch chunks at a time
+// through the last chunk and writes the final state at (b, d, n). The pairs are loaded kCarryBatch chunks at a time
 // before they are folded, so a thread waits for memory once per batch rather
 // than once per chunk (the fold itself is one FMA per chunk).
 constexpr int kCarryBatch = 8;
 
 __global__ __launch_bounds__(256) void chunk_carry_kernel(int64_t columns, int64_t nchunks,
-                                                          Carry c, float* hL) {
+                                                          Carry c, float* hL, int64_t dim,
+                                                          int64_t nstate) {
     const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
     // chunks whose pair is folded: 1 .. last - 1 (the last one only with hL)
     const int64_t last = hL != nullptr ? nchunks : nchunks - 1;
@@ -770,7 +780,12 @@ __global__ __launch_bounds__(256) void chunk_carry_kernel(int64_t columns, int64
                 if (k < last) H = fmaf(P[u], H, E[u]);
             }
         }
-        if (hL != nullptr) hL[col] = H;
+        if (hL != nullptr) {
+            const int64_t b = col / (nstate * dim);
+            const int64_t r = col - b * nstate * dim;
+            const int64_t n = r / dim;
+            hL[(b * dim + (r - n * dim)) * nstate + n] = H;
+        }
     }
 }
 
@@ -796,9 +811,9 @@ __device__ __forceinline__ void output_group(const ScanArgs& a, const ChunkGrid&
         // kFoldBatch chunks are loaded before they are folded.
         constexpr int kFoldBatch = 4;
         const int64_t cols = a.batch * a.dim * N;
-        const int64_t col = (s.b * a.dim + s.d) * N + s.n0;
+        const int64_t col = carry_at(a, N, 0, s.b, s.d, s.n0);
 #pragma unroll
-        for (int q = 0; q < NPW; ++q) h[q] = c.end[col + q];
+        for (int q = 0; q < NPW; ++q) h[q] = c.end[col + q * a.dim];
         for (int64_t j0 = 1; j0 < s.k; j0 += kFoldBatch) {
             float P[kFoldBatch][NPW], E[kFoldBatch][NPW];
 #pragma unroll
@@ -807,8 +822,8 @@ __device__ __forceinline__ void output_group(const ScanArgs& a, const ChunkGrid&
                 const int64_t row = min(j0 + u, s.k - 1) * cols + col;
 #pragma unroll
                 for (int q = 0; q < NPW; ++q) {
-                    P[u][q] = c.decay[row + q];
-                    E[u][q] = c.end[row + q];
+                    P[u][q] = c.decay[row + q * a.dim];
+                    E[u][q] = c.end[row + q * a.dim];
                 }
             }
 #pragma unroll
@@ -820,9 +835,9 @@ __device__ __forceinline__ void output_group(const ScanArgs& a, const ChunkGrid&
             }
         }
     } else {
-        const int64_t srow = ((s.k * a.batch + s.b) * a.dim + s.d) * N + s.n0;
+        const int64_t srow = carry_at(a, N, s.k, s.b, s.d, s.n0);
 #pragma unroll
-        for (int q = 0; q < NPW; ++q) h[q] = c.start[srow + q];
+        for (int q = 0; q < NPW; ++q) h[q] = c.start[srow + q * a.dim];
     }
     const float dskip = HAS_D ? a.D[s.d] : 0.0f;
     float dsum = 0.0f;
@@ -831,9 +846,9 @@ __device__ __forceinline__ void output_group(const ScanArgs& a, const ChunkGrid&
     if constexpr (STORE_END) {
         // chunk 0 of a cut sequence: its end state, exact since it started
         // from h0, is the state entering chunk 1 and where the fold starts
-        const int64_t srow = ((s.k * a.batch + s.b) * a.dim + s.d) * N + s.n0;
+        const int64_t srow = carry_at(a, N, s.k, s.b, s.d, s.n0);
 #pragma unroll
-        for (int q = 0; q < NPW; ++q) c.end[srow + q] = h[q];
+        for (int q = 0; q < NPW; ++q) c.end[srow + q * a.dim] = h[q];
     } else if (s.k == g.seq_chunks - 1 && a.hL != nullptr) {
 #pragma unroll
         for (int q = 0; q < NPW; ++q) a.hL[(s.b * a.dim + s.d) * N + s.n0 + q] = h[q];
@@ -1123,7 +1138,7 @@ void chunk_local_kernel(ScanArgs a, ChunkGrid g, Carry c) {
     __shared__ ScanLds<N, S> lds;
     const WaveSlot s = wave_slot<N, S, IO>(a, g, blockIdx.x);
     float A2[NPW], h[NPW];
-    const int64_t srow = ((s.k * a.batch + s.b) * a.dim + s.d) * N + s.n0;
+    const int64_t srow = carry_at(a, N, s.k, s.b, s.d, s.n0);
 #pragma unroll
     for (int q = 0; q < NPW; ++q) {
         A2[q] = a.A[s.d * N + s.n0 + q] * kLog2e;
@@ -1135,8 +1150,8 @@ void chunk_local_kernel(ScanArgs a, ChunkGrid g, Carry c) {
                                                        lds, A2, h, dskip, 0.0f, dsum);
 #pragma unroll
     for (int q = 0; q < NPW; ++q) {
-        c.end[srow + q] = h[q];
-        c.decay[srow + q] = fast_exp2(A2[q] * dsum);
+        c.end[srow + q * a.dim] = h[q];
+        c.decay[srow + q * a.dim] = fast_exp2(A2[q] * dsum);
     }
 }
 
@@ -1150,13 +1165,13 @@ void chunk_fixup_kernel(ScanArgs a, ChunkGrid g, Carry c) {
     __shared__ ScanLds<N, S, true, true> lds;
     const WaveSlot s = wave_slot<N, S, IO>(a, g, blockIdx.x);
     float A2[NPW], h[NPW];
-    const int64_t srow = ((s.k * a.batch + s.b) * a.dim + s.d) * N + s.n0;
+    const int64_t srow = carry_at(a, N, s.k, s.b, s.d, s.n0);
     float a2max = -__builtin_inff();
     bool finite = true;
 #pragma unroll
     for (int q = 0; q < NPW; ++q) {
         A2[q] = a.A[s.d * N + s.n0 + q] * kLog2e;
-        h[q] = c.start[srow + q];
+        h[q] = c.start[srow + q * a.dim];
         a2max = fmaxf(a2max, A2[q]);
         finite = finite && __builtin_isfinite(h[q]);
     }
@@ -1178,7 +1193,7 @@ hipError_t launch_repaired(const ScanArgs& a, const ChunkGrid& g, const Carry& c
     hipLaunchKernelGGL((chunk_local_kernel<N, S, IO, SP, HAS_D, HAS_Z>),
                        dim3(g.nblk_d * g.nchunks * a.batch), block, 0, s, a, g, c);
     hipLaunchKernelGGL(chunk_carry_kernel, dim3(stride_blocks(columns)), dim3(256), 0, s, columns,
-                       g.nchunks, c, a.hL);
+                       g.nchunks, c, a.hL, a.dim, static_cast<int64_t>(N));
     ChunkGrid g2 = g;
     g2.nchunks = g.nchunks - 1;
     g2.first_chunk = 1;
@@ -1206,7 +1221,7 @@ hipError_t launch_rerun(const ScanArgs& a, const ChunkGrid& g, const Carry& c, i
         g2.fold = 1;
     } else {
         hipLaunchKernelGGL(chunk_carry_kernel, dim3(stride_blocks(columns)), dim3(256), 0, s,
-                           columns, g.seq_chunks, c, nullptr);
+                           columns, g.seq_chunks, c, nullptr, a.dim, static_cast<int64_t>(N));
     }
     hipLaunchKernelGGL((chunk_output_kernel<N, S, IO, SP, HAS_D, HAS_Z>), grid, block, 0, s, a, g2, c);
     return hipGetLastError();
