@@ -273,6 +273,7 @@ CHUNK_CASES = [
     (1, 129, 33, 2, "f32", 8),       # one tile per chunk, 17 chunks
     (3, 100, 20, 4, "f32", 24),
     (2, 64, 64, 16, "f32", 64),      # chunk_len == seqlen: one chunk
+    (1, 300, 96, 13, "bf16", 48),    # 4 waves, the last with padding states
 ]
 
 
