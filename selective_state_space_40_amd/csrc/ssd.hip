@@ -239,7 +239,6 @@ __global__ __launch_bounds__(kSsdThreads) __attribute__((amdgpu_waves_per_eu(2))
 void ssd_fwd_kernel(SsdArgs a) {
     constexpr int NW = N / 4;        // state rows n per wave
     constexpr int NTN = NW / 16;     // 16-row blocks of them
-    constexpr int RN = SsdLds<N>::kRowN, RQ = SsdLds<N>::kRowQ;
     __shared__ __attribute__((aligned(16))) SsdLds<N> lds;
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -257,16 +256,18 @@ void ssd_fwd_kernel(SsdArgs a) {
     // state H^T: block (nt, pt) holds rows n = nw0 + 16 nt + 4 g + v, column p = 16 pt + c
     const int nw0 = NW * w;
     if (tid < kP) lds.D[tid] = HAS_D ? a.D[hd * kP + tid] : 0.0f;
+    // the 4 values of a lane's block are 4 consecutive states of one channel:
+    // one 16-byte load (and, at the end, store) each
     f32x4 H[NTN][4];
 #pragma unroll
     for (int nt = 0; nt < NTN; ++nt)
 #pragma unroll
-        for (int pt = 0; pt < 4; ++pt)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int n = nw0 + 16 * nt + 4 * g + v, p = 16 * pt + c;
-                H[nt][pt][v] = a.h0 != nullptr ? a.h0[((bb * a.nheads + hd) * kP + p) * N + n] : 0.0f;
-            }
+        for (int pt = 0; pt < 4; ++pt) {
+            const int n = nw0 + 16 * nt + 4 * g, p = 16 * pt + c;
+            H[nt][pt] = a.h0 != nullptr
+                            ? *reinterpret_cast<const f32x4*>(&a.h0[((bb * a.nheads + hd) * kP + p) * N + n])
+                            : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        }
 
     const int64_t nchunks = (L + kQ - 1) / kQ;
     // the chunk whose loads a step issues: the next one, the last one
@@ -476,12 +477,10 @@ void ssd_fwd_kernel(SsdArgs a) {
 #pragma unroll
         for (int nt = 0; nt < NTN; ++nt)
 #pragma unroll
-            for (int pt = 0; pt < 4; ++pt)
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const int n = nw0 + 16 * nt + 4 * g + v, p = 16 * pt + c;
-                    a.hL[((bb * a.nheads + hd) * kP + p) * N + n] = H[nt][pt][v];
-                }
+            for (int pt = 0; pt < 4; ++pt) {
+                const int n = nw0 + 16 * nt + 4 * g, p = 16 * pt + c;
+                *reinterpret_cast<f32x4*>(&a.hL[((bb * a.nheads + hd) * kP + p) * N + n]) = H[nt][pt];
+            }
     }
 }
 
