@@ -113,10 +113,11 @@ typedef enum mamba_carry {
  * up to rounding (and, with MAMBA_CARRY_REPAIR, the bound stated above).
  *
  * chunk_len    tokens per parallel chunk. Each sequence is cut into chunks
- *              that run in parallel and are joined as `carry` says. A
- *              chunk_len of seqlen or more means one chunk and a single
- *              pass. The library may shorten a chunk so a chunk of one
- *              channel group spans less than 4 GiB.
+ *              that run in parallel and are joined as `carry` says; when
+ *              chunk_len does not divide seqlen, the first chunk is the
+ *              shorter one. A chunk_len of seqlen or more means one chunk
+ *              and a single pass. The library may shorten a chunk so a
+ *              chunk of one channel group spans less than 4 GiB.
  * state_split  waves sharing the dstate states of each channel: 1, 2, 4 or
  *              8. Values above 1 need dstate of 4, 8 or 16 divisible by the
  *              split.

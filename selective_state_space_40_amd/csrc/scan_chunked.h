@@ -640,6 +640,7 @@ struct ChunkGrid {
     int64_t nblk_d;           // channel groups per batch row
     int64_t nchunks;          // chunks per sequence the grid covers
     int64_t chunk_len;        // tokens per chunk
+    int64_t lead = 0;         // tokens by which sequence chunk 0 is shorter
     int64_t first_chunk = 0;  // sequence chunk of the grid's chunk 0
     int64_t seq_chunks = 1;   // chunks of the whole sequence (the last one writes hL)
     int fold = 0;             // output pass: fold the chunk summaries itself (no carry pass)
@@ -691,8 +692,11 @@ __device__ __forceinline__ WaveSlot wave_slot(const ScanArgs& a, const ChunkGrid
     // lanes past the last channel work on channel dim-1 (see compute_tile)
     const int64_t d0 = dblk * kWave;
     s.d = min(d0 + lane, a.dim - 1);
-    const int64_t t0 = s.k * g.chunk_len;
-    const int64_t t1 = min(a.seqlen, t0 + g.chunk_len);
+    // chunk k covers [k len - lead, (k+1) len - lead): the tokens that do
+    // not fill whole chunks shorten chunk 0, which the rerun carry's first
+    // pass scans to its outputs while the other chunks are only summarised
+    const int64_t t0 = s.k == 0 ? 0 : s.k * g.chunk_len - g.lead;
+    const int64_t t1 = min(a.seqlen, (s.k + 1) * g.chunk_len - g.lead);
     s.ntok = static_cast<int>(t1 - t0);
     s.dbias = a.delta_bias != nullptr ? a.delta_bias[s.d] : 0.0f;
     const int64_t first = (s.b * a.seqlen + t0) * a.dim + d0;  // element (b, t0, d0)
@@ -1234,6 +1238,7 @@ hipError_t launch_scan_ns(const ScanArgs& a, const ScanPlan& plan, void* ws, hip
     g.nchunks = plan.nchunks;
     g.seq_chunks = plan.nchunks;
     g.chunk_len = plan.chunk_len;
+    g.lead = plan.nchunks * plan.chunk_len - a.seqlen;
     Carry c{nullptr, nullptr, nullptr};
     const int64_t columns = a.batch * a.dim * N;
     if (plan.nchunks > 1) {
