@@ -152,6 +152,18 @@ __device__ __forceinline__ int64_t tent_index(const ScanArgs& f, int64_t tile, i
     return (((tile * f.batch + b) * groups + n0 / 4) * f.dim + d) * 4 + (n0 & 3);
 }
 
+// The per-group dB/dC partials are laid out [dB|dC][slot][batch row][group
+// of 4 states][token][4], `per` floats per slot: the 32 sums a wave holds
+// for one of them after its butterfly (8 tokens x 4 states) are 128
+// contiguous bytes. Index within a slot of (row b, token t, state n).
+__device__ __forceinline__ int64_t bc_index(const ScanArgs& f, int64_t b, int64_t t, int n) {
+    return ((b * ((f.dstate + 3) / 4) + n / 4) * f.seqlen + t) * 4 + (n & 3);
+}
+
+__device__ __forceinline__ int64_t bc_slot_floats(const ScanArgs& f) {
+    return f.batch * ((f.dstate + 3) / 4) * f.seqlen * 4;
+}
+
 template <int S, int IO, bool HAS_Z, bool WANT_G, bool CORR = false, bool WANT_H = WANT_G>
 __device__ __forceinline__ void fetch_tile(const BwdArgs& a, const Place& pl, const float* tent,
                                            int64_t tile, int cnt, TileRaw<S>& r,
@@ -597,8 +609,8 @@ __device__ __forceinline__ void bwd_whole_group(const BwdArgs& a, int64_t ngroup
                 const int j = r / kNpw;
                 const int n = pl.n0 + (r - j * kNpw);
                 if (j < cnt && n < N) {
-                    const int64_t per = f.batch * L * N;
-                    part_bc[(which * ws.nslots + pl.grp) * per + (pl.b * L + t0 + j) * N + n] = sum;
+                    part_bc[(which * ws.nslots + pl.grp) * bc_slot_floats(f) + bc_index(f, pl.b, t0 + j, n)] =
+                        sum;
                 }
             }
             __syncthreads();
@@ -1054,8 +1066,8 @@ __device__ __forceinline__ void bwd_half_group(const BwdArgs& a, int64_t ngroups
                 const int j = r / kHalfNps;
                 const int n = n0 + (r - j * kHalfNps);
                 if (j < cnt && n < N) {
-                    const int64_t per = f.batch * L * N;
-                    ws.part_bc[(which * ws.nslots + slot) * per + (b * L + t0 + j) * N + n] = sum;
+                    ws.part_bc[(which * ws.nslots + slot) * bc_slot_floats(f) + bc_index(f, b, t0 + j, n)] =
+                        sum;
                 }
             }
             __syncthreads();
@@ -1166,17 +1178,28 @@ __global__ __launch_bounds__(kWave * S) void bwd_forward_kernel(BwdArgs a, int64
 
 // dB and dC: the partials of all channel groups added in group order, a
 // split group's second half right after its first. Groups of row b from
-// index nwhole on in (row, group) order are split.
-__global__ __launch_bounds__(256) void bwd_bc_reduce_kernel(int64_t per, int64_t row,
-                                                            int64_t ngroups, int64_t nslots,
-                                                            int64_t nwhole, const float* part,
-                                                            float* dB, float* dC) {
+// index nwhole on in (row, group) order are split. Threads walk the
+// partials' layout (per floats per slot, [row][group of 4 states][token][4])
+// so their loads are contiguous; padding states are skipped.
+__global__ __launch_bounds__(256) void bwd_bc_reduce_kernel(int64_t per, int64_t seqlen,
+                                                            int dstate, int64_t ngroups,
+                                                            int64_t nslots, int64_t nwhole,
+                                                            const float* part, float* dB,
+                                                            float* dC) {
     const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+    const int64_t row = ((dstate + 3) / 4) * seqlen * 4;   // floats of one batch row
     for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < 2 * per;
          i += stride) {
         const int64_t which = i / per;
         const int64_t r = i - which * per;
-        const int64_t first_split = nwhole - (r / row) * ngroups;  // groups of this row
+        const int64_t b = r / row;
+        const int64_t gq = r - b * row;
+        const int64_t grp4 = gq / (seqlen * 4);
+        const int64_t tq = gq - grp4 * seqlen * 4;
+        const int64_t t = tq >> 2;
+        const int n = static_cast<int>(grp4 * 4 + (tq & 3));
+        if (n >= dstate) continue;
+        const int64_t first_split = nwhole - b * ngroups;  // groups of this row
         const bool halves = first_split < ngroups;
         // 8 groups' partials are loaded before they are added (in group order),
         // so a thread waits for memory once per 8 groups
@@ -1198,7 +1221,7 @@ __global__ __launch_bounds__(256) void bwd_bc_reduce_kernel(int64_t per, int64_t
                 }
             }
         }
-        (which ? dC : dB)[r] = s;
+        (which ? dC : dB)[(b * seqlen + t) * dstate + n] = s;
     }
 }
 
@@ -1297,8 +1320,8 @@ BwdLayout bwd_layout(int64_t batch, int64_t seqlen, int64_t dim, int dstate, int
     size_t off = 0;
     l.tent = off;   // states padded to whole groups of 4
     off += round64(static_cast<size_t>(l.ntiles) * batch * dim * ((dstate + 3) / 4 * 4));
-    l.part_bc = off;
-    off += round64(2 * static_cast<size_t>(l.nslots) * batch * seqlen * dstate);
+    l.part_bc = off;   // states padded to whole groups of 4
+    off += round64(2 * static_cast<size_t>(l.nslots) * batch * seqlen * ((dstate + 3) / 4 * 4));
     const size_t nc = static_cast<size_t>(l.nchunks);
     l.part_a = off;
     off += round64(nc * states);
@@ -1395,11 +1418,10 @@ hipError_t launch_bwd_io(const BwdArgs& a, float* ws, hipStream_t s) {
         default: return hipErrorInvalidValue;
     }
     if (e != hipSuccess) return e;
-    const int64_t per = f.batch * f.seqlen * f.dstate;
+    const int64_t per = f.batch * f.seqlen * ((f.dstate + 3) / 4 * 4);
     const int64_t nwhole = f.batch * l.ngroups - (bwd_halvable(f.dstate) ? a.halves : 0);
     hipLaunchKernelGGL(bwd_bc_reduce_kernel, dim3(stride_blocks(2 * per)), dim3(256), 0, s, per,
-                       f.seqlen * f.dstate, l.ngroups, l.nslots, nwhole, ws + l.part_bc, a.dB,
-                       a.dC);
+                       f.seqlen, f.dstate, l.ngroups, l.nslots, nwhole, ws + l.part_bc, a.dB, a.dC);
     hipLaunchKernelGGL(bwd_param_reduce_kernel, dim3(stride_blocks(f.dim * f.dstate)), dim3(256),
                        0, s, l.nchunks * f.batch, f.dim, f.dstate, ws + l.part_a, ws + l.part_d,
                        ws + l.part_bias, a.dA, a.dD, a.ddelta_bias);
