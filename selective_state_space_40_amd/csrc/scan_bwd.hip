@@ -489,8 +489,9 @@ __device__ __forceinline__ void bwd_whole_group(const BwdArgs& a, int64_t ngroup
         float hin[kNpw];
 #pragma unroll
         for (int q = 0; q < kNpw; ++q)
-            hin[q] = (CORR && chunk > 0 && sv[q] && pl.valid) ? ws.hin[chunk * f.batch * f.dim * N + col0 + pl.n0 + q]
-                                                  : 0.0f;
+            hin[q] = (CORR && chunk > 0 && sv[q] && pl.valid)
+                         ? ws.hin[chunk * f.batch * f.dim * N + col0 + pl.n0 + q]
+                         : 0.0f;
         float h[kNpw];
         TileRaw<S> raw;
         fetch_tile<S, IO, HAS_Z, true, CORR>(a, pl, tent, i_end - 1,
