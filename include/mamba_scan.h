@@ -294,10 +294,12 @@ int ssm_state_update(int64_t batch, int64_t dim, int dstate, int dtype, float* h
  *
  * The intermediate states are recomputed from checkpoints every 8 tokens
  * that the call itself computes into the workspace. A chunked sequence first
- * summarises every chunk but one twice, the state forward from a zero start
- * and the adjoint back from a zero start, and folds the summaries in chunk
- * order into each chunk's entering state and adjoint (the same combine as
- * the forward chunks'), so each chunk's gradients follow from its own
+ * runs every chunk forward from a zero start (chunk 0 from h0), writing its
+ * checkpoints and its summary, and summarises every chunk but the first
+ * backward from a zero adjoint; both summaries are folded in chunk order
+ * into each chunk's entering state and adjoint (the same combine as the
+ * forward chunks'), and the walk back adds the entering state, decayed, to
+ * each checkpoint it reads, so each chunk's gradients follow from its own
  * tokens. Sums over channels and rows are taken in a fixed order, so
  * results are reproducible bit for bit for a given plan. seqlen == 0 writes
  * zero dA, dD, ddelta_bias and dh0 = dhL. Outputs must not overlap inputs or
