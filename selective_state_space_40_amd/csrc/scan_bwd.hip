@@ -551,9 +551,9 @@ __device__ __forceinline__ void bwd_whole_group(const BwdArgs& a, int64_t ngroup
                 }
             }
 
+            // dB and dC terms: set token by token (zero past the sequence, in
+            // the branch only partial tiles take)
             float vals[kVals];
-#pragma unroll
-            for (int e = 0; e < kVals; ++e) vals[e] = 0.0f;
 #pragma unroll
             for (int j1 = kBT - 1; j1 >= 0; j1 -= 2) {
               // the LDS inputs of tokens j1 and j1 - 1 are read before either
@@ -597,6 +597,12 @@ __device__ __forceinline__ void bwd_whole_group(const BwdArgs& a, int64_t ngroup
                     lds.slot[pl.w][j][lane] = dt * lb;
                     lds.slot[pl.w][j][kWave + lane] = fmaf(x, lb, dap);
                     lds.slot[pl.w][j][2 * kWave + lane] = pp;
+                } else {
+#pragma unroll
+                    for (int q = 0; q < kNpw; ++q) {
+                        vals[j * kNpw + q] = 0.0f;
+                        vals[kBT * kNpw + j * kNpw + q] = 0.0f;
+                    }
                 }
               }
             }
@@ -1013,9 +1019,8 @@ __device__ __forceinline__ void bwd_half_group(const BwdArgs& a, int64_t ngroups
                 }
             }
 
+            // dB and dC terms: set token by token (zero past the sequence)
             float vals[kHalfVals];
-#pragma unroll
-            for (int e = 0; e < kHalfVals; ++e) vals[e] = 0.0f;
 #pragma unroll
             for (int j1 = kBT - 1; j1 >= 0; j1 -= 2) {
                 float2 vv[2], bq[2], cq[2];
@@ -1054,6 +1059,12 @@ __device__ __forceinline__ void bwd_half_group(const BwdArgs& a, int64_t ngroups
                         lds.red[0][v][j][ch] = dt * lb;
                         lds.red[1][v][j][ch] = fmaf(x, lb, dap);
                         lds.red[2][v][j][ch] = pp;
+                    } else {
+#pragma unroll
+                        for (int q = 0; q < kHalfNps; ++q) {
+                            vals[j * kHalfNps + q] = 0.0f;
+                            vals[kBT * kHalfNps + j * kHalfNps + q] = 0.0f;
+                        }
                     }
                 }
             }
