@@ -43,3 +43,22 @@ def test_roofline_names_the_planned_kernel():
     mixed = ms.Plan(2048, 4, ms.CARRY_RERUN, 128, 0)
     assert bench.dominant_kernel(whole) == "chunk_output_kernel"
     assert bench.dominant_kernel(mixed) == "chunk_mixed_kernel"
+
+
+def test_backward_algorithmic_counts():
+    # per element: two forward state updates of 4 operations per state, 9 per
+    # state walking back (lam, Abar lam, lam Abar h, dA, the A term of
+    # d delta, sum of lam B, the readout, the dB and dC terms) and 22 per
+    # element; transcendentals: the two updates' exps and the gate's exp and
+    # reciprocal
+    w = W.WORKLOADS["mamba28b_layer"]
+    elems = 8 * 2048 * 5120
+    assert bench.backward_alu_ops(w) == (8 * 16 + 9 * 16 + 22) * elems
+    assert bench.backward_alu_ops(w, softplus=True) == (8 * 16 + 9 * 16 + 22 + 16) * elems
+    assert bench.backward_transcendentals(w) == 2 * 16 + 2
+    assert bench.backward_transcendentals(w, softplus=True) == 2 * 16 + 2 + 4
+    # bytes: x, delta, z, dy in and dx, ddelta, dz out (bf16), B and C in
+    # (bf16) and dB, dC out (fp32), A, D in and dA, dD out, dh0 out
+    b, l, d, n = 8, 2048, 5120, 16
+    want = 7 * b * l * d * 2 + 2 * b * l * n * (2 + 4) + 2 * (d * n * 4 + d * 4) + b * d * n * 4
+    assert bench.backward_bytes(w) == want
