@@ -65,11 +65,17 @@ static_assert(kVals == kWave, "the butterfly leaves exactly one sum per lane");
 constexpr int kSlot = kNpw * kWave;
 static_assert(3 * kWave <= kSlot, "the partial sums fit in the slot of the factors");
 
+// The staged tile (all a forward pass or an adjoint summary needs, 7 KB
+// for 4 waves), and with the slots the whole walk back's LDS.
 template <int S>
-struct BwdLds {
+struct BwdLdsIn {
     float2 dtx[kBT][kWave];                    // (delta as used, x) per token and channel
     float g[kBT][kWave];                       // dy * silu(z)
     alignas(16) float bc[2][kBT][kNpw * S];    // B and C rows of the tile, padded states 0
+};
+
+template <int S>
+struct BwdLds : BwdLdsIn<S> {
     alignas(16) float slot[S][kBT][kSlot];
 };
 
@@ -199,7 +205,7 @@ __device__ __forceinline__ void fetch_tile(const BwdArgs& a, const Place& pl, co
 // Stage a fetched tile: wave w converts its tokens j = w, w+S, ... (delta
 // activated once per (channel, token)) and every thread its B or C element.
 template <int S, int IO, bool SP, bool HAS_Z, bool WANT_G>
-__device__ __forceinline__ void put_tile(const TileRaw<S>& r, const Place& pl, BwdLds<S>& lds,
+__device__ __forceinline__ void put_tile(const TileRaw<S>& r, const Place& pl, BwdLdsIn<S>& lds,
                                          int cnt, int nstate, Own (&own)[(kBT + S - 1) / S]) {
     const int lane = threadIdx.x & (kWave - 1);
 #pragma unroll
@@ -354,9 +360,9 @@ __device__ __forceinline__ Place make_place(const ScanArgs& f, int64_t ngroups, 
     return pl;
 }
 
-template <int S, int IO, bool SP, bool HAS_D, bool HAS_Z, int MODE = kBwdBoth>
+template <int S, int IO, bool SP, bool HAS_D, bool HAS_Z, int MODE = kBwdBoth, class LDS>
 __device__ __forceinline__ void bwd_whole_group(const BwdArgs& a, int64_t ngroups, int64_t blk,
-                                                const BwdWs& ws, BwdLds<S>& lds) {
+                                                const BwdWs& ws, LDS& lds) {
     constexpr int OW = (kBT + S - 1) / S;
     float* const tent = ws.tent;
     float* const part_bc = ws.part_bc;
@@ -483,8 +489,9 @@ __device__ __forceinline__ void bwd_whole_group(const BwdArgs& a, int64_t ngroup
     }
 
     // (2) the tiles in reverse. Walking alone, a chunk after the first adds
-    // its entering state, decayed to the tile, to each checkpoint.
-    {
+    // its entering state, decayed to the tile, to each checkpoint. (Not
+    // compiled for the forward pass alone, whose LDS has no slots.)
+    if constexpr (MODE != kBwdForward) {
         constexpr bool CORR = MODE == kBwdWalk;
         float hin[kNpw];
 #pragma unroll
@@ -657,33 +664,35 @@ __device__ __forceinline__ void bwd_whole_group(const BwdArgs& a, int64_t ngroup
         }
     }
 
-    // the gradient at h0 (first chunk; later chunks' en * lam is what their
+    // the gradient at h0 (first chunk; later chunks' Abar lam is what their
     // left neighbour takes in, already folded by the carry) and the
     // per-(chunk, row) partials of dA, dD, d bias
-    const int64_t prow = chunk * f.batch + pl.b;
-    if (pl.valid) {
+    if constexpr (MODE != kBwdForward) {
+        const int64_t prow = chunk * f.batch + pl.b;
+        if (pl.valid) {
 #pragma unroll
-        for (int q = 0; q < kNpw; ++q) {
-            if (sv[q]) {
-                const int64_t col = (pl.b * f.dim + pl.d) * N + pl.n0 + q;
-                if (chunk == 0 && a.dh0 != nullptr) a.dh0[col] = m[q];
-                part_a[(prow * f.dim + pl.d) * N + pl.n0 + q] = dA[q];
+            for (int q = 0; q < kNpw; ++q) {
+                if (sv[q]) {
+                    const int64_t col = (pl.b * f.dim + pl.d) * N + pl.n0 + q;
+                    if (chunk == 0 && a.dh0 != nullptr) a.dh0[col] = m[q];
+                    part_a[(prow * f.dim + pl.d) * N + pl.n0 + q] = dA[q];
+                }
             }
         }
-    }
-    __syncthreads();
-    lds.slot[pl.w][0][lane] = dD_acc;
-    lds.slot[pl.w][0][kWave + lane] = dbias_acc;
-    __syncthreads();
-    if (pl.w == 0 && pl.valid) {
-        float sd = 0.0f, sb = 0.0f;
+        __syncthreads();
+        lds.slot[pl.w][0][lane] = dD_acc;
+        lds.slot[pl.w][0][kWave + lane] = dbias_acc;
+        __syncthreads();
+        if (pl.w == 0 && pl.valid) {
+            float sd = 0.0f, sb = 0.0f;
 #pragma unroll
-        for (int u = 0; u < S; ++u) {
-            sd += lds.slot[u][0][lane];
-            sb += lds.slot[u][0][kWave + lane];
+            for (int u = 0; u < S; ++u) {
+                sd += lds.slot[u][0][lane];
+                sb += lds.slot[u][0][kWave + lane];
+            }
+            part_d[prow * f.dim + pl.d] = sd;
+            part_bias[prow * f.dim + pl.d] = sb;
         }
-        part_d[prow * f.dim + pl.d] = sd;
-        part_bias[prow * f.dim + pl.d] = sb;
     }
 }
 
@@ -711,7 +720,7 @@ __device__ __forceinline__ void bwd_whole_group(const BwdArgs& a, int64_t ngroup
 template <int S, int IO, bool SP, bool HAS_Z>
 __device__ __forceinline__ void bwd_adjoint_summary(const BwdArgs& a, int64_t ngroups,
                                                     const BwdWs& ws, float* end, float* decay,
-                                                    int64_t blk, BwdLds<S>& lds) {
+                                                    int64_t blk, BwdLdsIn<S>& lds) {
     const ScanArgs& f = a.fwd;
     const int N = f.dstate;
     const int64_t L = f.seqlen;
@@ -1180,7 +1189,7 @@ template <int S, int IO, bool SP, bool HAS_Z>
 __global__ __launch_bounds__(kWave * S) void bwd_forward_kernel(BwdArgs a, int64_t ngroups,
                                                                 BwdWs ws, BwdCarry c,
                                                                 int64_t nfwd) {
-    __shared__ BwdLds<S> lds;
+    __shared__ BwdLdsIn<S> lds;
     const int64_t blk = blockIdx.x;
     if (blk < nfwd)
         bwd_whole_group<S, IO, SP, false, false, kBwdForward>(a, ngroups, blk, ws, lds);
