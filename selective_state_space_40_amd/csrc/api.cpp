@@ -394,9 +394,10 @@ namespace {
 // SIMD; it is then cut into chunks of at least kMinChunk tokens for about
 // kBwdWavesPerSimd waves per SIMD (two rounds of the three the kernel holds
 // per SIMD), at the price of a state and an adjoint summary over every chunk
-// but one. (Measured on MI355X: the Mamba-130M layer 759 us with 8 chunks,
-// 774 with 4, 1028 with 2, 1185 whole; the million-token scan 61.4 ms with
-// 48 chunks, 65.8 with 24, 88.4 with 12.) Halves
+// but one. (Measured on MI355X: the Mamba-130M layer 0.50 ms with 8 chunks,
+// 0.51-0.53 ms with 6, 7, 9, 10, 12 or 16; the Mamba-2.8B layer, whose 640
+// groups fill 2.5 waves per SIMD, 1.35 ms whole against 1.47-1.55 ms with
+// 2 to 8 chunks.) Halves
 // (the last groups as two 32-channel halves, as in the forward plan) need
 // a whole sequence: forced halves keep it whole.
 constexpr int64_t kBwdWavesPerSimd = 6;
