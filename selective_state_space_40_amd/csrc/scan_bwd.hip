@@ -19,9 +19,10 @@
 // tokens and writes the state entering every tile to the workspace: the
 // checkpoints, 4 B per state and tile. (2) It takes the tiles from last to
 // first, carrying lam in registers: it reads the tile's checkpoint,
-// recomputes the tile's 8 states per lane into registers (whole groups also
-// keep the tile's decay factors in LDS, so the walk back does not evaluate
-// them again) and walks the tile backwards. Walking back, the adjoint is
+// recomputes the tile's 8 states per lane into registers, keeping the
+// tile's decay factors too (whole groups in LDS, half groups in registers),
+// so the walk back does not evaluate them again, and walks the tile
+// backwards. Walking back, the adjoint is
 // carried as m = Abar lam, what a token hands to the one before it: then
 // lam_t = C_t g_t + m is one FMA, and with lb = sum_n lam B the per-state
 // work is 9 operations (dx = D g + dt lb, d dt = sum_n A lam Abar h_{t-1} +
@@ -999,7 +1000,9 @@ __device__ __forceinline__ void bwd_half_group(const BwdArgs& a, int64_t ngroups
             prio.at(ntiles - 1 - i, 2);
             const int64_t t0 = i * kBT;
             const int cnt = static_cast<int>(min<int64_t>(kBT, L - t0));
-            float he[kHalfNps], hs[kBT][kHalfNps], h[kHalfNps];
+            // the recomputed states and the decay factors of the tile's
+            // tokens stay in registers for the walk back (2 states per lane)
+            float he[kHalfNps], hs[kBT][kHalfNps], ev[kBT][kHalfNps], h[kHalfNps];
 #pragma unroll
             for (int q = 0; q < kHalfNps; ++q) he[q] = (valid && sv[q]) ? raw.he[q] : 0.0f;
             put(Yes{}, raw, cnt);
@@ -1021,8 +1024,10 @@ __device__ __forceinline__ void bwd_half_group(const BwdArgs& a, int64_t ngroups
                 for (int jj = 0; jj < 2; ++jj) {
                     const int j = j0 + jj;
                     const float du = vq[jj].x * vq[jj].y;
-                    h[0] = fmaf(fast_exp2(vq[jj].x * A2[0]), h[0], du * bq[jj].x);
-                    h[1] = fmaf(fast_exp2(vq[jj].x * A2[1]), h[1], du * bq[jj].y);
+                    ev[j][0] = fast_exp2(vq[jj].x * A2[0]);
+                    ev[j][1] = fast_exp2(vq[jj].x * A2[1]);
+                    h[0] = fmaf(ev[j][0], h[0], du * bq[jj].x);
+                    h[1] = fmaf(ev[j][1], h[1], du * bq[jj].y);
                     hs[j][0] = h[0];
                     hs[j][1] = h[1];
                 }
@@ -1056,7 +1061,7 @@ __device__ __forceinline__ void bwd_half_group(const BwdArgs& a, int64_t ngroups
                         for (int q = 0; q < kHalfNps; ++q) {
                             const float lam = fmaf(Cv[q], gg, m[q]);
                             const float hprev = j > 0 ? hs[j > 0 ? j - 1 : 0][q] : he[q];
-                            m[q] = fast_exp2(dt * A2[q]) * lam;
+                            m[q] = ev[j][q] * lam;
                             const float le = m[q] * hprev;
                             dA[q] = fmaf(dt, le, dA[q]);
                             dap = fmaf(A[q], le, dap);
