@@ -25,7 +25,8 @@
 // the same permutation) and M never goes through LDS. C is read only by the
 // wave that owns the token, so each lane keeps its token's C row in
 // registers in operand layout. The chunk's x and B are staged once in LDS
-// (rows padded by 16 bytes), B also transposed for the state update, and the
+// as they lie in memory (token rows, padded by 16 bytes); the products that
+// contract over tokens take them through the LDS transpose read, and the
 // next chunk's inputs (x, B, C, z and the steps) are loaded into registers
 // while this one is computed; nothing in the chunk waits on global memory
 // until the next chunk is staged. bf16 I/O, head size 64, N = 64 or 128,
@@ -54,8 +55,7 @@ struct SsdLds {
     static constexpr int kRowN = N + 8;   // padded row of N bf16
     static constexpr int kRowQ = kQ + 8;  // padded row of 64 bf16
     __bf16 B[kQ][kRowN];     // B rows (j, n)
-    __bf16 Bt[N][kRowQ];     // B transposed (n, j), 8-value runs of j swizzled (tcol)
-    __bf16 Xt[kP][kRowQ];    // x transposed (p, j), swizzled the same way
+    __bf16 X[kQ][kRowQ];     // x rows (j, p)
     __bf16 H[kP][kRowN];     // the state entering the chunk (p, n)
     alignas(16) float dt[kQ];  // the step as used
     float S[kQ];             // log2 of the decay from chunk start through token j
@@ -63,14 +63,6 @@ struct SsdLds {
     alignas(16) float D[kP];   // the skip weights of the head's channels
     float Y[4][16][kP + 4];    // per wave: its 16 tokens' outputs before the gate (i, p)
 };
-
-// Column of element (row, col) of a transposed tile: the 16-byte run of 8
-// columns is XOR-ed with bits 3..5 of the row, so the 8 rows that the staging
-// lanes write together land in 8 different bank groups. A run of 8 (or of 4
-// starting at a multiple of 4) stays contiguous.
-__device__ __forceinline__ int tcol(int row, int col) {
-    return ((((col >> 3) ^ (row >> 3)) & 7) << 3) | (col & 7);
-}
 
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -80,18 +72,30 @@ __device__ __forceinline__ bf16x8 lds8(const __bf16* p) {
     return *reinterpret_cast<const bf16x8*>(p);
 }
 
-// Operand whose 8 K values are two runs of 4: p[0..3] and q[0..3].
-__device__ __forceinline__ bf16x8 lds4x2(const __bf16* p, const __bf16* q) {
-    typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
-    const bf16x4 a = *reinterpret_cast<const bf16x4*>(p);
-    const bf16x4 b = *reinterpret_cast<const bf16x4*>(q);
-    bf16x8 v;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        v[e] = a[e];
-        v[e + 4] = b[e];
-    }
-    return v;
+// Operands that contract over tokens read a token-major LDS tile T (rows of
+// RS bf16) through the LDS transpose read (ds_read_b64_tr_b16). Within each
+// group of 16 lanes, lane r receives element (r mod 4) of the 8 bytes that
+// lane 4e + r/4 of its group addresses, as its element e. So when lane s of
+// the group addresses row R + s/4, columns C + 4 (s mod 4) .. + 3, lane r
+// receives T[R + e][C + r] for e = 0..3: four consecutive K values of column
+// C + r, as an MFMA operand takes them. Lane (c, g) of the operand gets
+// T[r0 + e][c0 + c] as its K values 0..3 and T[r1 + e][c0 + c] as 4..7; r0
+// and r1 may differ per group g.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ s16x4 lds_tr4(const __bf16* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(const_cast<__bf16*>(p)));
+}
+
+template <int RS>
+__device__ __forceinline__ bf16x8 lds_tr8(const __bf16* T, int r0, int r1, int c0) {
+    const int s = threadIdx.x & 15;
+    const int off = (s >> 2) * RS + c0 + 4 * (s & 3);
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    const s16x4 a = lds_tr4(T + r0 * RS + off);
+    const s16x4 b = lds_tr4(T + r1 * RS + off);
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
 // How the chunk's inputs are spread over the threads. Threads 0 .. 63 each
@@ -214,26 +218,6 @@ __device__ __forceinline__ float wave_prefix_sum(float v) {
     return v;
 }
 
-// 8 x 8 bf16 transpose in registers: in[r] holds row r (8 values), out[f]
-// column f.
-__device__ __forceinline__ void transpose8(const uint4 (&in)[8], uint4 (&out)[8]) {
-    uint32_t iw[8][4];
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-        iw[r][0] = in[r].x; iw[r][1] = in[r].y; iw[r][2] = in[r].z; iw[r][3] = in[r].w;
-    }
-#pragma unroll
-    for (int f = 0; f < 8; ++f) {
-        uint32_t o[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const uint32_t lo = iw[2 * q][f >> 1], hi = iw[2 * q + 1][f >> 1];
-            o[q] = (f & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
-        }
-        out[f] = make_uint4(o[0], o[1], o[2], o[3]);
-    }
-}
-
 template <int N, bool SP, bool HAS_D, bool HAS_Z>
 __global__ __launch_bounds__(kSsdThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void ssd_fwd_kernel(SsdArgs a) {
@@ -287,26 +271,18 @@ void ssd_fwd_kernel(SsdArgs a) {
         const int64_t t0 = ch * kQ;
         const int cnt = static_cast<int>(min<int64_t>(kQ, L - t0));
 
-        // (1) stage the chunk: x transposed, B as it is and transposed; the
-        // steps, their running sum and the token weights; the state entering
-        // the chunk as bf16 (p, n)
-        if (tid < Layout<N>::kXBlocks + Layout<N>::kBBlocks) {
-            uint4 tr[8];
-            transpose8(blk, tr);
-            if (tid < Layout<N>::kXBlocks) {
-                const int jb = tid / (kP / 8), pb = tid % (kP / 8);
+        // (1) stage the chunk: x and B rows as they are; the steps, their
+        // running sum and the token weights; the state entering the chunk as
+        // bf16 (p, n)
+        if (tid < Layout<N>::kXBlocks) {
+            const int jb = tid / (kP / 8), pb = tid % (kP / 8);
 #pragma unroll
-                for (int f = 0; f < 8; ++f)
-                    *reinterpret_cast<uint4*>(&lds.Xt[8 * pb + f][tcol(8 * pb + f, 8 * jb)]) = tr[f];
-            } else {
-                const int e = tid - Layout<N>::kXBlocks;
-                const int jb = e / (N / 8), nb = e % (N / 8);
+            for (int f = 0; f < 8; ++f) *reinterpret_cast<uint4*>(&lds.X[8 * jb + f][8 * pb]) = blk[f];
+        } else if (tid < Layout<N>::kXBlocks + Layout<N>::kBBlocks) {
+            const int e = tid - Layout<N>::kXBlocks;
+            const int jb = e / (N / 8), nb = e % (N / 8);
 #pragma unroll
-                for (int f = 0; f < 8; ++f) {
-                    *reinterpret_cast<uint4*>(&lds.Bt[8 * nb + f][tcol(8 * nb + f, 8 * jb)]) = tr[f];
-                    *reinterpret_cast<uint4*>(&lds.B[8 * jb + f][8 * nb]) = blk[f];
-                }
-            }
+            for (int f = 0; f < 8; ++f) *reinterpret_cast<uint4*>(&lds.B[8 * jb + f][8 * nb]) = blk[f];
         }
         if (w == 0) {
             const float v = raw_to_f32<kIoBF16>(dtr) + bias;
@@ -373,8 +349,8 @@ void ssd_fwd_kernel(SsdArgs a) {
                 }
 #pragma unroll
                 for (int pt = 0; pt < 4; ++pt)
-                    Yd[pt] = mfma16(lds4x2(&lds.Xt[16 * pt + c][tcol(16 * pt + c, 32 * s2 + 4 * g)],
-                                           &lds.Xt[16 * pt + c][tcol(16 * pt + c, 32 * s2 + 16 + 4 * g)]),
+                    Yd[pt] = mfma16(lds_tr8<SsdLds<N>::kRowQ>(&lds.X[0][0], 32 * s2 + 4 * g,
+                                                              32 * s2 + 16 + 4 * g, 16 * pt),
                                     mb, Yd[pt]);
             }
         }
@@ -460,14 +436,18 @@ void ssd_fwd_kernel(SsdArgs a) {
             float wk[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) wk[e] = lds.w[k + 8 * g + e];
+            bf16x8 xo[4];
+#pragma unroll
+            for (int pt = 0; pt < 4; ++pt)
+                xo[pt] = lds_tr8<SsdLds<N>::kRowQ>(&lds.X[0][0], k + 8 * g, k + 8 * g + 4, 16 * pt);
 #pragma unroll
             for (int nt = 0; nt < NTN; ++nt) {
-                bf16x8 bw = lds8(&lds.Bt[nw0 + 16 * nt + c][tcol(nw0 + 16 * nt + c, k + 8 * g)]);
+                bf16x8 bw = lds_tr8<SsdLds<N>::kRowN>(&lds.B[0][0], k + 8 * g, k + 8 * g + 4,
+                                                      nw0 + 16 * nt);
 #pragma unroll
                 for (int e = 0; e < 8; ++e) bw[e] = static_cast<__bf16>(static_cast<float>(bw[e]) * wk[e]);
 #pragma unroll
-                for (int pt = 0; pt < 4; ++pt)
-                    H[nt][pt] = mfma16(bw, lds8(&lds.Xt[16 * pt + c][tcol(16 * pt + c, k + 8 * g)]), H[nt][pt]);
+                for (int pt = 0; pt < 4; ++pt) H[nt][pt] = mfma16(bw, xo[pt], H[nt][pt]);
             }
         }
         __syncthreads();
