@@ -57,9 +57,13 @@ struct SsdLds {
     __bf16 B[kQ][kRowN];     // B rows (j, n)
     __bf16 X[kQ][kRowQ];     // x rows (j, p)
     __bf16 H[kP][kRowN];     // the state entering the chunk (p, n)
-    alignas(16) float dt[kQ];  // the step as used
-    float S[kQ];             // log2 of the decay from chunk start through token j
-    float w[kQ];             // exp(S_last - S_j) dt_j: weight of token j in the state update
+    // Per-token values of a chunk, double-buffered by chunk parity: wave 0
+    // forms those of the next chunk at the end of the current one.
+    struct Steps {
+        alignas(16) float dt[kQ];  // the step as used
+        float S[kQ];               // log2 of the decay from chunk start through token j
+        float w[kQ];               // exp(S_last - S_j) dt_j: weight of token j in the state update
+    } st[2];
     alignas(16) float D[kP];   // the skip weights of the head's channels
     float Y[4][16][kP + 4];    // per wave: its 16 tokens' outputs before the gate (i, p)
 };
@@ -105,6 +109,8 @@ __device__ __forceinline__ bf16x8 lds_tr8(const __bf16* T, int r0, int r1, int c
 // products read it (8 values of n at 8 g + 32 k for k < N / 32), and the gate
 // z and input x of 8 channels of two of its wave's tokens in row order (see
 // the output step).
+constexpr int kXWave = 3;  // the wave that stages x
+
 template <int N>
 struct Layout {
     static constexpr int kXBlocks = (kQ / 8) * (kP / 8);
@@ -138,8 +144,10 @@ struct ChunkPos {
 
 // x and B blocks and the step, consumed when the chunk is staged. One load
 // sequence for every wave (a branch per tensor would merge the loaded
-// registers through copies that wait for the loads): wave 0 loads x blocks,
-// the next waves B blocks, any other wave an empty range.
+// registers through copies that wait for the loads): wave 3, which has the
+// most causal work but nothing else before the staging barrier, loads x
+// blocks, waves 1 (and 2 for N = 128) B blocks, any other wave an empty
+// range; wave 0 forms the steps of the chunk ahead.
 template <int N>
 __device__ __forceinline__ void fetch_tiles(const SsdArgs& a, int64_t hd, ChunkPos c,
                                             uint4 (&blk)[8], uint32_t& dt) {
@@ -147,13 +155,14 @@ __device__ __forceinline__ void fetch_tiles(const SsdArgs& a, int64_t hd, ChunkP
     const int lane = tid & (kWave - 1);
     const int dim = static_cast<int>(a.nheads) * kP;
     const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);
-    const bool isx = wv == 0, isb = wv > 0 && wv * kWave < Layout<N>::kXBlocks + Layout<N>::kBBlocks;
+    const bool isx = wv == kXWave;
+    const bool isb = wv >= 1 && wv < kXWave && (wv - 1) * kWave < Layout<N>::kBBlocks;
     const __amdgpu_buffer_rsrc_t rx = chunk_rsrc(
         static_cast<const uint16_t*>(a.x) + c.row0 * dim + hd * kP, ((c.cnt - 1) * dim + kP) * 2);
     const __amdgpu_buffer_rsrc_t rb =
         chunk_rsrc(static_cast<const uint16_t*>(a.B) + c.row0 * N, isb ? c.cnt * N * 2 : 0);
-    const int e = tid - Layout<N>::kXBlocks;
-    const int off = isx ? ((tid / (kP / 8)) * 8 * dim + 8 * (tid % (kP / 8))) * 2
+    const int xe = tid - kXWave * kWave, e = tid - kWave;
+    const int off = isx ? ((xe / (kP / 8)) * 8 * dim + 8 * (xe % (kP / 8))) * 2
                         : ((e / (N / 8)) * 8 * N + 8 * (e % (N / 8))) * 2;
     const int step = isx ? dim * 2 : N * 2;
     const __amdgpu_buffer_rsrc_t rblk = isx ? rx : rb;
@@ -264,34 +273,39 @@ void ssd_fwd_kernel(SsdArgs a) {
     uint4 blk[8], zc[2], xc[2];
     uint32_t dtr;
     bf16x8 cop[Layout<N>::kCk];
+    // Wave 0: the steps of a chunk of cnt_k tokens from their raw values in
+    // dtr, their running sum (a DPP prefix sum) and the token weights.
+    auto form_steps = [&](typename SsdLds<N>::Steps& o, int cnt_k) {
+        const float v = raw_to_f32<kIoBF16>(dtr) + bias;
+        const float dtv = lane < cnt_k ? (SP ? softplus_f32(v) : v) : 0.0f;
+        const float s = wave_prefix_sum(dtv) * alog2;
+        const float last = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s), kWave - 1));
+        o.dt[lane] = dtv;
+        o.S[lane] = s;
+        o.w[lane] = fast_exp2(last - s) * dtv;
+    };
     fetch_tiles<N>(a, hd, pos(0), blk, dtr);
     fetch_c<N>(a, pos(0), cop);
     fetch_out<HAS_D, HAS_Z>(a, hd, pos(0), zc, xc);
+    if (w == 0) form_steps(lds.st[0], pos(0).cnt);
     for (int64_t ch = 0; ch < nchunks; ++ch) {
         const int64_t t0 = ch * kQ;
         const int cnt = static_cast<int>(min<int64_t>(kQ, L - t0));
 
-        // (1) stage the chunk: x and B rows as they are; the steps, their
-        // running sum and the token weights; the state entering the chunk as
-        // bf16 (p, n)
-        if (tid < Layout<N>::kXBlocks) {
-            const int jb = tid / (kP / 8), pb = tid % (kP / 8);
+        // (1) stage the chunk: x and B rows as they are and the state
+        // entering the chunk as bf16 (p, n); its steps were formed at the end
+        // of the chunk before
+        const typename SsdLds<N>::Steps& sp = lds.st[ch & 1];
+        if (w == kXWave) {
+            const int xe = tid - kXWave * kWave;
+            const int jb = xe / (kP / 8), pb = xe % (kP / 8);
 #pragma unroll
             for (int f = 0; f < 8; ++f) *reinterpret_cast<uint4*>(&lds.X[8 * jb + f][8 * pb]) = blk[f];
-        } else if (tid < Layout<N>::kXBlocks + Layout<N>::kBBlocks) {
-            const int e = tid - Layout<N>::kXBlocks;
+        } else if (w >= 1 && tid - kWave < Layout<N>::kBBlocks) {
+            const int e = tid - kWave;
             const int jb = e / (N / 8), nb = e % (N / 8);
 #pragma unroll
             for (int f = 0; f < 8; ++f) *reinterpret_cast<uint4*>(&lds.B[8 * jb + f][8 * nb]) = blk[f];
-        }
-        if (w == 0) {
-            const float v = raw_to_f32<kIoBF16>(dtr) + bias;
-            const float dtv = lane < cnt ? (SP ? softplus_f32(v) : v) : 0.0f;
-            const float s = wave_prefix_sum(dtv) * alog2;
-            const float last = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s), kWave - 1));
-            lds.dt[lane] = dtv;
-            lds.S[lane] = s;
-            lds.w[lane] = fast_exp2(last - s) * dtv;
         }
 #pragma unroll
         for (int nt = 0; nt < NTN; ++nt)
@@ -307,11 +321,11 @@ void ssd_fwd_kernel(SsdArgs a) {
 
         // the next chunk's tiles and steps go out now and land during this one
         fetch_tiles<N>(a, hd, pos(ch + 1), blk, dtr);
-        const float s_last = lds.S[kQ - 1];
+        const float s_last = sp.S[kQ - 1];
 
         // (3) M^T for this wave's tokens: blocks jt = 0 .. w of G^T = B C^T
         f32x4 Mt[4];
-        const float si = lds.S[i];
+        const float si = sp.S[i];
 #pragma unroll
         for (int jt = 0; jt < 4; ++jt) {
             Mt[jt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -321,8 +335,8 @@ void ssd_fwd_kernel(SsdArgs a) {
                     Mt[jt] = mfma16(lds8(&lds.B[16 * jt + c][k + 8 * g]), cop[k / 32], Mt[jt]);
                 // token j = 16 jt + 4 g + v; above the diagonal (j > i) the
                 // factor may overflow and is discarded by the select
-                const f32x4 sj = *reinterpret_cast<const f32x4*>(&lds.S[16 * jt + 4 * g]);
-                const f32x4 dj = *reinterpret_cast<const f32x4*>(&lds.dt[16 * jt + 4 * g]);
+                const f32x4 sj = *reinterpret_cast<const f32x4*>(&sp.S[16 * jt + 4 * g]);
+                const f32x4 dj = *reinterpret_cast<const f32x4*>(&sp.dt[16 * jt + 4 * g]);
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
                     const float e = fast_exp2(si - sj[v]) * dj[v];
@@ -435,7 +449,7 @@ void ssd_fwd_kernel(SsdArgs a) {
         for (int k = 0; k < kQ; k += 32) {
             float wk[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) wk[e] = lds.w[k + 8 * g + e];
+            for (int e = 0; e < 8; ++e) wk[e] = sp.w[k + 8 * g + e];
             bf16x8 xo[4];
 #pragma unroll
             for (int pt = 0; pt < 4; ++pt)
@@ -450,6 +464,10 @@ void ssd_fwd_kernel(SsdArgs a) {
                 for (int pt = 0; pt < 4; ++pt) H[nt][pt] = mfma16(bw, xo[pt], H[nt][pt]);
             }
         }
+        // the next chunk's steps, by the wave with the least causal work
+        // (its raw steps were loaded after this chunk was staged; the buffer
+        // was last read in the chunk before this one)
+        if (w == 0) form_steps(lds.st[(ch + 1) & 1], pos(ch + 1).cnt);
         __syncthreads();
     }
 
