@@ -123,6 +123,20 @@ def test_conv_decode_steps_equal_forward(orc):
             _state_equal(state, so, f"conv decode W={width} D={dim}")
 
 
+def test_conv_decode_many_rows(orc):
+    # 70,001 batch rows of a few channels: more rows than a grid dimension
+    # of 65,535 holds, even and odd channel counts
+    for io, dim in (("bf16", 6), ("f32", 5)):
+        inp = _inputs(70001, 1, dim, 4, io, seed=dim)
+        yo, so = orc.conv1d_fwd(inp["x"], inp["weight"], inp["bias"], inp["state_in"])
+        state = inp["state_in"].clone()
+        _say(f"case conv decode 70001 rows D={dim} {io}")
+        y = ms.conv1d_update(state, inp["x"][:, 0].contiguous(), inp["weight"], inp["bias"])
+        torch.cuda.synchronize()
+        assert_close(y, yo[:, 0], TOL[io], f"conv decode 70001 rows D={dim} y")
+        _state_equal(state, so, f"conv decode 70001 rows D={dim}")
+
+
 @pytest.mark.parametrize("layer", [0, 41])
 def test_conv_decode_layer_full_size(orc, layer):
     w = W.CONV_WORKLOADS["conv_decode_64layer"]
