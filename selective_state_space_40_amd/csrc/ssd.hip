@@ -98,16 +98,15 @@ template <int RS>
 __device__ __forceinline__ bf16x8 lds_tr8(const __bf16* T, int r0, int r1, int c0) {
     const int s = threadIdx.x & 15;
     const int off = (s >> 2) * RS + c0 + 4 * (s & 3);
-    typedef short s16x8 __attribute__((ext_vector_type(8)));
     const s16x4 a = lds_tr4(T + r0 * RS + off);
     const s16x4 b = lds_tr4(T + r1 * RS + off);
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-// How the chunk's inputs are spread over the threads. Threads 0 .. 63 each
-// load an 8 x 8 block (8 tokens, 8 channels) of x, the next N threads (N / 8
-// blocks per 8 tokens) an 8 x 8 block of B; lanes of wave 0 load the raw
-// step of token `lane`. Every lane loads the C row of its own token i as the
+// How the chunk's inputs are spread over the threads. 64 threads each
+// load an 8 x 8 block (8 tokens, 8 channels) of x, N threads (N / 8
+// blocks per 8 tokens) an 8 x 8 block of B; every lane loads the raw step
+// of token `lane` (wave 0 forms the steps from it). Every lane loads the C row of its own token i as the
 // products read it (8 values of n at 8 g + 32 k for k < N / 32), and the gate
 // z and input x of 8 channels of two of its wave's tokens in row order (see
 // the output step).
