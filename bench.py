@@ -312,14 +312,19 @@ def main():
     # it, the vector issue fraction and the HBM fraction this formulation
     # would reach with every issue slot busy (the step needs at least
     # algorithmic_slots / ISSUE_PEAK_T of issue time), with transcendentals
-    # at one slot and, as a bound from the other side, at two.
+    # at one slot and, as a bound from the other side, at two; and the issue
+    # fraction with every transcendental priced at the two issue cycles it
+    # holds the vector ALU for (frac_trans_at_2).
     hbm_frac = gbps / HBM_PEAK_GBPS
     slots = ops
     issue = issue_roofline(slots, sec)
+    slots2 = slots + transcendentals(w, sp) * elems
+    issue["frac_trans_at_2"] = round(slots2 / sec / 1e12 / ISSUE_PEAK_T, 4)
+    issue["algorithmic_slots_trans_at_2"] = slots2
     hbm_time = bytes_alg / (HBM_PEAK_GBPS * 1e9)
     issue["hbm_frac_at_full_issue"] = round(hbm_time / (slots / (ISSUE_PEAK_T * 1e12)), 4)
     issue["hbm_frac_at_full_issue_trans_at_2"] = round(
-        hbm_time / ((slots + transcendentals(w, sp) * elems) / (ISSUE_PEAK_T * 1e12)), 4)
+        hbm_time / (slots2 / (ISSUE_PEAK_T * 1e12)), 4)
     plain = not (args.batch or args.dim or sp or args.chunk_len or args.state_split or args.halves
                  or args.carry != "auto")
     traffic = recorded_traffic(w.name, dominant_kernel(plan)) if nchunks == 1 and plain else None

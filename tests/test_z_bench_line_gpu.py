@@ -67,6 +67,11 @@ def test_default_bench_line():
     assert iss["algorithmic_slots"] == slots == 89 * elems
     assert iss["frac"] == pytest.approx(slots / (d["ms_per_step"] / 1e3) / 39.3216e12, abs=1e-3)
     assert 0.0 < iss["frac"] < 1.0
+    # the same with each transcendental (N + 2 per element) at two issue cycles
+    assert iss["algorithmic_slots_trans_at_2"] == (89 + 18) * elems
+    assert iss["frac_trans_at_2"] == pytest.approx(
+        (89 + 18) * elems / (d["ms_per_step"] / 1e3) / 39.3216e12, abs=1e-3)
+    assert iss["frac"] < iss["frac_trans_at_2"] < 1.0
     assert iss["hbm_frac_at_full_issue"] == pytest.approx(
         (nbytes / 8e12) / (slots / 39.3216e12), abs=1e-3)
     assert iss["hbm_frac_at_full_issue_trans_at_2"] == pytest.approx(
