@@ -57,6 +57,9 @@ CASES = [
     # (batch, seqlen, nheads, dstate)
     (1, 1, 1, 64), (1, 5, 2, 128), (2, 63, 1, 64), (1, 64, 3, 128), (2, 65, 2, 64),
     (1, 128, 1, 128), (2, 200, 3, 128), (1, 257, 2, 64), (3, 31, 1, 128),
+    # many chunks with a ragged last one: the per-chunk step values alternate
+    # between two buffers, formed one chunk ahead
+    (1, 4097, 2, 128), (2, 1000, 1, 64),
 ]
 
 
